@@ -1,0 +1,237 @@
+"""Seeded generators for the synthetic MoE workloads.
+
+Every tensor of every layer comes from its own counter-keyed stream
+``numpy.random.Generator(PCG64(SeedSequence([workload, layer, tensor, index])))``
+so any expert of any layer can be regenerated alone, in any order, and the
+bytes are identical on every machine with the same numpy.
+
+What the streams hold (the recipe is the library's reading of the pages'
+workload; the pages themselves print no weights):
+
+* routed expert matrices: raw block bytes of the two 2-bit formats the
+  QuarkStar and DwarfStar pages name for routed experts (QuarkStar README,
+  "Model Weights": gate/up at a codebook 2-bit type, down at a Q2_K-type),
+  with every quantised field uniform over its range and every fp16 scale
+  drawn as fp16(U[0,1) * 2^-10), rounded to nearest even;
+* the codebook: 256 rows x 8 entries, each uniform over {1, 3, 5, 7};
+* router weights fp32 ~ N(0, 0.02^2); an optional Zipf(s) expert-popularity
+  bias b[e] = -s * ln(1 + rank(e)) with rank a seeded permutation;
+* the shared expert in bf16 ~ N(0, 0.02^2), rounded to nearest even;
+* token activations fp32 ~ N(0, 1).
+
+The module does no part of the MoE step's arithmetic.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+
+# Block geometry of the two routed-expert formats (bytes per 256 weights).
+Q2K_BLOCK_BYTES = 84
+CB2_BLOCK_BYTES = 70
+BLOCK_WEIGHTS = 256
+
+# Tensor ids used in the seed key.
+T_ROUTER, T_BIAS, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN, T_X, T_CODEBOOK = range(10)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shapes, formats and router bias of one synthetic MoE workload."""
+
+    name: str
+    seed_id: int
+    hidden: int            # H
+    n_experts: int         # E
+    top_k: int             # k
+    expert_ffn: int        # F
+    shared_ffn: int        # Fs (0 = no shared expert)
+    gate_up_format: str    # "cb2" or "q2k"
+    down_format: str       # "cb2" or "q2k"
+    n_layers: int
+    tokens: Tuple[int, ...] = (1,)
+    zipf_s: Optional[float] = None
+    note: str = ""
+
+    def block_bytes(self, fmt: str) -> int:
+        return block_bytes(fmt)
+
+    def expert_bytes(self) -> Tuple[int, int, int]:
+        """Bytes of one expert's gate, up and down matrices in the raw format."""
+        H, F = self.hidden, self.expert_ffn
+        g = F * (H // BLOCK_WEIGHTS) * block_bytes(self.gate_up_format)
+        d = H * (F // BLOCK_WEIGHTS) * block_bytes(self.down_format)
+        return g, g, d
+
+    def router_bytes(self) -> int:
+        return self.n_experts * self.hidden * 4
+
+    def shared_bytes(self) -> int:
+        return 3 * self.shared_ffn * self.hidden * 2
+
+    def stored_bytes(self) -> int:
+        g, u, d = self.expert_bytes()
+        per_layer = self.n_experts * (g + u + d) + self.router_bytes() + self.shared_bytes()
+        return self.n_layers * per_layer
+
+    def step_bytes(self, distinct_experts_per_layer, n_tokens: int) -> int:
+        """Algorithmic bytes one decode step must read and write: per layer the
+        router, the shared expert and each distinct selected expert once, plus
+        the activations in and out."""
+        g, u, d = self.expert_bytes()
+        total = 0
+        for u_l in distinct_experts_per_layer:
+            total += self.router_bytes() + self.shared_bytes() + int(u_l) * (g + u + d)
+        return total + 2 * n_tokens * self.hidden * 4
+
+
+WORKLOADS = {
+    # tiny single layer, every matrix Q2_K-style, no shared expert
+    "tiny_q2k": Workload("tiny_q2k", 0, 512, 16, 2, 256, 0, "q2k", "q2k", 1, (1, 4, 16, 64),
+                         note="tiny single layer, all Q2_K-style"),
+    # Qwen3.6-35B-A3B-class single layer with a bf16 shared expert
+    "a3b_layer": Workload("a3b_layer", 1, 2048, 256, 8, 512, 512, "cb2", "q2k", 1, (1,),
+                          note="Qwen3.6-35B-A3B-class single layer"),
+    # 40 routed-only layers of the A3B shapes, near-uniform picks
+    "a3b_routed40": Workload("a3b_routed40", 2, 2048, 256, 8, 512, 0, "cb2", "q2k", 40, (1,),
+                             note="40-layer routed-expert stack, A3B shapes"),
+    # the same stack with every matrix Q2_K-style (secondary reading)
+    "a3b_routed40_q2k": Workload("a3b_routed40_q2k", 5, 2048, 256, 8, 512, 0, "q2k", "q2k", 40, (1,),
+                                 note="40-layer routed stack, all Q2_K-style"),
+    # 40 layers of the single-layer shapes incl. shared expert, Zipf(1.1) router bias
+    "a3b_stack40_zipf": Workload("a3b_stack40_zipf", 3, 2048, 256, 8, 512, 512, "cb2", "q2k", 40,
+                                 (1, 4, 16, 64), zipf_s=1.1,
+                                 note="40-layer A3B stack with shared expert, Zipf(1.1) popularity"),
+    # DeepSeek-V4-Flash-class large layer, 8 stacked
+    "flash_stack8_zipf": Workload("flash_stack8_zipf", 4, 4096, 256, 6, 2048, 2048, "cb2", "q2k", 8,
+                                  (1, 8, 32), zipf_s=1.1,
+                                  note="8-layer DeepSeek-V4-Flash-class stack, Zipf(1.1) popularity"),
+}
+
+
+def block_bytes(fmt: str) -> int:
+    if fmt == "q2k":
+        return Q2K_BLOCK_BYTES
+    if fmt == "cb2":
+        return CB2_BLOCK_BYTES
+    raise ValueError(f"unknown block format {fmt!r}")
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
+
+
+def _fp16_scales(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n fp16 bit patterns of fp16(U[0,1) * 2^-10), round to nearest even."""
+    u = rng.random(n, dtype=np.float32) * np.float32(2.0 ** -10)
+    return u.astype(np.float16).view(np.uint16)
+
+
+def fp32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest even) and return the 16-bit patterns."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def codebook(seed: int = 0) -> np.ndarray:
+    """The 256 x 8 codebook of the codebook 2-bit format: int8 entries, each
+    uniform over {1, 3, 5, 7}, row-major, from stream (seed, codebook)."""
+    rng = _rng(seed, T_CODEBOOK)
+    return (2 * rng.integers(0, 4, size=(256, 8)) + 1).astype(np.int8)
+
+
+def _raw(rng, nblocks, bb, out):
+    src = np.frombuffer(rng.bytes(nblocks * bb), dtype=np.uint8).reshape(nblocks, bb)
+    if out is None:
+        return src.copy()
+    out = out.reshape(nblocks, bb)
+    out[...] = src
+    return out
+
+
+def q2k_blocks(rng: np.random.Generator, nblocks: int, out=None) -> np.ndarray:
+    """nblocks raw Q2_K-style blocks [nblocks][84]: bytes 0..79 (scales and
+    2-bit codes) uniform, d and dmin (bytes 80..83) fp16(U[0,1)*2^-10)."""
+    raw = _raw(rng, nblocks, Q2K_BLOCK_BYTES, out)
+    dd = _fp16_scales(rng, 2 * nblocks).reshape(nblocks, 2)
+    raw[:, 80:84] = dd.view(np.uint8).reshape(nblocks, 4)
+    return raw
+
+
+def cb2_blocks(rng: np.random.Generator, nblocks: int, out=None) -> np.ndarray:
+    """nblocks raw codebook 2-bit blocks [nblocks][70]: d (bytes 0..1)
+    fp16(U[0,1)*2^-10); scales, codebook indices and sign masks uniform."""
+    raw = _raw(rng, nblocks, CB2_BLOCK_BYTES, out)
+    d = _fp16_scales(rng, nblocks)
+    raw[:, 0:2] = d.view(np.uint8).reshape(nblocks, 2)
+    return raw
+
+
+def expert_tensor(wl: Workload, layer: int, tensor: int, expert: int, out=None) -> np.ndarray:
+    """Raw bytes of one expert matrix, shape [rows][cols/256][block bytes]:
+    gate/up are [F][H/256] blocks, down is [H][F/256] blocks."""
+    H, F = wl.hidden, wl.expert_ffn
+    if tensor in (T_GATE, T_UP):
+        rows, kb, fmt = F, H // BLOCK_WEIGHTS, wl.gate_up_format
+    elif tensor == T_DOWN:
+        rows, kb, fmt = H, F // BLOCK_WEIGHTS, wl.down_format
+    else:
+        raise ValueError("not an expert tensor")
+    rng = _rng(wl.seed_id, layer, tensor, expert)
+    gen = q2k_blocks if fmt == "q2k" else cb2_blocks
+    return gen(rng, rows * kb, out).reshape(rows, kb, block_bytes(fmt))
+
+
+@dataclass
+class LayerWeights:
+    """One layer's tensors in the raw (upload) layout."""
+
+    router: np.ndarray                 # fp32 [E][H]
+    router_bias: Optional[np.ndarray]  # fp32 [E] or None
+    gate: np.ndarray                   # uint8 [E][F][H/256][bb]
+    up: np.ndarray                     # uint8 [E][F][H/256][bb]
+    down: np.ndarray                   # uint8 [E][H][F/256][bb]
+    shared_gate: Optional[np.ndarray] = None   # uint16 bf16 bits [Fs][H]
+    shared_up: Optional[np.ndarray] = None     # uint16 bf16 bits [Fs][H]
+    shared_down: Optional[np.ndarray] = None   # uint16 bf16 bits [H][Fs]
+    experts: Tuple[int, ...] = field(default_factory=tuple)
+
+
+def layer_weights(wl: Workload, layer: int, experts=None) -> LayerWeights:
+    """Generate one layer.  ``experts`` restricts the routed matrices to a
+    subset (in the given order); the router and shared expert are whole."""
+    E, H, Fs = wl.n_experts, wl.hidden, wl.shared_ffn
+    ex = tuple(range(E)) if experts is None else tuple(int(e) for e in experts)
+    router = _rng(wl.seed_id, layer, T_ROUTER, 0).standard_normal((E, H), dtype=np.float32)
+    router *= np.float32(0.02)
+    bias = None
+    if wl.zipf_s is not None:
+        rank = _rng(wl.seed_id, layer, T_BIAS, 0).permutation(E)
+        bias = (-wl.zipf_s * np.log1p(rank.astype(np.float64))).astype(np.float32)
+    H, F = wl.hidden, wl.expert_ffn
+    bg, bd = block_bytes(wl.gate_up_format), block_bytes(wl.down_format)
+    gate = np.empty((len(ex), F, H // BLOCK_WEIGHTS, bg), dtype=np.uint8)
+    up = np.empty_like(gate)
+    down = np.empty((len(ex), H, F // BLOCK_WEIGHTS, bd), dtype=np.uint8)
+    for i, e in enumerate(ex):
+        expert_tensor(wl, layer, T_GATE, e, gate[i])
+        expert_tensor(wl, layer, T_UP, e, up[i])
+        expert_tensor(wl, layer, T_DOWN, e, down[i])
+    lw = LayerWeights(router, bias, gate, up, down, experts=ex)
+    if Fs:
+        def bf16(tid, shape):
+            a = _rng(wl.seed_id, layer, tid, 0).standard_normal(shape, dtype=np.float32)
+            return fp32_to_bf16_bits(a * np.float32(0.02))
+        lw.shared_gate = bf16(T_SGATE, (Fs, H))
+        lw.shared_up = bf16(T_SUP, (Fs, H))
+        lw.shared_down = bf16(T_SDOWN, (H, Fs))
+    return lw
+
+
+def tokens(wl: Workload, n_tokens: int, batch: int = 0) -> np.ndarray:
+    """Token activations fp32 [T][H] ~ N(0, 1) for input batch ``batch``."""
+    return _rng(wl.seed_id, 0xFFFF, T_X, n_tokens, batch).standard_normal(
+        (n_tokens, wl.hidden), dtype=np.float32)

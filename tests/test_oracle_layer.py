@@ -1,0 +1,147 @@
+"""Pins of the oracle's expert FFN, combine and stacked layers against
+brute force (every expert evaluated densely with torch's fp64 ops, then the
+router's mask applied) and closed-form special cases."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe as om
+
+
+def _tiny(gate_up="q2k", shared=0, E=8, k=2, zipf=None, L=1):
+    return synth.Workload("pin", 99, 256, E, k, 256, shared, gate_up, "q2k", L, (1,), zipf_s=zipf)
+
+
+def _dense_reference(wl, lw, cb, x):
+    """All E experts evaluated densely with torch fp64, combined through a
+    one-hot selection mask built from torch.topk on the logits."""
+    xt = torch.from_numpy(x.astype(np.float64))
+    lg = xt @ torch.from_numpy(lw.router.astype(np.float64)).T
+    if lw.router_bias is not None:
+        lg = lg + torch.from_numpy(lw.router_bias.astype(np.float64))
+    vals, idx = torch.topk(lg, wl.top_k, dim=1)
+    wts = torch.softmax(vals, dim=1)
+    mask = torch.zeros(lg.shape, dtype=torch.float64)
+    mask.scatter_(1, idx, wts)
+    y = torch.zeros((x.shape[0], wl.hidden), dtype=torch.float64)
+    for e in range(wl.n_experts):
+        wg = torch.from_numpy(om.dequant_matrix(lw.gate[e], wl.gate_up_format, cb).astype(np.float64))
+        wu = torch.from_numpy(om.dequant_matrix(lw.up[e], wl.gate_up_format, cb).astype(np.float64))
+        wd = torch.from_numpy(om.dequant_matrix(lw.down[e], wl.down_format, cb).astype(np.float64))
+        o = (torch.nn.functional.silu(xt @ wg.T) * (xt @ wu.T)) @ wd.T
+        y += mask[:, e:e + 1] * o
+    if wl.shared_ffn:
+        sg, su, sd = (torch.from_numpy(om.bf16_bits_to_f64(m)) for m in
+                      (lw.shared_gate, lw.shared_up, lw.shared_down))
+        y += (torch.nn.functional.silu(xt @ sg.T) * (xt @ su.T)) @ sd.T
+    return y.numpy(), idx.numpy()
+
+
+@pytest.mark.parametrize("gate_up,shared,zipf", [("q2k", 0, None), ("cb2", 0, None),
+                                                 ("cb2", 256, 1.1), ("q2k", 256, None)])
+def test_routed_layer_equals_dense_masked_brute_force(gate_up, shared, zipf):
+    wl = _tiny(gate_up, shared, zipf=zipf)
+    lw = synth.layer_weights(wl, 0)
+    cb = synth.codebook()
+    x = synth.tokens(wl, 6)
+    r = om.moe_layer(om.Layer(wl, lw, cb), x)
+    y, idx = _dense_reference(wl, lw, cb, x)
+    assert np.all(r["gap"] > 1e-9)                 # no near-ties in the set
+    assert np.array_equal(r["ids"], idx)
+    assert np.max(om.rel_l2(r["y"], y)) < 1e-6      # fp32 rounding of the output only
+
+
+def test_silu_matches_torch():
+    v = np.linspace(-30, 30, 2001)
+    assert np.allclose(om.silu(v), torch.nn.functional.silu(torch.from_numpy(v)).numpy(),
+                       rtol=1e-14, atol=1e-300)
+    assert om.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_identical_experts_make_routing_irrelevant():
+    """All experts equal and no shared expert: y = FFN(x) for any routing."""
+    wl = _tiny("cb2", 0, E=6, k=3)
+    lw = synth.layer_weights(wl, 0)
+    for m in (lw.gate, lw.up, lw.down):
+        m[:] = m[0]
+    cb = synth.codebook()
+    x = synth.tokens(wl, 3)
+    r = om.moe_layer(om.Layer(wl, lw, cb), x)
+    xt = torch.from_numpy(x.astype(np.float64))
+    wg = torch.from_numpy(om.dequant_matrix(lw.gate[0], "cb2", cb).astype(np.float64))
+    wu = torch.from_numpy(om.dequant_matrix(lw.up[0], "cb2", cb).astype(np.float64))
+    wd = torch.from_numpy(om.dequant_matrix(lw.down[0], "q2k", cb).astype(np.float64))
+    ref = ((torch.nn.functional.silu(xt @ wg.T) * (xt @ wu.T)) @ wd.T).numpy()
+    assert np.max(om.rel_l2(r["y"], ref)) < 1e-6
+
+
+def test_zero_input_gives_zero_output():
+    wl = _tiny("cb2", 256)
+    lw = synth.layer_weights(wl, 0)
+    r = om.moe_layer(om.Layer(wl, lw, synth.codebook()), np.zeros((2, wl.hidden), np.float32))
+    assert np.all(r["y"] == 0.0)
+
+
+def test_k1_output_is_the_argmax_expert_plus_shared():
+    wl = _tiny("q2k", 256, E=5, k=1)
+    lw = synth.layer_weights(wl, 0)
+    cb = synth.codebook()
+    L = om.Layer(wl, lw, cb)
+    x = synth.tokens(wl, 2)
+    r = om.moe_layer(L, x)
+    lg = om.router_logits(x, lw.router)
+    for t in range(2):
+        e = int(np.argmax(lg[t]))
+        _, o = om.swiglu_ffn(x[t], *L.expert(e))
+        _, s = om.swiglu_ffn(x[t], *L.shared())
+        assert np.max(om.rel_l2(r["y"][t], o + s)) < 1e-6
+
+
+def _scale_fields(down, fn):
+    for field in (80, 82):
+        bits = down[..., field].astype(np.uint16) | (down[..., field + 1].astype(np.uint16) << 8)
+        bits = fn(bits)
+        down[..., field] = bits & 0xFF
+        down[..., field + 1] = bits >> 8
+
+
+def test_combine_is_linear_in_expert_outputs():
+    """Scaling every down matrix by 2 (exactly: d and dmin exponents +1)
+    doubles the routed part of the output."""
+    wl = _tiny("cb2", 0)
+    cb = synth.codebook()
+    x = synth.tokens(wl, 2)
+    lw = synth.layer_weights(wl, 0)
+    _scale_fields(lw.down, lambda b: np.where((b >> 10) & 0x1F == 0, b | 0x0400, b))  # all normal
+    lw2 = synth.layer_weights(wl, 0)
+    lw2.down[:] = lw.down
+    _scale_fields(lw2.down, lambda b: b + 0x0400)                                    # exactly 2x
+    y1 = om.moe_layer(om.Layer(wl, lw, cb), x)["y"]
+    y2 = om.moe_layer(om.Layer(wl, lw2, cb), x)["y"]
+    assert np.max(om.rel_l2(y2, 2 * y1.astype(np.float64))) < 1e-6
+
+
+def test_residual_and_stack_chain():
+    wl = _tiny("cb2", 256, L=3)
+    cb = synth.codebook()
+    layers = [om.Layer(wl, synth.layer_weights(wl, l), cb) for l in range(3)]
+    x = synth.tokens(wl, 2)
+    out, per = om.moe_stack(layers, x)
+    cur = x
+    for l in range(3):
+        r = om.moe_layer(layers[l], cur)
+        cur = (cur.astype(np.float64) + r["y"].astype(np.float64))
+        assert np.max(om.rel_l2(per[l]["y"], cur)) < 1e-6
+        cur = per[l]["y"]
+    assert np.array_equal(out, per[-1]["y"])
+
+
+def test_generator_is_deterministic_and_keyed():
+    wl = synth.WORKLOADS["tiny_q2k"]
+    a = synth.layer_weights(wl, 0)
+    b = synth.layer_weights(wl, 0, experts=[3, 1])
+    assert np.array_equal(a.gate[3], b.gate[0]) and np.array_equal(a.down[1], b.down[1])
+    c = synth.layer_weights(wl, 1)
+    assert not np.array_equal(a.gate, c.gate)
+    assert np.array_equal(synth.tokens(wl, 4, 2), synth.tokens(wl, 4, 2))
