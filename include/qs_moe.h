@@ -1,0 +1,176 @@
+/*
+ * qs_moe.h -- C ABI of the decode-time routed-expert MoE step over 2-bit
+ * block-quantised weights, for AMD Instinct MI355X (gfx950).
+ *
+ * The step: router logits -> top-k with renormalised softmax -> grouping of
+ * (token, slot) pairs by expert -> for each selected expert a fused
+ * dequantise + gate/up GEMV + SwiGLU -> down GEMV -> weighted combine, plus an
+ * ungated high-precision shared expert.  Only the routed experts are 2-bit:
+ * gate/up in a codebook 2-bit type, down in a Q2_K type; router and shared
+ * expert stay at high precision (QuarkStar README, "Model Weights"; DwarfStar
+ * page, "Model Weights").  Dequantisation is fused into the GEMV, since
+ * single-stream decode is bound by reading the weights (Quasar README,
+ * "Performance model" and "Design decisions").
+ *
+ * Pointers: every pointer argument is a plain address.  "device" means GPU
+ * memory readable by the handle's device; "host or device" means either
+ * (the library copies with hipMemcpyDefault).  No pointer is retained
+ * after a call returns, except inside the handle's own allocations.
+ *
+ * Errors: every entry point returns a qs_status.  Arguments are validated on
+ * the host before anything is enqueued; on error nothing has been enqueued
+ * unless the status is QS_E_HIP, in which case the outputs of that call are
+ * undefined (no partial results are defined).  qs_moe_status_string() names
+ * a status.
+ *
+ * Threading: a handle may be used by one host thread at a time.  Calls on one
+ * handle share the handle's scratch memory, so two decode calls on the same
+ * handle must be ordered (the same stream, or the caller's events).
+ */
+#ifndef QS_MOE_H
+#define QS_MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QS_MOE_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define QS_API __attribute__((visibility("default")))
+#else
+#define QS_API
+#endif
+
+typedef enum {
+  QS_OK = 0,
+  QS_E_INVAL = -1,        /* bad argument: NULL, size, range, alignment */
+  QS_E_NOMEM = -2,        /* a device or host allocation failed */
+  QS_E_HIP = -3,          /* a HIP runtime call or kernel launch failed */
+  QS_E_STATE = -4,        /* a layer used before it was uploaded */
+  QS_E_UNSUPPORTED = -5   /* a valid but unsupported configuration */
+} qs_status;
+
+/* Routed-expert block formats (256 weights per block, little endian).
+ *
+ * QS_FMT_Q2K, 84 bytes (the Q2_K type of the pages' down projections):
+ *   [0,16)  scales[16]: sub-block i = weights 16i..16i+15 has
+ *           sc = scales[i] & 15 and m = scales[i] >> 4
+ *   [16,80) qs[64]: weight j has q = (qs[j/4] >> 2*(j%4)) & 3
+ *   [80,82) d (IEEE binary16), [82,84) dmin (binary16)
+ *   value w_j = d*sc*q_j - dmin*m, rounded once to fp32.
+ *
+ * QS_FMT_CB2, 70 bytes (the codebook 2-bit type of the pages' gate/up):
+ *   [0,2)   d (binary16)
+ *   [2,6)   scales: sub-block i = weights 32i..32i+31 has
+ *           s = (byte[2 + i/2] >> 4*(i%2)) & 15
+ *   [6,38)  idx[32]: group g = weights 8g..8g+7 uses codebook row idx[g]
+ *   [38,70) sign[32]: bit b of sign[g] set => weight 8g+b is negated
+ *   value w_j = +/- d*s*C[idx[j/8]][j%8] (exact in fp32), with C the
+ *   256 x 8 int8 codebook given to qs_moe_create.
+ *
+ * Matrix layout: row-major [rows][cols/256] blocks, rows consecutive.
+ * gate/up of one expert are [F][H/256] blocks, down is [H][F/256] blocks;
+ * the E experts of a layer are consecutive. */
+typedef enum { QS_FMT_Q2K = 1, QS_FMT_CB2 = 2 } qs_format;
+
+/* qs_moe_decode flags */
+#define QS_DECODE_RESIDUAL 1u   /* x_{l+1} = x_l + MoE_l(x_l); y gets the last x */
+
+typedef struct qs_moe qs_moe;   /* opaque, owned by the library */
+
+typedef struct {
+  int32_t abi_version;     /* QS_MOE_ABI_VERSION */
+  int32_t hidden;          /* H: multiple of 256, 256..16384 */
+  int32_t n_experts;       /* E: 1..1024 */
+  int32_t top_k;           /* k: 1..min(E, 16) */
+  int32_t expert_ffn;      /* F: multiple of 256, 256..16384 */
+  int32_t shared_ffn;      /* Fs: 0 (no shared expert) or a multiple of 64 up to 16384 */
+  int32_t gate_up_format;  /* QS_FMT_CB2 or QS_FMT_Q2K */
+  int32_t down_format;     /* QS_FMT_Q2K (QS_FMT_CB2 down is QS_E_UNSUPPORTED) */
+  int32_t n_layers;        /* layers held resident: 1..4096 */
+  int32_t max_tokens;      /* largest n_tokens of a decode call: 1..256, and
+                              max_tokens * top_k <= 1024 */
+  int32_t mfma_min_tokens; /* expert bucket size at which the matrix-core path
+                              replaces the GEMV path; 0 = library default */
+  int32_t device;          /* HIP device ordinal; -1 = the current device */
+} qs_moe_config;
+
+/* One layer's weights in the raw block layout above.  Host or device
+ * pointers; all are only read during qs_moe_upload. */
+typedef struct {
+  const float*    router;       /* fp32 [E][H] */
+  const float*    router_bias;  /* fp32 [E], or NULL for zeros */
+  const void*     gate;         /* [E][F][H/256] blocks of gate_up_format */
+  const void*     up;           /* [E][F][H/256] blocks of gate_up_format */
+  const void*     down;         /* [E][H][F/256] blocks of down_format */
+  const uint16_t* shared_gate;  /* bf16 [Fs][H]; NULL iff Fs == 0 */
+  const uint16_t* shared_up;    /* bf16 [Fs][H] */
+  const uint16_t* shared_down;  /* bf16 [H][Fs] */
+} qs_moe_layer_weights;
+
+/* Create a handle: validates cfg, allocates all device memory for n_layers
+ * layers and every scratch buffer a decode call of max_tokens needs.
+ * codebook: host int8 [256][8] (required iff either format is QS_FMT_CB2,
+ * else ignored, may be NULL).  On success *out owns the allocations; on
+ * error *out is NULL and nothing stays allocated.  Validation happens before
+ * any HIP call, so an invalid cfg fails without touching the GPU. */
+QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_moe** out);
+
+/* Copy one layer's weights into the handle's device memory, re-laying the
+ * routed blocks out for the kernels (the dequantised values are unchanged).
+ * hip_stream: a hipStream_t or NULL for the null stream.  Returns after the
+ * copies are complete, so the sources may be freed at once.  Re-uploading a
+ * layer replaces it. */
+QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, void* hip_stream);
+
+/* Decode n_tokens tokens through layers [layer0, layer0 + n_layers).
+ * x: device fp32 [n_tokens][H]; y: device fp32 [n_tokens][H].
+ * Without QS_DECODE_RESIDUAL: n_layers must be 1 and y = MoE(x); x and y must
+ * not overlap.  With it: x_{l+1} = x_l + MoE_l(x_l) layer by layer and y
+ * receives the final x; y == x (in place) is allowed.
+ * ids_out: device int32 [n_layers][n_tokens][k] or NULL -- selected experts
+ * in rank order (logit descending, ties to the lower index).
+ * w_out: device fp32 [n_layers][n_tokens][k] or NULL -- their renormalised
+ * softmax weights.  Asynchronous on hip_stream; performs no allocation and
+ * no host synchronisation.  1 <= n_tokens <= max_tokens. */
+QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, float* y,
+                  int n_tokens, uint32_t flags, int32_t* ids_out, float* w_out,
+                  void* hip_stream);
+
+/* Routing only (diagnostics and tests): the router, top-k and grouping steps
+ * of one layer for n_tokens tokens, with every intermediate written out.
+ * Any output pointer may be NULL.  All outputs are device memory:
+ *   logits_out fp64 [n_tokens][E]       router logits
+ *   ids_out    int32 [n_tokens][k]      as in qs_moe_decode
+ *   w_out      fp32 [n_tokens][k]       as in qs_moe_decode
+ *   group_out  int32 [3*E + 2 + n_tokens*k]:
+ *      [0, E)              count of pairs per expert
+ *      [E, 2E+1)           exclusive offsets (offsets[E] = n_tokens*k)
+ *      [2E+1, 2E+1+T*k)    pairs token*k + slot, ordered by (expert, token)
+ *      [2E+1+T*k]          number of experts with a non-empty bucket, U
+ *      [2E+2+T*k, 3E+2+T*k) those experts ascending (entries >= U are -1)
+ * Asynchronous on hip_stream. */
+QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, double* logits_out,
+                 int32_t* ids_out, float* w_out, int32_t* group_out, void* hip_stream);
+
+/* Dequantise one routed matrix from the handle's device copy with the same
+ * field decoding the GEMV kernels use (tests).  which: 0 gate, 1 up, 2 down.
+ * out: device fp32 [F][H] (gate/up) or [H][F] (down).  Asynchronous. */
+QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* out, void* hip_stream);
+
+/* Bytes of device memory the handle holds (weights + scratch). */
+QS_API int qs_moe_memory_bytes(const qs_moe* h, uint64_t* bytes);
+
+/* Synchronise the handle's device, then free everything.  NULL is a no-op. */
+QS_API int qs_moe_destroy(qs_moe* h);
+
+/* Static string naming a status; never NULL. */
+QS_API const char* qs_moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QS_MOE_H */

@@ -1,0 +1,15 @@
+"""MI355X-native decode-time routed-expert MoE over 2-bit block weights.
+
+The compute path is libqsmoe.so (hand-written HIP for gfx950) behind the C ABI
+of include/qs_moe.h; this package is its ctypes binding plus a small handle
+class that marshals torch tensors and numpy arrays.  PyTorch is used only
+for device memory and streams.
+"""
+from ._lib import (  # noqa: F401
+    LIB, LIB_PATH, EXPORTS, QsError, QsMoeConfig, QsMoeLayerWeights, status_string, make_config,
+    qs_moe_create, qs_moe_upload, qs_moe_decode, qs_moe_route, qs_moe_dequant,
+    qs_moe_memory_bytes, qs_moe_destroy,
+    QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED,
+    QS_FMT_Q2K, QS_FMT_CB2, QS_DECODE_RESIDUAL, QS_MOE_ABI_VERSION,
+)
+from .handle import MoE  # noqa: F401

@@ -1,0 +1,540 @@
+// qs_moe.hip -- the C ABI declared in include/qs_moe.h.
+//
+// Ownership: the handle owns one device allocation per layer (router, bias,
+// repacked routed matrices, shared expert) and one scratch allocation sized
+// for max_tokens at create time, so decode neither allocates nor
+// synchronises.  Upload stages raw blocks through a device buffer the
+// handle keeps until destroy and re-lays them out with a repack kernel.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "qs_moe.h"
+#include "qs_kernels.h"
+#include "qs_layout.h"
+
+using namespace qs;
+
+namespace {
+
+struct LayerDev {
+  uint8_t* base = nullptr;   // single allocation
+  float* router = nullptr;
+  float* bias = nullptr;
+  uint8_t* gate = nullptr;
+  uint8_t* up = nullptr;
+  uint8_t* down = nullptr;
+  uint16_t* sg = nullptr;
+  uint16_t* su = nullptr;
+  uint16_t* sd = nullptr;
+  bool uploaded = false;
+};
+
+struct Scratch {
+  uint8_t* base = nullptr;
+  size_t bytes = 0;
+  double* logits;
+  int32_t* ids;
+  float* wts;
+  int32_t* cnt;
+  int32_t* off;
+  int32_t* pairs;
+  int32_t* n_active;
+  int32_t* active;
+  int32_t* tok_order;
+  uint32_t* xh;
+  uint32_t* xl;
+  float* xs;
+  int32_t* xa;
+  uint32_t* ah;
+  uint32_t* al;
+  float* as;
+  int32_t* aa;
+  float* ash;
+  float* xbuf[2];
+};
+
+}  // namespace
+
+struct qs_moe {
+  qs_moe_config cfg;
+  int device = 0;
+  size_t gu_stride = 0;      // bytes per repacked gate/up expert matrix
+  size_t dn_stride = 0;      // bytes per repacked down expert matrix
+  size_t layer_bytes = 0;
+  std::vector<LayerDev> layers;
+  Scratch s;
+  uint32_t* cbtab = nullptr; // device codebook quad tables
+  uint8_t* staging = nullptr;
+  size_t staging_bytes = 0;
+  uint64_t total_bytes = 0;
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (dev >= 0 && dev != prev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+#define QS_HIP(call)                                                      \
+  do {                                                                    \
+    hipError_t err_ = (call);                                             \
+    if (err_ != hipSuccess) {                                             \
+      fprintf(stderr, "qs_moe: %s failed: %s\n", #call, hipGetErrorString(err_)); \
+      return QS_E_HIP;                                                    \
+    }                                                                     \
+  } while (0)
+
+size_t gate_up_block_bytes(const qs_moe_config& c) {
+  return c.gate_up_format == QS_FMT_CB2 ? kCB2Bytes : kQ2KBytes;
+}
+
+int validate_config(const qs_moe_config* c) {
+  if (!c) return QS_E_INVAL;
+  if (c->abi_version != QS_MOE_ABI_VERSION) return QS_E_INVAL;
+  if (c->hidden < 256 || c->hidden > 16384 || c->hidden % 256) return QS_E_INVAL;
+  if (c->expert_ffn < 256 || c->expert_ffn > 16384 || c->expert_ffn % 256) return QS_E_INVAL;
+  if (c->n_experts < 1 || c->n_experts > 1024) return QS_E_INVAL;
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return QS_E_INVAL;
+  if (c->shared_ffn < 0 || c->shared_ffn > 16384 || c->shared_ffn % 64) return QS_E_INVAL;
+  if (c->gate_up_format != QS_FMT_CB2 && c->gate_up_format != QS_FMT_Q2K) return QS_E_INVAL;
+  if (c->down_format != QS_FMT_CB2 && c->down_format != QS_FMT_Q2K) return QS_E_INVAL;
+  if (c->n_layers < 1 || c->n_layers > 4096) return QS_E_INVAL;
+  if (c->max_tokens < 1 || c->max_tokens > kMaxTokens) return QS_E_INVAL;
+  if ((long)c->max_tokens * c->top_k > kMaxPairs) return QS_E_INVAL;
+  if (c->mfma_min_tokens < 0) return QS_E_INVAL;
+  if (c->device < -1) return QS_E_INVAL;
+  if (c->down_format != QS_FMT_Q2K) return QS_E_UNSUPPORTED;
+  return QS_OK;
+}
+
+// Signed int8 quads of the codebook with the sign nibbles applied.
+void build_cb_tables(const int8_t* cb, std::vector<uint32_t>& tab) {
+  tab.assign(kCbTabWords, 0);
+  for (int idx = 0; idx < 256; ++idx)
+    for (int s = 0; s < 16; ++s) {
+      uint32_t lo = 0, hi = 0;
+      for (int b = 0; b < 4; ++b) {
+        const int vlo = ((s >> b) & 1) ? -cb[idx * 8 + b] : cb[idx * 8 + b];
+        const int vhi = ((s >> b) & 1) ? -cb[idx * 8 + 4 + b] : cb[idx * 8 + 4 + b];
+        lo |= (uint32_t)(uint8_t)(int8_t)vlo << (8 * b);
+        hi |= (uint32_t)(uint8_t)(int8_t)vhi << (8 * b);
+      }
+      tab[idx * 16 + s] = lo;
+      tab[4096 + s * 256 + idx] = hi;
+    }
+}
+
+template <typename T>
+T* carve(uint8_t*& p, size_t count) {
+  T* r = (T*)p;
+  p += align_up(count * sizeof(T), 256);
+  return r;
+}
+
+size_t scratch_bytes(const qs_moe_config& c) {
+  const size_t T = c.max_tokens, E = c.n_experts, k = c.top_k, H = c.hidden, F = c.expert_ffn;
+  const size_t P = T * k;
+  size_t b = 0;
+  auto add = [&](size_t n) { b += align_up(n, 256); };
+  add(T * E * 8);                 // logits
+  add(P * 4); add(P * 4);         // ids, wts
+  add(E * 4); add((E + 1) * 4);   // cnt, off
+  add(P * 4); add(4); add(E * 4); add(P * 4);  // pairs, n_active, active, tok_order
+  add(T * H); add(T * H);         // xh, xl (H/4 dwords)
+  add(T * (H / 16) * 4); add(T * (H / 16) * 4);
+  add(P * F); add(P * F);         // ah, al
+  add(P * (F / 16) * 4); add(P * (F / 16) * 4);
+  add(T * (size_t)(c.shared_ffn ? c.shared_ffn : 1) * 4);
+  add(T * H * 4); add(T * H * 4); // residual ping-pong
+  return b;
+}
+
+void carve_scratch(const qs_moe_config& c, Scratch& s) {
+  const size_t T = c.max_tokens, E = c.n_experts, k = c.top_k, H = c.hidden, F = c.expert_ffn;
+  const size_t P = T * k;
+  uint8_t* p = s.base;
+  s.logits = carve<double>(p, T * E);
+  s.ids = carve<int32_t>(p, P);
+  s.wts = carve<float>(p, P);
+  s.cnt = carve<int32_t>(p, E);
+  s.off = carve<int32_t>(p, E + 1);
+  s.pairs = carve<int32_t>(p, P);
+  s.n_active = carve<int32_t>(p, 1);
+  s.active = carve<int32_t>(p, E);
+  s.tok_order = carve<int32_t>(p, P);
+  s.xh = carve<uint32_t>(p, T * H / 4);
+  s.xl = carve<uint32_t>(p, T * H / 4);
+  s.xs = carve<float>(p, T * H / 16);
+  s.xa = carve<int32_t>(p, T * H / 16);
+  s.ah = carve<uint32_t>(p, P * F / 4);
+  s.al = carve<uint32_t>(p, P * F / 4);
+  s.as = carve<float>(p, P * F / 16);
+  s.aa = carve<int32_t>(p, P * F / 16);
+  s.ash = carve<float>(p, T * (size_t)(c.shared_ffn ? c.shared_ffn : 1));
+  s.xbuf[0] = carve<float>(p, T * H);
+  s.xbuf[1] = carve<float>(p, T * H);
+}
+
+void free_all(qs_moe* h) {
+  for (auto& L : h->layers)
+    if (L.base) (void)hipFree(L.base);
+  if (h->s.base) (void)hipFree(h->s.base);
+  if (h->cbtab) (void)hipFree(h->cbtab);
+  if (h->staging) (void)hipFree(h->staging);
+}
+
+int check_layer_range(const qs_moe* h, int layer0, int n) {
+  if (layer0 < 0 || n < 1 || layer0 + n > h->cfg.n_layers) return QS_E_INVAL;
+  for (int l = layer0; l < layer0 + n; ++l)
+    if (!h->layers[l].uploaded) return QS_E_STATE;
+  return QS_OK;
+}
+
+// Router, top-k and grouping of one layer.
+int launch_route(qs_moe* h, const LayerDev& L, const float* x, int T, int32_t* ids_out,
+                 float* w_out, hipStream_t st) {
+  const qs_moe_config& c = h->cfg;
+  const int E = c.n_experts, k = c.top_k, H = c.hidden;
+  Scratch& s = h->s;
+  hipLaunchKernelGGL(k_router, dim3((E + 3) / 4), dim3(256), 0, st, L.router, L.bias, x, T, H, E,
+                     s.logits);
+  hipLaunchKernelGGL(k_topk, dim3(T), dim3(64), 0, st, (const double*)s.logits, E, k, s.ids, s.wts,
+                     ids_out, w_out);
+  GroupOut g{s.cnt, s.off, s.pairs, s.n_active, s.active, s.tok_order};
+  hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, st, (const int32_t*)s.ids, T, k, E, g);
+  return hipGetLastError() == hipSuccess ? QS_OK : QS_E_HIP;
+}
+
+int launch_layer(qs_moe* h, const LayerDev& L, const float* x, float* y, int T, bool residual,
+                 int32_t* ids_out, float* w_out, hipStream_t st) {
+  const qs_moe_config& c = h->cfg;
+  const int E = c.n_experts, k = c.top_k, H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn;
+  Scratch& s = h->s;
+  int rc = launch_route(h, L, x, T, ids_out, w_out, st);
+  if (rc) return rc;
+  const bool gq2k = c.gate_up_format == QS_FMT_Q2K;
+  if (gq2k)
+    hipLaunchKernelGGL(k_quant_x<true>, dim3(T), dim3(256), 0, st, x, H, s.xh, s.xl, s.xs, s.xa);
+  else
+    hipLaunchKernelGGL(k_quant_x<false>, dim3(T), dim3(256), 0, st, x, H, s.xh, s.xl, s.xs, s.xa);
+
+  GateUpArgs ga{};
+  ga.gate = L.gate;
+  ga.up = L.up;
+  ga.mat_stride = h->gu_stride;
+  ga.cbtab = h->cbtab;
+  ga.H = H; ga.F = F; ga.k = k; ga.T = T;
+  ga.xh = s.xh; ga.xl = s.xl; ga.xs = s.xs; ga.xa = s.xa;
+  ga.pairs = s.pairs; ga.off = s.off; ga.active = s.active; ga.n_active = s.n_active;
+  ga.ah = s.ah; ga.al = s.al; ga.as = s.as; ga.aa = s.aa;
+  ga.sg = L.sg; ga.su = L.su; ga.x = x; ga.ash = s.ash; ga.Fs = Fs;
+  ga.n_shared_items = Fs ? (Fs + kSharedRows - 1) / kSharedRows : 0;
+  const int maxU = E < T * k ? E : T * k;
+  const int n_items = ga.n_shared_items + maxU * (F / kGateTile);
+  if (gq2k)
+    hipLaunchKernelGGL(k_gateup<1>, dim3(n_items), dim3(256), 0, st, ga);
+  else
+    hipLaunchKernelGGL(k_gateup<2>, dim3(n_items), dim3(256), 0, st, ga);
+
+  DownArgs da{};
+  da.down = L.down;
+  da.mat_stride = h->dn_stride;
+  da.H = H; da.F = F; da.k = k; da.T = T; da.E = E;
+  da.ah = s.ah; da.al = s.al; da.as = s.as; da.aa = s.aa;
+  da.pairs = s.pairs; da.off = s.off; da.active = s.active; da.n_active = s.n_active;
+  da.tok_order = s.tok_order; da.wts = s.wts;
+  da.sd = L.sd; da.ash = s.ash; da.Fs = Fs;
+  da.xres = residual ? x : nullptr;
+  da.y = y;
+  const size_t lds = (size_t)T * k * kDownRows * sizeof(float);
+  hipLaunchKernelGGL(k_down, dim3(H / kDownRows), dim3(256), lds, st, da);
+  return hipGetLastError() == hipSuccess ? QS_OK : QS_E_HIP;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+QS_API const char* qs_moe_status_string(int status) {
+  switch (status) {
+    case QS_OK: return "ok";
+    case QS_E_INVAL: return "invalid argument";
+    case QS_E_NOMEM: return "out of memory";
+    case QS_E_HIP: return "HIP runtime error";
+    case QS_E_STATE: return "layer not uploaded";
+    case QS_E_UNSUPPORTED: return "unsupported configuration";
+    default: return "unknown status";
+  }
+}
+
+QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_moe** out) {
+  if (!out) return QS_E_INVAL;
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  const bool need_cb = cfg->gate_up_format == QS_FMT_CB2 || cfg->down_format == QS_FMT_CB2;
+  if (need_cb && !codebook) return QS_E_INVAL;
+
+  qs_moe* h = new (std::nothrow) qs_moe();
+  if (!h) return QS_E_NOMEM;
+  h->cfg = *cfg;
+  DeviceGuard dg(cfg->device);
+  if (!dg.ok) {
+    delete h;
+    return QS_E_HIP;
+  }
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return QS_E_HIP;
+  }
+  const qs_moe_config& c = h->cfg;
+  const size_t E = c.n_experts, H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn;
+  const size_t gu_blk = F * (H / kBlockW), dn_blk = H * (F / kBlockW);
+  h->gu_stride = align_up(gu_blk * gate_up_block_bytes(c), 256);
+  h->dn_stride = align_up(dn_blk * kQ2KBytes, 256);
+  size_t lb = 0;
+  lb += align_up(E * H * 4, 256) + align_up(E * 4, 256);
+  lb += 2 * E * h->gu_stride + E * h->dn_stride;
+  lb += 3 * align_up(Fs * H * 2, 256);
+  h->layer_bytes = lb;
+  h->layers.resize(c.n_layers);
+  rc = QS_OK;
+  for (int l = 0; l < c.n_layers && rc == QS_OK; ++l) {
+    LayerDev& L = h->layers[l];
+    if (hipMalloc(&L.base, lb) != hipSuccess) {
+      L.base = nullptr;
+      rc = QS_E_NOMEM;
+      break;
+    }
+    uint8_t* p = L.base;
+    L.router = carve<float>(p, E * H);
+    L.bias = carve<float>(p, E);
+    L.gate = p; p += E * h->gu_stride;
+    L.up = p; p += E * h->gu_stride;
+    L.down = p; p += E * h->dn_stride;
+    if (Fs) {
+      L.sg = carve<uint16_t>(p, Fs * H);
+      L.su = carve<uint16_t>(p, Fs * H);
+      L.sd = carve<uint16_t>(p, Fs * H);
+    }
+    h->total_bytes += lb;
+  }
+  if (rc == QS_OK) {
+    h->s.bytes = scratch_bytes(c);
+    if (hipMalloc(&h->s.base, h->s.bytes) != hipSuccess) {
+      h->s.base = nullptr;
+      rc = QS_E_NOMEM;
+    } else {
+      carve_scratch(c, h->s);
+      h->total_bytes += h->s.bytes;
+    }
+  }
+  if (rc == QS_OK) {
+    std::vector<uint32_t> tab;
+    std::vector<int8_t> ones(256 * 8, 1);
+    build_cb_tables(codebook ? codebook : ones.data(), tab);
+    if (hipMalloc(&h->cbtab, tab.size() * 4) != hipSuccess) {
+      h->cbtab = nullptr;
+      rc = QS_E_NOMEM;
+    } else if (hipMemcpy(h->cbtab, tab.data(), tab.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+      rc = QS_E_HIP;
+    } else {
+      h->total_bytes += tab.size() * 4;
+    }
+  }
+  if (rc != QS_OK) {
+    free_all(h);
+    delete h;
+    return rc;
+  }
+  *out = h;
+  return QS_OK;
+}
+
+QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, void* hip_stream) {
+  if (!h || !w) return QS_E_INVAL;
+  const qs_moe_config& c = h->cfg;
+  if (layer < 0 || layer >= c.n_layers) return QS_E_INVAL;
+  if (!w->router || !w->gate || !w->up || !w->down) return QS_E_INVAL;
+  if (c.shared_ffn && (!w->shared_gate || !w->shared_up || !w->shared_down)) return QS_E_INVAL;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const size_t E = c.n_experts, H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn;
+  LayerDev& L = h->layers[layer];
+  L.uploaded = false;
+  QS_HIP(hipMemcpyAsync(L.router, w->router, E * H * 4, hipMemcpyDefault, st));
+  if (w->router_bias)
+    QS_HIP(hipMemcpyAsync(L.bias, w->router_bias, E * 4, hipMemcpyDefault, st));
+  else
+    QS_HIP(hipMemsetAsync(L.bias, 0, E * 4, st));
+  if (Fs) {
+    QS_HIP(hipMemcpyAsync(L.sg, w->shared_gate, Fs * H * 2, hipMemcpyDefault, st));
+    QS_HIP(hipMemcpyAsync(L.su, w->shared_up, Fs * H * 2, hipMemcpyDefault, st));
+    QS_HIP(hipMemcpyAsync(L.sd, w->shared_down, Fs * H * 2, hipMemcpyDefault, st));
+  }
+  const size_t gu_blk = F * (H / kBlockW), dn_blk = H * (F / kBlockW);
+  const size_t gbb = gate_up_block_bytes(c);
+  const size_t need = std::max(E * gu_blk * gbb, E * dn_blk * (size_t)kQ2KBytes);
+  if (h->staging_bytes < need) {
+    if (h->staging) QS_HIP(hipFree(h->staging));
+    h->staging = nullptr;
+    h->staging_bytes = 0;
+    if (hipMalloc(&h->staging, need) != hipSuccess) {
+      h->staging = nullptr;
+      return QS_E_NOMEM;
+    }
+    h->staging_bytes = need;
+  }
+  struct Job { const void* src; uint8_t* dst; size_t nblk; size_t stride; bool cb2; };
+  const Job jobs[3] = {
+      {w->gate, L.gate, gu_blk, h->gu_stride, c.gate_up_format == QS_FMT_CB2},
+      {w->up, L.up, gu_blk, h->gu_stride, c.gate_up_format == QS_FMT_CB2},
+      {w->down, L.down, dn_blk, h->dn_stride, false},
+  };
+  for (const Job& j : jobs) {
+    const size_t bytes = E * j.nblk * (j.cb2 ? kCB2Bytes : kQ2KBytes);
+    QS_HIP(hipMemcpyAsync(h->staging, j.src, bytes, hipMemcpyDefault, st));
+    const size_t total = E * j.nblk;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (j.cb2)
+      hipLaunchKernelGGL(k_repack_cb2, grid, dim3(256), 0, st, (const uint8_t*)h->staging, j.dst,
+                         j.nblk, j.stride, E);
+    else
+      hipLaunchKernelGGL(k_repack_q2k, grid, dim3(256), 0, st, (const uint8_t*)h->staging, j.dst,
+                         j.nblk, j.stride, E);
+    QS_HIP(hipGetLastError());
+  }
+  QS_HIP(hipStreamSynchronize(st));
+  L.uploaded = true;
+  return QS_OK;
+}
+
+QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, float* y, int n_tokens,
+                  uint32_t flags, int32_t* ids_out, float* w_out, void* hip_stream) {
+  if (!h || !x || !y) return QS_E_INVAL;
+  const qs_moe_config& c = h->cfg;
+  if (flags & ~QS_DECODE_RESIDUAL) return QS_E_INVAL;
+  if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
+  if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
+  const bool residual = flags & QS_DECODE_RESIDUAL;
+  if (!residual && n_layers != 1) return QS_E_INVAL;
+  const size_t act_bytes = (size_t)n_tokens * c.hidden * sizeof(float);
+  if (!residual && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
+  if (residual && x != y && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
+  int rc = check_layer_range(h, layer0, n_layers);
+  if (rc) return rc;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const size_t per = (size_t)n_tokens * c.top_k;
+  const float* cur = x;
+  for (int i = 0; i < n_layers; ++i) {
+    const bool last = i == n_layers - 1;
+    float* dst = last ? y : h->s.xbuf[i & 1];
+    rc = launch_layer(h, h->layers[layer0 + i], cur, dst, n_tokens, residual,
+                      ids_out ? ids_out + i * per : nullptr, w_out ? w_out + i * per : nullptr, st);
+    if (rc) return rc;
+    cur = dst;
+  }
+  return QS_OK;
+}
+
+QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, double* logits_out,
+                 int32_t* ids_out, float* w_out, int32_t* group_out, void* hip_stream) {
+  if (!h || !x) return QS_E_INVAL;
+  const qs_moe_config& c = h->cfg;
+  if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
+  if ((uintptr_t)x & 15) return QS_E_INVAL;
+  int rc = check_layer_range(h, layer, 1);
+  if (rc) return rc;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
+  hipStream_t st = (hipStream_t)hip_stream;
+  rc = launch_route(h, h->layers[layer], x, n_tokens, ids_out, w_out, st);
+  if (rc) return rc;
+  const size_t E = c.n_experts, P = (size_t)n_tokens * c.top_k;
+  Scratch& s = h->s;
+  if (logits_out)
+    QS_HIP(hipMemcpyAsync(logits_out, s.logits, n_tokens * E * 8, hipMemcpyDeviceToDevice, st));
+  if (group_out) {
+    QS_HIP(hipMemcpyAsync(group_out, s.cnt, E * 4, hipMemcpyDeviceToDevice, st));
+    QS_HIP(hipMemcpyAsync(group_out + E, s.off, (E + 1) * 4, hipMemcpyDeviceToDevice, st));
+    QS_HIP(hipMemcpyAsync(group_out + 2 * E + 1, s.pairs, P * 4, hipMemcpyDeviceToDevice, st));
+    QS_HIP(hipMemcpyAsync(group_out + 2 * E + 1 + P, s.n_active, 4, hipMemcpyDeviceToDevice, st));
+    QS_HIP(hipMemcpyAsync(group_out + 2 * E + 2 + P, s.active, E * 4, hipMemcpyDeviceToDevice, st));
+  }
+  return QS_OK;
+}
+
+QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* out, void* hip_stream) {
+  if (!h || !out) return QS_E_INVAL;
+  const qs_moe_config& c = h->cfg;
+  if (expert < 0 || expert >= c.n_experts || which < 0 || which > 2) return QS_E_INVAL;
+  int rc = check_layer_range(h, layer, 1);
+  if (rc) return rc;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const LayerDev& L = h->layers[layer];
+  const size_t H = c.hidden, F = c.expert_ffn;
+  const uint8_t* mat;
+  size_t nblk;
+  bool cb2;
+  if (which < 2) {
+    mat = (which == 0 ? L.gate : L.up) + (size_t)expert * h->gu_stride;
+    nblk = F * (H / kBlockW);
+    cb2 = c.gate_up_format == QS_FMT_CB2;
+  } else {
+    mat = L.down + (size_t)expert * h->dn_stride;
+    nblk = H * (F / kBlockW);
+    cb2 = false;
+  }
+  const dim3 grid((unsigned)((nblk + 255) / 256));
+  if (cb2)
+    hipLaunchKernelGGL(k_dequant_cb2, grid, dim3(256), 0, st, mat, (const uint32_t*)h->cbtab, nblk, out);
+  else
+    hipLaunchKernelGGL(k_dequant_q2k, grid, dim3(256), 0, st, mat, nblk, out);
+  QS_HIP(hipGetLastError());
+  return QS_OK;
+}
+
+QS_API int qs_moe_memory_bytes(const qs_moe* h, uint64_t* bytes) {
+  if (!h || !bytes) return QS_E_INVAL;
+  *bytes = h->total_bytes;
+  return QS_OK;
+}
+
+QS_API int qs_moe_destroy(qs_moe* h) {
+  if (!h) return QS_OK;
+  int rc = QS_OK;
+  {
+    DeviceGuard dg(h->device);
+    if (hipDeviceSynchronize() != hipSuccess) rc = QS_E_HIP;
+    free_all(h);
+  }
+  delete h;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+"""A thin owner of one qs_moe handle: torch tensors in, torch tensors out.
+Marshalling only; all compute is in libqsmoe.so."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import _lib as L
+
+
+class MoE:
+    """qs_moe handle for one model configuration on the current HIP device."""
+
+    def __init__(self, hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format,
+                 down_format, n_layers, max_tokens, codebook=None, mfma_min_tokens=0, device=-1):
+        self.cfg = L.make_config(hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format,
+                                 down_format, n_layers, max_tokens, mfma_min_tokens, device)
+        cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
+        self._cb = cb
+        self.h = L.qs_moe_create(self.cfg, cb)
+
+    @classmethod
+    def for_workload(cls, wl, codebook, n_layers=None, max_tokens=64, **kw):
+        return cls(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ffn, wl.shared_ffn,
+                   wl.gate_up_format, wl.down_format, n_layers or wl.n_layers, max_tokens,
+                   codebook=codebook, **kw)
+
+    # -- lifetime ---------------------------------------------------------
+    def close(self):
+        if getattr(self, "h", None):
+            L.qs_moe_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # -- calls ------------------------------------------------------------
+    def upload(self, layer, lw, stream=None):
+        """Upload a synth.LayerWeights-like object (numpy, host memory)."""
+        c = np.ascontiguousarray
+        L.qs_moe_upload(self.h, layer, c(lw.router), None if lw.router_bias is None else c(lw.router_bias),
+                        c(lw.gate), c(lw.up), c(lw.down),
+                        None if lw.shared_gate is None else c(lw.shared_gate),
+                        None if lw.shared_up is None else c(lw.shared_up),
+                        None if lw.shared_down is None else c(lw.shared_down), stream)
+
+    def decode(self, x, y=None, layer0=0, n_layers=1, residual=False, ids_out=None, w_out=None,
+               stream=None):
+        import torch
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty_like(x)
+        flags = L.QS_DECODE_RESIDUAL if residual else 0
+        L.qs_moe_decode(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
+        return y
+
+    def route(self, x, layer=0, stream=None):
+        import torch
+        T = x.shape[0]
+        E, k = self.cfg.n_experts, self.cfg.top_k
+        dev = x.device
+        logits = torch.empty((T, E), dtype=torch.float64, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        grp = torch.empty(3 * E + 2 + T * k, dtype=torch.int32, device=dev)
+        L.qs_moe_route(self.h, layer, x, T, logits, ids, w, grp, stream)
+        P = T * k
+        return {
+            "logits": logits, "ids": ids, "w": w,
+            "counts": grp[:E], "offsets": grp[E:2 * E + 1], "pairs": grp[2 * E + 1:2 * E + 1 + P],
+            "n_active": grp[2 * E + 1 + P], "active": grp[2 * E + 2 + P:],
+        }
+
+    def dequant(self, layer, expert, which, stream=None):
+        import torch
+        H, F = self.cfg.hidden, self.cfg.expert_ffn
+        shape = (F, H) if which < 2 else (H, F)
+        out = torch.empty(shape, dtype=torch.float32, device="cuda")
+        L.qs_moe_dequant(self.h, layer, expert, which, out, stream)
+        return out
+
+    def memory_bytes(self):
+        return L.qs_moe_memory_bytes(self.h)

@@ -1,0 +1,228 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: bit-exact dequantised weights, expert ids and grouping; router weights
+within 1e-6; layer outputs within a max relative L2 error of 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe as om
+from tests.gpu_util import TOL_REL_L2, check_layer, make_handle, oracle_layer, say, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny(lib):
+    wl = workload("tiny_q2k")
+    moe, lws = make_handle(lib, wl, max_tokens=64)
+    yield wl, moe, lws
+    moe.close()
+
+
+@pytest.fixture(scope="module")
+def a3b(lib):
+    wl = workload("a3b_layer")
+    moe, lws = make_handle(lib, wl, max_tokens=16)
+    yield wl, moe, lws
+    moe.close()
+
+
+def _equal_fp32(a, b):
+    return bool(np.all(a == b))          # +0 == -0
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_dequant_bit_exact_tiny(tiny, which):
+    wl, moe, lws = tiny
+    for e in (0, 7, wl.n_experts - 1):
+        say(f"dequant tiny expert {e} matrix {which}")
+        got = moe.dequant(0, e, which).cpu().numpy()
+        raw = (lws[0].gate, lws[0].up, lws[0].down)[which][e]
+        fmt = wl.gate_up_format if which < 2 else wl.down_format
+        assert _equal_fp32(got, om.dequant_matrix(raw, fmt, synth.codebook()))
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_dequant_bit_exact_a3b(a3b, which):
+    wl, moe, lws = a3b
+    for e in (0, 128, 255):
+        say(f"dequant a3b expert {e} matrix {which}")
+        got = moe.dequant(0, e, which).cpu().numpy()
+        raw = (lws[0].gate, lws[0].up, lws[0].down)[which][e]
+        fmt = wl.gate_up_format if which < 2 else wl.down_format
+        ref = om.dequant_matrix(raw, fmt, synth.codebook())
+        assert _equal_fp32(got, ref)
+
+
+def _route_check(wl, moe, lw, T, batch=0):
+    x = synth.tokens(wl, T, batch)
+    r = moe.route(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    lg_ref = om.router_logits(x, lw.router, lw.router_bias)
+    ids_ref, w_ref, gap = om.top_k(lg_ref, wl.top_k)
+    cnt, off, pairs, active = om.group_by_expert(ids_ref, wl.n_experts)
+    lg = r["logits"].cpu().numpy()
+    scale = np.abs(x).astype(np.float64) @ np.abs(lw.router.astype(np.float64)).T
+    assert np.all(np.abs(lg - lg_ref) <= 1e-13 * (scale + 1.0)), "logits differ beyond fp64 rounding"
+    assert np.all(gap > 1e-9)
+    assert np.array_equal(r["ids"].cpu().numpy(), ids_ref)
+    assert np.max(np.abs(r["w"].cpu().numpy() - w_ref)) < 1e-6
+    assert np.array_equal(r["counts"].cpu().numpy(), cnt)
+    assert np.array_equal(r["offsets"].cpu().numpy(), off)
+    assert np.array_equal(r["pairs"].cpu().numpy(), pairs)
+    na = int(r["n_active"].item())
+    assert na == len(active)
+    act = r["active"].cpu().numpy()
+    assert np.array_equal(act[:na], active) and np.all(act[na:] == -1)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 64])
+def test_route_tiny(tiny, T):
+    wl, moe, lws = tiny
+    say(f"route tiny T={T}")
+    _route_check(wl, moe, lws[0], T)
+
+
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_route_a3b(a3b, T):
+    wl, moe, lws = a3b
+    say(f"route a3b T={T}")
+    _route_check(wl, moe, lws[0], T)
+
+
+def _decode_check(wl, moe, lw, T, batch=0, label=""):
+    x = synth.tokens(wl, T, batch)
+    xd = torch.from_numpy(x).cuda()
+    ids = torch.empty((T, wl.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, wl.top_k), dtype=torch.float32, device="cuda")
+    y = moe.decode(xd, ids_out=ids, w_out=w)
+    torch.cuda.synchronize()
+    return check_layer(wl, lw, x, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), label=label)
+
+
+@pytest.mark.parametrize("T", [1, 3, 4, 16, 33, 64])
+def test_decode_tiny(tiny, T):
+    wl, moe, lws = tiny
+    say(f"decode tiny T={T}")
+    _decode_check(wl, moe, lws[0], T, label=f"tiny T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 4, 7, 16])
+def test_decode_a3b(a3b, T):
+    wl, moe, lws = a3b
+    say(f"decode a3b T={T}")
+    _decode_check(wl, moe, lws[0], T, label=f"a3b T={T}")
+
+
+@pytest.mark.parametrize("name", ["tiny_q2k", "a3b_layer"])
+def test_batch_invariance_and_determinism(request, name):
+    wl, moe, _ = request.getfixturevalue("tiny" if name == "tiny_q2k" else "a3b")
+    T = 8
+    say(f"batch invariance {name} T={T}")
+    x = torch.from_numpy(synth.tokens(wl, T, 3)).cuda()
+    y = moe.decode(x)
+    y2 = moe.decode(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "two runs differ"
+    for t in (0, 3, T - 1):
+        yt = moe.decode(x[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(yt[0], y[t]), f"token {t} differs between T=1 and T={T}"
+    perm = torch.tensor([5, 2, 7, 0, 1, 6, 4, 3], device="cuda")
+    yp = moe.decode(x[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y[perm]), "permuting tokens does not permute outputs"
+
+
+def test_zero_input_gives_zero(a3b):
+    wl, moe, _ = a3b
+    say("zero input")
+    x = torch.zeros((3, wl.hidden), device="cuda")
+    y = moe.decode(x)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
+
+
+def test_ties_break_to_lower_index(lib):
+    wl = workload("tiny_q2k")
+    cb = synth.codebook()
+    lw = synth.layer_weights(wl, 0)
+    lw.router[9] = lw.router[3]
+    lw.router[12] = lw.router[3]
+    say("ties")
+    with lib.MoE.for_workload(wl, cb, max_tokens=16) as moe:
+        moe.upload(0, lw)
+        x = synth.tokens(wl, 16, 5)
+        r = moe.route(torch.from_numpy(x).cuda())
+        torch.cuda.synchronize()
+        ids_ref, _, _ = om.top_k(om.router_logits(x, lw.router), wl.top_k)
+        assert np.array_equal(r["ids"].cpu().numpy(), ids_ref)
+        lg = r["logits"].cpu().numpy()
+        assert np.array_equal(lg[:, 3], lg[:, 9]) and np.array_equal(lg[:, 3], lg[:, 12])
+
+
+def test_all_experts_selected(lib):
+    """k = E: every expert is used by every token."""
+    wl = synth.Workload("all", 41, 512, 4, 4, 256, 64, "cb2", "q2k", 1, (1,))
+    say("k = E")
+    moe, lws = make_handle(lib, wl, max_tokens=8)
+    with moe:
+        _decode_check(wl, moe, lws[0], 8, label="k=E T=8")
+
+
+def test_max_tokens_edge(lib):
+    """T = max_tokens with T*k at the pair budget (256 tokens x 4 = 1024)."""
+    wl = synth.Workload("maxT", 42, 256, 32, 4, 256, 0, "cb2", "q2k", 1, (1,))
+    say("T = 256, k = 4")
+    moe, lws = make_handle(lib, wl, max_tokens=256)
+    with moe:
+        _decode_check(wl, moe, lws[0], 256, label="T=256 k=4")
+
+
+def test_residual_chain_and_in_place(lib):
+    wl = workload("a3b_stack40_zipf")
+    L = 3
+    say("residual chain 3 layers")
+    moe, lws = make_handle(lib, wl, n_layers=L, max_tokens=8)
+    with moe:
+        x = torch.from_numpy(synth.tokens(wl, 4, 1)).cuda()
+        ids = torch.empty((L, 4, wl.top_k), dtype=torch.int32, device="cuda")
+        y_all = moe.decode(x, n_layers=L, residual=True, ids_out=ids)
+        cur = x
+        for l in range(L):
+            nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True)
+            torch.cuda.synchronize()
+            check_layer(wl, lws[l], cur.cpu().numpy(), nxt.cpu().numpy(), residual=True,
+                        label=f"layer {l} (teacher-forced)")
+            cur = nxt
+        torch.cuda.synchronize()
+        assert torch.equal(y_all, cur), "multi-layer call differs from chained single layers"
+        xin = x.clone()
+        moe.decode(xin, y=xin, n_layers=L, residual=True)
+        torch.cuda.synchronize()
+        assert torch.equal(xin, y_all), "in-place decode differs"
+
+
+def test_error_statuses_with_gpu(lib):
+    wl = workload("tiny_q2k")
+    cb = synth.codebook()
+    say("error statuses")
+    with lib.MoE.for_workload(wl, cb, n_layers=2, max_tokens=4) as moe:
+        moe.upload(0, synth.layer_weights(wl, 0))
+        x = torch.zeros((4, wl.hidden), device="cuda")
+        y = torch.empty_like(x)
+        st = torch.cuda.current_stream().cuda_stream
+        L = lib.LIB
+        assert L.qs_moe_decode(moe.h, 1, 1, x.data_ptr(), y.data_ptr(), 4, 0, None, None, st) == lib.QS_E_STATE
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 5, 0, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 0, 0, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 0, 2, x.data_ptr(), y.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), x.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr() + 4, y.data_ptr(), 2, 0, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 8, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 2, 1, x.data_ptr(), y.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_dequant(moe.h, 0, wl.n_experts, 0, y.data_ptr(), st) == lib.QS_E_INVAL
+        assert L.qs_moe_dequant(moe.h, 0, 0, 3, y.data_ptr(), st) == lib.QS_E_INVAL
+        assert moe.memory_bytes() > 0
