@@ -82,19 +82,19 @@ def main():
         ids = torch.empty((N_BATCHES, L, T, wl.top_k), dtype=torch.int32, device="cuda")
         # untimed pass: the experts each batch selects, for the byte count
         for b in range(N_BATCHES):
-            moe.decode(xs[b], y, n_layers=L, residual=True, ids_out=ids[b])
+            moe.decode(xs[b], y, n_layers=L, residual=True, prenorm=True, ids_out=ids[b])
         torch.cuda.synchronize()
         idn = ids.cpu().numpy()
         uniq = np.array([[len(np.unique(idn[b, l])) for l in range(L)] for b in range(N_BATCHES)])
         bytes_batch = uniq.sum(axis=1) * per_expert + L * fixed_layer + 2 * T * wl.hidden * 4
         for i in range(args.warmup):
-            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True)
+            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True, prenorm=True)
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for i in range(args.steps):
-            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True)
+            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True, prenorm=True)
         end.record(stream)
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / args.steps
@@ -166,7 +166,7 @@ def cpu_baseline(wl, T, L, n_layers_sample):
     t0 = time.perf_counter()
     cur = x
     for layer in layers:
-        cur = om.moe_layer(layer, cur, residual=True)["y"]
+        cur = om.moe_layer(layer, cur, residual=True, prenorm=True)["y"]
     dt = time.perf_counter() - t0
     if limit is not None:
         limit.unregister() if hasattr(limit, "unregister") else None

@@ -76,8 +76,12 @@ typedef enum {
  * the E experts of a layer are consecutive. */
 typedef enum { QS_FMT_Q2K = 1, QS_FMT_CB2 = 2 } qs_format;
 
-/* qs_moe_decode flags */
-#define QS_DECODE_RESIDUAL 1u   /* x_{l+1} = x_l + MoE_l(x_l); y gets the last x */
+/* qs_moe_decode / qs_moe_route flags */
+#define QS_DECODE_RESIDUAL 1u   /* x_{l+1} = x_l + MoE_l(u_l); y gets the last x */
+#define QS_DECODE_RMSNORM  2u   /* u_l = x_l / sqrt(mean(x_l^2) + 1e-6) (an RMSNorm
+                                   without learned weight, as a pre-norm residual
+                                   stream applies before each MoE block); without
+                                   this flag u_l = x_l */
 
 typedef struct qs_moe qs_moe;   /* opaque, owned by the library */
 
@@ -128,14 +132,17 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
 
 /* Decode n_tokens tokens through layers [layer0, layer0 + n_layers).
  * x: device fp32 [n_tokens][H]; y: device fp32 [n_tokens][H].
- * Without QS_DECODE_RESIDUAL: n_layers must be 1 and y = MoE(x); x and y must
- * not overlap.  With it: x_{l+1} = x_l + MoE_l(x_l) layer by layer and y
- * receives the final x; y == x (in place) is allowed.
+ * u_l is x_l, or RMSNorm(x_l) with QS_DECODE_RMSNORM (router and experts both
+ * see u_l).  Without QS_DECODE_RESIDUAL: n_layers must be 1 and y = MoE(u);
+ * x and y must not overlap.  With it: x_{l+1} = x_l + MoE_l(u_l) layer by
+ * layer and y receives the final x; y == x (in place) is allowed.
+ * x and y must be 16-byte aligned.
  * ids_out: device int32 [n_layers][n_tokens][k] or NULL -- selected experts
  * in rank order (logit descending, ties to the lower index).
  * w_out: device fp32 [n_layers][n_tokens][k] or NULL -- their renormalised
  * softmax weights.  Asynchronous on hip_stream; performs no allocation and
- * no host synchronisation.  1 <= n_tokens <= max_tokens. */
+ * no host synchronisation.  1 <= n_tokens <= max_tokens.  Non-finite inputs
+ * give non-finite outputs but never an out-of-range expert id. */
 QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, float* y,
                   int n_tokens, uint32_t flags, int32_t* ids_out, float* w_out,
                   void* hip_stream);
@@ -152,9 +159,11 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
  *      [2E+1, 2E+1+T*k)    pairs token*k + slot, ordered by (expert, token)
  *      [2E+1+T*k]          number of experts with a non-empty bucket, U
  *      [2E+2+T*k, 3E+2+T*k) those experts ascending (entries >= U are -1)
+ * flags: 0 or QS_DECODE_RMSNORM (routes u = RMSNorm(x) as qs_moe_decode does).
  * Asynchronous on hip_stream. */
-QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, double* logits_out,
-                 int32_t* ids_out, float* w_out, int32_t* group_out, void* hip_stream);
+QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, uint32_t flags,
+                 double* logits_out, int32_t* ids_out, float* w_out, int32_t* group_out,
+                 void* hip_stream);
 
 /* Dequantise one routed matrix from the handle's device copy with the same
  * field decoding the GEMV kernels use (tests).  which: 0 gate, 1 up, 2 down.

@@ -234,41 +234,64 @@ class Layer:
         return self._cache["shared"]
 
 
-def moe_layer(layer: Layer, x: np.ndarray, residual: bool = False):
+RMS_EPS = 1e-6
+
+
+def rms_inv(x: np.ndarray) -> np.ndarray:
+    """Per row 1 / sqrt(mean(x^2) + eps) in fp64: the scale of an RMSNorm
+    without learned weight, as the pre-norm residual stream of the pages'
+    model families applies before each MoE block (norm layers are kept at
+    f32 in the Quasar README, "Design decisions")."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / np.sqrt(np.mean(x * x, axis=-1) + RMS_EPS)
+
+
+def moe_layer(layer: Layer, x: np.ndarray, residual: bool = False, prenorm: bool = False):
     """One decode step of one MoE layer for T tokens.
 
-    y[t] = sum_{j<k} w[t][j] * FFN_{ids[t][j]}(x[t]) + S(x[t])  (+ x[t] if
-    residual), with S the ungated shared expert (weight 1) when present.
+    With u = x (or u = x * rms_inv(x) if prenorm):
+    y[t] = sum_{j<k} w[t][j] * FFN_{ids[t][j]}(u[t]) + S(u[t])  (+ x[t] if
+    residual), with S the ungated shared expert (weight 1) when present and
+    the router evaluated on u.
     Returns a dict with y (fp32 [T][H]), ids, w (fp64), logits, gap.
     """
     wl, lw = layer.wl, layer.lw
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
-    logits = router_logits(x, lw.router, lw.router_bias)
+    if prenorm:
+        r = rms_inv(x)
+        logits = router_logits(x, lw.router) * r[:, None]
+        if lw.router_bias is not None:
+            logits = logits + np.asarray(lw.router_bias, dtype=np.float64)[None, :]
+        u = x.astype(np.float64) * r[:, None]
+    else:
+        logits = router_logits(x, lw.router, lw.router_bias)
+        u = x.astype(np.float64)
     ids, wts, gap = top_k(logits, wl.top_k)
     y = np.zeros((T, wl.hidden), dtype=np.float64)
     for t in range(T):
         for j in range(wl.top_k):
             wg, wu, wd = layer.expert(int(ids[t, j]))
-            _, o = swiglu_ffn(x[t], wg, wu, wd)
+            _, o = swiglu_ffn(u[t], wg, wu, wd)
             y[t] += wts[t, j] * o
         if wl.shared_ffn:
             sg, su, sd = layer.shared()
-            _, s = swiglu_ffn(x[t], sg, su, sd)
+            _, s = swiglu_ffn(u[t], sg, su, sd)
             y[t] += s
         if residual:
             y[t] += x[t].astype(np.float64)
     return {"y": y.astype(np.float32), "ids": ids, "w": wts, "logits": logits, "gap": gap}
 
 
-def moe_stack(layers, x: np.ndarray):
-    """Stacked layers chained by the residual: x_{l+1} = x_l + MoE_l(x_l),
-    each layer's output rounded to fp32.  Returns the final x and the per-layer
-    results."""
+def moe_stack(layers, x: np.ndarray, prenorm: bool = True):
+    """Stacked layers chained by the residual stream:
+    x_{l+1} = x_l + MoE_l(RMSNorm(x_l)) (pre-norm; without the norm an
+    un-normalised SwiGLU chain grows without bound), each layer's output
+    rounded to fp32.  Returns the final x and the per-layer results."""
     outs = []
     cur = np.asarray(x, dtype=np.float32)
     for layer in layers:
-        r = moe_layer(layer, cur, residual=True)
+        r = moe_layer(layer, cur, residual=True, prenorm=prenorm)
         outs.append(r)
         cur = r["y"]
     return cur, outs

@@ -14,6 +14,7 @@ QS_MOE_ABI_VERSION = 1
 QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 QS_FMT_Q2K, QS_FMT_CB2 = 1, 2
 QS_DECODE_RESIDUAL = 1
+QS_DECODE_RMSNORM = 2
 
 FORMATS = {"q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2}
 
@@ -42,6 +43,14 @@ class QsError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own libamdhip64 (same soname, different file name).  Load
+    # it before libqsmoe.so so that the library binds to that one runtime;
+    # loading libqsmoe.so first would bring in a second HIP runtime when torch
+    # is imported later, and the two cannot share the device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
@@ -51,7 +60,7 @@ def _load() -> ctypes.CDLL:
         "qs_moe_create": [ctypes.POINTER(QsMoeConfig), vp, ctypes.POINTER(vp)],
         "qs_moe_upload": [vp, i32, ctypes.POINTER(QsMoeLayerWeights), vp],
         "qs_moe_decode": [vp, i32, i32, vp, vp, i32, u32, vp, vp, vp],
-        "qs_moe_route": [vp, i32, vp, i32, vp, vp, vp, vp, vp],
+        "qs_moe_route": [vp, i32, vp, i32, u32, vp, vp, vp, vp, vp],
         "qs_moe_dequant": [vp, i32, i32, i32, vp, vp],
         "qs_moe_memory_bytes": [vp, ctypes.POINTER(ctypes.c_uint64)],
         "qs_moe_destroy": [vp],
@@ -128,9 +137,9 @@ def qs_moe_decode(h: int, layer0: int, n_layers: int, x, y, n_tokens: int, flags
                                              flags, _ptr(ids_out), _ptr(w_out), _stream(stream)))
 
 
-def qs_moe_route(h: int, layer: int, x, n_tokens: int, logits_out=None, ids_out=None,
-                 w_out=None, group_out=None, stream=None) -> None:
-    check("qs_moe_route", LIB.qs_moe_route(h, layer, _ptr(x), n_tokens, _ptr(logits_out),
+def qs_moe_route(h: int, layer: int, x, n_tokens: int, flags: int = 0, logits_out=None,
+                 ids_out=None, w_out=None, group_out=None, stream=None) -> None:
+    check("qs_moe_route", LIB.qs_moe_route(h, layer, _ptr(x), n_tokens, flags, _ptr(logits_out),
                                            _ptr(ids_out), _ptr(w_out), _ptr(group_out),
                                            _stream(stream)))
 

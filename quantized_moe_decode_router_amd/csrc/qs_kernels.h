@@ -94,6 +94,10 @@ __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
+// Expert ids come from k_topk and are always in range; the clamp keeps every
+// index derived from them inside its buffer whatever the input data.
+__device__ __forceinline__ int valid_id(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
+
 // --------------------------------------------- codebook 2-bit decoding ---
 // Two LDS tables of signed int8 quads built from the codebook:
 //   tab[idx*16 + s]           weights 0..3 of a group with row idx, sign nibble s
@@ -232,10 +236,15 @@ __global__ void k_dequant_q2k(const uint8_t* __restrict__ mat, size_t nblk, floa
 }
 
 // ----------------------------------------------------------- router ---
+constexpr double kRmsEps = 1e-6;
+
 // One wave per expert row; fp64 accumulation of exact fp32 x fp32 products.
+// With prenorm the logit is (Wr x) * r + b, r = 1/sqrt(mean(x^2) + eps) in
+// fp64 (the router is linear, so this is Wr applied to RMSNorm(x)); every
+// wave computes r in the same order and the wave of expert 0 stores it.
 __global__ void k_router(const float* __restrict__ wr, const float* __restrict__ bias,
-                         const float* __restrict__ x, int T, int H, int E,
-                         double* __restrict__ logits) {
+                         const float* __restrict__ x, int T, int H, int E, int prenorm,
+                         double* __restrict__ logits, double* __restrict__ rinv) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * (blockDim.x >> 6) + wave;
   if (e >= E) return;
@@ -243,16 +252,27 @@ __global__ void k_router(const float* __restrict__ wr, const float* __restrict__
   const double b = (double)bias[e];
   for (int t = 0; t < T; ++t) {
     const float4* xt = (const float4*)(x + (size_t)t * H);
-    double acc = 0.0;
+    double acc = 0.0, ss = 0.0;
     for (int i = lane; i < H / 4; i += 64) {
       const float4 a = row[i], v = xt[i];
       acc = fma((double)a.x, (double)v.x, acc);
       acc = fma((double)a.y, (double)v.y, acc);
       acc = fma((double)a.z, (double)v.z, acc);
       acc = fma((double)a.w, (double)v.w, acc);
+      if (prenorm) {
+        ss = fma((double)v.x, (double)v.x, ss);
+        ss = fma((double)v.y, (double)v.y, ss);
+        ss = fma((double)v.z, (double)v.z, ss);
+        ss = fma((double)v.w, (double)v.w, ss);
+      }
     }
     acc = wave_sum_f64(acc);
-    if (lane == 0) logits[(size_t)t * E + e] = acc + b;
+    double r = 1.0;
+    if (prenorm) r = 1.0 / sqrt(wave_sum_f64(ss) / (double)H + kRmsEps);
+    if (lane == 0) {
+      logits[(size_t)t * E + e] = prenorm ? fma(acc, r, b) : acc + b;
+      if (e == 0) rinv[t] = r;
+    }
   }
 }
 
@@ -268,7 +288,8 @@ __global__ void k_topk(const double* __restrict__ logits, int E, int k, int32_t*
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? logits[(size_t)t * E + e] : 0.0;
+    const double l = e < E ? logits[(size_t)t * E + e] : 0.0;
+    v[i] = l != l ? -INFINITY : l;   // NaN ranks last, so every pick is a valid, distinct expert
   }
   uint32_t taken = 0;
   for (int j = 0; j < k; ++j) {
@@ -278,6 +299,7 @@ __global__ void k_topk(const double* __restrict__ logits, int E, int k, int32_t*
     for (int i = 0; i < 16; ++i) {
       const int e = lane + 64 * i;
       if (e < E && !((taken >> i) & 1u) && (bi == 0x7FFFFFFF || v[i] > bv)) {
+        // first untaken candidate, then strictly larger ones (lower index wins ties)
         bv = v[i];
         bi = e;
       }
@@ -339,7 +361,7 @@ __global__ void k_group(const int32_t* __restrict__ ids, int T, int k, int E, Gr
   for (int i = tid; i < E * 8; i += nt) mask[i] = 0;
   __syncthreads();
   for (int p = tid; p < P; p += nt) {
-    const int e = ids[p], t = p / k;
+    const int e = valid_id(ids[p], E), t = p / k;
     atomicAdd(&cnt[e], 1);
     atomicOr(&mask[e * 8 + (t >> 5)], 1u << (t & 31));
   }
@@ -363,7 +385,7 @@ __global__ void k_group(const int32_t* __restrict__ ids, int T, int k, int E, Gr
   }
   if (tid == 0) g.off[E] = off[E];
   for (int p = tid; p < P; p += nt) {
-    const int e = ids[p], t = p / k;
+    const int e = valid_id(ids[p], E), t = p / k;
     int rank = 0;
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(mask[e * 8 + w]);
     rank += __popc(mask[e * 8 + (t >> 5)] & ((1u << (t & 31)) - 1u));
@@ -373,7 +395,7 @@ __global__ void k_group(const int32_t* __restrict__ ids, int T, int k, int E, Gr
     // the token's k (expert, bucket position) sorted by expert id
     int ee[16], pp[16];
     for (int j = 0; j < k; ++j) {
-      const int e = ids[t * k + j];
+      const int e = valid_id(ids[t * k + j], E);
       int rank = 0;
       for (int w = 0; w < (t >> 5); ++w) rank += __popc(mask[e * 8 + w]);
       rank += __popc(mask[e * 8 + (t >> 5)] & ((1u << (t & 31)) - 1u));
@@ -395,11 +417,12 @@ __global__ void k_group(const int32_t* __restrict__ ids, int T, int k, int E, Gr
 // shared exponent.  Writes limbs packed for the gate/up format, the per-16
 // scale 2^(e-14) and (Q2_K consumers) the per-16 sums of the fixed values.
 template <bool Q2K>
-__global__ void k_quant_x(const float* __restrict__ x, int H, uint32_t* __restrict__ xh,
-                          uint32_t* __restrict__ xl, float* __restrict__ xs,
-                          int32_t* __restrict__ xa) {
+__global__ void k_quant_x(const float* __restrict__ x, int H, const double* __restrict__ rinv,
+                          uint32_t* __restrict__ xh, uint32_t* __restrict__ xl,
+                          float* __restrict__ xs, int32_t* __restrict__ xa) {
   const int t = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nblk = H / kBlockW;
+  const float r = (float)rinv[t];          // 1, or the RMSNorm scale folded into x's scales
   for (int b = wave; b < nblk; b += blockDim.x >> 6) {
     const float4 v = *(const float4*)(x + (size_t)t * H + b * kBlockW + 4 * lane);
     const int e = fixed_exp(wave_max_abs(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)))));
@@ -431,7 +454,7 @@ __global__ void k_quant_x(const float* __restrict__ x, int H, uint32_t* __restri
     s += __shfl_xor(s, 2, 64);
     if ((lane & 3) == 0) {
       const size_t si = (size_t)t * (H / kSubW) + b * 16 + (lane >> 2);
-      xs[si] = ldexpf(1.0f, e - kFixedBits);
+      xs[si] = ldexpf(r, e - kFixedBits);
       if (Q2K) xa[si] = s;
     }
   }
@@ -460,6 +483,7 @@ struct GateUpArgs {
   const uint16_t* sg;        // bf16 [Fs][H]
   const uint16_t* su;
   const float* x;            // fp32 [T][H]
+  const double* rinv;        // [T] input scale (RMSNorm or 1)
   float* ash;                // fp32 [T][Fs]
   int Fs;
   int n_shared_items;
@@ -491,8 +515,9 @@ __device__ void shared_gateup_item(const GateUpArgs& a, int item) {
         u = fmaf(bf16_to_f32(uw[c] >> 16), xv[2 * c + 1], u);
       }
     }
-    g = group_sum<64>(g);
-    u = group_sum<64>(u);
+    const float r = (float)a.rinv[t];
+    g = group_sum<64>(g) * r;
+    u = group_sum<64>(u) * r;
     if (lane == 0) a.ash[(size_t)t * a.Fs + f] = silu_mul(g, u);
   }
 }

@@ -58,6 +58,7 @@ struct Scratch {
   int32_t* aa;
   float* ash;
   float* xbuf[2];
+  double* rinv;
 };
 
 }  // namespace
@@ -98,6 +99,12 @@ struct DeviceGuard {
       return QS_E_HIP;                                                    \
     }                                                                     \
   } while (0)
+
+bool hip_ok(hipError_t e, const char* what) {
+  if (e == hipSuccess) return true;
+  fprintf(stderr, "qs_moe: %s failed: %s\n", what, hipGetErrorString(e));
+  return false;
+}
 
 size_t gate_up_block_bytes(const qs_moe_config& c) {
   return c.gate_up_format == QS_FMT_CB2 ? kCB2Bytes : kQ2KBytes;
@@ -161,6 +168,7 @@ size_t scratch_bytes(const qs_moe_config& c) {
   add(P * (F / 16) * 4); add(P * (F / 16) * 4);
   add(T * (size_t)(c.shared_ffn ? c.shared_ffn : 1) * 4);
   add(T * H * 4); add(T * H * 4); // residual ping-pong
+  add(T * 8);                     // rinv
   return b;
 }
 
@@ -188,6 +196,7 @@ void carve_scratch(const qs_moe_config& c, Scratch& s) {
   s.ash = carve<float>(p, T * (size_t)(c.shared_ffn ? c.shared_ffn : 1));
   s.xbuf[0] = carve<float>(p, T * H);
   s.xbuf[1] = carve<float>(p, T * H);
+  s.rinv = carve<double>(p, T);
 }
 
 void free_all(qs_moe* h) {
@@ -206,13 +215,13 @@ int check_layer_range(const qs_moe* h, int layer0, int n) {
 }
 
 // Router, top-k and grouping of one layer.
-int launch_route(qs_moe* h, const LayerDev& L, const float* x, int T, int32_t* ids_out,
-                 float* w_out, hipStream_t st) {
+int launch_route(qs_moe* h, const LayerDev& L, const float* x, int T, bool prenorm,
+                 int32_t* ids_out, float* w_out, hipStream_t st) {
   const qs_moe_config& c = h->cfg;
   const int E = c.n_experts, k = c.top_k, H = c.hidden;
   Scratch& s = h->s;
   hipLaunchKernelGGL(k_router, dim3((E + 3) / 4), dim3(256), 0, st, L.router, L.bias, x, T, H, E,
-                     s.logits);
+                     (int)prenorm, s.logits, s.rinv);
   hipLaunchKernelGGL(k_topk, dim3(T), dim3(64), 0, st, (const double*)s.logits, E, k, s.ids, s.wts,
                      ids_out, w_out);
   GroupOut g{s.cnt, s.off, s.pairs, s.n_active, s.active, s.tok_order};
@@ -221,17 +230,19 @@ int launch_route(qs_moe* h, const LayerDev& L, const float* x, int T, int32_t* i
 }
 
 int launch_layer(qs_moe* h, const LayerDev& L, const float* x, float* y, int T, bool residual,
-                 int32_t* ids_out, float* w_out, hipStream_t st) {
+                 bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
   const qs_moe_config& c = h->cfg;
   const int E = c.n_experts, k = c.top_k, H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn;
   Scratch& s = h->s;
-  int rc = launch_route(h, L, x, T, ids_out, w_out, st);
+  int rc = launch_route(h, L, x, T, prenorm, ids_out, w_out, st);
   if (rc) return rc;
   const bool gq2k = c.gate_up_format == QS_FMT_Q2K;
   if (gq2k)
-    hipLaunchKernelGGL(k_quant_x<true>, dim3(T), dim3(256), 0, st, x, H, s.xh, s.xl, s.xs, s.xa);
+    hipLaunchKernelGGL(k_quant_x<true>, dim3(T), dim3(256), 0, st, x, H, (const double*)s.rinv,
+                       s.xh, s.xl, s.xs, s.xa);
   else
-    hipLaunchKernelGGL(k_quant_x<false>, dim3(T), dim3(256), 0, st, x, H, s.xh, s.xl, s.xs, s.xa);
+    hipLaunchKernelGGL(k_quant_x<false>, dim3(T), dim3(256), 0, st, x, H, (const double*)s.rinv,
+                       s.xh, s.xl, s.xs, s.xa);
 
   GateUpArgs ga{};
   ga.gate = L.gate;
@@ -242,7 +253,7 @@ int launch_layer(qs_moe* h, const LayerDev& L, const float* x, float* y, int T, 
   ga.xh = s.xh; ga.xl = s.xl; ga.xs = s.xs; ga.xa = s.xa;
   ga.pairs = s.pairs; ga.off = s.off; ga.active = s.active; ga.n_active = s.n_active;
   ga.ah = s.ah; ga.al = s.al; ga.as = s.as; ga.aa = s.aa;
-  ga.sg = L.sg; ga.su = L.su; ga.x = x; ga.ash = s.ash; ga.Fs = Fs;
+  ga.sg = L.sg; ga.su = L.su; ga.x = x; ga.rinv = s.rinv; ga.ash = s.ash; ga.Fs = Fs;
   ga.n_shared_items = Fs ? (Fs + kSharedRows - 1) / kSharedRows : 0;
   const int maxU = E < T * k ? E : T * k;
   const int n_items = ga.n_shared_items + maxU * (F / kGateTile);
@@ -300,10 +311,11 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   h->cfg = *cfg;
   DeviceGuard dg(cfg->device);
   if (!dg.ok) {
+    fprintf(stderr, "qs_moe: hipSetDevice(%d) failed\n", cfg->device);
     delete h;
     return QS_E_HIP;
   }
-  if (hipGetDevice(&h->device) != hipSuccess) {
+  if (!hip_ok(hipGetDevice(&h->device), "hipGetDevice")) {
     delete h;
     return QS_E_HIP;
   }
@@ -321,7 +333,7 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   rc = QS_OK;
   for (int l = 0; l < c.n_layers && rc == QS_OK; ++l) {
     LayerDev& L = h->layers[l];
-    if (hipMalloc(&L.base, lb) != hipSuccess) {
+    if (!hip_ok(hipMalloc(&L.base, lb), "hipMalloc(layer)")) {
       L.base = nullptr;
       rc = QS_E_NOMEM;
       break;
@@ -341,7 +353,7 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   }
   if (rc == QS_OK) {
     h->s.bytes = scratch_bytes(c);
-    if (hipMalloc(&h->s.base, h->s.bytes) != hipSuccess) {
+    if (!hip_ok(hipMalloc(&h->s.base, h->s.bytes), "hipMalloc(scratch)")) {
       h->s.base = nullptr;
       rc = QS_E_NOMEM;
     } else {
@@ -353,10 +365,11 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
     std::vector<uint32_t> tab;
     std::vector<int8_t> ones(256 * 8, 1);
     build_cb_tables(codebook ? codebook : ones.data(), tab);
-    if (hipMalloc(&h->cbtab, tab.size() * 4) != hipSuccess) {
+    if (!hip_ok(hipMalloc(&h->cbtab, tab.size() * 4), "hipMalloc(codebook)")) {
       h->cbtab = nullptr;
       rc = QS_E_NOMEM;
-    } else if (hipMemcpy(h->cbtab, tab.data(), tab.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+    } else if (!hip_ok(hipMemcpy(h->cbtab, tab.data(), tab.size() * 4, hipMemcpyHostToDevice),
+                       "hipMemcpy(codebook)")) {
       rc = QS_E_HIP;
     } else {
       h->total_bytes += tab.size() * 4;
@@ -434,10 +447,11 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
                   uint32_t flags, int32_t* ids_out, float* w_out, void* hip_stream) {
   if (!h || !x || !y) return QS_E_INVAL;
   const qs_moe_config& c = h->cfg;
-  if (flags & ~QS_DECODE_RESIDUAL) return QS_E_INVAL;
+  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM)) return QS_E_INVAL;
   if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
   if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
   const bool residual = flags & QS_DECODE_RESIDUAL;
+  const bool prenorm = flags & QS_DECODE_RMSNORM;
   if (!residual && n_layers != 1) return QS_E_INVAL;
   const size_t act_bytes = (size_t)n_tokens * c.hidden * sizeof(float);
   if (!residual && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
@@ -452,7 +466,7 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
   for (int i = 0; i < n_layers; ++i) {
     const bool last = i == n_layers - 1;
     float* dst = last ? y : h->s.xbuf[i & 1];
-    rc = launch_layer(h, h->layers[layer0 + i], cur, dst, n_tokens, residual,
+    rc = launch_layer(h, h->layers[layer0 + i], cur, dst, n_tokens, residual, prenorm,
                       ids_out ? ids_out + i * per : nullptr, w_out ? w_out + i * per : nullptr, st);
     if (rc) return rc;
     cur = dst;
@@ -460,10 +474,12 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
   return QS_OK;
 }
 
-QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, double* logits_out,
-                 int32_t* ids_out, float* w_out, int32_t* group_out, void* hip_stream) {
+QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, uint32_t flags,
+                        double* logits_out, int32_t* ids_out, float* w_out, int32_t* group_out,
+                        void* hip_stream) {
   if (!h || !x) return QS_E_INVAL;
   const qs_moe_config& c = h->cfg;
+  if (flags & ~QS_DECODE_RMSNORM) return QS_E_INVAL;
   if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
   if ((uintptr_t)x & 15) return QS_E_INVAL;
   int rc = check_layer_range(h, layer, 1);
@@ -471,7 +487,8 @@ QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, doub
   DeviceGuard dg(h->device);
   if (!dg.ok) return QS_E_HIP;
   hipStream_t st = (hipStream_t)hip_stream;
-  rc = launch_route(h, h->layers[layer], x, n_tokens, ids_out, w_out, st);
+  rc = launch_route(h, h->layers[layer], x, n_tokens, (flags & QS_DECODE_RMSNORM) != 0, ids_out,
+                    w_out, st);
   if (rc) return rc;
   const size_t E = c.n_experts, P = (size_t)n_tokens * c.top_k;
   Scratch& s = h->s;

@@ -52,17 +52,17 @@ class MoE:
                         None if lw.shared_up is None else c(lw.shared_up),
                         None if lw.shared_down is None else c(lw.shared_down), stream)
 
-    def decode(self, x, y=None, layer0=0, n_layers=1, residual=False, ids_out=None, w_out=None,
-               stream=None):
+    def decode(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
+               w_out=None, stream=None):
         import torch
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
-        flags = L.QS_DECODE_RESIDUAL if residual else 0
+        flags = (L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
         L.qs_moe_decode(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
 
-    def route(self, x, layer=0, stream=None):
+    def route(self, x, layer=0, prenorm=False, stream=None):
         import torch
         T = x.shape[0]
         E, k = self.cfg.n_experts, self.cfg.top_k
@@ -71,7 +71,8 @@ class MoE:
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
         grp = torch.empty(3 * E + 2 + T * k, dtype=torch.int32, device=dev)
-        L.qs_moe_route(self.h, layer, x, T, logits, ids, w, grp, stream)
+        L.qs_moe_route(self.h, layer, x, T, L.QS_DECODE_RMSNORM if prenorm else 0, logits, ids, w,
+                       grp, stream)
         P = T * k
         return {
             "logits": logits, "ids": ids, "w": w,

@@ -99,6 +99,6 @@ def test_null_arguments():
     assert qm.LIB.qs_moe_destroy(None) == qm.QS_OK
     assert qm.LIB.qs_moe_decode(None, 0, 1, None, None, 1, 0, None, None, None) == qm.QS_E_INVAL
     assert qm.LIB.qs_moe_upload(None, 0, None, None) == qm.QS_E_INVAL
-    assert qm.LIB.qs_moe_route(None, 0, None, 1, None, None, None, None, None) == qm.QS_E_INVAL
+    assert qm.LIB.qs_moe_route(None, 0, None, 1, 0, None, None, None, None, None) == qm.QS_E_INVAL
     assert qm.LIB.qs_moe_dequant(None, 0, 0, 0, None, None) == qm.QS_E_INVAL
     assert qm.LIB.qs_moe_memory_bytes(None, None) == qm.QS_E_INVAL

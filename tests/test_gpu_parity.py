@@ -181,28 +181,47 @@ def test_max_tokens_edge(lib):
         _decode_check(wl, moe, lws[0], 256, label="T=256 k=4")
 
 
-def test_residual_chain_and_in_place(lib):
+@pytest.mark.parametrize("prenorm", [False, True])
+def test_residual_chain_and_in_place(lib, prenorm):
     wl = workload("a3b_stack40_zipf")
     L = 3
-    say("residual chain 3 layers")
+    say(f"residual chain 3 layers prenorm={prenorm}")
     moe, lws = make_handle(lib, wl, n_layers=L, max_tokens=8)
     with moe:
         x = torch.from_numpy(synth.tokens(wl, 4, 1)).cuda()
         ids = torch.empty((L, 4, wl.top_k), dtype=torch.int32, device="cuda")
-        y_all = moe.decode(x, n_layers=L, residual=True, ids_out=ids)
+        w = torch.empty((L, 4, wl.top_k), dtype=torch.float32, device="cuda")
+        y_all = moe.decode(x, n_layers=L, residual=True, prenorm=prenorm, ids_out=ids, w_out=w)
         cur = x
         for l in range(L):
-            nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True)
+            nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True, prenorm=prenorm)
             torch.cuda.synchronize()
-            check_layer(wl, lws[l], cur.cpu().numpy(), nxt.cpu().numpy(), residual=True,
+            check_layer(wl, lws[l], cur.cpu().numpy(), nxt.cpu().numpy(), ids[l].cpu().numpy(),
+                        w[l].cpu().numpy(), residual=True, prenorm=prenorm,
                         label=f"layer {l} (teacher-forced)")
             cur = nxt
         torch.cuda.synchronize()
         assert torch.equal(y_all, cur), "multi-layer call differs from chained single layers"
         xin = x.clone()
-        moe.decode(xin, y=xin, n_layers=L, residual=True)
+        moe.decode(xin, y=xin, n_layers=L, residual=True, prenorm=prenorm)
         torch.cuda.synchronize()
         assert torch.equal(xin, y_all), "in-place decode differs"
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_prenorm_single_layer(a3b, T):
+    wl, moe, lws = a3b
+    say(f"prenorm a3b T={T}")
+    x = synth.tokens(wl, T, 9) * 3.0
+    xd = torch.from_numpy(x).cuda()
+    ids = torch.empty((T, wl.top_k), dtype=torch.int32, device="cuda")
+    y = moe.decode(xd, prenorm=True, ids_out=ids)
+    r = moe.route(xd, prenorm=True)
+    torch.cuda.synchronize()
+    check_layer(wl, lws[0], x, y.cpu().numpy(), ids.cpu().numpy(), prenorm=True,
+                label=f"prenorm T={T}")
+    lg_ref = om.moe_layer(oracle_layer(wl, lws[0]), x, prenorm=True)["logits"]
+    assert np.allclose(r["logits"].cpu().numpy(), lg_ref, rtol=1e-12, atol=1e-12)
 
 
 def test_error_statuses_with_gpu(lib):

@@ -127,14 +127,48 @@ def test_residual_and_stack_chain():
     cb = synth.codebook()
     layers = [om.Layer(wl, synth.layer_weights(wl, l), cb) for l in range(3)]
     x = synth.tokens(wl, 2)
-    out, per = om.moe_stack(layers, x)
-    cur = x
-    for l in range(3):
-        r = om.moe_layer(layers[l], cur)
-        cur = (cur.astype(np.float64) + r["y"].astype(np.float64))
-        assert np.max(om.rel_l2(per[l]["y"], cur)) < 1e-6
-        cur = per[l]["y"]
-    assert np.array_equal(out, per[-1]["y"])
+    for prenorm in (False, True):
+        out, per = om.moe_stack(layers, x, prenorm=prenorm)
+        cur = x
+        for l in range(3):
+            r = om.moe_layer(layers[l], cur, prenorm=prenorm)
+            cur = (cur.astype(np.float64) + r["y"].astype(np.float64))
+            assert np.max(om.rel_l2(per[l]["y"], cur)) < 1e-6
+            cur = per[l]["y"]
+        assert np.array_equal(out, per[-1]["y"])
+
+
+def test_rms_inv_matches_torch_rms_norm():
+    x = np.random.default_rng(5).standard_normal((7, 512)).astype(np.float32) * 3
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x.astype(np.float64)), (512,), eps=om.RMS_EPS)
+    got = x.astype(np.float64) * om.rms_inv(x)[:, None]
+    assert np.allclose(got, ref.numpy(), rtol=1e-14, atol=0)
+    c = 0.5
+    assert om.rms_inv(np.full((1, 64), c))[0] == 1.0 / np.sqrt(c * c + om.RMS_EPS)
+
+
+def test_prenorm_layer_is_scale_invariant():
+    """With the pre-norm, MoE(RMSNorm(a*x)) = MoE(RMSNorm(x)) for a > 0 (up to
+    the eps term), so y(a*x) - a*x equals y(x) - x."""
+    wl = _tiny("cb2", 256, zipf=1.1)
+    L = om.Layer(wl, synth.layer_weights(wl, 0), synth.codebook())
+    x = synth.tokens(wl, 3)
+    r1 = om.moe_layer(L, x, residual=False, prenorm=True)
+    r2 = om.moe_layer(L, 8 * x, residual=False, prenorm=True)
+    assert np.array_equal(r1["ids"], r2["ids"])
+    assert np.max(om.rel_l2(r2["y"], r1["y"])) < 1e-5
+    # and the routing equals routing the explicitly normalised input
+    xn = (x.astype(np.float64) * om.rms_inv(x)[:, None]).astype(np.float32)
+    r3 = om.moe_layer(L, xn, prenorm=False)
+    assert np.array_equal(r1["ids"], r3["ids"])
+
+
+def test_prenorm_chain_stays_bounded():
+    wl = _tiny("cb2", 256, L=12, zipf=1.1)
+    cb = synth.codebook()
+    layers = [om.Layer(wl, synth.layer_weights(wl, l), cb) for l in range(12)]
+    out, _ = om.moe_stack(layers, synth.tokens(wl, 2), prenorm=True)
+    assert np.all(np.isfinite(out)) and np.sqrt(np.mean(out.astype(np.float64) ** 2)) < 10
 
 
 def test_generator_is_deterministic_and_keyed():
