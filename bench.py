@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=6, help="layers in the oracle sample")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    p.add_argument("--multikernel", action="store_true", help="time the one-kernel-per-step path")
     return p.parse_args()
 
 
@@ -82,19 +83,22 @@ def main():
         ids = torch.empty((N_BATCHES, L, T, wl.top_k), dtype=torch.int32, device="cuda")
         # untimed pass: the experts each batch selects, for the byte count
         for b in range(N_BATCHES):
-            moe.decode(xs[b], y, n_layers=L, residual=True, prenorm=True, ids_out=ids[b])
+            moe.decode(xs[b], y, n_layers=L, residual=True, prenorm=True, ids_out=ids[b],
+                       multikernel=args.multikernel)
         torch.cuda.synchronize()
         idn = ids.cpu().numpy()
         uniq = np.array([[len(np.unique(idn[b, l])) for l in range(L)] for b in range(N_BATCHES)])
         bytes_batch = uniq.sum(axis=1) * per_expert + L * fixed_layer + 2 * T * wl.hidden * 4
         for i in range(args.warmup):
-            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True, prenorm=True)
+            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True, prenorm=True,
+                       multikernel=args.multikernel)
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for i in range(args.steps):
-            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True, prenorm=True)
+            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True, prenorm=True,
+                       multikernel=args.multikernel)
         end.record(stream)
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / args.steps

@@ -82,6 +82,9 @@ typedef enum { QS_FMT_Q2K = 1, QS_FMT_CB2 = 2 } qs_format;
                                    without learned weight, as a pre-norm residual
                                    stream applies before each MoE block); without
                                    this flag u_l = x_l */
+#define QS_DECODE_MULTIKERNEL 4u /* run each step as its own kernel launch instead of
+                                   the single persistent kernel (same results up to
+                                   summation order; for comparison and debugging) */
 
 typedef struct qs_moe qs_moe;   /* opaque, owned by the library */
 

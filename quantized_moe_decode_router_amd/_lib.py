@@ -15,6 +15,7 @@ QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED = 0, -1, -
 QS_FMT_Q2K, QS_FMT_CB2 = 1, 2
 QS_DECODE_RESIDUAL = 1
 QS_DECODE_RMSNORM = 2
+QS_DECODE_MULTIKERNEL = 4
 
 FORMATS = {"q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2}
 

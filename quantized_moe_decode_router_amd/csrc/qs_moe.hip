@@ -18,6 +18,7 @@
 #include "qs_moe.h"
 #include "qs_kernels.h"
 #include "qs_layout.h"
+#include "qs_persist.h"
 
 using namespace qs;
 
@@ -75,6 +76,13 @@ struct qs_moe {
   uint8_t* staging = nullptr;
   size_t staging_bytes = 0;
   uint64_t total_bytes = 0;
+  // persistent kernel
+  LayerPtrs* d_layers = nullptr;  // device table of every layer's pointers
+  uint32_t* sync = nullptr;       // barrier words
+  uint32_t epoch = 0;             // barriers completed on `sync`
+  int grid = 0;                   // workgroups of the persistent kernel (one per CU)
+  size_t lds_limit = 0;           // LDS bytes per workgroup available on the device
+  bool persist_ok = false;
 };
 
 namespace {
@@ -205,6 +213,127 @@ void free_all(qs_moe* h) {
   if (h->s.base) (void)hipFree(h->s.base);
   if (h->cbtab) (void)hipFree(h->cbtab);
   if (h->staging) (void)hipFree(h->staging);
+  if (h->d_layers) (void)hipFree(h->d_layers);
+  if (h->sync) (void)hipFree(h->sync);
+}
+
+__global__ void k_sync_reset(uint32_t* s) {
+  for (int i = threadIdx.x; i < kSyncWords; i += blockDim.x) s[i] = 0;
+}
+
+// LDS of one persistent launch: the fixed carve plus as much prefetch buffer
+// (up to kPfbMax) as the device's LDS leaves.
+size_t persist_pfb(const qs_moe* h, int T, bool small) {
+  const qs_moe_config& c = h->cfg;
+  const size_t base = persist_lds_bytes(c.n_experts, T, T * c.top_k, c.hidden,
+                                        c.gate_up_format == QS_FMT_CB2, small, 0);
+  if (base >= h->lds_limit) return 0;
+  return std::min(kPfbMax, (h->lds_limit - base) & ~(size_t)15);
+}
+
+size_t persist_lds_total(const qs_moe* h, int T, bool small) {
+  const qs_moe_config& c = h->cfg;
+  return persist_lds_bytes(c.n_experts, T, T * c.top_k, c.hidden, c.gate_up_format == QS_FMT_CB2, small,
+                           persist_pfb(h, T, small));
+}
+
+// Set up the persistent kernel: layer table, barrier words, grid size and an
+// occupancy check (all workgroups must be resident at once for the grid
+// barrier; a cooperative launch also enforces this).
+int setup_persistent(qs_moe* h) {
+  const qs_moe_config& c = h->cfg;
+  std::vector<LayerPtrs> tab(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerDev& L = h->layers[l];
+    tab[l] = LayerPtrs{L.router, L.bias, L.gate, L.up, L.down, L.sg, L.su, L.sd};
+  }
+  if (!hip_ok(hipMalloc(&h->d_layers, tab.size() * sizeof(LayerPtrs)), "hipMalloc(layers)")) {
+    h->d_layers = nullptr;
+    return QS_E_NOMEM;
+  }
+  if (!hip_ok(hipMemcpy(h->d_layers, tab.data(), tab.size() * sizeof(LayerPtrs), hipMemcpyHostToDevice),
+              "hipMemcpy(layers)"))
+    return QS_E_HIP;
+  if (!hip_ok(hipMalloc(&h->sync, kSyncWords * 4), "hipMalloc(sync)")) {
+    h->sync = nullptr;
+    return QS_E_NOMEM;
+  }
+  if (!hip_ok(hipMemset(h->sync, 0, kSyncWords * 4), "hipMemset(sync)")) return QS_E_HIP;
+  h->total_bytes += tab.size() * sizeof(LayerPtrs) + kSyncWords * 4;
+  hipDeviceProp_t prop;
+  if (!hip_ok(hipGetDeviceProperties(&prop, h->device), "hipGetDeviceProperties")) return QS_E_HIP;
+  int coop = 0;
+  (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device);
+  h->grid = prop.multiProcessorCount & ~7;
+  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
+  const int Ts = c.max_tokens < kSmallT ? c.max_tokens : kSmallT;
+  h->lds_limit = prop.maxSharedMemoryPerMultiProcessor;
+  size_t lds = persist_lds_total(h, c.max_tokens, false);
+  if (persist_lds_bytes(c.n_experts, Ts, Ts * c.top_k, c.hidden, cb2, true, 0) <= h->lds_limit)
+    lds = std::max(lds, persist_lds_total(h, Ts, true));
+  const void* fn = cb2 ? (const void*)k_persist<2> : (const void*)k_persist<1>;
+  if (lds > h->lds_limit || !coop || h->grid < 8) return QS_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return QS_OK;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return QS_OK;
+  }
+  h->persist_ok = occ >= 1;
+  return QS_OK;
+}
+
+// The whole decode call as one cooperative launch.
+int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, int T, bool residual,
+                      bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
+  const qs_moe_config& c = h->cfg;
+  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
+  // small batches: every workgroup routes and quantises all tokens itself
+  const bool small = T <= kSmallT &&
+                     persist_lds_bytes(c.n_experts, T, T * c.top_k, c.hidden, cb2, true, 0) <= h->lds_limit;
+  const uint32_t barriers = (small ? 3u : 4u) * nL - 1u;
+  if (h->epoch + barriers > (1u << 26)) {
+    hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
+    h->epoch = 0;
+  }
+  Scratch& s = h->s;
+  PersistArgs a{};
+  a.layers = h->d_layers + layer0;
+  a.n_layers = nL;
+  a.T = T; a.H = c.hidden; a.E = c.n_experts; a.k = c.top_k; a.F = c.expert_ffn; a.Fs = c.shared_ffn;
+  a.gq2k = c.gate_up_format == QS_FMT_Q2K;
+  a.prenorm = prenorm;
+  a.residual = residual;
+  a.small = small;
+  a.r_tt = T < 4 ? T : 4;
+  const int ntt = (T + a.r_tt - 1) / a.r_tt;
+  a.r_et = 1;
+  while (a.r_et < 4 && ((c.n_experts + a.r_et - 1) / a.r_et) * ntt > h->grid) a.r_et *= 2;
+  a.gu_stride = h->gu_stride;
+  a.dn_stride = h->dn_stride;
+  a.cbtab = h->cbtab;
+  a.x_in = x; a.y_out = y; a.ids_out = ids_out; a.w_out = w_out;
+  a.logits = s.logits; a.rinv = s.rinv; a.ids = s.ids; a.wts = s.wts;
+  a.xh = s.xh; a.xl = s.xl; a.xs = s.xs; a.xa = s.xa;
+  a.ah = s.ah; a.al = s.al; a.as = s.as; a.aa = s.aa; a.ash = s.ash;
+  a.xbuf0 = s.xbuf[0]; a.xbuf1 = s.xbuf[1];
+  a.sync = h->sync;
+  a.epoch0 = h->epoch;
+  const size_t lds = persist_lds_total(h, T, small);
+  a.pfb = (int)persist_pfb(h, T, small);
+  void* args[] = {&a};
+  const void* fn = cb2 ? (const void*)k_persist<2> : (const void*)k_persist<1>;
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(kPersistThreads), args,
+                                            (unsigned)lds, st);
+  if (e != hipSuccess) {
+    fprintf(stderr, "qs_moe: persistent launch failed: %s\n", hipGetErrorString(e));
+    return QS_E_HIP;
+  }
+  h->epoch += barriers;
+  return QS_OK;
 }
 
 int check_layer_range(const qs_moe* h, int layer0, int n) {
@@ -375,6 +504,7 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
       h->total_bytes += tab.size() * 4;
     }
   }
+  if (rc == QS_OK) rc = setup_persistent(h);
   if (rc != QS_OK) {
     free_all(h);
     delete h;
@@ -447,7 +577,7 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
                   uint32_t flags, int32_t* ids_out, float* w_out, void* hip_stream) {
   if (!h || !x || !y) return QS_E_INVAL;
   const qs_moe_config& c = h->cfg;
-  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM)) return QS_E_INVAL;
+  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM | QS_DECODE_MULTIKERNEL)) return QS_E_INVAL;
   if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
   if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
   const bool residual = flags & QS_DECODE_RESIDUAL;
@@ -461,6 +591,9 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
   DeviceGuard dg(h->device);
   if (!dg.ok) return QS_E_HIP;
   hipStream_t st = (hipStream_t)hip_stream;
+  if (h->persist_ok && !(flags & QS_DECODE_MULTIKERNEL))
+    return launch_persistent(h, layer0, n_layers, x, y, n_tokens, residual, prenorm, ids_out,
+                             w_out, st);
   const size_t per = (size_t)n_tokens * c.top_k;
   const float* cur = x;
   for (int i = 0; i < n_layers; ++i) {

@@ -53,12 +53,13 @@ class MoE:
                         None if lw.shared_down is None else c(lw.shared_down), stream)
 
     def decode(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
-               w_out=None, stream=None):
+               w_out=None, stream=None, multikernel=False):
         import torch
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
-        flags = (L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
+        flags = ((L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
+                 | (L.QS_DECODE_MULTIKERNEL if multikernel else 0))
         L.qs_moe_decode(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
 
