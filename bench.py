@@ -1,19 +1,29 @@
 """Benchmark of the routed-expert MoE decode step on one MI355X.
 
 A step is one qs_moe_decode call through every layer of the workload (the
-residual chain x_{l+1} = x_l + MoE_l(x_l)) for one batch of T tokens.  The
-inputs rotate through 64 seeded batches already resident in HBM, so picks
-change from step to step.  Throughput is tokens/s; the weight-read rate is
-the algorithmic bytes of a step (router, shared expert and each distinct
-selected expert once per layer, plus activations in and out) over the step
-time, against the 8 TB/s HBM peak.
+pre-norm residual chain x_{l+1} = x_l + MoE_l(RMSNorm(x_l))) for one batch of
+T tokens.  The inputs rotate through 64 seeded batches already resident in
+HBM, so expert picks change from step to step.  Throughput is tokens/s; the
+weight-read rate is the algorithmic bytes of a step (each layer's router,
+shared expert and every distinct selected expert read once, plus the
+activations in and out) over the step time, against the 8 TB/s HBM peak.
+
+The roofline entry is for the decode kernel itself (one launch per step):
+algorithmic bytes per launch over its mean duration, timed with HIP events on
+the stream it is launched on.  Its "traffic" is the HBM bytes per launch that
+the FETCH_SIZE / WRITE_SIZE counters recorded for the same kernel, scaled by
+what the counters read for a plain copy of known size; it is read from the
+committed counter summary and reported only if that summary was taken from
+the current kernel sources (sha256 of csrc/ and include/), else null.
 
 Prints one JSON line.  --gpus above 1 is refused: this path is measured on
-one GPU.
+one GPU.  `--copy-calibration MiB` instead runs a plain device copy (the
+reference kernel for the counter scaling) and prints what it moved.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 N_BATCHES = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_persist_a3b_stack40_zipf_T1_hbm_traffic.txt")
 
 
 def parse():
@@ -36,9 +47,11 @@ def parse():
     p.add_argument("--workload", default="a3b_stack40_zipf")
     p.add_argument("--tokens", default="1,4,16", help="batch sizes; the first is the headline")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-layers", type=int, default=6, help="layers in the oracle sample")
+    p.add_argument("--cpu-layers", type=int, default=40, help="layers in the oracle sample")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     p.add_argument("--multikernel", action="store_true", help="time the one-kernel-per-step path")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of this many MiB, 20 times")
     return p.parse_args()
 
 
@@ -46,12 +59,61 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def source_digest() -> str:
+    """sha256 over the kernel sources and the public header."""
+    h = hashlib.sha256()
+    dirs = [os.path.join(ROOT, "quantized_moe_decode_router_amd", "csrc"), os.path.join(ROOT, "include")]
+    for d in dirs:
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".h", ".hip", ".cpp")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str, T: int):
+    """HBM bytes per launch from the committed counter summary, when it
+    matches this workload, batch and the current sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "\t", "#", "$")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if (kv.get("source_sha256") != source_digest() or kv.get("workload") != workload
+                or int(kv.get("tokens", -1)) != T):
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                                           "launches": 20}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path runs on one MI355X, see DESIGN.md for how it would shard)")
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this build runs "
+              "and is measured on a single MI355X (the design notes say how it would shard)")
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
 
     import quantized_moe_decode_router_amd as qm
@@ -74,7 +136,13 @@ def main():
     g, u, d = wl.expert_bytes()
     per_expert = g + u + d
     fixed_layer = wl.router_bytes() + wl.shared_bytes()
+    # decode() launches on torch's current stream; every event below is
+    # recorded on that same stream
     stream = torch.cuda.current_stream()
+
+    def step(x, y, ids=None):
+        moe.decode(x, y, n_layers=L, residual=True, prenorm=True, ids_out=ids,
+                   multikernel=args.multikernel, stream=stream)
 
     results = {}
     for T in tok_list:
@@ -83,34 +151,46 @@ def main():
         ids = torch.empty((N_BATCHES, L, T, wl.top_k), dtype=torch.int32, device="cuda")
         # untimed pass: the experts each batch selects, for the byte count
         for b in range(N_BATCHES):
-            moe.decode(xs[b], y, n_layers=L, residual=True, prenorm=True, ids_out=ids[b],
-                       multikernel=args.multikernel)
+            step(xs[b], y, ids[b])
         torch.cuda.synchronize()
         idn = ids.cpu().numpy()
         uniq = np.array([[len(np.unique(idn[b, l])) for l in range(L)] for b in range(N_BATCHES)])
         bytes_batch = uniq.sum(axis=1) * per_expert + L * fixed_layer + 2 * T * wl.hidden * 4
         for i in range(args.warmup):
-            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True, prenorm=True,
-                       multikernel=args.multikernel)
+            step(xs[i % N_BATCHES], y)
         torch.cuda.synchronize()
+        # whole timed region: K steps back to back
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for i in range(args.steps):
-            moe.decode(xs[i % N_BATCHES], y, n_layers=L, residual=True, prenorm=True,
-                       multikernel=args.multikernel)
+            step(xs[i % N_BATCHES], y)
         end.record(stream)
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / args.steps
+        # per launch: an event pair around each decode call (one kernel launch
+        # on the persistent path), same stream, same inputs
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step(xs[i % N_BATCHES], y)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
         step_bytes = float(np.mean([bytes_batch[i % N_BATCHES] for i in range(args.steps)]))
         gbs = step_bytes / (ms * 1e-3) / 1e9
         results[T] = {
             "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms, "bytes_per_step": step_bytes,
             "weight_read_GBps": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
             "mean_distinct_experts_per_layer": float(uniq.mean()),
+            "launch_ms_mean": float(launch_ms.mean()), "launch_ms_p10": float(np.percentile(launch_ms, 10)),
+            "launch_ms_p90": float(np.percentile(launch_ms, 90)),
         }
         log(f"[bench] T={T}: {ms:.3f} ms/step, {T / (ms * 1e-3):.1f} tok/s, {gbs:.1f} GB/s "
-            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), U={uniq.mean():.1f}")
+            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), U={uniq.mean():.1f}, "
+            f"launch {launch_ms.mean():.3f} ms (p10 {np.percentile(launch_ms, 10):.3f}, "
+            f"p90 {np.percentile(launch_ms, 90):.3f})")
         del xs, ids
     moe.close()
 
@@ -119,6 +199,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, T0, L, args.cpu_layers)
+    kname = ("k_persist<" + ("cb2" if wl.gate_up_format == "cb2" else "q2k") + "> (whole decode call)"
+             if not args.multikernel else "decode call (one launch per step kind)")
+    achieved = head["bytes_per_step"] / (head["launch_ms_mean"] * 1e-3) / 1e9
+    traffic = None if args.multikernel or args.layers else committed_traffic(wl.name, T0)
     line = {
         "metric": "MoE decode tokens/s and weight-read GB/s as % of HBM peak, batch 1/4/16",
         "value": head["tokens_per_s"],
@@ -140,9 +224,12 @@ def main():
                    "tokens": T0, "zipf_s": wl.zipf_s, "parallelism": "single GPU"},
         "weight_read_GBps": head["weight_read_GBps"],
         "pct_hbm_peak": head["pct_hbm_peak"],
-        "roofline": {"bound": "hbm", "kernel": "decode step (all kernels of one call)",
-                     "achieved": head["weight_read_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["weight_read_GBps"] / HBM_PEAK_GBS, "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": kname,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "algorithmic_bytes_per_launch": head["bytes_per_step"],
+                     "launch_ms": head["launch_ms_mean"],
+                     "traffic": traffic},
         "per_batch": {str(T): r for T, r in results.items()},
         "cpu_baseline": cpu,
     }
@@ -172,13 +259,14 @@ def cpu_baseline(wl, T, L, n_layers_sample):
     for layer in layers:
         cur = om.moe_layer(layer, cur, residual=True, prenorm=True)["y"]
     dt = time.perf_counter() - t0
-    if limit is not None:
-        limit.unregister() if hasattr(limit, "unregister") else None
+    if limit is not None and hasattr(limit, "unregister"):
+        limit.unregister()
     step_s = dt * L / n
-    log(f"[bench] oracle: {n} layers at T={T} in {dt:.2f}s -> {T / step_s:.3f} tok/s for {L} layers")
+    log(f"[bench] oracle: {n} layers at T={T} in {dt:.2f}s -> {T / step_s:.4f} tok/s for {L} layers")
     return {"value": T / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {L} layers of one step at T={T} (numpy fp64, one thread), "
-                      f"{dt:.1f}s, scaled by {L}/{n}"}
+            "sample": (f"all {L} layers" if n == L else f"first {n} of {L} layers, scaled by {L}/{n},")
+                      + f" of one step at T={T} (numpy fp64 with one BLAS thread, dequantising each"
+                      f" touched expert): {dt:.1f}s"}
 
 
 if __name__ == "__main__":
