@@ -142,7 +142,7 @@ def main():
 
     def step(x, y, ids=None):
         moe.decode(x, y, n_layers=L, residual=True, prenorm=True, ids_out=ids,
-                   multikernel=args.multikernel, stream=stream)
+                   path="multikernel" if args.multikernel else "persistent", stream=stream)
 
     results = {}
     for T in tok_list:

@@ -85,6 +85,12 @@ typedef enum { QS_FMT_Q2K = 1, QS_FMT_CB2 = 2 } qs_format;
 #define QS_DECODE_MULTIKERNEL 4u /* run each step as its own kernel launch instead of
                                    the single persistent kernel (same results up to
                                    summation order; for comparison and debugging) */
+#define QS_DECODE_REQUIRE_PERSISTENT 8u /* fail with QS_E_UNSUPPORTED (nothing enqueued)
+                                   instead of falling back to one launch per step when
+                                   the persistent kernel cannot run this call (device
+                                   without cooperative launch, or a shape whose working
+                                   set does not fit the workgroup's LDS); not
+                                   combinable with QS_DECODE_MULTIKERNEL */
 
 typedef struct qs_moe qs_moe;   /* opaque, owned by the library */
 

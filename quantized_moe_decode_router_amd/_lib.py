@@ -16,6 +16,7 @@ QS_FMT_Q2K, QS_FMT_CB2 = 1, 2
 QS_DECODE_RESIDUAL = 1
 QS_DECODE_RMSNORM = 2
 QS_DECODE_MULTIKERNEL = 4
+QS_DECODE_REQUIRE_PERSISTENT = 8
 
 FORMATS = {"q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2}
 

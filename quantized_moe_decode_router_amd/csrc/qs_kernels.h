@@ -103,7 +103,8 @@ __device__ __forceinline__ int valid_id(int e, int E) { return e < 0 ? 0 : (e >=
 //   tab[idx*16 + s]           weights 0..3 of a group with row idx, sign nibble s
 //   tab[4096 + s*256 + idx]   weights 4..7, sign nibble s
 // A code dword holds two groups (low half: group 2i, high half: 2i+1).
-__device__ __forceinline__ void cb2_decode_dword(const uint32_t* __restrict__ tab, uint32_t v,
+template <typename TabPtr>   // the tables in LDS (any address-space-qualified pointer)
+__device__ __forceinline__ void cb2_decode_dword(TabPtr tab, uint32_t v,
                                                  uint32_t& q0, uint32_t& q1, uint32_t& q2,
                                                  uint32_t& q3) {
   q0 = tab[v & 0xFFFu];

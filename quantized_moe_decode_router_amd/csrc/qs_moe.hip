@@ -82,7 +82,8 @@ struct qs_moe {
   uint32_t epoch = 0;             // barriers completed on `sync`
   int grid = 0;                   // workgroups of the persistent kernel (one per CU)
   size_t lds_limit = 0;           // LDS bytes per workgroup available on the device
-  bool persist_ok = false;
+  bool persist_small_ok = false; // T <= kSmallT instantiation usable
+  bool persist_big_ok = false;   // T > kSmallT instantiation usable
 };
 
 namespace {
@@ -221,25 +222,64 @@ __global__ void k_sync_reset(uint32_t* s) {
   for (int i = threadIdx.x; i < kSyncWords; i += blockDim.x) s[i] = 0;
 }
 
-// LDS of one persistent launch: the fixed carve plus as much prefetch buffer
-// (up to kPfbMax) as the device's LDS leaves.
-size_t persist_pfb(const qs_moe* h, int T, bool small) {
+// Shape of one persistent launch: LDS carve plus as much weight-staging
+// buffer (up to kPfbMax) as the device's LDS leaves, the router unit, and
+// whether the buffer holds one piece of every kind the kernel stages (the
+// same sizes the kernel's staging plans use).
+struct PersistShape {
+  bool ok = false;
+  uint32_t pfb = 0;
+  size_t lds = 0;
+  int r_et = 1, r_tt = 1;
+};
+
+PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   const qs_moe_config& c = h->cfg;
-  const size_t base = persist_lds_bytes(c.n_experts, T, T * c.top_k, c.hidden,
-                                        c.gate_up_format == QS_FMT_CB2, small, 0);
-  if (base >= h->lds_limit) return 0;
-  return std::min(kPfbMax, (h->lds_limit - base) & ~(size_t)15);
+  PersistShape p;
+  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
+  const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, cb2, small,
+                                 0).end;
+  if (base >= h->lds_limit || h->grid < 8) return p;
+  p.pfb = (uint32_t)std::min((size_t)kPfbMax, (h->lds_limit - base) & ~(size_t)15);
+  p.lds = base + p.pfb;
+  p.r_tt = T < 4 ? T : 4;
+  while (p.r_et < 4 && (c.n_experts + p.r_et - 1) / p.r_et > h->grid) p.r_et *= 2;
+  const uint64_t H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn, nbh = H / 256, nb = F / 256;
+  const uint64_t rb = (uint64_t)p.r_et * H * 4, item = 8 * H;
+  const uint64_t tile = 2ull * 16 * nbh * (64 + (cb2 ? 4 : 16) + (cb2 ? 2 : 4));
+  const uint64_t sd = 16 * Fs, pe = 8 * nb * 84;
+  auto a16 = [](uint64_t v) { return (v + 15) & ~15ull; };
+  bool fits = rb <= p.pfb && tile <= p.pfb && a16(sd) + pe <= p.pfb;
+  // SMALL: shared items after the router rows; otherwise at least one
+  // shared item ahead of the routed tiles' slots
+  if (Fs) fits = fits && (small ? a16(rb) + item : item + tile) <= p.pfb;
+  p.ok = fits;
+  return p;
 }
 
-size_t persist_lds_total(const qs_moe* h, int T, bool small) {
-  const qs_moe_config& c = h->cfg;
-  return persist_lds_bytes(c.n_experts, T, T * c.top_k, c.hidden, c.gate_up_format == QS_FMT_CB2, small,
-                           persist_pfb(h, T, small));
+const void* persist_fn(bool cb2, bool small) {
+  if (cb2) return small ? (const void*)k_persist<2, true> : (const void*)k_persist<2, false>;
+  return small ? (const void*)k_persist<1, true> : (const void*)k_persist<1, false>;
 }
 
-// Set up the persistent kernel: layer table, barrier words, grid size and an
-// occupancy check (all workgroups must be resident at once for the grid
-// barrier; a cooperative launch also enforces this).
+// Every workgroup must be resident at once for the grid barrier (a
+// cooperative launch also enforces this).
+bool persist_resident(const qs_moe* h, bool small, size_t lds) {
+  const void* fn = persist_fn(h->cfg.gate_up_format == QS_FMT_CB2, small);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return occ >= 1;
+}
+
+// Set up the persistent kernels: layer table, barrier words, grid size and
+// the residency check of each instantiation at its largest launch.
 int setup_persistent(qs_moe* h) {
   const qs_moe_config& c = h->cfg;
   std::vector<LayerPtrs> tab(c.n_layers);
@@ -265,35 +305,45 @@ int setup_persistent(qs_moe* h) {
   int coop = 0;
   (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device);
   h->grid = prop.multiProcessorCount & ~7;
-  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
-  const int Ts = c.max_tokens < kSmallT ? c.max_tokens : kSmallT;
-  h->lds_limit = prop.maxSharedMemoryPerMultiProcessor;
-  size_t lds = persist_lds_total(h, c.max_tokens, false);
-  if (persist_lds_bytes(c.n_experts, Ts, Ts * c.top_k, c.hidden, cb2, true, 0) <= h->lds_limit)
-    lds = std::max(lds, persist_lds_total(h, Ts, true));
-  const void* fn = cb2 ? (const void*)k_persist<2> : (const void*)k_persist<1>;
-  if (lds > h->lds_limit || !coop || h->grid < 8) return QS_OK;
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-    (void)hipGetLastError();
-    return QS_OK;
+  // dynamic LDS available to a workgroup: the device's LDS minus the largest
+  // static LDS of the persistent instantiations (the block-wide vote of the
+  // barrier keeps a few bytes there)
+  size_t static_lds = 0;
+  for (int cb = 0; cb < 2; ++cb)
+    for (int sm = 0; sm < 2; ++sm) {
+      hipFuncAttributes fa;
+      if (hipFuncGetAttributes(&fa, persist_fn(cb != 0, sm != 0)) != hipSuccess) {
+        (void)hipGetLastError();
+        return QS_OK;
+      }
+      static_lds = std::max(static_lds, (size_t)fa.sharedSizeBytes);
+    }
+  const size_t dev_lds = prop.maxSharedMemoryPerMultiProcessor;
+  h->lds_limit = dev_lds > static_lds ? (dev_lds - static_lds) & ~(size_t)255 : 0;
+  if (!coop || h->grid < 8) return QS_OK;
+  // the largest LDS of each instantiation: the carve grows with T
+  size_t lds_small = 0, lds_big = 0;
+  for (int T = 1; T <= c.max_tokens; ++T) {
+    const bool small = T <= kSmallT;
+    const PersistShape p = persist_shape(h, T, small);
+    if (!p.ok) continue;
+    (small ? lds_small : lds_big) = std::max(small ? lds_small : lds_big, p.lds);
   }
-  int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds) != hipSuccess) {
-    (void)hipGetLastError();
-    return QS_OK;
-  }
-  h->persist_ok = occ >= 1;
+  h->persist_small_ok = lds_small && persist_resident(h, true, lds_small);
+  h->persist_big_ok = lds_big && persist_resident(h, false, lds_big);
   return QS_OK;
 }
 
-// The whole decode call as one cooperative launch.
+// The whole decode call as one cooperative launch.  Returns 1 (nothing
+// enqueued) when this batch size has no persistent instantiation that fits.
 int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, int T, bool residual,
                       bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
   const qs_moe_config& c = h->cfg;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
-  // small batches: every workgroup routes and quantises all tokens itself
-  const bool small = T <= kSmallT &&
-                     persist_lds_bytes(c.n_experts, T, T * c.top_k, c.hidden, cb2, true, 0) <= h->lds_limit;
+  const bool small = T <= kSmallT;
+  if (!(small ? h->persist_small_ok : h->persist_big_ok)) return 1;
+  const PersistShape p = persist_shape(h, T, small);
+  if (!p.ok) return 1;
   const uint32_t barriers = (small ? 3u : 4u) * nL - 1u;
   if (h->epoch + barriers > (1u << 26)) {
     hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
@@ -307,11 +357,9 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   a.gq2k = c.gate_up_format == QS_FMT_Q2K;
   a.prenorm = prenorm;
   a.residual = residual;
-  a.small = small;
-  a.r_tt = T < 4 ? T : 4;
-  const int ntt = (T + a.r_tt - 1) / a.r_tt;
-  a.r_et = 1;
-  while (a.r_et < 4 && ((c.n_experts + a.r_et - 1) / a.r_et) * ntt > h->grid) a.r_et *= 2;
+  a.r_tt = p.r_tt;
+  a.r_et = p.r_et;
+  a.pfb = p.pfb;
   a.gu_stride = h->gu_stride;
   a.dn_stride = h->dn_stride;
   a.cbtab = h->cbtab;
@@ -322,12 +370,9 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   a.xbuf0 = s.xbuf[0]; a.xbuf1 = s.xbuf[1];
   a.sync = h->sync;
   a.epoch0 = h->epoch;
-  const size_t lds = persist_lds_total(h, T, small);
-  a.pfb = (int)persist_pfb(h, T, small);
   void* args[] = {&a};
-  const void* fn = cb2 ? (const void*)k_persist<2> : (const void*)k_persist<1>;
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(kPersistThreads), args,
-                                            (unsigned)lds, st);
+  hipError_t e = hipLaunchCooperativeKernel(persist_fn(cb2, small), dim3(h->grid), dim3(kPersistThreads), args,
+                                            (unsigned)p.lds, st);
   if (e != hipSuccess) {
     fprintf(stderr, "qs_moe: persistent launch failed: %s\n", hipGetErrorString(e));
     return QS_E_HIP;
@@ -577,7 +622,9 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
                   uint32_t flags, int32_t* ids_out, float* w_out, void* hip_stream) {
   if (!h || !x || !y) return QS_E_INVAL;
   const qs_moe_config& c = h->cfg;
-  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM | QS_DECODE_MULTIKERNEL)) return QS_E_INVAL;
+  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM | QS_DECODE_MULTIKERNEL | QS_DECODE_REQUIRE_PERSISTENT))
+    return QS_E_INVAL;
+  if ((flags & QS_DECODE_MULTIKERNEL) && (flags & QS_DECODE_REQUIRE_PERSISTENT)) return QS_E_INVAL;
   if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
   if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
   const bool residual = flags & QS_DECODE_RESIDUAL;
@@ -591,9 +638,13 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
   DeviceGuard dg(h->device);
   if (!dg.ok) return QS_E_HIP;
   hipStream_t st = (hipStream_t)hip_stream;
-  if (h->persist_ok && !(flags & QS_DECODE_MULTIKERNEL))
-    return launch_persistent(h, layer0, n_layers, x, y, n_tokens, residual, prenorm, ids_out,
-                             w_out, st);
+  if (!(flags & QS_DECODE_MULTIKERNEL)) {
+    // one persistent launch when an instantiation fits this batch size;
+    // otherwise the same arithmetic as one launch per step
+    rc = launch_persistent(h, layer0, n_layers, x, y, n_tokens, residual, prenorm, ids_out, w_out, st);
+    if (rc != 1) return rc;
+    if (flags & QS_DECODE_REQUIRE_PERSISTENT) return QS_E_UNSUPPORTED;
+  }
   const size_t per = (size_t)n_tokens * c.top_k;
   const float* cur = x;
   for (int i = 0; i < n_layers; ++i) {

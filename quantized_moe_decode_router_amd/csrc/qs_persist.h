@@ -4,34 +4,45 @@
 // Why one kernel: each layer has three all-to-all dependencies (all logits
 // before top-k, all SwiGLU outputs of an expert before its down GEMV, all of
 // x_{l+1} before the next router).  A kernel boundary costs ~2.5 us on
-// MI355X and a grid barrier about the same, but inside one kernel the
-// weights that do not depend on the pending result (router rows, shared
-// expert rows, the down rows of experts already chosen) are requested before
-// the wait, straight into LDS, so their HBM latency hides behind it.
+// MI355X and a grid barrier about the same; inside one kernel the weights
+// that do not depend on the pending result (router rows, shared-expert rows,
+// the down rows of experts already chosen) are copied into LDS while the
+// workgroup waits, so their HBM latency hides behind the wait.
 //
-// Phases of one layer (G workgroups x 512 threads, one per CU):
-//   R   router logits (fp64, exact products) and the per-token RMS scale;
-//       then the shared gate/up rows of this workgroup's first item are issued
-//   K   top-k per token (one wave each) and x -> fixed-point limbs; for
-//       T <= kSmallT every workgroup does this itself into LDS, which saves
-//       the barrier after K
-//   GU  grouping rebuilt in LDS by every workgroup; shared-expert and routed
-//       gate/up items; then the down rows of this workgroup's first tile
-//   D   down row tiles + combine + shared down + residual -> x_{l+1}; then
-//       the next layer's router rows
-// The three prefetches share one LDS buffer: each is consumed before the
-// next is issued.  Phases are joined by a fence-free grid barrier: per-XCD
-// arrival counters, a global counter bumped by each XCD's last arriver, and
-// per-XCD release lines written by the global last arriver.  Data crossing a
-// barrier is written and read with agent-scope (sc1) atomic accesses, which
-// are coherent across the XCDs' separate L2s without the whole-L2
-// writeback/invalidate of a release or acquire fence; an s_waitcnt before
-// arriving orders them (and completes the LDS prefetches).  Every wait is
+// Every weight the kernel multiplies is read from LDS: a workgroup's first
+// piece of each kind is copied during the preceding wait, later pieces are
+// copied on demand.  Each compute routine therefore exists once, which keeps
+// the kernel's code small enough for the instruction cache: a layer walks
+// through all of it, so code that does not fit is re-fetched every layer.
+//
+// Two instantiations, chosen per call:
+// SMALL (T <= kSmallT), per layer:
+//   R   x -> LDS (one coherent copy); per-token RMS scale; router logits;
+//       the shared expert's gate/up items (they need only x)
+//   --- barrier
+//   K   logits -> LDS; top-k of every token, grouping, x -> fixed-point
+//       limbs, all redundantly in every workgroup (this saves a barrier);
+//       routed gate/up tiles -> LDS; SwiGLU outputs
+//   --- barrier (meanwhile: shared and routed down rows -> LDS)
+//   D   SwiGLU limbs -> LDS; down rows + combine + shared down + residual
+//   --- barrier (meanwhile: next layer's router rows and shared items -> LDS)
+// otherwise the activations stay in global scratch and one more barrier
+// follows top-k / quantisation (one wave per token or x block).
+//
+// Barrier: per-XCD arrival counters, a global counter bumped by each XCD's
+// last arriver, per-XCD release lines written by the global last arriver.
+// Data crossing a barrier is written and read with agent-scope (sc1)
+// accesses, coherent across the XCDs' separate L2s without the whole-L2
+// writeback/invalidate of a release or acquire fence.  Before arriving, a
+// workgroup drains its own stores; the prefetch copies are issued after
+// that drain by waves 1..7 while wave 0 arrives and polls.  Every wait is
 // bounded: a workgroup that gives up raises an error flag and every
 // workgroup leaves at its next barrier, so the grid always drains.
 #pragma once
 #include "qs_kernels.h"
 #include "qs_wave.h"
+
+#define QS_LDS __attribute__((address_space(3)))
 
 namespace qs {
 
@@ -42,8 +53,9 @@ constexpr int kSpinMax = 1 << 22;
 // [144 + 16*x] release lines, [272] error flag
 constexpr int kSyncWords = 512;
 constexpr int kSyncGlobal = 128, kSyncRelease = 144, kSyncError = 272;
-constexpr int kSharedItemRows = 2;    // shared gate/up rows per item (4 waves per row)
-constexpr size_t kPfbMax = 64 * 1024; // LDS prefetch buffer upper bound
+constexpr int kSharedItemRows = 2;     // shared gate/up rows per item (4 waves per row)
+constexpr uint32_t kPfbMax = 128 * 1024;
+constexpr int kCoherent = 16;          // cache-policy bits of an agent-coherent (sc1) load
 
 struct LayerPtrs {
   const float* router;
@@ -59,9 +71,9 @@ struct LayerPtrs {
 struct PersistArgs {
   const LayerPtrs* layers;   // device array, first entry = layer0
   int n_layers, T, H, E, k, F, Fs;
-  int gq2k, prenorm, residual, small;
-  int r_et, r_tt;            // router tile: experts x tokens per unit
-  int pfb;                   // bytes of the LDS prefetch buffer
+  int gq2k, prenorm, residual;
+  int r_et, r_tt;            // router unit: experts x tokens
+  uint32_t pfb;              // bytes of the LDS prefetch buffer
   size_t gu_stride, dn_stride;
   const uint32_t* cbtab;
   const float* x_in;
@@ -70,9 +82,9 @@ struct PersistArgs {
   float* w_out;
   double* logits;            // [T][E]
   double* rinv;              // [T]
-  int32_t* ids;              // [T][k]      (T > kSmallT)
-  float* wts;                // [T][k]      (T > kSmallT)
-  uint32_t* xh;              // [T][H/4]    (T > kSmallT)
+  int32_t* ids;              // [T][k]      (not SMALL)
+  float* wts;                // [T][k]      (not SMALL)
+  uint32_t* xh;              // [T][H/4]    (not SMALL)
   uint32_t* xl;
   float* xs;                 // [T][H/16]
   int32_t* xa;
@@ -117,25 +129,64 @@ __device__ __forceinline__ uint32_t catomic_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Copy `bytes` (a multiple of 16) from global memory straight into LDS with
-// global_load_lds_dwordx4: each wave instruction moves 64 x 16 bytes to
-// consecutive LDS slots.  Completion is awaited by the next s_waitcnt(0).
-__device__ __forceinline__ void copy_to_lds(const void* g, void* lds, size_t bytes) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  const size_t n16 = bytes / 16;
-  for (size_t base = (size_t)wave * 64; base < n16; base += (size_t)nw * 64) {
+// --------------------------------------------------------- LDS loads ---
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef const QS_LDS uint8_t* lds_cptr;
+__device__ __forceinline__ uint4 ld16(lds_cptr p) {
+  const u32x4_t v = *(const QS_LDS u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld4(lds_cptr p) { return *(const QS_LDS uint32_t*)p; }
+__device__ __forceinline__ uint32_t ld2(lds_cptr p) { return *(const QS_LDS uint16_t*)p; }
+__device__ __forceinline__ uint32_t ld1(lds_cptr p) { return *p; }
+__device__ __forceinline__ float4 lds_f4(const QS_LDS float* p) {
+  const f32x4_t v = *(const QS_LDS f32x4_t*)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 lds_u4(const QS_LDS uint32_t* p) { return ld16((lds_cptr)p); }
+
+// ------------------------------------------------------ global -> LDS ---
+// Copy `bytes` (rounded up to 16) from global memory straight into LDS with
+// global_load_lds_dwordx4, spread over waves w = 0..nw-1 of the calling
+// set; each wave instruction moves 64 x 16 bytes to consecutive LDS slots.
+// AUX = kCoherent reads through to the agent-coherent level (data written by
+// other workgroups in this launch).  Completion is awaited by s_waitcnt.
+template <int AUX>
+__device__ __forceinline__ void dma_to_lds(const void* g, QS_LDS void* lds, uint32_t bytes, int w, int nw) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t n16 = (bytes + 15u) >> 4;
+  for (uint32_t base = (uint32_t)w * 64u; base < n16; base += (uint32_t)nw * 64u) {
     if (base + lane < n16)
-      __builtin_amdgcn_global_load_lds((const uint4*)g + base + lane,
-                                       (__attribute__((address_space(3))) void*)((uint4*)lds + base),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const uint4*)g + base + lane, (QS_LDS uint4*)lds + base, 16, 0,
+                                       AUX);
   }
 }
 
-// ------------------------------------------------------- grid barrier ---
-__device__ bool grid_barrier(const PersistArgs& a, uint32_t epoch) {
-  const uint32_t G = gridDim.x, x = blockIdx.x & 7u, per = G >> 3;
-  __builtin_amdgcn_s_waitcnt(0);     // coherent stores and LDS prefetches have completed
+__device__ __forceinline__ void wait_all_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+}
+
+// A whole-workgroup copy that is consumed at once: the slot is free (every
+// wave is past its previous use), copy, wait, and make it visible.
+template <class CP>
+__device__ __forceinline__ void stage_now(CP&& cp) {
+  __syncthreads();
+  cp((int)(threadIdx.x >> 6), (int)(blockDim.x >> 6));
+  wait_all_and_sync();
+}
+
+// ------------------------------------------------------- grid barrier ---
+// `pf(w, nw)` issues this workgroup's prefetch copies (waves 1..7 run it,
+// after the drain and while wave 0 waits).
+template <class PF>
+__device__ __forceinline__ bool grid_barrier(const PersistArgs& a, uint32_t epoch, PF&& pf) {
+  const uint32_t x = blockIdx.x & 7u, per = gridDim.x >> 3;
+  __builtin_amdgcn_s_waitcnt(0);     // this wave's coherent stores have completed
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (wave > 0) pf(wave - 1, nw - 1);
   int ok = 1;
   if (threadIdx.x == 0) {
     uint32_t* s = a.sync;
@@ -159,221 +210,536 @@ __device__ bool grid_barrier(const PersistArgs& a, uint32_t epoch) {
       __builtin_amdgcn_s_sleep(1);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);     // this wave's prefetch copies have landed
   return __syncthreads_and(ok);
 }
 
 // --------------------------------------------------------- LDS layout ---
-struct PersistLds {
-  uint32_t* tab;        // [8192] codebook quads (codebook gate/up only)
-  int* cnt;             // [E]
-  int* off;             // [E+1]
-  int* act;             // [E]
-  int* nact;            // [1]
-  uint32_t* mask;       // [E*8]
-  int* ids;             // [P]   expert of pair id
-  int* pairs;           // [P]   pair id at bucket position
-  int* tok_order;       // [P]   per token, positions by ascending expert
-  int* pos_of;          // [P]   bucket position of pair id
-  float* wl;            // [P]   router weight of pair id
-  float* o;             // [P*kDownRows] down outputs
-  double* red;          // [8*64] router cross-wave partials
-  float* sh;            // [T*kDownRows] shared-expert down outputs
-  float* ga;            // [T*kGateTile] SwiGLU tile, per bucket token
-  float* sred;          // [8*T*2] shared gate/up cross-wave partials
-  int* qtmp;            // [T*kGateTile] fixed-point tile values
-  uint32_t* xh;         // [T*H/4] small path: x limbs
-  uint32_t* xl;
-  float* xs;            // [T*H/16]
-  int* xa;
-  uint8_t* pfb;         // prefetch buffer
+__host__ __device__ inline uint32_t al16(uint32_t v) { return (v + 15u) & ~15u; }
+
+// SMALL activation buffer: [x fp32 T*H | logits fp64 T*E] during R and K;
+// [a limbs hi | lo | scales | sums | shared SwiGLU T*Fs] during D.
+__host__ __device__ inline uint32_t abuf_bytes(int T, int H, int E, int P, int F, int Fs) {
+  const uint32_t rk = al16((uint32_t)T * H * 4) + al16((uint32_t)T * E * 8);
+  const uint32_t dn = 2 * al16((uint32_t)P * F) + 2 * al16((uint32_t)P * F / 4) + al16((uint32_t)T * Fs * 4);
+  return rk > dn ? rk : dn;
+}
+
+struct LdsLayout {
+  uint32_t tab, cnt, off, act, nact, mask, ids, pairs, tok_order, pos_of, wl, o, red, sh, ga, sred,
+      qtmp, rinv, xh, xl, xs, xa, abuf, pfb, end;
 };
 
-template <typename LdsT>
-__host__ __device__ inline size_t carve_lds_impl(uint8_t* base, int E, int T, int P, int H,
-                                                 bool cb2, bool small, size_t pfb, LdsT* L) {
-  size_t off = 0;
-  auto take = [&](size_t n) {
-    uint8_t* r = base ? base + off : nullptr;
-    off += align_up(n, 16);
+__host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int F, int Fs, bool cb2,
+                                                bool small, uint32_t pfb) {
+  LdsLayout l;
+  uint32_t o = 0;
+  auto take = [&](uint32_t n) {
+    const uint32_t r = o;
+    o += al16(n);
     return r;
   };
-  uint8_t* tab = take(cb2 ? (size_t)kCbTabWords * 4 : 0);
-  uint8_t* cnt = take((size_t)E * 4);
-  uint8_t* offp = take((size_t)(E + 1) * 4);
-  uint8_t* act = take((size_t)E * 4);
-  uint8_t* nact = take(4);
-  uint8_t* mask = take((size_t)E * 32);
-  uint8_t* ids = take((size_t)P * 4);
-  uint8_t* pairs = take((size_t)P * 4);
-  uint8_t* tok_order = take((size_t)P * 4);
-  uint8_t* pos_of = take((size_t)P * 4);
-  uint8_t* wl = take((size_t)P * 4);
-  uint8_t* o = take((size_t)P * kDownRows * 4);
-  uint8_t* red = take(8 * 64 * 8);
-  uint8_t* sh = take((size_t)T * kDownRows * 4);
-  uint8_t* ga = take((size_t)T * kGateTile * 4);
-  uint8_t* sred = take((size_t)8 * T * 2 * 4);
-  uint8_t* qtmp = take((size_t)T * kGateTile * 4);
-  const size_t xq = small ? (size_t)T * H : 0;
-  uint8_t* xh = take(xq);          // T*H/4 dwords
-  uint8_t* xl = take(xq);
-  uint8_t* xs = take(xq / 4);      // T*H/16 floats
-  uint8_t* xa = take(xq / 4);
-  uint8_t* pf = take(pfb);
-  if (L) {
-    L->tab = (uint32_t*)tab;
-    L->cnt = (int*)cnt;
-    L->off = (int*)offp;
-    L->act = (int*)act;
-    L->nact = (int*)nact;
-    L->mask = (uint32_t*)mask;
-    L->ids = (int*)ids;
-    L->pairs = (int*)pairs;
-    L->tok_order = (int*)tok_order;
-    L->pos_of = (int*)pos_of;
-    L->wl = (float*)wl;
-    L->o = (float*)o;
-    L->red = (double*)red;
-    L->sh = (float*)sh;
-    L->ga = (float*)ga;
-    L->sred = (float*)sred;
-    L->qtmp = (int*)qtmp;
-    L->xh = (uint32_t*)xh;
-    L->xl = (uint32_t*)xl;
-    L->xs = (float*)xs;
-    L->xa = (int*)xa;
-    L->pfb = pf;
-  }
-  return off;
+  l.tab = take(cb2 ? (uint32_t)kCbTabWords * 4 : 0);
+  l.cnt = take((uint32_t)E * 4);
+  l.off = take((uint32_t)(E + 1) * 4);
+  l.act = take((uint32_t)E * 4);
+  l.nact = take(4);
+  l.mask = take((uint32_t)E * 32);
+  l.ids = take((uint32_t)P * 4);
+  l.pairs = take((uint32_t)P * 4);
+  l.tok_order = take((uint32_t)P * 4);
+  l.pos_of = take((uint32_t)P * 4);
+  l.wl = take((uint32_t)P * 4);
+  l.o = take((uint32_t)P * kDownRows * 4);
+  l.red = take(8 * 64 * 8);
+  l.sh = take((uint32_t)T * kDownRows * 4);
+  l.ga = take((uint32_t)T * kGateTile * 4);
+  l.sred = take((uint32_t)8 * T * 2 * 4);
+  l.qtmp = take((uint32_t)T * kGateTile * 4);
+  l.rinv = take((uint32_t)T * 8);
+  const uint32_t xq = small ? (uint32_t)T * H : 0;
+  l.xh = take(xq);          // T*H/4 dwords
+  l.xl = take(xq);
+  l.xs = take(xq / 4);      // T*H/16 floats
+  l.xa = take(xq / 4);
+  l.abuf = take(small ? abuf_bytes(T, H, E, P, F, Fs) : 0);
+  l.pfb = take(pfb);
+  l.end = o;
+  return l;
 }
 
-inline size_t persist_lds_bytes(int E, int T, int P, int H, bool cb2, bool small, size_t pfb) {
-  return carve_lds_impl<PersistLds>(nullptr, E, T, P, H, cb2, small, pfb, nullptr);
-}
+struct PersistLds {
+  QS_LDS uint32_t* tab;   // [8192] codebook quads (codebook gate/up only)
+  QS_LDS int* cnt;        // [E]
+  QS_LDS int* off;        // [E+1]
+  QS_LDS int* act;        // [E]
+  QS_LDS int* nact;       // [1]
+  QS_LDS uint32_t* mask;  // [E*8]
+  QS_LDS int* ids;        // [P]   expert of pair id
+  QS_LDS int* pairs;      // [P]   pair id at bucket position
+  QS_LDS int* tok_order;  // [P]   per token, positions by ascending expert
+  QS_LDS int* pos_of;     // [P]   bucket position of pair id
+  QS_LDS float* wl;       // [P]   router weight of pair id
+  QS_LDS float* o;        // [P*kDownRows] down outputs
+  QS_LDS double* red;     // [8*64] cross-wave partials
+  QS_LDS float* sh;       // [T*kDownRows] shared-expert down outputs
+  QS_LDS float* ga;       // [T*kGateTile] SwiGLU tile, per bucket token
+  QS_LDS float* sred;     // [8*T*2] shared gate/up cross-wave partials
+  QS_LDS int* qtmp;       // [T*kGateTile] fixed-point tile values
+  QS_LDS double* rinv;    // [T] per-token RMS scale
+  QS_LDS uint32_t* xh;    // [T*H/4] SMALL: x limbs
+  QS_LDS uint32_t* xl;
+  QS_LDS float* xs;       // [T*H/16]
+  QS_LDS int* xa;
+  QS_LDS uint8_t* pfb;    // weight staging buffer
+  // SMALL views into the activation buffer
+  QS_LDS float* ax;       // [T][H] x
+  QS_LDS double* lg;      // [T][E] logits
+  QS_LDS uint32_t* dah;   // [P][F/4]
+  QS_LDS uint32_t* dal;
+  QS_LDS float* das;      // [P][F/16]
+  QS_LDS int* daa;
+  QS_LDS float* dash;     // [T][Fs]
+};
 
-__device__ inline PersistLds carve_lds(uint8_t* base, const PersistArgs& a, bool cb2) {
+template <bool SMALL>
+__device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const PersistArgs& a, bool cb2) {
+  const uint32_t T = a.T, H = a.H, E = a.E, F = a.F, P = T * a.k;
+  const LdsLayout l = lds_layout(E, T, P, H, F, a.Fs, cb2, SMALL, a.pfb);
+  QS_LDS uint8_t* b = (QS_LDS uint8_t*)raw;
   PersistLds L;
-  carve_lds_impl(base, a.E, a.T, a.T * a.k, a.H, cb2, (bool)a.small, (size_t)a.pfb, &L);
+  L.tab = (QS_LDS uint32_t*)(b + l.tab);
+  L.cnt = (QS_LDS int*)(b + l.cnt);
+  L.off = (QS_LDS int*)(b + l.off);
+  L.act = (QS_LDS int*)(b + l.act);
+  L.nact = (QS_LDS int*)(b + l.nact);
+  L.mask = (QS_LDS uint32_t*)(b + l.mask);
+  L.ids = (QS_LDS int*)(b + l.ids);
+  L.pairs = (QS_LDS int*)(b + l.pairs);
+  L.tok_order = (QS_LDS int*)(b + l.tok_order);
+  L.pos_of = (QS_LDS int*)(b + l.pos_of);
+  L.wl = (QS_LDS float*)(b + l.wl);
+  L.o = (QS_LDS float*)(b + l.o);
+  L.red = (QS_LDS double*)(b + l.red);
+  L.sh = (QS_LDS float*)(b + l.sh);
+  L.ga = (QS_LDS float*)(b + l.ga);
+  L.sred = (QS_LDS float*)(b + l.sred);
+  L.qtmp = (QS_LDS int*)(b + l.qtmp);
+  L.rinv = (QS_LDS double*)(b + l.rinv);
+  L.xh = (QS_LDS uint32_t*)(b + l.xh);
+  L.xl = (QS_LDS uint32_t*)(b + l.xl);
+  L.xs = (QS_LDS float*)(b + l.xs);
+  L.xa = (QS_LDS int*)(b + l.xa);
+  L.pfb = b + l.pfb;
+  QS_LDS uint8_t* ab = b + l.abuf;
+  L.ax = (QS_LDS float*)ab;
+  L.lg = (QS_LDS double*)(ab + al16(T * H * 4));
+  L.dah = (QS_LDS uint32_t*)ab;
+  L.dal = (QS_LDS uint32_t*)(ab + al16(P * F));
+  L.das = (QS_LDS float*)(ab + 2 * al16(P * F));
+  L.daa = (QS_LDS int*)(ab + 2 * al16(P * F) + al16(P * F / 4));
+  L.dash = (QS_LDS float*)(ab + 2 * al16(P * F) + 2 * al16(P * F / 4));
   return L;
 }
 
+// ------------------------------------------------------ staging plans ---
+// Pure functions of the arguments, the workgroup index and (for routed
+// work) the active-expert count: a workgroup computes the same offsets when
+// it issues a copy and when it consumes it.  The host checks that the
+// buffer holds at least one piece of each kind next to its neighbours.
+__device__ __forceinline__ int my_count(int n) {       // items b + j*G below n
+  const int b = blockIdx.x, G = gridDim.x;
+  return b < n ? (n - 1 - b) / G + 1 : 0;
+}
+
+// router: expert group eg = b + i*G of r_et rows, staged at [0, router_bytes)
+__device__ __forceinline__ int router_groups(const PersistArgs& a) { return (a.E + a.r_et - 1) / a.r_et; }
+__device__ __forceinline__ uint32_t router_bytes(const PersistArgs& a) { return (uint32_t)a.r_et * a.H * 4; }
+
+__device__ __forceinline__ int n_shared_items(const PersistArgs& a) { return a.Fs / kSharedItemRows; }
+__device__ __forceinline__ uint32_t shared_item_bytes(const PersistArgs& a) {
+  return (uint32_t)kSharedItemRows * 2 * a.H * 2;
+}
+__device__ __forceinline__ uint32_t gu_tile_bytes(const PersistArgs& a) {
+  const uint32_t nbh = a.H / kBlockW;
+  const uint32_t sper = a.gq2k ? 16u : 4u, dper = a.gq2k ? 4u : 2u;
+  return 2u * (uint32_t)kGateTile * nbh * (64u + sper + dper);
+}
+__device__ __forceinline__ uint32_t sd_bytes(const PersistArgs& a) { return (uint32_t)kDownRows * a.Fs * 2; }
+__device__ __forceinline__ uint32_t dn_expert_bytes(const PersistArgs& a) {
+  return (uint32_t)kDownRows * (a.F / kBlockW) * kQ2KBytes;
+}
+
+// shared items: SMALL after the router rows; otherwise at 0 with room for one tile
+template <bool SMALL>
+__device__ __forceinline__ uint32_t shared_off(const PersistArgs& a) {
+  return SMALL ? al16(router_bytes(a)) : 0;
+}
+template <bool SMALL>
+__device__ __forceinline__ int shared_pf_count(const PersistArgs& a) {
+  const uint32_t off = shared_off<SMALL>(a), reserve = SMALL ? 0 : gu_tile_bytes(a);
+  const int fit = a.pfb > off + reserve ? (int)((a.pfb - off - reserve) / shared_item_bytes(a)) : 0;
+  const int mine = my_count(n_shared_items(a));
+  return mine < fit ? mine : fit;
+}
+
+// routed gate/up tiles: SMALL at 0; otherwise after the shared items
+template <bool SMALL>
+__device__ __forceinline__ int gu_items_base(const PersistArgs& a) { return SMALL ? 0 : n_shared_items(a); }
+template <bool SMALL>
+__device__ __forceinline__ uint32_t tile_off(const PersistArgs& a) {
+  return SMALL ? 0 : shared_off<SMALL>(a) + shared_pf_count<SMALL>(a) * shared_item_bytes(a);
+}
+template <bool SMALL>
+__device__ __forceinline__ int tile_pf_count(const PersistArgs& a, int na) {
+  const uint32_t off = tile_off<SMALL>(a);
+  const int fit = a.pfb > off ? (int)((a.pfb - off) / gu_tile_bytes(a)) : 0;
+  const int base = gu_items_base<SMALL>(a);
+  const int mine = my_count(base + na * (a.F / kGateTile)) - my_count(base);
+  return mine < fit ? mine : fit;
+}
+
+// down: [shared rows | a chunk of experts' rows]; the first chunk of the
+// first tile is copied during the barrier
+__device__ __forceinline__ int down_chunk(const PersistArgs& a) {
+  const uint32_t fixed = al16(sd_bytes(a));
+  return a.pfb > fixed ? (int)((a.pfb - fixed) / dn_expert_bytes(a)) : 0;
+}
+__device__ __forceinline__ int down_pf_count(const PersistArgs& a, int na) {
+  if ((int)blockIdx.x * kDownRows >= a.H) return 0;
+  const int fit = down_chunk(a);
+  return na < fit ? na : fit;
+}
+
+// ------------------------------------------------------ copy issuers ---
+__device__ __forceinline__ void copy_router_rows(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int eg,
+                                                 int w, int nw) {
+  const int e0 = eg * a.r_et;
+  const int ne = a.E - e0 < a.r_et ? a.E - e0 : a.r_et;
+  dma_to_lds<0>(Lp.router + (size_t)e0 * a.H, L.pfb, (uint32_t)ne * a.H * 4, w, nw);
+}
+
+__device__ __forceinline__ void copy_shared_item(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
+                                                 int item, int w, int nw) {
+  const uint32_t row = (uint32_t)a.H * 2;
+  for (int r = 0; r < kSharedItemRows; ++r) {
+    const int f = item * kSharedItemRows + r;
+    dma_to_lds<0>(Lp.sg + (size_t)f * a.H, dst + (2 * r) * row, row, w, nw);
+    dma_to_lds<0>(Lp.su + (size_t)f * a.H, dst + (2 * r + 1) * row, row, w, nw);
+  }
+}
+
+// Routed gate/up tile (expert e, rows f0..f0+15) in LDS as
+// [gate codes | up codes | gate scales | up scales | gate d | up d].
+struct TileLds {
+  uint32_t qb, sb, db, s, d;
+};
+__device__ __forceinline__ TileLds tile_lds(const PersistArgs& a) {
+  TileLds t;
+  const uint32_t nbh = a.H / kBlockW;
+  t.qb = (uint32_t)kGateTile * nbh * 64;
+  t.sb = (uint32_t)kGateTile * nbh * (a.gq2k ? 16u : 4u);
+  t.db = (uint32_t)kGateTile * nbh * (a.gq2k ? 4u : 2u);
+  t.s = 2 * t.qb;
+  t.d = 2 * t.qb + 2 * t.sb;
+  return t;
+}
+
+__device__ __forceinline__ void copy_tile(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int e,
+                                          int f0, int w, int nw) {
+  const uint32_t nbh = a.H / kBlockW;
+  const size_t nblk = (size_t)a.F * nbh;
+  const MatPlanes pl = a.gq2k ? q2k_planes(nblk) : cb2_planes(nblk);
+  const uint32_t sper = a.gq2k ? 16u : 4u, dper = a.gq2k ? 4u : 2u;
+  const TileLds tl = tile_lds(a);
+  const size_t b0 = (size_t)f0 * nbh;
+  for (int m = 0; m < 2; ++m) {
+    const uint8_t* src = (m ? Lp.up : Lp.gate) + (size_t)e * a.gu_stride;
+    dma_to_lds<0>(src + pl.q + b0 * 64, dst + m * tl.qb, tl.qb, w, nw);
+    dma_to_lds<0>(src + pl.s + b0 * sper, dst + tl.s + m * tl.sb, tl.sb, w, nw);
+    dma_to_lds<0>(src + pl.d + b0 * dper, dst + tl.d + m * tl.db, tl.db, w, nw);
+  }
+}
+
+// Routed down rows r0..r0+7 of expert e as [codes 8*nb*64 | scales 8*nb*16 | d,dmin 8*nb*4].
+__device__ __forceinline__ void copy_down_rows(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
+                                               int e, int r0, int w, int nw) {
+  const uint32_t nb = a.F / kBlockW;
+  const MatPlanes pl = q2k_planes((size_t)a.H * nb);
+  const uint8_t* base = Lp.down + (size_t)e * a.dn_stride;
+  const size_t b0 = (size_t)r0 * nb;
+  dma_to_lds<0>(base + pl.q + b0 * 64, dst, kDownRows * nb * 64, w, nw);
+  dma_to_lds<0>(base + pl.s + b0 * 16, dst + kDownRows * nb * 64, kDownRows * nb * 16, w, nw);
+  dma_to_lds<0>(base + pl.d + b0 * 4, dst + kDownRows * nb * 80, kDownRows * nb * 4, w, nw);
+}
+
+__device__ __forceinline__ void copy_sd_rows(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int r0,
+                                             int w, int nw) {
+  if (a.Fs) dma_to_lds<0>(Lp.sd + (size_t)r0 * a.Fs, L.pfb, sd_bytes(a), w, nw);
+}
+
+// prefetches issued during barriers
+template <bool SMALL>
+__device__ __forceinline__ void pf_router_and_shared(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L,
+                                                     int w, int nw) {
+  if ((int)blockIdx.x < router_groups(a)) copy_router_rows(a, Lp, L, blockIdx.x, w, nw);
+  if (SMALL) {
+    const int n = shared_pf_count<true>(a);
+    for (int j = 0; j < n; ++j)
+      copy_shared_item(a, Lp, L.pfb + shared_off<true>(a) + (uint32_t)j * shared_item_bytes(a),
+                       (int)blockIdx.x + j * (int)gridDim.x, w, nw);
+  }
+}
+
+__device__ __forceinline__ void pf_shared_items(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int w,
+                                                int nw) {
+  const int n = shared_pf_count<false>(a);
+  for (int j = 0; j < n; ++j)
+    copy_shared_item(a, Lp, L.pfb + (uint32_t)j * shared_item_bytes(a), (int)blockIdx.x + j * (int)gridDim.x, w,
+                     nw);
+}
+
+template <bool SMALL>
+__device__ __forceinline__ void pf_tiles(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
+  const int na = *L.nact, tiles = a.F / kGateTile, base = gu_items_base<SMALL>(a);
+  const int n = tile_pf_count<SMALL>(a, na), j0 = my_count(base);
+  for (int j = 0; j < n; ++j) {
+    const int r = (int)blockIdx.x + (j0 + j) * (int)gridDim.x - base;
+    copy_tile(a, Lp, L.pfb + tile_off<SMALL>(a) + (uint32_t)j * gu_tile_bytes(a), L.act[r / tiles],
+              (r % tiles) * kGateTile, w, nw);
+  }
+}
+
+__device__ __forceinline__ void pf_down(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
+  const int r0 = blockIdx.x * kDownRows;
+  if (r0 >= a.H) return;
+  copy_sd_rows(a, Lp, L, r0, w, nw);
+  const int n = down_pf_count(a, *L.nact);
+  for (int u = 0; u < n; ++u)
+    copy_down_rows(a, Lp, L.pfb + al16(sd_bytes(a)) + (uint32_t)u * dn_expert_bytes(a), L.act[u], r0, w, nw);
+}
+
 // ------------------------------------------------------------ phase R ---
-// Unit = (ET experts, TT tokens); the 8 waves split H into slices of H/8.
-// The router rows of this workgroup's first unit are prefetched into the
-// LDS buffer as [ET][H] floats when they fit.
-__device__ __forceinline__ bool router_pf_fits(const PersistArgs& a) {
-  return (size_t)a.r_et * a.H * 4 <= (size_t)a.pfb;
+__device__ __forceinline__ double sumsq_part(float4 v, double s) {
+  s = fma((double)v.x, (double)v.x, s);
+  s = fma((double)v.y, (double)v.y, s);
+  s = fma((double)v.z, (double)v.z, s);
+  s = fma((double)v.w, (double)v.w, s);
+  return s;
 }
 
-__device__ void router_prefetch(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L) {
-  const int ET = a.r_et, TT = a.r_tt;
-  const int ntt = (a.T + TT - 1) / TT, net = (a.E + ET - 1) / ET;
-  if ((int)blockIdx.x >= net * ntt || !router_pf_fits(a)) return;
-  const int e0 = ((int)blockIdx.x / ntt) * ET;
-  const int ne = a.E - e0 < ET ? a.E - e0 : ET;
-  copy_to_lds(Lp.router + (size_t)e0 * a.H, L.pfb, (size_t)ne * a.H * 4);
+__device__ __forceinline__ double rms_inv_of(double q, int H) { return 1.0 / sqrt(q / (double)H + kRmsEps); }
+
+template <bool SMALL>
+__device__ __forceinline__ float4 x_f4(const PersistArgs& a, const PersistLds& L, const float* x, int t, int h) {
+  if (SMALL) return lds_f4(L.ax + t * a.H + h);
+  return cldf4(x + (size_t)t * a.H + h);
 }
 
-__device__ void phase_router(const PersistArgs& a, const LayerPtrs& Lp, const float* x, PersistLds& L) {
+// Per-token RMS scales of tokens t0..t0+n-1 into LDS: wave w covers
+// [w*H/8, (w+1)*H/8) with lane stride 4, fp64 FMAs in order, a butterfly,
+// then the waves in order -- the same order phase_router uses, so the scale
+// is the same for every batch size.
+template <bool SMALL>
+__device__ __forceinline__ void token_rinv(const PersistArgs& a, PersistLds& L, const float* x, int t0, int n) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int hw = a.H / nw;
+  for (int j = 0; j < n; ++j) {
+    double s = 0.0;
+#pragma unroll 1
+    for (int h = wave * hw + 4 * lane; h < (wave + 1) * hw; h += 256) s = sumsq_part(x_f4<SMALL>(a, L, x, t0 + j, h), s);
+    s = bfly_sum_f64<6>(s);
+    if (lane == 0) L.red[wave * 4 + j] = s;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < n) {
+    double q = 0.0;
+    for (int w = 0; w < nw; ++w) q += L.red[w * 4 + threadIdx.x];
+    L.rinv[t0 + threadIdx.x] = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
+  }
+  __syncthreads();
+}
+
+// Router: this workgroup's expert groups (rows in LDS) against every token
+// group.  Otherwise-flow workgroups also sum x^2 of the tokens they route
+// (same order as token_rinv); the owner of expert group 0 publishes the
+// RMS scales.
+template <bool SMALL>
+__device__ __forceinline__ void phase_router(const PersistArgs& a, const LayerPtrs& Lp, const float* x,
+                                             PersistLds& L) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const int ET = a.r_et, TT = a.r_tt;
-  const int net = (a.E + ET - 1) / ET, ntt = (a.T + TT - 1) / TT;
-  const int hw = a.H / nw;                     // elements per wave (multiple of 32)
+  const int ntt = (a.T + TT - 1) / TT;
+  const int hw = a.H / nw;
   const int V = ET * TT + TT;
-  const float* pfr = (const float*)L.pfb;
-  for (int u = blockIdx.x; u < net * ntt; u += gridDim.x) {
-    const int e0 = (u / ntt) * ET, t0 = (u % ntt) * TT;
-    const bool from_lds = u == (int)blockIdx.x && router_pf_fits(a);
-    double acc[4][4], ss[4];
+  const bool want_ss = !SMALL && a.prenorm;
+  const QS_LDS float* wr = (const QS_LDS float*)L.pfb;
+  int i = 0;
+  for (int eg = blockIdx.x; eg < router_groups(a); eg += gridDim.x, ++i) {
+    if (i > 0) stage_now([&](int w, int n) { copy_router_rows(a, Lp, L, eg, w, n); });
+    const int e0 = eg * ET;
+#pragma unroll 1
+    for (int tg = 0; tg < ntt; ++tg) {
+      const int t0 = tg * TT, nt = a.T - t0 < TT ? a.T - t0 : TT;
+      double acc[4][4], ss[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ss[i] = 0.0;
+      for (int ii = 0; ii < 4; ++ii) {
+        ss[ii] = 0.0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+        for (int j = 0; j < 4; ++j) acc[ii][j] = 0.0;
+      }
+#pragma unroll 1
+      for (int h = wave * hw + 4 * lane; h < (wave + 1) * hw; h += 256) {
+        float4 xv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xv[j] = j < nt ? x_f4<SMALL>(a, L, x, t0 + j, h) : make_float4(0, 0, 0, 0);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          if (ii >= ET || e0 + ii >= a.E) continue;
+          const float4 w = lds_f4(wr + ii * a.H + h);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[ii][j] = fma((double)w.x, (double)xv[j].x, acc[ii][j]);
+            acc[ii][j] = fma((double)w.y, (double)xv[j].y, acc[ii][j]);
+            acc[ii][j] = fma((double)w.z, (double)xv[j].z, acc[ii][j]);
+            acc[ii][j] = fma((double)w.w, (double)xv[j].w, acc[ii][j]);
+          }
+        }
+        if (want_ss) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ss[j] = sumsq_part(xv[j], ss[j]);
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (ii < ET && j < TT) {
+            const double s = bfly_sum_f64<6>(acc[ii][j]);
+            if (lane == 0) L.red[32 + wave * V + ii * TT + j] = s;
+          }
+      if (want_ss) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j < TT) {
+            const double s = bfly_sum_f64<6>(ss[j]);
+            if (lane == 0) L.red[32 + wave * V + ET * TT + j] = s;
+          }
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < ET * TT) {
+        const int ii = threadIdx.x / TT, j = threadIdx.x % TT;
+        const int e = e0 + ii, t = t0 + j;
+        if (e < a.E && j < nt) {
+          double s = 0.0, q = 0.0;
+          for (int w = 0; w < nw; ++w) {
+            s += L.red[32 + w * V + ii * TT + j];
+            if (want_ss) q += L.red[32 + w * V + ET * TT + j];
+          }
+          double r;
+          if (SMALL) r = L.rinv[t];
+          else r = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
+          const double b = (double)Lp.bias[e];
+          cstd(&a.logits[(size_t)t * a.E + e], a.prenorm ? fma(s, r, b) : s + b);
+          if (!SMALL && e == 0) cstd(&a.rinv[t], r);
+        }
+      }
+      __syncthreads();
     }
-    for (int h = wave * hw + 4 * lane; h < (wave + 1) * hw; h += 256) {
-      float4 xv[4];
+  }
+}
+
+// ------------------------------------------------- shared gate/up item ---
+// Rows [2*item, 2*item+2) from LDS ([row][gate, up][H] bf16), 4 waves per
+// row, each over a quarter of H; fp32 FMA.
+template <bool SMALL>
+__device__ __forceinline__ void shared_gu_item(const PersistArgs& a, lds_cptr wbase, const float* x, int item,
+                                               PersistLds& L) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rw = wave >> 2, qtr = wave & 3;
+  const int hq = a.H / 4;
+  const int T = a.T;
+  const uint32_t row = (uint32_t)a.H * 2;
+  lds_cptr gsrc = wbase + (2 * rw) * row;
+  lds_cptr usrc = wbase + (2 * rw + 1) * row;
+#pragma unroll 1
+  for (int t = 0; t < T; ++t) {
+    float g = 0.f, u = 0.f;
+#pragma unroll 1
+    for (int h = qtr * hq + 8 * lane; h < (qtr + 1) * hq; h += 512) {
+      const uint4 wg = ld16(gsrc + h * 2), wu = ld16(usrc + h * 2);
+      const float4 x0 = x_f4<SMALL>(a, L, x, t, h), x1 = x_f4<SMALL>(a, L, x, t, h + 4);
+      const uint32_t gw[4] = {wg.x, wg.y, wg.z, wg.w}, uw[4] = {wu.x, wu.y, wu.z, wu.w};
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xv[j] = (j < TT && t0 + j < a.T) ? cldf4(x + (size_t)(t0 + j) * a.H + h) : make_float4(0, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i >= ET || e0 + i >= a.E) continue;
-        const float4 w = from_lds ? *(const float4*)(pfr + (size_t)i * a.H + h)
-                                  : *(const float4*)(Lp.router + (size_t)(e0 + i) * a.H + h);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j >= TT) continue;
-          acc[i][j] = fma((double)w.x, (double)xv[j].x, acc[i][j]);
-          acc[i][j] = fma((double)w.y, (double)xv[j].y, acc[i][j]);
-          acc[i][j] = fma((double)w.z, (double)xv[j].z, acc[i][j]);
-          acc[i][j] = fma((double)w.w, (double)xv[j].w, acc[i][j]);
-        }
-      }
-      if (a.prenorm) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j >= TT) continue;
-          ss[j] = fma((double)xv[j].x, (double)xv[j].x, ss[j]);
-          ss[j] = fma((double)xv[j].y, (double)xv[j].y, ss[j]);
-          ss[j] = fma((double)xv[j].z, (double)xv[j].z, ss[j]);
-          ss[j] = fma((double)xv[j].w, (double)xv[j].w, ss[j]);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (i < ET && j < TT) {
-          const double s = bfly_sum_f64<6>(acc[i][j]);
-          if (lane == 0) L.red[wave * V + i * TT + j] = s;
-        }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j < TT) {
-        const double s = bfly_sum_f64<6>(ss[j]);
-        if (lane == 0) L.red[wave * V + ET * TT + j] = s;
-      }
-    __syncthreads();
-    if ((int)threadIdx.x < ET * TT) {
-      const int i = threadIdx.x / TT, j = threadIdx.x % TT;
-      const int e = e0 + i, t = t0 + j;
-      if (e < a.E && t < a.T) {
-        double s = 0.0, q = 0.0;
-        for (int w = 0; w < nw; ++w) {
-          s += L.red[w * V + i * TT + j];
-          q += L.red[w * V + ET * TT + j];
-        }
-        double r = 1.0;
-        if (a.prenorm) r = 1.0 / sqrt(q / (double)a.H + kRmsEps);
-        const double b = (double)Lp.bias[e];
-        cstd(&a.logits[(size_t)t * a.E + e], a.prenorm ? fma(s, r, b) : s + b);
-        if (e == 0) cstd(&a.rinv[t], r);
+      for (int c = 0; c < 4; ++c) {
+        g = fmaf(bf16_to_f32(gw[c] & 0xFFFFu), xv[2 * c], g);
+        g = fmaf(bf16_to_f32(gw[c] >> 16), xv[2 * c + 1], g);
+        u = fmaf(bf16_to_f32(uw[c] & 0xFFFFu), xv[2 * c], u);
+        u = fmaf(bf16_to_f32(uw[c] >> 16), xv[2 * c + 1], u);
       }
     }
-    __syncthreads();
+    g = bfly_sum<6>(g);
+    u = bfly_sum<6>(u);
+    if (lane == 0) {
+      L.sred[(wave * T + t) * 2] = g;
+      L.sred[(wave * T + t) * 2 + 1] = u;
+    }
+  }
+  __syncthreads();
+  // combine the 4 quarter-row partials in a fixed order
+  for (int q = threadIdx.x; q < kSharedItemRows * T; q += blockDim.x) {
+    const int r = q / T, t = q % T;
+    const int ff = item * kSharedItemRows + r;
+    float g = 0.f, u = 0.f;
+    for (int w4 = 0; w4 < 4; ++w4) {
+      g += L.sred[((r * 4 + w4) * T + t) * 2];
+      u += L.sred[((r * 4 + w4) * T + t) * 2 + 1];
+    }
+    const float rs = SMALL ? (float)L.rinv[t] : (float)cldd(&a.rinv[t]);
+    cstf(&a.ash[(size_t)t * a.Fs + ff], silu_mul(g * rs, u * rs));
+  }
+  __syncthreads();
+}
+
+template <bool SMALL>
+__device__ __forceinline__ void shared_items(const PersistArgs& a, const LayerPtrs& Lp, const float* x,
+                                             PersistLds& L) {
+  const int npf = shared_pf_count<SMALL>(a);
+  const uint32_t off = shared_off<SMALL>(a), item_b = shared_item_bytes(a);
+  int j = 0;
+  for (int it = blockIdx.x; it < n_shared_items(a); it += gridDim.x, ++j) {
+    uint32_t slot = off + (uint32_t)j * item_b;
+    if (j >= npf) {      // not prefetched: copy into the first slot (already consumed)
+      slot = off;
+      stage_now([&](int w, int n) { copy_shared_item(a, Lp, L.pfb + off, it, w, n); });
+    }
+    shared_gu_item<SMALL>(a, L.pfb + slot, x, it, L);
   }
 }
 
 // ------------------------------------------------------------ phase K ---
 // Top-k of token t by one wave: (logit desc, index asc), weights are the
-// softmax over the k picks.  Results go to LDS (small path, every
-// workgroup) or to global scratch (one wave per token); workgroup 0 / the
-// token's wave also writes the caller's ids_out / w_out.
-__device__ void topk_wave(const PersistArgs& a, int t, int layer_i, PersistLds* L, bool write_out) {
+// softmax over the k picks.  SMALL: logits from LDS, results into LDS (every
+// workgroup); otherwise logits and results in global scratch (one wave per
+// token).  Workgroup 0 / the token's wave also writes ids_out / w_out.
+template <bool SMALL>
+__device__ __forceinline__ void topk_wave(const PersistArgs& a, int t, int layer_i, PersistLds& L, bool write_out) {
   const int lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
   double v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    const double l = e < E ? cldd(&a.logits[(size_t)t * E + e]) : 0.0;
+    double l = 0.0;
+    if (e < E) l = SMALL ? L.lg[t * E + e] : cldd(&a.logits[(size_t)t * E + e]);
     v[i] = l != l ? -INFINITY : l;     // NaN ranks last; every pick stays valid and distinct
   }
   uint32_t taken = 0;
   double top0 = 0.0, selv = 0.0;
   int seli = 0;
+#pragma unroll 1
   for (int j = 0; j < k; ++j) {
     double bv = -INFINITY;
     int bi = 0x7FFFFFFF;
@@ -397,9 +763,9 @@ __device__ void topk_wave(const PersistArgs& a, int t, int layer_i, PersistLds* 
   const double sum = bfly_sum_f64<6>(z);
   if (lane < k) {
     const float w = (float)(z / sum);
-    if (L) {
-      L->ids[t * k + lane] = seli;
-      L->wl[t * k + lane] = w;
+    if (SMALL) {
+      L.ids[t * k + lane] = seli;
+      L.wl[t * k + lane] = w;
     } else {
       csti(&a.ids[t * k + lane], seli);
       cstf(&a.wts[t * k + lane], w);
@@ -412,12 +778,13 @@ __device__ void topk_wave(const PersistArgs& a, int t, int layer_i, PersistLds* 
   }
 }
 
-// x block b (256 elements) of token t -> limbs, one wave; into LDS when
-// `L` is given, else into global scratch.
-__device__ void quant_x_wave(const PersistArgs& a, const float* x, int t, int b, PersistLds* L) {
+// x block b (256 elements) of token t -> limbs, one wave.  SMALL: from and
+// into LDS; otherwise global scratch.
+template <bool SMALL>
+__device__ __forceinline__ void quant_x_wave(const PersistArgs& a, const float* x, int t, int b, PersistLds& L) {
   const int lane = threadIdx.x & 63;
-  const float4 v = cldf4(x + (size_t)t * a.H + b * kBlockW + 4 * lane);
-  const float r = (float)cldd(&a.rinv[t]);
+  const float4 v = x_f4<SMALL>(a, L, x, t, b * kBlockW + 4 * lane);
+  const float r = SMALL ? (float)L.rinv[t] : (float)cldd(&a.rinv[t]);
   const float m = bfly_max<6>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   const int e = fixed_exp(m);
   const int q0 = to_fixed(v.x, e), q1 = to_fixed(v.y, e), q2 = to_fixed(v.z, e), q3 = to_fixed(v.w, e);
@@ -451,12 +818,12 @@ __device__ void quant_x_wave(const PersistArgs& a, const float* x, int t, int b,
   const float scale = ldexpf(r, e - kFixedBits);
   const size_t base = (size_t)t * (a.H / 4) + b * 64;
   const size_t si = (size_t)t * (a.H / kSubW) + b * 16 + (lane >> 2);
-  if (L) {
-    L->xh[base + lane] = ph;
-    L->xl[base + lane] = pl;
+  if (SMALL) {
+    L.xh[base + lane] = ph;
+    L.xl[base + lane] = pl;
     if ((lane & 3) == 0) {
-      L->xs[si] = scale;
-      L->xa[si] = s;
+      L.xs[si] = scale;
+      L.xa[si] = s;
     }
   } else {
     cst(&a.xh[base + lane], ph);
@@ -468,38 +835,15 @@ __device__ void quant_x_wave(const PersistArgs& a, const float* x, int t, int b,
   }
 }
 
-// T > kSmallT: one wave per token (top-k) and per x block (limbs), global.
-__device__ void phase_topk_quant(const PersistArgs& a, const float* x, int layer_i) {
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
-  const int nb = a.H / kBlockW;
-  const int units = a.T + a.T * nb;
-  for (int u = blockIdx.x * nw + wave; u < units; u += gridDim.x * nw) {
-    if (u < a.T) topk_wave(a, u, layer_i, nullptr, true);
-    else quant_x_wave(a, x, (u - a.T) / nb, (u - a.T) % nb, nullptr);
-  }
-}
-
-// T <= kSmallT: every workgroup routes all tokens and quantises all of x
-// into its own LDS.
-__device__ void local_topk_quant(const PersistArgs& a, const float* x, int layer_i, PersistLds& L) {
-  const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
-  const int nb = a.H / kBlockW;
-  const int units = a.T + a.T * nb;
-  for (int u = wave; u < units; u += nw) {
-    if (u < a.T) topk_wave(a, u, layer_i, &L, blockIdx.x == 0);
-    else quant_x_wave(a, x, (u - a.T) / nb, (u - a.T) % nb, &L);
-  }
-  __syncthreads();
-}
-
 // ------------------------------------------------------ grouping (LDS) ---
 // Stable bucket sort of (token, slot) pairs by expert.
-__device__ void build_groups(const PersistArgs& a, PersistLds& L) {
+template <bool SMALL>
+__device__ __forceinline__ void build_groups(const PersistArgs& a, PersistLds& L) {
   const int tid = threadIdx.x, nt = blockDim.x, E = a.E, k = a.k, T = a.T, P = T * k;
   const int wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < E; i += nt) L.cnt[i] = 0;
   for (int i = tid; i < E * 8; i += nt) L.mask[i] = 0;
-  if (!a.small) {
+  if (!SMALL) {
     for (int p = tid; p < P; p += nt) {
       L.ids[p] = cldi(&a.ids[p]);
       L.wl[p] = cldf(&a.wts[p]);
@@ -508,13 +852,14 @@ __device__ void build_groups(const PersistArgs& a, PersistLds& L) {
   __syncthreads();
   for (int p = tid; p < P; p += nt) {
     const int e = valid_id(L.ids[p], E), t = p / k;
-    atomicAdd(&L.cnt[e], 1);
-    atomicOr(&L.mask[e * 8 + (t >> 5)], 1u << (t & 31));
+    __hip_atomic_fetch_add(&L.cnt[e], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_or(&L.mask[e * 8 + (t >> 5)], 1u << (t & 31), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
   // exclusive scans of counts and of the non-empty flags, 64 experts per wave
-  // and pass, wave totals combined through LDS (E <= 1024)
-  int* wsum = (int*)L.red;              // [2 * 16] chunk totals (router scratch is free here)
+  // and pass, chunk totals combined through LDS (E <= 1024)
+  QS_LDS int* wsum = (QS_LDS int*)L.red;   // [2 * 16] chunk totals
   const int nchunk = (E + 63) / 64;
   for (int c = wave; c < nchunk; c += nt / 64) {
     const int e = c * 64 + lane;
@@ -569,17 +914,16 @@ __device__ void build_groups(const PersistArgs& a, PersistLds& L) {
 }
 
 // ----------------------------------------------------------- phase GU ---
+template <bool SMALL>
 __device__ __forceinline__ void x_chunk(const PersistArgs& a, const PersistLds& L, int t, int ch,
                                         uint32_t (&xh)[16], uint32_t (&xl)[16], float (&xs)[4],
                                         int (&xa)[4]) {
   const size_t xo = (size_t)t * (a.H / 4) + ch * 16;
   const size_t si = (size_t)t * (a.H / kSubW) + ch * 4;
-  if (a.small) {
-    const uint4* ph = (const uint4*)(L.xh + xo);
-    const uint4* pl = (const uint4*)(L.xl + xo);
+  if (SMALL) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 h = ph[i], l = pl[i];
+      const uint4 h = lds_u4(L.xh + xo + 4 * i), l = lds_u4(L.xl + xo + 4 * i);
       xh[4 * i] = h.x; xh[4 * i + 1] = h.y; xh[4 * i + 2] = h.z; xh[4 * i + 3] = h.w;
       xl[4 * i] = l.x; xl[4 * i + 1] = l.y; xl[4 * i + 2] = l.z; xl[4 * i + 3] = l.w;
     }
@@ -605,121 +949,56 @@ __device__ __forceinline__ void x_chunk(const PersistArgs& a, const PersistLds& 
   }
 }
 
-// Shared-expert gate/up item: rows [2*item, 2*item+2), 4 waves per row, each
-// over a quarter of H; fp32 FMA on bf16 weights.  The first item of a
-// workgroup has its rows in the LDS buffer as [row][gate, up][H] bf16.
-__device__ __forceinline__ bool shared_pf_fits(const PersistArgs& a) {
-  return (size_t)kSharedItemRows * 2 * a.H * 2 <= (size_t)a.pfb;
-}
-
-__device__ void shared_gu_prefetch(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L) {
-  const int n_shared = a.Fs / kSharedItemRows;
-  if ((int)blockIdx.x >= n_shared || !shared_pf_fits(a)) return;
-  for (int r = 0; r < kSharedItemRows; ++r) {
-    const int f = blockIdx.x * kSharedItemRows + r;
-    copy_to_lds(Lp.sg + (size_t)f * a.H, L.pfb + (size_t)(2 * r) * a.H * 2, (size_t)a.H * 2);
-    copy_to_lds(Lp.su + (size_t)f * a.H, L.pfb + (size_t)(2 * r + 1) * a.H * 2, (size_t)a.H * 2);
-  }
-}
-
-__device__ void shared_gu_item(const PersistArgs& a, const LayerPtrs& Lp, const float* x, int item,
-                               PersistLds& L) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rw = wave >> 2, qtr = wave & 3;
-  const int f = item * kSharedItemRows + rw;
-  const int hq = a.H / 4;
-  const int T = a.T;
-  const bool from_lds = item == (int)blockIdx.x && shared_pf_fits(a);
-  const uint16_t* gsrc = from_lds ? (const uint16_t*)(L.pfb + (size_t)(2 * rw) * a.H * 2) : Lp.sg + (size_t)f * a.H;
-  const uint16_t* usrc = from_lds ? (const uint16_t*)(L.pfb + (size_t)(2 * rw + 1) * a.H * 2) : Lp.su + (size_t)f * a.H;
-  for (int t = 0; t < T; ++t) {
-    float g = 0.f, u = 0.f;
-    for (int h = qtr * hq + 8 * lane; h < (qtr + 1) * hq; h += 512) {
-      const uint4 wg = *(const uint4*)(gsrc + h), wu = *(const uint4*)(usrc + h);
-      const float4 x0 = cldf4(x + (size_t)t * a.H + h), x1 = cldf4(x + (size_t)t * a.H + h + 4);
-      const uint32_t gw[4] = {wg.x, wg.y, wg.z, wg.w}, uw[4] = {wu.x, wu.y, wu.z, wu.w};
-      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        g = fmaf(bf16_to_f32(gw[c] & 0xFFFFu), xv[2 * c], g);
-        g = fmaf(bf16_to_f32(gw[c] >> 16), xv[2 * c + 1], g);
-        u = fmaf(bf16_to_f32(uw[c] & 0xFFFFu), xv[2 * c], u);
-        u = fmaf(bf16_to_f32(uw[c] >> 16), xv[2 * c + 1], u);
-      }
-    }
-    g = bfly_sum<6>(g);
-    u = bfly_sum<6>(u);
-    if (lane == 0) {
-      L.sred[(wave * T + t) * 2] = g;
-      L.sred[(wave * T + t) * 2 + 1] = u;
-    }
-  }
-  __syncthreads();
-  // combine the 4 quarter-row partials in a fixed order
-  for (int q = threadIdx.x; q < kSharedItemRows * T; q += blockDim.x) {
-    const int r = q / T, t = q % T;
-    const int ff = item * kSharedItemRows + r;
-    float g = 0.f, u = 0.f;
-    for (int w4 = 0; w4 < 4; ++w4) {
-      g += L.sred[((r * 4 + w4) * T + t) * 2];
-      u += L.sred[((r * 4 + w4) * T + t) * 2 + 1];
-    }
-    const float rs = (float)cldd(&a.rinv[t]);
-    cstf(&a.ash[(size_t)t * a.Fs + ff], silu_mul(g * rs, u * rs));
-  }
-  __syncthreads();
-}
-
-// Routed gate/up tile: rows [16*tile, +16) of expert act[u] for every token
-// of its bucket, four tokens per pass over the decoded weights.
-template <int FMT>
-__device__ void routed_gu_tile(const PersistArgs& a, const LayerPtrs& Lp, int u, int tile,
-                               PersistLds& L) {
-  const int e = L.act[u];
+// Routed gate/up tile from LDS: rows [f0, f0+16) of expert e for every
+// token of its bucket; each 64-weight chunk is decoded once and applied to
+// the tokens one at a time.  SwiGLU outputs are quantised per 16 rows.
+template <int FMT, bool SMALL>
+__device__ __forceinline__ void routed_gu_tile(const PersistArgs& a, lds_cptr tile, int e, int f0, PersistLds& L) {
   const int p0 = L.off[e], n = L.off[e + 1] - p0;
+  const int nbh = a.H / kBlockW;
   const int nch = a.H / kChunkW;
   const int lpr = lanes_per_row(nch);
   const int cpl = nch / lpr;
   const int slots = blockDim.x / lpr;
   const int slot = threadIdx.x / lpr, j = threadIdx.x % lpr;
-  const size_t nblk = (size_t)a.F * (a.H / kBlockW);
   constexpr bool q2k = FMT == 1;
-  const MatPlanes pl = q2k ? q2k_planes(nblk) : cb2_planes(nblk);
-  const uint8_t* gbase = Lp.gate + (size_t)e * a.gu_stride;
-  const uint8_t* ubase = Lp.up + (size_t)e * a.gu_stride;
-  const int f0 = tile * kGateTile;
+  const TileLds tl = tile_lds(a);
+  lds_cptr gq = tile, uq_ = tile + tl.qb, gs = tile + tl.s, us = tile + tl.s + tl.sb, gd = tile + tl.d,
+           ud = tile + tl.d + tl.db;
+#pragma unroll 1
   for (int r = slot; r < kGateTile; r += slots) {
-    const int f = f0 + r;
+#pragma unroll 1
     for (int tg = 0; tg < n; tg += 4) {
       float gacc[4] = {0.f, 0.f, 0.f, 0.f}, uacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
       for (int cc = 0; cc < cpl; ++cc) {
         const int ch = j + cc * lpr;
-        const size_t blk = (size_t)f * (a.H / kBlockW) + ch / 4;
+        const uint32_t blk = (uint32_t)r * nbh + ch / 4;
         const int c = ch & 3;
-        uint32_t gq[16], uq[16];
+        uint32_t gw[16], uw[16];
         uint32_t gsc, usc, gdd, udd;
-        const uint4 gv = *(const uint4*)(gbase + pl.q + blk * 64 + c * 16);
-        const uint4 uv = *(const uint4*)(ubase + pl.q + blk * 64 + c * 16);
+        const uint4 gv = ld16(gq + blk * 64 + c * 16);
+        const uint4 uv = ld16(uq_ + blk * 64 + c * 16);
         if (q2k) {
-          gsc = *(const uint32_t*)(gbase + pl.s + blk * 16 + c * 4);
-          usc = *(const uint32_t*)(ubase + pl.s + blk * 16 + c * 4);
-          gdd = *(const uint32_t*)(gbase + pl.d + blk * 4);
-          udd = *(const uint32_t*)(ubase + pl.d + blk * 4);
-          gq[0] = gv.x; gq[1] = gv.y; gq[2] = gv.z; gq[3] = gv.w;
-          uq[0] = uv.x; uq[1] = uv.y; uq[2] = uv.z; uq[3] = uv.w;
+          gsc = ld4(gs + blk * 16 + c * 4);
+          usc = ld4(us + blk * 16 + c * 4);
+          gdd = ld4(gd + blk * 4);
+          udd = ld4(ud + blk * 4);
+          gw[0] = gv.x; gw[1] = gv.y; gw[2] = gv.z; gw[3] = gv.w;
+          uw[0] = uv.x; uw[1] = uv.y; uw[2] = uv.z; uw[3] = uv.w;
         } else {
-          gsc = gbase[pl.s + blk * 4 + c];
-          usc = ubase[pl.s + blk * 4 + c];
-          gdd = *(const uint16_t*)(gbase + pl.d + blk * 2);
-          udd = *(const uint16_t*)(ubase + pl.d + blk * 2);
-          cb2_decode_dword(L.tab, gv.x, gq[0], gq[1], gq[2], gq[3]);
-          cb2_decode_dword(L.tab, gv.y, gq[4], gq[5], gq[6], gq[7]);
-          cb2_decode_dword(L.tab, gv.z, gq[8], gq[9], gq[10], gq[11]);
-          cb2_decode_dword(L.tab, gv.w, gq[12], gq[13], gq[14], gq[15]);
-          cb2_decode_dword(L.tab, uv.x, uq[0], uq[1], uq[2], uq[3]);
-          cb2_decode_dword(L.tab, uv.y, uq[4], uq[5], uq[6], uq[7]);
-          cb2_decode_dword(L.tab, uv.z, uq[8], uq[9], uq[10], uq[11]);
-          cb2_decode_dword(L.tab, uv.w, uq[12], uq[13], uq[14], uq[15]);
+          gsc = ld1(gs + blk * 4 + c);
+          usc = ld1(us + blk * 4 + c);
+          gdd = ld2(gd + blk * 2);
+          udd = ld2(ud + blk * 2);
+          cb2_decode_dword(L.tab, gv.x, gw[0], gw[1], gw[2], gw[3]);
+          cb2_decode_dword(L.tab, gv.y, gw[4], gw[5], gw[6], gw[7]);
+          cb2_decode_dword(L.tab, gv.z, gw[8], gw[9], gw[10], gw[11]);
+          cb2_decode_dword(L.tab, gv.w, gw[12], gw[13], gw[14], gw[15]);
+          cb2_decode_dword(L.tab, uv.x, uw[0], uw[1], uw[2], uw[3]);
+          cb2_decode_dword(L.tab, uv.y, uw[4], uw[5], uw[6], uw[7]);
+          cb2_decode_dword(L.tab, uv.z, uw[8], uw[9], uw[10], uw[11]);
+          cb2_decode_dword(L.tab, uv.w, uw[12], uw[13], uw[14], uw[15]);
         }
         // one token at a time (its x chunk is 40 registers); the decoded
         // weights stay live across the four tokens
@@ -730,15 +1009,15 @@ __device__ void routed_gu_tile(const PersistArgs& a, const LayerPtrs& Lp, int u,
           uint32_t xh[16], xl[16];
           float xs[4];
           int xa[4];
-          x_chunk(a, L, t, ch, xh, xl, xs, xa);
+          x_chunk<SMALL>(a, L, t, ch, xh, xl, xs, xa);
           float gp, up;
           if (q2k) {
-            const uint32_t gw[4] = {gq[0], gq[1], gq[2], gq[3]}, uw[4] = {uq[0], uq[1], uq[2], uq[3]};
-            gp = q2k_chunk_dot(gw, gsc, half_to_f32(gdd & 0xFFFFu), half_to_f32(gdd >> 16), xh, xl, xs, xa);
-            up = q2k_chunk_dot(uw, usc, half_to_f32(udd & 0xFFFFu), half_to_f32(udd >> 16), xh, xl, xs, xa);
+            const uint32_t g4[4] = {gw[0], gw[1], gw[2], gw[3]}, u4[4] = {uw[0], uw[1], uw[2], uw[3]};
+            gp = q2k_chunk_dot(g4, gsc, half_to_f32(gdd & 0xFFFFu), half_to_f32(gdd >> 16), xh, xl, xs, xa);
+            up = q2k_chunk_dot(u4, usc, half_to_f32(udd & 0xFFFFu), half_to_f32(udd >> 16), xh, xl, xs, xa);
           } else {
-            gp = half_to_f32(gdd) * xs[0] * (float)cb2_chunk_dot(gq, xh, xl, gsc);
-            up = half_to_f32(udd) * xs[0] * (float)cb2_chunk_dot(uq, xh, xl, usc);
+            gp = half_to_f32(gdd) * xs[0] * (float)cb2_chunk_dot(gw, xh, xl, gsc);
+            up = half_to_f32(udd) * xs[0] * (float)cb2_chunk_dot(uw, xh, xl, usc);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -787,158 +1066,174 @@ __device__ void routed_gu_tile(const PersistArgs& a, const LayerPtrs& Lp, int u,
   __syncthreads();
 }
 
-template <int FMT>
-__device__ void phase_gateup(const PersistArgs& a, const LayerPtrs& Lp, const float* x, PersistLds& L) {
-  const int n_shared = a.Fs / kSharedItemRows;
+// Routed tiles of this workgroup: the first ones were copied ahead, the rest
+// are copied into the first slot on demand.
+template <int FMT, bool SMALL>
+__device__ __forceinline__ void routed_tiles(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L) {
   const int tiles = a.F / kGateTile;
   const int na = *L.nact;
-  const int n_items = n_shared + na * tiles;
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    if (it < n_shared) {
-      shared_gu_item(a, Lp, x, it, L);
-    } else {
-      const int r = it - n_shared;
-      routed_gu_tile<FMT>(a, Lp, r / tiles, r % tiles, L);
+  const int base = gu_items_base<SMALL>(a);
+  const int npf = tile_pf_count<SMALL>(a, na);
+  const uint32_t off = tile_off<SMALL>(a), tb = gu_tile_bytes(a);
+  int j = 0;
+  for (int it = (int)blockIdx.x + my_count(base) * (int)gridDim.x; it < base + na * tiles;
+       it += gridDim.x, ++j) {
+    const int r = it - base;
+    const int e = L.act[r / tiles], f0 = (r % tiles) * kGateTile;
+    uint32_t slot = off + (uint32_t)j * tb;
+    if (j >= npf) {
+      slot = off;
+      stage_now([&](int w, int n) { copy_tile(a, Lp, L.pfb + off, e, f0, w, n); });
     }
+    routed_gu_tile<FMT, SMALL>(a, L.pfb + slot, e, f0, L);
   }
 }
 
 // ------------------------------------------------------------ phase D ---
-// The first tile of a workgroup (rows r0 = 8*blockIdx.x ..) has its shared
-// down rows ([8][Fs] bf16) and the Q2_K planes of up to `npf` experts
-// ([qs 8*nb*64][scales 8*nb*16][d,dmin 8*nb*4], nb = F/256) in the LDS
-// buffer.
-struct DownPfPlan {
-  size_t sd_bytes, per_expert;
-  int npf;
-};
-
-__device__ __forceinline__ DownPfPlan down_pf_plan(const PersistArgs& a, int na) {
-  DownPfPlan p;
-  const int nb = a.F / kBlockW;
-  p.sd_bytes = a.Fs ? (size_t)kDownRows * a.Fs * 2 : 0;
-  if (p.sd_bytes > (size_t)a.pfb) p.sd_bytes = 0;          // shared rows do not fit: not prefetched
-  p.per_expert = (size_t)kDownRows * nb * kQ2KBytes;
-  const size_t room = (size_t)a.pfb - p.sd_bytes;
-  const int fit = (int)(room / p.per_expert);
-  p.npf = na < fit ? na : fit;
-  return p;
-}
-
-__device__ void down_prefetch(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L) {
-  const int r0 = blockIdx.x * kDownRows;
-  if (r0 >= a.H) return;
-  const DownPfPlan p = down_pf_plan(a, *L.nact);
-  const int nb = a.F / kBlockW;
-  if (p.sd_bytes) copy_to_lds(Lp.sd + (size_t)r0 * a.Fs, L.pfb, p.sd_bytes);
-  const size_t nblk = (size_t)a.H * nb;
-  const MatPlanes pl = q2k_planes(nblk);
-  for (int u = 0; u < p.npf; ++u) {
-    const uint8_t* base = Lp.down + (size_t)L.act[u] * a.dn_stride;
-    uint8_t* dst = L.pfb + p.sd_bytes + (size_t)u * p.per_expert;
-    const size_t b0 = (size_t)r0 * nb;
-    copy_to_lds(base + pl.q + b0 * 64, dst, (size_t)kDownRows * nb * 64);
-    copy_to_lds(base + pl.s + b0 * 16, dst + (size_t)kDownRows * nb * 64, (size_t)kDownRows * nb * 16);
-    copy_to_lds(base + pl.d + b0 * 4, dst + (size_t)kDownRows * nb * 80, (size_t)kDownRows * nb * 4);
-  }
-}
-
-__device__ void phase_down(const PersistArgs& a, const LayerPtrs& Lp, const float* x, float* y,
-                           PersistLds& L) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+// One wave: rows r0..r0+7 of expert e (in LDS) against every pair of its bucket.
+template <bool SMALL>
+__device__ __forceinline__ void down_expert(const PersistArgs& a, lds_cptr w, int e, PersistLds& L) {
+  const int lane = threadIdx.x & 63;
   const int nb = a.F / kBlockW;
   const int nch = a.F / kChunkW;
   const int lpr = lanes_per_row(nch);
   const int cpl = nch / lpr;
   const int rpi = 64 / lpr;
   const int rsub = lane / lpr, j = lane % lpr;
-  const size_t nblk = (size_t)a.H * nb;
-  const MatPlanes pl = q2k_planes(nblk);
+  const int q0 = L.off[e], q1 = L.off[e + 1];
+  lds_cptr wq = w, ws = w + kDownRows * nb * 64, wd = w + kDownRows * nb * 80;
+#pragma unroll 1
+  for (int rr = rsub; rr < kDownRows; rr += rpi) {
+    // one 64-weight chunk of this row at a time, read once for all pairs
+#pragma unroll 1
+    for (int cc = 0; cc < cpl; ++cc) {
+      const int ch = j + cc * lpr;
+      const int c = ch & 3;
+      const uint32_t blk = (uint32_t)rr * nb + ch / 4;
+      const uint4 qv = ld16(wq + blk * 64 + c * 16);
+      const uint32_t scm = ld4(ws + blk * 16 + c * 4);
+      const uint32_t dd = ld4(wd + blk * 4);
+      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+      const float d = half_to_f32(dd & 0xFFFFu), dm = half_to_f32(dd >> 16);
+#pragma unroll 1
+      for (int pos = q0; pos < q1; ++pos) {
+        const int pair = L.pairs[pos];
+        uint32_t xh[16], xl[16];
+        float xs[4];
+        int xa[4];
+        const size_t ao = (size_t)pair * (a.F / 4) + ch * 16;
+        const size_t si = (size_t)pair * (a.F / kSubW) + ch * 4;
+        if (SMALL) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 hv = lds_u4(L.dah + ao + 4 * i);
+            const uint4 lv = lds_u4(L.dal + ao + 4 * i);
+            xh[4 * i] = hv.x; xh[4 * i + 1] = hv.y; xh[4 * i + 2] = hv.z; xh[4 * i + 3] = hv.w;
+            xl[4 * i] = lv.x; xl[4 * i + 1] = lv.y; xl[4 * i + 2] = lv.z; xl[4 * i + 3] = lv.w;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xs[i] = L.das[si + i];
+            xa[i] = L.daa[si + i];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint64_t hv = cld64(a.ah + ao + 2 * i), lv = cld64(a.al + ao + 2 * i);
+            xh[2 * i] = (uint32_t)hv;
+            xh[2 * i + 1] = (uint32_t)(hv >> 32);
+            xl[2 * i] = (uint32_t)lv;
+            xl[2 * i + 1] = (uint32_t)(lv >> 32);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xs[i] = cldf(&a.as[si + i]);
+            xa[i] = cldi(&a.aa[si + i]);
+          }
+        }
+        float part = q2k_chunk_dot(qw, scm, d, dm, xh, xl, xs, xa);
+        part = bfly_sum_dyn(part, lpr);
+        // lane j == 0 of this row group owns the entry for every chunk
+        if (j == 0) L.o[pos * kDownRows + rr] = cc == 0 ? part : L.o[pos * kDownRows + rr] + part;
+      }
+    }
+  }
+}
+
+// Shared expert down row (in LDS), one wave, lanes over Fs, all tokens.
+template <bool SMALL>
+__device__ __forceinline__ void shared_down_row(const PersistArgs& a, lds_cptr srow, PersistLds& L) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll 1
+  for (int t = 0; t < a.T; ++t) {
+    float s = 0.f;
+#pragma unroll 1
+    for (int f = 8 * lane; f < a.Fs; f += 512) {
+      const uint4 w = ld16(srow + f * 2);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      float av[8];
+      if (SMALL) {
+        const float4 a0 = lds_f4(L.dash + t * a.Fs + f);
+        const float4 a1 = lds_f4(L.dash + t * a.Fs + f + 4);
+        av[0] = a0.x; av[1] = a0.y; av[2] = a0.z; av[3] = a0.w;
+        av[4] = a1.x; av[5] = a1.y; av[6] = a1.z; av[7] = a1.w;
+      } else {
+        const float* at = a.ash + (size_t)t * a.Fs + f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint64_t v = cld64(at + 2 * c);
+          av[2 * c] = __uint_as_float((uint32_t)v);
+          av[2 * c + 1] = __uint_as_float((uint32_t)(v >> 32));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s = fmaf(bf16_to_f32(ww[c] & 0xFFFFu), av[2 * c], s);
+        s = fmaf(bf16_to_f32(ww[c] >> 16), av[2 * c + 1], s);
+      }
+    }
+    s = bfly_sum<6>(s);
+    if (lane == 0) L.sh[t * kDownRows + wave] = s;
+  }
+}
+
+template <bool SMALL>
+__device__ __forceinline__ void phase_down(const PersistArgs& a, const LayerPtrs& Lp, const float* x, float* y,
+                                           PersistLds& L) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int na = *L.nact;
   const int n_tiles = a.H / kDownRows;
-  const int T = a.T;
-  const DownPfPlan pp = down_pf_plan(a, na);
+  const int T = a.T, P = a.T * a.k;
+  const int chunk = down_chunk(a);
+  const uint32_t pe = dn_expert_bytes(a), sdb = al16(sd_bytes(a));
+  if (SMALL) {
+    // every pair's SwiGLU limbs and the shared SwiGLU vector -> LDS
+    dma_to_lds<kCoherent>(a.ah, L.dah, (uint32_t)P * a.F, wave, nw);
+    dma_to_lds<kCoherent>(a.al, L.dal, (uint32_t)P * a.F, wave, nw);
+    dma_to_lds<kCoherent>(a.as, L.das, (uint32_t)P * a.F / 4, wave, nw);
+    dma_to_lds<kCoherent>(a.aa, L.daa, (uint32_t)P * a.F / 4, wave, nw);
+    if (a.Fs) dma_to_lds<kCoherent>(a.ash, L.dash, (uint32_t)T * a.Fs * 4, wave, nw);
+  }
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     const int r0 = tile * kDownRows;
     const bool first = tile == (int)blockIdx.x;
-    for (int u = wave; u < na; u += nw) {
-      const int e = L.act[u];
-      const bool lds_w = first && u < pp.npf;
-      const uint8_t* gbase = Lp.down + (size_t)e * a.dn_stride;
-      const uint8_t* lbase = L.pfb + pp.sd_bytes + (size_t)u * pp.per_expert;
-      const int q0 = L.off[e], q1 = L.off[e + 1];
-      for (int rr = rsub; rr < kDownRows; rr += rpi) {
-        const int h = r0 + rr;
-        // one 64-weight chunk of this row at a time, read once for all pairs
-#pragma unroll 1
-        for (int cc = 0; cc < cpl; ++cc) {
-          const int ch = j + cc * lpr;
-          const int c = ch & 3;
-          uint4 qv;
-          uint32_t scm, dd;
-          if (lds_w) {
-            const size_t lb = (size_t)rr * nb + ch / 4;      // block within the tile
-            qv = *(const uint4*)(lbase + lb * 64 + c * 16);
-            scm = *(const uint32_t*)(lbase + (size_t)kDownRows * nb * 64 + lb * 16 + c * 4);
-            dd = *(const uint32_t*)(lbase + (size_t)kDownRows * nb * 80 + lb * 4);
-          } else {
-            const size_t blk = (size_t)h * nb + ch / 4;
-            qv = *(const uint4*)(gbase + pl.q + blk * 64 + c * 16);
-            scm = *(const uint32_t*)(gbase + pl.s + blk * 16 + c * 4);
-            dd = *(const uint32_t*)(gbase + pl.d + blk * 4);
-          }
-          const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-          const float d = half_to_f32(dd & 0xFFFFu), dm = half_to_f32(dd >> 16);
-          for (int pos = q0; pos < q1; ++pos) {
-            const int pair = L.pairs[pos];
-            uint32_t xh[16], xl[16];
-            float xs[4];
-            int xa[4];
-            const uint32_t* ph = a.ah + (size_t)pair * (a.F / 4) + ch * 16;
-            const uint32_t* plw = a.al + (size_t)pair * (a.F / 4) + ch * 16;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const uint64_t hv = cld64(ph + 2 * i), lv = cld64(plw + 2 * i);
-              xh[2 * i] = (uint32_t)hv;
-              xh[2 * i + 1] = (uint32_t)(hv >> 32);
-              xl[2 * i] = (uint32_t)lv;
-              xl[2 * i + 1] = (uint32_t)(lv >> 32);
-            }
-            const size_t si = (size_t)pair * (a.F / kSubW) + ch * 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              xs[i] = cldf(&a.as[si + i]);
-              xa[i] = cldi(&a.aa[si + i]);
-            }
-            float part = q2k_chunk_dot(qw, scm, d, dm, xh, xl, xs, xa);
-            part = bfly_sum_dyn(part, lpr);
-            // lane j == 0 of this row group owns the entry for every chunk
-            if (j == 0) L.o[pos * kDownRows + rr] = cc == 0 ? part : L.o[pos * kDownRows + rr] + part;
-          }
-        }
+    // residual inputs of this tile, requested before the wait
+    float xres = 0.f;
+    if (a.residual && (int)threadIdx.x < T * kDownRows)
+      xres = cldf(&x[(size_t)(threadIdx.x / kDownRows) * a.H + r0 + threadIdx.x % kDownRows]);
+    if (first && SMALL) wait_all_and_sync();
+    // experts in chunks that fit beside the shared rows; the first chunk of
+    // the first tile (and its shared rows) arrived during the barrier
+    for (int u0 = 0; u0 < na; u0 += chunk) {       // na >= 1, chunk >= 1
+      const int u1 = na - u0 < chunk ? na : u0 + chunk;
+      if (!first || u0 > 0) {
+        stage_now([&](int w, int n) {
+          if (u0 == 0) copy_sd_rows(a, Lp, L, r0, w, n);
+          for (int u = u0; u < u1; ++u) copy_down_rows(a, Lp, L.pfb + sdb + (uint32_t)(u - u0) * pe, L.act[u], r0, w, n);
+        });
       }
-    }
-    // shared expert down: one row per wave, lanes over Fs, all tokens
-    if (a.Fs && wave < kDownRows) {
-      const int h = r0 + wave;
-      const uint16_t* srow = (first && pp.sd_bytes) ? (const uint16_t*)L.pfb + (size_t)wave * a.Fs
-                                                    : Lp.sd + (size_t)h * a.Fs;
-      for (int t = 0; t < T; ++t) {
-        const float* at = a.ash + (size_t)t * a.Fs;
-        float s = 0.f;
-        for (int f = 8 * lane; f < a.Fs; f += 512) {
-          const uint4 w = *(const uint4*)(srow + f);
-          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint64_t av = cld64(at + f + 2 * c);
-            s = fmaf(bf16_to_f32(ww[c] & 0xFFFFu), __uint_as_float((uint32_t)av), s);
-            s = fmaf(bf16_to_f32(ww[c] >> 16), __uint_as_float((uint32_t)(av >> 32)), s);
-          }
-        }
-        s = bfly_sum<6>(s);
-        if (lane == 0) L.sh[t * kDownRows + wave] = s;
-      }
+      for (int u = u0 + wave; u < u1; u += nw) down_expert<SMALL>(a, L.pfb + sdb + (uint32_t)(u - u0) * pe, L.act[u], L);
+      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<SMALL>(a, L.pfb + (uint32_t)wave * a.Fs * 2, L);
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < T * kDownRows; idx += blockDim.x) {
@@ -950,44 +1245,72 @@ __device__ void phase_down(const PersistArgs& a, const LayerPtrs& Lp, const floa
         acc = fmaf(L.wl[pair], L.o[pos * kDownRows + rr], acc);
       }
       if (a.Fs) acc += L.sh[idx];
-      if (a.residual) acc += cldf(&x[(size_t)t * a.H + h]);
+      if (a.residual) acc += idx == (int)threadIdx.x ? xres : cldf(&x[(size_t)t * a.H + h]);
       cstf(&y[(size_t)t * a.H + h], acc);
     }
-    __syncthreads();
+    __syncthreads();     // L.o and L.sh are rewritten by the next tile
   }
+  // a workgroup without tiles still has its copies in flight
+  if (SMALL && (int)blockIdx.x >= n_tiles) wait_all_and_sync();
 }
 
 // ------------------------------------------------------------- kernel ---
-template <int FMT>
+template <int FMT, bool SMALL>
 __global__ void __launch_bounds__(kPersistThreads) k_persist(PersistArgs a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
-  PersistLds L = carve_lds(lds_raw, a, FMT == 2);
-  if (FMT == 2) copy_to_lds(a.cbtab, L.tab, (size_t)kCbTabWords * 4);
-  router_prefetch(a, a.layers[0], L);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  PersistLds L = carve_lds<SMALL>(lds_raw, a, FMT == 2);
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (FMT == 2) dma_to_lds<0>(a.cbtab, L.tab, (uint32_t)kCbTabWords * 4, wave, nw);
+  pf_router_and_shared<SMALL>(a, a.layers[0], L, wave, nw);
+  wait_all_and_sync();
   uint32_t epoch = a.epoch0;
   for (int li = 0; li < a.n_layers; ++li) {
     const LayerPtrs Lp = a.layers[li];
     const float* x = li == 0 ? a.x_in : ((li - 1) & 1 ? a.xbuf1 : a.xbuf0);
     float* y = li == a.n_layers - 1 ? a.y_out : (li & 1 ? a.xbuf1 : a.xbuf0);
-    phase_router(a, Lp, x, L);
-    shared_gu_prefetch(a, Lp, L);              // buffer is free: the router rows are consumed
-    if (!grid_barrier(a, ++epoch)) return;
-    if (a.small) {
-      local_topk_quant(a, x, li, L);
+    if (SMALL) {
+      // ---- R: x -> LDS, RMS scales, router, shared gate/up
+      dma_to_lds<kCoherent>(x, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
+      wait_all_and_sync();
+      token_rinv<true>(a, L, x, 0, a.T);
+      phase_router<true>(a, Lp, x, L);
+      shared_items<true>(a, Lp, x, L);
+      if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
+      // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
+      dma_to_lds<kCoherent>(a.logits, L.lg, (uint32_t)a.T * a.E * 8, wave, nw);
+      wait_all_and_sync();
+      if (wave < a.T) topk_wave<true>(a, wave, li, L, blockIdx.x == 0);
+      __syncthreads();
+      build_groups<true>(a, L);
+      pf_tiles<true>(a, Lp, L, wave, nw);
+      {
+        const int nb = a.H / kBlockW;
+        for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, x, u / nb, u % nb, L);
+      }
+      wait_all_and_sync();
+      routed_tiles<FMT, true>(a, Lp, L);
     } else {
-      phase_topk_quant(a, x, li);
-      if (!grid_barrier(a, ++epoch)) return;
+      phase_router<false>(a, Lp, x, L);
+      if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_shared_items(a, Lp, L, w, n); })) return;
+      {
+        const int nb = a.H / kBlockW, units = a.T + a.T * nb;
+        for (int u = blockIdx.x * nw + wave; u < units; u += gridDim.x * nw) {
+          if (u < a.T) topk_wave<false>(a, u, li, L, true);
+          else quant_x_wave<false>(a, x, (u - a.T) / nb, (u - a.T) % nb, L);
+        }
+      }
+      if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
+      build_groups<false>(a, L);
+      pf_tiles<false>(a, Lp, L, wave, nw);
+      shared_items<false>(a, Lp, x, L);
+      wait_all_and_sync();
+      routed_tiles<FMT, false>(a, Lp, L);
     }
-    build_groups(a, L);
-    phase_gateup<FMT>(a, Lp, x, L);
-    down_prefetch(a, Lp, L);                   // shared gate/up rows are consumed
-    if (!grid_barrier(a, ++epoch)) return;
-    phase_down(a, Lp, x, y, L);
+    if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_down(a, Lp, L, w, n); })) return;
+    phase_down<SMALL>(a, Lp, x, y, L);
     if (li + 1 < a.n_layers) {
-      router_prefetch(a, a.layers[li + 1], L); // down rows are consumed
-      if (!grid_barrier(a, ++epoch)) return;
+      const LayerPtrs Ln = a.layers[li + 1];
+      if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_router_and_shared<SMALL>(a, Ln, L, w, n); })) return;
     }
   }
 }

@@ -53,13 +53,18 @@ class MoE:
                         None if lw.shared_down is None else c(lw.shared_down), stream)
 
     def decode(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
-               w_out=None, stream=None, multikernel=False):
+               w_out=None, stream=None, path="auto"):
+        """path: "auto" (the persistent kernel when it can run this call, else
+        one launch per step), "persistent" (that kernel or QS_E_UNSUPPORTED),
+        "multikernel" (one launch per step)."""
         import torch
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
+        mode = {"auto": 0, "persistent": L.QS_DECODE_REQUIRE_PERSISTENT,
+                "multikernel": L.QS_DECODE_MULTIKERNEL}[path]
         flags = ((L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
-                 | (L.QS_DECODE_MULTIKERNEL if multikernel else 0))
+                 | mode)
         L.qs_moe_decode(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
 

@@ -36,6 +36,15 @@ def test_no_other_exported_qs_symbols():
     assert exported == header_functions()
 
 
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+(QS_\w+)\s+(\d+)u?\b", text))
+    for name in ("QS_MOE_ABI_VERSION", "QS_DECODE_RESIDUAL", "QS_DECODE_RMSNORM",
+                 "QS_DECODE_MULTIKERNEL", "QS_DECODE_REQUIRE_PERSISTENT"):
+        assert hasattr(qm, name), name
+        assert int(defs[name]) == getattr(qm, name), name
+
+
 def test_status_strings():
     assert qm.status_string(qm.QS_OK) == "ok"
     for s in (qm.QS_E_INVAL, qm.QS_E_NOMEM, qm.QS_E_HIP, qm.QS_E_STATE, qm.QS_E_UNSUPPORTED):

@@ -65,12 +65,13 @@ def test_full_stack_parity(lib, stacks, name, T):
     x = torch.from_numpy(synth.tokens(wl, T, 7)).cuda()
     ids = torch.empty((L, T, wl.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((L, T, wl.top_k), dtype=torch.float32, device="cuda")
-    y_full = moe.decode(x, n_layers=L, residual=True, prenorm=True, ids_out=ids, w_out=w)
+    y_full = moe.decode(x, n_layers=L, residual=True, prenorm=True, ids_out=ids, w_out=w,
+                        path="persistent")
     torch.cuda.synchronize()
     assert torch.isfinite(y_full).all()
     cur = x
     for l in range(L):
-        nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True, prenorm=True)
+        nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True, prenorm=True, path="persistent")
         if l in st.oracle:
             torch.cuda.synchronize()
             toks = np.sort(rng.choice(T, size=min(n_tok, T), replace=False))

@@ -92,34 +92,34 @@ def test_route_a3b(a3b, T):
     _route_check(wl, moe, lws[0], T)
 
 
-def _decode_check(wl, moe, lw, T, batch=0, label="", multikernel=False):
+def _decode_check(wl, moe, lw, T, batch=0, label="", path="auto"):
     x = synth.tokens(wl, T, batch)
     xd = torch.from_numpy(x).cuda()
     ids = torch.empty((T, wl.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, wl.top_k), dtype=torch.float32, device="cuda")
-    y = moe.decode(xd, ids_out=ids, w_out=w, multikernel=multikernel)
+    y = moe.decode(xd, ids_out=ids, w_out=w, path=path)
     torch.cuda.synchronize()
     return check_layer(wl, lw, x, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), label=label)
 
 
-PATHS = [False, True]
-PATH_IDS = ["persistent", "multikernel"]
+PATHS = ["persistent", "multikernel"]
+PATH_IDS = PATHS
 
 
 @pytest.mark.parametrize("mk", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("T", [1, 3, 4, 16, 33, 64])
 def test_decode_tiny(tiny, T, mk):
     wl, moe, lws = tiny
-    say(f"decode tiny T={T} multikernel={mk}")
-    _decode_check(wl, moe, lws[0], T, label=f"tiny T={T}", multikernel=mk)
+    say(f"decode tiny T={T} path={mk}")
+    _decode_check(wl, moe, lws[0], T, label=f"tiny T={T}", path=mk)
 
 
 @pytest.mark.parametrize("mk", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("T", [1, 4, 7, 16])
 def test_decode_a3b(a3b, T, mk):
     wl, moe, lws = a3b
-    say(f"decode a3b T={T} multikernel={mk}")
-    _decode_check(wl, moe, lws[0], T, label=f"a3b T={T}", multikernel=mk)
+    say(f"decode a3b T={T} path={mk}")
+    _decode_check(wl, moe, lws[0], T, label=f"a3b T={T}", path=mk)
 
 
 @pytest.mark.parametrize("mk", PATHS, ids=PATH_IDS)
@@ -127,18 +127,18 @@ def test_decode_a3b(a3b, T, mk):
 def test_batch_invariance_and_determinism(request, name, mk):
     wl, moe, _ = request.getfixturevalue("tiny" if name == "tiny_q2k" else "a3b")
     T = 8
-    say(f"batch invariance {name} T={T} multikernel={mk}")
+    say(f"batch invariance {name} T={T} path={mk}")
     x = torch.from_numpy(synth.tokens(wl, T, 3)).cuda()
-    y = moe.decode(x, multikernel=mk)
-    y2 = moe.decode(x, multikernel=mk)
+    y = moe.decode(x, path=mk)
+    y2 = moe.decode(x, path=mk)
     torch.cuda.synchronize()
     assert torch.equal(y, y2), "two runs differ"
     for t in (0, 3, T - 1):
-        yt = moe.decode(x[t:t + 1].contiguous(), multikernel=mk)
+        yt = moe.decode(x[t:t + 1].contiguous(), path=mk)
         torch.cuda.synchronize()
         assert torch.equal(yt[0], y[t]), f"token {t} differs between T=1 and T={T}"
     perm = torch.tensor([5, 2, 7, 0, 1, 6, 4, 3], device="cuda")
-    yp = moe.decode(x[perm].contiguous(), multikernel=mk)
+    yp = moe.decode(x[perm].contiguous(), path=mk)
     torch.cuda.synchronize()
     assert torch.equal(yp, y[perm]), "permuting tokens does not permute outputs"
 
@@ -200,10 +200,10 @@ def test_residual_chain_and_in_place(lib, prenorm, mk):
         ids = torch.empty((L, 4, wl.top_k), dtype=torch.int32, device="cuda")
         w = torch.empty((L, 4, wl.top_k), dtype=torch.float32, device="cuda")
         y_all = moe.decode(x, n_layers=L, residual=True, prenorm=prenorm, ids_out=ids, w_out=w,
-                           multikernel=mk)
+                           path=mk)
         cur = x
         for l in range(L):
-            nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True, prenorm=prenorm, multikernel=mk)
+            nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True, prenorm=prenorm, path=mk)
             torch.cuda.synchronize()
             check_layer(wl, lws[l], cur.cpu().numpy(), nxt.cpu().numpy(), ids[l].cpu().numpy(),
                         w[l].cpu().numpy(), residual=True, prenorm=prenorm,
@@ -212,7 +212,7 @@ def test_residual_chain_and_in_place(lib, prenorm, mk):
         torch.cuda.synchronize()
         assert torch.equal(y_all, cur), "multi-layer call differs from chained single layers"
         xin = x.clone()
-        moe.decode(xin, y=xin, n_layers=L, residual=True, prenorm=prenorm, multikernel=mk)
+        moe.decode(xin, y=xin, n_layers=L, residual=True, prenorm=prenorm, path=mk)
         torch.cuda.synchronize()
         assert torch.equal(xin, y_all), "in-place decode differs"
 
@@ -250,6 +250,8 @@ def test_error_statuses_with_gpu(lib):
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), x.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr() + 4, y.data_ptr(), 2, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 16, None, None, st) == lib.QS_E_INVAL
+        both = lib.QS_DECODE_MULTIKERNEL | lib.QS_DECODE_REQUIRE_PERSISTENT
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, both, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 2, 1, x.data_ptr(), y.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_dequant(moe.h, 0, wl.n_experts, 0, y.data_ptr(), st) == lib.QS_E_INVAL
         assert L.qs_moe_dequant(moe.h, 0, 0, 3, y.data_ptr(), st) == lib.QS_E_INVAL
