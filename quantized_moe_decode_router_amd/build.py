@@ -23,6 +23,10 @@ HIPCC_FLAGS = [
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden",
+    # The persistent kernel is one long loop over layers whose body is every
+    # step of the path; hoisting loop-invariant machine code out of it keeps
+    # per-phase values live across all phases and spills to scratch.
+    "-mllvm", "-disable-machine-licm",
 ]
 
 

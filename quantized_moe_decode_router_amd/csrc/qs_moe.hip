@@ -228,7 +228,7 @@ __global__ void k_sync_reset(uint32_t* s) {
 // same sizes the kernel's staging plans use).
 struct PersistShape {
   bool ok = false;
-  uint32_t pfb = 0;
+  uint32_t pfb = 0, pfa = 0;
   size_t lds = 0;
   int r_et = 1, r_tt = 1;
 };
@@ -249,10 +249,21 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   const uint64_t tile = 2ull * 16 * nbh * (64 + (cb2 ? 4 : 16) + (cb2 ? 2 : 4));
   const uint64_t sd = 16 * Fs, pe = 8 * nb * 84;
   auto a16 = [](uint64_t v) { return (v + 15) & ~15ull; };
-  bool fits = rb <= p.pfb && tile <= p.pfb && a16(sd) + pe <= p.pfb;
-  // SMALL: shared items after the router rows; otherwise at least one
-  // shared item ahead of the routed tiles' slots
-  if (Fs) fits = fits && (small ? a16(rb) + item : item + tile) <= p.pfb;
+  bool fits;
+  if (small) {
+    // region A: router rows + one shared item, then gate/up tiles (two when
+    // region B still holds eight experts' down rows, else one); region B:
+    // the shared down rows and at least one expert's
+    const uint64_t r_sh = a16(rb) + (Fs ? item : 0), b_min = a16(sd) + pe;
+    uint64_t A = a16(std::max(r_sh, 2 * tile));
+    if (A + a16(sd) + 8 * pe > p.pfb) A = a16(std::max(r_sh, tile));
+    p.pfa = (uint32_t)A;
+    fits = A + b_min <= p.pfb;
+  } else {
+    fits = rb <= p.pfb && tile <= p.pfb && a16(sd) + pe <= p.pfb;
+    // at least one shared item ahead of the routed tiles' slot
+    if (Fs) fits = fits && item + tile <= p.pfb;
+  }
   p.ok = fits;
   return p;
 }
@@ -324,10 +335,12 @@ int setup_persistent(qs_moe* h) {
   // the largest LDS of each instantiation: the carve grows with T
   size_t lds_small = 0, lds_big = 0;
   for (int T = 1; T <= c.max_tokens; ++T) {
-    const bool small = T <= kSmallT;
-    const PersistShape p = persist_shape(h, T, small);
-    if (!p.ok) continue;
-    (small ? lds_small : lds_big) = std::max(small ? lds_small : lds_big, p.lds);
+    if (T <= kSmallT) {
+      const PersistShape p = persist_shape(h, T, true);
+      if (p.ok) lds_small = std::max(lds_small, p.lds);
+    }
+    const PersistShape p = persist_shape(h, T, false);     // also the fallback of small batches
+    if (p.ok) lds_big = std::max(lds_big, p.lds);
   }
   h->persist_small_ok = lds_small && persist_resident(h, true, lds_small);
   h->persist_big_ok = lds_big && persist_resident(h, false, lds_big);
@@ -340,10 +353,19 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
                       bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
   const qs_moe_config& c = h->cfg;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
-  const bool small = T <= kSmallT;
-  if (!(small ? h->persist_small_ok : h->persist_big_ok)) return 1;
-  const PersistShape p = persist_shape(h, T, small);
-  if (!p.ok) return 1;
+  // small batches take the SMALL instantiation when its working set fits,
+  // otherwise the general one
+  bool small = T <= kSmallT && h->persist_small_ok;
+  PersistShape p;
+  if (small) {
+    p = persist_shape(h, T, true);
+    small = p.ok;
+  }
+  if (!small) {
+    if (!h->persist_big_ok) return 1;
+    p = persist_shape(h, T, false);
+    if (!p.ok) return 1;
+  }
   const uint32_t barriers = (small ? 3u : 4u) * nL - 1u;
   if (h->epoch + barriers > (1u << 26)) {
     hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
@@ -352,6 +374,7 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   Scratch& s = h->s;
   PersistArgs a{};
   a.layers = h->d_layers + layer0;
+  a.G = h->grid;
   a.n_layers = nL;
   a.T = T; a.H = c.hidden; a.E = c.n_experts; a.k = c.top_k; a.F = c.expert_ffn; a.Fs = c.shared_ffn;
   a.gq2k = c.gate_up_format == QS_FMT_Q2K;
@@ -360,6 +383,7 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   a.r_tt = p.r_tt;
   a.r_et = p.r_et;
   a.pfb = p.pfb;
+  a.pfa = p.pfa;
   a.gu_stride = h->gu_stride;
   a.dn_stride = h->dn_stride;
   a.cbtab = h->cbtab;

@@ -20,12 +20,14 @@
 //   R   x -> LDS (one coherent copy); per-token RMS scale; router logits;
 //       the shared expert's gate/up items (they need only x)
 //   --- barrier
-//   K   logits -> LDS; top-k of every token, grouping, x -> fixed-point
-//       limbs, all redundantly in every workgroup (this saves a barrier);
-//       routed gate/up tiles -> LDS; SwiGLU outputs
-//   --- barrier (meanwhile: shared and routed down rows -> LDS)
-//   D   SwiGLU limbs -> LDS; down rows + combine + shared down + residual
-//   --- barrier (meanwhile: next layer's router rows and shared items -> LDS)
+//   K   logits -> LDS; top-k of every token and the grouping, redundantly
+//       in every workgroup (this saves a barrier); routed gate/up tiles ->
+//       LDS while x becomes fixed-point limbs
+//   GU  SwiGLU outputs of the routed tiles
+//   --- barrier (meanwhile: down rows, next layer's router rows and shared
+//       items -> LDS)
+//   D   SwiGLU limbs -> LDS; down GEMVs + combine + shared down + residual
+//   --- barrier
 // otherwise the activations stay in global scratch and one more barrier
 // follows top-k / quantisation (one wave per token or x block).
 //
@@ -70,10 +72,13 @@ struct LayerPtrs {
 
 struct PersistArgs {
   const LayerPtrs* layers;   // device array, first entry = layer0
+  int G;                     // workgroups of the launch (a multiple of 8)
   int n_layers, T, H, E, k, F, Fs;
   int gq2k, prenorm, residual;
   int r_et, r_tt;            // router unit: experts x tokens
-  uint32_t pfb;              // bytes of the LDS prefetch buffer
+  uint32_t pfb;              // bytes of the LDS weight-staging buffer
+  uint32_t pfa;              // SMALL: bytes of its first region (router, shared items, gate/up tiles);
+                             // the rest holds the down rows
   size_t gu_stride, dn_stride;
   const uint32_t* cbtab;
   const float* x_in;
@@ -98,6 +103,15 @@ struct PersistArgs {
   uint32_t* sync;
   uint32_t epoch0;
 };
+
+// Thread index through an opaque move: values derived from it are then
+// recomputed in each phase instead of being hoisted out of the layer loop
+// and kept live (in registers) across every phase.
+__device__ __forceinline__ int qs_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
 
 // ------------------------------------------------- coherent accesses ---
 __device__ __forceinline__ uint32_t cld(const uint32_t* p) {
@@ -149,17 +163,37 @@ __device__ __forceinline__ uint4 lds_u4(const QS_LDS uint32_t* p) { return ld16(
 // ------------------------------------------------------ global -> LDS ---
 // Copy `bytes` (rounded up to 16) from global memory straight into LDS with
 // global_load_lds_dwordx4, spread over waves w = 0..nw-1 of the calling
-// set; each wave instruction moves 64 x 16 bytes to consecutive LDS slots.
-// AUX = kCoherent reads through to the agent-coherent level (data written by
-// other workgroups in this launch).  Completion is awaited by s_waitcnt.
+// set; each wave instruction moves 64 x 16 bytes to consecutive LDS slots
+// starting at M0.  AUX = kCoherent reads through to the agent-coherent level
+// (sc1: data written by other workgroups in this launch).
+//
+// The instruction is issued from inline assembly on purpose: for the
+// compiler's own form it must assume that any later LDS read may alias the
+// copy and waits for it there, which would serialise every prefetch with the
+// work it is meant to overlap.  The kernel orders these copies itself: an
+// s_waitcnt (wait_all_and_sync or a grid barrier) precedes every read of a
+// copied region, and a __syncthreads precedes every copy into a region that
+// was read before.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int AUX>
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  if (AUX == kCoherent)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
+                 : : "s"(lds_addr), "v"(g) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 : : "s"(lds_addr), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int AUX>
 __device__ __forceinline__ void dma_to_lds(const void* g, QS_LDS void* lds, uint32_t bytes, int w, int nw) {
-  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t lane = qs_tid() & 63;
   const uint32_t n16 = (bytes + 15u) >> 4;
   for (uint32_t base = (uint32_t)w * 64u; base < n16; base += (uint32_t)nw * 64u) {
-    if (base + lane < n16)
-      __builtin_amdgcn_global_load_lds((const uint4*)g + base + lane, (QS_LDS uint4*)lds + base, 16, 0,
-                                       AUX);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((QS_LDS uint4*)lds + base));
+    if (base + lane < n16) dma16<AUX>((const uint4*)g + base + lane, dst);
   }
 }
 
@@ -173,22 +207,23 @@ __device__ __forceinline__ void wait_all_and_sync() {
 template <class CP>
 __device__ __forceinline__ void stage_now(CP&& cp) {
   __syncthreads();
-  cp((int)(threadIdx.x >> 6), (int)(blockDim.x >> 6));
+  cp((int)(qs_tid() >> 6), (int)(kPersistThreads >> 6));
   wait_all_and_sync();
 }
 
 // ------------------------------------------------------- grid barrier ---
 // `pf(w, nw)` issues this workgroup's prefetch copies (waves 1..7 run it,
-// after the drain and while wave 0 waits).
+// after the drain and while wave 0 waits); they complete in the background
+// and whoever reads them first waits (wait_all_and_sync).
 template <class PF>
 __device__ __forceinline__ bool grid_barrier(const PersistArgs& a, uint32_t epoch, PF&& pf) {
-  const uint32_t x = blockIdx.x & 7u, per = gridDim.x >> 3;
+  const uint32_t x = blockIdx.x & 7u, per = (uint32_t)a.G >> 3;
   __builtin_amdgcn_s_waitcnt(0);     // this wave's coherent stores have completed
   __syncthreads();
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
   if (wave > 0) pf(wave - 1, nw - 1);
   int ok = 1;
-  if (threadIdx.x == 0) {
+  if (qs_tid() == 0) {
     uint32_t* s = a.sync;
     const uint32_t old = catomic_add(&s[16 * x], 1u);
     if (old == epoch * per - 1u) {
@@ -210,8 +245,10 @@ __device__ __forceinline__ bool grid_barrier(const PersistArgs& a, uint32_t epoc
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);     // this wave's prefetch copies have landed
-  return __syncthreads_and(ok);
+  // the prefetch copies may still be in flight: their consumer waits for them
+  const int all = __syncthreads_and(ok);
+  if (!all) __builtin_amdgcn_s_waitcnt(0);   // leaving: nothing may still write LDS
+  return all;
 }
 
 // --------------------------------------------------------- LDS layout ---
@@ -226,9 +263,11 @@ __host__ __device__ inline uint32_t abuf_bytes(int T, int H, int E, int P, int F
 }
 
 struct LdsLayout {
-  uint32_t tab, cnt, off, act, nact, mask, ids, pairs, tok_order, pos_of, wl, o, red, sh, ga, sred,
-      qtmp, rinv, xh, xl, xs, xa, abuf, pfb, end;
+  uint32_t tab, cnt, off, act, aoff, nact, mask, ids, pairs, tok_order, pos_of, wl, o, red, sh, ga, sred,
+      qtmp, rinv, kf, cand, ncand, sv, xh, xl, xs, xa, abuf, pfb, end;
 };
+
+__host__ __device__ inline int kf_stride(int E) { return (E + 7) & ~7; }
 
 __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int F, int Fs, bool cb2,
                                                 bool small, uint32_t pfb) {
@@ -240,11 +279,12 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
     return r;
   };
   l.tab = take(cb2 ? (uint32_t)kCbTabWords * 4 : 0);
-  l.cnt = take((uint32_t)E * 4);
-  l.off = take((uint32_t)(E + 1) * 4);
+  l.cnt = take(small ? 0 : (uint32_t)E * 4);           // general grouping only
+  l.off = take(small ? 0 : (uint32_t)(E + 1) * 4);
   l.act = take((uint32_t)E * 4);
+  l.aoff = take((uint32_t)(E + 1) * 4);
   l.nact = take(4);
-  l.mask = take((uint32_t)E * 32);
+  l.mask = take(small ? 0 : (uint32_t)E * 32);
   l.ids = take((uint32_t)P * 4);
   l.pairs = take((uint32_t)P * 4);
   l.tok_order = take((uint32_t)P * 4);
@@ -257,6 +297,12 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.sred = take((uint32_t)8 * T * 2 * 4);
   l.qtmp = take((uint32_t)T * kGateTile * 4);
   l.rinv = take((uint32_t)T * 8);
+  // SMALL top-k: keys [T][S], group maxima [T][S/8], thresholds [T]
+  l.kf = take(small ? (uint32_t)T * kf_stride(E) * 4 + (uint32_t)T * (((kf_stride(E) / 8) + 3) & ~3) * 4 +
+                          (uint32_t)T * 4 : 0);
+  l.cand = take(small ? (uint32_t)T * E * 4 : 0);
+  l.ncand = take(small ? (uint32_t)T * 4 : 0);
+  l.sv = take(small ? (uint32_t)P * 8 : 0);
   const uint32_t xq = small ? (uint32_t)T * H : 0;
   l.xh = take(xq);          // T*H/4 dwords
   l.xl = take(xq);
@@ -272,7 +318,8 @@ struct PersistLds {
   QS_LDS uint32_t* tab;   // [8192] codebook quads (codebook gate/up only)
   QS_LDS int* cnt;        // [E]
   QS_LDS int* off;        // [E+1]
-  QS_LDS int* act;        // [E]
+  QS_LDS int* act;        // [E]   active experts, ascending
+  QS_LDS int* aoff;       // [E+1] bucket of active expert u: positions [aoff[u], aoff[u+1])
   QS_LDS int* nact;       // [1]
   QS_LDS uint32_t* mask;  // [E*8]
   QS_LDS int* ids;        // [P]   expert of pair id
@@ -287,6 +334,10 @@ struct PersistLds {
   QS_LDS float* sred;     // [8*T*2] shared gate/up cross-wave partials
   QS_LDS int* qtmp;       // [T*kGateTile] fixed-point tile values
   QS_LDS double* rinv;    // [T] per-token RMS scale
+  QS_LDS float* kf;       // SMALL [T][kf_stride(E)] fp32 selection keys
+  QS_LDS int* cand;       // SMALL [T][E] top-k candidates
+  QS_LDS int* ncand;      // SMALL [T]
+  QS_LDS double* sv;      // SMALL [T*k] selected logits in rank order
   QS_LDS uint32_t* xh;    // [T*H/4] SMALL: x limbs
   QS_LDS uint32_t* xl;
   QS_LDS float* xs;       // [T*H/16]
@@ -312,6 +363,7 @@ __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const PersistArgs&
   L.cnt = (QS_LDS int*)(b + l.cnt);
   L.off = (QS_LDS int*)(b + l.off);
   L.act = (QS_LDS int*)(b + l.act);
+  L.aoff = (QS_LDS int*)(b + l.aoff);
   L.nact = (QS_LDS int*)(b + l.nact);
   L.mask = (QS_LDS uint32_t*)(b + l.mask);
   L.ids = (QS_LDS int*)(b + l.ids);
@@ -326,6 +378,10 @@ __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const PersistArgs&
   L.sred = (QS_LDS float*)(b + l.sred);
   L.qtmp = (QS_LDS int*)(b + l.qtmp);
   L.rinv = (QS_LDS double*)(b + l.rinv);
+  L.kf = (QS_LDS float*)(b + l.kf);
+  L.cand = (QS_LDS int*)(b + l.cand);
+  L.ncand = (QS_LDS int*)(b + l.ncand);
+  L.sv = (QS_LDS double*)(b + l.sv);
   L.xh = (QS_LDS uint32_t*)(b + l.xh);
   L.xl = (QS_LDS uint32_t*)(b + l.xl);
   L.xs = (QS_LDS float*)(b + l.xs);
@@ -347,8 +403,8 @@ __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const PersistArgs&
 // work) the active-expert count: a workgroup computes the same offsets when
 // it issues a copy and when it consumes it.  The host checks that the
 // buffer holds at least one piece of each kind next to its neighbours.
-__device__ __forceinline__ int my_count(int n) {       // items b + j*G below n
-  const int b = blockIdx.x, G = gridDim.x;
+__device__ __forceinline__ int my_count(const PersistArgs& a, int n) {   // items b + j*G below n
+  const int b = blockIdx.x, G = a.G;
   return b < n ? (n - 1 - b) / G + 1 : 0;
 }
 
@@ -370,6 +426,10 @@ __device__ __forceinline__ uint32_t dn_expert_bytes(const PersistArgs& a) {
   return (uint32_t)kDownRows * (a.F / kBlockW) * kQ2KBytes;
 }
 
+// SMALL: region A = [0, pfa) holds the router rows and shared items (phase
+// R), then the routed gate/up tiles (K and GU); region B = [pfa, pfb) holds
+// the down rows (copied during GU, used in D).  Otherwise the whole buffer
+// is reused phase by phase.
 // shared items: SMALL after the router rows; otherwise at 0 with room for one tile
 template <bool SMALL>
 __device__ __forceinline__ uint32_t shared_off(const PersistArgs& a) {
@@ -377,9 +437,9 @@ __device__ __forceinline__ uint32_t shared_off(const PersistArgs& a) {
 }
 template <bool SMALL>
 __device__ __forceinline__ int shared_pf_count(const PersistArgs& a) {
-  const uint32_t off = shared_off<SMALL>(a), reserve = SMALL ? 0 : gu_tile_bytes(a);
-  const int fit = a.pfb > off + reserve ? (int)((a.pfb - off - reserve) / shared_item_bytes(a)) : 0;
-  const int mine = my_count(n_shared_items(a));
+  const uint32_t off = shared_off<SMALL>(a), end = SMALL ? a.pfa : a.pfb - gu_tile_bytes(a);
+  const int fit = end > off ? (int)((end - off) / shared_item_bytes(a)) : 0;
+  const int mine = my_count(a, n_shared_items(a));
   return mine < fit ? mine : fit;
 }
 
@@ -392,22 +452,27 @@ __device__ __forceinline__ uint32_t tile_off(const PersistArgs& a) {
 }
 template <bool SMALL>
 __device__ __forceinline__ int tile_pf_count(const PersistArgs& a, int na) {
-  const uint32_t off = tile_off<SMALL>(a);
-  const int fit = a.pfb > off ? (int)((a.pfb - off) / gu_tile_bytes(a)) : 0;
+  const uint32_t off = tile_off<SMALL>(a), end = SMALL ? a.pfa : a.pfb;
+  const int fit = end > off ? (int)((end - off) / gu_tile_bytes(a)) : 0;
   const int base = gu_items_base<SMALL>(a);
-  const int mine = my_count(base + na * (a.F / kGateTile)) - my_count(base);
+  const int mine = my_count(a, base + na * (a.F / kGateTile)) - my_count(a, base);
   return mine < fit ? mine : fit;
 }
 
-// down: [shared rows | a chunk of experts' rows]; the first chunk of the
-// first tile is copied during the barrier
+// down: [shared rows | a chunk of experts' rows] from down_base; the first
+// chunk of the first tile is copied ahead (SMALL: during GU, otherwise during
+// the barrier before D)
+template <bool SMALL>
+__device__ __forceinline__ uint32_t down_base(const PersistArgs& a) { return SMALL ? a.pfa : 0; }
+template <bool SMALL>
 __device__ __forceinline__ int down_chunk(const PersistArgs& a) {
-  const uint32_t fixed = al16(sd_bytes(a));
+  const uint32_t fixed = down_base<SMALL>(a) + al16(sd_bytes(a));
   return a.pfb > fixed ? (int)((a.pfb - fixed) / dn_expert_bytes(a)) : 0;
 }
+template <bool SMALL>
 __device__ __forceinline__ int down_pf_count(const PersistArgs& a, int na) {
   if ((int)blockIdx.x * kDownRows >= a.H) return 0;
-  const int fit = down_chunk(a);
+  const int fit = down_chunk<SMALL>(a);
   return na < fit ? na : fit;
 }
 
@@ -473,9 +538,9 @@ __device__ __forceinline__ void copy_down_rows(const PersistArgs& a, const Layer
   dma_to_lds<0>(base + pl.d + b0 * 4, dst + kDownRows * nb * 80, kDownRows * nb * 4, w, nw);
 }
 
-__device__ __forceinline__ void copy_sd_rows(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int r0,
+__device__ __forceinline__ void copy_sd_rows(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int r0,
                                              int w, int nw) {
-  if (a.Fs) dma_to_lds<0>(Lp.sd + (size_t)r0 * a.Fs, L.pfb, sd_bytes(a), w, nw);
+  if (a.Fs) dma_to_lds<0>(Lp.sd + (size_t)r0 * a.Fs, dst, sd_bytes(a), w, nw);
 }
 
 // prefetches issued during barriers
@@ -487,7 +552,7 @@ __device__ __forceinline__ void pf_router_and_shared(const PersistArgs& a, const
     const int n = shared_pf_count<true>(a);
     for (int j = 0; j < n; ++j)
       copy_shared_item(a, Lp, L.pfb + shared_off<true>(a) + (uint32_t)j * shared_item_bytes(a),
-                       (int)blockIdx.x + j * (int)gridDim.x, w, nw);
+                       (int)blockIdx.x + j * a.G, w, nw);
   }
 }
 
@@ -495,28 +560,30 @@ __device__ __forceinline__ void pf_shared_items(const PersistArgs& a, const Laye
                                                 int nw) {
   const int n = shared_pf_count<false>(a);
   for (int j = 0; j < n; ++j)
-    copy_shared_item(a, Lp, L.pfb + (uint32_t)j * shared_item_bytes(a), (int)blockIdx.x + j * (int)gridDim.x, w,
+    copy_shared_item(a, Lp, L.pfb + (uint32_t)j * shared_item_bytes(a), (int)blockIdx.x + j * a.G, w,
                      nw);
 }
 
 template <bool SMALL>
 __device__ __forceinline__ void pf_tiles(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
   const int na = *L.nact, tiles = a.F / kGateTile, base = gu_items_base<SMALL>(a);
-  const int n = tile_pf_count<SMALL>(a, na), j0 = my_count(base);
+  const int n = tile_pf_count<SMALL>(a, na), j0 = my_count(a, base);
   for (int j = 0; j < n; ++j) {
-    const int r = (int)blockIdx.x + (j0 + j) * (int)gridDim.x - base;
+    const int r = (int)blockIdx.x + (j0 + j) * a.G - base;
     copy_tile(a, Lp, L.pfb + tile_off<SMALL>(a) + (uint32_t)j * gu_tile_bytes(a), L.act[r / tiles],
               (r % tiles) * kGateTile, w, nw);
   }
 }
 
+template <bool SMALL>
 __device__ __forceinline__ void pf_down(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
   const int r0 = blockIdx.x * kDownRows;
   if (r0 >= a.H) return;
-  copy_sd_rows(a, Lp, L, r0, w, nw);
-  const int n = down_pf_count(a, *L.nact);
+  QS_LDS uint8_t* base = L.pfb + down_base<SMALL>(a);
+  copy_sd_rows(a, Lp, base, r0, w, nw);
+  const int n = down_pf_count<SMALL>(a, *L.nact);
   for (int u = 0; u < n; ++u)
-    copy_down_rows(a, Lp, L.pfb + al16(sd_bytes(a)) + (uint32_t)u * dn_expert_bytes(a), L.act[u], r0, w, nw);
+    copy_down_rows(a, Lp, base + al16(sd_bytes(a)) + (uint32_t)u * dn_expert_bytes(a), L.act[u], r0, w, nw);
 }
 
 // ------------------------------------------------------------ phase R ---
@@ -542,7 +609,7 @@ __device__ __forceinline__ float4 x_f4(const PersistArgs& a, const PersistLds& L
 // is the same for every batch size.
 template <bool SMALL>
 __device__ __forceinline__ void token_rinv(const PersistArgs& a, PersistLds& L, const float* x, int t0, int n) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
   const int hw = a.H / nw;
   for (int j = 0; j < n; ++j) {
     double s = 0.0;
@@ -552,10 +619,10 @@ __device__ __forceinline__ void token_rinv(const PersistArgs& a, PersistLds& L, 
     if (lane == 0) L.red[wave * 4 + j] = s;
   }
   __syncthreads();
-  if ((int)threadIdx.x < n) {
+  if (qs_tid() < n) {
     double q = 0.0;
-    for (int w = 0; w < nw; ++w) q += L.red[w * 4 + threadIdx.x];
-    L.rinv[t0 + threadIdx.x] = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
+    for (int w = 0; w < nw; ++w) q += L.red[w * 4 + qs_tid()];
+    L.rinv[t0 + qs_tid()] = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
   }
   __syncthreads();
 }
@@ -567,15 +634,16 @@ __device__ __forceinline__ void token_rinv(const PersistArgs& a, PersistLds& L, 
 template <bool SMALL>
 __device__ __forceinline__ void phase_router(const PersistArgs& a, const LayerPtrs& Lp, const float* x,
                                              PersistLds& L) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
   const int ET = a.r_et, TT = a.r_tt;
   const int ntt = (a.T + TT - 1) / TT;
   const int hw = a.H / nw;
   const int V = ET * TT + TT;
   const bool want_ss = !SMALL && a.prenorm;
   const QS_LDS float* wr = (const QS_LDS float*)L.pfb;
+  if (!SMALL) wait_all_and_sync();   // router rows prefetched during the last barrier
   int i = 0;
-  for (int eg = blockIdx.x; eg < router_groups(a); eg += gridDim.x, ++i) {
+  for (int eg = blockIdx.x; eg < router_groups(a); eg += a.G, ++i) {
     if (i > 0) stage_now([&](int w, int n) { copy_router_rows(a, Lp, L, eg, w, n); });
     const int e0 = eg * ET;
 #pragma unroll 1
@@ -628,8 +696,8 @@ __device__ __forceinline__ void phase_router(const PersistArgs& a, const LayerPt
           }
       }
       __syncthreads();
-      if ((int)threadIdx.x < ET * TT) {
-        const int ii = threadIdx.x / TT, j = threadIdx.x % TT;
+      if (qs_tid() < ET * TT) {
+        const int ii = qs_tid() / TT, j = qs_tid() % TT;
         const int e = e0 + ii, t = t0 + j;
         if (e < a.E && j < nt) {
           double s = 0.0, q = 0.0;
@@ -656,7 +724,7 @@ __device__ __forceinline__ void phase_router(const PersistArgs& a, const LayerPt
 template <bool SMALL>
 __device__ __forceinline__ void shared_gu_item(const PersistArgs& a, lds_cptr wbase, const float* x, int item,
                                                PersistLds& L) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
   const int rw = wave >> 2, qtr = wave & 3;
   const int hq = a.H / 4;
   const int T = a.T;
@@ -689,7 +757,7 @@ __device__ __forceinline__ void shared_gu_item(const PersistArgs& a, lds_cptr wb
   }
   __syncthreads();
   // combine the 4 quarter-row partials in a fixed order
-  for (int q = threadIdx.x; q < kSharedItemRows * T; q += blockDim.x) {
+  for (int q = qs_tid(); q < kSharedItemRows * T; q += kPersistThreads) {
     const int r = q / T, t = q % T;
     const int ff = item * kSharedItemRows + r;
     float g = 0.f, u = 0.f;
@@ -709,7 +777,7 @@ __device__ __forceinline__ void shared_items(const PersistArgs& a, const LayerPt
   const int npf = shared_pf_count<SMALL>(a);
   const uint32_t off = shared_off<SMALL>(a), item_b = shared_item_bytes(a);
   int j = 0;
-  for (int it = blockIdx.x; it < n_shared_items(a); it += gridDim.x, ++j) {
+  for (int it = blockIdx.x; it < n_shared_items(a); it += a.G, ++j) {
     uint32_t slot = off + (uint32_t)j * item_b;
     if (j >= npf) {      // not prefetched: copy into the first slot (already consumed)
       slot = off;
@@ -726,7 +794,7 @@ __device__ __forceinline__ void shared_items(const PersistArgs& a, const LayerPt
 // token).  Workgroup 0 / the token's wave also writes ids_out / w_out.
 template <bool SMALL>
 __device__ __forceinline__ void topk_wave(const PersistArgs& a, int t, int layer_i, PersistLds& L, bool write_out) {
-  const int lane = threadIdx.x & 63;
+  const int lane = qs_tid() & 63;
   const int E = a.E, k = a.k;
   double v[16];
 #pragma unroll
@@ -778,11 +846,164 @@ __device__ __forceinline__ void topk_wave(const PersistArgs& a, int t, int layer
   }
 }
 
+// SMALL top-k of every token by the whole workgroup, exact in (logit desc,
+// index asc).  Rounding a logit to fp32 is monotone, so fp32 keys give a
+// cheap superset of the top-k: take the largest key of each group of 8
+// experts; the k-th largest of those group maxima, tau, is a lower bound of
+// the key of every top-k expert (k groups hold an expert with a key >= tau,
+// and a key that is larger means a larger logit).  The experts with key >=
+// tau -- usually few more than k -- are then ranked exactly in fp64.  NaN
+// logits rank as -inf.
+__device__ __forceinline__ double nan_low(double v) { return v != v ? -INFINITY : v; }
+
+// order-preserving int of a float (for an atomic minimum)
+__device__ __forceinline__ int f32_ord(float f) {
+  const int i = __float_as_int(f);
+  return i >= 0 ? i : (int)(0x80000000u - (uint32_t)i) ;
+}
+__device__ __forceinline__ float f32_unord(int o) {
+  return __int_as_float(o >= 0 ? o : (int)(0x80000000u - (uint32_t)o));
+}
+
+__device__ __forceinline__ void topk_small(const PersistArgs& a, int layer_i, PersistLds& L) {
+  const int tid = qs_tid(), nt = kPersistThreads, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, k = a.k, T = a.T, S = kf_stride(E), NG = S / 8, G4 = (NG + 3) & ~3;
+  QS_LDS float* gm = L.kf + T * S;                 // [T][G4] group maxima, -inf padded
+  QS_LDS int* tau = (QS_LDS int*)(gm + T * G4);    // [T]
+  for (int i = tid; i < T * S; i += nt) {
+    const int t = i / S, e = i % S;
+    L.kf[i] = e < E ? (float)nan_low(L.lg[t * E + e]) : -INFINITY;
+  }
+  if (tid < T) {
+    L.ncand[tid] = 0;
+    // fewer than k groups: no bound, every expert is a candidate
+    tau[tid] = NG < k ? f32_ord(-INFINITY) : 0x7FFFFFFF;
+  }
+  __syncthreads();
+  for (int i = tid; i < T * G4; i += nt) {
+    const int t = i / G4, g = i % G4;
+    float mx = -INFINITY;
+    if (g < NG) {
+      const float4 p = lds_f4(L.kf + t * S + g * 8), q = lds_f4(L.kf + t * S + g * 8 + 4);
+      mx = fmaxf(fmaxf(fmaxf(p.x, p.y), fmaxf(p.z, p.w)), fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
+    }
+    gm[i] = mx;
+  }
+  __syncthreads();
+  // tau = the smallest group maximum with fewer than k larger ones
+  if (NG >= k) {
+    for (int i = tid; i < T * G4; i += nt) {
+      const int t = i / G4;
+      if (i % G4 >= NG) continue;
+      const QS_LDS float* row = gm + t * G4;
+      const float g = gm[i];
+      int c = 0;
+#pragma unroll 4
+      for (int j = 0; j < G4; j += 4) {
+        const float4 q = lds_f4(row + j);
+        c += (q.x > g) + (q.y > g) + (q.z > g) + (q.w > g);
+      }
+      if (c < k) __hip_atomic_fetch_min(&tau[t], f32_ord(g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < T * E; i += nt) {
+    const int t = i / E, e = i % E;
+    if (L.kf[t * S + e] >= f32_unord(tau[t])) {
+      const int slot = __hip_atomic_fetch_add(&L.ncand[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      L.cand[t * E + slot] = e;
+    }
+  }
+  __syncthreads();
+  if (wave < T) {                      // exact rank among the candidates, one wave per token
+    const int t = wave, m = L.ncand[t];
+    const QS_LDS int* cd = L.cand + t * E;
+    for (int i0 = 0; i0 < m; i0 += 64) {
+      const int i = i0 + lane;
+      const int e = i < m ? cd[i] : 0;
+      const double v = i < m ? nan_low(L.lg[t * E + e]) : 0.0;
+      int r = 0;
+      for (int j0 = 0; j0 < m; j0 += 64) {
+        // candidates j0..j0+63 broadcast from the lanes that hold them
+        const int ej = j0 + lane < m ? cd[j0 + lane] : 0;
+        const double vj = j0 + lane < m ? nan_low(L.lg[t * E + ej]) : 0.0;
+        const int nj = m - j0 < 64 ? m - j0 : 64;
+        for (int j = 0; j < nj; ++j) {
+          const int e2 = __builtin_amdgcn_readlane(ej, j);
+          const double v2 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(vj), j),
+                                             __builtin_amdgcn_readlane(__double2loint(vj), j));
+          r += (v2 > v || (v2 == v && e2 < e)) ? 1 : 0;
+        }
+      }
+      if (i < m && r < k) {
+        L.ids[t * k + r] = e;
+        L.sv[t * k + r] = v;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave < T) {                      // renormalised softmax over the picks
+    const int t = wave;
+    const double top0 = L.sv[t * k];
+    const double z = lane < k ? exp(L.sv[t * k + lane] - top0) : 0.0;
+    const double sum = bfly_sum_f64<6>(z);
+    if (lane < k) {
+      const float w = (float)(z / sum);
+      L.wl[t * k + lane] = w;
+      if (blockIdx.x == 0) {
+        const size_t o = (size_t)layer_i * T * k + t * k + lane;
+        if (a.ids_out) a.ids_out[o] = L.ids[t * k + lane];
+        if (a.w_out) a.w_out[o] = w;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// SMALL grouping by wave 0 (P = T*k <= 64 pairs, one per lane): sort the
+// pairs by (expert, pair id) -- stable by token -- with a rank count, move
+// each to the lane of its rank, mark the first pair of each expert (a scan
+// of the marks numbers the active experts), and place each position in its
+// token's ascending list with one ballot per token.
+__device__ __forceinline__ void group_small(const PersistArgs& a, PersistLds& L) {
+  const int lane = qs_tid() & 63, k = a.k, P = a.T * k;
+  if ((qs_tid() >> 6) == 0) {
+    const bool live = lane < P;
+    const int e = live ? valid_id(L.ids[lane], a.E) : 0x7FFF;
+    const int key = e * 64 + lane;                 // unique; dead lanes sort last
+    int rank = 0;
+    for (int q = 0; q < P; ++q) rank += (int)(__builtin_amdgcn_readlane(key, q) < key);
+    // lane r receives the key of the pair ranked r
+    const int ks = __builtin_amdgcn_ds_permute(rank * 4, key);
+    const int es = ks >> 6, ps = ks & 63;
+    const int prev = __builtin_amdgcn_ds_bpermute((lane > 0 ? lane - 1 : 0) * 4, es);
+    const int head = (lane < P && (lane == 0 || prev != es)) ? 1 : 0;
+    const int u = wave_incl_scan(head) - 1;
+    if (head) {
+      L.act[u] = es;
+      L.aoff[u] = lane;
+    }
+    const int na = __builtin_amdgcn_readlane(u, 63) + 1;
+    if (lane == 0) {
+      *L.nact = na;
+      L.aoff[na] = P;
+    }
+    const int tok = ps / k;
+    if (live) L.pairs[lane] = ps;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int tt = 0; tt < a.T; ++tt) {
+      const uint64_t m = __ballot(live && tok == tt);
+      if (live && tok == tt) L.tok_order[tt * k + __popcll(m & below)] = lane;
+    }
+  }
+  __syncthreads();
+}
+
 // x block b (256 elements) of token t -> limbs, one wave.  SMALL: from and
 // into LDS; otherwise global scratch.
 template <bool SMALL>
 __device__ __forceinline__ void quant_x_wave(const PersistArgs& a, const float* x, int t, int b, PersistLds& L) {
-  const int lane = threadIdx.x & 63;
+  const int lane = qs_tid() & 63;
   const float4 v = x_f4<SMALL>(a, L, x, t, b * kBlockW + 4 * lane);
   const float r = SMALL ? (float)L.rinv[t] : (float)cldd(&a.rinv[t]);
   const float m = bfly_max<6>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
@@ -839,7 +1060,7 @@ __device__ __forceinline__ void quant_x_wave(const PersistArgs& a, const float* 
 // Stable bucket sort of (token, slot) pairs by expert.
 template <bool SMALL>
 __device__ __forceinline__ void build_groups(const PersistArgs& a, PersistLds& L) {
-  const int tid = threadIdx.x, nt = blockDim.x, E = a.E, k = a.k, T = a.T, P = T * k;
+  const int tid = qs_tid(), nt = kPersistThreads, E = a.E, k = a.k, T = a.T, P = T * k;
   const int wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < E; i += nt) L.cnt[i] = 0;
   for (int i = tid; i < E * 8; i += nt) L.mask[i] = 0;
@@ -884,9 +1105,13 @@ __device__ __forceinline__ void build_groups(const PersistArgs& a, PersistLds& L
     const int sf = wave_incl_scan(cv > 0 ? 1 : 0) + bf;
     if (e < E) {
       L.off[e] = sc - cv;
-      if (cv > 0) L.act[sf - 1] = e;
+      if (cv > 0) {
+        L.act[sf - 1] = e;
+        L.aoff[sf - 1] = sc - cv;
+      }
       if (e == E - 1) {
         L.off[E] = sc;
+        L.aoff[sf] = sc;
         *L.nact = sf;
       }
     }
@@ -953,14 +1178,14 @@ __device__ __forceinline__ void x_chunk(const PersistArgs& a, const PersistLds& 
 // token of its bucket; each 64-weight chunk is decoded once and applied to
 // the tokens one at a time.  SwiGLU outputs are quantised per 16 rows.
 template <int FMT, bool SMALL>
-__device__ __forceinline__ void routed_gu_tile(const PersistArgs& a, lds_cptr tile, int e, int f0, PersistLds& L) {
-  const int p0 = L.off[e], n = L.off[e + 1] - p0;
+__device__ __forceinline__ void routed_gu_tile(const PersistArgs& a, lds_cptr tile, int u, int f0, PersistLds& L) {
+  const int p0 = L.aoff[u], n = L.aoff[u + 1] - p0;
   const int nbh = a.H / kBlockW;
   const int nch = a.H / kChunkW;
   const int lpr = lanes_per_row(nch);
   const int cpl = nch / lpr;
-  const int slots = blockDim.x / lpr;
-  const int slot = threadIdx.x / lpr, j = threadIdx.x % lpr;
+  const int slots = kPersistThreads / lpr;
+  const int slot = qs_tid() / lpr, j = qs_tid() % lpr;
   constexpr bool q2k = FMT == 1;
   const TileLds tl = tile_lds(a);
   lds_cptr gq = tile, uq_ = tile + tl.qb, gs = tile + tl.s, us = tile + tl.s + tl.sb, gd = tile + tl.d,
@@ -1037,7 +1262,7 @@ __device__ __forceinline__ void routed_gu_tile(const PersistArgs& a, lds_cptr ti
   }
   __syncthreads();
   // quantise each bucket token's 16 outputs: 16 lanes per token
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
   for (int tb = wave * 4; tb < n; tb += nw * 4) {
     const int tt = tb + (lane >> 4), r = lane & 15;
     const bool live = tt < n;
@@ -1076,31 +1301,31 @@ __device__ __forceinline__ void routed_tiles(const PersistArgs& a, const LayerPt
   const int npf = tile_pf_count<SMALL>(a, na);
   const uint32_t off = tile_off<SMALL>(a), tb = gu_tile_bytes(a);
   int j = 0;
-  for (int it = (int)blockIdx.x + my_count(base) * (int)gridDim.x; it < base + na * tiles;
-       it += gridDim.x, ++j) {
+  for (int it = (int)blockIdx.x + my_count(a, base) * a.G; it < base + na * tiles;
+       it += a.G, ++j) {
     const int r = it - base;
-    const int e = L.act[r / tiles], f0 = (r % tiles) * kGateTile;
+    const int u = r / tiles, f0 = (r % tiles) * kGateTile;
     uint32_t slot = off + (uint32_t)j * tb;
     if (j >= npf) {
       slot = off;
-      stage_now([&](int w, int n) { copy_tile(a, Lp, L.pfb + off, e, f0, w, n); });
+      stage_now([&](int w, int n) { copy_tile(a, Lp, L.pfb + off, L.act[u], f0, w, n); });
     }
-    routed_gu_tile<FMT, SMALL>(a, L.pfb + slot, e, f0, L);
+    routed_gu_tile<FMT, SMALL>(a, L.pfb + slot, u, f0, L);
   }
 }
 
 // ------------------------------------------------------------ phase D ---
-// One wave: rows r0..r0+7 of expert e (in LDS) against every pair of its bucket.
+// One wave: rows r0..r0+7 of active expert u (in LDS) against every pair of its bucket.
 template <bool SMALL>
-__device__ __forceinline__ void down_expert(const PersistArgs& a, lds_cptr w, int e, PersistLds& L) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void down_expert(const PersistArgs& a, lds_cptr w, int u, PersistLds& L) {
+  const int lane = qs_tid() & 63;
   const int nb = a.F / kBlockW;
   const int nch = a.F / kChunkW;
   const int lpr = lanes_per_row(nch);
   const int cpl = nch / lpr;
   const int rpi = 64 / lpr;
   const int rsub = lane / lpr, j = lane % lpr;
-  const int q0 = L.off[e], q1 = L.off[e + 1];
+  const int q0 = L.aoff[u], q1 = L.aoff[u + 1];
   lds_cptr wq = w, ws = w + kDownRows * nb * 64, wd = w + kDownRows * nb * 80;
 #pragma unroll 1
   for (int rr = rsub; rr < kDownRows; rr += rpi) {
@@ -1163,7 +1388,7 @@ __device__ __forceinline__ void down_expert(const PersistArgs& a, lds_cptr w, in
 // Shared expert down row (in LDS), one wave, lanes over Fs, all tokens.
 template <bool SMALL>
 __device__ __forceinline__ void shared_down_row(const PersistArgs& a, lds_cptr srow, PersistLds& L) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
 #pragma unroll 1
   for (int t = 0; t < a.T; ++t) {
     float s = 0.f;
@@ -1197,15 +1422,18 @@ __device__ __forceinline__ void shared_down_row(const PersistArgs& a, lds_cptr s
   }
 }
 
-template <bool SMALL>
+// `after_wait(w, nw)` runs once, right after the first wait for this
+// phase's inputs (copies issued there overlap the down GEMVs).
+template <bool SMALL, class AW>
 __device__ __forceinline__ void phase_down(const PersistArgs& a, const LayerPtrs& Lp, const float* x, float* y,
-                                           PersistLds& L) {
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+                                           PersistLds& L, AW&& after_wait) {
+  const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
   const int na = *L.nact;
   const int n_tiles = a.H / kDownRows;
   const int T = a.T, P = a.T * a.k;
-  const int chunk = down_chunk(a);
+  const int chunk = down_chunk<SMALL>(a);
   const uint32_t pe = dn_expert_bytes(a), sdb = al16(sd_bytes(a));
+  QS_LDS uint8_t* base = L.pfb + down_base<SMALL>(a);
   if (SMALL) {
     // every pair's SwiGLU limbs and the shared SwiGLU vector -> LDS
     dma_to_lds<kCoherent>(a.ah, L.dah, (uint32_t)P * a.F, wave, nw);
@@ -1214,29 +1442,32 @@ __device__ __forceinline__ void phase_down(const PersistArgs& a, const LayerPtrs
     dma_to_lds<kCoherent>(a.aa, L.daa, (uint32_t)P * a.F / 4, wave, nw);
     if (a.Fs) dma_to_lds<kCoherent>(a.ash, L.dash, (uint32_t)T * a.Fs * 4, wave, nw);
   }
-  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  for (int tile = blockIdx.x; tile < n_tiles; tile += a.G) {
     const int r0 = tile * kDownRows;
     const bool first = tile == (int)blockIdx.x;
     // residual inputs of this tile, requested before the wait
     float xres = 0.f;
-    if (a.residual && (int)threadIdx.x < T * kDownRows)
-      xres = cldf(&x[(size_t)(threadIdx.x / kDownRows) * a.H + r0 + threadIdx.x % kDownRows]);
-    if (first && SMALL) wait_all_and_sync();
+    if (a.residual && qs_tid() < T * kDownRows)
+      xres = cldf(&x[(size_t)(qs_tid() / kDownRows) * a.H + r0 + qs_tid() % kDownRows]);
+    if (first) {
+      wait_all_and_sync();   // the tile's prefetched rows (and SMALL activations)
+      after_wait(wave, nw);
+    }
     // experts in chunks that fit beside the shared rows; the first chunk of
     // the first tile (and its shared rows) arrived during the barrier
     for (int u0 = 0; u0 < na; u0 += chunk) {       // na >= 1, chunk >= 1
       const int u1 = na - u0 < chunk ? na : u0 + chunk;
       if (!first || u0 > 0) {
         stage_now([&](int w, int n) {
-          if (u0 == 0) copy_sd_rows(a, Lp, L, r0, w, n);
-          for (int u = u0; u < u1; ++u) copy_down_rows(a, Lp, L.pfb + sdb + (uint32_t)(u - u0) * pe, L.act[u], r0, w, n);
+          if (u0 == 0) copy_sd_rows(a, Lp, base, r0, w, n);
+          for (int u = u0; u < u1; ++u) copy_down_rows(a, Lp, base + sdb + (uint32_t)(u - u0) * pe, L.act[u], r0, w, n);
         });
       }
-      for (int u = u0 + wave; u < u1; u += nw) down_expert<SMALL>(a, L.pfb + sdb + (uint32_t)(u - u0) * pe, L.act[u], L);
-      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<SMALL>(a, L.pfb + (uint32_t)wave * a.Fs * 2, L);
+      for (int u = u0 + wave; u < u1; u += nw) down_expert<SMALL>(a, base + sdb + (uint32_t)(u - u0) * pe, u, L);
+      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<SMALL>(a, base + (uint32_t)wave * a.Fs * 2, L);
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < T * kDownRows; idx += blockDim.x) {
+    for (int idx = qs_tid(); idx < T * kDownRows; idx += kPersistThreads) {
       const int t = idx / kDownRows, rr = idx % kDownRows, h = r0 + rr;
       float acc = 0.f;
       for (int jj = 0; jj < a.k; ++jj) {
@@ -1245,13 +1476,16 @@ __device__ __forceinline__ void phase_down(const PersistArgs& a, const LayerPtrs
         acc = fmaf(L.wl[pair], L.o[pos * kDownRows + rr], acc);
       }
       if (a.Fs) acc += L.sh[idx];
-      if (a.residual) acc += idx == (int)threadIdx.x ? xres : cldf(&x[(size_t)t * a.H + h]);
+      if (a.residual) acc += idx == qs_tid() ? xres : cldf(&x[(size_t)t * a.H + h]);
       cstf(&y[(size_t)t * a.H + h], acc);
     }
     __syncthreads();     // L.o and L.sh are rewritten by the next tile
   }
-  // a workgroup without tiles still has its copies in flight
-  if (SMALL && (int)blockIdx.x >= n_tiles) wait_all_and_sync();
+  // a workgroup without tiles
+  if ((int)blockIdx.x >= n_tiles) {
+    if (SMALL) wait_all_and_sync();
+    after_wait(wave, nw);
+  }
 }
 
 // ------------------------------------------------------------- kernel ---
@@ -1259,7 +1493,7 @@ template <int FMT, bool SMALL>
 __global__ void __launch_bounds__(kPersistThreads) k_persist(PersistArgs a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   PersistLds L = carve_lds<SMALL>(lds_raw, a, FMT == 2);
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
   if (FMT == 2) dma_to_lds<0>(a.cbtab, L.tab, (uint32_t)kCbTabWords * 4, wave, nw);
   pf_router_and_shared<SMALL>(a, a.layers[0], L, wave, nw);
   wait_all_and_sync();
@@ -1268,6 +1502,7 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist(PersistArgs a) {
     const LayerPtrs Lp = a.layers[li];
     const float* x = li == 0 ? a.x_in : ((li - 1) & 1 ? a.xbuf1 : a.xbuf0);
     float* y = li == a.n_layers - 1 ? a.y_out : (li & 1 ? a.xbuf1 : a.xbuf0);
+    const bool more = li + 1 < a.n_layers;
     if (SMALL) {
       // ---- R: x -> LDS, RMS scales, router, shared gate/up
       dma_to_lds<kCoherent>(x, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
@@ -1279,22 +1514,32 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist(PersistArgs a) {
       // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
       dma_to_lds<kCoherent>(a.logits, L.lg, (uint32_t)a.T * a.E * 8, wave, nw);
       wait_all_and_sync();
-      if (wave < a.T) topk_wave<true>(a, wave, li, L, blockIdx.x == 0);
-      __syncthreads();
-      build_groups<true>(a, L);
+      topk_small(a, li, L);
+      group_small(a, L);
       pf_tiles<true>(a, Lp, L, wave, nw);
       {
         const int nb = a.H / kBlockW;
         for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, x, u / nb, u % nb, L);
       }
       wait_all_and_sync();
+      // ---- GU
       routed_tiles<FMT, true>(a, Lp, L);
+      // down rows -> region B; region A is free: the next layer's router rows
+      // and shared items
+      if (!grid_barrier(a, ++epoch, [&](int w, int n) {
+            pf_down<true>(a, Lp, L, w, n);
+            if (more) pf_router_and_shared<true>(a, a.layers[li + 1], L, w, n);
+          }))
+        return;
+      // ---- D
+      phase_down<true>(a, Lp, x, y, L, [](int, int) {});
+      if (more && !grid_barrier(a, ++epoch, [](int, int) {})) return;
     } else {
       phase_router<false>(a, Lp, x, L);
       if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_shared_items(a, Lp, L, w, n); })) return;
       {
         const int nb = a.H / kBlockW, units = a.T + a.T * nb;
-        for (int u = blockIdx.x * nw + wave; u < units; u += gridDim.x * nw) {
+        for (int u = blockIdx.x * nw + wave; u < units; u += a.G * nw) {
           if (u < a.T) topk_wave<false>(a, u, li, L, true);
           else quant_x_wave<false>(a, x, (u - a.T) / nb, (u - a.T) % nb, L);
         }
@@ -1305,12 +1550,12 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist(PersistArgs a) {
       shared_items<false>(a, Lp, x, L);
       wait_all_and_sync();
       routed_tiles<FMT, false>(a, Lp, L);
-    }
-    if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_down(a, Lp, L, w, n); })) return;
-    phase_down<SMALL>(a, Lp, x, y, L);
-    if (li + 1 < a.n_layers) {
-      const LayerPtrs Ln = a.layers[li + 1];
-      if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_router_and_shared<SMALL>(a, Ln, L, w, n); })) return;
+      if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_down<false>(a, Lp, L, w, n); })) return;
+      phase_down<false>(a, Lp, x, y, L, [](int, int) {});
+      if (more && !grid_barrier(a, ++epoch, [&](int w, int n) {
+            pf_router_and_shared<false>(a, a.layers[li + 1], L, w, n);
+          }))
+        return;
     }
   }
 }
