@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqsmoe.so")
 SOURCES = ["qs_moe.hip"]
-HEADERS = ["qs_kernels.h", "qs_layout.h", "qs_persist.h", "qs_wave.h"]
+HEADERS = ["qs_big.h", "qs_kernels.h", "qs_layout.h", "qs_persist.h", "qs_wave.h"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

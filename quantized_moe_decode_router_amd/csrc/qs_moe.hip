@@ -19,6 +19,7 @@
 #include "qs_kernels.h"
 #include "qs_layout.h"
 #include "qs_persist.h"
+#include "qs_big.h"
 
 using namespace qs;
 
@@ -60,6 +61,9 @@ struct Scratch {
   float* ash;
   float* xbuf[2];
   double* rinv;
+  float* af;     // batched persistent flow: SwiGLU outputs of MFMA buckets [P][F]
+  float* ob;     // routed down outputs by bucket position [P][H]
+  float* sb;     // shared-expert down outputs [T][H]
 };
 
 }  // namespace
@@ -83,7 +87,8 @@ struct qs_moe {
   int grid = 0;                   // workgroups of the persistent kernel (one per CU)
   size_t lds_limit = 0;           // LDS bytes per workgroup available on the device
   bool persist_small_ok = false; // T <= kSmallT instantiation usable
-  bool persist_big_ok = false;   // T > kSmallT instantiation usable
+  bool persist_big_ok = false;   // batched instantiation usable
+  int mfma_min = 16;              // bucket size from which the MFMA path runs
 };
 
 namespace {
@@ -178,6 +183,9 @@ size_t scratch_bytes(const qs_moe_config& c) {
   add(T * (size_t)(c.shared_ffn ? c.shared_ffn : 1) * 4);
   add(T * H * 4); add(T * H * 4); // residual ping-pong
   add(T * 8);                     // rinv
+  add(P * F * 4);                 // af
+  add(P * H * 4);                 // ob
+  add(T * H * 4);                 // sb
   return b;
 }
 
@@ -206,6 +214,9 @@ void carve_scratch(const qs_moe_config& c, Scratch& s) {
   s.xbuf[0] = carve<float>(p, T * H);
   s.xbuf[1] = carve<float>(p, T * H);
   s.rinv = carve<double>(p, T);
+  s.af = carve<float>(p, P * F);
+  s.ob = carve<float>(p, P * H);
+  s.sb = carve<float>(p, T * H);
 }
 
 void free_all(qs_moe* h) {
@@ -233,8 +244,23 @@ struct PersistShape {
   int r_et = 1, r_tt = 1;
 };
 
+PersistShape big_shape(const qs_moe* h, int T) {
+  const qs_moe_config& c = h->cfg;
+  PersistShape p;
+  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
+  const size_t base = big_layout(c.n_experts, T, T * c.top_k, cb2, 0).end;
+  if (base >= h->lds_limit || h->grid < 8) return p;
+  p.pfb = (uint32_t)std::min((size_t)kPfbMax, (h->lds_limit - base) & ~(size_t)15);
+  p.lds = base + p.pfb;
+  p.r_tt = T < 4 ? T : 4;
+  while (p.r_et < 4 && (c.n_experts + p.r_et - 1) / p.r_et > h->grid) p.r_et *= 2;
+  p.ok = big_plan(c.hidden, c.expert_ffn, c.shared_ffn, !cb2, p.pfb, p.r_et * c.hidden * 4).ok;
+  return p;
+}
+
 PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   const qs_moe_config& c = h->cfg;
+  if (!small) return big_shape(h, T);
   PersistShape p;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
   const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, cb2, small,
@@ -269,8 +295,8 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
 }
 
 const void* persist_fn(bool cb2, bool small) {
-  if (cb2) return small ? (const void*)k_persist<2, true> : (const void*)k_persist<2, false>;
-  return small ? (const void*)k_persist<1, true> : (const void*)k_persist<1, false>;
+  if (cb2) return small ? (const void*)k_persist_small<2> : (const void*)k_persist_big<2>;
+  return small ? (const void*)k_persist_small<1> : (const void*)k_persist_big<1>;
 }
 
 // Every workgroup must be resident at once for the grid barrier (a
@@ -353,9 +379,9 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
                       bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
   const qs_moe_config& c = h->cfg;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
-  // small batches take the SMALL instantiation when its working set fits,
-  // otherwise the general one
-  bool small = T <= kSmallT && h->persist_small_ok;
+  // small batches take the SMALL instantiation when its working set fits and
+  // no bucket can reach the MFMA size, otherwise the batched one
+  bool small = T <= kSmallT && T < h->mfma_min && h->persist_small_ok;
   PersistShape p;
   if (small) {
     p = persist_shape(h, T, true);
@@ -366,7 +392,7 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
     p = persist_shape(h, T, false);
     if (!p.ok) return 1;
   }
-  const uint32_t barriers = (small ? 3u : 4u) * nL - 1u;
+  const uint32_t barriers = (small ? 3u : 5u) * nL - 1u;
   if (h->epoch + barriers > (1u << 26)) {
     hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
     h->epoch = 0;
@@ -392,6 +418,8 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   a.xh = s.xh; a.xl = s.xl; a.xs = s.xs; a.xa = s.xa;
   a.ah = s.ah; a.al = s.al; a.as = s.as; a.aa = s.aa; a.ash = s.ash;
   a.xbuf0 = s.xbuf[0]; a.xbuf1 = s.xbuf[1];
+  a.mfma_min = h->mfma_min;
+  a.af = s.af; a.ob = s.ob; a.sb = s.sb;
   a.sync = h->sync;
   a.epoch0 = h->epoch;
   void* args[] = {&a};
@@ -507,6 +535,7 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   qs_moe* h = new (std::nothrow) qs_moe();
   if (!h) return QS_E_NOMEM;
   h->cfg = *cfg;
+  h->mfma_min = cfg->mfma_min_tokens ? cfg->mfma_min_tokens : 16;
   DeviceGuard dg(cfg->device);
   if (!dg.ok) {
     fprintf(stderr, "qs_moe: hipSetDevice(%d) failed\n", cfg->device);

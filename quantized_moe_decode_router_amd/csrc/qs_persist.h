@@ -15,8 +15,9 @@
 // the kernel's code small enough for the instruction cache: a layer walks
 // through all of it, so code that does not fit is re-fetched every layer.
 //
-// Two instantiations, chosen per call:
-// SMALL (T <= kSmallT), per layer:
+// This file holds the small-batch kernel (T <= kSmallT) and the helpers both
+// persistent kernels share; qs_big.h holds the batched kernel.
+// Small batches, per layer:
 //   R   x -> LDS (one coherent copy); per-token RMS scale; router logits;
 //       the shared expert's gate/up items (they need only x)
 //   --- barrier
@@ -28,8 +29,6 @@
 //       items -> LDS)
 //   D   SwiGLU limbs -> LDS; down GEMVs + combine + shared down + residual
 //   --- barrier
-// otherwise the activations stay in global scratch and one more barrier
-// follows top-k / quantisation (one wave per token or x block).
 //
 // Barrier: per-XCD arrival counters, a global counter bumped by each XCD's
 // last arriver, per-XCD release lines written by the global last arriver.
@@ -102,6 +101,11 @@ struct PersistArgs {
   float* xbuf1;
   uint32_t* sync;
   uint32_t epoch0;
+  // batched flow only
+  int mfma_min;              // bucket size from which the MFMA path runs
+  float* af;                 // [T*k][F] SwiGLU outputs of MFMA buckets (by pair id)
+  float* ob;                 // [T*k][H] routed down outputs (by bucket position)
+  float* sb;                 // [T][H]   shared-expert down outputs
 };
 
 // Thread index through an opaque move: values derived from it are then
@@ -646,6 +650,9 @@ __device__ __forceinline__ void phase_router(const PersistArgs& a, const LayerPt
   for (int eg = blockIdx.x; eg < router_groups(a); eg += a.G, ++i) {
     if (i > 0) stage_now([&](int w, int n) { copy_router_rows(a, Lp, L, eg, w, n); });
     const int e0 = eg * ET;
+    // the bias of the logit this thread finishes, requested before the sums
+    double bias = 0.0;
+    if (qs_tid() < ET * TT && e0 + qs_tid() / TT < a.E) bias = (double)Lp.bias[e0 + qs_tid() / TT];
 #pragma unroll 1
     for (int tg = 0; tg < ntt; ++tg) {
       const int t0 = tg * TT, nt = a.T - t0 < TT ? a.T - t0 : TT;
@@ -708,8 +715,7 @@ __device__ __forceinline__ void phase_router(const PersistArgs& a, const LayerPt
           double r;
           if (SMALL) r = L.rinv[t];
           else r = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
-          const double b = (double)Lp.bias[e];
-          cstd(&a.logits[(size_t)t * a.E + e], a.prenorm ? fma(s, r, b) : s + b);
+          cstd(&a.logits[(size_t)t * a.E + e], a.prenorm ? fma(s, r, bias) : s + bias);
           if (!SMALL && e == 0) cstd(&a.rinv[t], r);
         }
       }
@@ -999,6 +1005,27 @@ __device__ __forceinline__ void group_small(const PersistArgs& a, PersistLds& L)
   __syncthreads();
 }
 
+// Lane l holds the limb bytes of elements 4l..4l+3 of a 256-element block
+// (byte j = element 4l+j).  Returns this lane's dword in the Q2_K consumer
+// order: dword 4i+p of the block holds elements p, 4+p, 8+p, 12+p of 16-wide
+// sub-block i, gathered from byte p of lanes 4i..4i+3.
+__device__ __forceinline__ uint32_t q2k_order(uint32_t v) {
+  const int p = qs_tid() & 3;
+  uint32_t bv[4];
+  bv[0] = v;
+  bv[1] = partner_u32<0>(v);         // lane ^ 1
+  bv[2] = partner_u32<1>(v);         // lane ^ 2
+  bv[3] = partner_u32<1>(bv[1]);     // lane ^ 3
+  uint32_t o = 0;
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    const int src = bb ^ p;          // bv[src] holds the word of lane 4i+bb
+    const uint32_t w = src == 0 ? bv[0] : src == 1 ? bv[1] : src == 2 ? bv[2] : bv[3];
+    o |= ((w >> (8 * p)) & 0xFFu) << (8 * bb);
+  }
+  return o;
+}
+
 // x block b (256 elements) of token t -> limbs, one wave.  SMALL: from and
 // into LDS; otherwise global scratch.
 template <bool SMALL>
@@ -1016,24 +1043,8 @@ __device__ __forceinline__ void quant_x_wave(const PersistArgs& a, const float* 
   split_limbs(q3, h3, l3);
   uint32_t ph = pack4(h0, h1, h2, h3), pl = pack4(l0, l1, l2, l3);
   if (a.gq2k) {
-    // dword 4i+p of sub-block i gathers element p of lanes 4i..4i+3
-    const int p = lane & 3;
-    uint32_t bh[4], bl[4];
-    bh[0] = ph; bl[0] = pl;
-    bh[1] = partner_u32<0>(ph); bl[1] = partner_u32<0>(pl);        // lane ^ 1
-    bh[2] = partner_u32<1>(ph); bl[2] = partner_u32<1>(pl);        // lane ^ 2
-    bh[3] = partner_u32<1>(bh[1]); bl[3] = partner_u32<1>(bl[1]);  // lane ^ 3
-    uint32_t oh = 0, ol = 0;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int src = bb ^ p;                    // bh[src] holds group lane bb's dword
-      const uint32_t hv = src == 0 ? bh[0] : src == 1 ? bh[1] : src == 2 ? bh[2] : bh[3];
-      const uint32_t lv = src == 0 ? bl[0] : src == 1 ? bl[1] : src == 2 ? bl[2] : bl[3];
-      oh |= ((hv >> (8 * p)) & 0xFFu) << (8 * bb);
-      ol |= ((lv >> (8 * p)) & 0xFFu) << (8 * bb);
-    }
-    ph = oh;
-    pl = ol;
+    ph = q2k_order(ph);
+    pl = q2k_order(pl);
   }
   const int s = bfly_sum_i32<2>(q0 + q1 + q2 + q3);
   const float scale = ldexpf(r, e - kFixedBits);
@@ -1489,13 +1500,14 @@ __device__ __forceinline__ void phase_down(const PersistArgs& a, const LayerPtrs
 }
 
 // ------------------------------------------------------------- kernel ---
-template <int FMT, bool SMALL>
-__global__ void __launch_bounds__(kPersistThreads) k_persist(PersistArgs a) {
+// The small-batch kernel (T <= kSmallT); qs_big.h holds the batched one.
+template <int FMT>
+__global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
-  PersistLds L = carve_lds<SMALL>(lds_raw, a, FMT == 2);
+  PersistLds L = carve_lds<true>(lds_raw, a, FMT == 2);
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
   if (FMT == 2) dma_to_lds<0>(a.cbtab, L.tab, (uint32_t)kCbTabWords * 4, wave, nw);
-  pf_router_and_shared<SMALL>(a, a.layers[0], L, wave, nw);
+  pf_router_and_shared<true>(a, a.layers[0], L, wave, nw);
   wait_all_and_sync();
   uint32_t epoch = a.epoch0;
   for (int li = 0; li < a.n_layers; ++li) {
@@ -1503,60 +1515,36 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist(PersistArgs a) {
     const float* x = li == 0 ? a.x_in : ((li - 1) & 1 ? a.xbuf1 : a.xbuf0);
     float* y = li == a.n_layers - 1 ? a.y_out : (li & 1 ? a.xbuf1 : a.xbuf0);
     const bool more = li + 1 < a.n_layers;
-    if (SMALL) {
-      // ---- R: x -> LDS, RMS scales, router, shared gate/up
-      dma_to_lds<kCoherent>(x, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
-      wait_all_and_sync();
-      token_rinv<true>(a, L, x, 0, a.T);
-      phase_router<true>(a, Lp, x, L);
-      shared_items<true>(a, Lp, x, L);
-      if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
-      // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
-      dma_to_lds<kCoherent>(a.logits, L.lg, (uint32_t)a.T * a.E * 8, wave, nw);
-      wait_all_and_sync();
-      topk_small(a, li, L);
-      group_small(a, L);
-      pf_tiles<true>(a, Lp, L, wave, nw);
-      {
-        const int nb = a.H / kBlockW;
-        for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, x, u / nb, u % nb, L);
-      }
-      wait_all_and_sync();
-      // ---- GU
-      routed_tiles<FMT, true>(a, Lp, L);
-      // down rows -> region B; region A is free: the next layer's router rows
-      // and shared items
-      if (!grid_barrier(a, ++epoch, [&](int w, int n) {
-            pf_down<true>(a, Lp, L, w, n);
-            if (more) pf_router_and_shared<true>(a, a.layers[li + 1], L, w, n);
-          }))
-        return;
-      // ---- D
-      phase_down<true>(a, Lp, x, y, L, [](int, int) {});
-      if (more && !grid_barrier(a, ++epoch, [](int, int) {})) return;
-    } else {
-      phase_router<false>(a, Lp, x, L);
-      if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_shared_items(a, Lp, L, w, n); })) return;
-      {
-        const int nb = a.H / kBlockW, units = a.T + a.T * nb;
-        for (int u = blockIdx.x * nw + wave; u < units; u += a.G * nw) {
-          if (u < a.T) topk_wave<false>(a, u, li, L, true);
-          else quant_x_wave<false>(a, x, (u - a.T) / nb, (u - a.T) % nb, L);
-        }
-      }
-      if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
-      build_groups<false>(a, L);
-      pf_tiles<false>(a, Lp, L, wave, nw);
-      shared_items<false>(a, Lp, x, L);
-      wait_all_and_sync();
-      routed_tiles<FMT, false>(a, Lp, L);
-      if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_down<false>(a, Lp, L, w, n); })) return;
-      phase_down<false>(a, Lp, x, y, L, [](int, int) {});
-      if (more && !grid_barrier(a, ++epoch, [&](int w, int n) {
-            pf_router_and_shared<false>(a, a.layers[li + 1], L, w, n);
-          }))
-        return;
+    // ---- R: x -> LDS, RMS scales, router, shared gate/up
+    dma_to_lds<kCoherent>(x, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
+    wait_all_and_sync();
+    token_rinv<true>(a, L, x, 0, a.T);
+    phase_router<true>(a, Lp, x, L);
+    shared_items<true>(a, Lp, x, L);
+    if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
+    // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
+    dma_to_lds<kCoherent>(a.logits, L.lg, (uint32_t)a.T * a.E * 8, wave, nw);
+    wait_all_and_sync();
+    topk_small(a, li, L);
+    group_small(a, L);
+    pf_tiles<true>(a, Lp, L, wave, nw);
+    {
+      const int nb = a.H / kBlockW;
+      for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, x, u / nb, u % nb, L);
     }
+    wait_all_and_sync();
+    // ---- GU
+    routed_tiles<FMT, true>(a, Lp, L);
+    // down rows -> region B; region A is free: the next layer's router rows
+    // and shared items
+    if (!grid_barrier(a, ++epoch, [&](int w, int n) {
+          pf_down<true>(a, Lp, L, w, n);
+          if (more) pf_router_and_shared<true>(a, a.layers[li + 1], L, w, n);
+        }))
+      return;
+    // ---- D
+    phase_down<true>(a, Lp, x, y, L, [](int, int) {});
+    if (more && !grid_barrier(a, ++epoch, [](int, int) {})) return;
   }
 }
 

@@ -143,6 +143,59 @@ def test_batch_invariance_and_determinism(request, name, mk):
     assert torch.equal(yp, y[perm]), "permuting tokens does not permute outputs"
 
 
+# ---- MFMA path (buckets of at least mfma_min_tokens tokens) ------------------
+# mfma_min_tokens=1 sends every bucket through the matrix-core items, =4 mixes
+# GEMV and MFMA buckets inside one call.
+
+@pytest.fixture(scope="module", params=[1, 4], ids=["mfma1", "mfma4"])
+def tiny_mfma(lib, request):
+    wl = workload("tiny_q2k")
+    moe, lws = make_handle(lib, wl, max_tokens=64, mfma_min_tokens=request.param)
+    yield wl, moe, lws, request.param
+    moe.close()
+
+
+@pytest.fixture(scope="module", params=[1, 4], ids=["mfma1", "mfma4"])
+def a3b_mfma(lib, request):
+    wl = workload("a3b_layer")
+    moe, lws = make_handle(lib, wl, max_tokens=32, mfma_min_tokens=request.param)
+    yield wl, moe, lws, request.param
+    moe.close()
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 64])
+def test_decode_tiny_mfma(tiny_mfma, T):
+    wl, moe, lws, thr = tiny_mfma
+    say(f"decode tiny T={T} mfma_min={thr}")
+    _decode_check(wl, moe, lws[0], T, label=f"tiny mfma{thr} T={T}", path="persistent")
+
+
+@pytest.mark.parametrize("T", [1, 7, 32])
+def test_decode_a3b_mfma(a3b_mfma, T):
+    wl, moe, lws, thr = a3b_mfma
+    say(f"decode a3b T={T} mfma_min={thr}")
+    _decode_check(wl, moe, lws[0], T, label=f"a3b mfma{thr} T={T}", path="persistent")
+
+
+def test_mfma_deterministic_and_permutation(a3b_mfma):
+    wl, moe, _, thr = a3b_mfma
+    T = 24
+    say(f"mfma determinism a3b T={T} mfma_min={thr}")
+    x = torch.from_numpy(synth.tokens(wl, T, 4)).cuda()
+    y = moe.decode(x, path="persistent")
+    y2 = moe.decode(x, path="persistent")
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "two runs differ"
+    perm = torch.randperm(T, generator=torch.Generator().manual_seed(3)).cuda()
+    yp = moe.decode(x[perm].contiguous(), path="persistent")
+    torch.cuda.synchronize()
+    # a bucket's tokens sit in other MFMA columns after the permutation; the
+    # integer sums are exact, so only fp32 rounding of the block scales differs
+    err = float(np.max(om.rel_l2(yp.cpu().numpy(), y[perm].cpu().numpy())))
+    say(f"  permuted vs unpermuted: max rel-L2 {err:.3e}, bitwise {torch.equal(yp, y[perm])}")
+    assert err <= 1e-6
+
+
 def test_zero_input_gives_zero(a3b):
     wl, moe, _ = a3b
     say("zero input")
