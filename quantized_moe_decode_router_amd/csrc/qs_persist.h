@@ -1512,9 +1512,10 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a
   uint32_t epoch = a.epoch0;
   for (int li = 0; li < a.n_layers; ++li) {
     const LayerPtrs Lp = a.layers[li];
+    const bool more = li + 1 < a.n_layers;
+    const LayerPtrs Ln = a.layers[more ? li + 1 : li];   // requested now, used at the end of D
     const float* x = li == 0 ? a.x_in : ((li - 1) & 1 ? a.xbuf1 : a.xbuf0);
     float* y = li == a.n_layers - 1 ? a.y_out : (li & 1 ? a.xbuf1 : a.xbuf0);
-    const bool more = li + 1 < a.n_layers;
     // ---- R: x -> LDS, RMS scales, router, shared gate/up
     dma_to_lds<kCoherent>(x, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
     wait_all_and_sync();
@@ -1535,15 +1536,13 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a
     wait_all_and_sync();
     // ---- GU
     routed_tiles<FMT, true>(a, Lp, L);
-    // down rows -> region B; region A is free: the next layer's router rows
-    // and shared items
-    if (!grid_barrier(a, ++epoch, [&](int w, int n) {
-          pf_down<true>(a, Lp, L, w, n);
-          if (more) pf_router_and_shared<true>(a, a.layers[li + 1], L, w, n);
-        }))
-      return;
+    // down rows -> region B during the barrier
+    if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_down<true>(a, Lp, L, w, n); })) return;
     // ---- D
     phase_down<true>(a, Lp, x, y, L, [](int, int) {});
+    // region A is free: the next layer's router rows and shared items, in
+    // flight during the last barrier of the layer
+    if (more) pf_router_and_shared<true>(a, Ln, L, wave, nw);
     if (more && !grid_barrier(a, ++epoch, [](int, int) {})) return;
   }
 }
