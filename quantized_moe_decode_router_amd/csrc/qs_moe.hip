@@ -89,6 +89,7 @@ struct qs_moe {
   bool persist_small_ok = false; // T <= kSmallT instantiation usable
   bool persist_big_ok = false;   // batched instantiation usable
   int mfma_min = 16;              // bucket size from which the MFMA path runs
+  bool fixed_ok = false;          // the fixed-shape small-batch kernels are usable
 };
 
 namespace {
@@ -299,6 +300,31 @@ const void* persist_fn(bool cb2, bool small) {
   return small ? (const void*)k_persist_small<1> : (const void*)k_persist_big<1>;
 }
 
+// Small-batch instantiations with the layer shape fixed at compile time:
+// hidden 2048, 256 experts, top-8, expert width 512, shared width 512 or 0,
+// codebook gate/up, one workgroup per CU of a 256-CU device.
+template <int FS>
+const void* fixed_a3b(int T) {
+  switch (T) {
+    case 1: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, 1, 256>;
+    case 2: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, 2, 256>;
+    case 3: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, 3, 256>;
+    case 4: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, 4, 256>;
+    default: return nullptr;
+  }
+}
+
+// The fixed-shape kernel for a T-token call of this handle, or nullptr.
+const void* persist_fixed_fn(const qs_moe* h, int T) {
+  const qs_moe_config& c = h->cfg;
+  if (h->grid != 256 || c.gate_up_format != QS_FMT_CB2 || c.hidden != 2048 || c.n_experts != 256 ||
+      c.top_k != 8 || c.expert_ffn != 512)
+    return nullptr;
+  if (c.shared_ffn == 512) return fixed_a3b<512>(T);
+  if (c.shared_ffn == 0) return fixed_a3b<0>(T);
+  return nullptr;
+}
+
 // Every workgroup must be resident at once for the grid barrier (a
 // cooperative launch also enforces this).
 bool persist_resident(const qs_moe* h, bool small, size_t lds) {
@@ -370,6 +396,19 @@ int setup_persistent(qs_moe* h) {
   }
   h->persist_small_ok = lds_small && persist_resident(h, true, lds_small);
   h->persist_big_ok = lds_big && persist_resident(h, false, lds_big);
+  // fixed-shape instantiations: the same LDS limit, checked one by one
+  h->fixed_ok = h->persist_small_ok;
+  for (int T = 1; T <= kSmallT && h->fixed_ok; ++T) {
+    const void* fn = persist_fixed_fn(h, T);
+    if (!fn) continue;
+    int occ = 0;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_small) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds_small) != hipSuccess ||
+        occ < 1) {
+      (void)hipGetLastError();
+      h->fixed_ok = false;
+    }
+  }
   return QS_OK;
 }
 
@@ -423,7 +462,11 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   a.sync = h->sync;
   a.epoch0 = h->epoch;
   void* args[] = {&a};
-  hipError_t e = hipLaunchCooperativeKernel(persist_fn(cb2, small), dim3(h->grid), dim3(kPersistThreads), args,
+  // the fixed-shape kernel needs the router unit it assumes (one expert per
+  // workgroup, all tokens at once)
+  const void* fn = small && h->fixed_ok && p.r_et == 1 && p.r_tt == T ? persist_fixed_fn(h, T) : nullptr;
+  if (!fn) fn = persist_fn(cb2, small);
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(kPersistThreads), args,
                                             (unsigned)p.lds, st);
   if (e != hipSuccess) {
     fprintf(stderr, "qs_moe: persistent launch failed: %s\n", hipGetErrorString(e));

@@ -219,8 +219,8 @@ __device__ __forceinline__ void stage_now(CP&& cp) {
 // `pf(w, nw)` issues this workgroup's prefetch copies (waves 1..7 run it,
 // after the drain and while wave 0 waits); they complete in the background
 // and whoever reads them first waits (wait_all_and_sync).
-template <class PF>
-__device__ __forceinline__ bool grid_barrier(const PersistArgs& a, uint32_t epoch, PF&& pf) {
+template <class PF, class A>
+__device__ __forceinline__ bool grid_barrier(const A& a, uint32_t epoch, PF&& pf) {
   const uint32_t x = blockIdx.x & 7u, per = (uint32_t)a.G >> 3;
   __builtin_amdgcn_s_waitcnt(0);     // this wave's coherent stores have completed
   __syncthreads();
@@ -357,8 +357,8 @@ struct PersistLds {
   QS_LDS float* dash;     // [T][Fs]
 };
 
-template <bool SMALL>
-__device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const PersistArgs& a, bool cb2) {
+template <bool SMALL, class A>
+__device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const A& a, bool cb2) {
   const uint32_t T = a.T, H = a.H, E = a.E, F = a.F, P = T * a.k;
   const LdsLayout l = lds_layout(E, T, P, H, F, a.Fs, cb2, SMALL, a.pfb);
   QS_LDS uint8_t* b = (QS_LDS uint8_t*)raw;
@@ -407,26 +407,34 @@ __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const PersistArgs&
 // work) the active-expert count: a workgroup computes the same offsets when
 // it issues a copy and when it consumes it.  The host checks that the
 // buffer holds at least one piece of each kind next to its neighbours.
-__device__ __forceinline__ int my_count(const PersistArgs& a, int n) {   // items b + j*G below n
+template <class A>
+__device__ __forceinline__ int my_count(const A& a, int n) {   // items b + j*G below n
   const int b = blockIdx.x, G = a.G;
   return b < n ? (n - 1 - b) / G + 1 : 0;
 }
 
 // router: expert group eg = b + i*G of r_et rows, staged at [0, router_bytes)
-__device__ __forceinline__ int router_groups(const PersistArgs& a) { return (a.E + a.r_et - 1) / a.r_et; }
-__device__ __forceinline__ uint32_t router_bytes(const PersistArgs& a) { return (uint32_t)a.r_et * a.H * 4; }
+template <class A>
+__device__ __forceinline__ int router_groups(const A& a) { return (a.E + a.r_et - 1) / a.r_et; }
+template <class A>
+__device__ __forceinline__ uint32_t router_bytes(const A& a) { return (uint32_t)a.r_et * a.H * 4; }
 
-__device__ __forceinline__ int n_shared_items(const PersistArgs& a) { return a.Fs / kSharedItemRows; }
-__device__ __forceinline__ uint32_t shared_item_bytes(const PersistArgs& a) {
+template <class A>
+__device__ __forceinline__ int n_shared_items(const A& a) { return a.Fs / kSharedItemRows; }
+template <class A>
+__device__ __forceinline__ uint32_t shared_item_bytes(const A& a) {
   return (uint32_t)kSharedItemRows * 2 * a.H * 2;
 }
-__device__ __forceinline__ uint32_t gu_tile_bytes(const PersistArgs& a) {
+template <class A>
+__device__ __forceinline__ uint32_t gu_tile_bytes(const A& a) {
   const uint32_t nbh = a.H / kBlockW;
   const uint32_t sper = a.gq2k ? 16u : 4u, dper = a.gq2k ? 4u : 2u;
   return 2u * (uint32_t)kGateTile * nbh * (64u + sper + dper);
 }
-__device__ __forceinline__ uint32_t sd_bytes(const PersistArgs& a) { return (uint32_t)kDownRows * a.Fs * 2; }
-__device__ __forceinline__ uint32_t dn_expert_bytes(const PersistArgs& a) {
+template <class A>
+__device__ __forceinline__ uint32_t sd_bytes(const A& a) { return (uint32_t)kDownRows * a.Fs * 2; }
+template <class A>
+__device__ __forceinline__ uint32_t dn_expert_bytes(const A& a) {
   return (uint32_t)kDownRows * (a.F / kBlockW) * kQ2KBytes;
 }
 
@@ -435,12 +443,12 @@ __device__ __forceinline__ uint32_t dn_expert_bytes(const PersistArgs& a) {
 // the down rows (copied during GU, used in D).  Otherwise the whole buffer
 // is reused phase by phase.
 // shared items: SMALL after the router rows; otherwise at 0 with room for one tile
-template <bool SMALL>
-__device__ __forceinline__ uint32_t shared_off(const PersistArgs& a) {
+template <bool SMALL, class A>
+__device__ __forceinline__ uint32_t shared_off(const A& a) {
   return SMALL ? al16(router_bytes(a)) : 0;
 }
-template <bool SMALL>
-__device__ __forceinline__ int shared_pf_count(const PersistArgs& a) {
+template <bool SMALL, class A>
+__device__ __forceinline__ int shared_pf_count(const A& a) {
   const uint32_t off = shared_off<SMALL>(a), end = SMALL ? a.pfa : a.pfb - gu_tile_bytes(a);
   const int fit = end > off ? (int)((end - off) / shared_item_bytes(a)) : 0;
   const int mine = my_count(a, n_shared_items(a));
@@ -448,14 +456,14 @@ __device__ __forceinline__ int shared_pf_count(const PersistArgs& a) {
 }
 
 // routed gate/up tiles: SMALL at 0; otherwise after the shared items
-template <bool SMALL>
-__device__ __forceinline__ int gu_items_base(const PersistArgs& a) { return SMALL ? 0 : n_shared_items(a); }
-template <bool SMALL>
-__device__ __forceinline__ uint32_t tile_off(const PersistArgs& a) {
+template <bool SMALL, class A>
+__device__ __forceinline__ int gu_items_base(const A& a) { return SMALL ? 0 : n_shared_items(a); }
+template <bool SMALL, class A>
+__device__ __forceinline__ uint32_t tile_off(const A& a) {
   return SMALL ? 0 : shared_off<SMALL>(a) + shared_pf_count<SMALL>(a) * shared_item_bytes(a);
 }
-template <bool SMALL>
-__device__ __forceinline__ int tile_pf_count(const PersistArgs& a, int na) {
+template <bool SMALL, class A>
+__device__ __forceinline__ int tile_pf_count(const A& a, int na) {
   const uint32_t off = tile_off<SMALL>(a), end = SMALL ? a.pfa : a.pfb;
   const int fit = end > off ? (int)((end - off) / gu_tile_bytes(a)) : 0;
   const int base = gu_items_base<SMALL>(a);
@@ -466,29 +474,31 @@ __device__ __forceinline__ int tile_pf_count(const PersistArgs& a, int na) {
 // down: [shared rows | a chunk of experts' rows] from down_base; the first
 // chunk of the first tile is copied ahead (SMALL: during GU, otherwise during
 // the barrier before D)
-template <bool SMALL>
-__device__ __forceinline__ uint32_t down_base(const PersistArgs& a) { return SMALL ? a.pfa : 0; }
-template <bool SMALL>
-__device__ __forceinline__ int down_chunk(const PersistArgs& a) {
+template <bool SMALL, class A>
+__device__ __forceinline__ uint32_t down_base(const A& a) { return SMALL ? a.pfa : 0; }
+template <bool SMALL, class A>
+__device__ __forceinline__ int down_chunk(const A& a) {
   const uint32_t fixed = down_base<SMALL>(a) + al16(sd_bytes(a));
   return a.pfb > fixed ? (int)((a.pfb - fixed) / dn_expert_bytes(a)) : 0;
 }
-template <bool SMALL>
-__device__ __forceinline__ int down_pf_count(const PersistArgs& a, int na) {
+template <bool SMALL, class A>
+__device__ __forceinline__ int down_pf_count(const A& a, int na) {
   if ((int)blockIdx.x * kDownRows >= a.H) return 0;
   const int fit = down_chunk<SMALL>(a);
   return na < fit ? na : fit;
 }
 
 // ------------------------------------------------------ copy issuers ---
-__device__ __forceinline__ void copy_router_rows(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int eg,
+template <class A>
+__device__ __forceinline__ void copy_router_rows(const A& a, const LayerPtrs& Lp, PersistLds& L, int eg,
                                                  int w, int nw) {
   const int e0 = eg * a.r_et;
   const int ne = a.E - e0 < a.r_et ? a.E - e0 : a.r_et;
   dma_to_lds<0>(Lp.router + (size_t)e0 * a.H, L.pfb, (uint32_t)ne * a.H * 4, w, nw);
 }
 
-__device__ __forceinline__ void copy_shared_item(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
+template <class A>
+__device__ __forceinline__ void copy_shared_item(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
                                                  int item, int w, int nw) {
   const uint32_t row = (uint32_t)a.H * 2;
   for (int r = 0; r < kSharedItemRows; ++r) {
@@ -503,7 +513,8 @@ __device__ __forceinline__ void copy_shared_item(const PersistArgs& a, const Lay
 struct TileLds {
   uint32_t qb, sb, db, s, d;
 };
-__device__ __forceinline__ TileLds tile_lds(const PersistArgs& a) {
+template <class A>
+__device__ __forceinline__ TileLds tile_lds(const A& a) {
   TileLds t;
   const uint32_t nbh = a.H / kBlockW;
   t.qb = (uint32_t)kGateTile * nbh * 64;
@@ -514,7 +525,8 @@ __device__ __forceinline__ TileLds tile_lds(const PersistArgs& a) {
   return t;
 }
 
-__device__ __forceinline__ void copy_tile(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int e,
+template <class A>
+__device__ __forceinline__ void copy_tile(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int e,
                                           int f0, int w, int nw) {
   const uint32_t nbh = a.H / kBlockW;
   const size_t nblk = (size_t)a.F * nbh;
@@ -531,7 +543,8 @@ __device__ __forceinline__ void copy_tile(const PersistArgs& a, const LayerPtrs&
 }
 
 // Routed down rows r0..r0+7 of expert e as [codes 8*nb*64 | scales 8*nb*16 | d,dmin 8*nb*4].
-__device__ __forceinline__ void copy_down_rows(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
+template <class A>
+__device__ __forceinline__ void copy_down_rows(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
                                                int e, int r0, int w, int nw) {
   const uint32_t nb = a.F / kBlockW;
   const MatPlanes pl = q2k_planes((size_t)a.H * nb);
@@ -542,14 +555,15 @@ __device__ __forceinline__ void copy_down_rows(const PersistArgs& a, const Layer
   dma_to_lds<0>(base + pl.d + b0 * 4, dst + kDownRows * nb * 80, kDownRows * nb * 4, w, nw);
 }
 
-__device__ __forceinline__ void copy_sd_rows(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int r0,
+template <class A>
+__device__ __forceinline__ void copy_sd_rows(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int r0,
                                              int w, int nw) {
   if (a.Fs) dma_to_lds<0>(Lp.sd + (size_t)r0 * a.Fs, dst, sd_bytes(a), w, nw);
 }
 
 // prefetches issued during barriers
-template <bool SMALL>
-__device__ __forceinline__ void pf_router_and_shared(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L,
+template <bool SMALL, class A>
+__device__ __forceinline__ void pf_router_and_shared(const A& a, const LayerPtrs& Lp, PersistLds& L,
                                                      int w, int nw) {
   if ((int)blockIdx.x < router_groups(a)) copy_router_rows(a, Lp, L, blockIdx.x, w, nw);
   if (SMALL) {
@@ -560,7 +574,8 @@ __device__ __forceinline__ void pf_router_and_shared(const PersistArgs& a, const
   }
 }
 
-__device__ __forceinline__ void pf_shared_items(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int w,
+template <class A>
+__device__ __forceinline__ void pf_shared_items(const A& a, const LayerPtrs& Lp, PersistLds& L, int w,
                                                 int nw) {
   const int n = shared_pf_count<false>(a);
   for (int j = 0; j < n; ++j)
@@ -568,8 +583,8 @@ __device__ __forceinline__ void pf_shared_items(const PersistArgs& a, const Laye
                      nw);
 }
 
-template <bool SMALL>
-__device__ __forceinline__ void pf_tiles(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
+template <bool SMALL, class A>
+__device__ __forceinline__ void pf_tiles(const A& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
   const int na = *L.nact, tiles = a.F / kGateTile, base = gu_items_base<SMALL>(a);
   const int n = tile_pf_count<SMALL>(a, na), j0 = my_count(a, base);
   for (int j = 0; j < n; ++j) {
@@ -579,8 +594,8 @@ __device__ __forceinline__ void pf_tiles(const PersistArgs& a, const LayerPtrs& 
   }
 }
 
-template <bool SMALL>
-__device__ __forceinline__ void pf_down(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
+template <bool SMALL, class A>
+__device__ __forceinline__ void pf_down(const A& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
   const int r0 = blockIdx.x * kDownRows;
   if (r0 >= a.H) return;
   QS_LDS uint8_t* base = L.pfb + down_base<SMALL>(a);
@@ -601,8 +616,8 @@ __device__ __forceinline__ double sumsq_part(float4 v, double s) {
 
 __device__ __forceinline__ double rms_inv_of(double q, int H) { return 1.0 / sqrt(q / (double)H + kRmsEps); }
 
-template <bool SMALL>
-__device__ __forceinline__ float4 x_f4(const PersistArgs& a, const PersistLds& L, const float* x, int t, int h) {
+template <bool SMALL, class A>
+__device__ __forceinline__ float4 x_f4(const A& a, const PersistLds& L, const float* x, int t, int h) {
   if (SMALL) return lds_f4(L.ax + t * a.H + h);
   return cldf4(x + (size_t)t * a.H + h);
 }
@@ -611,8 +626,8 @@ __device__ __forceinline__ float4 x_f4(const PersistArgs& a, const PersistLds& L
 // [w*H/8, (w+1)*H/8) with lane stride 4, fp64 FMAs in order, a butterfly,
 // then the waves in order -- the same order phase_router uses, so the scale
 // is the same for every batch size.
-template <bool SMALL>
-__device__ __forceinline__ void token_rinv(const PersistArgs& a, PersistLds& L, const float* x, int t0, int n) {
+template <bool SMALL, class A>
+__device__ __forceinline__ void token_rinv(const A& a, PersistLds& L, const float* x, int t0, int n) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
   const int hw = a.H / nw;
   for (int j = 0; j < n; ++j) {
@@ -635,8 +650,8 @@ __device__ __forceinline__ void token_rinv(const PersistArgs& a, PersistLds& L, 
 // group.  Otherwise-flow workgroups also sum x^2 of the tokens they route
 // (same order as token_rinv); the owner of expert group 0 publishes the
 // RMS scales.
-template <bool SMALL>
-__device__ __forceinline__ void phase_router(const PersistArgs& a, const LayerPtrs& Lp, const float* x,
+template <bool SMALL, class A>
+__device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, const float* x,
                                              PersistLds& L) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
   const int ET = a.r_et, TT = a.r_tt;
@@ -727,8 +742,8 @@ __device__ __forceinline__ void phase_router(const PersistArgs& a, const LayerPt
 // ------------------------------------------------- shared gate/up item ---
 // Rows [2*item, 2*item+2) from LDS ([row][gate, up][H] bf16), 4 waves per
 // row, each over a quarter of H; fp32 FMA.
-template <bool SMALL>
-__device__ __forceinline__ void shared_gu_item(const PersistArgs& a, lds_cptr wbase, const float* x, int item,
+template <bool SMALL, class A>
+__device__ __forceinline__ void shared_gu_item(const A& a, lds_cptr wbase, const float* x, int item,
                                                PersistLds& L) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
   const int rw = wave >> 2, qtr = wave & 3;
@@ -777,8 +792,8 @@ __device__ __forceinline__ void shared_gu_item(const PersistArgs& a, lds_cptr wb
   __syncthreads();
 }
 
-template <bool SMALL>
-__device__ __forceinline__ void shared_items(const PersistArgs& a, const LayerPtrs& Lp, const float* x,
+template <bool SMALL, class A>
+__device__ __forceinline__ void shared_items(const A& a, const LayerPtrs& Lp, const float* x,
                                              PersistLds& L) {
   const int npf = shared_pf_count<SMALL>(a);
   const uint32_t off = shared_off<SMALL>(a), item_b = shared_item_bytes(a);
@@ -798,8 +813,8 @@ __device__ __forceinline__ void shared_items(const PersistArgs& a, const LayerPt
 // softmax over the k picks.  SMALL: logits from LDS, results into LDS (every
 // workgroup); otherwise logits and results in global scratch (one wave per
 // token).  Workgroup 0 / the token's wave also writes ids_out / w_out.
-template <bool SMALL>
-__device__ __forceinline__ void topk_wave(const PersistArgs& a, int t, int layer_i, PersistLds& L, bool write_out) {
+template <bool SMALL, class A>
+__device__ __forceinline__ void topk_wave(const A& a, int t, int layer_i, PersistLds& L, bool write_out) {
   const int lane = qs_tid() & 63;
   const int E = a.E, k = a.k;
   double v[16];
@@ -871,7 +886,8 @@ __device__ __forceinline__ float f32_unord(int o) {
   return __int_as_float(o >= 0 ? o : (int)(0x80000000u - (uint32_t)o));
 }
 
-__device__ __forceinline__ void topk_small(const PersistArgs& a, int layer_i, PersistLds& L) {
+template <class A>
+__device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& L) {
   const int tid = qs_tid(), nt = kPersistThreads, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k, T = a.T, S = kf_stride(E), NG = S / 8, G4 = (NG + 3) & ~3;
   QS_LDS float* gm = L.kf + T * S;                 // [T][G4] group maxima, -inf padded
@@ -971,7 +987,8 @@ __device__ __forceinline__ void topk_small(const PersistArgs& a, int layer_i, Pe
 // each to the lane of its rank, mark the first pair of each expert (a scan
 // of the marks numbers the active experts), and place each position in its
 // token's ascending list with one ballot per token.
-__device__ __forceinline__ void group_small(const PersistArgs& a, PersistLds& L) {
+template <class A>
+__device__ __forceinline__ void group_small(const A& a, PersistLds& L) {
   const int lane = qs_tid() & 63, k = a.k, P = a.T * k;
   if ((qs_tid() >> 6) == 0) {
     const bool live = lane < P;
@@ -1028,8 +1045,8 @@ __device__ __forceinline__ uint32_t q2k_order(uint32_t v) {
 
 // x block b (256 elements) of token t -> limbs, one wave.  SMALL: from and
 // into LDS; otherwise global scratch.
-template <bool SMALL>
-__device__ __forceinline__ void quant_x_wave(const PersistArgs& a, const float* x, int t, int b, PersistLds& L) {
+template <bool SMALL, class A>
+__device__ __forceinline__ void quant_x_wave(const A& a, const float* x, int t, int b, PersistLds& L) {
   const int lane = qs_tid() & 63;
   const float4 v = x_f4<SMALL>(a, L, x, t, b * kBlockW + 4 * lane);
   const float r = SMALL ? (float)L.rinv[t] : (float)cldd(&a.rinv[t]);
@@ -1069,8 +1086,8 @@ __device__ __forceinline__ void quant_x_wave(const PersistArgs& a, const float* 
 
 // ------------------------------------------------------ grouping (LDS) ---
 // Stable bucket sort of (token, slot) pairs by expert.
-template <bool SMALL>
-__device__ __forceinline__ void build_groups(const PersistArgs& a, PersistLds& L) {
+template <bool SMALL, class A>
+__device__ __forceinline__ void build_groups(const A& a, PersistLds& L) {
   const int tid = qs_tid(), nt = kPersistThreads, E = a.E, k = a.k, T = a.T, P = T * k;
   const int wave = tid >> 6, lane = tid & 63;
   for (int i = tid; i < E; i += nt) L.cnt[i] = 0;
@@ -1150,8 +1167,8 @@ __device__ __forceinline__ void build_groups(const PersistArgs& a, PersistLds& L
 }
 
 // ----------------------------------------------------------- phase GU ---
-template <bool SMALL>
-__device__ __forceinline__ void x_chunk(const PersistArgs& a, const PersistLds& L, int t, int ch,
+template <bool SMALL, class A>
+__device__ __forceinline__ void x_chunk(const A& a, const PersistLds& L, int t, int ch,
                                         uint32_t (&xh)[16], uint32_t (&xl)[16], float (&xs)[4],
                                         int (&xa)[4]) {
   const size_t xo = (size_t)t * (a.H / 4) + ch * 16;
@@ -1188,8 +1205,8 @@ __device__ __forceinline__ void x_chunk(const PersistArgs& a, const PersistLds& 
 // Routed gate/up tile from LDS: rows [f0, f0+16) of expert e for every
 // token of its bucket; each 64-weight chunk is decoded once and applied to
 // the tokens one at a time.  SwiGLU outputs are quantised per 16 rows.
-template <int FMT, bool SMALL>
-__device__ __forceinline__ void routed_gu_tile(const PersistArgs& a, lds_cptr tile, int u, int f0, PersistLds& L) {
+template <int FMT, bool SMALL, class A>
+__device__ __forceinline__ void routed_gu_tile(const A& a, lds_cptr tile, int u, int f0, PersistLds& L) {
   const int p0 = L.aoff[u], n = L.aoff[u + 1] - p0;
   const int nbh = a.H / kBlockW;
   const int nch = a.H / kChunkW;
@@ -1304,8 +1321,8 @@ __device__ __forceinline__ void routed_gu_tile(const PersistArgs& a, lds_cptr ti
 
 // Routed tiles of this workgroup: the first ones were copied ahead, the rest
 // are copied into the first slot on demand.
-template <int FMT, bool SMALL>
-__device__ __forceinline__ void routed_tiles(const PersistArgs& a, const LayerPtrs& Lp, PersistLds& L) {
+template <int FMT, bool SMALL, class A>
+__device__ __forceinline__ void routed_tiles(const A& a, const LayerPtrs& Lp, PersistLds& L) {
   const int tiles = a.F / kGateTile;
   const int na = *L.nact;
   const int base = gu_items_base<SMALL>(a);
@@ -1327,8 +1344,8 @@ __device__ __forceinline__ void routed_tiles(const PersistArgs& a, const LayerPt
 
 // ------------------------------------------------------------ phase D ---
 // One wave: rows r0..r0+7 of active expert u (in LDS) against every pair of its bucket.
-template <bool SMALL>
-__device__ __forceinline__ void down_expert(const PersistArgs& a, lds_cptr w, int u, PersistLds& L) {
+template <bool SMALL, class A>
+__device__ __forceinline__ void down_expert(const A& a, lds_cptr w, int u, PersistLds& L) {
   const int lane = qs_tid() & 63;
   const int nb = a.F / kBlockW;
   const int nch = a.F / kChunkW;
@@ -1397,8 +1414,8 @@ __device__ __forceinline__ void down_expert(const PersistArgs& a, lds_cptr w, in
 }
 
 // Shared expert down row (in LDS), one wave, lanes over Fs, all tokens.
-template <bool SMALL>
-__device__ __forceinline__ void shared_down_row(const PersistArgs& a, lds_cptr srow, PersistLds& L) {
+template <bool SMALL, class A>
+__device__ __forceinline__ void shared_down_row(const A& a, lds_cptr srow, PersistLds& L) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
 #pragma unroll 1
   for (int t = 0; t < a.T; ++t) {
@@ -1435,8 +1452,8 @@ __device__ __forceinline__ void shared_down_row(const PersistArgs& a, lds_cptr s
 
 // `after_wait(w, nw)` runs once, right after the first wait for this
 // phase's inputs (copies issued there overlap the down GEMVs).
-template <bool SMALL, class AW>
-__device__ __forceinline__ void phase_down(const PersistArgs& a, const LayerPtrs& Lp, const float* x, float* y,
+template <bool SMALL, class AW, class A>
+__device__ __forceinline__ void phase_down(const A& a, const LayerPtrs& Lp, const float* x, float* y,
                                            PersistLds& L, AW&& after_wait) {
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
   const int na = *L.nact;
@@ -1501,8 +1518,10 @@ __device__ __forceinline__ void phase_down(const PersistArgs& a, const LayerPtrs
 
 // ------------------------------------------------------------- kernel ---
 // The small-batch kernel (T <= kSmallT); qs_big.h holds the batched one.
-template <int FMT>
-__global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a) {
+// Every step takes its arguments as `const A&`: PersistArgs, or FixedArgs,
+// whose compile-time shape constants shadow the runtime fields.
+template <int FMT, class A>
+__device__ __forceinline__ void persist_small_body(const A& a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   PersistLds L = carve_lds<true>(lds_raw, a, FMT == 2);
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
@@ -1545,6 +1564,26 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a
     if (more) pf_router_and_shared<true>(a, Ln, L, wave, nw);
     if (more && !grid_barrier(a, ++epoch, [](int, int) {})) return;
   }
+}
+
+// Any shape: the layer shapes come from the arguments.
+template <int FMT>
+__global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a) {
+  persist_small_body<FMT>(a);
+}
+
+// One layer shape fixed at compile time.  The launch passes the same values
+// in the runtime fields (the host checks); the static members shadow them,
+// so every loop bound, offset and division by a shape folds to a constant.
+template <int FMT, int H_, int E_, int K_, int F_, int FS_, int T_, int G_>
+struct FixedArgs : PersistArgs {
+  static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, T = T_, G = G_;
+  static constexpr int gq2k = FMT == 1, r_et = 1, r_tt = T_;
+};
+
+template <int FMT, int H, int E, int K, int F, int FS, int T, int G>
+__global__ void __launch_bounds__(kPersistThreads) k_persist_small_fixed(PersistArgs a) {
+  persist_small_body<FMT>(static_cast<const FixedArgs<FMT, H, E, K, F, FS, T, G>&>(a));
 }
 
 }  // namespace qs
