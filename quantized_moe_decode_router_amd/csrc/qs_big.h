@@ -99,7 +99,8 @@ struct BigL {
   QS_LDS int* bat;       // [kBatchMax][4] staged batch: expert, first row, weight and activation offsets
 };
 
-__device__ __forceinline__ BigL carve_big(uint8_t* raw, const PersistArgs& a, bool cb2) {
+template <class A>
+__device__ __forceinline__ BigL carve_big(uint8_t* raw, const A& a, bool cb2) {
   const BigLayout l = big_layout(a.E, a.T, a.T * a.k, cb2, a.pfb);
   QS_LDS uint8_t* b = (QS_LDS uint8_t*)raw;
   BigL L;
@@ -198,7 +199,8 @@ __host__ __device__ inline BigPlan big_plan(int H, int F, int Fs, bool q2k, uint
   return p;
 }
 
-__device__ __forceinline__ BigPlan big_plan_of(const PersistArgs& a) {
+template <class A>
+__device__ __forceinline__ BigPlan big_plan_of(const A& a) {
   return big_plan(a.H, a.F, a.Fs, a.gq2k != 0, a.pfb, (int)router_bytes(a));
 }
 
@@ -207,27 +209,32 @@ __device__ __forceinline__ BigPlan big_plan_of(const PersistArgs& a) {
 // staging round trip (~1.5 us) is kStageCost.  Only the ratios matter.
 constexpr int kStageCost = 240;
 
-__device__ __forceinline__ int gu_gemv_cost(const PersistArgs& a, int n) {
+template <class A>
+__device__ __forceinline__ int gu_gemv_cost(const A& a, int n) {
   const int w = (int)(big_tile_b(a.H, a.gq2k != 0) >> 8);
   return kStageCost + w + (3 * w * n) / 5;
 }
-__device__ __forceinline__ int gu_mfma_cost(const PersistArgs& a, int n) {
+template <class A>
+__device__ __forceinline__ int gu_mfma_cost(const A& a, int n) {
   const int w = (int)(big_tile_b(a.H, a.gq2k != 0) >> 8) * (kMfmaRows / kGateTile);
   const int ng = (n + kMfmaTok - 1) / kMfmaTok;
   return w + ng * (kStageCost + 16 * (a.H / kBlockW));
 }
-__device__ __forceinline__ int dn_gemv_cost(const PersistArgs& a, int n) {
+template <class A>
+__device__ __forceinline__ int dn_gemv_cost(const A& a, int n) {
   const int w = (int)(big_dnw_b(a.F) >> 8);
   return kStageCost + w + (w * n) / 8;
 }
-__device__ __forceinline__ int dn_mfma_cost(const PersistArgs& a, int n) {
+template <class A>
+__device__ __forceinline__ int dn_mfma_cost(const A& a, int n) {
   const int w = (int)(big_dnw_b(a.F) >> 8) * (kMfmaRows / kDnRows);
   const int ng = (n + kMfmaTok - 1) / kMfmaTok;
   return w + ng * (kStageCost + 16 * (a.F / kBlockW));
 }
 
 // Items of active expert u in one phase: count m and unit cost c.
-__device__ __forceinline__ void gu_items_of(const PersistArgs& a, const PersistLds& L, int u, int& m, int& c) {
+template <class A>
+__device__ __forceinline__ void gu_items_of(const A& a, const PersistLds& L, int u, int& m, int& c) {
   const int n = L.aoff[u + 1] - L.aoff[u];
   if (n >= a.mfma_min) {
     m = a.F / kMfmaRows;
@@ -237,7 +244,8 @@ __device__ __forceinline__ void gu_items_of(const PersistArgs& a, const PersistL
     c = gu_gemv_cost(a, n);
   }
 }
-__device__ __forceinline__ void dn_items_of(const PersistArgs& a, const PersistLds& L, int u, int& m, int& c) {
+template <class A>
+__device__ __forceinline__ void dn_items_of(const A& a, const PersistLds& L, int u, int& m, int& c) {
   const int n = L.aoff[u + 1] - L.aoff[u];
   if (n >= a.mfma_min) {
     m = a.H / kMfmaRows;
@@ -253,8 +261,8 @@ __device__ __forceinline__ void dn_items_of(const PersistArgs& a, const PersistL
 // computes, for every active expert, the range [jlo, jhi) of its items this
 // workgroup owns (an empty range for most).  Every workgroup evaluates the
 // same integers, so the items are split exactly once.
-template <class MC>
-__device__ __forceinline__ void assign_items(const PersistArgs& a, const PersistLds& L, QS_LDS int* jlo,
+template <class MC, class A>
+__device__ __forceinline__ void assign_items(const A& a, const PersistLds& L, QS_LDS int* jlo,
                                              QS_LDS int* jhi, MC&& items_of) {
   const int lane = qs_tid() & 63, na = *L.nact;
   if ((qs_tid() >> 6) != 0) return;
@@ -288,7 +296,8 @@ __device__ __forceinline__ void assign_items(const PersistArgs& a, const Persist
 
 // ------------------------------------------------------ copy issuers ---
 // Rows [r0, r0+n) of one Q2_K down matrix as [codes | scales | d,dmin].
-__device__ __forceinline__ void copy_dn_rows(const PersistArgs& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int e,
+template <class A>
+__device__ __forceinline__ void copy_dn_rows(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int e,
                                              int r0, int n, int w, int nw) {
   const uint32_t nb = a.F / kBlockW;
   const MatPlanes pl = q2k_planes((size_t)a.H * nb);
@@ -324,7 +333,8 @@ __device__ __forceinline__ void dma_rows(SRC&& src, QS_LDS uint8_t* dst, uint32_
 // logits equal the small-batch kernel's bit for bit.
 constexpr int kRtTok = 8;
 
-__device__ __forceinline__ void big_router(const PersistArgs& a, const LayerPtrs& Lp, const float* x, PersistLds& L) {
+template <class A>
+__device__ __forceinline__ void big_router(const A& a, const LayerPtrs& Lp, const float* x, PersistLds& L) {
   if (a.r_et != 1) {
     phase_router<false>(a, Lp, x, L);
     return;
@@ -391,7 +401,8 @@ __device__ __forceinline__ void big_router(const PersistArgs& a, const LayerPtrs
 // shared_gu_item's (bitwise equal results).
 constexpr int kShTok = 8;
 
-__device__ __forceinline__ void shared_gu_item_big(const PersistArgs& a, lds_cptr wbase, const float* x, int item,
+template <class A>
+__device__ __forceinline__ void shared_gu_item_big(const A& a, lds_cptr wbase, const float* x, int item,
                                                    PersistLds& L) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
   const int rw = wave >> 2, qtr = wave & 3;
@@ -454,8 +465,8 @@ __device__ __forceinline__ void shared_gu_item_big(const PersistArgs& a, lds_cpt
 }
 
 // ------------------------------------------------ shared gate/up (GU) ---
-template <bool PRE>
-__device__ __forceinline__ void big_shared_gu(const PersistArgs& a, const LayerPtrs& Lp, const float* x, BigL& L) {
+template <bool PRE, class A>
+__device__ __forceinline__ void big_shared_gu(const A& a, const LayerPtrs& Lp, const float* x, BigL& L) {
   int j = 0;
   for (int it = blockIdx.x; it < n_shared_items(a); it += a.G, ++j) {
     if (j > 0 || !PRE) stage_now([&](int w, int n) { copy_shared_item(a, Lp, L.P.pfb, it, w, n); });
@@ -473,7 +484,8 @@ struct XStage {
   QS_LDS float* xs;
   QS_LDS int* xa;
 };
-__device__ __forceinline__ XStage x_stage(const PersistArgs& a, QS_LDS uint8_t* base, int xg) {
+template <class A>
+__device__ __forceinline__ XStage x_stage(const A& a, QS_LDS uint8_t* base, int xg) {
   XStage s;
   s.xh = (QS_LDS uint32_t*)base;
   s.xl = s.xh + (size_t)xg * (a.H / 4);
@@ -483,7 +495,8 @@ __device__ __forceinline__ XStage x_stage(const PersistArgs& a, QS_LDS uint8_t* 
 }
 
 // Tokens of bucket positions [q0, q0+n) -> staged slots 0..n-1.
-__device__ __forceinline__ void copy_x_tokens(const PersistArgs& a, const PersistLds& L, const XStage& s, int q0,
+template <class A>
+__device__ __forceinline__ void copy_x_tokens(const A& a, const PersistLds& L, const XStage& s, int q0,
                                               int n, int w, int nw) {
   const int H = a.H, k = a.k;
   auto tok = [&](int i) { return L.pairs[q0 + i] / k; };
@@ -498,7 +511,8 @@ __device__ __forceinline__ void copy_x_tokens(const PersistArgs& a, const Persis
                         (QS_LDS uint8_t*)s.xa, (uint32_t)H / 4, (uint32_t)H / 4, n, w, nw);
 }
 
-__device__ __forceinline__ void x_chunk_st(const PersistArgs& a, const XStage& s, int slot, int ch,
+template <class A>
+__device__ __forceinline__ void x_chunk_st(const A& a, const XStage& s, int slot, int ch,
                                            uint32_t (&xh)[16], uint32_t (&xl)[16], float (&xs)[4], int (&xa)[4]) {
   const size_t xo = (size_t)slot * (a.H / 4) + ch * 16;
   const size_t si = (size_t)slot * (a.H / kSubW) + ch * 4;
@@ -518,8 +532,8 @@ __device__ __forceinline__ void x_chunk_st(const PersistArgs& a, const XStage& s
 // Rows [f0, f0+16) of the tile in LDS for the ng staged tokens whose bucket
 // positions start at q0.  The per-(row, token) arithmetic -- lanes per row,
 // chunk order, butterfly, SwiGLU, per-16 quantisation -- is routed_gu_tile's.
-template <int FMT>
-__device__ __forceinline__ void gu_gemv_compute(const PersistArgs& a, lds_cptr tile, const XStage& xst, int q0,
+template <int FMT, class A>
+__device__ __forceinline__ void gu_gemv_compute(const A& a, lds_cptr tile, const XStage& xst, int q0,
                                                 int ng, int f0, PersistLds& L) {
   const int nbh = a.H / kBlockW;
   const int nch = a.H / kChunkW;
@@ -632,8 +646,8 @@ __device__ __forceinline__ void gu_gemv_compute(const PersistArgs& a, lds_cptr t
 // One GEMV gate/up item.  `pre`: its first staging (weights and the first
 // token group) was issued earlier.  `xkeep`: the staged tokens of the
 // previous item are this bucket's (same expert, whole bucket staged).
-template <int FMT>
-__device__ __forceinline__ void gu_gemv_item(const PersistArgs& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
+template <int FMT, class A>
+__device__ __forceinline__ void gu_gemv_item(const A& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
                                              int u, int f0, bool pre, bool xkeep) {
   PersistLds& P = L.P;
   const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0, e = P.act[u];
@@ -752,8 +766,8 @@ __device__ __forceinline__ MguStage mgu_stage(QS_LDS uint8_t* base, int kb) {
   return s;
 }
 
-template <int FMT>
-__device__ __forceinline__ void gu_mfma_item(const PersistArgs& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
+template <int FMT, class A>
+__device__ __forceinline__ void gu_mfma_item(const A& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
                                              int u, int f0) {
   constexpr bool q2k = FMT == 1;
   PersistLds& P = L.P;
@@ -861,8 +875,8 @@ struct Batcher {
   uint32_t last_x;
 };
 
-template <int FMT>
-__device__ __forceinline__ void big_gu_phase(const PersistArgs& a, const LayerPtrs& Lp, const float* x, BigL& L,
+template <int FMT, class A>
+__device__ __forceinline__ void big_gu_phase(const A& a, const LayerPtrs& Lp, const float* x, BigL& L,
                                              const BigPlan& pp) {
   PersistLds& P = L.P;
   build_groups<false>(a, P);
@@ -955,7 +969,8 @@ struct AStage {
   QS_LDS int* aa;
   QS_LDS float* o;     // [xp][kDnRows] outputs (accumulated over chunks)
 };
-__device__ __forceinline__ AStage a_stage(const PersistArgs& a, QS_LDS uint8_t* base, int xp) {
+template <class A>
+__device__ __forceinline__ AStage a_stage(const A& a, QS_LDS uint8_t* base, int xp) {
   AStage s;
   s.ah = (QS_LDS uint32_t*)base;
   s.al = s.ah + (size_t)xp * (a.F / 4);
@@ -965,7 +980,8 @@ __device__ __forceinline__ AStage a_stage(const PersistArgs& a, QS_LDS uint8_t* 
   return s;
 }
 
-__device__ __forceinline__ void copy_a_pairs(const PersistArgs& a, const PersistLds& L, const AStage& s, int q0, int n,
+template <class A>
+__device__ __forceinline__ void copy_a_pairs(const A& a, const PersistLds& L, const AStage& s, int q0, int n,
                                              int w, int nw) {
   const int F = a.F;
   auto pr = [&](int i) { return L.pairs[q0 + i]; };
@@ -981,7 +997,8 @@ __device__ __forceinline__ void copy_a_pairs(const PersistArgs& a, const Persist
 
 // One wave: its 8 rows (of the item's 64, in LDS) against the ng staged
 // pairs; the per-(row, pair) arithmetic is down_expert's.
-__device__ __forceinline__ void dn_gemv_rows(const PersistArgs& a, lds_cptr w, int wrow0, const AStage& st, int ng) {
+template <class A>
+__device__ __forceinline__ void dn_gemv_rows(const A& a, lds_cptr w, int wrow0, const AStage& st, int ng) {
   const int lane = qs_tid() & 63;
   const int nb = a.F / kBlockW;
   const int nch = a.F / kChunkW;
@@ -1030,7 +1047,8 @@ __device__ __forceinline__ void dn_gemv_rows(const PersistArgs& a, lds_cptr w, i
   }
 }
 
-__device__ __forceinline__ void dn_gemv_item(const PersistArgs& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
+template <class A>
+__device__ __forceinline__ void dn_gemv_item(const A& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
                                              int u, int h0, bool pre) {
   PersistLds& P = L.P;
   const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0, e = P.act[u];
@@ -1093,7 +1111,8 @@ __device__ __forceinline__ DnFrag load_dn_frag(const uint8_t* mat, const MatPlan
   return f;
 }
 
-__device__ __forceinline__ void dn_mfma_item(const PersistArgs& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
+template <class A>
+__device__ __forceinline__ void dn_mfma_item(const A& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
                                              int u, int h0) {
   PersistLds& P = L.P;
   const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0, e = P.act[u];
@@ -1143,11 +1162,11 @@ __device__ __forceinline__ void dn_mfma_item(const PersistArgs& a, const LayerPt
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const uint32_t scm = (f.scm >> (8 * s)) & 0xFFu;
-          const v4i A = q2k_afrag(qd[s], scm & 15u), M = splat4(scm >> 4);
+          const v4i Wm = q2k_afrag(qd[s], scm & 15u), M = splat4(scm >> 4);
           const QS_LDS uint8_t* bp = st.lh + r * st.stride + b * kBlockW + 64 * g + 16 * s;
           const v4i bh = lds_v4i(bp), bl = lds_v4i(bp + (st.ll - st.lh));
-          mh = mfma_i8(A, bh, mh);
-          ml = mfma_i8(A, bl, ml);
+          mh = mfma_i8(Wm, bh, mh);
+          ml = mfma_i8(Wm, bl, ml);
           nh = mfma_i8(M, bh, nh);
           nl = mfma_i8(M, bl, nl);
         }
@@ -1172,7 +1191,8 @@ __device__ __forceinline__ void dn_mfma_item(const PersistArgs& a, const LayerPt
 // Shared down rows [r0, r0+8) (in LDS at `srows`, one row per wave) for
 // tokens [t0, t0+nt) whose SwiGLU vectors are staged at `as_` ([nt][Fs]);
 // the per-token arithmetic is shared_down_row's.
-__device__ __forceinline__ void big_shared_dn_tile(const PersistArgs& a, lds_cptr srows, const QS_LDS float* as_,
+template <class A>
+__device__ __forceinline__ void big_shared_dn_tile(const A& a, lds_cptr srows, const QS_LDS float* as_,
                                                    int t0, int nt, int r0, BigL& L) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
   lds_cptr srow = srows + (uint32_t)wave * a.Fs * 2;
@@ -1202,7 +1222,8 @@ __device__ __forceinline__ void big_shared_dn_tile(const PersistArgs& a, lds_cpt
   __syncthreads();
 }
 
-__device__ __forceinline__ void big_dn_phase(const PersistArgs& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp) {
+template <class A>
+__device__ __forceinline__ void big_dn_phase(const A& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp) {
   PersistLds& P = L.P;
   const int na = *P.nact;
   if (a.Fs && (int)blockIdx.x < a.H / kDownRows) {
@@ -1299,7 +1320,8 @@ __device__ __forceinline__ void big_dn_phase(const PersistArgs& a, const LayerPt
 }
 
 // -------------------------------------------------- C phase (combine) ---
-__device__ __forceinline__ void big_combine(const PersistArgs& a, const PersistLds& L, const float* x, float* y) {
+template <class A>
+__device__ __forceinline__ void big_combine(const A& a, const PersistLds& L, const float* x, float* y) {
   const int N = a.T * a.H;
   for (int i = (int)blockIdx.x * kPersistThreads + qs_tid(); i < N; i += a.G * kPersistThreads) {
     const int t = i / a.H, h = i % a.H;
@@ -1316,8 +1338,8 @@ __device__ __forceinline__ void big_combine(const PersistArgs& a, const PersistL
 }
 
 // ------------------------------------------------------------- kernel ---
-template <int FMT>
-__global__ void __launch_bounds__(kPersistThreads) k_persist_big(PersistArgs a) {
+template <int FMT, class A>
+__device__ __forceinline__ void persist_big_body(const A& a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   BigL L = carve_big(lds_raw, a, FMT == 2);
   const BigPlan pp = big_plan_of(a);
@@ -1362,6 +1384,24 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist_big(PersistArgs a) 
         }))
       return;
   }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(kPersistThreads) k_persist_big(PersistArgs a) {
+  persist_big_body<FMT>(a);
+}
+
+// The layer shape fixed at compile time, the batch size at run time (as
+// FixedArgs for the small-batch kernel).
+template <int FMT, int H_, int E_, int K_, int F_, int FS_, int G_>
+struct FixedBigArgs : PersistArgs {
+  static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, G = G_;
+  static constexpr int gq2k = FMT == 1, r_et = 1;
+};
+
+template <int FMT, int H, int E, int K, int F, int FS, int G>
+__global__ void __launch_bounds__(kPersistThreads) k_persist_big_fixed(PersistArgs a) {
+  persist_big_body<FMT>(static_cast<const FixedBigArgs<FMT, H, E, K, F, FS, G>&>(a));
 }
 
 }  // namespace qs

@@ -90,6 +90,7 @@ struct qs_moe {
   bool persist_big_ok = false;   // batched instantiation usable
   int mfma_min = 16;              // bucket size from which the MFMA path runs
   bool fixed_ok = false;          // the fixed-shape small-batch kernels are usable
+  bool big_fixed_ok = false;      // the fixed-shape batched kernel is usable
 };
 
 namespace {
@@ -314,6 +315,21 @@ const void* fixed_a3b(int T) {
   }
 }
 
+// Batched instantiations with the layer shape fixed (the batch size stays a
+// run-time value): the shapes above, and hidden 4096, 256 experts, top-6,
+// expert and shared width 2048.
+const void* persist_big_fixed_fn(const qs_moe* h) {
+  const qs_moe_config& c = h->cfg;
+  if (h->grid != 256 || c.gate_up_format != QS_FMT_CB2 || c.n_experts != 256) return nullptr;
+  if (c.hidden == 2048 && c.top_k == 8 && c.expert_ffn == 512) {
+    if (c.shared_ffn == 512) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 256>;
+    if (c.shared_ffn == 0) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 0, 256>;
+  }
+  if (c.hidden == 4096 && c.top_k == 6 && c.expert_ffn == 2048 && c.shared_ffn == 2048)
+    return (const void*)k_persist_big_fixed<2, 4096, 256, 6, 2048, 2048, 256>;
+  return nullptr;
+}
+
 // The fixed-shape kernel for a T-token call of this handle, or nullptr.
 const void* persist_fixed_fn(const qs_moe* h, int T) {
   const qs_moe_config& c = h->cfg;
@@ -396,6 +412,15 @@ int setup_persistent(qs_moe* h) {
   }
   h->persist_small_ok = lds_small && persist_resident(h, true, lds_small);
   h->persist_big_ok = lds_big && persist_resident(h, false, lds_big);
+  if (h->persist_big_ok) {
+    const void* fn = persist_big_fixed_fn(h);
+    int occ = 0;
+    h->big_fixed_ok = fn && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_big) ==
+                                hipSuccess &&
+                      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds_big) == hipSuccess &&
+                      occ >= 1;
+    (void)hipGetLastError();
+  }
   // fixed-shape instantiations: the same LDS limit, checked one by one
   h->fixed_ok = h->persist_small_ok;
   for (int T = 1; T <= kSmallT && h->fixed_ok; ++T) {
@@ -464,7 +489,9 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   void* args[] = {&a};
   // the fixed-shape kernel needs the router unit it assumes (one expert per
   // workgroup, all tokens at once)
-  const void* fn = small && h->fixed_ok && p.r_et == 1 && p.r_tt == T ? persist_fixed_fn(h, T) : nullptr;
+  const void* fn = nullptr;
+  if (small && h->fixed_ok && p.r_et == 1 && p.r_tt == T) fn = persist_fixed_fn(h, T);
+  if (!small && h->big_fixed_ok && p.r_et == 1) fn = persist_big_fixed_fn(h);
   if (!fn) fn = persist_fn(cb2, small);
   hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(kPersistThreads), args,
                                             (unsigned)p.lds, st);
