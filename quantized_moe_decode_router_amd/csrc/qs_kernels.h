@@ -490,7 +490,8 @@ struct GateUpArgs {
   int n_shared_items;
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u with the hardware reciprocal (about 1 ulp), not an IEEE divide
+__device__ __forceinline__ float silu_mul(float g, float u) { return __fdividef(g, 1.0f + __expf(-g)) * u; }
 
 // Shared-expert gate/up rows: one wave per row, fp32 FMA over bf16 weights.
 __device__ void shared_gateup_item(const GateUpArgs& a, int item) {

@@ -61,6 +61,10 @@ struct Scratch {
   float* ash;
   float* xbuf[2];
   double* rinv;
+  uint64_t* ll_lg;   // small-batch persistent flow: flagged logits, SwiGLU outputs, residual stream
+  uint64_t* ll_a;
+  uint64_t* llx[2];
+  size_t ll_bytes;   // bytes of the flagged buffers (contiguous, zeroed at create)
   float* af;     // batched persistent flow: SwiGLU outputs of MFMA buckets [P][F]
   float* ob;     // routed down outputs by bucket position [P][H]
   float* sb;     // shared-expert down outputs [T][H]
@@ -91,6 +95,7 @@ struct qs_moe {
   int mfma_min = 16;              // bucket size from which the MFMA path runs
   bool fixed_ok = false;          // the fixed-shape small-batch kernels are usable
   bool big_fixed_ok = false;      // the fixed-shape batched kernel is usable
+  uint32_t ll_epoch = 0;          // flags used by the small-batch kernel so far
 };
 
 namespace {
@@ -169,11 +174,23 @@ T* carve(uint8_t*& p, size_t count) {
   return r;
 }
 
+// Words of the small-batch kernel's flagged buffers (batches of up to kSmallT).
+struct LLWords {
+  size_t lg, a, x;
+};
+LLWords ll_words(const qs_moe_config& c) {
+  const size_t T = std::min(c.max_tokens, kSmallT), P = T * c.top_k, F = c.expert_ffn;
+  return LLWords{T * c.n_experts * 2, 2 * P * (F / 4) + 2 * P * (F / 16) + T * (size_t)c.shared_ffn,
+                 T * (size_t)c.hidden};
+}
+
 size_t scratch_bytes(const qs_moe_config& c) {
   const size_t T = c.max_tokens, E = c.n_experts, k = c.top_k, H = c.hidden, F = c.expert_ffn;
   const size_t P = T * k;
   size_t b = 0;
   auto add = [&](size_t n) { b += align_up(n, 256); };
+  const LLWords lw = ll_words(c);
+  add(lw.lg * 8); add(lw.a * 8); add(lw.x * 8); add(lw.x * 8);
   add(T * E * 8);                 // logits
   add(P * 4); add(P * 4);         // ids, wts
   add(E * 4); add((E + 1) * 4);   // cnt, off
@@ -195,6 +212,12 @@ void carve_scratch(const qs_moe_config& c, Scratch& s) {
   const size_t T = c.max_tokens, E = c.n_experts, k = c.top_k, H = c.hidden, F = c.expert_ffn;
   const size_t P = T * k;
   uint8_t* p = s.base;
+  const LLWords lw = ll_words(c);
+  s.ll_lg = carve<uint64_t>(p, lw.lg);
+  s.ll_a = carve<uint64_t>(p, lw.a);
+  s.llx[0] = carve<uint64_t>(p, lw.x);
+  s.llx[1] = carve<uint64_t>(p, lw.x);
+  s.ll_bytes = (size_t)(p - s.base);
   s.logits = carve<double>(p, T * E);
   s.ids = carve<int32_t>(p, P);
   s.wts = carve<float>(p, P);
@@ -287,6 +310,11 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
     if (A + a16(sd) + 8 * pe > p.pfb) A = a16(std::max(r_sh, tile));
     p.pfa = (uint32_t)A;
     fits = A + b_min <= p.pfb;
+    // each flagged read is at most 32 words per thread
+    const uint64_t P = (uint64_t)T * c.top_k;
+    const uint64_t wa = 2 * P * (F / 4) + 2 * P * (F / 16) + (uint64_t)T * Fs;
+    fits = fits && wa <= 32u * kPersistThreads && (uint64_t)T * H <= 32u * kPersistThreads &&
+           2ull * T * c.n_experts <= 32u * kPersistThreads;
   } else {
     fits = rb <= p.pfb && tile <= p.pfb && a16(sd) + pe <= p.pfb;
     // at least one shared item ahead of the routed tiles' slot
@@ -456,7 +484,12 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
     p = persist_shape(h, T, false);
     if (!p.ok) return 1;
   }
-  const uint32_t barriers = (small ? 3u : 5u) * nL - 1u;
+  const uint32_t barriers = small ? 0u : 5u * nL - 1u;
+  if (small && h->ll_epoch > 0xF0000000u - 3u * (uint32_t)nL) {
+    // flags are about to wrap: clear the flagged buffers and start again
+    if (hipMemsetAsync(h->s.base, 0, h->s.ll_bytes, st) != hipSuccess) return QS_E_HIP;
+    h->ll_epoch = 0;
+  }
   if (h->epoch + barriers > (1u << 26)) {
     hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
     h->epoch = 0;
@@ -483,6 +516,8 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   a.ah = s.ah; a.al = s.al; a.as = s.as; a.aa = s.aa; a.ash = s.ash;
   a.xbuf0 = s.xbuf[0]; a.xbuf1 = s.xbuf[1];
   a.mfma_min = h->mfma_min;
+  a.ll_lg = s.ll_lg; a.ll_a = s.ll_a; a.llx0 = s.llx[0]; a.llx1 = s.llx[1];
+  a.ll_epoch = h->ll_epoch;
   a.af = s.af; a.ob = s.ob; a.sb = s.sb;
   a.sync = h->sync;
   a.epoch0 = h->epoch;
@@ -500,6 +535,7 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
     return QS_E_HIP;
   }
   h->epoch += barriers;
+  if (small) h->ll_epoch += 3u * (uint32_t)nL;
   return QS_OK;
 }
 
@@ -656,6 +692,7 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
     } else {
       carve_scratch(c, h->s);
       h->total_bytes += h->s.bytes;
+      if (!hip_ok(hipMemset(h->s.base, 0, h->s.ll_bytes), "hipMemset(flags)")) rc = QS_E_HIP;
     }
   }
   if (rc == QS_OK) {

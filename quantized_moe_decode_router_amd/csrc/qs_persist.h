@@ -50,6 +50,7 @@ namespace qs {
 constexpr int kPersistThreads = 512;
 constexpr int kSmallT = 4;
 constexpr int kSpinMax = 1 << 22;
+constexpr int kLLSpinMax = 1 << 16;    // polls of a flagged read (about 0.1 s) before it gives up
 // sync words (uint32 index): [16*x] per-XCD counters, [128] global counter,
 // [144 + 16*x] release lines, [272] error flag
 constexpr int kSyncWords = 512;
@@ -101,6 +102,12 @@ struct PersistArgs {
   float* xbuf1;
   uint32_t* sync;
   uint32_t epoch0;
+  // small-batch flow: flagged copies of the data that crosses workgroups
+  uint64_t* ll_lg;           // [T][E][2]  logits (low, high words)
+  uint64_t* ll_a;            // [ah | al | as | aa | ash] words of the SwiGLU outputs
+  uint64_t* llx0;            // [T][H]     residual stream between layers
+  uint64_t* llx1;
+  uint32_t ll_epoch;         // flags of this call: ll_epoch + 3*layer + {0: x in, 1: logits, 2: SwiGLU}
   // batched flow only
   int mfma_min;              // bucket size from which the MFMA path runs
   float* af;                 // [T*k][F] SwiGLU outputs of MFMA buckets (by pair id)
@@ -147,6 +154,52 @@ __device__ __forceinline__ uint32_t catomic_add(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------- flagged words ---
+// Data that one workgroup writes and every other one reads, without a grid
+// barrier between them: each 8-byte word carries 32 bits of data and a 32-bit
+// flag, written by one 64-bit store (8-byte stores are single-copy atomic),
+// so a reader that sees the flag it expects has the data of the same store.
+// Flags grow with every layer of every call, so stale words never match.
+__device__ __forceinline__ void ll_store(uint64_t* p, uint32_t v, uint32_t flag) {
+  __hip_atomic_store(p, (uint64_t)v | ((uint64_t)flag << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every thread of the workgroup: read words [0, n) of src into dst (their
+// data halves), re-reading the words whose flag is not `flag` yet.  Each
+// thread owns words tid + 512*j (j < 32, so n <= 16384).  Bounded: false
+// (after raising the error word) when the data does not arrive.
+template <class A>
+__device__ __forceinline__ bool ll_read(const A& a, const uint64_t* src, QS_LDS uint32_t* dst, int n,
+                                        uint32_t flag) {
+  const int tid = qs_tid();
+  uint32_t missing = 0;
+  for (int j = 0; j < 32; ++j)
+    if (tid + j * kPersistThreads < n) missing |= 1u << j;
+  for (int spins = 0;; ++spins) {
+    // a batch of loads in flight at once, then the checks
+    for (int j0 = 0; j0 < 32; j0 += 8) {
+      if (!((missing >> j0) & 0xFFu)) continue;
+      uint64_t w[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if ((missing >> (j0 + jj)) & 1u) w[jj] = cld64(src + tid + (j0 + jj) * kPersistThreads);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (((missing >> (j0 + jj)) & 1u) && (uint32_t)(w[jj] >> 32) == flag) {
+          dst[tid + (j0 + jj) * kPersistThreads] = (uint32_t)w[jj];
+          missing &= ~(1u << (j0 + jj));
+        }
+    }
+    if (!__syncthreads_or(missing != 0)) return true;
+    if (spins > kLLSpinMax) {
+      if (tid == 0) cst(&a.sync[kSyncError], 1u);
+      return false;
+    }
+    if ((spins & 63) == 63 && cld(&a.sync[kSyncError])) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // --------------------------------------------------------- LDS loads ---
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -191,11 +244,16 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 }
 #pragma clang diagnostic pop
 
+// Instruction i of a copy (1 KiB) goes to wave (lds/1024 + i) mod nw, so
+// the many small copies at different destinations spread over the waves
+// instead of all landing on the first one.
 template <int AUX>
 __device__ __forceinline__ void dma_to_lds(const void* g, QS_LDS void* lds, uint32_t bytes, int w, int nw) {
   const uint32_t lane = qs_tid() & 63;
   const uint32_t n16 = (bytes + 15u) >> 4;
-  for (uint32_t base = (uint32_t)w * 64u; base < n16; base += (uint32_t)nw * 64u) {
+  const uint32_t rot = ((uint32_t)(uintptr_t)lds >> 10) % (uint32_t)nw;
+  const uint32_t first = ((uint32_t)w + (uint32_t)nw - rot) % (uint32_t)nw;
+  for (uint32_t base = first * 64u; base < n16; base += (uint32_t)nw * 64u) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((QS_LDS uint4*)lds + base));
     if (base + lane < n16) dma16<AUX>((const uint4*)g + base + lane, dst);
   }
@@ -652,7 +710,7 @@ __device__ __forceinline__ void token_rinv(const A& a, PersistLds& L, const floa
 // RMS scales.
 template <bool SMALL, class A>
 __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, const float* x,
-                                             PersistLds& L) {
+                                             PersistLds& L, uint32_t flag = 0) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
   const int ET = a.r_et, TT = a.r_tt;
   const int ntt = (a.T + TT - 1) / TT;
@@ -730,7 +788,15 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
           double r;
           if (SMALL) r = L.rinv[t];
           else r = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
-          cstd(&a.logits[(size_t)t * a.E + e], a.prenorm ? fma(s, r, bias) : s + bias);
+          const double lv = a.prenorm ? fma(s, r, bias) : s + bias;
+          if (SMALL) {
+            const uint64_t bits = (uint64_t)__double_as_longlong(lv);
+            uint64_t* wp = a.ll_lg + 2 * ((size_t)t * a.E + e);
+            ll_store(wp, (uint32_t)bits, flag);
+            ll_store(wp + 1, (uint32_t)(bits >> 32), flag);
+          } else {
+            cstd(&a.logits[(size_t)t * a.E + e], lv);
+          }
           if (!SMALL && e == 0) cstd(&a.rinv[t], r);
         }
       }
@@ -742,9 +808,22 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
 // ------------------------------------------------- shared gate/up item ---
 // Rows [2*item, 2*item+2) from LDS ([row][gate, up][H] bf16), 4 waves per
 // row, each over a quarter of H; fp32 FMA.
+// Word offsets of the SwiGLU outputs in the flagged buffer, in the order
+// the down phase copies them into LDS: [ah P*F/4 | al | as P*F/16 | aa | ash T*Fs].
+template <class A>
+__device__ __forceinline__ size_t ll_al(const A& a) { return (size_t)a.T * a.k * (a.F / 4); }
+template <class A>
+__device__ __forceinline__ size_t ll_as(const A& a) { return 2 * (size_t)a.T * a.k * (a.F / 4); }
+template <class A>
+__device__ __forceinline__ size_t ll_aa(const A& a) { return ll_as(a) + (size_t)a.T * a.k * (a.F / kSubW); }
+template <class A>
+__device__ __forceinline__ size_t ll_ash(const A& a) { return ll_as(a) + 2 * (size_t)a.T * a.k * (a.F / kSubW); }
+template <class A>
+__device__ __forceinline__ int ll_a_words(const A& a) { return (int)(ll_ash(a) + (size_t)a.T * a.Fs); }
+
 template <bool SMALL, class A>
 __device__ __forceinline__ void shared_gu_item(const A& a, lds_cptr wbase, const float* x, int item,
-                                               PersistLds& L) {
+                                               PersistLds& L, uint32_t flag = 0) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
   const int rw = wave >> 2, qtr = wave & 3;
   const int hq = a.H / 4;
@@ -787,14 +866,16 @@ __device__ __forceinline__ void shared_gu_item(const A& a, lds_cptr wbase, const
       u += L.sred[((r * 4 + w4) * T + t) * 2 + 1];
     }
     const float rs = SMALL ? (float)L.rinv[t] : (float)cldd(&a.rinv[t]);
-    cstf(&a.ash[(size_t)t * a.Fs + ff], silu_mul(g * rs, u * rs));
+    const float v = silu_mul(g * rs, u * rs);
+    if (SMALL) ll_store(a.ll_a + ll_ash(a) + (size_t)t * a.Fs + ff, __float_as_uint(v), flag);
+    else cstf(&a.ash[(size_t)t * a.Fs + ff], v);
   }
   __syncthreads();
 }
 
 template <bool SMALL, class A>
 __device__ __forceinline__ void shared_items(const A& a, const LayerPtrs& Lp, const float* x,
-                                             PersistLds& L) {
+                                             PersistLds& L, uint32_t flag = 0) {
   const int npf = shared_pf_count<SMALL>(a);
   const uint32_t off = shared_off<SMALL>(a), item_b = shared_item_bytes(a);
   int j = 0;
@@ -804,7 +885,7 @@ __device__ __forceinline__ void shared_items(const A& a, const LayerPtrs& Lp, co
       slot = off;
       stage_now([&](int w, int n) { copy_shared_item(a, Lp, L.pfb + off, it, w, n); });
     }
-    shared_gu_item<SMALL>(a, L.pfb + slot, x, it, L);
+    shared_gu_item<SMALL>(a, L.pfb + slot, x, it, L, flag);
   }
 }
 
@@ -1206,7 +1287,8 @@ __device__ __forceinline__ void x_chunk(const A& a, const PersistLds& L, int t, 
 // token of its bucket; each 64-weight chunk is decoded once and applied to
 // the tokens one at a time.  SwiGLU outputs are quantised per 16 rows.
 template <int FMT, bool SMALL, class A>
-__device__ __forceinline__ void routed_gu_tile(const A& a, lds_cptr tile, int u, int f0, PersistLds& L) {
+__device__ __forceinline__ void routed_gu_tile(const A& a, lds_cptr tile, int u, int f0, PersistLds& L,
+                                               uint32_t flag = 0) {
   const int p0 = L.aoff[u], n = L.aoff[u + 1] - p0;
   const int nbh = a.H / kBlockW;
   const int nch = a.H / kChunkW;
@@ -1307,12 +1389,24 @@ __device__ __forceinline__ void routed_gu_tile(const A& a, lds_cptr tile, int u,
         int h[4], l[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) split_limbs(L.qtmp[tt * kGateTile + 4 * i + r], h[i], l[i]);
-        cst(&a.ah[(size_t)pair * (a.F / 4) + f0 / 4 + r], pack4(h[0], h[1], h[2], h[3]));
-        cst(&a.al[(size_t)pair * (a.F / 4) + f0 / 4 + r], pack4(l[0], l[1], l[2], l[3]));
+        const size_t wi = (size_t)pair * (a.F / 4) + f0 / 4 + r;
+        if (SMALL) {
+          ll_store(a.ll_a + wi, pack4(h[0], h[1], h[2], h[3]), flag);
+          ll_store(a.ll_a + ll_al(a) + wi, pack4(l[0], l[1], l[2], l[3]), flag);
+        } else {
+          cst(&a.ah[wi], pack4(h[0], h[1], h[2], h[3]));
+          cst(&a.al[wi], pack4(l[0], l[1], l[2], l[3]));
+        }
       }
       if (r == 0) {
-        cstf(&a.as[(size_t)pair * (a.F / kSubW) + f0 / kSubW], ldexpf(1.0f, ex - kFixedBits));
-        csti(&a.aa[(size_t)pair * (a.F / kSubW) + f0 / kSubW], s);
+        const size_t si = (size_t)pair * (a.F / kSubW) + f0 / kSubW;
+        if (SMALL) {
+          ll_store(a.ll_a + ll_as(a) + si, __float_as_uint(ldexpf(1.0f, ex - kFixedBits)), flag);
+          ll_store(a.ll_a + ll_aa(a) + si, (uint32_t)s, flag);
+        } else {
+          cstf(&a.as[si], ldexpf(1.0f, ex - kFixedBits));
+          csti(&a.aa[si], s);
+        }
       }
     }
   }
@@ -1322,7 +1416,7 @@ __device__ __forceinline__ void routed_gu_tile(const A& a, lds_cptr tile, int u,
 // Routed tiles of this workgroup: the first ones were copied ahead, the rest
 // are copied into the first slot on demand.
 template <int FMT, bool SMALL, class A>
-__device__ __forceinline__ void routed_tiles(const A& a, const LayerPtrs& Lp, PersistLds& L) {
+__device__ __forceinline__ void routed_tiles(const A& a, const LayerPtrs& Lp, PersistLds& L, uint32_t flag = 0) {
   const int tiles = a.F / kGateTile;
   const int na = *L.nact;
   const int base = gu_items_base<SMALL>(a);
@@ -1338,7 +1432,7 @@ __device__ __forceinline__ void routed_tiles(const A& a, const LayerPtrs& Lp, Pe
       slot = off;
       stage_now([&](int w, int n) { copy_tile(a, Lp, L.pfb + off, L.act[u], f0, w, n); });
     }
-    routed_gu_tile<FMT, SMALL>(a, L.pfb + slot, u, f0, L);
+    routed_gu_tile<FMT, SMALL>(a, L.pfb + slot, u, f0, L, flag);
   }
 }
 
@@ -1450,39 +1544,36 @@ __device__ __forceinline__ void shared_down_row(const A& a, lds_cptr srow, Persi
   }
 }
 
-// `after_wait(w, nw)` runs once, right after the first wait for this
-// phase's inputs (copies issued there overlap the down GEMVs).
-template <bool SMALL, class AW, class A>
-__device__ __forceinline__ void phase_down(const A& a, const LayerPtrs& Lp, const float* x, float* y,
-                                           PersistLds& L, AW&& after_wait) {
-  const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
+// Down phase of the small-batch kernel.  The SwiGLU outputs arrive as
+// flagged words (flag_a); the layer input x is plain (layer 0) or flagged
+// words xll, already checked complete by this workgroup in phase R; the
+// output goes to y (plain, last layer) or as flagged words (flag_y) to yll.
+// The down rows of the first chunk were copied ahead into region B.
+template <class A>
+__device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp, const float* x,
+                                                 const uint64_t* xll, float* y, uint64_t* yll, uint32_t flag_a,
+                                                 uint32_t flag_y, PersistLds& L) {
+  const int wave = qs_tid() >> 6;
   const int na = *L.nact;
   const int n_tiles = a.H / kDownRows;
-  const int T = a.T, P = a.T * a.k;
-  const int chunk = down_chunk<SMALL>(a);
+  const int T = a.T;
+  const int chunk = down_chunk<true>(a);
   const uint32_t pe = dn_expert_bytes(a), sdb = al16(sd_bytes(a));
-  QS_LDS uint8_t* base = L.pfb + down_base<SMALL>(a);
-  if (SMALL) {
-    // every pair's SwiGLU limbs and the shared SwiGLU vector -> LDS
-    dma_to_lds<kCoherent>(a.ah, L.dah, (uint32_t)P * a.F, wave, nw);
-    dma_to_lds<kCoherent>(a.al, L.dal, (uint32_t)P * a.F, wave, nw);
-    dma_to_lds<kCoherent>(a.as, L.das, (uint32_t)P * a.F / 4, wave, nw);
-    dma_to_lds<kCoherent>(a.aa, L.daa, (uint32_t)P * a.F / 4, wave, nw);
-    if (a.Fs) dma_to_lds<kCoherent>(a.ash, L.dash, (uint32_t)T * a.Fs * 4, wave, nw);
+  QS_LDS uint8_t* base = L.pfb + down_base<true>(a);
+  // residual inputs of the first tile, requested before the waits
+  float xres = 0.f;
+  const bool own_res = a.residual && qs_tid() < T * kDownRows && (int)blockIdx.x < n_tiles;
+  if (own_res) {
+    const size_t xi = (size_t)(qs_tid() / kDownRows) * a.H + blockIdx.x * kDownRows + qs_tid() % kDownRows;
+    xres = xll ? __uint_as_float((uint32_t)cld64(xll + xi)) : cldf(&x[xi]);
   }
+  // every pair's SwiGLU limbs and the shared SwiGLU vector -> LDS
+  if (!ll_read(a, a.ll_a, (QS_LDS uint32_t*)L.dah, ll_a_words(a), flag_a)) return false;
+  wait_all_and_sync();   // the down rows copied ahead
   for (int tile = blockIdx.x; tile < n_tiles; tile += a.G) {
     const int r0 = tile * kDownRows;
     const bool first = tile == (int)blockIdx.x;
-    // residual inputs of this tile, requested before the wait
-    float xres = 0.f;
-    if (a.residual && qs_tid() < T * kDownRows)
-      xres = cldf(&x[(size_t)(qs_tid() / kDownRows) * a.H + r0 + qs_tid() % kDownRows]);
-    if (first) {
-      wait_all_and_sync();   // the tile's prefetched rows (and SMALL activations)
-      after_wait(wave, nw);
-    }
-    // experts in chunks that fit beside the shared rows; the first chunk of
-    // the first tile (and its shared rows) arrived during the barrier
+    // experts in chunks that fit beside the shared rows
     for (int u0 = 0; u0 < na; u0 += chunk) {       // na >= 1, chunk >= 1
       const int u1 = na - u0 < chunk ? na : u0 + chunk;
       if (!first || u0 > 0) {
@@ -1491,8 +1582,8 @@ __device__ __forceinline__ void phase_down(const A& a, const LayerPtrs& Lp, cons
           for (int u = u0; u < u1; ++u) copy_down_rows(a, Lp, base + sdb + (uint32_t)(u - u0) * pe, L.act[u], r0, w, n);
         });
       }
-      for (int u = u0 + wave; u < u1; u += nw) down_expert<SMALL>(a, base + sdb + (uint32_t)(u - u0) * pe, u, L);
-      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<SMALL>(a, base + (uint32_t)wave * a.Fs * 2, L);
+      for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, base + sdb + (uint32_t)(u - u0) * pe, u, L);
+      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, base + (uint32_t)wave * a.Fs * 2, L);
     }
     __syncthreads();
     for (int idx = qs_tid(); idx < T * kDownRows; idx += kPersistThreads) {
@@ -1504,16 +1595,17 @@ __device__ __forceinline__ void phase_down(const A& a, const LayerPtrs& Lp, cons
         acc = fmaf(L.wl[pair], L.o[pos * kDownRows + rr], acc);
       }
       if (a.Fs) acc += L.sh[idx];
-      if (a.residual) acc += idx == qs_tid() ? xres : cldf(&x[(size_t)t * a.H + h]);
-      cstf(&y[(size_t)t * a.H + h], acc);
+      if (a.residual) {
+        const size_t xi = (size_t)t * a.H + h;
+        acc += first && own_res && idx == qs_tid() ? xres
+                                                   : (xll ? __uint_as_float((uint32_t)cld64(xll + xi)) : cldf(&x[xi]));
+      }
+      if (yll) ll_store(yll + (size_t)t * a.H + h, __float_as_uint(acc), flag_y);
+      else cstf(&y[(size_t)t * a.H + h], acc);
     }
     __syncthreads();     // L.o and L.sh are rewritten by the next tile
   }
-  // a workgroup without tiles
-  if ((int)blockIdx.x >= n_tiles) {
-    if (SMALL) wait_all_and_sync();
-    after_wait(wave, nw);
-  }
+  return true;
 }
 
 // ------------------------------------------------------------- kernel ---
@@ -1528,41 +1620,39 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
   if (FMT == 2) dma_to_lds<0>(a.cbtab, L.tab, (uint32_t)kCbTabWords * 4, wave, nw);
   pf_router_and_shared<true>(a, a.layers[0], L, wave, nw);
   wait_all_and_sync();
-  uint32_t epoch = a.epoch0;
   for (int li = 0; li < a.n_layers; ++li) {
     const LayerPtrs Lp = a.layers[li];
     const bool more = li + 1 < a.n_layers;
     const LayerPtrs Ln = a.layers[more ? li + 1 : li];   // requested now, used at the end of D
-    const float* x = li == 0 ? a.x_in : ((li - 1) & 1 ? a.xbuf1 : a.xbuf0);
-    float* y = li == a.n_layers - 1 ? a.y_out : (li & 1 ? a.xbuf1 : a.xbuf0);
+    // flags of this layer: fl = its input x, fl+1 logits, fl+2 SwiGLU, fl+3 its output
+    const uint32_t fl = a.ll_epoch + 3u * (uint32_t)li;
+    const uint64_t* xll = li == 0 ? nullptr : ((li - 1) & 1 ? a.llx1 : a.llx0);
+    uint64_t* yll = more ? (li & 1 ? a.llx1 : a.llx0) : nullptr;
     // ---- R: x -> LDS, RMS scales, router, shared gate/up
-    dma_to_lds<kCoherent>(x, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
-    wait_all_and_sync();
-    token_rinv<true>(a, L, x, 0, a.T);
-    phase_router<true>(a, Lp, x, L);
-    shared_items<true>(a, Lp, x, L);
-    if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
+    if (li == 0) dma_to_lds<kCoherent>(a.x_in, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
+    else if (!ll_read(a, xll, (QS_LDS uint32_t*)L.ax, a.T * a.H, fl)) return;
+    wait_all_and_sync();   // (and this layer's router rows and shared items)
+    token_rinv<true>(a, L, a.x_in, 0, a.T);
+    phase_router<true>(a, Lp, a.x_in, L, fl + 1);
+    shared_items<true>(a, Lp, a.x_in, L, fl + 2);
     // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
-    dma_to_lds<kCoherent>(a.logits, L.lg, (uint32_t)a.T * a.E * 8, wave, nw);
-    wait_all_and_sync();
+    if (!ll_read(a, a.ll_lg, (QS_LDS uint32_t*)L.lg, 2 * a.T * a.E, fl + 1)) return;
     topk_small(a, li, L);
     group_small(a, L);
     pf_tiles<true>(a, Lp, L, wave, nw);
     {
       const int nb = a.H / kBlockW;
-      for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, x, u / nb, u % nb, L);
+      for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, a.x_in, u / nb, u % nb, L);
     }
     wait_all_and_sync();
     // ---- GU
-    routed_tiles<FMT, true>(a, Lp, L);
-    // down rows -> region B during the barrier
-    if (!grid_barrier(a, ++epoch, [&](int w, int n) { pf_down<true>(a, Lp, L, w, n); })) return;
+    routed_tiles<FMT, true>(a, Lp, L, fl + 2);
+    // region B (unused during GU) receives the down rows of the active experts
+    pf_down<true>(a, Lp, L, wave, nw);
     // ---- D
-    phase_down<true>(a, Lp, x, y, L, [](int, int) {});
-    // region A is free: the next layer's router rows and shared items, in
-    // flight during the last barrier of the layer
+    if (!phase_down_small(a, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L)) return;
+    // region A is free: the next layer's router rows and shared items
     if (more) pf_router_and_shared<true>(a, Ln, L, wave, nw);
-    if (more && !grid_barrier(a, ++epoch, [](int, int) {})) return;
   }
 }
 

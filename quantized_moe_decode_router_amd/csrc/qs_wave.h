@@ -18,9 +18,12 @@
 
 namespace qs {
 
+// Every control used here reads a valid lane for every lane, so the move
+// needs no "old" value; that lets the compiler fold it into the consuming
+// VALU instruction as a DPP operand.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
 // Partner value of butterfly stage S (see above).
