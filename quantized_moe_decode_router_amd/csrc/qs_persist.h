@@ -973,25 +973,23 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
   const int E = a.E, k = a.k, T = a.T, S = kf_stride(E), NG = S / 8, G4 = (NG + 3) & ~3;
   QS_LDS float* gm = L.kf + T * S;                 // [T][G4] group maxima, -inf padded
   QS_LDS int* tau = (QS_LDS int*)(gm + T * G4);    // [T]
-  for (int i = tid; i < T * S; i += nt) {
-    const int t = i / S, e = i % S;
-    L.kf[i] = e < E ? (float)nan_low(L.lg[t * E + e]) : -INFINITY;
-  }
-  if (tid < T) {
-    L.ncand[tid] = 0;
-    // fewer than k groups: no bound, every expert is a candidate
-    tau[tid] = NG < k ? f32_ord(-INFINITY) : 0x7FFFFFFF;
-  }
-  __syncthreads();
+  // keys of one group of 8 experts and their maximum, one thread per (token, group)
   for (int i = tid; i < T * G4; i += nt) {
     const int t = i / G4, g = i % G4;
     float mx = -INFINITY;
     if (g < NG) {
-      const float4 p = lds_f4(L.kf + t * S + g * 8), q = lds_f4(L.kf + t * S + g * 8 + 4);
-      mx = fmaxf(fmaxf(fmaxf(p.x, p.y), fmaxf(p.z, p.w)), fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = 8 * g + j;
+        const float key = e < E ? (float)nan_low(L.lg[t * E + e]) : -INFINITY;
+        L.kf[t * S + e] = key;
+        mx = fmaxf(mx, key);
+      }
     }
     gm[i] = mx;
   }
+  // fewer than k groups: no bound, every expert is a candidate
+  if (tid < T) tau[tid] = NG < k ? f32_ord(-INFINITY) : 0x7FFFFFFF;
   __syncthreads();
   // tau = the smallest group maximum with fewer than k larger ones
   if (NG >= k) {
@@ -1010,17 +1008,22 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
     }
   }
   __syncthreads();
-  for (int i = tid; i < T * E; i += nt) {
-    const int t = i / E, e = i % E;
-    if (L.kf[t * S + e] >= f32_unord(tau[t])) {
-      const int slot = __hip_atomic_fetch_add(&L.ncand[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      L.cand[t * E + slot] = e;
+  if (wave < T) {
+    // one wave per token from here on (its own LDS rows, no block barrier):
+    // the experts with key >= tau, compacted in index order by ballots
+    const int t = wave;
+    const float thr = f32_unord(tau[t]);
+    QS_LDS int* cd = L.cand + t * E;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int m = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const bool p = e < E && L.kf[t * S + e] >= thr;
+      const uint64_t bm = __ballot(p);
+      if (p) cd[m + __popcll(bm & below)] = e;
+      m += __popcll(bm);
     }
-  }
-  __syncthreads();
-  if (wave < T) {                      // exact rank among the candidates, one wave per token
-    const int t = wave, m = L.ncand[t];
-    const QS_LDS int* cd = L.cand + t * E;
+    // exact rank among the candidates in (logit desc, index asc)
     for (int i0 = 0; i0 < m; i0 += 64) {
       const int i = i0 + lane;
       const int e = i < m ? cd[i] : 0;
@@ -1043,10 +1046,7 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
         L.sv[t * k + r] = v;
       }
     }
-  }
-  __syncthreads();
-  if (wave < T) {                      // renormalised softmax over the picks
-    const int t = wave;
+    // renormalised softmax over the picks
     const double top0 = L.sv[t * k];
     const double z = lane < k ? exp(L.sv[t * k + lane] - top0) : 0.0;
     const double sum = bfly_sum_f64<6>(z);
@@ -1549,10 +1549,12 @@ __device__ __forceinline__ void shared_down_row(const A& a, lds_cptr srow, Persi
 // words xll, already checked complete by this workgroup in phase R; the
 // output goes to y (plain, last layer) or as flagged words (flag_y) to yll.
 // The down rows of the first chunk were copied ahead into region B.
-template <class A>
+// `spare(w, nw)` runs once, on the waves that have no combine work of the
+// last tile.
+template <class A, class HK>
 __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp, const float* x,
                                                  const uint64_t* xll, float* y, uint64_t* yll, uint32_t flag_a,
-                                                 uint32_t flag_y, PersistLds& L) {
+                                                 uint32_t flag_y, PersistLds& L, HK&& spare) {
   const int wave = qs_tid() >> 6;
   const int na = *L.nact;
   const int n_tiles = a.H / kDownRows;
@@ -1586,6 +1588,8 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
       if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, base + (uint32_t)wave * a.Fs * 2, L);
     }
     __syncthreads();
+    const int cw = (T * kDownRows + 63) / 64;     // waves with combine work
+    if (tile + a.G >= n_tiles && wave >= cw) spare(wave - cw, kPersistThreads / 64 - cw);
     for (int idx = qs_tid(); idx < T * kDownRows; idx += kPersistThreads) {
       const int t = idx / kDownRows, rr = idx % kDownRows, h = r0 + rr;
       float acc = 0.f;
@@ -1605,6 +1609,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
     }
     __syncthreads();     // L.o and L.sh are rewritten by the next tile
   }
+  if ((int)blockIdx.x >= n_tiles) spare(wave, kPersistThreads / 64);
   return true;
 }
 
@@ -1649,10 +1654,12 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     routed_tiles<FMT, true>(a, Lp, L, fl + 2);
     // region B (unused during GU) receives the down rows of the active experts
     pf_down<true>(a, Lp, L, wave, nw);
-    // ---- D
-    if (!phase_down_small(a, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L)) return;
-    // region A is free: the next layer's router rows and shared items
-    if (more) pf_router_and_shared<true>(a, Ln, L, wave, nw);
+    // ---- D; region A is free: the next layer's router rows and shared
+    // items are issued beside the combine
+    if (!phase_down_small(a, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L, [&](int w, int n) {
+          if (more) pf_router_and_shared<true>(a, Ln, L, w, n);
+        }))
+      return;
   }
 }
 
