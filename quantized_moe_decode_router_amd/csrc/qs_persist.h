@@ -325,7 +325,7 @@ __host__ __device__ inline uint32_t abuf_bytes(int T, int H, int E, int P, int F
 }
 
 struct LdsLayout {
-  uint32_t tab, cnt, off, act, aoff, nact, mask, ids, pairs, tok_order, pos_of, wl, o, red, sh, ga, sred,
+  uint32_t tab, cnt, off, act, aoff, nact, mask, ids, pairs, tok_order, cw, pos_of, wl, o, red, sh, ga, sred,
       qtmp, rinv, kf, cand, ncand, sv, xh, xl, xs, xa, abuf, pfb, end;
 };
 
@@ -350,6 +350,7 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.ids = take((uint32_t)P * 4);
   l.pairs = take((uint32_t)P * 4);
   l.tok_order = take((uint32_t)P * 4);
+  l.cw = take(small ? (uint32_t)P * 4 : 0);
   l.pos_of = take((uint32_t)P * 4);
   l.wl = take((uint32_t)P * 4);
   l.o = take((uint32_t)P * kDownRows * 4);
@@ -387,6 +388,7 @@ struct PersistLds {
   QS_LDS int* ids;        // [P]   expert of pair id
   QS_LDS int* pairs;      // [P]   pair id at bucket position
   QS_LDS int* tok_order;  // [P]   per token, positions by ascending expert
+  QS_LDS float* cw;       // [P]   SMALL: router weight of tok_order's entry
   QS_LDS int* pos_of;     // [P]   bucket position of pair id
   QS_LDS float* wl;       // [P]   router weight of pair id
   QS_LDS float* o;        // [P*kDownRows] down outputs
@@ -431,6 +433,7 @@ __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const A& a, bool c
   L.ids = (QS_LDS int*)(b + l.ids);
   L.pairs = (QS_LDS int*)(b + l.pairs);
   L.tok_order = (QS_LDS int*)(b + l.tok_order);
+  L.cw = (QS_LDS float*)(b + l.cw);
   L.pos_of = (QS_LDS int*)(b + l.pos_of);
   L.wl = (QS_LDS float*)(b + l.wl);
   L.o = (QS_LDS float*)(b + l.o);
@@ -657,7 +660,7 @@ __device__ __forceinline__ void pf_down(const A& a, const LayerPtrs& Lp, Persist
   const int r0 = blockIdx.x * kDownRows;
   if (r0 >= a.H) return;
   QS_LDS uint8_t* base = L.pfb + down_base<SMALL>(a);
-  copy_sd_rows(a, Lp, base, r0, w, nw);
+  if (!SMALL) copy_sd_rows(a, Lp, base, r0, w, nw);   // SMALL: copied ahead with the layer's router rows
   const int n = down_pf_count<SMALL>(a, *L.nact);
   for (int u = 0; u < n; ++u)
     copy_down_rows(a, Lp, base + al16(sd_bytes(a)) + (uint32_t)u * dn_expert_bytes(a), L.act[u], r0, w, nw);
@@ -929,10 +932,10 @@ __device__ __forceinline__ void topk_wave(const A& a, int t, int layer_i, Persis
       seli = bi;
     }
   }
-  const double z = lane < k ? exp(selv - top0) : 0.0;
-  const double sum = bfly_sum_f64<6>(z);
+  const float z = lane < k ? __expf((float)(selv - top0)) : 0.f;
+  const float sum = bfly_sum<6>(z);
   if (lane < k) {
-    const float w = (float)(z / sum);
+    const float w = __fdividef(z, sum);
     if (SMALL) {
       L.ids[t * k + lane] = seli;
       L.wl[t * k + lane] = w;
@@ -1046,12 +1049,13 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
         L.sv[t * k + r] = v;
       }
     }
-    // renormalised softmax over the picks
+    // renormalised softmax over the picks: exponent of the fp64 difference
+    // to the top pick, in fp32
     const double top0 = L.sv[t * k];
-    const double z = lane < k ? exp(L.sv[t * k + lane] - top0) : 0.0;
-    const double sum = bfly_sum_f64<6>(z);
+    const float z = lane < k ? __expf((float)(L.sv[t * k + lane] - top0)) : 0.f;
+    const float sum = bfly_sum<6>(z);
     if (lane < k) {
-      const float w = (float)(z / sum);
+      const float w = __fdividef(z, sum);
       L.wl[t * k + lane] = w;
       if (blockIdx.x == 0) {
         const size_t o = (size_t)layer_i * T * k + t * k + lane;
@@ -1097,7 +1101,10 @@ __device__ __forceinline__ void group_small(const A& a, PersistLds& L) {
     const uint64_t below = (1ull << lane) - 1ull;
     for (int tt = 0; tt < a.T; ++tt) {
       const uint64_t m = __ballot(live && tok == tt);
-      if (live && tok == tt) L.tok_order[tt * k + __popcll(m & below)] = lane;
+      if (live && tok == tt) {
+        L.tok_order[tt * k + __popcll(m & below)] = lane;
+        L.cw[tt * k + __popcll(m & below)] = L.wl[ps];
+      }
     }
   }
   __syncthreads();
@@ -1595,8 +1602,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
       float acc = 0.f;
       for (int jj = 0; jj < a.k; ++jj) {
         const int pos = L.tok_order[t * a.k + jj];
-        const int pair = L.pairs[pos];
-        acc = fmaf(L.wl[pair], L.o[pos * kDownRows + rr], acc);
+        acc = fmaf(L.cw[t * a.k + jj], L.o[pos * kDownRows + rr], acc);
       }
       if (a.Fs) acc += L.sh[idx];
       if (a.residual) {
@@ -1624,6 +1630,8 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
   if (FMT == 2) dma_to_lds<0>(a.cbtab, L.tab, (uint32_t)kCbTabWords * 4, wave, nw);
   pf_router_and_shared<true>(a, a.layers[0], L, wave, nw);
+  if ((int)blockIdx.x * kDownRows < a.H)
+    copy_sd_rows(a, a.layers[0], L.pfb + down_base<true>(a), blockIdx.x * kDownRows, wave, nw);
   wait_all_and_sync();
   for (int li = 0; li < a.n_layers; ++li) {
     const LayerPtrs Lp = a.layers[li];
@@ -1657,7 +1665,11 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     // ---- D; region A is free: the next layer's router rows and shared
     // items are issued beside the combine
     if (!phase_down_small(a, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L, [&](int w, int n) {
-          if (more) pf_router_and_shared<true>(a, Ln, L, w, n);
+          if (!more) return;
+          pf_router_and_shared<true>(a, Ln, L, w, n);
+          // the shared down rows are no longer read by this layer
+          if ((int)blockIdx.x * kDownRows < a.H)
+            copy_sd_rows(a, Ln, L.pfb + down_base<true>(a), blockIdx.x * kDownRows, w, n);
         }))
       return;
   }
