@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 N_BATCHES = 64
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_persist_a3b_stack40_zipf_T1_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_persist_small_a3b_stack40_zipf_T1_hbm_traffic.txt")
 
 
 def parse():
@@ -199,7 +199,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, T0, L, args.cpu_layers)
-    kname = ("k_persist<" + ("cb2" if wl.gate_up_format == "cb2" else "q2k") + "> (whole decode call)"
+    fmt = "cb2" if wl.gate_up_format == "cb2" else "q2k"
+    kname = (("k_persist_small" if T0 <= 4 else "k_persist_big") + f"<{fmt}> (one launch = the whole decode call)"
              if not args.multikernel else "decode call (one launch per step kind)")
     achieved = head["bytes_per_step"] / (head["launch_ms_mean"] * 1e-3) / 1e9
     traffic = None if args.multikernel or args.layers else committed_traffic(wl.name, T0)
