@@ -164,40 +164,54 @@ __device__ __forceinline__ void ll_store(uint64_t* p, uint32_t v, uint32_t flag)
   __hip_atomic_store(p, (uint64_t)v | ((uint64_t)flag << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Every thread of the workgroup: read words [0, n) of src into dst (their
-// data halves), re-reading the words whose flag is not `flag` yet.  Each
-// thread owns words tid + 512*j (j < 32, so n <= 16384).  Bounded: false
-// (after raising the error word) when the data does not arrive.
+// Waves [0, nwp) of the workgroup read words [0, n) of src into dst (their
+// data halves), re-reading the words whose flag is not `flag` yet.  Thread
+// tid owns words tid + 64*nwp*j (j < 32, so n <= 2048*nwp).  Each wave polls
+// on its own until its words are in; the other waves only meet them at the
+// closing barrier, so they may have copies into LDS in flight (a wave that
+// has issued one waits for it at its next LDS access).  Bounded: false for
+// every thread (after raising the error word) when the data does not arrive;
+// `err` is an LDS word that is 0 at kernel start.
 template <class A>
 __device__ __forceinline__ bool ll_read(const A& a, const uint64_t* src, QS_LDS uint32_t* dst, int n,
-                                        uint32_t flag) {
-  const int tid = qs_tid();
-  uint32_t missing = 0;
-  for (int j = 0; j < 32; ++j)
-    if (tid + j * kPersistThreads < n) missing |= 1u << j;
-  for (int spins = 0;; ++spins) {
-    // a batch of loads in flight at once, then the checks
-    for (int j0 = 0; j0 < 32; j0 += 8) {
-      if (!((missing >> j0) & 0xFFu)) continue;
-      uint64_t w[8];
+                                        uint32_t flag, QS_LDS int* err, int nwp = kPersistThreads / 64) {
+  const int tid = qs_tid(), nth = nwp * 64;
+  if (tid < nth) {
+    uint32_t missing = 0;
+    for (int j = 0; j < 32; ++j)
+      if (tid + j * nth < n) missing |= 1u << j;
+    for (int spins = 0;; ++spins) {
+      // a batch of loads in flight at once, then the checks
+      for (int j0 = 0; j0 < 32; j0 += 8) {
+        if (!((missing >> j0) & 0xFFu)) continue;
+        uint64_t w[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if ((missing >> (j0 + jj)) & 1u) w[jj] = cld64(src + tid + (j0 + jj) * kPersistThreads);
+        for (int jj = 0; jj < 8; ++jj)
+          if ((missing >> (j0 + jj)) & 1u) w[jj] = cld64(src + tid + (j0 + jj) * nth);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if (((missing >> (j0 + jj)) & 1u) && (uint32_t)(w[jj] >> 32) == flag) {
-          dst[tid + (j0 + jj) * kPersistThreads] = (uint32_t)w[jj];
-          missing &= ~(1u << (j0 + jj));
+        for (int jj = 0; jj < 8; ++jj)
+          if (((missing >> (j0 + jj)) & 1u) && (uint32_t)(w[jj] >> 32) == flag) {
+            dst[tid + (j0 + jj) * nth] = (uint32_t)w[jj];
+            missing &= ~(1u << (j0 + jj));
+          }
+      }
+      if (!__builtin_amdgcn_ballot_w64(missing != 0)) break;
+      if (spins > kLLSpinMax) {
+        if ((tid & 63) == 0) {
+          cst(&a.sync[kSyncError], 1u);
+          *err = 1;
         }
+        break;
+      }
+      if ((spins & 63) == 63 && cld(&a.sync[kSyncError])) {
+        if ((tid & 63) == 0) *err = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
-    if (!__syncthreads_or(missing != 0)) return true;
-    if (spins > kLLSpinMax) {
-      if (tid == 0) cst(&a.sync[kSyncError], 1u);
-      return false;
-    }
-    if ((spins & 63) == 63 && cld(&a.sync[kSyncError])) return false;
-    __builtin_amdgcn_s_sleep(1);
   }
+  __syncthreads();
+  return *err == 0;
 }
 
 // --------------------------------------------------------- LDS loads ---
@@ -325,7 +339,7 @@ __host__ __device__ inline uint32_t abuf_bytes(int T, int H, int E, int P, int F
 }
 
 struct LdsLayout {
-  uint32_t tab, cnt, off, act, aoff, nact, mask, ids, pairs, tok_order, cw, pos_of, wl, o, red, sh, ga, sred,
+  uint32_t tab, cnt, off, act, aoff, nact, llerr, mask, ids, pairs, tok_order, cw, pos_of, wl, o, red, sh, ga, sred,
       qtmp, rinv, kf, cand, ncand, sv, xh, xl, xs, xa, abuf, pfb, end;
 };
 
@@ -346,6 +360,7 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.act = take((uint32_t)E * 4);
   l.aoff = take((uint32_t)(E + 1) * 4);
   l.nact = take(4);
+  l.llerr = take(4);
   l.mask = take(small ? 0 : (uint32_t)E * 32);
   l.ids = take((uint32_t)P * 4);
   l.pairs = take((uint32_t)P * 4);
@@ -384,6 +399,7 @@ struct PersistLds {
   QS_LDS int* act;        // [E]   active experts, ascending
   QS_LDS int* aoff;       // [E+1] bucket of active expert u: positions [aoff[u], aoff[u+1])
   QS_LDS int* nact;       // [1]
+  QS_LDS int* llerr;      // [1] a flagged read gave up (0 at kernel start)
   QS_LDS uint32_t* mask;  // [E*8]
   QS_LDS int* ids;        // [P]   expert of pair id
   QS_LDS int* pairs;      // [P]   pair id at bucket position
@@ -429,6 +445,7 @@ __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const A& a, bool c
   L.act = (QS_LDS int*)(b + l.act);
   L.aoff = (QS_LDS int*)(b + l.aoff);
   L.nact = (QS_LDS int*)(b + l.nact);
+  L.llerr = (QS_LDS int*)(b + l.llerr);
   L.mask = (QS_LDS uint32_t*)(b + l.mask);
   L.ids = (QS_LDS int*)(b + l.ids);
   L.pairs = (QS_LDS int*)(b + l.pairs);
@@ -644,14 +661,30 @@ __device__ __forceinline__ void pf_shared_items(const A& a, const LayerPtrs& Lp,
                      nw);
 }
 
+// A wave that has issued a copy into LDS waits at its next LDS access until
+// the copied data has landed, so the expert ids a burst of copies needs are
+// read first: L.act[u0 + lane] (0 past n) in every lane.
+__device__ __forceinline__ int act_lanes(const PersistLds& L, int u0, int n) {
+  const int i = u0 + (int)(qs_tid() & 63);
+  return i < n ? L.act[i] : 0;
+}
+
 template <bool SMALL, class A>
 __device__ __forceinline__ void pf_tiles(const A& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
   const int na = *L.nact, tiles = a.F / kGateTile, base = gu_items_base<SMALL>(a);
   const int n = tile_pf_count<SMALL>(a, na), j0 = my_count(a, base);
-  for (int j = 0; j < n; ++j) {
-    const int r = (int)blockIdx.x + (j0 + j) * a.G - base;
-    copy_tile(a, Lp, L.pfb + tile_off<SMALL>(a) + (uint32_t)j * gu_tile_bytes(a), L.act[r / tiles],
-              (r % tiles) * kGateTile, w, nw);
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    // lane i: the expert of tile c0 + i
+    const int i = c0 + (int)(qs_tid() & 63);
+    const int ri = (int)blockIdx.x + (j0 + i) * a.G - base;
+    const int el = i < n ? L.act[ri / tiles] : 0;
+    const int m = n - c0 < 64 ? n - c0 : 64;
+    for (int jj = 0; jj < m; ++jj) {
+      const int j = c0 + jj;
+      const int r = (int)blockIdx.x + (j0 + j) * a.G - base;
+      copy_tile(a, Lp, L.pfb + tile_off<SMALL>(a) + (uint32_t)j * gu_tile_bytes(a),
+                __builtin_amdgcn_readlane(el, jj), (r % tiles) * kGateTile, w, nw);
+    }
   }
 }
 
@@ -660,10 +693,15 @@ __device__ __forceinline__ void pf_down(const A& a, const LayerPtrs& Lp, Persist
   const int r0 = blockIdx.x * kDownRows;
   if (r0 >= a.H) return;
   QS_LDS uint8_t* base = L.pfb + down_base<SMALL>(a);
-  if (!SMALL) copy_sd_rows(a, Lp, base, r0, w, nw);   // SMALL: copied ahead with the layer's router rows
   const int n = down_pf_count<SMALL>(a, *L.nact);
-  for (int u = 0; u < n; ++u)
-    copy_down_rows(a, Lp, base + al16(sd_bytes(a)) + (uint32_t)u * dn_expert_bytes(a), L.act[u], r0, w, nw);
+  if (!SMALL) copy_sd_rows(a, Lp, base, r0, w, nw);   // SMALL: copied ahead with the layer's router rows
+  for (int u0 = 0; u0 < n; u0 += 64) {
+    const int el = act_lanes(L, u0, n);
+    const int m = n - u0 < 64 ? n - u0 : 64;
+    for (int i = 0; i < m; ++i)
+      copy_down_rows(a, Lp, base + al16(sd_bytes(a)) + (uint32_t)(u0 + i) * dn_expert_bytes(a),
+                     __builtin_amdgcn_readlane(el, i), r0, w, nw);
+  }
 }
 
 // ------------------------------------------------------------ phase R ---
@@ -707,10 +745,19 @@ __device__ __forceinline__ void token_rinv(const A& a, PersistLds& L, const floa
   __syncthreads();
 }
 
+// The router bias of the logit this thread finishes for expert group eg
+// (0 on the other threads).
+template <class A>
+__device__ __forceinline__ double router_bias(const A& a, const LayerPtrs& Lp, int eg) {
+  const int e = eg * a.r_et + qs_tid() / a.r_tt;
+  return qs_tid() < a.r_et * a.r_tt && eg < router_groups(a) && e < a.E ? (double)Lp.bias[e] : 0.0;
+}
+
 // Router: this workgroup's expert groups (rows in LDS) against every token
-// group.  Otherwise-flow workgroups also sum x^2 of the tokens they route
-// (same order as token_rinv); the owner of expert group 0 publishes the
-// RMS scales.
+// group.  Each workgroup also sums x^2 of the tokens it routes (same order
+// as token_rinv).  SMALL: the sums give L.rinv, read after the next block
+// barrier (workgroups without a router group call token_rinv instead).
+// Otherwise: the owner of expert group 0 publishes the RMS scales.
 template <bool SMALL, class A>
 __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, const float* x,
                                              PersistLds& L, uint32_t flag = 0) {
@@ -719,7 +766,7 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
   const int ntt = (a.T + TT - 1) / TT;
   const int hw = a.H / nw;
   const int V = ET * TT + TT;
-  const bool want_ss = !SMALL && a.prenorm;
+  const bool want_ss = a.prenorm;
   const QS_LDS float* wr = (const QS_LDS float*)L.pfb;
   if (!SMALL) wait_all_and_sync();   // router rows prefetched during the last barrier
   int i = 0;
@@ -727,8 +774,7 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
     if (i > 0) stage_now([&](int w, int n) { copy_router_rows(a, Lp, L, eg, w, n); });
     const int e0 = eg * ET;
     // the bias of the logit this thread finishes, requested before the sums
-    double bias = 0.0;
-    if (qs_tid() < ET * TT && e0 + qs_tid() / TT < a.E) bias = (double)Lp.bias[e0 + qs_tid() / TT];
+    const double bias = router_bias(a, Lp, eg);
 #pragma unroll 1
     for (int tg = 0; tg < ntt; ++tg) {
       const int t0 = tg * TT, nt = a.T - t0 < TT ? a.T - t0 : TT;
@@ -788,10 +834,9 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
             s += L.red[32 + w * V + ii * TT + j];
             if (want_ss) q += L.red[32 + w * V + ET * TT + j];
           }
-          double r;
-          if (SMALL) r = L.rinv[t];
-          else r = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
+          const double r = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
           const double lv = a.prenorm ? fma(s, r, bias) : s + bias;
+          if (SMALL && ii == 0) L.rinv[t] = r;
           if (SMALL) {
             const uint64_t bits = (uint64_t)__double_as_longlong(lv);
             uint64_t* wp = a.ll_lg + 2 * ((size_t)t * a.E + e);
@@ -823,6 +868,15 @@ template <class A>
 __device__ __forceinline__ size_t ll_ash(const A& a) { return ll_as(a) + 2 * (size_t)a.T * a.k * (a.F / kSubW); }
 template <class A>
 __device__ __forceinline__ int ll_a_words(const A& a) { return (int)(ll_ash(a) + (size_t)a.T * a.Fs); }
+// SMALL flow: waves [kCopyW0, 8) issue the copies that overlap a flagged
+// read, waves [0, kCopyW0) poll (when the words fit 32 per thread of them).
+constexpr int kCopyW0 = 4;
+template <class A>
+__device__ __forceinline__ int ll_waves(const A& a, int words) {
+  return words <= 32 * 64 * kCopyW0 ? kCopyW0 : kPersistThreads / 64;
+}
+template <class A>
+__device__ __forceinline__ int ll_a_waves(const A& a) { return ll_waves(a, ll_a_words(a)); }
 
 template <bool SMALL, class A>
 __device__ __forceinline__ void shared_gu_item(const A& a, lds_cptr wbase, const float* x, int item,
@@ -1576,8 +1630,9 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
     const size_t xi = (size_t)(qs_tid() / kDownRows) * a.H + blockIdx.x * kDownRows + qs_tid() % kDownRows;
     xres = xll ? __uint_as_float((uint32_t)cld64(xll + xi)) : cldf(&x[xi]);
   }
-  // every pair's SwiGLU limbs and the shared SwiGLU vector -> LDS
-  if (!ll_read(a, a.ll_a, (QS_LDS uint32_t*)L.dah, ll_a_words(a), flag_a)) return false;
+  // every pair's SwiGLU limbs and the shared SwiGLU vector -> LDS (on the
+  // waves without down-row copies in flight, when the words fit them)
+  if (!ll_read(a, a.ll_a, (QS_LDS uint32_t*)L.dah, ll_a_words(a), flag_a, L.llerr, ll_a_waves(a))) return false;
   wait_all_and_sync();   // the down rows copied ahead
   for (int tile = blockIdx.x; tile < n_tiles; tile += a.G) {
     const int r0 = tile * kDownRows;
@@ -1588,15 +1643,20 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
       if (!first || u0 > 0) {
         stage_now([&](int w, int n) {
           if (u0 == 0) copy_sd_rows(a, Lp, base, r0, w, n);
-          for (int u = u0; u < u1; ++u) copy_down_rows(a, Lp, base + sdb + (uint32_t)(u - u0) * pe, L.act[u], r0, w, n);
+          for (int c0 = u0; c0 < u1; c0 += 64) {
+            const int el = act_lanes(L, c0, u1);
+            const int m = u1 - c0 < 64 ? u1 - c0 : 64;
+            for (int i = 0; i < m; ++i)
+              copy_down_rows(a, Lp, base + sdb + (uint32_t)(c0 + i - u0) * pe, __builtin_amdgcn_readlane(el, i), r0, w, n);
+          }
         });
       }
       for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, base + sdb + (uint32_t)(u - u0) * pe, u, L);
       if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, base + (uint32_t)wave * a.Fs * 2, L);
     }
     __syncthreads();
-    const int cw = (T * kDownRows + 63) / 64;     // waves with combine work
-    if (tile + a.G >= n_tiles && wave >= cw) spare(wave - cw, kPersistThreads / 64 - cw);
+    // waves [0, kCopyW0) have the combine work (T * kDownRows <= 64 words)
+    if (tile + a.G >= n_tiles && wave >= kCopyW0) spare(wave - kCopyW0, kPersistThreads / 64 - kCopyW0);
     for (int idx = qs_tid(); idx < T * kDownRows; idx += kPersistThreads) {
       const int t = idx / kDownRows, rr = idx % kDownRows, h = r0 + rr;
       float acc = 0.f;
@@ -1615,7 +1675,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
     }
     __syncthreads();     // L.o and L.sh are rewritten by the next tile
   }
-  if ((int)blockIdx.x >= n_tiles) spare(wave, kPersistThreads / 64);
+  if ((int)blockIdx.x >= n_tiles && wave >= kCopyW0) spare(wave - kCopyW0, kPersistThreads / 64 - kCopyW0);
   return true;
 }
 
@@ -1628,6 +1688,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   PersistLds L = carve_lds<true>(lds_raw, a, FMT == 2);
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
+  if (qs_tid() == 0) *L.llerr = 0;
   if (FMT == 2) dma_to_lds<0>(a.cbtab, L.tab, (uint32_t)kCbTabWords * 4, wave, nw);
   pf_router_and_shared<true>(a, a.layers[0], L, wave, nw);
   if ((int)blockIdx.x * kDownRows < a.H)
@@ -1643,25 +1704,31 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     uint64_t* yll = more ? (li & 1 ? a.llx1 : a.llx0) : nullptr;
     // ---- R: x -> LDS, RMS scales, router, shared gate/up
     if (li == 0) dma_to_lds<kCoherent>(a.x_in, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
-    else if (!ll_read(a, xll, (QS_LDS uint32_t*)L.ax, a.T * a.H, fl)) return;
+    else if (!ll_read(a, xll, (QS_LDS uint32_t*)L.ax, a.T * a.H, fl, L.llerr, ll_waves(a, a.T * a.H))) return;
     wait_all_and_sync();   // (and this layer's router rows and shared items)
-    token_rinv<true>(a, L, a.x_in, 0, a.T);
-    phase_router<true>(a, Lp, a.x_in, L, fl + 1);
+    if ((int)blockIdx.x >= router_groups(a)) token_rinv<true>(a, L, a.x_in, 0, a.T);
+    phase_router<true>(a, Lp, a.x_in, L, fl + 1);   // ends with a block barrier
     shared_items<true>(a, Lp, a.x_in, L, fl + 2);
     // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
-    if (!ll_read(a, a.ll_lg, (QS_LDS uint32_t*)L.lg, 2 * a.T * a.E, fl + 1)) return;
+    if (!ll_read(a, a.ll_lg, (QS_LDS uint32_t*)L.lg, 2 * a.T * a.E, fl + 1, L.llerr)) return;
     topk_small(a, li, L);
     group_small(a, L);
-    pf_tiles<true>(a, Lp, L, wave, nw);
+    // tiles copied by waves [kCopyW0, 8) while the others quantise x
+    if (wave >= kCopyW0) pf_tiles<true>(a, Lp, L, wave - kCopyW0, nw - kCopyW0);
     {
       const int nb = a.H / kBlockW;
-      for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, a.x_in, u / nb, u % nb, L);
+      if (wave < kCopyW0)
+        for (int u = wave; u < a.T * nb; u += kCopyW0) quant_x_wave<true>(a, a.x_in, u / nb, u % nb, L);
     }
     wait_all_and_sync();
     // ---- GU
     routed_tiles<FMT, true>(a, Lp, L, fl + 2);
-    // region B (unused during GU) receives the down rows of the active experts
-    pf_down<true>(a, Lp, L, wave, nw);
+    // region B (unused during GU) receives the down rows of the active
+    // experts, from the waves that do not poll the SwiGLU words
+    {
+      const int dw = ll_a_waves(a) == kCopyW0 ? kCopyW0 : 0;
+      if (wave >= dw) pf_down<true>(a, Lp, L, wave - dw, nw - dw);
+    }
     // ---- D; region A is free: the next layer's router rows and shared
     // items are issued beside the combine
     if (!phase_down_small(a, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L, [&](int w, int n) {
