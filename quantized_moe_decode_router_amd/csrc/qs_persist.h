@@ -1024,8 +1024,117 @@ __device__ __forceinline__ float f32_unord(int o) {
   return __int_as_float(o >= 0 ? o : (int)(0x80000000u - (uint32_t)o));
 }
 
+// Order-preserving integer image of an fp64 value, -0 taken as +0: a
+// larger value has a larger image, equal values the same image.
+__device__ __forceinline__ uint64_t f64_ord(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
+  return (b >> 63) ? ~b : (b | (1ull << 63));
+}
+__device__ __forceinline__ double f64_unord(uint64_t o) {
+  return __longlong_as_double((long long)((o >> 63) ? (o & ~(1ull << 63)) : ~o));
+}
+
+// The renormalised softmax over token t's picks (their logits in L.sv in
+// rank order): the exponent of the fp64 difference to the top pick, in fp32.
+// One wave.
+template <class A>
+__device__ __forceinline__ void topk_weights(const A& a, int layer_i, int t, PersistLds& L) {
+  const int lane = qs_tid() & 63, k = a.k;
+  const double top0 = L.sv[t * k];
+  const float z = lane < k ? __expf((float)(L.sv[t * k + lane] - top0)) : 0.f;
+  const float sum = bfly_sum<6>(z);
+  if (lane < k) {
+    const float w = __fdividef(z, sum);
+    L.wl[t * k + lane] = w;
+    if (blockIdx.x == 0) {
+      const size_t o = (size_t)layer_i * a.T * k + t * k + lane;
+      if (a.ids_out) a.ids_out[o] = L.ids[t * k + lane];
+      if (a.w_out) a.w_out[o] = w;
+    }
+  }
+}
+
+// E <= 256: one wave per token, no block barrier before the last.  Lane l
+// holds experts 4l..4l+3; a lane pair is a group of 8.  The k-th largest
+// group maximum is found with one broadcast per group, the candidates are
+// compacted in index order with a prefix sum, and each is ranked against all
+// of them on the order-preserving integer images of their fp64 logits --
+// since candidates sit in index order, a tie goes to the lower position.
+// (L.kf is not used.)
+template <class A>
+__device__ __forceinline__ void topk_small_lds(const A& a, int layer_i, PersistLds& L);
+
 template <class A>
 __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& L) {
+  if (a.E > 256) {
+    topk_small_lds(a, layer_i, L);
+    return;
+  }
+  const int lane = qs_tid() & 63, wave = qs_tid() >> 6;
+  const int E = a.E, k = a.k, T = a.T, NG = kf_stride(E) / 8;
+  if (wave < T) {
+    const int t = wave, e0 = 4 * lane;
+    double v[4];
+    float key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = e0 + j < E ? nan_low(L.lg[t * E + e0 + j]) : -INFINITY;
+      key[j] = e0 + j < E ? (float)v[j] : -INFINITY;
+    }
+    float g = fmaxf(fmaxf(key[0], key[1]), fmaxf(key[2], key[3]));
+    g = fmaxf(g, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(g), 0xB1, 0xF, 0xF, false)));  // quad_perm [1,0,3,2]
+    float tau = -INFINITY;     // fewer than k groups: every expert is a candidate
+    if (NG >= k) {
+      int c = 0;
+      for (int j = 0; j < NG; ++j) c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 2 * j)) > g;
+      const float q = (lane & 1) == 0 && (lane >> 1) < NG && c < k ? g : INFINITY;
+      tau = -bfly_max<6>(-q);
+    }
+    bool p[4];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = e0 + j < E && key[j] >= tau;
+      cnt += p[j];
+    }
+    const int incl = wave_incl_scan(cnt);
+    const int m = __builtin_amdgcn_readlane(incl, 63);
+    QS_LDS int* cd = L.cand + t * E;
+    int pos = incl - cnt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (p[j]) cd[pos++] = e0 + j;
+    // (the wave's own LDS writes are visible to its later reads)
+    const QS_LDS double* lg = L.lg + t * E;
+    for (int i0 = 0; i0 < m; i0 += 64) {
+      const int i = i0 + lane;
+      const int e = i < m ? cd[i] : 0;
+      const uint64_t K = f64_ord(nan_low(lg[e]));
+      int r = 0;
+      for (int j0 = 0; j0 < m; j0 += 64) {
+        uint64_t Kj = K;
+        if (j0 != i0) Kj = f64_ord(nan_low(lg[j0 + lane < m ? cd[j0 + lane] : 0]));
+        const int nj = m - j0 < 64 ? m - j0 : 64;
+        for (int j = 0; j < nj; ++j) {
+          const uint64_t K2 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(Kj >> 32), j) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)Kj, j);
+          r += (K2 > K || (K2 == K && j0 + j < i)) ? 1 : 0;
+        }
+      }
+      if (i < m && r < k) {
+        L.ids[t * k + r] = e;
+        L.sv[t * k + r] = f64_unord(K);
+      }
+    }
+    topk_weights(a, layer_i, t, L);
+  }
+  __syncthreads();
+}
+
+// Any E: keys and group maxima by (token, group) threads, the threshold with
+// an LDS minimum, then one wave per token ranks its candidates.
+template <class A>
+__device__ __forceinline__ void topk_small_lds(const A& a, int layer_i, PersistLds& L) {
   const int tid = qs_tid(), nt = kPersistThreads, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k, T = a.T, S = kf_stride(E), NG = S / 8, G4 = (NG + 3) & ~3;
   QS_LDS float* gm = L.kf + T * S;                 // [T][G4] group maxima, -inf padded
@@ -1103,20 +1212,7 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
         L.sv[t * k + r] = v;
       }
     }
-    // renormalised softmax over the picks: exponent of the fp64 difference
-    // to the top pick, in fp32
-    const double top0 = L.sv[t * k];
-    const float z = lane < k ? __expf((float)(L.sv[t * k + lane] - top0)) : 0.f;
-    const float sum = bfly_sum<6>(z);
-    if (lane < k) {
-      const float w = __fdividef(z, sum);
-      L.wl[t * k + lane] = w;
-      if (blockIdx.x == 0) {
-        const size_t o = (size_t)layer_i * T * k + t * k + lane;
-        if (a.ids_out) a.ids_out[o] = L.ids[t * k + lane];
-        if (a.w_out) a.w_out[o] = w;
-      }
-    }
+    topk_weights(a, layer_i, t, L);
   }
   __syncthreads();
 }

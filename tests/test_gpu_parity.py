@@ -223,6 +223,34 @@ def test_ties_break_to_lower_index(lib):
         assert np.array_equal(lg[:, 3], lg[:, 9]) and np.array_equal(lg[:, 3], lg[:, 12])
 
 
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_decode_ties_break_to_lower_index(lib, T):
+    """Three experts with exactly equal logits at the top of the routing set
+    (router row and bias copied), through the decode kernels of each batch
+    class: the tie goes to the lower expert index, as in the oracle's order."""
+    wl = workload("a3b_layer")
+    cb = synth.codebook()
+    lw = synth.layer_weights(wl, 0)
+    x1 = synth.tokens(wl, 1, 7)
+    top = int(np.argmax(om.router_logits(x1, lw.router, lw.router_bias)[0]))
+    lo, hi = (top + 97) % wl.n_experts, (top + 161) % wl.n_experts
+    for e in (lo, hi):
+        lw.router[e] = lw.router[top]
+        if lw.router_bias is not None:
+            lw.router_bias[e] = lw.router_bias[top]
+    x = np.repeat(x1, T, axis=0)
+    say(f"decode ties T={T}")
+    with lib.MoE.for_workload(wl, cb, max_tokens=16) as moe:
+        moe.upload(0, lw)
+        ids = torch.empty((T, wl.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, wl.top_k), dtype=torch.float32, device="cuda")
+        y = moe.decode(torch.from_numpy(x).cuda(), ids_out=ids, w_out=w)
+        torch.cuda.synchronize()
+        ids_np = ids.cpu().numpy()
+        assert np.array_equal(ids_np[:, :3], np.tile(sorted([top, lo, hi]), (T, 1)))
+        check_layer(wl, lw, x, y.cpu().numpy(), ids_np, w.cpu().numpy(), label=f"ties T={T}")
+
+
 def test_all_experts_selected(lib):
     """k = E: every expert is used by every token."""
     wl = synth.Workload("all", 41, 512, 4, 4, 256, 64, "cb2", "q2k", 1, (1,))
