@@ -1567,6 +1567,7 @@ __device__ __forceinline__ void routed_gu_tile(const A& a, lds_cptr tile, int u,
       }
     }
   }
+  // (also keeps the other waves' copies and reads behind this tile's stores)
   __syncthreads();
 }
 
@@ -1786,12 +1787,12 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
   if (qs_tid() == 0) *L.llerr = 0;
   if (FMT == 2) dma_to_lds<0>(a.cbtab, L.tab, (uint32_t)kCbTabWords * 4, wave, nw);
-  pf_router_and_shared<true>(a, a.layers[0], L, wave, nw);
+  LayerPtrs Lp = a.layers[0];
+  pf_router_and_shared<true>(a, Lp, L, wave, nw);
   if ((int)blockIdx.x * kDownRows < a.H)
-    copy_sd_rows(a, a.layers[0], L.pfb + down_base<true>(a), blockIdx.x * kDownRows, wave, nw);
+    copy_sd_rows(a, Lp, L.pfb + down_base<true>(a), blockIdx.x * kDownRows, wave, nw);
   wait_all_and_sync();
   for (int li = 0; li < a.n_layers; ++li) {
-    const LayerPtrs Lp = a.layers[li];
     const bool more = li + 1 < a.n_layers;
     const LayerPtrs Ln = a.layers[more ? li + 1 : li];   // requested now, used at the end of D
     // flags of this layer: fl = its input x, fl+1 logits, fl+2 SwiGLU, fl+3 its output
@@ -1835,6 +1836,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
             copy_sd_rows(a, Ln, L.pfb + down_base<true>(a), blockIdx.x * kDownRows, w, n);
         }))
       return;
+    Lp = Ln;
   }
 }
 
