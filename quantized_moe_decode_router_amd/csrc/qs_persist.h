@@ -868,12 +868,18 @@ template <class A>
 __device__ __forceinline__ size_t ll_ash(const A& a) { return ll_as(a) + 2 * (size_t)a.T * a.k * (a.F / kSubW); }
 template <class A>
 __device__ __forceinline__ int ll_a_words(const A& a) { return (int)(ll_ash(a) + (size_t)a.T * a.Fs); }
-// SMALL flow: waves [kCopyW0, 8) issue the copies that overlap a flagged
-// read, waves [0, kCopyW0) poll (when the words fit 32 per thread of them).
-constexpr int kCopyW0 = 4;
+// SMALL flow: waves [copy_w0, 8) issue the copies that overlap a flagged
+// read, waves [0, copy_w0) poll (when the words fit 32 per thread of them);
+// the gate/up tiles are copied by waves [tile_w0, 8) while waves
+// [0, tile_w0) quantise x.  (Measured choices; T is a compile-time constant
+// in the fixed-shape kernels.)
+template <class A>
+__device__ __forceinline__ int copy_w0(const A& a) { return a.T == 1 ? 7 : 6; }
+template <class A>
+__device__ __forceinline__ int tile_w0(const A& a) { return a.T == 1 ? 4 : 6; }
 template <class A>
 __device__ __forceinline__ int ll_waves(const A& a, int words) {
-  return words <= 32 * 64 * kCopyW0 ? kCopyW0 : kPersistThreads / 64;
+  return words <= 32 * 64 * copy_w0(a) ? copy_w0(a) : kPersistThreads / 64;
 }
 template <class A>
 __device__ __forceinline__ int ll_a_waves(const A& a) { return ll_waves(a, ll_a_words(a)); }
@@ -1752,8 +1758,8 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
       if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, base + (uint32_t)wave * a.Fs * 2, L);
     }
     __syncthreads();
-    // waves [0, kCopyW0) have the combine work (T * kDownRows <= 64 words)
-    if (tile + a.G >= n_tiles && wave >= kCopyW0) spare(wave - kCopyW0, kPersistThreads / 64 - kCopyW0);
+    // wave 0 has the combine work (T * kDownRows <= 64 words)
+    if (tile + a.G >= n_tiles && wave >= copy_w0(a)) spare(wave - copy_w0(a), kPersistThreads / 64 - copy_w0(a));
     for (int idx = qs_tid(); idx < T * kDownRows; idx += kPersistThreads) {
       const int t = idx / kDownRows, rr = idx % kDownRows, h = r0 + rr;
       float acc = 0.f;
@@ -1772,7 +1778,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
     }
     __syncthreads();     // L.o and L.sh are rewritten by the next tile
   }
-  if ((int)blockIdx.x >= n_tiles && wave >= kCopyW0) spare(wave - kCopyW0, kPersistThreads / 64 - kCopyW0);
+  if ((int)blockIdx.x >= n_tiles && wave >= copy_w0(a)) spare(wave - copy_w0(a), kPersistThreads / 64 - copy_w0(a));
   return true;
 }
 
@@ -1810,12 +1816,12 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     if (!ll_read(a, a.ll_lg, (QS_LDS uint32_t*)L.lg, 2 * a.T * a.E, fl + 1, L.llerr)) return;
     topk_small(a, li, L);
     group_small(a, L);
-    // tiles copied by waves [kCopyW0, 8) while the others quantise x
-    if (wave >= kCopyW0) pf_tiles<true>(a, Lp, L, wave - kCopyW0, nw - kCopyW0);
+    // tiles copied by waves [tile_w0, 8) while the others quantise x
+    if (wave >= tile_w0(a)) pf_tiles<true>(a, Lp, L, wave - tile_w0(a), nw - tile_w0(a));
     {
       const int nb = a.H / kBlockW;
-      if (wave < kCopyW0)
-        for (int u = wave; u < a.T * nb; u += kCopyW0) quant_x_wave<true>(a, a.x_in, u / nb, u % nb, L);
+      if (wave < tile_w0(a))
+        for (int u = wave; u < a.T * nb; u += tile_w0(a)) quant_x_wave<true>(a, a.x_in, u / nb, u % nb, L);
     }
     wait_all_and_sync();
     // ---- GU
@@ -1823,7 +1829,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     // region B (unused during GU) receives the down rows of the active
     // experts, from the waves that do not poll the SwiGLU words
     {
-      const int dw = ll_a_waves(a) == kCopyW0 ? kCopyW0 : 0;
+      const int dw = ll_a_waves(a) == copy_w0(a) ? copy_w0(a) : 0;
       if (wave >= dw) pf_down<true>(a, Lp, L, wave - dw, nw - dw);
     }
     // ---- D; region A is free: the next layer's router rows and shared
