@@ -302,14 +302,15 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   auto a16 = [](uint64_t v) { return (v + 15) & ~15ull; };
   bool fits;
   if (small) {
-    // region A: router rows + one shared item, then gate/up tiles (two when
-    // region B still holds eight experts' down rows, else one); region B:
-    // the shared down rows and at least one expert's
-    const uint64_t r_sh = a16(rb) + (Fs ? item : 0), b_min = a16(sd) + pe;
-    uint64_t A = a16(std::max(r_sh, 2 * tile));
-    if (A + a16(sd) + 8 * pe > p.pfb) A = a16(std::max(r_sh, tile));
+    // region A: router rows + one shared item (phase R); regions A and B:
+    // gate/up tiles (K, GU); region B and the x limbs after it: experts'
+    // down rows (D).  The shared down rows have their own slot.
+    const uint64_t r_sh = a16(rb) + (Fs ? item : 0);
+    const uint64_t xl = 2 * a16((uint64_t)T * H) + 2 * a16((uint64_t)T * H / 4);
+    const uint64_t A = a16(r_sh);
     p.pfa = (uint32_t)A;
-    fits = A + b_min <= p.pfb;
+    fits = A <= p.pfb && tile <= p.pfb && (p.pfb - A) + xl >= pe;
+    (void)sd;
     // each flagged read is at most 32 words per thread
     const uint64_t P = (uint64_t)T * c.top_k;
     const uint64_t wa = 2 * P * (F / 4) + 2 * P * (F / 16) + (uint64_t)T * Fs;

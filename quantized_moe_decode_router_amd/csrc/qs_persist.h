@@ -340,7 +340,7 @@ __host__ __device__ inline uint32_t abuf_bytes(int T, int H, int E, int P, int F
 
 struct LdsLayout {
   uint32_t tab, cnt, off, act, aoff, nact, llerr, mask, ids, pairs, tok_order, cw, pos_of, wl, o, red, sh, ga, sred,
-      qtmp, rinv, kf, cand, ncand, sv, xh, xl, xs, xa, abuf, pfb, end;
+      qtmp, rinv, kf, cand, ncand, sv, xh, xl, xs, xa, abuf, pfb, sdr, end;
 };
 
 __host__ __device__ inline int kf_stride(int E) { return (E + 7) & ~7; }
@@ -376,18 +376,22 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.qtmp = take((uint32_t)T * kGateTile * 4);
   l.rinv = take((uint32_t)T * 8);
   // SMALL top-k: keys [T][S], group maxima [T][S/8], thresholds [T]
-  l.kf = take(small ? (uint32_t)T * kf_stride(E) * 4 + (uint32_t)T * (((kf_stride(E) / 8) + 3) & ~3) * 4 +
-                          (uint32_t)T * 4 : 0);
+  l.kf = take(small && E > 256 ? (uint32_t)T * kf_stride(E) * 4 + (uint32_t)T * (((kf_stride(E) / 8) + 3) & ~3) * 4 +
+                                     (uint32_t)T * 4 : 0);
   l.cand = take(small ? (uint32_t)T * E * 4 : 0);
   l.ncand = take(small ? (uint32_t)T * 4 : 0);
   l.sv = take(small ? (uint32_t)P * 8 : 0);
+  l.abuf = take(small ? abuf_bytes(T, H, E, P, F, Fs) : 0);
+  l.pfb = take(pfb);
+  // SMALL: the x limbs follow the staging buffer, so that once the gate/up
+  // tiles are done the down rows can spill over them; the shared down rows
+  // (copied a layer ahead) have their own slot.
   const uint32_t xq = small ? (uint32_t)T * H : 0;
   l.xh = take(xq);          // T*H/4 dwords
   l.xl = take(xq);
   l.xs = take(xq / 4);      // T*H/16 floats
   l.xa = take(xq / 4);
-  l.abuf = take(small ? abuf_bytes(T, H, E, P, F, Fs) : 0);
-  l.pfb = take(pfb);
+  l.sdr = take(small ? (uint32_t)kDownRows * Fs * 2 : 0);
   l.end = o;
   return l;
 }
@@ -423,6 +427,7 @@ struct PersistLds {
   QS_LDS float* xs;       // [T*H/16]
   QS_LDS int* xa;
   QS_LDS uint8_t* pfb;    // weight staging buffer
+  QS_LDS uint8_t* sdr;    // SMALL: shared-expert down rows of this workgroup's output rows
   // SMALL views into the activation buffer
   QS_LDS float* ax;       // [T][H] x
   QS_LDS double* lg;      // [T][E] logits
@@ -469,6 +474,7 @@ __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const A& a, bool c
   L.xs = (QS_LDS float*)(b + l.xs);
   L.xa = (QS_LDS int*)(b + l.xa);
   L.pfb = b + l.pfb;
+  L.sdr = b + l.sdr;
   QS_LDS uint8_t* ab = b + l.abuf;
   L.ax = (QS_LDS float*)ab;
   L.lg = (QS_LDS double*)(ab + al16(T * H * 4));
@@ -542,7 +548,7 @@ __device__ __forceinline__ uint32_t tile_off(const A& a) {
 }
 template <bool SMALL, class A>
 __device__ __forceinline__ int tile_pf_count(const A& a, int na) {
-  const uint32_t off = tile_off<SMALL>(a), end = SMALL ? a.pfa : a.pfb;
+  const uint32_t off = tile_off<SMALL>(a), end = a.pfb;   // SMALL: regions A and B
   const int fit = end > off ? (int)((end - off) / gu_tile_bytes(a)) : 0;
   const int base = gu_items_base<SMALL>(a);
   const int mine = my_count(a, base + na * (a.F / kGateTile)) - my_count(a, base);
@@ -554,10 +560,18 @@ __device__ __forceinline__ int tile_pf_count(const A& a, int na) {
 // the barrier before D)
 template <bool SMALL, class A>
 __device__ __forceinline__ uint32_t down_base(const A& a) { return SMALL ? a.pfa : 0; }
+// SMALL: bytes of the x limbs, which follow the staging buffer
+template <class A>
+__device__ __forceinline__ uint32_t xlimb_bytes(const A& a) {
+  return 2 * al16((uint32_t)a.T * a.H) + 2 * al16((uint32_t)a.T * a.H / 4);
+}
 template <bool SMALL, class A>
 __device__ __forceinline__ int down_chunk(const A& a) {
-  const uint32_t fixed = down_base<SMALL>(a) + al16(sd_bytes(a));
-  return a.pfb > fixed ? (int)((a.pfb - fixed) / dn_expert_bytes(a)) : 0;
+  // SMALL: region B and the x limbs (free once the gate/up tiles are done);
+  // the shared down rows have their own slot.  Otherwise after the shared rows.
+  const uint32_t fixed = SMALL ? down_base<SMALL>(a) : al16(sd_bytes(a));
+  const uint32_t end = SMALL ? a.pfb + xlimb_bytes(a) : a.pfb;
+  return end > fixed ? (int)((end - fixed) / dn_expert_bytes(a)) : 0;
 }
 template <bool SMALL, class A>
 __device__ __forceinline__ int down_pf_count(const A& a, int na) {
@@ -694,12 +708,12 @@ __device__ __forceinline__ void pf_down(const A& a, const LayerPtrs& Lp, Persist
   if (r0 >= a.H) return;
   QS_LDS uint8_t* base = L.pfb + down_base<SMALL>(a);
   const int n = down_pf_count<SMALL>(a, *L.nact);
-  if (!SMALL) copy_sd_rows(a, Lp, base, r0, w, nw);   // SMALL: copied ahead with the layer's router rows
+  if (!SMALL) copy_sd_rows(a, Lp, base, r0, w, nw);   // SMALL: in L.sdr, copied a layer ahead
   for (int u0 = 0; u0 < n; u0 += 64) {
     const int el = act_lanes(L, u0, n);
     const int m = n - u0 < 64 ? n - u0 : 64;
     for (int i = 0; i < m; ++i)
-      copy_down_rows(a, Lp, base + al16(sd_bytes(a)) + (uint32_t)(u0 + i) * dn_expert_bytes(a),
+      copy_down_rows(a, Lp, base + (SMALL ? 0u : al16(sd_bytes(a))) + (uint32_t)(u0 + i) * dn_expert_bytes(a),
                      __builtin_amdgcn_readlane(el, i), r0, w, nw);
   }
 }
@@ -1724,8 +1738,8 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
   const int n_tiles = a.H / kDownRows;
   const int T = a.T;
   const int chunk = down_chunk<true>(a);
-  const uint32_t pe = dn_expert_bytes(a), sdb = al16(sd_bytes(a));
-  QS_LDS uint8_t* base = L.pfb + down_base<true>(a);
+  const uint32_t pe = dn_expert_bytes(a);
+  QS_LDS uint8_t* base = L.pfb + down_base<true>(a);   // experts' rows; the shared rows are in L.sdr
   // residual inputs of the first tile, requested before the waits
   float xres = 0.f;
   const bool own_res = a.residual && qs_tid() < T * kDownRows && (int)blockIdx.x < n_tiles;
@@ -1745,17 +1759,17 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
       const int u1 = na - u0 < chunk ? na : u0 + chunk;
       if (!first || u0 > 0) {
         stage_now([&](int w, int n) {
-          if (u0 == 0) copy_sd_rows(a, Lp, base, r0, w, n);
+          if (u0 == 0) copy_sd_rows(a, Lp, L.sdr, r0, w, n);
           for (int c0 = u0; c0 < u1; c0 += 64) {
             const int el = act_lanes(L, c0, u1);
             const int m = u1 - c0 < 64 ? u1 - c0 : 64;
             for (int i = 0; i < m; ++i)
-              copy_down_rows(a, Lp, base + sdb + (uint32_t)(c0 + i - u0) * pe, __builtin_amdgcn_readlane(el, i), r0, w, n);
+              copy_down_rows(a, Lp, base + (uint32_t)(c0 + i - u0) * pe, __builtin_amdgcn_readlane(el, i), r0, w, n);
           }
         });
       }
-      for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, base + sdb + (uint32_t)(u - u0) * pe, u, L);
-      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, base + (uint32_t)wave * a.Fs * 2, L);
+      for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, base + (uint32_t)(u - u0) * pe, u, L);
+      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, L.sdr + (uint32_t)wave * a.Fs * 2, L);
     }
     __syncthreads();
     // wave 0 has the combine work (T * kDownRows <= 64 words)
@@ -1796,7 +1810,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
   LayerPtrs Lp = a.layers[0];
   pf_router_and_shared<true>(a, Lp, L, wave, nw);
   if ((int)blockIdx.x * kDownRows < a.H)
-    copy_sd_rows(a, Lp, L.pfb + down_base<true>(a), blockIdx.x * kDownRows, wave, nw);
+    copy_sd_rows(a, Lp, L.sdr, blockIdx.x * kDownRows, wave, nw);
   wait_all_and_sync();
   for (int li = 0; li < a.n_layers; ++li) {
     const bool more = li + 1 < a.n_layers;
@@ -1839,7 +1853,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
           pf_router_and_shared<true>(a, Ln, L, w, n);
           // the shared down rows are no longer read by this layer
           if ((int)blockIdx.x * kDownRows < a.H)
-            copy_sd_rows(a, Ln, L.pfb + down_base<true>(a), blockIdx.x * kDownRows, w, n);
+            copy_sd_rows(a, Ln, L.sdr, blockIdx.x * kDownRows, w, n);
         }))
       return;
     Lp = Ln;
