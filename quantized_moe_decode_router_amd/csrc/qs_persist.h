@@ -1074,6 +1074,29 @@ __device__ __forceinline__ void topk_weights(const A& a, int layer_i, int t, Per
   }
 }
 
+// T = 1, in the wave that ranked the token: the grouping of its k distinct
+// experts (what group_small gives for one token): position u of a pair is the
+// rank of its expert among the k, each bucket holds one pair.
+template <class A>
+__device__ __forceinline__ void group_one_token(const A& a, PersistLds& L) {
+  const int lane = qs_tid() & 63, k = a.k;
+  const bool live = lane < k;
+  const int e = live ? L.ids[lane] : 0x7FFFFFFF;
+  int u = 0;
+  for (int q = 0; q < k; ++q) u += __builtin_amdgcn_readlane(e, q) < e ? 1 : 0;
+  if (live) {
+    L.act[u] = e;
+    L.aoff[u] = u;
+    L.pairs[u] = lane;
+    L.tok_order[u] = u;
+    L.cw[u] = L.wl[lane];
+  }
+  if (lane == 0) {
+    *L.nact = k;
+    L.aoff[k] = k;
+  }
+}
+
 // E <= 256: one wave per token, no block barrier before the last.  Lane l
 // holds experts 4l..4l+3; a lane pair is a group of 8.  The k-th largest
 // group maximum is found with one broadcast per group, the candidates are
@@ -1147,6 +1170,7 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
       }
     }
     topk_weights(a, layer_i, t, L);
+    if (T == 1) group_one_token(a, L);
   }
   __syncthreads();
 }
@@ -1233,6 +1257,7 @@ __device__ __forceinline__ void topk_small_lds(const A& a, int layer_i, PersistL
       }
     }
     topk_weights(a, layer_i, t, L);
+    if (T == 1) group_one_token(a, L);
   }
   __syncthreads();
 }
@@ -1828,8 +1853,8 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     shared_items<true>(a, Lp, a.x_in, L, fl + 2);
     // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
     if (!ll_read(a, a.ll_lg, (QS_LDS uint32_t*)L.lg, 2 * a.T * a.E, fl + 1, L.llerr)) return;
-    topk_small(a, li, L);
-    group_small(a, L);
+    topk_small(a, li, L);   // (groups one token itself)
+    if (a.T > 1) group_small(a, L);
     // tiles copied by waves [tile_w0, 8) while the others quantise x
     if (wave >= tile_w0(a)) pf_tiles<true>(a, Lp, L, wave - tile_w0(a), nw - tile_w0(a));
     {
