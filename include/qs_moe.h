@@ -107,7 +107,11 @@ typedef struct {
   int32_t max_tokens;      /* largest n_tokens of a decode call: 1..256, and
                               max_tokens * top_k <= 1024 */
   int32_t mfma_min_tokens; /* expert bucket size at which the matrix-core path
-                              replaces the GEMV path; 0 = library default */
+                              replaces the GEMV path; a batch that could reach
+                              it takes the batched kernel.  0 = library
+                              default: batches of up to 4 tokens take the
+                              small-batch kernel (GEMV), larger batches send
+                              every bucket through the matrix cores */
   int32_t device;          /* HIP device ordinal; -1 = the current device */
 } qs_moe_config;
 
