@@ -110,8 +110,9 @@ typedef struct {
                               replaces the GEMV path; a batch that could reach
                               it takes the batched kernel.  0 = library
                               default: batches of up to 4 tokens take the
-                              small-batch kernel (GEMV), larger batches send
-                              every bucket through the matrix cores */
+                              small-batch kernel (GEMV) where it fits; in the
+                              batched kernel every bucket goes through the
+                              matrix cores, except in one-token batches */
   int32_t device;          /* HIP device ordinal; -1 = the current device */
 } qs_moe_config;
 

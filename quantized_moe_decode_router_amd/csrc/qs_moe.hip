@@ -518,7 +518,9 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   a.xh = s.xh; a.xl = s.xl; a.xs = s.xs; a.xa = s.xa;
   a.ah = s.ah; a.al = s.al; a.as = s.as; a.aa = s.aa; a.ash = s.ash;
   a.xbuf0 = s.xbuf[0]; a.xbuf1 = s.xbuf[1];
-  a.mfma_min = h->mfma_min;
+  // default threshold: one-token buckets of a one-token batch stay on the
+  // GEMV items (measured faster there: Flash stack T = 1, 1680 vs 1274 tok/s)
+  a.mfma_min = !h->mfma_explicit && T == 1 ? 2 : h->mfma_min;
   a.ll_lg = s.ll_lg; a.ll_a = s.ll_a; a.llx0 = s.llx[0]; a.llx1 = s.llx[1];
   a.ll_epoch = h->ll_epoch;
   a.af = s.af; a.ob = s.ob; a.sb = s.sb;
@@ -645,8 +647,8 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   if (!h) return QS_E_NOMEM;
   h->cfg = *cfg;
   // default: the small-batch kernel (GEMV only) up to kSmallT tokens, the
-  // matrix cores for every bucket above (measured faster at every bucket size
-  // in the batched kernel: T = 16 +39 %, T = 32 +32 % over a threshold of 16)
+  // matrix cores for every bucket of a larger batch in the batched kernel
+  // (measured: T = 16 +39 %, T = 32 +32 % over a threshold of 16)
   h->mfma_explicit = cfg->mfma_min_tokens != 0;
   h->mfma_min = cfg->mfma_min_tokens ? cfg->mfma_min_tokens : 1;
   DeviceGuard dg(cfg->device);
