@@ -261,6 +261,18 @@ def test_decode_ties_break_to_lower_index(lib, T):
         check_layer(wl, lw, x, y.cpu().numpy(), ids_np, w.cpu().numpy(), label=f"ties T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_many_experts(lib, T):
+    """E = 512 (> 256): the small-batch kernel's general top-k (keys and group
+    maxima by (token, group) threads, an LDS threshold) instead of the
+    register one."""
+    wl = synth.Workload("e512", 43, 512, 512, 6, 256, 64, "cb2", "q2k", 1, (1,))
+    say(f"E = 512 T={T}")
+    moe, lws = make_handle(lib, wl, max_tokens=4)
+    with moe:
+        _decode_check(wl, moe, lws[0], T, label=f"E=512 T={T}")
+
+
 def test_all_experts_selected(lib):
     """k = E: every expert is used by every token."""
     wl = synth.Workload("all", 41, 512, 4, 4, 256, 64, "cb2", "q2k", 1, (1,))
