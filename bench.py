@@ -108,8 +108,8 @@ def copy_calibration(mib: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this build runs "
-              "and is measured on a single MI355X (the design notes say how it would shard)")
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the decode step "
+              "runs and is measured on a single MI355X (the design notes say how it would shard)")
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
