@@ -42,7 +42,8 @@ namespace qs {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaRows = 128;     // rows of an MFMA item (8 waves x 16)
+constexpr int kMfmaRows = 128;     // rows of a down MFMA item (8 waves x 16)
+constexpr int kMguRows = 64;       // rows of a gate/up MFMA item (4 row groups x 16, two waves each)
 constexpr int kMfmaTok = 16;       // tokens per MFMA column tile
 constexpr int kDnRows = 64;        // rows of a GEMV down item (8 waves x kDownRows)
 constexpr int kXgMax = 16;         // tokens staged per GEMV gate/up pass
@@ -216,7 +217,7 @@ __device__ __forceinline__ int gu_gemv_cost(const A& a, int n) {
 }
 template <class A>
 __device__ __forceinline__ int gu_mfma_cost(const A& a, int n) {
-  const int w = (int)(big_tile_b(a.H, a.gq2k != 0) >> 8) * (kMfmaRows / kGateTile);
+  const int w = (int)(big_tile_b(a.H, a.gq2k != 0) >> 8) * (kMguRows / kGateTile);
   const int ng = (n + kMfmaTok - 1) / kMfmaTok;
   return w + ng * (kStageCost + 16 * (a.H / kBlockW));
 }
@@ -237,7 +238,7 @@ template <class A>
 __device__ __forceinline__ void gu_items_of(const A& a, const PersistLds& L, int u, int& m, int& c) {
   const int n = L.aoff[u + 1] - L.aoff[u];
   if (n >= a.mfma_min) {
-    m = a.F / kMfmaRows;
+    m = a.F / kMguRows;
     c = gu_mfma_cost(a, n);
   } else {
     m = a.F / kGateTile;
@@ -773,11 +774,14 @@ __device__ __forceinline__ void gu_mfma_item(const A& a, const LayerPtrs& Lp, Bi
   PersistLds& P = L.P;
   const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0, e = P.act[u];
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63, r = lane & 15, g = lane >> 4;
+  // waves w and w+4 take row group w&3; wave w>>2 == 0 the even blocks of
+  // each staged slice, == 1 the odd ones (their sums are added at the end)
+  const int rg = wave & 3, kh = wave >> 2;
   const int H = a.H, nbh = H / kBlockW;
   const MatPlanes pl = q2k ? q2k_planes((size_t)a.F * nbh) : cb2_planes((size_t)a.F * nbh);
   const uint8_t* gm = Lp.gate + (size_t)e * a.gu_stride;
   const uint8_t* um = Lp.up + (size_t)e * a.gu_stride;
-  const int arow = f0 + 16 * wave + r, drow0 = f0 + 16 * wave + 4 * g;
+  const int arow = f0 + 16 * rg + r, drow0 = f0 + 16 * rg + 4 * g;
   const MguStage st = mgu_stage(P.pfb + big_gu_area(H, a.Fs), pp.kbg);
 #pragma unroll 1
   for (int g0 = 0; g0 < n; g0 += kMfmaTok) {
@@ -788,9 +792,11 @@ __device__ __forceinline__ void gu_mfma_item(const A& a, const LayerPtrs& Lp, Bi
       const int kb = nbh - k0 < pp.kbg ? nbh - k0 : pp.kbg;
       // slots beyond the bucket repeat its last token (their columns are dropped)
       auto tok = [&](int i) { return P.pairs[q0 + g0 + (i < ng ? i : ng - 1)] / a.k; };
-      // the slice's first weights are requested before the wait for the tokens
-      GuFrag fg = load_gu_frag<FMT>(gm, pl, nbh, arow, drow0, k0, g);
-      GuFrag fu = load_gu_frag<FMT>(um, pl, nbh, arow, drow0, k0, g);
+      // this wave's first block of the slice is requested before the wait
+      // for the tokens
+      const int kf = kh < kb ? k0 + kh : k0;
+      GuFrag fg = load_gu_frag<FMT>(gm, pl, nbh, arow, drow0, kf, g);
+      GuFrag fu = load_gu_frag<FMT>(um, pl, nbh, arow, drow0, kf, g);
       stage_now([&](int w, int nw) {
         dma_rows<kCoherent>([&](int i) { return (const uint8_t*)(a.xh + (size_t)tok(i) * (H / 4)) + k0 * kBlockW; },
                             st.xh, st.stride, (uint32_t)kb * kBlockW, kMfmaTok, w, nw);
@@ -801,11 +807,11 @@ __device__ __forceinline__ void gu_mfma_item(const A& a, const LayerPtrs& Lp, Bi
             (QS_LDS uint8_t*)st.xs, (uint32_t)pp.kbg * 64, (uint32_t)kb * 64, kMfmaTok, w, nw);
       });
 #pragma unroll 1
-      for (int b = 0; b < kb; ++b) {
+      for (int b = kh; b < kb; b += 2) {
         GuFrag ng_ = fg, nu_ = fu;
-        if (b + 1 < kb) {
-          ng_ = load_gu_frag<FMT>(gm, pl, nbh, arow, drow0, k0 + b + 1, g);
-          nu_ = load_gu_frag<FMT>(um, pl, nbh, arow, drow0, k0 + b + 1, g);
+        if (b + 2 < kb) {
+          ng_ = load_gu_frag<FMT>(gm, pl, nbh, arow, drow0, k0 + b + 2, g);
+          nu_ = load_gu_frag<FMT>(um, pl, nbh, arow, drow0, k0 + b + 2, g);
         }
         v4i ihg = {0, 0, 0, 0}, ilg = ihg, ihu = ihg, ilu = ihg;
         v4i mhg = ihg, mlg = ihg, mhu = ihg, mlu = ihg;   // Q2_K min terms
@@ -852,11 +858,23 @@ __device__ __forceinline__ void gu_mfma_item(const A& a, const LayerPtrs& Lp, Bi
         fu = nu_;
       }
     }
-    if (r < ng) {
+    // the odd blocks' sums join the even ones' through the staging area
+    // (8 KiB <= its two token tiles; every wave is done with them first)
+    __syncthreads();
+    QS_LDS float* part = (QS_LDS float*)st.xh + (rg * 64 + lane) * 8;
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part[i] = ag[i];
+        part[4 + i] = au[i];
+      }
+    }
+    __syncthreads();
+    if (kh == 0 && r < ng) {
       const int pair = P.pairs[q0 + g0 + r];
       float* o = a.af + (size_t)pair * a.F + drow0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) cstf(o + i, silu_mul(ag[i], au[i]));
+      for (int i = 0; i < 4; ++i) cstf(o + i, silu_mul(ag[i] + part[i], au[i] + part[4 + i]));
     }
   }
   __syncthreads();   // every wave is done with the staged tiles
@@ -935,7 +953,7 @@ __device__ __forceinline__ void big_gu_phase(const A& a, const LayerPtrs& Lp, co
         continue;
       }
       if (end) break;
-      if (mf) gu_mfma_item<FMT>(a, Lp, L, pp, u, j * kMfmaRows);
+      if (mf) gu_mfma_item<FMT>(a, Lp, L, pp, u, j * kMguRows);
       else gu_gemv_item<FMT>(a, Lp, L, pp, u, j * kGateTile, false, false);
       ++j;
       continue;
