@@ -132,8 +132,9 @@ def dequant_matrix(raw: np.ndarray, fmt: str, codebook=None) -> np.ndarray:
 
 
 def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
-    """logit[t][e] = sum_h Wr[e][h] * x[t][h] + b[e], in fp64.  Each product
-    of two fp32 values is exact in fp64."""
+    """logit[t][e] = sum_h Wr[e][h] * x[t][h] + b[e], in fp64.  For fp32 x
+    each product of two fp32 values is exact in fp64; x may also be an fp64
+    vector (the pre-normalised input)."""
     lg = np.asarray(x, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64).T
     if bias is not None:
         lg = lg + np.asarray(bias, dtype=np.float64)[None, :]
@@ -258,15 +259,12 @@ def moe_layer(layer: Layer, x: np.ndarray, residual: bool = False, prenorm: bool
     wl, lw = layer.wl, layer.lw
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
+    # the normalised input u is formed first and everything (router and
+    # experts) is evaluated on it, as the definition reads
+    u = x.astype(np.float64)
     if prenorm:
-        r = rms_inv(x)
-        logits = router_logits(x, lw.router) * r[:, None]
-        if lw.router_bias is not None:
-            logits = logits + np.asarray(lw.router_bias, dtype=np.float64)[None, :]
-        u = x.astype(np.float64) * r[:, None]
-    else:
-        logits = router_logits(x, lw.router, lw.router_bias)
-        u = x.astype(np.float64)
+        u = u * rms_inv(x)[:, None]
+    logits = router_logits(u, lw.router, lw.router_bias)
     ids, wts, gap = top_k(logits, wl.top_k)
     y = np.zeros((T, wl.hidden), dtype=np.float64)
     for t in range(T):

@@ -292,3 +292,34 @@ def test_codebook_entries():
     cb = synth_codebook()
     assert cb.shape == (256, 8) and cb.dtype == np.int8
     assert set(np.unique(cb)) == {1, 3, 5, 7}
+
+
+# ------------------------------------------------- matrix block order ---
+
+def _fp16_bits(v):
+    return int(np.array([v], dtype=np.float16).view(np.uint16)[0])
+
+
+@pytest.mark.parametrize("fmt", ["q2k", "cb2"])
+def test_dequant_matrix_block_order(fmt):
+    """A matrix is [rows][cols/256] blocks, row-major: block (r, b) holds
+    columns 256*b .. 256*b+255 of row r.  Every block here decodes to the
+    constant r*nb + b + 1 (its d, with unit scale and code), so a transposed
+    or shuffled block order shows up as a wrong constant."""
+    rows, nb = 3, 4
+    raw = []
+    for r in range(rows):
+        row = []
+        for b in range(nb):
+            d = _fp16_bits(float(r * nb + b + 1))
+            if fmt == "q2k":   # w = d*1*1 - 0*0
+                row.append(pack_q2k(d=d, sc=np.ones(16, int), q=np.ones(256, int)))
+            else:              # w = d*1*C[0][j%8] with an all-ones codebook row 0
+                row.append(pack_cb2(d=d, s=np.ones(8, int)))
+        raw.append(row)
+    raw = np.array(raw, dtype=np.uint8)
+    w = om.dequant_matrix(raw, fmt, hand_codebook())
+    assert w.shape == (rows, nb * 256)
+    for r in range(rows):
+        for b in range(nb):
+            assert np.all(w[r, 256 * b:256 * (b + 1)] == np.float32(r * nb + b + 1)), (r, b)

@@ -179,3 +179,27 @@ def test_generator_is_deterministic_and_keyed():
     c = synth.layer_weights(wl, 1)
     assert not np.array_equal(a.gate, c.gate)
     assert np.array_equal(synth.tokens(wl, 4, 2), synth.tokens(wl, 4, 2))
+
+
+def test_rel_l2_hand_worked():
+    """Per row ||got - ref|| / ||ref||, worked by hand: (3,4)->(3,9) differs by
+    (0,5), |ref| = 5 -> 1.0; (1,0,0)->(3,2,1) differs by (2,2,1), |.| = 3,
+    |ref| = 1 -> 3.0; a zero reference row divides by 1 (|got| = 1 -> 1.0);
+    an exact match gives 0."""
+    got = om.rel_l2(np.array([[3.0, 9.0, 0.0], [3.0, 2.0, 1.0], [0.6, 0.8, 0.0], [1.5, -2.0, 0.25]]),
+                    np.array([[3.0, 4.0, 0.0], [1.0, 0.0, 0.0], [0.0, 0.0, 0.0], [1.5, -2.0, 0.25]]))
+    assert got.tolist() == [1.0, 3.0, 1.0, 0.0]
+    assert om.rel_l2(np.array([2.0, 0.0]), np.array([1.0, 0.0])) == 1.0    # one row
+
+
+def test_prenorm_logits_are_the_router_on_the_normalised_input():
+    """With the pre-norm the router sees RMSNorm(x): torch's rms_norm (no
+    weight) followed by a torch fp64 matmul and the bias gives the logits."""
+    wl = _tiny("cb2", 0, zipf=1.1)
+    lw = synth.layer_weights(wl, 0)
+    x = synth.tokens(wl, 4) * 3
+    r = om.moe_layer(om.Layer(wl, lw, synth.codebook()), x, prenorm=True)
+    u = torch.nn.functional.rms_norm(torch.from_numpy(x.astype(np.float64)), (wl.hidden,), eps=om.RMS_EPS)
+    ref = u @ torch.from_numpy(lw.router.astype(np.float64)).T + torch.from_numpy(
+        lw.router_bias.astype(np.float64))
+    assert np.allclose(r["logits"], ref.numpy(), rtol=1e-13, atol=1e-13)
