@@ -46,13 +46,21 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="a3b_stack40_zipf")
     p.add_argument("--tokens", default="1,4,16", help="batch sizes; the first is the headline")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the other HBM-target workloads (routed-only stack, large-layer stack)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=40, help="layers in the oracle sample")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
-    p.add_argument("--multikernel", action="store_true", help="time the one-kernel-per-step path")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of this many MiB, 20 times")
     return p.parse_args()
+
+
+# The other workloads the bench line reports beside the headline one: the
+# routed-only 40-layer stack and the 8-layer large-layer stack, at their
+# batch sizes, with fewer timed steps.
+EXTRA = (("a3b_routed40", (1, 4)), ("flash_stack8_zipf", (1, 8, 32)))
+EXTRA_STEPS = 100
 
 
 def log(*a):
@@ -105,6 +113,92 @@ def copy_calibration(mib: int):
                                            "launches": 20}}), flush=True)
 
 
+def kernel_name(wl, T):
+    fmt = "cb2" if wl.gate_up_format == "cb2" else "q2k"
+    small = T <= 4 and wl.hidden <= 2048
+    return ("k_persist_small" if small else "k_persist_big") + f"<{fmt}> (one launch = the whole decode call)"
+
+
+def run_workload(qm, wl, L, tok_list, steps, warmup):
+    """Time `steps` decode calls through all L layers at each batch size;
+    returns {T: figures}."""
+    import torch
+    import synth
+    cb = synth.codebook()
+    log(f"[bench] workload {wl.name}: {L} layers, H={wl.hidden} E={wl.n_experts} k={wl.top_k} "
+        f"F={wl.expert_ffn} Fs={wl.shared_ffn}, tokens {list(tok_list)}")
+    t0 = time.time()
+    moe = qm.MoE.for_workload(wl, cb, n_layers=L, max_tokens=max(tok_list))
+    for l in range(L):
+        moe.upload(l, synth.layer_weights(wl, l))
+        if l % 10 == 9 or l == L - 1:
+            log(f"[bench] uploaded {l + 1}/{L} layers ({time.time() - t0:.1f}s)")
+    g, u, d = wl.expert_bytes()
+    per_expert = g + u + d
+    fixed_layer = wl.router_bytes() + wl.shared_bytes()
+    # decode() launches on torch's current stream; every event below is
+    # recorded on that same stream
+    stream = torch.cuda.current_stream()
+
+    def step(x, y, ids=None):
+        moe.decode(x, y, n_layers=L, residual=True, prenorm=True, ids_out=ids, stream=stream)
+
+    results = {}
+    for T in tok_list:
+        xs = torch.from_numpy(np.stack([synth.tokens(wl, T, b) for b in range(N_BATCHES)])).cuda()
+        y = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
+        ids = torch.empty((N_BATCHES, L, T, wl.top_k), dtype=torch.int32, device="cuda")
+        # untimed pass: the experts each batch selects, for the byte count
+        for b in range(N_BATCHES):
+            step(xs[b], y, ids[b])
+        moe.sync_status(stream)
+        idn = ids.cpu().numpy()
+        uniq = np.array([[len(np.unique(idn[b, l])) for l in range(L)] for b in range(N_BATCHES)])
+        bytes_batch = uniq.sum(axis=1) * per_expert + L * fixed_layer + 2 * T * wl.hidden * 4
+        for i in range(warmup):
+            step(xs[i % N_BATCHES], y)
+        torch.cuda.synchronize()
+        # whole timed region: K steps back to back
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            step(xs[i % N_BATCHES], y)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        # per launch: an event pair around each decode call (one kernel
+        # launch), same stream, same inputs
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            step(xs[i % N_BATCHES], y)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        moe.sync_status(stream)          # no timed call gave up a wait
+        launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+        step_bytes = float(np.mean([bytes_batch[i % N_BATCHES] for i in range(steps)]))
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        achieved = step_bytes / (launch_ms.mean() * 1e-3) / 1e9
+        results[T] = {
+            "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms, "bytes_per_step": step_bytes,
+            "weight_read_GBps": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+            "mean_distinct_experts_per_layer": float(uniq.mean()),
+            "launch_ms_mean": float(launch_ms.mean()), "launch_ms_p10": float(np.percentile(launch_ms, 10)),
+            "launch_ms_p90": float(np.percentile(launch_ms, 90)),
+            "roofline": {"bound": "hbm", "kernel": kernel_name(wl, T), "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS},
+        }
+        log(f"[bench] {wl.name} T={T}: {ms:.3f} ms/step, {T / (ms * 1e-3):.1f} tok/s, {gbs:.1f} GB/s "
+            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), U={uniq.mean():.1f}, "
+            f"launch {launch_ms.mean():.3f} ms (p10 {np.percentile(launch_ms, 10):.3f}, "
+            f"p90 {np.percentile(launch_ms, 90):.3f})")
+        del xs, ids
+    moe.close()
+    return results
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,91 +213,29 @@ def main():
     import quantized_moe_decode_router_amd as qm
     import synth
 
+    torch.cuda.init()
     wl = synth.WORKLOADS[args.workload]
     L = args.layers or wl.n_layers
     tok_list = [int(t) for t in args.tokens.split(",")]
-    maxT = max(tok_list)
-    cb = synth.codebook()
-    torch.cuda.init()
-    log(f"[bench] workload {wl.name}: {L} layers, H={wl.hidden} E={wl.n_experts} k={wl.top_k} "
-        f"F={wl.expert_ffn} Fs={wl.shared_ffn}, tokens {tok_list}")
-    t0 = time.time()
-    moe = qm.MoE.for_workload(wl, cb, n_layers=L, max_tokens=maxT)
-    for l in range(L):
-        moe.upload(l, synth.layer_weights(wl, l))
-        if l % 10 == 9 or l == L - 1:
-            log(f"[bench] uploaded {l + 1}/{L} layers ({time.time() - t0:.1f}s)")
-    g, u, d = wl.expert_bytes()
-    per_expert = g + u + d
-    fixed_layer = wl.router_bytes() + wl.shared_bytes()
-    # decode() launches on torch's current stream; every event below is
-    # recorded on that same stream
-    stream = torch.cuda.current_stream()
-
-    def step(x, y, ids=None):
-        moe.decode(x, y, n_layers=L, residual=True, prenorm=True, ids_out=ids,
-                   path="multikernel" if args.multikernel else "persistent", stream=stream)
-
-    results = {}
-    for T in tok_list:
-        xs = torch.from_numpy(np.stack([synth.tokens(wl, T, b) for b in range(N_BATCHES)])).cuda()
-        y = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
-        ids = torch.empty((N_BATCHES, L, T, wl.top_k), dtype=torch.int32, device="cuda")
-        # untimed pass: the experts each batch selects, for the byte count
-        for b in range(N_BATCHES):
-            step(xs[b], y, ids[b])
-        torch.cuda.synchronize()
-        idn = ids.cpu().numpy()
-        uniq = np.array([[len(np.unique(idn[b, l])) for l in range(L)] for b in range(N_BATCHES)])
-        bytes_batch = uniq.sum(axis=1) * per_expert + L * fixed_layer + 2 * T * wl.hidden * 4
-        for i in range(args.warmup):
-            step(xs[i % N_BATCHES], y)
-        torch.cuda.synchronize()
-        # whole timed region: K steps back to back
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for i in range(args.steps):
-            step(xs[i % N_BATCHES], y)
-        end.record(stream)
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / args.steps
-        # per launch: an event pair around each decode call (one kernel launch
-        # on the persistent path), same stream, same inputs
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        for i in range(args.steps):
-            ev[i][0].record(stream)
-            step(xs[i % N_BATCHES], y)
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
-        step_bytes = float(np.mean([bytes_batch[i % N_BATCHES] for i in range(args.steps)]))
-        gbs = step_bytes / (ms * 1e-3) / 1e9
-        results[T] = {
-            "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms, "bytes_per_step": step_bytes,
-            "weight_read_GBps": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
-            "mean_distinct_experts_per_layer": float(uniq.mean()),
-            "launch_ms_mean": float(launch_ms.mean()), "launch_ms_p10": float(np.percentile(launch_ms, 10)),
-            "launch_ms_p90": float(np.percentile(launch_ms, 90)),
-        }
-        log(f"[bench] T={T}: {ms:.3f} ms/step, {T / (ms * 1e-3):.1f} tok/s, {gbs:.1f} GB/s "
-            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), U={uniq.mean():.1f}, "
-            f"launch {launch_ms.mean():.3f} ms (p10 {np.percentile(launch_ms, 10):.3f}, "
-            f"p90 {np.percentile(launch_ms, 90):.3f})")
-        del xs, ids
-    moe.close()
+    results = run_workload(qm, wl, L, tok_list, args.steps, args.warmup)
+    others = {}
+    if not args.no_extra and not args.layers:
+        for name, toks in EXTRA:
+            if name == wl.name:
+                continue
+            w2 = synth.WORKLOADS[name]
+            r = run_workload(qm, w2, w2.n_layers, toks, min(args.steps, EXTRA_STEPS), args.warmup)
+            others[name] = {"layers": w2.n_layers, "per_batch": {str(T): v for T, v in r.items()}}
 
     T0 = tok_list[0]
     head = results[T0]
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, T0, L, args.cpu_layers)
-    fmt = "cb2" if wl.gate_up_format == "cb2" else "q2k"
-    kname = (("k_persist_small" if T0 <= 4 else "k_persist_big") + f"<{fmt}> (one launch = the whole decode call)"
-             if not args.multikernel else "decode call (one launch per step kind)")
-    achieved = head["bytes_per_step"] / (head["launch_ms_mean"] * 1e-3) / 1e9
-    traffic = None if args.multikernel or args.layers else committed_traffic(wl.name, T0)
+    traffic = None if args.layers else committed_traffic(wl.name, T0)
+    roof = dict(head["roofline"])
+    roof.update({"algorithmic_bytes_per_launch": head["bytes_per_step"], "launch_ms": head["launch_ms_mean"],
+                 "traffic": traffic})
     line = {
         "metric": "MoE decode tokens/s and weight-read GB/s as % of HBM peak, batch 1/4/16",
         "value": head["tokens_per_s"],
@@ -225,16 +257,23 @@ def main():
                    "tokens": T0, "zipf_s": wl.zipf_s, "parallelism": "single GPU"},
         "weight_read_GBps": head["weight_read_GBps"],
         "pct_hbm_peak": head["pct_hbm_peak"],
-        "roofline": {"bound": "hbm", "kernel": kname,
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "algorithmic_bytes_per_launch": head["bytes_per_step"],
-                     "launch_ms": head["launch_ms_mean"],
-                     "traffic": traffic},
+        "roofline": roof,
         "per_batch": {str(T): r for T, r in results.items()},
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, T, L, n_layers_sample):
@@ -265,6 +304,7 @@ def cpu_baseline(wl, T, L, n_layers_sample):
     step_s = dt * L / n
     log(f"[bench] oracle: {n} layers at T={T} in {dt:.2f}s -> {T / step_s:.4f} tok/s for {L} layers")
     return {"value": T / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host_cpu": cpu_model(), "host_nproc": os.cpu_count(),
             "sample": (f"all {L} layers" if n == L else f"first {n} of {L} layers, scaled by {L}/{n},")
                       + f" of one step at T={T} (numpy fp64 with one BLAS thread, dequantising each"
                       f" touched expert): {dt:.1f}s"}

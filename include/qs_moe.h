@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define QS_MOE_ABI_VERSION 1
+#define QS_MOE_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define QS_API __attribute__((visibility("default")))
@@ -82,15 +82,6 @@ typedef enum { QS_FMT_Q2K = 1, QS_FMT_CB2 = 2 } qs_format;
                                    without learned weight, as a pre-norm residual
                                    stream applies before each MoE block); without
                                    this flag u_l = x_l */
-#define QS_DECODE_MULTIKERNEL 4u /* run each step as its own kernel launch instead of
-                                   the single persistent kernel (same results up to
-                                   summation order; for comparison and debugging) */
-#define QS_DECODE_REQUIRE_PERSISTENT 8u /* fail with QS_E_UNSUPPORTED (nothing enqueued)
-                                   instead of falling back to one launch per step when
-                                   the persistent kernel cannot run this call (device
-                                   without cooperative launch, or a shape whose working
-                                   set does not fit the workgroup's LDS); not
-                                   combinable with QS_DECODE_MULTIKERNEL */
 
 typedef struct qs_moe qs_moe;   /* opaque, owned by the library */
 
@@ -106,13 +97,15 @@ typedef struct {
   int32_t n_layers;        /* layers held resident: 1..4096 */
   int32_t max_tokens;      /* largest n_tokens of a decode call: 1..256, and
                               max_tokens * top_k <= 1024 */
-  int32_t mfma_min_tokens; /* expert bucket size at which the matrix-core path
-                              replaces the GEMV path; a batch that could reach
-                              it takes the batched kernel.  0 = library
-                              default: batches of up to 4 tokens take the
-                              small-batch kernel (GEMV) where it fits; in the
-                              batched kernel every bucket goes through the
-                              matrix cores, except in one-token batches */
+  int32_t mfma_min_tokens; /* expert bucket size (tokens routed to one expert in
+                              one call) from which the matrix-core (MFMA) items
+                              replace the GEMV items; a batch that could reach it
+                              runs the batched kernel.  0 = library default:
+                              batches of up to 4 tokens run the small-batch
+                              kernel (GEMV items only) where it fits; larger
+                              batches run the batched kernel with every bucket
+                              on the matrix cores, one-token batches on the GEMV
+                              items (the measured faster choice on MI355X) */
   int32_t device;          /* HIP device ordinal; -1 = the current device */
 } qs_moe_config;
 
@@ -129,22 +122,36 @@ typedef struct {
   const uint16_t* shared_down;  /* bf16 [H][Fs] */
 } qs_moe_layer_weights;
 
-/* Create a handle: validates cfg, allocates all device memory for n_layers
- * layers and every scratch buffer a decode call of max_tokens needs.
+/* Create a handle for one model shape (the routed-expert MoE layer of the
+ * QuarkStar README, "Model Weights": top-k routed experts in 2-bit types
+ * plus an unquantised shared expert and router).  Validates cfg, allocates
+ * all device memory for n_layers layers and every scratch buffer a decode
+ * call of max_tokens needs, so a decode call allocates nothing.
  * codebook: host int8 [256][8] (required iff either format is QS_FMT_CB2,
  * else ignored, may be NULL).  On success *out owns the allocations; on
  * error *out is NULL and nothing stays allocated.  Validation happens before
- * any HIP call, so an invalid cfg fails without touching the GPU. */
+ * any HIP call, so an invalid cfg fails without touching the GPU.
+ * QS_E_UNSUPPORTED: a valid shape for which the device cannot run the
+ * persistent decode kernel at some batch size up to max_tokens (no
+ * cooperative launch, or a working set larger than a workgroup's LDS). */
 QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_moe** out);
 
 /* Copy one layer's weights into the handle's device memory, re-laying the
  * routed blocks out for the kernels (the dequantised values are unchanged).
+ * The weights stay resident in HBM, as the pages keep the whole quantised
+ * model resident when it fits (QuarkStar README, "Model Weights" and
+ * "Running Models Larger Than Available Memory").
  * hip_stream: a hipStream_t or NULL for the null stream.  Returns after the
  * copies are complete, so the sources may be freed at once.  Re-uploading a
  * layer replaces it. */
 QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, void* hip_stream);
 
-/* Decode n_tokens tokens through layers [layer0, layer0 + n_layers).
+/* Decode n_tokens tokens through layers [layer0, layer0 + n_layers): the
+ * routed-expert MoE step of each layer -- router, top-k with renormalised
+ * softmax, fused dequantise + gate/up GEMV + SwiGLU, down GEMV and weighted
+ * combine, plus the shared expert (QuarkStar README, "Model Weights"; with
+ * n_tokens > 1 the row-batched decode of several sessions in one model step,
+ * QuarkStar README, "Server").
  * x: device fp32 [n_tokens][H]; y: device fp32 [n_tokens][H].
  * u_l is x_l, or RMSNorm(x_l) with QS_DECODE_RMSNORM (router and experts both
  * see u_l).  Without QS_DECODE_RESIDUAL: n_layers must be 1 and y = MoE(u);
@@ -154,15 +161,40 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
  * ids_out: device int32 [n_layers][n_tokens][k] or NULL -- selected experts
  * in rank order (logit descending, ties to the lower index).
  * w_out: device fp32 [n_layers][n_tokens][k] or NULL -- their renormalised
- * softmax weights.  Asynchronous on hip_stream; performs no allocation and
- * no host synchronisation.  1 <= n_tokens <= max_tokens.  Non-finite inputs
- * give non-finite outputs but never an out-of-range expert id. */
+ * softmax weights.  One persistent kernel launch on hip_stream, asynchronous;
+ * performs no allocation and no host synchronisation.
+ * 1 <= n_tokens <= max_tokens.  Non-finite inputs give non-finite outputs but
+ * never an out-of-range expert id.
+ * Every wait inside the kernel is bounded: a call whose wait gives up (a
+ * fault elsewhere on the device, or a limit set by qs_moe_set_wait_limit)
+ * still returns here with QS_OK, since the launch itself succeeded; its
+ * outputs are undefined, and qs_moe_sync_status reports it.  As with a
+ * failed batched step that invalidates every member (QuarkStar README,
+ * "Server"), no output of any call since the last qs_moe_sync_status may be
+ * used when that call returns QS_E_HIP. */
 QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, float* y,
                   int n_tokens, uint32_t flags, int32_t* ids_out, float* w_out,
                   void* hip_stream);
 
+/* Wait for hip_stream, then report whether any decode call on this handle
+ * since the last qs_moe_sync_status gave up a bounded wait: QS_E_HIP if so
+ * (the outputs of those calls are undefined; the handle's synchronisation
+ * words are reset, so the next call runs normally), QS_OK otherwise.
+ * Synchronises hip_stream; use it where the caller synchronises anyway. */
+QS_API int qs_moe_sync_status(qs_moe* h, void* hip_stream);
+
+/* Polls of every bounded wait inside the decode kernels before it gives up;
+ * 0 restores the library default (about 0.1 s for a flagged-word read, a few
+ * seconds for a grid barrier).  A tiny limit makes waits give up while the
+ * data is still on its way: every workgroup then exits through its normal
+ * path and qs_moe_sync_status reports the give-up (tests of the error path).
+ * Takes effect from the next decode call.  QS_E_INVAL for polls < 0. */
+QS_API int qs_moe_set_wait_limit(qs_moe* h, int32_t polls);
+
 /* Routing only (diagnostics and tests): the router, top-k and grouping steps
- * of one layer for n_tokens tokens, with every intermediate written out.
+ * of one layer for n_tokens tokens, with every intermediate written out
+ * (the selection of the QuarkStar README, "Model Weights": the router stays
+ * at full precision and picks the top-k routed experts).
  * Any output pointer may be NULL.  All outputs are device memory:
  *   logits_out fp64 [n_tokens][E]       router logits
  *   ids_out    int32 [n_tokens][k]      as in qs_moe_decode
@@ -180,11 +212,15 @@ QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, uint
                  void* hip_stream);
 
 /* Dequantise one routed matrix from the handle's device copy with the same
- * field decoding the GEMV kernels use (tests).  which: 0 gate, 1 up, 2 down.
- * out: device fp32 [F][H] (gate/up) or [H][F] (down).  Asynchronous. */
+ * field decoding the GEMV kernels use (tests of the IQ2_XXS-class gate/up and
+ * Q2_K down types of the QuarkStar README, "Model Weights").  which: 0 gate,
+ * 1 up, 2 down.  out: device fp32 [F][H] (gate/up) or [H][F] (down).
+ * Asynchronous. */
 QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* out, void* hip_stream);
 
-/* Bytes of device memory the handle holds (weights + scratch). */
+/* Bytes of device memory the handle holds (weights + scratch); the pages
+ * budget the resident weight footprint against the device memory
+ * (QuarkStar README, "Model Weights"). */
 QS_API int qs_moe_memory_bytes(const qs_moe* h, uint64_t* bytes);
 
 /* Synchronise the handle's device, then free everything.  NULL is a no-op. */

@@ -247,6 +247,19 @@ def rms_inv(x: np.ndarray) -> np.ndarray:
     return 1.0 / np.sqrt(np.mean(x * x, axis=-1) + RMS_EPS)
 
 
+def route(lw, x: np.ndarray, k: int, prenorm: bool = False):
+    """The routing of one layer for T tokens: the normalised input u (x, or
+    x * rms_inv(x) with the pre-norm) is formed first and the router is
+    evaluated on it.  Returns (u fp64 [T][H], logits, ids, w, gap)."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.astype(np.float64)
+    if prenorm:
+        u = u * rms_inv(x)[:, None]
+    logits = router_logits(u, lw.router, lw.router_bias)
+    ids, wts, gap = top_k(logits, k)
+    return u, logits, ids, wts, gap
+
+
 def moe_layer(layer: Layer, x: np.ndarray, residual: bool = False, prenorm: bool = False):
     """One decode step of one MoE layer for T tokens.
 
@@ -259,13 +272,7 @@ def moe_layer(layer: Layer, x: np.ndarray, residual: bool = False, prenorm: bool
     wl, lw = layer.wl, layer.lw
     x = np.asarray(x, dtype=np.float32)
     T = x.shape[0]
-    # the normalised input u is formed first and everything (router and
-    # experts) is evaluated on it, as the definition reads
-    u = x.astype(np.float64)
-    if prenorm:
-        u = u * rms_inv(x)[:, None]
-    logits = router_logits(u, lw.router, lw.router_bias)
-    ids, wts, gap = top_k(logits, wl.top_k)
+    u, logits, ids, wts, gap = route(lw, x, wl.top_k, prenorm)
     y = np.zeros((T, wl.hidden), dtype=np.float64)
     for t in range(T):
         for j in range(wl.top_k):

@@ -10,20 +10,18 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsmoe.so")
 
-QS_MOE_ABI_VERSION = 1
+QS_MOE_ABI_VERSION = 2
 QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 QS_FMT_Q2K, QS_FMT_CB2 = 1, 2
 QS_DECODE_RESIDUAL = 1
 QS_DECODE_RMSNORM = 2
-QS_DECODE_MULTIKERNEL = 4
-QS_DECODE_REQUIRE_PERSISTENT = 8
 
 FORMATS = {"q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2}
 
 # Every function include/qs_moe.h declares.
 EXPORTS = (
-    "qs_moe_create", "qs_moe_upload", "qs_moe_decode", "qs_moe_route", "qs_moe_dequant",
-    "qs_moe_memory_bytes", "qs_moe_destroy", "qs_moe_status_string",
+    "qs_moe_create", "qs_moe_upload", "qs_moe_decode", "qs_moe_sync_status", "qs_moe_set_wait_limit",
+    "qs_moe_route", "qs_moe_dequant", "qs_moe_memory_bytes", "qs_moe_destroy", "qs_moe_status_string",
 )
 
 
@@ -62,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "qs_moe_create": [ctypes.POINTER(QsMoeConfig), vp, ctypes.POINTER(vp)],
         "qs_moe_upload": [vp, i32, ctypes.POINTER(QsMoeLayerWeights), vp],
         "qs_moe_decode": [vp, i32, i32, vp, vp, i32, u32, vp, vp, vp],
+        "qs_moe_sync_status": [vp, vp],
+        "qs_moe_set_wait_limit": [vp, ctypes.c_int32],
         "qs_moe_route": [vp, i32, vp, i32, u32, vp, vp, vp, vp, vp],
         "qs_moe_dequant": [vp, i32, i32, i32, vp, vp],
         "qs_moe_memory_bytes": [vp, ctypes.POINTER(ctypes.c_uint64)],
@@ -137,6 +137,14 @@ def qs_moe_decode(h: int, layer0: int, n_layers: int, x, y, n_tokens: int, flags
                   ids_out=None, w_out=None, stream=None) -> None:
     check("qs_moe_decode", LIB.qs_moe_decode(h, layer0, n_layers, _ptr(x), _ptr(y), n_tokens,
                                              flags, _ptr(ids_out), _ptr(w_out), _stream(stream)))
+
+
+def qs_moe_sync_status(h: int, stream=None) -> None:
+    check("qs_moe_sync_status", LIB.qs_moe_sync_status(h, _stream(stream)))
+
+
+def qs_moe_set_wait_limit(h: int, polls: int) -> None:
+    check("qs_moe_set_wait_limit", LIB.qs_moe_set_wait_limit(h, polls))
 
 
 def qs_moe_route(h: int, layer: int, x, n_tokens: int, flags: int = 0, logits_out=None,

@@ -1,21 +1,14 @@
-// qs_kernels.h -- HIP kernels of the routed-expert MoE decode step (gfx950).
-//
-// Data flow of one layer (all on the caller's stream):
-//   k_router    logits[t][e] = sum_h Wr[e][h]*x[t][h] + b[e] in fp64
-//   k_topk      per token: top-k by (logit desc, index asc); renormalised
-//               softmax weights
-//   k_group     stable bucket sort of (token, slot) pairs by expert; the
-//               ascending list of experts in use
-//   k_quant_x   x -> 16-bit fixed point limbs for the integer dot products
-//   k_gateup    per (expert in use, 16-row tile): fused dequant + gate/up
-//               GEMV + SwiGLU for every token in the expert's bucket, output
-//               quantised per 16 rows; shared-expert gate/up in fp32
-//   k_down      per 8 output rows: fused dequant + down GEMV for every pair,
-//               then the weighted combine in a fixed order, shared-expert
-//               down, residual
-// The pages' engines fuse dequantisation into GEMV kernels for the same
-// reason (Quasar README, "Design decisions"); the integer formulation and
-// the layout are this library's own.
+// qs_kernels.h -- device helpers shared by the decode kernels (fixed-point
+// activations, the two block decoders, SwiGLU) and the stand-alone kernels
+// around the persistent decode kernel (gfx950):
+//   k_repack_*   raw blocks -> the planes the GEMVs read (at upload)
+//   k_dequant_*  one matrix decoded with the GEMVs' field decoding (tests)
+//   k_router, k_topk, k_group
+//                the routing steps of one layer with every intermediate
+//                written out (qs_moe_route: diagnostics and tests)
+// The pages' engines fuse dequantisation into GEMV kernels (Quasar README,
+// "Design decisions"); the integer formulation and the layout are this
+// library's own.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -413,358 +406,7 @@ __global__ void k_group(const int32_t* __restrict__ ids, int T, int k, int E, Gr
   }
 }
 
-// -------------------------------------------------------- quantise x ---
-// One workgroup (4 waves) per token; one wave per 256-element block with a
-// shared exponent.  Writes limbs packed for the gate/up format, the per-16
-// scale 2^(e-14) and (Q2_K consumers) the per-16 sums of the fixed values.
-template <bool Q2K>
-__global__ void k_quant_x(const float* __restrict__ x, int H, const double* __restrict__ rinv,
-                          uint32_t* __restrict__ xh, uint32_t* __restrict__ xl,
-                          float* __restrict__ xs, int32_t* __restrict__ xa) {
-  const int t = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nblk = H / kBlockW;
-  const float r = (float)rinv[t];          // 1, or the RMSNorm scale folded into x's scales
-  for (int b = wave; b < nblk; b += blockDim.x >> 6) {
-    const float4 v = *(const float4*)(x + (size_t)t * H + b * kBlockW + 4 * lane);
-    const int e = fixed_exp(wave_max_abs(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)))));
-    const int q0 = to_fixed(v.x, e), q1 = to_fixed(v.y, e), q2 = to_fixed(v.z, e), q3 = to_fixed(v.w, e);
-    int h0, l0, h1, l1, h2, l2, h3, l3;
-    split_limbs(q0, h0, l0);
-    split_limbs(q1, h1, l1);
-    split_limbs(q2, h2, l2);
-    split_limbs(q3, h3, l3);
-    uint32_t ph = pack4(h0, h1, h2, h3), pl = pack4(l0, l1, l2, l3);
-    const size_t base = (size_t)t * (H / 4) + b * 64;
-    if (Q2K) {
-      // dword 4i+p of sub-block i gathers element p of lanes 4i..4i+3
-      const int grp = lane & ~3, p = lane & 3;
-      uint32_t oh = 0, ol = 0;
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const uint32_t sh = __shfl(ph, grp + bb, 64), sl = __shfl(pl, grp + bb, 64);
-        oh |= ((sh >> (8 * p)) & 0xFFu) << (8 * bb);
-        ol |= ((sl >> (8 * p)) & 0xFFu) << (8 * bb);
-      }
-      ph = oh;
-      pl = ol;
-    }
-    xh[base + lane] = ph;
-    xl[base + lane] = pl;
-    int s = q0 + q1 + q2 + q3;
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    if ((lane & 3) == 0) {
-      const size_t si = (size_t)t * (H / kSubW) + b * 16 + (lane >> 2);
-      xs[si] = ldexpf(r, e - kFixedBits);
-      if (Q2K) xa[si] = s;
-    }
-  }
-}
-
-// ---------------------------------------------------------- gate/up ---
-struct GateUpArgs {
-  const uint8_t* gate;       // repacked expert matrices of this layer
-  const uint8_t* up;
-  size_t mat_stride;         // bytes per expert matrix
-  const uint32_t* cbtab;     // codebook tables (global)
-  int H, F, k, T;
-  const uint32_t* xh;        // [T][H/4]
-  const uint32_t* xl;
-  const float* xs;           // [T][H/16]
-  const int32_t* xa;         // [T][H/16] (Q2_K gate/up only)
-  const int32_t* pairs;
-  const int32_t* off;
-  const int32_t* active;
-  const int32_t* n_active;
-  uint32_t* ah;              // [T*k][F/4]   SwiGLU output limbs (Q2_K packing)
-  uint32_t* al;
-  float* as;                 // [T*k][F/16]
-  int32_t* aa;               // [T*k][F/16]
-  // shared expert
-  const uint16_t* sg;        // bf16 [Fs][H]
-  const uint16_t* su;
-  const float* x;            // fp32 [T][H]
-  const double* rinv;        // [T] input scale (RMSNorm or 1)
-  float* ash;                // fp32 [T][Fs]
-  int Fs;
-  int n_shared_items;
-};
-
 // silu(g) * u with the hardware reciprocal (about 1 ulp), not an IEEE divide
 __device__ __forceinline__ float silu_mul(float g, float u) { return __fdividef(g, 1.0f + __expf(-g)) * u; }
-
-// Shared-expert gate/up rows: one wave per row, fp32 FMA over bf16 weights.
-__device__ void shared_gateup_item(const GateUpArgs& a, int item) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int f = item * kSharedRows + wave;
-  if (f >= a.Fs) return;
-  const uint4* gr = (const uint4*)(a.sg + (size_t)f * a.H);
-  const uint4* ur = (const uint4*)(a.su + (size_t)f * a.H);
-  const int n16 = a.H / 8;
-  for (int t = 0; t < a.T; ++t) {
-    const float4* xt = (const float4*)(a.x + (size_t)t * a.H);
-    float g = 0.f, u = 0.f;
-    for (int i = lane; i < n16; i += 64) {
-      const uint4 wg = gr[i], wu = ur[i];
-      const float4 x0 = xt[2 * i], x1 = xt[2 * i + 1];
-      const uint32_t gw[4] = {wg.x, wg.y, wg.z, wg.w}, uw[4] = {wu.x, wu.y, wu.z, wu.w};
-      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        g = fmaf(bf16_to_f32(gw[c] & 0xFFFFu), xv[2 * c], g);
-        g = fmaf(bf16_to_f32(gw[c] >> 16), xv[2 * c + 1], g);
-        u = fmaf(bf16_to_f32(uw[c] & 0xFFFFu), xv[2 * c], u);
-        u = fmaf(bf16_to_f32(uw[c] >> 16), xv[2 * c + 1], u);
-      }
-    }
-    const float r = (float)a.rinv[t];
-    g = group_sum<64>(g) * r;
-    u = group_sum<64>(u) * r;
-    if (lane == 0) a.ash[(size_t)t * a.Fs + f] = silu_mul(g, u);
-  }
-}
-
-// Load one lane's x limbs for chunk `ch` of a token.
-__device__ __forceinline__ void load_x_chunk(const GateUpArgs& a, int t, int ch, uint32_t (&xh)[16],
-                                             uint32_t (&xl)[16], float (&xs)[4], int (&xa)[4],
-                                             bool q2k) {
-  const uint4* ph = (const uint4*)(a.xh + (size_t)t * (a.H / 4) + ch * 16);
-  const uint4* pl = (const uint4*)(a.xl + (size_t)t * (a.H / 4) + ch * 16);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 h = ph[i], l = pl[i];
-    xh[4 * i] = h.x; xh[4 * i + 1] = h.y; xh[4 * i + 2] = h.z; xh[4 * i + 3] = h.w;
-    xl[4 * i] = l.x; xl[4 * i + 1] = l.y; xl[4 * i + 2] = l.z; xl[4 * i + 3] = l.w;
-  }
-  const size_t si = (size_t)t * (a.H / kSubW) + ch * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    xs[i] = a.xs[si + i];
-    xa[i] = q2k ? a.xa[si + i] : 0;
-  }
-}
-
-// Routed gate/up task: rows [16*tile, 16*tile+16) of expert active[u], for
-// every token of its bucket, two tokens at a time.
-template <int FMT>
-__device__ void routed_gateup_item(const GateUpArgs& a, int u, int tile, uint32_t* tab,
-                                   float* lds_a) {
-  const int e = a.active[u];
-  const int p0 = a.off[e], n = a.off[e + 1] - p0;
-  const int nch = a.H / kChunkW;                      // chunks per row
-  const int lpr = lanes_per_row(nch);
-  const int cpl = nch / lpr;                          // chunks per lane
-  const int slots = blockDim.x / lpr;
-  const int slot = threadIdx.x / lpr, j = threadIdx.x % lpr;
-  const size_t nblk = (size_t)a.F * (a.H / kBlockW);
-  const bool q2k = FMT == 1;
-  const MatPlanes pl = q2k ? q2k_planes(nblk) : cb2_planes(nblk);
-  const uint8_t* gbase = a.gate + (size_t)e * a.mat_stride;
-  const uint8_t* ubase = a.up + (size_t)e * a.mat_stride;
-  const int f0 = tile * kGateTile;
-  for (int tg = 0; tg < n; tg += 2) {
-    const int pa = a.pairs[p0 + tg];
-    const int pb = tg + 1 < n ? a.pairs[p0 + tg + 1] : -1;
-    const int nt = pb >= 0 ? 2 : 1;
-    for (int r = slot; r < kGateTile; r += slots) {
-      const int f = f0 + r;
-      float gacc[2] = {0.f, 0.f}, uacc[2] = {0.f, 0.f};
-      for (int cc = 0; cc < cpl; ++cc) {
-        const int ch = j + cc * lpr;
-        const size_t blk = (size_t)f * (a.H / kBlockW) + ch / 4;
-        const int c = ch & 3;
-        for (int tt = 0; tt < nt; ++tt) {
-          const int t = (tt == 0 ? pa : pb) / a.k;
-          uint32_t xh[16], xl[16];
-          float xs[4];
-          int xa[4];
-          load_x_chunk(a, t, ch, xh, xl, xs, xa, q2k);
-          for (int m = 0; m < 2; ++m) {
-            const uint8_t* base = m == 0 ? gbase : ubase;
-            float part;
-            if (q2k) {
-              const uint4 qv = *(const uint4*)(base + pl.q + blk * 64 + c * 16);
-              const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-              const uint32_t scm = *(const uint32_t*)(base + pl.s + blk * 16 + c * 4);
-              const uint32_t dd = *(const uint32_t*)(base + pl.d + blk * 4);
-              part = q2k_chunk_dot(qw, scm, half_to_f32(dd & 0xFFFFu), half_to_f32(dd >> 16), xh,
-                                   xl, xs, xa);
-            } else {
-              const uint4 cv = *(const uint4*)(base + pl.q + blk * 64 + c * 16);
-              uint32_t wq[16];
-              cb2_decode_dword(tab, cv.x, wq[0], wq[1], wq[2], wq[3]);
-              cb2_decode_dword(tab, cv.y, wq[4], wq[5], wq[6], wq[7]);
-              cb2_decode_dword(tab, cv.z, wq[8], wq[9], wq[10], wq[11]);
-              cb2_decode_dword(tab, cv.w, wq[12], wq[13], wq[14], wq[15]);
-              const uint32_t scb = base[pl.s + blk * 4 + c];
-              const float d = half_to_f32(*(const uint16_t*)(base + pl.d + blk * 2));
-              part = d * xs[0] * (float)cb2_chunk_dot(wq, xh, xl, scb);
-            }
-            if (m == 0) gacc[tt] += part;
-            else uacc[tt] += part;
-          }
-        }
-      }
-      for (int tt = 0; tt < nt; ++tt) {
-        const float g = group_sum_dyn(gacc[tt], lpr);
-        const float uu = group_sum_dyn(uacc[tt], lpr);
-        if (j == 0) lds_a[tt * kGateTile + r] = silu_mul(g, uu);
-      }
-    }
-    __syncthreads();
-    // quantise the 16 SwiGLU outputs of each token: lanes 16*tt + r
-    if (threadIdx.x < 32) {
-      const int tt = threadIdx.x >> 4, r = threadIdx.x & 15;
-      const float v = tt < nt ? lds_a[tt * kGateTile + r] : 0.f;
-      float m = fabsf(v);
-#pragma unroll
-      for (int s = 1; s < 16; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-      const int ex = fixed_exp(m);
-      const int q = to_fixed(v, ex);
-      int hi, lo;
-      split_limbs(q, hi, lo);
-      // dword p gathers q_p, q_{4+p}, q_{8+p}, q_{12+p}
-      const int grp = threadIdx.x & ~15, p = r & 3;
-      const int h0 = __shfl(hi, grp + p, 64), h1 = __shfl(hi, grp + 4 + p, 64);
-      const int h2 = __shfl(hi, grp + 8 + p, 64), h3 = __shfl(hi, grp + 12 + p, 64);
-      const int l0 = __shfl(lo, grp + p, 64), l1 = __shfl(lo, grp + 4 + p, 64);
-      const int l2 = __shfl(lo, grp + 8 + p, 64), l3 = __shfl(lo, grp + 12 + p, 64);
-      int s = q;
-#pragma unroll
-      for (int sft = 1; sft < 16; sft <<= 1) s += __shfl_xor(s, sft, 64);
-      if (tt < nt) {
-        const int pair = tt == 0 ? pa : pb;
-        if (r < 4) {
-          a.ah[(size_t)pair * (a.F / 4) + f0 / 4 + r] = pack4(h0, h1, h2, h3);
-          a.al[(size_t)pair * (a.F / 4) + f0 / 4 + r] = pack4(l0, l1, l2, l3);
-        }
-        if (r == 0) {
-          a.as[(size_t)pair * (a.F / kSubW) + f0 / kSubW] = ldexpf(1.0f, ex - kFixedBits);
-          a.aa[(size_t)pair * (a.F / kSubW) + f0 / kSubW] = s;
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-template <int FMT>
-__global__ void __launch_bounds__(256) k_gateup(GateUpArgs a) {
-  __shared__ uint32_t tab[FMT == 2 ? kCbTabWords : 1];
-  __shared__ float lds_a[2 * kGateTile];
-  const int item = blockIdx.x;
-  if (item < a.n_shared_items) {
-    shared_gateup_item(a, item);
-    return;
-  }
-  const int r = item - a.n_shared_items;
-  const int tiles = a.F / kGateTile;
-  const int u = r / tiles, tile = r % tiles;
-  if (u >= *a.n_active) return;
-  if (FMT == 2) {
-    const uint4* src = (const uint4*)a.cbtab;
-    uint4* dst = (uint4*)tab;
-    for (int i = threadIdx.x; i < kCbTabWords / 4; i += blockDim.x) dst[i] = src[i];
-    __syncthreads();
-  }
-  routed_gateup_item<FMT>(a, u, tile, tab, lds_a);
-}
-
-// ------------------------------------------------------------- down ---
-struct DownArgs {
-  const uint8_t* down;       // repacked Q2_K expert matrices [E] of [H][F/256]
-  size_t mat_stride;
-  int H, F, k, T, E;
-  const uint32_t* ah;        // [T*k][F/4]
-  const uint32_t* al;
-  const float* as;           // [T*k][F/16]
-  const int32_t* aa;
-  const int32_t* pairs;
-  const int32_t* off;
-  const int32_t* active;
-  const int32_t* n_active;
-  const int32_t* tok_order;  // [T][k]
-  const float* wts;          // [T][k]
-  const uint16_t* sd;        // bf16 [H][Fs] or null
-  const float* ash;          // [T][Fs]
-  int Fs;
-  const float* xres;         // residual input [T][H] or null
-  float* y;                  // [T][H]
-};
-
-__global__ void __launch_bounds__(256) k_down(DownArgs a) {
-  extern __shared__ float o[];                       // [T*k][kDownRows]
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  const int r0 = blockIdx.x * kDownRows;
-  const int nch = a.F / kChunkW;
-  const int lpr = lanes_per_row(nch);
-  const int cpl = nch / lpr;
-  const int rpi = 64 / lpr;                          // rows per wave instruction
-  const int rsub = lane / lpr, j = lane % lpr;
-  const size_t nblk = (size_t)a.H * (a.F / kBlockW);
-  const MatPlanes pl = q2k_planes(nblk);
-  const int na = *a.n_active;
-  for (int u = wave; u < na; u += nw) {
-    const int e = a.active[u];
-    const uint8_t* base = a.down + (size_t)e * a.mat_stride;
-    const int q0 = a.off[e], q1 = a.off[e + 1];
-    for (int rr = rsub; rr < kDownRows; rr += rpi) {
-      const int h = r0 + rr;
-      for (int pos = q0; pos < q1; ++pos) {
-        const int pair = a.pairs[pos];
-        float part = 0.f;
-        for (int cc = 0; cc < cpl; ++cc) {
-          const int ch = j + cc * lpr;
-          const size_t blk = (size_t)h * (a.F / kBlockW) + ch / 4;
-          const int c = ch & 3;
-          const uint4 qv = *(const uint4*)(base + pl.q + blk * 64 + c * 16);
-          const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-          const uint32_t scm = *(const uint32_t*)(base + pl.s + blk * 16 + c * 4);
-          const uint32_t dd = *(const uint32_t*)(base + pl.d + blk * 4);
-          uint32_t xh[16], xl[16];
-          float xs[4];
-          int xa[4];
-          const uint4* ph = (const uint4*)(a.ah + (size_t)pair * (a.F / 4) + ch * 16);
-          const uint4* plw = (const uint4*)(a.al + (size_t)pair * (a.F / 4) + ch * 16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 hv = ph[i], lv = plw[i];
-            xh[4 * i] = hv.x; xh[4 * i + 1] = hv.y; xh[4 * i + 2] = hv.z; xh[4 * i + 3] = hv.w;
-            xl[4 * i] = lv.x; xl[4 * i + 1] = lv.y; xl[4 * i + 2] = lv.z; xl[4 * i + 3] = lv.w;
-          }
-          const size_t si = (size_t)pair * (a.F / kSubW) + ch * 4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            xs[i] = a.as[si + i];
-            xa[i] = a.aa[si + i];
-          }
-          part += q2k_chunk_dot(qw, scm, half_to_f32(dd & 0xFFFFu), half_to_f32(dd >> 16), xh, xl,
-                                xs, xa);
-        }
-        part = group_sum_dyn(part, lpr);
-        if (j == 0) o[pos * kDownRows + rr] = part;
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < a.T * kDownRows; idx += blockDim.x) {
-    const int t = idx / kDownRows, rr = idx % kDownRows, h = r0 + rr;
-    float acc = 0.f;
-    for (int jj = 0; jj < a.k; ++jj) {
-      const int pos = a.tok_order[t * a.k + jj];
-      const int slot = a.pairs[pos] - t * a.k;
-      acc = fmaf(a.wts[t * a.k + slot], o[pos * kDownRows + rr], acc);
-    }
-    if (a.Fs) {
-      const uint16_t* srow = a.sd + (size_t)h * a.Fs;
-      const float* at = a.ash + (size_t)t * a.Fs;
-      float s = 0.f;
-      for (int f = 0; f < a.Fs; ++f) s = fmaf(bf16_to_f32(srow[f]), at[f], s);
-      acc += s;
-    }
-    if (a.xres) acc += a.xres[(size_t)t * a.H + h];
-    a.y[(size_t)t * a.H + h] = acc;
-  }
-}
 
 }  // namespace qs

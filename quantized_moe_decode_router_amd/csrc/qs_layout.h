@@ -45,7 +45,6 @@ constexpr int kCbTabWords = 8192;     // two 4096-entry signed-quad tables
 constexpr int kFixedBits = 14;        // |v| <= 2^14 after scaling
 constexpr int kDownRows = 8;          // output rows per down-GEMV workgroup
 constexpr int kGateTile = 16;         // gate/up rows per workgroup task
-constexpr int kSharedRows = 4;        // shared gate/up rows per workgroup
 constexpr int kMaxTokens = 256;
 constexpr int kMaxPairs = 1024;
 

@@ -88,7 +88,11 @@ struct qs_moe {
   LayerPtrs* d_layers = nullptr;  // device table of every layer's pointers
   uint32_t* sync = nullptr;       // barrier words
   uint32_t epoch = 0;             // barriers completed on `sync`
-  int grid = 0;                   // workgroups of the persistent kernel (one per CU)
+  int grid = 0;                   // workgroups of the batched kernel (one per CU)
+  int grid_small = 0;             // workgroups of the small-batch kernel: at most
+                                  // H / kDownRows, so every workgroup owns a down tile
+  int wait_limit = 0;             // polls of a bounded wait before it gives up (0 = default)
+  uint32_t* host_err = nullptr;   // pinned host word the error flag is read into
   size_t lds_limit = 0;           // LDS bytes per workgroup available on the device
   bool persist_small_ok = false; // T <= kSmallT instantiation usable
   bool persist_big_ok = false;   // batched instantiation usable
@@ -253,6 +257,7 @@ void free_all(qs_moe* h) {
   if (h->staging) (void)hipFree(h->staging);
   if (h->d_layers) (void)hipFree(h->d_layers);
   if (h->sync) (void)hipFree(h->sync);
+  if (h->host_err) (void)hipHostFree(h->host_err);
 }
 
 __global__ void k_sync_reset(uint32_t* s) {
@@ -291,11 +296,11 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
   const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, cb2, small,
                                  0).end;
-  if (base >= h->lds_limit || h->grid < 8) return p;
+  if (base >= h->lds_limit || h->grid_small < 8) return p;
   p.pfb = (uint32_t)std::min((size_t)kPfbMax, (h->lds_limit - base) & ~(size_t)15);
   p.lds = base + p.pfb;
   p.r_tt = T < 4 ? T : 4;
-  while (p.r_et < 4 && (c.n_experts + p.r_et - 1) / p.r_et > h->grid) p.r_et *= 2;
+  while (p.r_et < 4 && (c.n_experts + p.r_et - 1) / p.r_et > h->grid_small) p.r_et *= 2;
   const uint64_t H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn, nbh = H / 256, nb = F / 256;
   const uint64_t rb = (uint64_t)p.r_et * H * 4, item = 8 * H;
   const uint64_t tile = 2ull * 16 * nbh * (64 + (cb2 ? 4 : 16) + (cb2 ? 2 : 4));
@@ -363,7 +368,7 @@ const void* persist_big_fixed_fn(const qs_moe* h) {
 // The fixed-shape kernel for a T-token call of this handle, or nullptr.
 const void* persist_fixed_fn(const qs_moe* h, int T) {
   const qs_moe_config& c = h->cfg;
-  if (h->grid != 256 || c.gate_up_format != QS_FMT_CB2 || c.hidden != 2048 || c.n_experts != 256 ||
+  if (h->grid_small != 256 || c.gate_up_format != QS_FMT_CB2 || c.hidden != 2048 || c.n_experts != 256 ||
       c.top_k != 8 || c.expert_ffn != 512)
     return nullptr;
   if (c.shared_ffn == 512) return fixed_a3b<512>(T);
@@ -414,6 +419,13 @@ int setup_persistent(qs_moe* h) {
   int coop = 0;
   (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device);
   h->grid = prop.multiProcessorCount & ~7;
+  // The small-batch kernel exchanges data through flagged words that are
+  // reused from layer to layer.  A workgroup rewrites layer l's words only
+  // after it has seen layer l+1's input complete, which every workgroup
+  // produces only after reading layer l's words -- provided every workgroup
+  // owns a down tile (kDownRows output rows).  Hence at most H / kDownRows
+  // workgroups.
+  h->grid_small = std::min(h->grid, (c.hidden / kDownRows) & ~7);
   // dynamic LDS available to a workgroup: the device's LDS minus the largest
   // static LDS of the persistent instantiations (the block-wide vote of the
   // barrier keeps a few bytes there)
@@ -467,26 +479,32 @@ int setup_persistent(qs_moe* h) {
   return QS_OK;
 }
 
-// The whole decode call as one cooperative launch.  Returns 1 (nothing
-// enqueued) when this batch size has no persistent instantiation that fits.
-int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, int T, bool residual,
-                      bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
-  const qs_moe_config& c = h->cfg;
-  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
-  // small batches take the SMALL instantiation when its working set fits
-  // and (with an explicit threshold) no bucket can reach the MFMA size,
-  // otherwise the batched one
-  bool small = T <= kSmallT && (!h->mfma_explicit || T < h->mfma_min) && h->persist_small_ok;
-  PersistShape p;
+// The kernel a T-token call runs: small batches take the small-batch
+// instantiation when its working set fits and (with an explicit threshold)
+// no bucket can reach the MFMA size, otherwise the batched one.  False when
+// neither fits.
+bool choose_kernel(const qs_moe* h, int T, bool& small, PersistShape& p) {
+  small = T <= kSmallT && (!h->mfma_explicit || T < h->mfma_min) && h->persist_small_ok;
   if (small) {
     p = persist_shape(h, T, true);
     small = p.ok;
   }
   if (!small) {
-    if (!h->persist_big_ok) return 1;
+    if (!h->persist_big_ok) return false;
     p = persist_shape(h, T, false);
-    if (!p.ok) return 1;
+    if (!p.ok) return false;
   }
+  return true;
+}
+
+// The whole decode call as one cooperative launch.
+int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, int T, bool residual,
+                      bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
+  const qs_moe_config& c = h->cfg;
+  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
+  bool small = false;
+  PersistShape p;
+  if (!choose_kernel(h, T, small, p)) return QS_E_UNSUPPORTED;   // (create checked every T)
   const uint32_t barriers = small ? 0u : 5u * nL - 1u;
   if (small && h->ll_epoch > 0xF0000000u - 3u * (uint32_t)nL) {
     // flags are about to wrap: clear the flagged buffers and start again
@@ -500,7 +518,9 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   Scratch& s = h->s;
   PersistArgs a{};
   a.layers = h->d_layers + layer0;
-  a.G = h->grid;
+  a.G = small ? h->grid_small : h->grid;
+  a.spin_ll = h->wait_limit ? h->wait_limit : kLLSpinMax;
+  a.spin_bar = h->wait_limit ? h->wait_limit : kSpinMax;
   a.n_layers = nL;
   a.T = T; a.H = c.hidden; a.E = c.n_experts; a.k = c.top_k; a.F = c.expert_ffn; a.Fs = c.shared_ffn;
   a.gq2k = c.gate_up_format == QS_FMT_Q2K;
@@ -533,7 +553,7 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   if (small && h->fixed_ok && p.r_et == 1 && p.r_tt == T) fn = persist_fixed_fn(h, T);
   if (!small && h->big_fixed_ok && p.r_et == 1) fn = persist_big_fixed_fn(h);
   if (!fn) fn = persist_fn(cb2, small);
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(kPersistThreads), args,
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kPersistThreads), args,
                                             (unsigned)p.lds, st);
   if (e != hipSuccess) {
     fprintf(stderr, "qs_moe: persistent launch failed: %s\n", hipGetErrorString(e));
@@ -563,54 +583,6 @@ int launch_route(qs_moe* h, const LayerDev& L, const float* x, int T, bool preno
                      ids_out, w_out);
   GroupOut g{s.cnt, s.off, s.pairs, s.n_active, s.active, s.tok_order};
   hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, st, (const int32_t*)s.ids, T, k, E, g);
-  return hipGetLastError() == hipSuccess ? QS_OK : QS_E_HIP;
-}
-
-int launch_layer(qs_moe* h, const LayerDev& L, const float* x, float* y, int T, bool residual,
-                 bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
-  const qs_moe_config& c = h->cfg;
-  const int E = c.n_experts, k = c.top_k, H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn;
-  Scratch& s = h->s;
-  int rc = launch_route(h, L, x, T, prenorm, ids_out, w_out, st);
-  if (rc) return rc;
-  const bool gq2k = c.gate_up_format == QS_FMT_Q2K;
-  if (gq2k)
-    hipLaunchKernelGGL(k_quant_x<true>, dim3(T), dim3(256), 0, st, x, H, (const double*)s.rinv,
-                       s.xh, s.xl, s.xs, s.xa);
-  else
-    hipLaunchKernelGGL(k_quant_x<false>, dim3(T), dim3(256), 0, st, x, H, (const double*)s.rinv,
-                       s.xh, s.xl, s.xs, s.xa);
-
-  GateUpArgs ga{};
-  ga.gate = L.gate;
-  ga.up = L.up;
-  ga.mat_stride = h->gu_stride;
-  ga.cbtab = h->cbtab;
-  ga.H = H; ga.F = F; ga.k = k; ga.T = T;
-  ga.xh = s.xh; ga.xl = s.xl; ga.xs = s.xs; ga.xa = s.xa;
-  ga.pairs = s.pairs; ga.off = s.off; ga.active = s.active; ga.n_active = s.n_active;
-  ga.ah = s.ah; ga.al = s.al; ga.as = s.as; ga.aa = s.aa;
-  ga.sg = L.sg; ga.su = L.su; ga.x = x; ga.rinv = s.rinv; ga.ash = s.ash; ga.Fs = Fs;
-  ga.n_shared_items = Fs ? (Fs + kSharedRows - 1) / kSharedRows : 0;
-  const int maxU = E < T * k ? E : T * k;
-  const int n_items = ga.n_shared_items + maxU * (F / kGateTile);
-  if (gq2k)
-    hipLaunchKernelGGL(k_gateup<1>, dim3(n_items), dim3(256), 0, st, ga);
-  else
-    hipLaunchKernelGGL(k_gateup<2>, dim3(n_items), dim3(256), 0, st, ga);
-
-  DownArgs da{};
-  da.down = L.down;
-  da.mat_stride = h->dn_stride;
-  da.H = H; da.F = F; da.k = k; da.T = T; da.E = E;
-  da.ah = s.ah; da.al = s.al; da.as = s.as; da.aa = s.aa;
-  da.pairs = s.pairs; da.off = s.off; da.active = s.active; da.n_active = s.n_active;
-  da.tok_order = s.tok_order; da.wts = s.wts;
-  da.sd = L.sd; da.ash = s.ash; da.Fs = Fs;
-  da.xres = residual ? x : nullptr;
-  da.y = y;
-  const size_t lds = (size_t)T * k * kDownRows * sizeof(float);
-  hipLaunchKernelGGL(k_down, dim3(H / kDownRows), dim3(256), lds, st, da);
   return hipGetLastError() == hipSuccess ? QS_OK : QS_E_HIP;
 }
 
@@ -719,6 +691,24 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
     }
   }
   if (rc == QS_OK) rc = setup_persistent(h);
+  if (rc == QS_OK) {
+    if (!hip_ok(hipHostMalloc((void**)&h->host_err, 256, hipHostMallocDefault), "hipHostMalloc(status)")) {
+      h->host_err = nullptr;
+      rc = QS_E_NOMEM;
+    }
+  }
+  if (rc == QS_OK) {
+    // every batch size up to max_tokens must have a persistent kernel that
+    // fits the device (there is no other decode path)
+    for (int T = 1; T <= c.max_tokens && rc == QS_OK; ++T) {
+      bool small = false;
+      PersistShape p;
+      if (!choose_kernel(h, T, small, p)) {
+        fprintf(stderr, "qs_moe: no persistent decode kernel fits a %d-token call of this shape\n", T);
+        rc = QS_E_UNSUPPORTED;
+      }
+    }
+  }
   if (rc != QS_OK) {
     free_all(h);
     delete h;
@@ -791,9 +781,7 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
                   uint32_t flags, int32_t* ids_out, float* w_out, void* hip_stream) {
   if (!h || !x || !y) return QS_E_INVAL;
   const qs_moe_config& c = h->cfg;
-  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM | QS_DECODE_MULTIKERNEL | QS_DECODE_REQUIRE_PERSISTENT))
-    return QS_E_INVAL;
-  if ((flags & QS_DECODE_MULTIKERNEL) && (flags & QS_DECODE_REQUIRE_PERSISTENT)) return QS_E_INVAL;
+  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM)) return QS_E_INVAL;
   if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
   if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
   const bool residual = flags & QS_DECODE_RESIDUAL;
@@ -806,24 +794,34 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
   if (rc) return rc;
   DeviceGuard dg(h->device);
   if (!dg.ok) return QS_E_HIP;
+  return launch_persistent(h, layer0, n_layers, x, y, n_tokens, residual, prenorm, ids_out, w_out,
+                           (hipStream_t)hip_stream);
+}
+
+QS_API int qs_moe_sync_status(qs_moe* h, void* hip_stream) {
+  if (!h) return QS_E_INVAL;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
   hipStream_t st = (hipStream_t)hip_stream;
-  if (!(flags & QS_DECODE_MULTIKERNEL)) {
-    // one persistent launch when an instantiation fits this batch size;
-    // otherwise the same arithmetic as one launch per step
-    rc = launch_persistent(h, layer0, n_layers, x, y, n_tokens, residual, prenorm, ids_out, w_out, st);
-    if (rc != 1) return rc;
-    if (flags & QS_DECODE_REQUIRE_PERSISTENT) return QS_E_UNSUPPORTED;
-  }
-  const size_t per = (size_t)n_tokens * c.top_k;
-  const float* cur = x;
-  for (int i = 0; i < n_layers; ++i) {
-    const bool last = i == n_layers - 1;
-    float* dst = last ? y : h->s.xbuf[i & 1];
-    rc = launch_layer(h, h->layers[layer0 + i], cur, dst, n_tokens, residual, prenorm,
-                      ids_out ? ids_out + i * per : nullptr, w_out ? w_out + i * per : nullptr, st);
-    if (rc) return rc;
-    cur = dst;
-  }
+  *h->host_err = 0;
+  QS_HIP(hipMemcpyAsync(h->host_err, h->sync + kSyncError, 4, hipMemcpyDeviceToHost, st));
+  QS_HIP(hipStreamSynchronize(st));
+  if (*h->host_err == 0) return QS_OK;
+  // A wait gave up: the barrier counters may be out of step with h->epoch.
+  // Clear every sync word (the error flag included) with a kernel, so the
+  // next call starts from a consistent state.  The flagged buffers need no
+  // reset: the flags of later calls are larger than any written so far.
+  hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
+  QS_HIP(hipGetLastError());
+  QS_HIP(hipStreamSynchronize(st));
+  h->epoch = 0;
+  fprintf(stderr, "qs_moe: a decode call gave up a bounded wait; its outputs are undefined\n");
+  return QS_E_HIP;
+}
+
+QS_API int qs_moe_set_wait_limit(qs_moe* h, int32_t polls) {
+  if (!h || polls < 0) return QS_E_INVAL;
+  h->wait_limit = polls;
   return QS_OK;
 }
 

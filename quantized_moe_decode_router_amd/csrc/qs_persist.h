@@ -102,6 +102,8 @@ struct PersistArgs {
   float* xbuf1;
   uint32_t* sync;
   uint32_t epoch0;
+  int spin_ll;               // polls of a flagged read before it gives up
+  int spin_bar;              // polls of a grid-barrier wait before it gives up
   // small-batch flow: flagged copies of the data that crosses workgroups
   uint64_t* ll_lg;           // [T][E][2]  logits (low, high words)
   uint64_t* ll_a;            // [ah | al | as | aa | ash] words of the SwiGLU outputs
@@ -196,7 +198,7 @@ __device__ __forceinline__ bool ll_read(const A& a, const uint64_t* src, QS_LDS 
           }
       }
       if (!__builtin_amdgcn_ballot_w64(missing != 0)) break;
-      if (spins > kLLSpinMax) {
+      if (spins + 1 >= a.spin_ll) {     // a.spin_ll polls have found the data missing
         if ((tid & 63) == 0) {
           cst(&a.sync[kSyncError], 1u);
           *err = 1;
@@ -309,7 +311,7 @@ __device__ __forceinline__ bool grid_barrier(const A& a, uint32_t epoch, PF&& pf
     }
     int spins = 0;
     while (cld(&s[kSyncRelease + 16 * x]) < epoch) {
-      if (++spins > kSpinMax) {
+      if (++spins >= a.spin_bar) {      // a.spin_bar polls have found the barrier closed
         cst(&s[kSyncError], 1u);
         ok = 0;
         break;

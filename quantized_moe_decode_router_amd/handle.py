@@ -53,20 +53,24 @@ class MoE:
                         None if lw.shared_down is None else c(lw.shared_down), stream)
 
     def decode(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
-               w_out=None, stream=None, path="auto"):
-        """path: "auto" (the persistent kernel when it can run this call, else
-        one launch per step), "persistent" (that kernel or QS_E_UNSUPPORTED),
-        "multikernel" (one launch per step)."""
+               w_out=None, stream=None):
+        """One qs_moe_decode call (one persistent kernel launch) on `stream`
+        (torch's current stream by default); asynchronous."""
         import torch
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
-        mode = {"auto": 0, "persistent": L.QS_DECODE_REQUIRE_PERSISTENT,
-                "multikernel": L.QS_DECODE_MULTIKERNEL}[path]
-        flags = ((L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
-                 | mode)
+        flags = (L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
         L.qs_moe_decode(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
+
+    def sync_status(self, stream=None):
+        """Synchronise the stream; raise QsError (QS_E_HIP) if a decode call
+        since the last check gave up a bounded wait."""
+        L.qs_moe_sync_status(self.h, stream)
+
+    def set_wait_limit(self, polls):
+        L.qs_moe_set_wait_limit(self.h, polls)
 
     def route(self, x, layer=0, prenorm=False, stream=None):
         import torch

@@ -39,8 +39,7 @@ def test_no_other_exported_qs_symbols():
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define\s+(QS_\w+)\s+(\d+)u?\b", text))
-    for name in ("QS_MOE_ABI_VERSION", "QS_DECODE_RESIDUAL", "QS_DECODE_RMSNORM",
-                 "QS_DECODE_MULTIKERNEL", "QS_DECODE_REQUIRE_PERSISTENT"):
+    for name in ("QS_MOE_ABI_VERSION", "QS_DECODE_RESIDUAL", "QS_DECODE_RMSNORM"):
         assert hasattr(qm, name), name
         assert int(defs[name]) == getattr(qm, name), name
 
@@ -111,3 +110,5 @@ def test_null_arguments():
     assert qm.LIB.qs_moe_route(None, 0, None, 1, 0, None, None, None, None, None) == qm.QS_E_INVAL
     assert qm.LIB.qs_moe_dequant(None, 0, 0, 0, None, None) == qm.QS_E_INVAL
     assert qm.LIB.qs_moe_memory_bytes(None, None) == qm.QS_E_INVAL
+    assert qm.LIB.qs_moe_sync_status(None, None) == qm.QS_E_INVAL
+    assert qm.LIB.qs_moe_set_wait_limit(None, 0) == qm.QS_E_INVAL

@@ -101,55 +101,48 @@ def test_route_a3b(a3b, T):
     _route_check(wl, moe, lws[0], T)
 
 
-def _decode_check(wl, moe, lw, T, batch=0, label="", path="auto"):
+def _decode_check(wl, moe, lw, T, batch=0, label=""):
     x = synth.tokens(wl, T, batch)
     xd = torch.from_numpy(x).cuda()
     ids = torch.empty((T, wl.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, wl.top_k), dtype=torch.float32, device="cuda")
-    y = moe.decode(xd, ids_out=ids, w_out=w, path=path)
-    torch.cuda.synchronize()
+    y = moe.decode(xd, ids_out=ids, w_out=w)
+    moe.sync_status()
     return check_layer(wl, lw, x, y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), label=label)
 
 
-PATHS = ["persistent", "multikernel"]
-PATH_IDS = PATHS
-
-
-@pytest.mark.parametrize("mk", PATHS, ids=PATH_IDS)
-@pytest.mark.parametrize("T", [1, 3, 4, 16, 33, 64])
-def test_decode_tiny(tiny, T, mk):
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 16, 33, 64])
+def test_decode_tiny(tiny, T):
     wl, moe, lws = tiny
-    say(f"decode tiny T={T} path={mk}")
-    _decode_check(wl, moe, lws[0], T, label=f"tiny T={T}", path=mk)
+    say(f"decode tiny T={T}")
+    _decode_check(wl, moe, lws[0], T, label=f"tiny T={T}")
 
 
-@pytest.mark.parametrize("mk", PATHS, ids=PATH_IDS)
-@pytest.mark.parametrize("T", [1, 4, 7, 16])
-def test_decode_a3b(a3b, T, mk):
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 7, 16])
+def test_decode_a3b(a3b, T):
     wl, moe, lws = a3b
-    say(f"decode a3b T={T} path={mk}")
-    _decode_check(wl, moe, lws[0], T, label=f"a3b T={T}", path=mk)
+    say(f"decode a3b T={T}")
+    _decode_check(wl, moe, lws[0], T, label=f"a3b T={T}")
 
 
-@pytest.mark.parametrize("mk", PATHS, ids=PATH_IDS)
-def test_batch_invariance_and_determinism(gemv_only, mk):
+def test_batch_invariance_and_determinism(gemv_only):
     """On the GEMV items a token's output does not depend on its batch: T = 1
     (small-batch kernel) equals the same token inside T = 8 (batched kernel)."""
     wl, moe, _ = gemv_only
     T = 8
-    say(f"batch invariance {wl.name} T={T} path={mk}")
+    say(f"batch invariance {wl.name} T={T}")
     x = torch.from_numpy(synth.tokens(wl, T, 3)).cuda()
-    y = moe.decode(x, path=mk)
-    y2 = moe.decode(x, path=mk)
+    y = moe.decode(x)
+    y2 = moe.decode(x)
     torch.cuda.synchronize()
     assert torch.equal(y, y2), "two runs differ"
     for t in (0, 3, T - 1):
-        yt = moe.decode(x[t:t + 1].contiguous(), path=mk)
+        yt = moe.decode(x[t:t + 1].contiguous())
         torch.cuda.synchronize()
         assert torch.equal(yt[0], y[t]), f"token {t} differs between T=1 and T={T}"
     perm = torch.tensor([5, 2, 7, 0, 1, 6, 4, 3], device="cuda")
-    yp = moe.decode(x[perm].contiguous(), path=mk)
-    torch.cuda.synchronize()
+    yp = moe.decode(x[perm].contiguous())
+    moe.sync_status()
     assert torch.equal(yp, y[perm]), "permuting tokens does not permute outputs"
 
 
@@ -177,14 +170,14 @@ def a3b_mfma(lib, request):
 def test_decode_tiny_mfma(tiny_mfma, T):
     wl, moe, lws, thr = tiny_mfma
     say(f"decode tiny T={T} mfma_min={thr}")
-    _decode_check(wl, moe, lws[0], T, label=f"tiny mfma{thr} T={T}", path="persistent")
+    _decode_check(wl, moe, lws[0], T, label=f"tiny mfma{thr} T={T}")
 
 
 @pytest.mark.parametrize("T", [1, 7, 32])
 def test_decode_a3b_mfma(a3b_mfma, T):
     wl, moe, lws, thr = a3b_mfma
     say(f"decode a3b T={T} mfma_min={thr}")
-    _decode_check(wl, moe, lws[0], T, label=f"a3b mfma{thr} T={T}", path="persistent")
+    _decode_check(wl, moe, lws[0], T, label=f"a3b mfma{thr} T={T}")
 
 
 def test_mfma_deterministic_and_permutation(a3b_mfma):
@@ -192,12 +185,12 @@ def test_mfma_deterministic_and_permutation(a3b_mfma):
     T = 24
     say(f"mfma determinism a3b T={T} mfma_min={thr}")
     x = torch.from_numpy(synth.tokens(wl, T, 4)).cuda()
-    y = moe.decode(x, path="persistent")
-    y2 = moe.decode(x, path="persistent")
+    y = moe.decode(x)
+    y2 = moe.decode(x)
     torch.cuda.synchronize()
     assert torch.equal(y, y2), "two runs differ"
     perm = torch.randperm(T, generator=torch.Generator().manual_seed(3)).cuda()
-    yp = moe.decode(x[perm].contiguous(), path="persistent")
+    yp = moe.decode(x[perm].contiguous())
     torch.cuda.synchronize()
     # a bucket's tokens sit in other MFMA columns after the permutation; the
     # integer sums are exact, so only fp32 rounding of the block scales differs
@@ -291,33 +284,83 @@ def test_max_tokens_edge(lib):
         _decode_check(wl, moe, lws[0], 256, label="T=256 k=4")
 
 
-@pytest.mark.parametrize("mk", PATHS, ids=PATH_IDS)
-@pytest.mark.parametrize("prenorm", [False, True])
-def test_residual_chain_and_in_place(lib, prenorm, mk):
-    wl = workload("a3b_stack40_zipf")
-    L = 3
-    say(f"residual chain 3 layers prenorm={prenorm}")
-    moe, lws = make_handle(lib, wl, n_layers=L, max_tokens=8)
+def _chain_check(lib, wl, L, T, prenorm, max_tokens=8):
+    """An L-layer call against chained single-layer calls (bitwise) and each
+    layer against the oracle, teacher-forced on the GPU's own x_l; then the
+    same call in place."""
+    moe, lws = make_handle(lib, wl, n_layers=L, max_tokens=max_tokens)
     with moe:
-        x = torch.from_numpy(synth.tokens(wl, 4, 1)).cuda()
-        ids = torch.empty((L, 4, wl.top_k), dtype=torch.int32, device="cuda")
-        w = torch.empty((L, 4, wl.top_k), dtype=torch.float32, device="cuda")
-        y_all = moe.decode(x, n_layers=L, residual=True, prenorm=prenorm, ids_out=ids, w_out=w,
-                           path=mk)
+        x = torch.from_numpy(synth.tokens(wl, T, 1)).cuda()
+        ids = torch.empty((L, T, wl.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((L, T, wl.top_k), dtype=torch.float32, device="cuda")
+        y_all = moe.decode(x, n_layers=L, residual=True, prenorm=prenorm, ids_out=ids, w_out=w)
         cur = x
         for l in range(L):
-            nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True, prenorm=prenorm, path=mk)
-            torch.cuda.synchronize()
+            nxt = moe.decode(cur, layer0=l, n_layers=1, residual=True, prenorm=prenorm)
+            moe.sync_status()
             check_layer(wl, lws[l], cur.cpu().numpy(), nxt.cpu().numpy(), ids[l].cpu().numpy(),
                         w[l].cpu().numpy(), residual=True, prenorm=prenorm,
-                        label=f"layer {l} (teacher-forced)")
+                        label=f"{wl.name} T={T} layer {l} (teacher-forced)")
             cur = nxt
-        torch.cuda.synchronize()
+        moe.sync_status()
         assert torch.equal(y_all, cur), "multi-layer call differs from chained single layers"
         xin = x.clone()
-        moe.decode(xin, y=xin, n_layers=L, residual=True, prenorm=prenorm, path=mk)
-        torch.cuda.synchronize()
+        moe.decode(xin, y=xin, n_layers=L, residual=True, prenorm=prenorm)
+        moe.sync_status()
         assert torch.equal(xin, y_all), "in-place decode differs"
+
+
+@pytest.mark.parametrize("prenorm", [False, True])
+def test_residual_chain_and_in_place(lib, prenorm):
+    say(f"residual chain 3 layers prenorm={prenorm}")
+    _chain_check(lib, workload("a3b_stack40_zipf"), 3, 4, prenorm)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_multilayer_small_hidden(lib, T):
+    """Several layers of a shape with H / 8 < 256 output-row tiles: the
+    small-batch kernel runs on fewer workgroups (one down tile each), so the
+    flagged words reused from layer to layer are rewritten only after every
+    workgroup has read them."""
+    say(f"5-layer tiny stack T={T}")
+    _chain_check(lib, workload("tiny_q2k", n_layers=5, zipf_s=1.1), 5, T, True)
+
+
+def test_wait_limit_reports_give_up(lib):
+    """A wait limit of one poll makes the kernels' bounded waits give up while
+    data is still on its way; every workgroup leaves through its normal path,
+    qs_moe_sync_status reports QS_E_HIP once, and after the limit is restored
+    the next call is clean and matches the oracle."""
+    wl = workload("a3b_stack40_zipf")
+    L = 4
+    moe, lws = make_handle(lib, wl, n_layers=L, max_tokens=16)
+    with moe:
+        for T in (1, 16):                        # small-batch and batched kernels
+            say(f"wait limit 1, T={T}")
+            x = torch.from_numpy(synth.tokens(wl, T, 2)).cuda()
+            moe.set_wait_limit(1)
+            seen = False
+            for _ in range(5):                   # a give-up is (almost) certain on the first call
+                moe.decode(x, n_layers=L, residual=True, prenorm=True)
+                try:
+                    moe.sync_status()
+                except lib.QsError as e:
+                    assert e.status == lib.QS_E_HIP
+                    seen = True
+                    break
+            assert seen, "no wait gave up with a limit of one poll"
+            moe.sync_status()                    # reported once, then clear
+            moe.set_wait_limit(0)
+            ids = torch.empty((L, T, wl.top_k), dtype=torch.int32, device="cuda")
+            y = moe.decode(x, n_layers=1, residual=True, prenorm=True, ids_out=ids)
+            moe.sync_status()
+            check_layer(wl, lws[0], x.cpu().numpy(), y.cpu().numpy(), ids[0].cpu().numpy(),
+                        residual=True, prenorm=True, label=f"after give-up T={T}")
+            y4 = moe.decode(x, n_layers=L, residual=True, prenorm=True)
+            moe.sync_status()
+            assert torch.isfinite(y4).all()
+        with pytest.raises(lib.QsError):
+            moe.set_wait_limit(-1)
 
 
 @pytest.mark.parametrize("T", [1, 5])
@@ -353,8 +396,7 @@ def test_error_statuses_with_gpu(lib):
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), x.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr() + 4, y.data_ptr(), 2, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 16, None, None, st) == lib.QS_E_INVAL
-        both = lib.QS_DECODE_MULTIKERNEL | lib.QS_DECODE_REQUIRE_PERSISTENT
-        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, both, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 4, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 2, 1, x.data_ptr(), y.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_dequant(moe.h, 0, wl.n_experts, 0, y.data_ptr(), st) == lib.QS_E_INVAL
         assert L.qs_moe_dequant(moe.h, 0, 0, 3, y.data_ptr(), st) == lib.QS_E_INVAL
