@@ -176,8 +176,26 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
                   int n_tokens, uint32_t flags, int32_t* ids_out, float* w_out,
                   void* hip_stream);
 
+/* qs_moe_decode for callers that cannot allocate device memory at the time
+ * of the call (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels and results as
+ * qs_moe_decode, but every per-call scratch buffer (synchronisation words,
+ * flagged words, logits, activation limbs, partial outputs) lives in one
+ * static device array of 8 MiB per device, which the library holds until
+ * the process ends; the call allocates nothing and runs no allocating
+ * library routine.  QS_E_UNSUPPORTED (nothing enqueued, a message on stderr)
+ * when this call's scratch -- sized for n_tokens tokens of the handle's
+ * shape -- exceeds that array.  All calls on one device share the array and
+ * it keeps the last call's contents: calls that overlap on one device (other
+ * streams, other handles, other host threads without ordering) race and
+ * give undefined results.  qs_moe_sync_status reports its give-ups too. */
+QS_API int qs_moe_decode_static(qs_moe* h, int layer0, int n_layers, const float* x, float* y,
+                                int n_tokens, uint32_t flags, int32_t* ids_out, float* w_out,
+                                void* hip_stream);
+
 /* Wait for hip_stream, then report whether any decode call on this handle
- * since the last qs_moe_sync_status gave up a bounded wait: QS_E_HIP if so
+ * (or a qs_moe_decode_static call on its device) since the last
+ * qs_moe_sync_status gave up a bounded wait: QS_E_HIP if so
  * (the outputs of those calls are undefined; the handle's synchronisation
  * words are reset, so the next call runs normally), QS_OK otherwise.
  * Synchronises hip_stream; use it where the caller synchronises anyway. */

@@ -20,7 +20,7 @@ FORMATS = {"q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2}
 
 # Every function include/qs_moe.h declares.
 EXPORTS = (
-    "qs_moe_create", "qs_moe_upload", "qs_moe_decode", "qs_moe_sync_status", "qs_moe_set_wait_limit",
+    "qs_moe_create", "qs_moe_upload", "qs_moe_decode", "qs_moe_decode_static", "qs_moe_sync_status", "qs_moe_set_wait_limit",
     "qs_moe_route", "qs_moe_dequant", "qs_moe_memory_bytes", "qs_moe_destroy", "qs_moe_status_string",
 )
 
@@ -60,6 +60,7 @@ def _load() -> ctypes.CDLL:
         "qs_moe_create": [ctypes.POINTER(QsMoeConfig), vp, ctypes.POINTER(vp)],
         "qs_moe_upload": [vp, i32, ctypes.POINTER(QsMoeLayerWeights), vp],
         "qs_moe_decode": [vp, i32, i32, vp, vp, i32, u32, vp, vp, vp],
+        "qs_moe_decode_static": [vp, i32, i32, vp, vp, i32, u32, vp, vp, vp],
         "qs_moe_sync_status": [vp, vp],
         "qs_moe_set_wait_limit": [vp, ctypes.c_int32],
         "qs_moe_route": [vp, i32, vp, i32, u32, vp, vp, vp, vp, vp],
@@ -137,6 +138,12 @@ def qs_moe_decode(h: int, layer0: int, n_layers: int, x, y, n_tokens: int, flags
                   ids_out=None, w_out=None, stream=None) -> None:
     check("qs_moe_decode", LIB.qs_moe_decode(h, layer0, n_layers, _ptr(x), _ptr(y), n_tokens,
                                              flags, _ptr(ids_out), _ptr(w_out), _stream(stream)))
+
+
+def qs_moe_decode_static(h: int, layer0: int, n_layers: int, x, y, n_tokens: int, flags: int = 0,
+                         ids_out=None, w_out=None, stream=None) -> None:
+    check("qs_moe_decode_static", LIB.qs_moe_decode_static(h, layer0, n_layers, _ptr(x), _ptr(y), n_tokens,
+                                                           flags, _ptr(ids_out), _ptr(w_out), _stream(stream)))
 
 
 def qs_moe_sync_status(h: int, stream=None) -> None:

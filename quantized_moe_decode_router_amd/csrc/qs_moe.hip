@@ -12,6 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -68,6 +69,18 @@ struct Scratch {
   float* af;     // batched persistent flow: SwiGLU outputs of MFMA buckets [P][F]
   float* ob;     // routed down outputs by bucket position [P][H]
   float* sb;     // shared-expert down outputs [T][H]
+};
+
+// What one decode launch needs besides the weights: the scratch carve, the
+// synchronisation words and the two flag counters that keep stale flagged
+// words and barrier arrivals from matching later calls.
+struct CallState {
+  Scratch* s;
+  uint32_t* sync;
+  uint32_t* epoch;      // barriers completed on `sync`
+  uint32_t* ll_epoch;   // flags used by the small-batch kernel so far
+  void* zero_base;      // what to clear when the flags wrap (every flagged word
+  size_t zero_bytes;    // any call on this state may have written)
 };
 
 }  // namespace
@@ -262,6 +275,19 @@ void free_all(qs_moe* h) {
 
 __global__ void k_sync_reset(uint32_t* s) {
   for (int i = threadIdx.x; i < kSyncWords; i += blockDim.x) s[i] = 0;
+}
+
+// Zero n 16-byte words (a kernel rather than hipMemsetAsync, so a caller may
+// capture the decode call in a graph).
+__global__ void k_zero16(uint4* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+void launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 16;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+  if (n) hipLaunchKernelGGL(k_zero16, dim3(blocks), dim3(256), 0, st, (uint4*)p, n);
 }
 
 // Shape of one persistent launch: LDS carve plus as much weight-staging
@@ -498,24 +524,24 @@ bool choose_kernel(const qs_moe* h, int T, bool& small, PersistShape& p) {
 }
 
 // The whole decode call as one cooperative launch.
-int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, int T, bool residual,
-                      bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
+int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const float* x, float* y, int T,
+                      bool residual, bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
   const qs_moe_config& c = h->cfg;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
   bool small = false;
   PersistShape p;
   if (!choose_kernel(h, T, small, p)) return QS_E_UNSUPPORTED;   // (create checked every T)
   const uint32_t barriers = small ? 0u : 5u * nL - 1u;
-  if (small && h->ll_epoch > 0xF0000000u - 3u * (uint32_t)nL) {
+  if (small && *cs.ll_epoch > 0xF0000000u - 3u * (uint32_t)nL) {
     // flags are about to wrap: clear the flagged buffers and start again
-    if (hipMemsetAsync(h->s.base, 0, h->s.ll_bytes, st) != hipSuccess) return QS_E_HIP;
-    h->ll_epoch = 0;
+    launch_zero(cs.zero_base, cs.zero_bytes, st);
+    *cs.ll_epoch = 0;
   }
-  if (h->epoch + barriers > (1u << 26)) {
-    hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
-    h->epoch = 0;
+  if (*cs.epoch + barriers > (1u << 26)) {
+    hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, cs.sync);
+    *cs.epoch = 0;
   }
-  Scratch& s = h->s;
+  const Scratch& s = *cs.s;
   PersistArgs a{};
   a.layers = h->d_layers + layer0;
   a.G = small ? h->grid_small : h->grid;
@@ -542,10 +568,10 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
   // GEMV items (measured faster there: Flash stack T = 1, 1680 vs 1274 tok/s)
   a.mfma_min = !h->mfma_explicit && T == 1 ? 2 : h->mfma_min;
   a.ll_lg = s.ll_lg; a.ll_a = s.ll_a; a.llx0 = s.llx[0]; a.llx1 = s.llx[1];
-  a.ll_epoch = h->ll_epoch;
+  a.ll_epoch = *cs.ll_epoch;
   a.af = s.af; a.ob = s.ob; a.sb = s.sb;
-  a.sync = h->sync;
-  a.epoch0 = h->epoch;
+  a.sync = cs.sync;
+  a.epoch0 = *cs.epoch;
   void* args[] = {&a};
   // the fixed-shape kernel needs the router unit it assumes (one expert per
   // workgroup, all tokens at once)
@@ -559,8 +585,8 @@ int launch_persistent(qs_moe* h, int layer0, int nL, const float* x, float* y, i
     fprintf(stderr, "qs_moe: persistent launch failed: %s\n", hipGetErrorString(e));
     return QS_E_HIP;
   }
-  h->epoch += barriers;
-  if (small) h->ll_epoch += 3u * (uint32_t)nL;
+  *cs.epoch += barriers;
+  if (small) *cs.ll_epoch += 3u * (uint32_t)nL;
   return QS_OK;
 }
 
@@ -589,6 +615,64 @@ int launch_route(qs_moe* h, const LayerDev& L, const float* x, int T, bool preno
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
+}
+
+// Host-side argument checks of a decode call (nothing is enqueued on error).
+int check_decode_args(const qs_moe* h, int layer0, int n_layers, const float* x, const float* y,
+                      int n_tokens, uint32_t flags) {
+  if (!h || !x || !y) return QS_E_INVAL;
+  const qs_moe_config& c = h->cfg;
+  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM)) return QS_E_INVAL;
+  if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
+  if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
+  const bool residual = flags & QS_DECODE_RESIDUAL;
+  if (!residual && n_layers != 1) return QS_E_INVAL;
+  const size_t act_bytes = (size_t)n_tokens * c.hidden * sizeof(float);
+  if (!residual && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
+  if (residual && x != y && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
+  return check_layer_range(h, layer0, n_layers);
+}
+
+// ---------------------------------------------- static decode scratch ---
+// qs_moe_decode_static keeps every per-call buffer (sync words, flagged
+// words, logits, activation limbs, partial outputs) in one file-scope device
+// array instead of the handle's allocation.  Each device the library runs
+// on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in: its device address, per device, comes from
+// hipGetSymbolAddress once (at the first qs_moe_create on that device) and
+// only that address is passed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr size_t kStaticSyncBytes = 4096;       // the sync words, then the carve
+constexpr int kMaxDevices = 64;
+
+struct StaticDev {
+  uint8_t* base = nullptr;   // device address of `scratch` on this device
+  uint32_t epoch = 0;        // barriers completed on its sync words
+  uint32_t ll_epoch = 0;     // flags used on its flagged words
+};
+StaticDev g_static[kMaxDevices];
+std::mutex g_static_mu;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+// With `dev` current: look up this device's copy of the array and zero it
+// (sync words, and flagged words that must never match a later flag).
+int static_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return QS_OK;   // the static variant then refuses
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDev& sd = g_static[dev];
+  if (sd.base) return QS_OK;
+  void* ptr = nullptr;
+  if (!hip_ok(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) return QS_E_HIP;
+  launch_zero(ptr, kStaticScratchBytes, nullptr);
+  if (!hip_ok(hipGetLastError(), "zero static scratch") || !hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize"))
+    return QS_E_HIP;
+  sd.base = (uint8_t*)ptr;
+  return QS_OK;
 }
 
 }  // namespace
@@ -691,6 +775,7 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
     }
   }
   if (rc == QS_OK) rc = setup_persistent(h);
+  if (rc == QS_OK) rc = static_setup(h->device);
   if (rc == QS_OK) {
     if (!hip_ok(hipHostMalloc((void**)&h->host_err, 256, hipHostMallocDefault), "hipHostMalloc(status)")) {
       h->host_err = nullptr;
@@ -779,23 +864,43 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
 
 QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, float* y, int n_tokens,
                   uint32_t flags, int32_t* ids_out, float* w_out, void* hip_stream) {
-  if (!h || !x || !y) return QS_E_INVAL;
-  const qs_moe_config& c = h->cfg;
-  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM)) return QS_E_INVAL;
-  if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
-  if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
-  const bool residual = flags & QS_DECODE_RESIDUAL;
-  const bool prenorm = flags & QS_DECODE_RMSNORM;
-  if (!residual && n_layers != 1) return QS_E_INVAL;
-  const size_t act_bytes = (size_t)n_tokens * c.hidden * sizeof(float);
-  if (!residual && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
-  if (residual && x != y && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
-  int rc = check_layer_range(h, layer0, n_layers);
+  int rc = check_decode_args(h, layer0, n_layers, x, y, n_tokens, flags);
   if (rc) return rc;
   DeviceGuard dg(h->device);
   if (!dg.ok) return QS_E_HIP;
-  return launch_persistent(h, layer0, n_layers, x, y, n_tokens, residual, prenorm, ids_out, w_out,
-                           (hipStream_t)hip_stream);
+  const CallState cs{&h->s, h->sync, &h->epoch, &h->ll_epoch, h->s.base, h->s.ll_bytes};
+  return launch_persistent(h, cs, layer0, n_layers, x, y, n_tokens, (flags & QS_DECODE_RESIDUAL) != 0,
+                           (flags & QS_DECODE_RMSNORM) != 0, ids_out, w_out, (hipStream_t)hip_stream);
+}
+
+QS_API int qs_moe_decode_static(qs_moe* h, int layer0, int n_layers, const float* x, float* y,
+                                int n_tokens, uint32_t flags, int32_t* ids_out, float* w_out,
+                                void* hip_stream) {
+  int rc = check_decode_args(h, layer0, n_layers, x, y, n_tokens, flags);
+  if (rc) return rc;
+  if (h->device < 0 || h->device >= kMaxDevices) return QS_E_UNSUPPORTED;
+  // this call's scratch, carved for exactly n_tokens tokens
+  qs_moe_config cc = h->cfg;
+  cc.max_tokens = n_tokens;
+  const size_t need = kStaticSyncBytes + scratch_bytes(cc);
+  if (need > kStaticScratchBytes) {
+    fprintf(stderr, "qs_moe: qs_moe_decode_static needs %zu bytes of scratch for %d tokens of this shape; "
+            "its static scratch holds %zu\n", need, n_tokens, kStaticScratchBytes);
+    return QS_E_UNSUPPORTED;
+  }
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDev& sd = g_static[h->device];
+  if (!sd.base) return QS_E_STATE;            // set up by qs_moe_create on this device
+  Scratch s;
+  s.base = sd.base + kStaticSyncBytes;
+  s.bytes = scratch_bytes(cc);
+  carve_scratch(cc, s);
+  const CallState cs{&s, (uint32_t*)sd.base, &sd.epoch, &sd.ll_epoch, s.base,
+                     kStaticScratchBytes - kStaticSyncBytes};
+  return launch_persistent(h, cs, layer0, n_layers, x, y, n_tokens, (flags & QS_DECODE_RESIDUAL) != 0,
+                           (flags & QS_DECODE_RMSNORM) != 0, ids_out, w_out, (hipStream_t)hip_stream);
 }
 
 QS_API int qs_moe_sync_status(qs_moe* h, void* hip_stream) {
@@ -803,18 +908,30 @@ QS_API int qs_moe_sync_status(qs_moe* h, void* hip_stream) {
   DeviceGuard dg(h->device);
   if (!dg.ok) return QS_E_HIP;
   hipStream_t st = (hipStream_t)hip_stream;
-  *h->host_err = 0;
+  // the handle's error flag and that of the device's static scratch (the
+  // calls of qs_moe_decode_static)
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDev* sd = h->device >= 0 && h->device < kMaxDevices && g_static[h->device].base ? &g_static[h->device]
+                                                                                        : nullptr;
+  h->host_err[0] = h->host_err[1] = 0;
   QS_HIP(hipMemcpyAsync(h->host_err, h->sync + kSyncError, 4, hipMemcpyDeviceToHost, st));
+  if (sd) QS_HIP(hipMemcpyAsync(h->host_err + 1, (uint32_t*)sd->base + kSyncError, 4, hipMemcpyDeviceToHost, st));
   QS_HIP(hipStreamSynchronize(st));
-  if (*h->host_err == 0) return QS_OK;
-  // A wait gave up: the barrier counters may be out of step with h->epoch.
+  if (h->host_err[0] == 0 && h->host_err[1] == 0) return QS_OK;
+  // A wait gave up: the barrier counters may be out of step with the epoch.
   // Clear every sync word (the error flag included) with a kernel, so the
   // next call starts from a consistent state.  The flagged buffers need no
   // reset: the flags of later calls are larger than any written so far.
-  hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
+  if (h->host_err[0]) {
+    hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, h->sync);
+    h->epoch = 0;
+  }
+  if (h->host_err[1]) {
+    hipLaunchKernelGGL(k_sync_reset, dim3(1), dim3(256), 0, st, (uint32_t*)sd->base);
+    sd->epoch = 0;
+  }
   QS_HIP(hipGetLastError());
   QS_HIP(hipStreamSynchronize(st));
-  h->epoch = 0;
   fprintf(stderr, "qs_moe: a decode call gave up a bounded wait; its outputs are undefined\n");
   return QS_E_HIP;
 }

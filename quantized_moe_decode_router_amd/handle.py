@@ -64,6 +64,17 @@ class MoE:
         L.qs_moe_decode(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
 
+    def decode_static(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
+                      w_out=None, stream=None):
+        """qs_moe_decode_static: decode with the library's static device scratch."""
+        import torch
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty_like(x)
+        flags = (L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
+        L.qs_moe_decode_static(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
+        return y
+
     def sync_status(self, stream=None):
         """Synchronise the stream; raise QsError (QS_E_HIP) if a decode call
         since the last check gave up a bounded wait."""
