@@ -469,8 +469,8 @@ __device__ __forceinline__ void shared_gu_item_big(const A& a, lds_cptr wbase, c
 template <bool PRE, class A>
 __device__ __forceinline__ void big_shared_gu(const A& a, const LayerPtrs& Lp, const float* x, BigL& L) {
   int j = 0;
-  for (int it = blockIdx.x; it < n_shared_items(a); it += a.G, ++j) {
-    if (j > 0 || !PRE) stage_now([&](int w, int n) { copy_shared_item(a, Lp, L.P.pfb, it, w, n); });
+  for (int it = blockIdx.x; it < n_shared_items<false>(a); it += a.G, ++j) {
+    if (j > 0 || !PRE) stage_now([&](int w, int n) { copy_shared_item<false>(a, Lp, L.P.pfb, it, w, n); });
     else wait_all_and_sync();
     shared_gu_item_big(a, L.P.pfb, x, it, L.P);
   }
@@ -1372,11 +1372,14 @@ __device__ __forceinline__ void persist_big_body(const A& a) {
     float* y = li == a.n_layers - 1 ? a.y_out : (li & 1 ? a.xbuf1 : a.xbuf0);
     const bool more = li + 1 < a.n_layers;
     // ---- R
+    QS_STAMP(li, 0);
     big_router(a, Lp, x, L.P);
+    QS_STAMP(li, 1);
     if (!grid_barrier(a, ++epoch, [&](int w, int n) {
-          if ((int)blockIdx.x < n_shared_items(a)) copy_shared_item(a, Lp, L.P.pfb, blockIdx.x, w, n);
+          if ((int)blockIdx.x < n_shared_items<false>(a)) copy_shared_item<false>(a, Lp, L.P.pfb, blockIdx.x, w, n);
         }))
       return;
+    QS_STAMP(li, 2);
     // ---- K
     {
       const int nb = a.H / kBlockW, units = a.T + a.T * nb;
@@ -1385,18 +1388,25 @@ __device__ __forceinline__ void persist_big_body(const A& a) {
         else quant_x_wave<false>(a, x, (u - a.T) / nb, (u - a.T) % nb, L.P);
       }
     }
+    QS_STAMP(li, 3);
     if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
+    QS_STAMP(li, 4);
     // ---- GU
     big_gu_phase<FMT>(a, Lp, x, L, pp);
+    QS_STAMP(li, 5);
     if (!grid_barrier(a, ++epoch, [&](int w, int n) {
           if (a.Fs && (int)blockIdx.x < a.H / kDownRows) copy_sd_rows(a, Lp, L.P.pfb, blockIdx.x * kDownRows, w, n);
         }))
       return;
+    QS_STAMP(li, 6);
     // ---- D
     big_dn_phase(a, Lp, L, pp);
+    QS_STAMP(li, 7);
     if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
+    QS_STAMP(li, 8);
     // ---- C
     big_combine(a, L.P, x, y);
+    QS_STAMP(li, 9);
     if (more && !grid_barrier(a, ++epoch, [&](int w, int n) {
           if ((int)blockIdx.x < router_groups(a)) copy_router_rows(a, a.layers[li + 1], L.P, blockIdx.x, w, n);
         }))

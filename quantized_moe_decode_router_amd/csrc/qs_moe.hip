@@ -315,6 +315,16 @@ PersistShape big_shape(const qs_moe* h, int T) {
   return p;
 }
 
+// (row, 64-weight chunk) units per thread in a 16-row gate/up tile of the
+// small-batch kernel (the lane layout of gu_tile_load).
+int gu_units(int H) {
+  const int nch = H / kChunkW;
+  int lpr = 64;
+  while (nch % lpr) lpr >>= 1;
+  const int slots = kPersistThreads / lpr;
+  return (slots >= kGateTile ? 1 : kGateTile / slots) * (nch / lpr);
+}
+
 PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   const qs_moe_config& c = h->cfg;
   if (!small) return big_shape(h, T);
@@ -337,11 +347,18 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
     // region A: router rows + one shared item (phase R); regions A and B:
     // gate/up tiles (K, GU); region B and the x limbs after it: experts'
     // down rows (D).  The shared down rows have their own slot.
-    const uint64_t r_sh = a16(rb) + (Fs ? item : 0);
+    // one shared gate/up row per item above hidden 2048, two otherwise (sh_rows)
+    const uint64_t sitem = (H > 2048 ? 4 : 8) * H;
+    const uint64_t r_sh = a16(rb) + (Fs ? sitem : 0);
     const uint64_t xl = 2 * a16((uint64_t)T * H) + 2 * a16((uint64_t)T * H / 4);
     const uint64_t A = a16(r_sh);
     p.pfa = (uint32_t)A;
-    fits = A <= p.pfb && tile <= p.pfb && (p.pfb - A) + xl >= pe;
+    // the routed gate/up tiles stream through registers (at most kGuUnits
+    // (row, chunk) units per thread and tile), not through the staging buffer
+    // Hidden sizes above 2048 take the batched kernel: on the 4096-wide
+    // large-layer shape the small-batch kernel, which streams its shared
+    // items and down rows one staging at a time, measured 5 % slower.
+    fits = A <= p.pfb && (p.pfb - A) + xl >= pe && gu_units(c.hidden) <= kGuUnits && c.hidden <= 2048;
     (void)sd;
     // each flagged read is at most 32 words per thread
     const uint64_t P = (uint64_t)T * c.top_k;
@@ -1021,5 +1038,15 @@ QS_API int qs_moe_destroy(qs_moe* h) {
   delete h;
   return rc;
 }
+
+#ifdef QS_STAMPS
+// Profiling builds only: copy the phase stamps to host memory.
+QS_API int qs_debug_read_stamps(void* host_dst, size_t bytes) {
+  if (bytes > sizeof(g_qs_stamps)) bytes = sizeof(g_qs_stamps);
+  return hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(g_qs_stamps), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess
+             ? QS_OK
+             : QS_E_HIP;
+}
+#endif
 
 }  // extern "C"

@@ -117,6 +117,30 @@ struct PersistArgs {
   float* sb;                 // [T][H]   shared-expert down outputs
 };
 
+// Phase stamps for profiling builds (-DQS_STAMPS): thread 0 of each
+// workgroup records the 100 MHz wall clock at point k of layer li.  The
+// default build compiles them out.
+#ifdef QS_STAMPS
+constexpr int kStampLayers = 64, kStampWgs = 256, kStampPts = 24;
+__device__ uint64_t g_qs_stamps[kStampLayers * kStampWgs * kStampPts];
+__device__ int g_qs_stamp_li[kStampWgs];   // layer of the workgroup's current stamps
+#define QS_STAMP(li, k)                                                                   \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && (li) < kStampLayers && blockIdx.x < kStampWgs) {             \
+      g_qs_stamps[((li) * kStampWgs + blockIdx.x) * kStampPts + (k)] = __builtin_amdgcn_s_memrealtime(); \
+      g_qs_stamp_li[blockIdx.x] = (li);                                                   \
+    }                                                                                     \
+  } while (0)
+#define QS_STAMP2(k) QS_STAMP(g_qs_stamp_li[blockIdx.x], k)
+#else
+#define QS_STAMP(li, k) \
+  do {                  \
+  } while (0)
+#define QS_STAMP2(k) \
+  do {               \
+  } while (0)
+#endif
+
 // Thread index through an opaque move: values derived from it are then
 // recomputed in each phase instead of being hoisted out of the layer loop
 // and kept live (in registers) across every phase.
@@ -505,11 +529,16 @@ __device__ __forceinline__ int router_groups(const A& a) { return (a.E + a.r_et 
 template <class A>
 __device__ __forceinline__ uint32_t router_bytes(const A& a) { return (uint32_t)a.r_et * a.H * 4; }
 
-template <class A>
-__device__ __forceinline__ int n_shared_items(const A& a) { return a.Fs / kSharedItemRows; }
-template <class A>
+// Shared gate/up rows per item: the small-batch kernel takes one row at a
+// time for hidden sizes above 2048 (its staging region then still holds a
+// router row and an item), two otherwise; the batched kernel always two.
+template <bool SMALL, class A>
+__device__ __forceinline__ int sh_rows(const A& a) { return SMALL && a.H > 2048 ? 1 : kSharedItemRows; }
+template <bool SMALL, class A>
+__device__ __forceinline__ int n_shared_items(const A& a) { return a.Fs / sh_rows<SMALL>(a); }
+template <bool SMALL, class A>
 __device__ __forceinline__ uint32_t shared_item_bytes(const A& a) {
-  return (uint32_t)kSharedItemRows * 2 * a.H * 2;
+  return (uint32_t)sh_rows<SMALL>(a) * 2 * a.H * 2;
 }
 template <class A>
 __device__ __forceinline__ uint32_t gu_tile_bytes(const A& a) {
@@ -536,24 +565,8 @@ __device__ __forceinline__ uint32_t shared_off(const A& a) {
 template <bool SMALL, class A>
 __device__ __forceinline__ int shared_pf_count(const A& a) {
   const uint32_t off = shared_off<SMALL>(a), end = SMALL ? a.pfa : a.pfb - gu_tile_bytes(a);
-  const int fit = end > off ? (int)((end - off) / shared_item_bytes(a)) : 0;
-  const int mine = my_count(a, n_shared_items(a));
-  return mine < fit ? mine : fit;
-}
-
-// routed gate/up tiles: SMALL at 0; otherwise after the shared items
-template <bool SMALL, class A>
-__device__ __forceinline__ int gu_items_base(const A& a) { return SMALL ? 0 : n_shared_items(a); }
-template <bool SMALL, class A>
-__device__ __forceinline__ uint32_t tile_off(const A& a) {
-  return SMALL ? 0 : shared_off<SMALL>(a) + shared_pf_count<SMALL>(a) * shared_item_bytes(a);
-}
-template <bool SMALL, class A>
-__device__ __forceinline__ int tile_pf_count(const A& a, int na) {
-  const uint32_t off = tile_off<SMALL>(a), end = a.pfb;   // SMALL: regions A and B
-  const int fit = end > off ? (int)((end - off) / gu_tile_bytes(a)) : 0;
-  const int base = gu_items_base<SMALL>(a);
-  const int mine = my_count(a, base + na * (a.F / kGateTile)) - my_count(a, base);
+  const int fit = end > off ? (int)((end - off) / shared_item_bytes<SMALL>(a)) : 0;
+  const int mine = my_count(a, n_shared_items<SMALL>(a));
   return mine < fit ? mine : fit;
 }
 
@@ -591,12 +604,13 @@ __device__ __forceinline__ void copy_router_rows(const A& a, const LayerPtrs& Lp
   dma_to_lds<0>(Lp.router + (size_t)e0 * a.H, L.pfb, (uint32_t)ne * a.H * 4, w, nw);
 }
 
-template <class A>
+template <bool SMALL, class A>
 __device__ __forceinline__ void copy_shared_item(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
                                                  int item, int w, int nw) {
   const uint32_t row = (uint32_t)a.H * 2;
-  for (int r = 0; r < kSharedItemRows; ++r) {
-    const int f = item * kSharedItemRows + r;
+  const int rows = sh_rows<SMALL>(a);
+  for (int r = 0; r < rows; ++r) {
+    const int f = item * rows + r;
     dma_to_lds<0>(Lp.sg + (size_t)f * a.H, dst + (2 * r) * row, row, w, nw);
     dma_to_lds<0>(Lp.su + (size_t)f * a.H, dst + (2 * r + 1) * row, row, w, nw);
   }
@@ -636,6 +650,7 @@ __device__ __forceinline__ void copy_tile(const A& a, const LayerPtrs& Lp, QS_LD
   }
 }
 
+
 // Routed down rows r0..r0+7 of expert e as [codes 8*nb*64 | scales 8*nb*16 | d,dmin 8*nb*4].
 template <class A>
 __device__ __forceinline__ void copy_down_rows(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
@@ -663,7 +678,7 @@ __device__ __forceinline__ void pf_router_and_shared(const A& a, const LayerPtrs
   if (SMALL) {
     const int n = shared_pf_count<true>(a);
     for (int j = 0; j < n; ++j)
-      copy_shared_item(a, Lp, L.pfb + shared_off<true>(a) + (uint32_t)j * shared_item_bytes(a),
+      copy_shared_item<true>(a, Lp, L.pfb + shared_off<true>(a) + (uint32_t)j * shared_item_bytes<true>(a),
                        (int)blockIdx.x + j * a.G, w, nw);
   }
 }
@@ -673,7 +688,7 @@ __device__ __forceinline__ void pf_shared_items(const A& a, const LayerPtrs& Lp,
                                                 int nw) {
   const int n = shared_pf_count<false>(a);
   for (int j = 0; j < n; ++j)
-    copy_shared_item(a, Lp, L.pfb + (uint32_t)j * shared_item_bytes(a), (int)blockIdx.x + j * a.G, w,
+    copy_shared_item<false>(a, Lp, L.pfb + (uint32_t)j * shared_item_bytes<false>(a), (int)blockIdx.x + j * a.G, w,
                      nw);
 }
 
@@ -683,25 +698,6 @@ __device__ __forceinline__ void pf_shared_items(const A& a, const LayerPtrs& Lp,
 __device__ __forceinline__ int act_lanes(const PersistLds& L, int u0, int n) {
   const int i = u0 + (int)(qs_tid() & 63);
   return i < n ? L.act[i] : 0;
-}
-
-template <bool SMALL, class A>
-__device__ __forceinline__ void pf_tiles(const A& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
-  const int na = *L.nact, tiles = a.F / kGateTile, base = gu_items_base<SMALL>(a);
-  const int n = tile_pf_count<SMALL>(a, na), j0 = my_count(a, base);
-  for (int c0 = 0; c0 < n; c0 += 64) {
-    // lane i: the expert of tile c0 + i
-    const int i = c0 + (int)(qs_tid() & 63);
-    const int ri = (int)blockIdx.x + (j0 + i) * a.G - base;
-    const int el = i < n ? L.act[ri / tiles] : 0;
-    const int m = n - c0 < 64 ? n - c0 : 64;
-    for (int jj = 0; jj < m; ++jj) {
-      const int j = c0 + jj;
-      const int r = (int)blockIdx.x + (j0 + j) * a.G - base;
-      copy_tile(a, Lp, L.pfb + tile_off<SMALL>(a) + (uint32_t)j * gu_tile_bytes(a),
-                __builtin_amdgcn_readlane(el, jj), (r % tiles) * kGateTile, w, nw);
-    }
-  }
 }
 
 template <bool SMALL, class A>
@@ -840,7 +836,9 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
             if (lane == 0) L.red[32 + wave * V + ET * TT + j] = s;
           }
       }
+      QS_STAMP2(21);
       __syncthreads();
+      QS_STAMP2(22);
       if (qs_tid() < ET * TT) {
         const int ii = qs_tid() / TT, j = qs_tid() % TT;
         const int e = e0 + ii, t = t0 + j;
@@ -885,14 +883,11 @@ __device__ __forceinline__ size_t ll_ash(const A& a) { return ll_as(a) + 2 * (si
 template <class A>
 __device__ __forceinline__ int ll_a_words(const A& a) { return (int)(ll_ash(a) + (size_t)a.T * a.Fs); }
 // SMALL flow: waves [copy_w0, 8) issue the copies that overlap a flagged
-// read, waves [0, copy_w0) poll (when the words fit 32 per thread of them);
-// the gate/up tiles are copied by waves [tile_w0, 8) while waves
-// [0, tile_w0) quantise x.  (Measured choices; T is a compile-time constant
-// in the fixed-shape kernels.)
+// read, waves [0, copy_w0) poll (when the words fit 32 per thread of them).
+// (Measured choices; T is a compile-time constant in the fixed-shape
+// kernels.)
 template <class A>
 __device__ __forceinline__ int copy_w0(const A& a) { return a.T == 1 ? 7 : 6; }
-template <class A>
-__device__ __forceinline__ int tile_w0(const A& a) { return a.T == 1 ? 4 : 6; }
 template <class A>
 __device__ __forceinline__ int ll_waves(const A& a, int words) {
   return words <= 32 * 64 * copy_w0(a) ? copy_w0(a) : kPersistThreads / 64;
@@ -904,8 +899,9 @@ template <bool SMALL, class A>
 __device__ __forceinline__ void shared_gu_item(const A& a, lds_cptr wbase, const float* x, int item,
                                                PersistLds& L, uint32_t flag = 0) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
-  const int rw = wave >> 2, qtr = wave & 3;
-  const int hq = a.H / 4;
+  const int rows = sh_rows<SMALL>(a), wpr = (kPersistThreads / 64) / rows;   // waves per row
+  const int rw = wave / wpr, qtr = wave % wpr;
+  const int hq = a.H / wpr;
   const int T = a.T;
   const uint32_t row = (uint32_t)a.H * 2;
   lds_cptr gsrc = wbase + (2 * rw) * row;
@@ -935,14 +931,14 @@ __device__ __forceinline__ void shared_gu_item(const A& a, lds_cptr wbase, const
     }
   }
   __syncthreads();
-  // combine the 4 quarter-row partials in a fixed order
-  for (int q = qs_tid(); q < kSharedItemRows * T; q += kPersistThreads) {
+  // combine the per-wave partials of a row in a fixed order
+  for (int q = qs_tid(); q < rows * T; q += kPersistThreads) {
     const int r = q / T, t = q % T;
-    const int ff = item * kSharedItemRows + r;
+    const int ff = item * rows + r;
     float g = 0.f, u = 0.f;
-    for (int w4 = 0; w4 < 4; ++w4) {
-      g += L.sred[((r * 4 + w4) * T + t) * 2];
-      u += L.sred[((r * 4 + w4) * T + t) * 2 + 1];
+    for (int w4 = 0; w4 < wpr; ++w4) {
+      g += L.sred[((r * wpr + w4) * T + t) * 2];
+      u += L.sred[((r * wpr + w4) * T + t) * 2 + 1];
     }
     const float rs = SMALL ? (float)L.rinv[t] : (float)cldd(&a.rinv[t]);
     const float v = silu_mul(g * rs, u * rs);
@@ -956,13 +952,13 @@ template <bool SMALL, class A>
 __device__ __forceinline__ void shared_items(const A& a, const LayerPtrs& Lp, const float* x,
                                              PersistLds& L, uint32_t flag = 0) {
   const int npf = shared_pf_count<SMALL>(a);
-  const uint32_t off = shared_off<SMALL>(a), item_b = shared_item_bytes(a);
+  const uint32_t off = shared_off<SMALL>(a), item_b = shared_item_bytes<SMALL>(a);
   int j = 0;
-  for (int it = blockIdx.x; it < n_shared_items(a); it += a.G, ++j) {
+  for (int it = blockIdx.x; it < n_shared_items<SMALL>(a); it += a.G, ++j) {
     uint32_t slot = off + (uint32_t)j * item_b;
     if (j >= npf) {      // not prefetched: copy into the first slot (already consumed)
       slot = off;
-      stage_now([&](int w, int n) { copy_shared_item(a, Lp, L.pfb + off, it, w, n); });
+      stage_now([&](int w, int n) { copy_shared_item<SMALL>(a, Lp, L.pfb + off, it, w, n); });
     }
     shared_gu_item<SMALL>(a, L.pfb + slot, x, it, L, flag);
   }
@@ -1100,14 +1096,23 @@ __device__ __forceinline__ void group_one_token(const A& a, PersistLds& L) {
 }
 
 // E <= 256: one wave per token, no block barrier before the last.  Lane l
-// holds experts 4l..4l+3; a lane pair is a group of 8.  The k-th largest
-// group maximum is found with one broadcast per group, the candidates are
-// compacted in index order with a prefix sum, and each is ranked against all
-// of them on the order-preserving integer images of their fp64 logits --
-// since candidates sit in index order, a tie goes to the lower position.
-// (L.kf is not used.)
+// holds experts 4l..4l+3 and their fp32 selection keys (order-preserving
+// integer images of the fp32 roundings of the fp64 logits).  A lane quad is
+// a group of 16 experts: the k-th largest of the 16 group maxima, tau,
+// bounds every top-k key from below (k groups hold a key >= tau, and a
+// larger key means a larger logit).  The experts with key >= tau -- about
+// k + 3 at these shapes -- are compacted in index order and each ranks
+// itself against all of them on the order-preserving images of their fp64
+// logits, ties to the lower position, i.e. the lower expert id.  The picks
+// are then moved to the lane of their rank (one crossbar permute) so that
+// the weights are summed in rank order, as the batched kernel does.
 template <class A>
 __device__ __forceinline__ void topk_small_lds(const A& a, int layer_i, PersistLds& L);
+
+__device__ __forceinline__ uint32_t f32_ordkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
 
 template <class A>
 __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& L) {
@@ -1116,63 +1121,125 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
     return;
   }
   const int lane = qs_tid() & 63, wave = qs_tid() >> 6;
-  const int E = a.E, k = a.k, T = a.T, NG = kf_stride(E) / 8;
+  const int E = a.E, k = a.k, T = a.T;
   if (wave < T) {
     const int t = wave, e0 = 4 * lane;
+    QS_LDS double* lg = L.lg + t * E;
     double v[4];
-    float key[4];
+    uint32_t ku[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[j] = e0 + j < E ? nan_low(L.lg[t * E + e0 + j]) : -INFINITY;
-      key[j] = e0 + j < E ? (float)v[j] : -INFINITY;
+      v[j] = e0 + j < E ? nan_low(lg[e0 + j]) : -INFINITY;
+      ku[j] = e0 + j < E ? f32_ordkey((float)v[j]) : 0u;   // padding below every real key
     }
-    float g = fmaxf(fmaxf(key[0], key[1]), fmaxf(key[2], key[3]));
-    g = fmaxf(g, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(g), 0xB1, 0xF, 0xF, false)));  // quad_perm [1,0,3,2]
-    float tau = -INFINITY;     // fewer than k groups: every expert is a candidate
-    if (NG >= k) {
-      int c = 0;
-      for (int j = 0; j < NG; ++j) c += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 2 * j)) > g;
-      const float q = (lane & 1) == 0 && (lane >> 1) < NG && c < k ? g : INFINITY;
-      tau = -bfly_max<6>(-q);
-    }
+    uint32_t g = max(max(ku[0], ku[1]), max(ku[2], ku[3]));
+    g = max(g, partner_u32<0>(g));
+    g = max(g, partner_u32<1>(g));
+    // the 16 group maxima through LDS (the head of this token's candidate
+    // row, rewritten only after these reads: a wave's LDS accesses are in order)
+    QS_LDS int* cd = L.cand + t * E;
+    QS_LDS uint32_t* gm = (QS_LDS uint32_t*)cd;
+    if ((lane & 3) == 0 && e0 < E) gm[lane >> 2] = g;
+    const int ng = (E + 15) >> 4;
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < ng) c += gm[j] > g ? 1 : 0;
+    // fewer than k groups: tau = 0, every expert is a candidate
+    uint32_t tau = c < k && e0 < E ? g : 0xFFFFFFFFu;
+    tau = min(tau, partner_u32<2>(tau));
+    tau = min(tau, partner_u32<3>(tau));
+    tau = min(tau, partner_u32<4>(tau));
+    tau = min(tau, partner_u32<5>(tau));
+    if (ng < k) tau = 0;
     bool p[4];
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      p[j] = e0 + j < E && key[j] >= tau;
+      p[j] = e0 + j < E && ku[j] >= tau;
       cnt += p[j];
     }
     const int incl = wave_incl_scan(cnt);
     const int m = __builtin_amdgcn_readlane(incl, 63);
-    QS_LDS int* cd = L.cand + t * E;
+    // candidates in index order: ids in cd, fp64 keys over this token's
+    // logit row (read into registers above)
+    QS_LDS uint64_t* ck = (QS_LDS uint64_t*)lg;
     int pos = incl - cnt;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (p[j]) cd[pos++] = e0 + j;
-    // (the wave's own LDS writes are visible to its later reads)
-    const QS_LDS double* lg = L.lg + t * E;
-    for (int i0 = 0; i0 < m; i0 += 64) {
-      const int i = i0 + lane;
-      const int e = i < m ? cd[i] : 0;
-      const uint64_t K = f64_ord(nan_low(lg[e]));
+      if (p[j]) {
+        cd[pos] = e0 + j;
+        ck[pos] = f64_ord(v[j]);
+        ++pos;
+      }
+    if (m <= 64) {
+      const bool live = lane < m;
+      const uint64_t K = live ? ck[lane] : 0;
+      const int e = live ? cd[lane] : 0;
       int r = 0;
-      for (int j0 = 0; j0 < m; j0 += 64) {
-        uint64_t Kj = K;
-        if (j0 != i0) Kj = f64_ord(nan_low(lg[j0 + lane < m ? cd[j0 + lane] : 0]));
-        const int nj = m - j0 < 64 ? m - j0 : 64;
-        for (int j = 0; j < nj; ++j) {
-          const uint64_t K2 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(Kj >> 32), j) << 32) |
-                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)Kj, j);
-          r += (K2 > K || (K2 == K && j0 + j < i)) ? 1 : 0;
+      for (int j0 = 0; j0 < m; j0 += 16) {
+        uint64_t w[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) w[jj] = j0 + jj < m ? ck[j0 + jj] : 0;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int j = j0 + jj;
+          r += (j < m && (w[jj] > K || (w[jj] == K && j < lane))) ? 1 : 0;
         }
       }
-      if (i < m && r < k) {
-        L.ids[t * k + r] = e;
-        L.sv[t * k + r] = f64_unord(K);
+      const bool sel = live && r < k;
+      // move each pick to the lane of its rank: expert, logit image, and its
+      // position among the picks in ascending expert order
+      const int u = wave_incl_scan(sel ? 1 : 0) - 1;
+      const int dst = (sel ? r : 63) * 4;
+      const int er = __builtin_amdgcn_ds_permute(dst, e);
+      const int ur = __builtin_amdgcn_ds_permute(dst, u);
+      const int khi = __builtin_amdgcn_ds_permute(dst, (int)(K >> 32));
+      const int klo = __builtin_amdgcn_ds_permute(dst, (int)(uint32_t)K);
+      const double vr = f64_unord(((uint64_t)(uint32_t)khi << 32) | (uint32_t)klo);
+      const uint64_t k0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(khi, 0) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane(klo, 0);
+      const float z = lane < k ? __expf((float)(vr - f64_unord(k0))) : 0.f;
+      const float sum = bfly_sum<6>(z);
+      if (lane < k) {
+        const float w = __fdividef(z, sum);
+        L.ids[t * k + lane] = er;
+        L.wl[t * k + lane] = w;
+        if (blockIdx.x == 0) {
+          const size_t o = (size_t)layer_i * a.T * k + t * k + lane;
+          if (a.ids_out) a.ids_out[o] = er;
+          if (a.w_out) a.w_out[o] = w;
+        }
+        if (T == 1) {       // the grouping of one token's k distinct experts
+          L.act[ur] = er;
+          L.aoff[ur] = ur;
+          L.pairs[ur] = lane;
+          L.tok_order[ur] = ur;
+          L.cw[ur] = w;
+        }
       }
+      if (T == 1 && lane == 0) {
+        *L.nact = k;
+        L.aoff[k] = k;
+      }
+    } else {
+      // many exact ties at the threshold: rank in chunks
+      for (int i0 = 0; i0 < m; i0 += 64) {
+        const int i = i0 + lane;
+        const uint64_t K = i < m ? ck[i] : 0;
+        int r = 0;
+        for (int j = 0; j < m; ++j) {
+          const uint64_t w = ck[j];
+          r += (w > K || (w == K && j < i)) ? 1 : 0;
+        }
+        if (i < m && r < k) {
+          L.ids[t * k + r] = cd[i];
+          L.sv[t * k + r] = f64_unord(K);
+        }
+      }
+      topk_weights(a, layer_i, t, L);
+      if (T == 1) group_one_token(a, L);
     }
-    topk_weights(a, layer_i, t, L);
-    if (T == 1) group_one_token(a, L);
   }
   __syncthreads();
 }
@@ -1487,95 +1554,72 @@ __device__ __forceinline__ void x_chunk(const A& a, const PersistLds& L, int t, 
   }
 }
 
-// Routed gate/up tile from LDS: rows [f0, f0+16) of expert e for every
-// token of its bucket; each 64-weight chunk is decoded once and applied to
-// the tokens one at a time.  SwiGLU outputs are quantised per 16 rows.
-template <int FMT, bool SMALL, class A>
-__device__ __forceinline__ void routed_gu_tile(const A& a, lds_cptr tile, int u, int f0, PersistLds& L,
-                                               uint32_t flag = 0) {
-  const int p0 = L.aoff[u], n = L.aoff[u + 1] - p0;
-  const int nbh = a.H / kBlockW;
-  const int nch = a.H / kChunkW;
-  const int lpr = lanes_per_row(nch);
-  const int cpl = nch / lpr;
-  const int slots = kPersistThreads / lpr;
-  const int slot = qs_tid() / lpr, j = qs_tid() % lpr;
-  constexpr bool q2k = FMT == 1;
-  const TileLds tl = tile_lds(a);
-  lds_cptr gq = tile, uq_ = tile + tl.qb, gs = tile + tl.s, us = tile + tl.s + tl.sb, gd = tile + tl.d,
-           ud = tile + tl.d + tl.db;
-#pragma unroll 1
-  for (int r = slot; r < kGateTile; r += slots) {
-#pragma unroll 1
-    for (int tg = 0; tg < n; tg += 4) {
-      float gacc[4] = {0.f, 0.f, 0.f, 0.f}, uacc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-      for (int cc = 0; cc < cpl; ++cc) {
-        const int ch = j + cc * lpr;
-        const uint32_t blk = (uint32_t)r * nbh + ch / 4;
-        const int c = ch & 3;
-        uint32_t gw[16], uw[16];
-        uint32_t gsc, usc, gdd, udd;
-        const uint4 gv = ld16(gq + blk * 64 + c * 16);
-        const uint4 uv = ld16(uq_ + blk * 64 + c * 16);
-        if (q2k) {
-          gsc = ld4(gs + blk * 16 + c * 4);
-          usc = ld4(us + blk * 16 + c * 4);
-          gdd = ld4(gd + blk * 4);
-          udd = ld4(ud + blk * 4);
-          gw[0] = gv.x; gw[1] = gv.y; gw[2] = gv.z; gw[3] = gv.w;
-          uw[0] = uv.x; uw[1] = uv.y; uw[2] = uv.z; uw[3] = uv.w;
-        } else {
-          gsc = ld1(gs + blk * 4 + c);
-          usc = ld1(us + blk * 4 + c);
-          gdd = ld2(gd + blk * 2);
-          udd = ld2(ud + blk * 2);
-          cb2_decode_dword(L.tab, gv.x, gw[0], gw[1], gw[2], gw[3]);
-          cb2_decode_dword(L.tab, gv.y, gw[4], gw[5], gw[6], gw[7]);
-          cb2_decode_dword(L.tab, gv.z, gw[8], gw[9], gw[10], gw[11]);
-          cb2_decode_dword(L.tab, gv.w, gw[12], gw[13], gw[14], gw[15]);
-          cb2_decode_dword(L.tab, uv.x, uw[0], uw[1], uw[2], uw[3]);
-          cb2_decode_dword(L.tab, uv.y, uw[4], uw[5], uw[6], uw[7]);
-          cb2_decode_dword(L.tab, uv.z, uw[8], uw[9], uw[10], uw[11]);
-          cb2_decode_dword(L.tab, uv.w, uw[12], uw[13], uw[14], uw[15]);
-        }
-        // one token at a time (its x chunk is 40 registers); the decoded
-        // weights stay live across the four tokens
-#pragma unroll 1
-        for (int tt = 0; tt < 4; ++tt) {
-          if (tg + tt >= n) break;
-          const int t = L.pairs[p0 + tg + tt] / a.k;
-          uint32_t xh[16], xl[16];
-          float xs[4];
-          int xa[4];
-          x_chunk<SMALL>(a, L, t, ch, xh, xl, xs, xa);
-          float gp, up;
-          if (q2k) {
-            const uint32_t g4[4] = {gw[0], gw[1], gw[2], gw[3]}, u4[4] = {uw[0], uw[1], uw[2], uw[3]};
-            gp = q2k_chunk_dot(g4, gsc, half_to_f32(gdd & 0xFFFFu), half_to_f32(gdd >> 16), xh, xl, xs, xa);
-            up = q2k_chunk_dot(u4, usc, half_to_f32(udd & 0xFFFFu), half_to_f32(udd >> 16), xh, xl, xs, xa);
-          } else {
-            gp = half_to_f32(gdd) * xs[0] * (float)cb2_chunk_dot(gw, xh, xl, gsc);
-            up = half_to_f32(udd) * xs[0] * (float)cb2_chunk_dot(uw, xh, xl, usc);
-          }
+// Routed gate/up tiles of the small-batch kernel, streamed from HBM into
+// registers.  The workgroup's tiles are items b, b+G, ... of the (active
+// expert, 16-row tile) list.  In a tile, thread (slot, j) takes rows slot,
+// slot + slots, ... and chunks j + cc*lpr of each row (the lane-per-chunk
+// layout of every gate/up GEMV here), so each 64-weight chunk is decoded
+// once and applied to every token of the bucket; a row's lanes then sum by
+// butterfly.  The chunks of the first kGuWin tiles are requested as soon as
+// the grouping is known, and each computed tile's registers are refilled
+// with the tile kGuWin ahead, so no tile waits for its own round trip.
+constexpr int kGuWin = 3;      // tiles in flight per workgroup
+constexpr int kGuUnits = 2;    // (row, chunk) units per thread and tile: H <= 4096
+
+struct GuChunk {
+  uint4 gq, uq;                // 16 code bytes of the gate and up chunk
+  uint32_t gs, us;             // codebook: the block's 4 scale bytes; Q2_K: the chunk's 4 scale/min bytes
+  uint32_t gd, ud;             // codebook: d; Q2_K: d | dmin << 16
+};
+struct GuTile {
+  GuChunk c[kGuUnits];
+};
+
+template <class A>
+__device__ __forceinline__ int gu_tiles_mine(const A& a, const PersistLds& L) {
+  return my_count(a, *L.nact * (a.F / kGateTile));
+}
+
+template <int FMT, class A>
+__device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, const PersistLds& L, int m,
+                                             GuTile& t) {
+  const int tiles = a.F / kGateTile, nch = a.H / kChunkW, lpr = lanes_per_row(nch), cpl = nch / lpr;
+  const int slots = kPersistThreads / lpr, slot = qs_tid() / lpr, j = qs_tid() % lpr;
+  const int item = (int)blockIdx.x + m * a.G;
+  const int u = item / tiles, f0 = (item % tiles) * kGateTile;
+  const int e = L.act[u];
+  const uint32_t nbh = a.H / kBlockW;
+  const size_t nblk = (size_t)a.F * nbh;
+  const MatPlanes pl = FMT == 1 ? q2k_planes(nblk) : cb2_planes(nblk);
+  const uint8_t* g = Lp.gate + (size_t)e * a.gu_stride;
+  const uint8_t* up = Lp.up + (size_t)e * a.gu_stride;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            gacc[i] = i == tt ? gacc[i] + gp : gacc[i];
-            uacc[i] = i == tt ? uacc[i] + up : uacc[i];
-          }
-        }
-      }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (tg + tt >= n) continue;
-        const float g = bfly_sum_dyn(gacc[tt], lpr);
-        const float uu = bfly_sum_dyn(uacc[tt], lpr);
-        if (j == 0) L.ga[(tg + tt) * kGateTile + r] = silu_mul(g, uu);
-      }
+  for (int i = 0; i < kGuUnits; ++i) {
+    const int r = slot + (i / cpl) * slots, ch = j + (i % cpl) * lpr;
+    if (r >= kGateTile || i >= ((kGateTile - 1 - slot) / slots + 1) * cpl) continue;
+    const size_t blk = (size_t)(f0 + r) * nbh + ch / 4;
+    const int c = ch & 3;
+    GuChunk& w = t.c[i];
+    w.gq = *(const uint4*)(g + pl.q + blk * 64 + c * 16);
+    w.uq = *(const uint4*)(up + pl.q + blk * 64 + c * 16);
+    if (FMT == 1) {
+      w.gs = *(const uint32_t*)(g + pl.s + blk * 16 + c * 4);
+      w.us = *(const uint32_t*)(up + pl.s + blk * 16 + c * 4);
+      w.gd = *(const uint32_t*)(g + pl.d + blk * 4);
+      w.ud = *(const uint32_t*)(up + pl.d + blk * 4);
+    } else {
+      w.gs = *(const uint32_t*)(g + pl.s + blk * 4);
+      w.us = *(const uint32_t*)(up + pl.s + blk * 4);
+      w.gd = *(const uint16_t*)(g + pl.d + blk * 2);
+      w.ud = *(const uint16_t*)(up + pl.d + blk * 2);
     }
   }
-  __syncthreads();
-  // quantise each bucket token's 16 outputs: 16 lanes per token
+}
+
+// Quantise the 16 SwiGLU outputs of each bucket token (16 lanes per token)
+// and store them as flagged words.
+template <class A>
+__device__ __forceinline__ void gu_tile_store(const A& a, int p0, int n, int f0, PersistLds& L, uint32_t flag) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
   for (int tb = wave * 4; tb < n; tb += nw * 4) {
     const int tt = tb + (lane >> 4), r = lane & 15;
@@ -1594,50 +1638,124 @@ __device__ __forceinline__ void routed_gu_tile(const A& a, lds_cptr tile, int u,
 #pragma unroll
         for (int i = 0; i < 4; ++i) split_limbs(L.qtmp[tt * kGateTile + 4 * i + r], h[i], l[i]);
         const size_t wi = (size_t)pair * (a.F / 4) + f0 / 4 + r;
-        if (SMALL) {
-          ll_store(a.ll_a + wi, pack4(h[0], h[1], h[2], h[3]), flag);
-          ll_store(a.ll_a + ll_al(a) + wi, pack4(l[0], l[1], l[2], l[3]), flag);
-        } else {
-          cst(&a.ah[wi], pack4(h[0], h[1], h[2], h[3]));
-          cst(&a.al[wi], pack4(l[0], l[1], l[2], l[3]));
-        }
+        ll_store(a.ll_a + wi, pack4(h[0], h[1], h[2], h[3]), flag);
+        ll_store(a.ll_a + ll_al(a) + wi, pack4(l[0], l[1], l[2], l[3]), flag);
       }
       if (r == 0) {
         const size_t si = (size_t)pair * (a.F / kSubW) + f0 / kSubW;
-        if (SMALL) {
-          ll_store(a.ll_a + ll_as(a) + si, __float_as_uint(ldexpf(1.0f, ex - kFixedBits)), flag);
-          ll_store(a.ll_a + ll_aa(a) + si, (uint32_t)s, flag);
-        } else {
-          cstf(&a.as[si], ldexpf(1.0f, ex - kFixedBits));
-          csti(&a.aa[si], s);
-        }
+        ll_store(a.ll_a + ll_as(a) + si, __float_as_uint(ldexpf(1.0f, ex - kFixedBits)), flag);
+        ll_store(a.ll_a + ll_aa(a) + si, (uint32_t)s, flag);
       }
     }
   }
-  // (also keeps the other waves' copies and reads behind this tile's stores)
+  // (also keeps the other waves' later reads of L.ga behind these stores)
   __syncthreads();
 }
 
-// Routed tiles of this workgroup: the first ones were copied ahead, the rest
-// are copied into the first slot on demand.
-template <int FMT, bool SMALL, class A>
-__device__ __forceinline__ void routed_tiles(const A& a, const LayerPtrs& Lp, PersistLds& L, uint32_t flag = 0) {
-  const int tiles = a.F / kGateTile;
-  const int na = *L.nact;
-  const int base = gu_items_base<SMALL>(a);
-  const int npf = tile_pf_count<SMALL>(a, na);
-  const uint32_t off = tile_off<SMALL>(a), tb = gu_tile_bytes(a);
-  int j = 0;
-  for (int it = (int)blockIdx.x + my_count(a, base) * a.G; it < base + na * tiles;
-       it += a.G, ++j) {
-    const int r = it - base;
-    const int u = r / tiles, f0 = (r % tiles) * kGateTile;
-    uint32_t slot = off + (uint32_t)j * tb;
-    if (j >= npf) {
-      slot = off;
-      stage_now([&](int w, int n) { copy_tile(a, Lp, L.pfb + off, L.act[u], f0, w, n); });
+// Tile m of this workgroup from its registers: SwiGLU of its 16 rows for
+// every token of the bucket (at most kSmallT), quantised per 16 rows and
+// stored as flagged words.
+template <int FMT, class A>
+__device__ __forceinline__ void gu_tile_compute(const A& a, const GuTile& t, int m, PersistLds& L, uint32_t flag) {
+  const int tiles = a.F / kGateTile, nch = a.H / kChunkW, lpr = lanes_per_row(nch), cpl = nch / lpr;
+  const int slots = kPersistThreads / lpr, slot = qs_tid() / lpr, j = qs_tid() % lpr;
+  const int item = (int)blockIdx.x + m * a.G;
+  const int u = item / tiles, f0 = (item % tiles) * kGateTile;
+  const int p0 = L.aoff[u], n = L.aoff[u + 1] - p0;
+  constexpr bool q2k = FMT == 1;
+  float gacc[4] = {0.f, 0.f, 0.f, 0.f}, uacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kGuUnits; ++i) {
+    const int r = slot + (i / cpl) * slots, ch = j + (i % cpl) * lpr, cc = i % cpl;
+    if (r >= kGateTile || i >= ((kGateTile - 1 - slot) / slots + 1) * cpl) continue;
+    if (cc == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) gacc[q] = uacc[q] = 0.f;
     }
-    routed_gu_tile<FMT, SMALL>(a, L.pfb + slot, u, f0, L, flag);
+    const GuChunk& w = t.c[i];
+    const int c = ch & 3;
+    uint32_t gw[16], uw[16];
+    uint32_t gsc, usc;
+    if (q2k) {
+      gsc = w.gs;
+      usc = w.us;
+      gw[0] = w.gq.x; gw[1] = w.gq.y; gw[2] = w.gq.z; gw[3] = w.gq.w;
+      uw[0] = w.uq.x; uw[1] = w.uq.y; uw[2] = w.uq.z; uw[3] = w.uq.w;
+    } else {
+      gsc = (w.gs >> (8 * c)) & 0xFFu;
+      usc = (w.us >> (8 * c)) & 0xFFu;
+      cb2_decode_dword(L.tab, w.gq.x, gw[0], gw[1], gw[2], gw[3]);
+      cb2_decode_dword(L.tab, w.gq.y, gw[4], gw[5], gw[6], gw[7]);
+      cb2_decode_dword(L.tab, w.gq.z, gw[8], gw[9], gw[10], gw[11]);
+      cb2_decode_dword(L.tab, w.gq.w, gw[12], gw[13], gw[14], gw[15]);
+      cb2_decode_dword(L.tab, w.uq.x, uw[0], uw[1], uw[2], uw[3]);
+      cb2_decode_dword(L.tab, w.uq.y, uw[4], uw[5], uw[6], uw[7]);
+      cb2_decode_dword(L.tab, w.uq.z, uw[8], uw[9], uw[10], uw[11]);
+      cb2_decode_dword(L.tab, w.uq.w, uw[12], uw[13], uw[14], uw[15]);
+    }
+    // one token at a time (its x chunk is 40 registers); the decoded
+    // weights stay live across the tokens
+#pragma unroll 1
+    for (int tt = 0; tt < 4; ++tt) {
+      if (tt >= n) break;
+      const int tok = L.pairs[p0 + tt] / a.k;
+      uint32_t xh[16], xl[16];
+      float xs[4];
+      int xa[4];
+      x_chunk<true>(a, L, tok, ch, xh, xl, xs, xa);
+      float gp, up;
+      if (q2k) {
+        const uint32_t g4[4] = {gw[0], gw[1], gw[2], gw[3]}, u4[4] = {uw[0], uw[1], uw[2], uw[3]};
+        gp = q2k_chunk_dot(g4, gsc, half_to_f32(w.gd & 0xFFFFu), half_to_f32(w.gd >> 16), xh, xl, xs, xa);
+        up = q2k_chunk_dot(u4, usc, half_to_f32(w.ud & 0xFFFFu), half_to_f32(w.ud >> 16), xh, xl, xs, xa);
+      } else {
+        gp = half_to_f32(w.gd) * xs[0] * (float)cb2_chunk_dot(gw, xh, xl, gsc);
+        up = half_to_f32(w.ud) * xs[0] * (float)cb2_chunk_dot(uw, xh, xl, usc);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        gacc[q] = q == tt ? gacc[q] + gp : gacc[q];
+        uacc[q] = q == tt ? uacc[q] + up : uacc[q];
+      }
+    }
+    if (cc == cpl - 1) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (tt >= n) continue;
+        const float g = bfly_sum_dyn(gacc[tt], lpr);
+        const float uu = bfly_sum_dyn(uacc[tt], lpr);
+        if (j == 0) L.ga[tt * kGateTile + r] = silu_mul(g, uu);
+      }
+    }
+  }
+  __syncthreads();
+  QS_STAMP2(16);
+  gu_tile_store(a, p0, n, f0, L, flag);
+}
+
+// Tiles [0, kGuWin) of this workgroup are requested by gu_tiles_issue; this
+// computes every tile and refills each buffer with the tile kGuWin ahead.
+template <int FMT, class A>
+__device__ __forceinline__ void gu_tiles_issue(const A& a, const LayerPtrs& Lp, const PersistLds& L,
+                                               GuTile (&b)[kGuWin]) {
+  const int n = gu_tiles_mine(a, L);
+#pragma unroll
+  for (int i = 0; i < kGuWin; ++i)
+    if (i < n) gu_tile_load<FMT>(a, Lp, L, i, b[i]);
+}
+
+template <int FMT, class A>
+__device__ __forceinline__ void gu_tiles_run(const A& a, const LayerPtrs& Lp, PersistLds& L, GuTile (&b)[kGuWin],
+                                             uint32_t flag) {
+  const int n = gu_tiles_mine(a, L);
+#pragma unroll 1
+  for (int m0 = 0; m0 < n; m0 += kGuWin) {
+#pragma unroll
+    for (int i = 0; i < kGuWin; ++i) {
+      if (m0 + i >= n) break;
+      gu_tile_compute<FMT>(a, b[i], m0 + i, L, flag);
+      if (m0 + i + kGuWin < n) gu_tile_load<FMT>(a, Lp, L, m0 + i + kGuWin, b[i]);
+    }
   }
 }
 
@@ -1757,7 +1875,7 @@ __device__ __forceinline__ void shared_down_row(const A& a, lds_cptr srow, Persi
 // `spare(w, nw)` runs once, on the waves that have no combine work of the
 // last tile.
 template <class A, class HK>
-__device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp, const float* x,
+__device__ __forceinline__ bool phase_down_small(const A& a, int li, const LayerPtrs& Lp, const float* x,
                                                  const uint64_t* xll, float* y, uint64_t* yll, uint32_t flag_a,
                                                  uint32_t flag_y, PersistLds& L, HK&& spare) {
   const int wave = qs_tid() >> 6;
@@ -1777,7 +1895,9 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
   // every pair's SwiGLU limbs and the shared SwiGLU vector -> LDS (on the
   // waves without down-row copies in flight, when the words fit them)
   if (!ll_read(a, a.ll_a, (QS_LDS uint32_t*)L.dah, ll_a_words(a), flag_a, L.llerr, ll_a_waves(a))) return false;
+  QS_STAMP(li, 11);
   wait_all_and_sync();   // the down rows copied ahead
+  QS_STAMP(li, 12);
   for (int tile = blockIdx.x; tile < n_tiles; tile += a.G) {
     const int r0 = tile * kDownRows;
     const bool first = tile == (int)blockIdx.x;
@@ -1796,9 +1916,11 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
         });
       }
       for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, base + (uint32_t)(u - u0) * pe, u, L);
+      QS_STAMP2(23);
       if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, L.sdr + (uint32_t)wave * a.Fs * 2, L);
     }
     __syncthreads();
+    QS_STAMP(li, 13);
     // wave 0 has the combine work (T * kDownRows <= 64 words)
     if (tile + a.G >= n_tiles && wave >= copy_w0(a)) spare(wave - copy_w0(a), kPersistThreads / 64 - copy_w0(a));
     for (int idx = qs_tid(); idx < T * kDownRows; idx += kPersistThreads) {
@@ -1817,6 +1939,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, const LayerPtrs& Lp
       if (yll) ll_store(yll + (size_t)t * a.H + h, __float_as_uint(acc), flag_y);
       else cstf(&y[(size_t)t * a.H + h], acc);
     }
+    QS_STAMP(li, 14);
     __syncthreads();     // L.o and L.sh are rewritten by the next tile
   }
   if ((int)blockIdx.x >= n_tiles && wave >= copy_w0(a)) spare(wave - copy_w0(a), kPersistThreads / 64 - copy_w0(a));
@@ -1847,26 +1970,37 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     const uint64_t* xll = li == 0 ? nullptr : ((li - 1) & 1 ? a.llx1 : a.llx0);
     uint64_t* yll = more ? (li & 1 ? a.llx1 : a.llx0) : nullptr;
     // ---- R: x -> LDS, RMS scales, router, shared gate/up
+    QS_STAMP(li, 0);
     if (li == 0) dma_to_lds<kCoherent>(a.x_in, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
     else if (!ll_read(a, xll, (QS_LDS uint32_t*)L.ax, a.T * a.H, fl, L.llerr, ll_waves(a, a.T * a.H))) return;
+    QS_STAMP(li, 1);
     wait_all_and_sync();   // (and this layer's router rows and shared items)
+    QS_STAMP(li, 2);
     if ((int)blockIdx.x >= router_groups(a)) token_rinv<true>(a, L, a.x_in, 0, a.T);
     phase_router<true>(a, Lp, a.x_in, L, fl + 1);   // ends with a block barrier
+    QS_STAMP(li, 3);
     shared_items<true>(a, Lp, a.x_in, L, fl + 2);
+    QS_STAMP(li, 4);
     // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
     if (!ll_read(a, a.ll_lg, (QS_LDS uint32_t*)L.lg, 2 * a.T * a.E, fl + 1, L.llerr)) return;
+    QS_STAMP(li, 5);
     topk_small(a, li, L);   // (groups one token itself)
     if (a.T > 1) group_small(a, L);
-    // tiles copied by waves [tile_w0, 8) while the others quantise x
-    if (wave >= tile_w0(a)) pf_tiles<true>(a, Lp, L, wave - tile_w0(a), nw - tile_w0(a));
+    QS_STAMP(li, 6);
+    // the routed gate/up tiles' chunks are requested at once (registers);
+    // meanwhile x becomes fixed-point limbs
+    GuTile gut[kGuWin];
+    gu_tiles_issue<FMT>(a, Lp, L, gut);
     {
       const int nb = a.H / kBlockW;
-      if (wave < tile_w0(a))
-        for (int u = wave; u < a.T * nb; u += tile_w0(a)) quant_x_wave<true>(a, a.x_in, u / nb, u % nb, L);
+      for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, a.x_in, u / nb, u % nb, L);
     }
-    wait_all_and_sync();
+    QS_STAMP(li, 7);
+    __syncthreads();
+    QS_STAMP(li, 8);
     // ---- GU
-    routed_tiles<FMT, true>(a, Lp, L, fl + 2);
+    gu_tiles_run<FMT>(a, Lp, L, gut, fl + 2);
+    QS_STAMP(li, 9);
     // region B (unused during GU) receives the down rows of the active
     // experts, from the waves that do not poll the SwiGLU words
     {
@@ -1875,7 +2009,8 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     }
     // ---- D; region A is free: the next layer's router rows and shared
     // items are issued beside the combine
-    if (!phase_down_small(a, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L, [&](int w, int n) {
+    QS_STAMP(li, 10);
+    if (!phase_down_small(a, li, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L, [&](int w, int n) {
           if (!more) return;
           pf_router_and_shared<true>(a, Ln, L, w, n);
           // the shared down rows are no longer read by this layer
@@ -1883,6 +2018,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
             copy_sd_rows(a, Ln, L.sdr, blockIdx.x * kDownRows, w, n);
         }))
       return;
+    QS_STAMP(li, 15);
     Lp = Ln;
   }
 }
