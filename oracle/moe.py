@@ -115,14 +115,36 @@ def dequant_cb2(blocks: np.ndarray, codebook: np.ndarray) -> np.ndarray:
     return w.astype(np.float32).reshape(*lead, 256)
 
 
+# 8-bit block, 34 bytes per 32 weights (the Q8_0 type the pages use for the
+# tensors they keep at 8 bits -- QuarkStar README, "Model Weights" (Q8 rest);
+# DwarfStar page, "Distributed Inference" (Q8 shared experts)):
+#   bytes 0..1   d (fp16)
+#   bytes 2..33  qs[32]: int8 codes
+#   w_j = d * qs[j]
+
+
+def dequant_q8(blocks: np.ndarray) -> np.ndarray:
+    """Raw 8-bit blocks [..., 34] uint8 -> fp32 weights [..., 32] (exact:
+    an 11-bit significand times an 8-bit integer fits fp32)."""
+    blk = np.asarray(blocks, dtype=np.uint8)
+    lead = blk.shape[:-1]
+    blk = blk.reshape(-1, 34)
+    d = fp16_bits_to_f64(blk[:, 0].astype(np.uint16) | (blk[:, 1].astype(np.uint16) << 8))[:, None]
+    q = blk[:, 2:34].view(np.int8).astype(np.float64)
+    return (d * q).astype(np.float32).reshape(*lead, 32)
+
+
 def dequant_matrix(raw: np.ndarray, fmt: str, codebook=None) -> np.ndarray:
-    """Raw matrix [rows][cols/256][block bytes] -> fp32 [rows][cols]."""
+    """Raw matrix [rows][cols/block][block bytes] -> fp32 [rows][cols]
+    (blocks of 256 weights for q2k/cb2, of 32 for q8)."""
     raw = np.asarray(raw, dtype=np.uint8)
     rows, nb = raw.shape[0], raw.shape[1]
     if fmt == "q2k":
         w = dequant_q2k(raw)
     elif fmt == "cb2":
         w = dequant_cb2(raw, codebook)
+    elif fmt == "q8":
+        return dequant_q8(raw).reshape(rows, nb * 32)
     else:
         raise ValueError(fmt)
     return w.reshape(rows, nb * 256)
@@ -230,8 +252,12 @@ class Layer:
     def shared(self):
         if "shared" not in self._cache:
             lw = self.lw
-            self._cache["shared"] = tuple(
-                bf16_bits_to_f64(m) for m in (lw.shared_gate, lw.shared_up, lw.shared_down))
+            if getattr(self.wl, "shared_format", "bf16") == "q8":
+                self._cache["shared"] = tuple(
+                    dequant_matrix(m, "q8").astype(np.float64) for m in (lw.shared_gate, lw.shared_up, lw.shared_down))
+            else:
+                self._cache["shared"] = tuple(
+                    bf16_bits_to_f64(m) for m in (lw.shared_gate, lw.shared_up, lw.shared_down))
         return self._cache["shared"]
 
 

@@ -32,6 +32,9 @@ import numpy as np
 Q2K_BLOCK_BYTES = 84
 CB2_BLOCK_BYTES = 70
 BLOCK_WEIGHTS = 256
+# 8-bit shared-expert blocks: 32 weights, fp16 scale + 32 int8 codes
+Q8_BLOCK_BYTES = 34
+Q8_BLOCK_WEIGHTS = 32
 
 # Tensor ids used in the seed key.
 T_ROUTER, T_BIAS, T_GATE, T_UP, T_DOWN, T_SGATE, T_SUP, T_SDOWN, T_X, T_CODEBOOK = range(10)
@@ -54,6 +57,7 @@ class Workload:
     tokens: Tuple[int, ...] = (1,)
     zipf_s: Optional[float] = None
     note: str = ""
+    shared_format: str = "bf16"   # "bf16" or "q8" (8-bit blocks of 32)
 
     def block_bytes(self, fmt: str) -> int:
         return block_bytes(fmt)
@@ -69,7 +73,10 @@ class Workload:
         return self.n_experts * self.hidden * 4
 
     def shared_bytes(self) -> int:
-        return 3 * self.shared_ffn * self.hidden * 2
+        n = 3 * self.shared_ffn * self.hidden
+        if self.shared_format == "q8":
+            return n // Q8_BLOCK_WEIGHTS * Q8_BLOCK_BYTES
+        return n * 2
 
     def stored_bytes(self) -> int:
         g, u, d = self.expert_bytes()
@@ -104,6 +111,11 @@ WORKLOADS = {
     "a3b_stack40_zipf": Workload("a3b_stack40_zipf", 3, 2048, 256, 8, 512, 512, "cb2", "q2k", 40,
                                  (1, 4, 16, 64), zipf_s=1.1,
                                  note="40-layer A3B stack with shared expert, Zipf(1.1) popularity"),
+    # the same with the shared expert in 8-bit blocks (the pages run every
+    # non-routed tensor at Q8)
+    "a3b_stack40_zipf_q8": Workload("a3b_stack40_zipf_q8", 6, 2048, 256, 8, 512, 512, "cb2", "q2k", 40,
+                                    (1, 4), zipf_s=1.1, shared_format="q8",
+                                    note="40-layer A3B stack, 8-bit shared expert, Zipf(1.1) popularity"),
     # DeepSeek-V4-Flash-class large layer, 8 stacked
     "flash_stack8_zipf": Workload("flash_stack8_zipf", 4, 4096, 256, 6, 2048, 2048, "cb2", "q2k", 8,
                                   (1, 8, 32), zipf_s=1.1,
@@ -170,6 +182,15 @@ def cb2_blocks(rng: np.random.Generator, nblocks: int, out=None) -> np.ndarray:
     return raw
 
 
+def q8_blocks(rng: np.random.Generator, nblocks: int) -> np.ndarray:
+    """nblocks 8-bit blocks [nblocks][34]: d (bytes 0..1) fp16(U[0,1)*2^-11),
+    then 32 int8 codes uniform over [-128, 127]."""
+    raw = np.frombuffer(rng.bytes(nblocks * Q8_BLOCK_BYTES), dtype=np.uint8).reshape(nblocks, Q8_BLOCK_BYTES).copy()
+    u = rng.random(nblocks, dtype=np.float32) * np.float32(2.0 ** -11)
+    raw[:, 0:2] = u.astype(np.float16).view(np.uint16).view(np.uint8).reshape(nblocks, 2)
+    return raw
+
+
 def expert_tensor(wl: Workload, layer: int, tensor: int, expert: int, out=None) -> np.ndarray:
     """Raw bytes of one expert matrix, shape [rows][cols/256][block bytes]:
     gate/up are [F][H/256] blocks, down is [H][F/256] blocks."""
@@ -194,9 +215,9 @@ class LayerWeights:
     gate: np.ndarray                   # uint8 [E][F][H/256][bb]
     up: np.ndarray                     # uint8 [E][F][H/256][bb]
     down: np.ndarray                   # uint8 [E][H][F/256][bb]
-    shared_gate: Optional[np.ndarray] = None   # uint16 bf16 bits [Fs][H]
-    shared_up: Optional[np.ndarray] = None     # uint16 bf16 bits [Fs][H]
-    shared_down: Optional[np.ndarray] = None   # uint16 bf16 bits [H][Fs]
+    shared_gate: Optional[np.ndarray] = None   # bf16 bits [Fs][H], or 8-bit blocks [Fs][H/32][34]
+    shared_up: Optional[np.ndarray] = None     # the same layout as shared_gate
+    shared_down: Optional[np.ndarray] = None   # bf16 bits [H][Fs], or 8-bit blocks [H][Fs/32][34]
     experts: Tuple[int, ...] = field(default_factory=tuple)
 
 
@@ -221,7 +242,14 @@ def layer_weights(wl: Workload, layer: int, experts=None) -> LayerWeights:
         expert_tensor(wl, layer, T_UP, e, up[i])
         expert_tensor(wl, layer, T_DOWN, e, down[i])
     lw = LayerWeights(router, bias, gate, up, down, experts=ex)
-    if Fs:
+    if Fs and wl.shared_format == "q8":
+        def q8(tid, rows, cols):
+            return q8_blocks(_rng(wl.seed_id, layer, tid, 0), rows * cols // Q8_BLOCK_WEIGHTS).reshape(
+                rows, cols // Q8_BLOCK_WEIGHTS, Q8_BLOCK_BYTES)
+        lw.shared_gate = q8(T_SGATE, Fs, H)
+        lw.shared_up = q8(T_SUP, Fs, H)
+        lw.shared_down = q8(T_SDOWN, H, Fs)
+    elif Fs:
         def bf16(tid, shape):
             a = _rng(wl.seed_id, layer, tid, 0).standard_normal(shape, dtype=np.float32)
             return fp32_to_bf16_bits(a * np.float32(0.02))

@@ -50,6 +50,14 @@ def pack_cb2(d=0, s=None, idx=None, sign=None):
     return blk
 
 
+def pack_q8(d=0, q=None):
+    blk = np.zeros(34, dtype=np.uint8)
+    q = np.zeros(32, int) if q is None else np.asarray(q)
+    blk[0], blk[1] = d & 0xFF, d >> 8
+    blk[2:34] = (q.astype(np.int64) & 0xFF).astype(np.uint8)
+    return blk
+
+
 def hand_codebook():
     cb = np.ones((256, 8), dtype=np.int8)
     cb[7] = [1, 3, 5, 7, 7, 5, 3, 1]
@@ -111,6 +119,9 @@ def test_handworked_block(case):
         blk = pack_q2k(d=int(kv.get("d", "0"), 16), dmin=int(kv.get("dmin", "0"), 16),
                        sc=_indexed(kv, "sc", 16), m=_indexed(kv, "m", 16), q=_indexed(kv, "q", 256))
         w = om.dequant_q2k(blk)
+    elif fmt == "q8":
+        blk = pack_q8(d=int(kv.get("d", "0"), 16), q=_indexed(kv, "q", 32))
+        w = om.dequant_q8(blk)
     else:
         blk = pack_cb2(d=int(kv.get("d", "0"), 16), s=_indexed(kv, "s", 8),
                        idx=_indexed(kv, "idx", 32), sign=_indexed(kv, "sign", 32, 16))
@@ -124,6 +135,7 @@ def test_handworked_block(case):
 def test_golden_file_has_cases():
     cases = _parse_golden()
     assert sum(c[0] == "q2k" for c in cases) >= 8 and sum(c[0] == "cb2" for c in cases) >= 8
+    assert sum(c[0] == "q8" for c in cases) >= 6
 
 
 # ---------------------------------------------------- layout invariants ---
@@ -300,7 +312,7 @@ def _fp16_bits(v):
     return int(np.array([v], dtype=np.float16).view(np.uint16)[0])
 
 
-@pytest.mark.parametrize("fmt", ["q2k", "cb2"])
+@pytest.mark.parametrize("fmt", ["q2k", "cb2", "q8"])
 def test_dequant_matrix_block_order(fmt):
     """A matrix is [rows][cols/256] blocks, row-major: block (r, b) holds
     columns 256*b .. 256*b+255 of row r.  Every block here decodes to the
@@ -314,12 +326,28 @@ def test_dequant_matrix_block_order(fmt):
             d = _fp16_bits(float(r * nb + b + 1))
             if fmt == "q2k":   # w = d*1*1 - 0*0
                 row.append(pack_q2k(d=d, sc=np.ones(16, int), q=np.ones(256, int)))
-            else:              # w = d*1*C[0][j%8] with an all-ones codebook row 0
+            elif fmt == "cb2":  # w = d*1*C[0][j%8] with an all-ones codebook row 0
                 row.append(pack_cb2(d=d, s=np.ones(8, int)))
+            else:              # w = d*1
+                row.append(pack_q8(d=d, q=np.ones(32, int)))
         raw.append(row)
     raw = np.array(raw, dtype=np.uint8)
+    bw = 32 if fmt == "q8" else 256
     w = om.dequant_matrix(raw, fmt, hand_codebook())
-    assert w.shape == (rows, nb * 256)
+    assert w.shape == (rows, nb * bw)
     for r in range(rows):
         for b in range(nb):
-            assert np.all(w[r, 256 * b:256 * (b + 1)] == np.float32(r * nb + b + 1)), (r, b)
+            assert np.all(w[r, bw * b:bw * (b + 1)] == np.float32(r * nb + b + 1)), (r, b)
+
+
+def test_q8_code_bytes_are_signed_and_linear():
+    """Every code byte 0..255 read as a signed int8 (0x80 = -128, 0xFF = -1);
+    each weight moves only with its own byte, exactly linearly."""
+    d = _fp16_bits(0.25)
+    for start in range(0, 256, 32):
+        codes = np.arange(start, start + 32)
+        blk = pack_q8(d=d)
+        blk[2:34] = codes.astype(np.uint8)
+        w = om.dequant_q8(blk)
+        signed = np.where(codes >= 128, codes - 256, codes)
+        assert np.all(w == np.float32(0.25) * signed.astype(np.float32))

@@ -9,8 +9,9 @@ import synth
 from oracle import moe as om
 
 
-def _tiny(gate_up="q2k", shared=0, E=8, k=2, zipf=None, L=1):
-    return synth.Workload("pin", 99, 256, E, k, 256, shared, gate_up, "q2k", L, (1,), zipf_s=zipf)
+def _tiny(gate_up="q2k", shared=0, E=8, k=2, zipf=None, L=1, shared_format="bf16"):
+    return synth.Workload("pin", 99, 256, E, k, 256, shared, gate_up, "q2k", L, (1,), zipf_s=zipf,
+                          shared_format=shared_format)
 
 
 def _dense_reference(wl, lw, cb, x):
@@ -31,17 +32,22 @@ def _dense_reference(wl, lw, cb, x):
         wd = torch.from_numpy(om.dequant_matrix(lw.down[e], wl.down_format, cb).astype(np.float64))
         o = (torch.nn.functional.silu(xt @ wg.T) * (xt @ wu.T)) @ wd.T
         y += mask[:, e:e + 1] * o
-    if wl.shared_ffn:
+    if wl.shared_ffn and wl.shared_format == "q8":
+        sg, su, sd = (torch.from_numpy(om.dequant_matrix(m, "q8").astype(np.float64)) for m in
+                      (lw.shared_gate, lw.shared_up, lw.shared_down))
+        y += (torch.nn.functional.silu(xt @ sg.T) * (xt @ su.T)) @ sd.T
+    elif wl.shared_ffn:
         sg, su, sd = (torch.from_numpy(om.bf16_bits_to_f64(m)) for m in
                       (lw.shared_gate, lw.shared_up, lw.shared_down))
         y += (torch.nn.functional.silu(xt @ sg.T) * (xt @ su.T)) @ sd.T
     return y.numpy(), idx.numpy()
 
 
-@pytest.mark.parametrize("gate_up,shared,zipf", [("q2k", 0, None), ("cb2", 0, None),
-                                                 ("cb2", 256, 1.1), ("q2k", 256, None)])
-def test_routed_layer_equals_dense_masked_brute_force(gate_up, shared, zipf):
-    wl = _tiny(gate_up, shared, zipf=zipf)
+@pytest.mark.parametrize("gate_up,shared,zipf,sfmt", [("q2k", 0, None, "bf16"), ("cb2", 0, None, "bf16"),
+                                                      ("cb2", 256, 1.1, "bf16"), ("q2k", 256, None, "bf16"),
+                                                      ("cb2", 256, 1.1, "q8")])
+def test_routed_layer_equals_dense_masked_brute_force(gate_up, shared, zipf, sfmt):
+    wl = _tiny(gate_up, shared, zipf=zipf, shared_format=sfmt)
     lw = synth.layer_weights(wl, 0)
     cb = synth.codebook()
     x = synth.tokens(wl, 6)
