@@ -59,7 +59,7 @@ def parse():
 # The other workloads the bench line reports beside the headline one: the
 # routed-only 40-layer stack and the 8-layer large-layer stack, at their
 # batch sizes, with fewer timed steps.
-EXTRA = (("a3b_routed40", (1, 4)), ("flash_stack8_zipf", (1, 8, 32)))
+EXTRA = (("a3b_routed40", (1, 4)), ("a3b_stack40_zipf_q8", (1, 4)), ("flash_stack8_zipf", (1, 8, 32)))
 EXTRA_STEPS = 100
 
 

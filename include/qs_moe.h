@@ -6,9 +6,10 @@
  * (token, slot) pairs by expert -> for each selected expert a fused
  * dequantise + gate/up GEMV + SwiGLU -> down GEMV -> weighted combine, plus an
  * ungated high-precision shared expert.  Only the routed experts are 2-bit:
- * gate/up in a codebook 2-bit type, down in a Q2_K type; router and shared
- * expert stay at high precision (QuarkStar README, "Model Weights"; DwarfStar
- * page, "Model Weights").  Dequantisation is fused into the GEMV, since
+ * gate/up in a codebook 2-bit type, down in a Q2_K type; the router stays
+ * fp32 and the shared expert bf16 or 8-bit (QuarkStar README, "Model
+ * Weights"; DwarfStar page, "Model Weights" and "Distributed Inference").
+ * Dequantisation is fused into the GEMV, since
  * single-stream decode is bound by reading the weights (Quasar README,
  * "Performance model" and "Design decisions").
  *
@@ -36,7 +37,7 @@
 extern "C" {
 #endif
 
-#define QS_MOE_ABI_VERSION 2
+#define QS_MOE_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define QS_API __attribute__((visibility("default")))
@@ -73,8 +74,18 @@ typedef enum {
  *
  * Matrix layout: row-major [rows][cols/256] blocks, rows consecutive.
  * gate/up of one expert are [F][H/256] blocks, down is [H][F/256] blocks;
- * the E experts of a layer are consecutive. */
-typedef enum { QS_FMT_Q2K = 1, QS_FMT_CB2 = 2 } qs_format;
+ * the E experts of a layer are consecutive.
+ *
+ * Shared-expert formats (shared_format):
+ * QS_FMT_BF16: bfloat16 weights, row-major [rows][cols].
+ * QS_FMT_Q8, 34 bytes per 32 weights (the 8-bit Q8_0 type at which the pages
+ *   keep the tensors they do not take to 2 bits: QuarkStar README, "Model
+ *   Weights", the "Q8rest" model; DwarfStar page, "Distributed Inference",
+ *   the "Q8Shared" model):
+ *   [0,2)   d (binary16)
+ *   [2,34)  q[32] int8
+ *   value w_j = d*q_j (exact in fp32); row-major [rows][cols/32] blocks. */
+typedef enum { QS_FMT_BF16 = 0, QS_FMT_Q2K = 1, QS_FMT_CB2 = 2, QS_FMT_Q8 = 3 } qs_format;
 
 /* qs_moe_decode / qs_moe_route flags */
 #define QS_DECODE_RESIDUAL 1u   /* x_{l+1} = x_l + MoE_l(u_l); y gets the last x */
@@ -107,6 +118,7 @@ typedef struct {
                               on the matrix cores, one-token batches on the GEMV
                               items (the measured faster choice on MI355X) */
   int32_t device;          /* HIP device ordinal; -1 = the current device */
+  int32_t shared_format;   /* QS_FMT_BF16 or QS_FMT_Q8 (shared expert weights) */
 } qs_moe_config;
 
 /* One layer's weights in the raw block layout above.  Host or device
@@ -117,9 +129,9 @@ typedef struct {
   const void*     gate;         /* [E][F][H/256] blocks of gate_up_format */
   const void*     up;           /* [E][F][H/256] blocks of gate_up_format */
   const void*     down;         /* [E][H][F/256] blocks of down_format */
-  const uint16_t* shared_gate;  /* bf16 [Fs][H]; NULL iff Fs == 0 */
-  const uint16_t* shared_up;    /* bf16 [Fs][H] */
-  const uint16_t* shared_down;  /* bf16 [H][Fs] */
+  const void*     shared_gate;  /* [Fs][H] in shared_format; NULL iff Fs == 0 */
+  const void*     shared_up;    /* [Fs][H] in shared_format */
+  const void*     shared_down;  /* [H][Fs] in shared_format */
 } qs_moe_layer_weights;
 
 /* Create a handle for one model shape (the routed-expert MoE layer of the
@@ -229,11 +241,13 @@ QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, uint
                  double* logits_out, int32_t* ids_out, float* w_out, int32_t* group_out,
                  void* hip_stream);
 
-/* Dequantise one routed matrix from the handle's device copy with the same
- * field decoding the GEMV kernels use (tests of the IQ2_XXS-class gate/up and
- * Q2_K down types of the QuarkStar README, "Model Weights").  which: 0 gate,
- * 1 up, 2 down.  out: device fp32 [F][H] (gate/up) or [H][F] (down).
- * Asynchronous. */
+/* Dequantise one matrix from the handle's device copy with the same field
+ * decoding the GEMV kernels use (tests of the IQ2_XXS-class gate/up, Q2_K
+ * down and Q8_0 shared types of the QuarkStar README, "Model Weights").
+ * which: 0 gate, 1 up, 2 down of routed expert `expert`; 3 gate, 4 up,
+ * 5 down of the shared expert (expert ignored; QS_E_INVAL when Fs == 0).
+ * out: device fp32 [F][H] (gate/up), [H][F] (down), [Fs][H] (shared
+ * gate/up) or [H][Fs] (shared down).  Asynchronous. */
 QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* out, void* hip_stream);
 
 /* Bytes of device memory the handle holds (weights + scratch); the pages

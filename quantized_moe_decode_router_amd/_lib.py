@@ -10,13 +10,13 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsmoe.so")
 
-QS_MOE_ABI_VERSION = 2
+QS_MOE_ABI_VERSION = 3
 QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
-QS_FMT_Q2K, QS_FMT_CB2 = 1, 2
+QS_FMT_BF16, QS_FMT_Q2K, QS_FMT_CB2, QS_FMT_Q8 = 0, 1, 2, 3
 QS_DECODE_RESIDUAL = 1
 QS_DECODE_RMSNORM = 2
 
-FORMATS = {"q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2}
+FORMATS = {"bf16": QS_FMT_BF16, "q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2, "q8": QS_FMT_Q8}
 
 # Every function include/qs_moe.h declares.
 EXPORTS = (
@@ -28,7 +28,8 @@ EXPORTS = (
 class QsMoeConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "n_experts", "top_k", "expert_ffn", "shared_ffn",
-        "gate_up_format", "down_format", "n_layers", "max_tokens", "mfma_min_tokens", "device")]
+        "gate_up_format", "down_format", "n_layers", "max_tokens", "mfma_min_tokens", "device",
+        "shared_format")]
 
 
 class QsMoeLayerWeights(ctypes.Structure):
@@ -114,11 +115,11 @@ def _stream(stream) -> int:
 
 
 def make_config(hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format, down_format,
-                n_layers, max_tokens, mfma_min_tokens=0, device=-1) -> QsMoeConfig:
+                n_layers, max_tokens, mfma_min_tokens=0, device=-1, shared_format="bf16") -> QsMoeConfig:
     fmt = lambda f: FORMATS[f] if isinstance(f, str) else int(f)  # noqa: E731
     return QsMoeConfig(QS_MOE_ABI_VERSION, hidden, n_experts, top_k, expert_ffn, shared_ffn,
                        fmt(gate_up_format), fmt(down_format), n_layers, max_tokens,
-                       mfma_min_tokens, device)
+                       mfma_min_tokens, device, fmt(shared_format))
 
 
 def qs_moe_create(cfg: QsMoeConfig, codebook=None) -> int:

@@ -136,8 +136,8 @@ __device__ __forceinline__ BigL carve_big(uint8_t* raw, const A& a, bool cb2) {
 // ------------------------------------------------------ staging plans ---
 // Byte sizes of the pieces a phase stages into the LDS buffer; pure
 // functions of the arguments (the host checks the same sizes).
-__host__ __device__ inline uint32_t big_item_b(int H) { return (uint32_t)kSharedItemRows * 2 * H * 2; }
-__host__ __device__ inline uint32_t big_sdrows_b(int Fs) { return (uint32_t)kDownRows * Fs * 2; }
+__host__ __device__ inline uint32_t big_item_b(int H, bool sq8) { return (uint32_t)kSharedItemRows * 2 * srow_bytes(H, sq8); }
+__host__ __device__ inline uint32_t big_sdrows_b(int Fs, bool sq8) { return (uint32_t)kDownRows * srow_bytes(Fs, sq8); }
 __host__ __device__ inline uint32_t big_tile_b(int H, bool q2k) {
   return 2u * (uint32_t)kGateTile * (H / kBlockW) * (64u + (q2k ? 16u : 4u) + (q2k ? 4u : 2u));
 }
@@ -158,8 +158,8 @@ __host__ __device__ inline uint32_t big_mdn_b(int kb) {
 
 // Offsets inside the buffer: the shared piece (prefetched during the
 // barrier before its phase) first, the routed area after it.
-__host__ __device__ inline uint32_t big_gu_area(int H, int Fs) { return Fs ? al16(big_item_b(H)) : 0u; }
-__host__ __device__ inline uint32_t big_dn_area(int Fs) { return Fs ? al16(big_sdrows_b(Fs)) : 0u; }
+__host__ __device__ inline uint32_t big_gu_area(int H, int Fs, bool sq8) { return Fs ? al16(big_item_b(H, sq8)) : 0u; }
+__host__ __device__ inline uint32_t big_dn_area(int Fs, bool sq8) { return Fs ? al16(big_sdrows_b(Fs, sq8)) : 0u; }
 
 struct BigPlan {
   int xg;     // tokens per GEMV gate/up pass
@@ -170,10 +170,10 @@ struct BigPlan {
   bool ok;
 };
 
-__host__ __device__ inline BigPlan big_plan(int H, int F, int Fs, bool q2k, uint32_t pfb, int rtr_bytes) {
+__host__ __device__ inline BigPlan big_plan(int H, int F, int Fs, bool sq8, bool q2k, uint32_t pfb, int rtr_bytes) {
   BigPlan p;
   const int nbh = H / kBlockW, nb = F / kBlockW;
-  const uint32_t ga = big_gu_area(H, Fs), da = big_dn_area(Fs);
+  const uint32_t ga = big_gu_area(H, Fs, sq8), da = big_dn_area(Fs, sq8);
   const uint32_t gfree = pfb > ga ? pfb - ga : 0u, dfree = pfb > da ? pfb - da : 0u;
   const uint32_t tb = al16(big_tile_b(H, q2k));
   p.xg = gfree > tb ? (int)((gfree - tb) / big_xtok_b(H, q2k)) : 0;
@@ -196,13 +196,13 @@ __host__ __device__ inline BigPlan big_plan(int H, int F, int Fs, bool q2k, uint
   p.shtok = Fs ? (int)(dfree / ((uint32_t)Fs * 4u)) : 1;
   if (p.shtok > kMaxTokens) p.shtok = kMaxTokens;
   p.ok = p.xg >= 1 && p.xp >= 1 && p.kbg >= 1 && p.kbd >= 1 && p.shtok >= 1 && (uint32_t)rtr_bytes <= pfb &&
-         (Fs == 0 || (big_item_b(H) <= pfb && big_sdrows_b(Fs) <= pfb));
+         (Fs == 0 || (big_item_b(H, sq8) <= pfb && big_sdrows_b(Fs, sq8) <= pfb));
   return p;
 }
 
 template <class A>
 __device__ __forceinline__ BigPlan big_plan_of(const A& a) {
-  return big_plan(a.H, a.F, a.Fs, a.gq2k != 0, a.pfb, (int)router_bytes(a));
+  return big_plan(a.H, a.F, a.Fs, a.sq8 != 0, a.gq2k != 0, a.pfb, (int)router_bytes(a));
 }
 
 // ------------------------------------------------------- cost model ---
@@ -409,7 +409,7 @@ __device__ __forceinline__ void shared_gu_item_big(const A& a, lds_cptr wbase, c
   const int rw = wave >> 2, qtr = wave & 3;
   const int hq = a.H / 4;
   const int T = a.T;
-  const uint32_t row = (uint32_t)a.H * 2;
+  const uint32_t row = srow_bytes(a.H, a.sq8 != 0);
   lds_cptr gsrc = wbase + (2 * rw) * row;
   lds_cptr usrc = wbase + (2 * rw + 1) * row;
 #pragma unroll 1
@@ -426,17 +426,16 @@ __device__ __forceinline__ void shared_gu_item_big(const A& a, lds_cptr wbase, c
         x0[j] = j < nt ? cldf4(x + (size_t)(t0 + j) * a.H + h) : make_float4(0, 0, 0, 0);
         x1[j] = j < nt ? cldf4(x + (size_t)(t0 + j) * a.H + h + 4) : make_float4(0, 0, 0, 0);
       }
-      const uint4 wg = ld16(gsrc + h * 2), wu = ld16(usrc + h * 2);
-      const uint32_t gw[4] = {wg.x, wg.y, wg.z, wg.w}, uw[4] = {wu.x, wu.y, wu.z, wu.w};
+      float gw[8], uw[8];
+      shared_w8(a, gsrc, a.H, h, gw);
+      shared_w8(a, usrc, a.H, h, uw);
 #pragma unroll
       for (int j = 0; j < kShTok; ++j) {
         const float xv[8] = {x0[j].x, x0[j].y, x0[j].z, x0[j].w, x1[j].x, x1[j].y, x1[j].z, x1[j].w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          g[j] = fmaf(bf16_to_f32(gw[c] & 0xFFFFu), xv[2 * c], g[j]);
-          g[j] = fmaf(bf16_to_f32(gw[c] >> 16), xv[2 * c + 1], g[j]);
-          u[j] = fmaf(bf16_to_f32(uw[c] & 0xFFFFu), xv[2 * c], u[j]);
-          u[j] = fmaf(bf16_to_f32(uw[c] >> 16), xv[2 * c + 1], u[j]);
+        for (int c = 0; c < 8; ++c) {
+          g[j] = fmaf(gw[c], xv[c], g[j]);
+          u[j] = fmaf(uw[c], xv[c], u[j]);
         }
       }
     }
@@ -652,7 +651,7 @@ __device__ __forceinline__ void gu_gemv_item(const A& a, const LayerPtrs& Lp, Bi
                                              int u, int f0, bool pre, bool xkeep) {
   PersistLds& P = L.P;
   const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0, e = P.act[u];
-  QS_LDS uint8_t* wt = P.pfb + big_gu_area(a.H, a.Fs);
+  QS_LDS uint8_t* wt = P.pfb + big_gu_area(a.H, a.Fs, a.sq8 != 0);
   const XStage xst = x_stage(a, wt + al16(big_tile_b(a.H, a.gq2k != 0)), pp.xg);
   for (int g0 = 0; g0 < n; g0 += pp.xg) {
     const int ng = n - g0 < pp.xg ? n - g0 : pp.xg;
@@ -782,7 +781,7 @@ __device__ __forceinline__ void gu_mfma_item(const A& a, const LayerPtrs& Lp, Bi
   const uint8_t* gm = Lp.gate + (size_t)e * a.gu_stride;
   const uint8_t* um = Lp.up + (size_t)e * a.gu_stride;
   const int arow = f0 + 16 * rg + r, drow0 = f0 + 16 * rg + 4 * g;
-  const MguStage st = mgu_stage(P.pfb + big_gu_area(H, a.Fs), pp.kbg);
+  const MguStage st = mgu_stage(P.pfb + big_gu_area(H, a.Fs, a.sq8 != 0), pp.kbg);
 #pragma unroll 1
   for (int g0 = 0; g0 < n; g0 += kMfmaTok) {
     const int ng = n - g0 < kMfmaTok ? n - g0 : kMfmaTok;
@@ -906,8 +905,8 @@ __device__ __forceinline__ void big_gu_phase(const A& a, const LayerPtrs& Lp, co
   const bool q2k = a.gq2k != 0;
   const uint32_t tb = al16(big_tile_b(a.H, q2k)), xtok = big_xtok_b(a.H, q2k);
   Batcher B;
-  B.area = P.pfb + big_gu_area(a.H, a.Fs);
-  B.cap = a.pfb - big_gu_area(a.H, a.Fs);
+  B.area = P.pfb + big_gu_area(a.H, a.Fs, a.sq8 != 0);
+  B.cap = a.pfb - big_gu_area(a.H, a.Fs, a.sq8 != 0);
   B.fill = 0;
   B.n = 0;
   B.last_u = -1;
@@ -1071,7 +1070,7 @@ __device__ __forceinline__ void dn_gemv_item(const A& a, const LayerPtrs& Lp, Bi
   PersistLds& P = L.P;
   const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0, e = P.act[u];
   const int wave = qs_tid() >> 6;
-  QS_LDS uint8_t* wt = P.pfb + big_dn_area(a.Fs);
+  QS_LDS uint8_t* wt = P.pfb + big_dn_area(a.Fs, a.sq8 != 0);
   const AStage st = a_stage(a, wt + al16(big_dnw_b(a.F)), pp.xp);
   for (int g0 = 0; g0 < n; g0 += pp.xp) {
     const int ng = n - g0 < pp.xp ? n - g0 : pp.xp;
@@ -1139,7 +1138,7 @@ __device__ __forceinline__ void dn_mfma_item(const A& a, const LayerPtrs& Lp, Bi
   const MatPlanes pl = q2k_planes((size_t)a.H * nb);
   const uint8_t* dm = Lp.down + (size_t)e * a.dn_stride;
   const int arow = h0 + 16 * wave + r, drow0 = h0 + 16 * wave + 4 * g;
-  const MdnStage st = mdn_stage(P.pfb + big_dn_area(a.Fs), pp.kbd);
+  const MdnStage st = mdn_stage(P.pfb + big_dn_area(a.Fs, a.sq8 != 0), pp.kbd);
 #pragma unroll 1
   for (int g0 = 0; g0 < n; g0 += kMfmaTok) {
     const int ng = n - g0 < kMfmaTok ? n - g0 : kMfmaTok;
@@ -1213,21 +1212,18 @@ template <class A>
 __device__ __forceinline__ void big_shared_dn_tile(const A& a, lds_cptr srows, const QS_LDS float* as_,
                                                    int t0, int nt, int r0, BigL& L) {
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
-  lds_cptr srow = srows + (uint32_t)wave * a.Fs * 2;
+  lds_cptr srow = srows + (uint32_t)wave * srow_bytes(a.Fs, a.sq8 != 0);
 #pragma unroll 1
   for (int j = 0; j < nt; ++j) {
     float sum = 0.f;
 #pragma unroll 1
     for (int f = 8 * lane; f < a.Fs; f += 512) {
-      const uint4 w = ld16(srow + f * 2);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      float ww[8];
+      shared_w8(a, srow, a.Fs, f, ww);
       const float4 a0 = lds_f4(as_ + j * a.Fs + f), a1 = lds_f4(as_ + j * a.Fs + f + 4);
       const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        sum = fmaf(bf16_to_f32(ww[c] & 0xFFFFu), av[2 * c], sum);
-        sum = fmaf(bf16_to_f32(ww[c] >> 16), av[2 * c + 1], sum);
-      }
+      for (int c = 0; c < 8; ++c) sum = fmaf(ww[c], av[c], sum);
     }
     sum = bfly_sum<6>(sum);
     if (lane == 0) L.P.sh[j * kDownRows + wave] = sum;
@@ -1246,7 +1242,7 @@ __device__ __forceinline__ void big_dn_phase(const A& a, const LayerPtrs& Lp, Bi
   const int na = *P.nact;
   if (a.Fs && (int)blockIdx.x < a.H / kDownRows) {
     // the shared SwiGLU vectors of as many tokens as fit beside the rows
-    QS_LDS float* as_ = (QS_LDS float*)(P.pfb + big_dn_area(a.Fs));
+    QS_LDS float* as_ = (QS_LDS float*)(P.pfb + big_dn_area(a.Fs, a.sq8 != 0));
     const int tg = pp.shtok;
     for (int t0 = 0; t0 < a.T; t0 += tg) {
       const int nt = a.T - t0 < tg ? a.T - t0 : tg;
@@ -1266,8 +1262,8 @@ __device__ __forceinline__ void big_dn_phase(const A& a, const LayerPtrs& Lp, Bi
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
   const uint32_t wb = al16(big_dnw_b(a.F)), pb = big_apair_b(a.F);
   Batcher B;
-  B.area = P.pfb + big_dn_area(a.Fs);
-  B.cap = a.pfb - big_dn_area(a.Fs);
+  B.area = P.pfb + big_dn_area(a.Fs, a.sq8 != 0);
+  B.cap = a.pfb - big_dn_area(a.Fs, a.sq8 != 0);
   B.fill = 0;
   B.n = 0;
   B.last_u = -1;
@@ -1421,15 +1417,15 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist_big(PersistArgs a) 
 
 // The layer shape fixed at compile time, the batch size at run time (as
 // FixedArgs for the small-batch kernel).
-template <int FMT, int H_, int E_, int K_, int F_, int FS_, int G_>
+template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int G_>
 struct FixedBigArgs : PersistArgs {
-  static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, G = G_;
+  static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, sq8 = SQ8_, G = G_;
   static constexpr int gq2k = FMT == 1, r_et = 1;
 };
 
-template <int FMT, int H, int E, int K, int F, int FS, int G>
+template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int G>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_big_fixed(PersistArgs a) {
-  persist_big_body<FMT>(static_cast<const FixedBigArgs<FMT, H, E, K, F, FS, G>&>(a));
+  persist_big_body<FMT>(static_cast<const FixedBigArgs<FMT, H, E, K, F, FS, SQ8, G>&>(a));
 }
 
 }  // namespace qs

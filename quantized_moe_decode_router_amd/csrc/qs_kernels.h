@@ -185,6 +185,22 @@ __global__ void k_repack_q2k(const uint8_t* __restrict__ src, uint8_t* __restric
   for (int i = 0; i < 4; ++i) base[pl.d + blk * 4 + i] = s[80 + i];
 }
 
+// 8-bit shared-expert blocks (d binary16, then 32 int8 codes; row-major
+// [rows][K/32]) -> padded rows [K codes | K/32 scales] of row_bytes each.
+// One thread per block.
+__global__ void k_repack_q8(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, size_t rows, int K,
+                            uint32_t row_bytes) {
+  const size_t nb = (size_t)K / kQ8W;
+  const size_t gi = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= rows * nb) return;
+  const size_t r = gi / nb, j = gi % nb;
+  const uint8_t* s = src + gi * kQ8Bytes;
+  uint8_t* o = dst + r * row_bytes;
+  for (int i = 0; i < kQ8W; ++i) o[j * kQ8W + i] = s[2 + i];
+  o[K + 2 * j] = s[0];
+  o[K + 2 * j + 1] = s[1];
+}
+
 // ---------------------------------------------------------- dequant ---
 // One thread per block: the GEMV kernels' field decoding, written out as
 // fp32 weights in natural order (used by tests through qs_moe_dequant).
@@ -226,6 +242,24 @@ __global__ void k_dequant_q2k(const uint8_t* __restrict__ mat, size_t nblk, floa
       const uint32_t quad = (qs[i] >> (2 * p)) & 0x03030303u;
       for (int b = 0; b < 4; ++b) o[16 * i + 4 * b + p] = fmaf(dsc, (float)((quad >> (8 * b)) & 3u), -dm);
     }
+  }
+}
+
+// A shared-expert matrix as the kernels hold it (bf16 rows, or padded
+// 8-bit rows) -> fp32 [rows][K]; one thread per weight.
+__global__ void k_dequant_shared(const uint8_t* __restrict__ mat, size_t rows, int K, int q8,
+                                 uint32_t row_bytes, float* __restrict__ out) {
+  const size_t gi = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= rows * (size_t)K) return;
+  const size_t r = gi / K;
+  const int h = (int)(gi % K);
+  const uint8_t* row = mat + r * row_bytes;
+  if (q8) {
+    const int j = h / kQ8W;
+    const uint32_t dbits = (uint32_t)row[K + 2 * j] | ((uint32_t)row[K + 2 * j + 1] << 8);
+    out[gi] = half_to_f32(dbits) * (float)(int8_t)row[h];
+  } else {
+    out[gi] = bf16_to_f32((uint32_t)row[2 * h] | ((uint32_t)row[2 * h + 1] << 8));
   }
 }
 

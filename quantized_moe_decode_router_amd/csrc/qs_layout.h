@@ -39,6 +39,8 @@ namespace qs {
 constexpr int kBlockW = 256;          // weights per block
 constexpr int kQ2KBytes = 84;
 constexpr int kCB2Bytes = 70;
+constexpr int kQ8Bytes = 34;           // 8-bit shared-expert block: d binary16 + 32 int8
+constexpr int kQ8W = 32;               // weights per 8-bit block
 constexpr int kChunkW = 64;           // weights per lane chunk
 constexpr int kSubW = 16;             // activation scale granularity
 constexpr int kCbTabWords = 8192;     // two 4096-entry signed-quad tables

@@ -33,9 +33,9 @@ struct LayerDev {
   uint8_t* gate = nullptr;
   uint8_t* up = nullptr;
   uint8_t* down = nullptr;
-  uint16_t* sg = nullptr;
-  uint16_t* su = nullptr;
-  uint16_t* sd = nullptr;
+  uint8_t* sg = nullptr;     // shared expert rows (srow_bytes each)
+  uint8_t* su = nullptr;
+  uint8_t* sd = nullptr;
   bool uploaded = false;
 };
 
@@ -164,6 +164,7 @@ int validate_config(const qs_moe_config* c) {
   if ((long)c->max_tokens * c->top_k > kMaxPairs) return QS_E_INVAL;
   if (c->mfma_min_tokens < 0) return QS_E_INVAL;
   if (c->device < -1) return QS_E_INVAL;
+  if (c->shared_format != QS_FMT_BF16 && c->shared_format != QS_FMT_Q8) return QS_E_INVAL;
   if (c->down_format != QS_FMT_Q2K) return QS_E_UNSUPPORTED;
   return QS_OK;
 }
@@ -311,7 +312,8 @@ PersistShape big_shape(const qs_moe* h, int T) {
   p.lds = base + p.pfb;
   p.r_tt = T < 4 ? T : 4;
   while (p.r_et < 4 && (c.n_experts + p.r_et - 1) / p.r_et > h->grid) p.r_et *= 2;
-  p.ok = big_plan(c.hidden, c.expert_ffn, c.shared_ffn, !cb2, p.pfb, p.r_et * c.hidden * 4).ok;
+  p.ok = big_plan(c.hidden, c.expert_ffn, c.shared_ffn, c.shared_format == QS_FMT_Q8, !cb2, p.pfb,
+                  p.r_et * c.hidden * 4).ok;
   return p;
 }
 
@@ -330,17 +332,18 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   if (!small) return big_shape(h, T);
   PersistShape p;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
-  const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, cb2, small,
-                                 0).end;
+  const bool sq8 = c.shared_format == QS_FMT_Q8;
+  const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, sq8, cb2,
+                                 small, 0).end;
   if (base >= h->lds_limit || h->grid_small < 8) return p;
   p.pfb = (uint32_t)std::min((size_t)kPfbMax, (h->lds_limit - base) & ~(size_t)15);
   p.lds = base + p.pfb;
   p.r_tt = T < 4 ? T : 4;
   while (p.r_et < 4 && (c.n_experts + p.r_et - 1) / p.r_et > h->grid_small) p.r_et *= 2;
   const uint64_t H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn, nbh = H / 256, nb = F / 256;
-  const uint64_t rb = (uint64_t)p.r_et * H * 4, item = 8 * H;
+  const uint64_t rb = (uint64_t)p.r_et * H * 4, item = big_item_b(c.hidden, sq8);
   const uint64_t tile = 2ull * 16 * nbh * (64 + (cb2 ? 4 : 16) + (cb2 ? 2 : 4));
-  const uint64_t sd = 16 * Fs, pe = 8 * nb * 84;
+  const uint64_t sd = big_sdrows_b(c.shared_ffn, sq8), pe = 8 * nb * 84;
   auto a16 = [](uint64_t v) { return (v + 15) & ~15ull; };
   bool fits;
   if (small) {
@@ -348,7 +351,7 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
     // gate/up tiles (K, GU); region B and the x limbs after it: experts'
     // down rows (D).  The shared down rows have their own slot.
     // one shared gate/up row per item above hidden 2048, two otherwise (sh_rows)
-    const uint64_t sitem = (H > 2048 ? 4 : 8) * H;
+    const uint64_t sitem = (H > 2048 ? 2 : 4) * (uint64_t)srow_bytes(c.hidden, sq8);
     const uint64_t r_sh = a16(rb) + (Fs ? sitem : 0);
     const uint64_t xl = 2 * a16((uint64_t)T * H) + 2 * a16((uint64_t)T * H / 4);
     const uint64_t A = a16(r_sh);
@@ -380,15 +383,16 @@ const void* persist_fn(bool cb2, bool small) {
 }
 
 // Small-batch instantiations with the layer shape fixed at compile time:
-// hidden 2048, 256 experts, top-8, expert width 512, shared width 512 or 0,
-// codebook gate/up, one workgroup per CU of a 256-CU device.
-template <int FS>
+// hidden 2048, 256 experts, top-8, expert width 512, shared width 512
+// (bf16 or 8-bit) or 0, codebook gate/up, one workgroup per CU of a 256-CU
+// device.
+template <int FS, int SQ8>
 const void* fixed_a3b(int T) {
   switch (T) {
-    case 1: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, 1, 256>;
-    case 2: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, 2, 256>;
-    case 3: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, 3, 256>;
-    case 4: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, 4, 256>;
+    case 1: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 1, 256>;
+    case 2: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 2, 256>;
+    case 3: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 3, 256>;
+    case 4: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 4, 256>;
     default: return nullptr;
   }
 }
@@ -399,12 +403,14 @@ const void* fixed_a3b(int T) {
 const void* persist_big_fixed_fn(const qs_moe* h) {
   const qs_moe_config& c = h->cfg;
   if (h->grid != 256 || c.gate_up_format != QS_FMT_CB2 || c.n_experts != 256) return nullptr;
+  const bool sq8 = c.shared_format == QS_FMT_Q8;
   if (c.hidden == 2048 && c.top_k == 8 && c.expert_ffn == 512) {
-    if (c.shared_ffn == 512) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 256>;
-    if (c.shared_ffn == 0) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 0, 256>;
+    if (c.shared_ffn == 512 && sq8) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 1, 256>;
+    if (c.shared_ffn == 512) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 0, 256>;
+    if (c.shared_ffn == 0) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 0, 0, 256>;
   }
-  if (c.hidden == 4096 && c.top_k == 6 && c.expert_ffn == 2048 && c.shared_ffn == 2048)
-    return (const void*)k_persist_big_fixed<2, 4096, 256, 6, 2048, 2048, 256>;
+  if (c.hidden == 4096 && c.top_k == 6 && c.expert_ffn == 2048 && c.shared_ffn == 2048 && !sq8)
+    return (const void*)k_persist_big_fixed<2, 4096, 256, 6, 2048, 2048, 0, 256>;
   return nullptr;
 }
 
@@ -414,8 +420,9 @@ const void* persist_fixed_fn(const qs_moe* h, int T) {
   if (h->grid_small != 256 || c.gate_up_format != QS_FMT_CB2 || c.hidden != 2048 || c.n_experts != 256 ||
       c.top_k != 8 || c.expert_ffn != 512)
     return nullptr;
-  if (c.shared_ffn == 512) return fixed_a3b<512>(T);
-  if (c.shared_ffn == 0) return fixed_a3b<0>(T);
+  if (c.shared_ffn == 512 && c.shared_format == QS_FMT_Q8) return fixed_a3b<512, 1>(T);
+  if (c.shared_ffn == 512) return fixed_a3b<512, 0>(T);
+  if (c.shared_ffn == 0) return fixed_a3b<0, 0>(T);
   return nullptr;
 }
 
@@ -567,6 +574,7 @@ int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const 
   a.n_layers = nL;
   a.T = T; a.H = c.hidden; a.E = c.n_experts; a.k = c.top_k; a.F = c.expert_ffn; a.Fs = c.shared_ffn;
   a.gq2k = c.gate_up_format == QS_FMT_Q2K;
+  a.sq8 = c.shared_format == QS_FMT_Q8;
   a.prenorm = prenorm;
   a.residual = residual;
   a.r_tt = p.r_tt;
@@ -742,7 +750,9 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   size_t lb = 0;
   lb += align_up(E * H * 4, 256) + align_up(E * 4, 256);
   lb += 2 * E * h->gu_stride + E * h->dn_stride;
-  lb += 3 * align_up(Fs * H * 2, 256);
+  const bool sq8 = c.shared_format == QS_FMT_Q8;
+  const size_t sgu = Fs * (size_t)srow_bytes((int)H, sq8), sdn = H * (size_t)srow_bytes((int)Fs, sq8);
+  if (Fs) lb += 2 * align_up(sgu, 256) + align_up(sdn, 256);
   h->layer_bytes = lb;
   h->layers.resize(c.n_layers);
   rc = QS_OK;
@@ -760,9 +770,9 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
     L.up = p; p += E * h->gu_stride;
     L.down = p; p += E * h->dn_stride;
     if (Fs) {
-      L.sg = carve<uint16_t>(p, Fs * H);
-      L.su = carve<uint16_t>(p, Fs * H);
-      L.sd = carve<uint16_t>(p, Fs * H);
+      L.sg = carve<uint8_t>(p, sgu);
+      L.su = carve<uint8_t>(p, sgu);
+      L.sd = carve<uint8_t>(p, sdn);
     }
     h->total_bytes += lb;
   }
@@ -837,14 +847,16 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
     QS_HIP(hipMemcpyAsync(L.bias, w->router_bias, E * 4, hipMemcpyDefault, st));
   else
     QS_HIP(hipMemsetAsync(L.bias, 0, E * 4, st));
-  if (Fs) {
+  const bool sq8 = c.shared_format == QS_FMT_Q8;
+  if (Fs && !sq8) {   // bf16 rows are already the kernels' layout
     QS_HIP(hipMemcpyAsync(L.sg, w->shared_gate, Fs * H * 2, hipMemcpyDefault, st));
     QS_HIP(hipMemcpyAsync(L.su, w->shared_up, Fs * H * 2, hipMemcpyDefault, st));
     QS_HIP(hipMemcpyAsync(L.sd, w->shared_down, Fs * H * 2, hipMemcpyDefault, st));
   }
   const size_t gu_blk = F * (H / kBlockW), dn_blk = H * (F / kBlockW);
   const size_t gbb = gate_up_block_bytes(c);
-  const size_t need = std::max(E * gu_blk * gbb, E * dn_blk * (size_t)kQ2KBytes);
+  const size_t q8_raw = Fs * (H / kQ8W) * (size_t)kQ8Bytes;   // one shared matrix in 8-bit blocks
+  const size_t need = std::max({E * gu_blk * gbb, E * dn_blk * (size_t)kQ2KBytes, sq8 ? q8_raw : (size_t)0});
   if (h->staging_bytes < need) {
     if (h->staging) QS_HIP(hipFree(h->staging));
     h->staging = nullptr;
@@ -873,6 +885,18 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
       hipLaunchKernelGGL(k_repack_q2k, grid, dim3(256), 0, st, (const uint8_t*)h->staging, j.dst,
                          j.nblk, j.stride, E);
     QS_HIP(hipGetLastError());
+  }
+  if (Fs && sq8) {    // 8-bit blocks -> padded rows [codes | scales]
+    struct SJob { const void* src; uint8_t* dst; size_t rows; int K; };
+    const SJob sj[3] = {{w->shared_gate, L.sg, Fs, (int)H}, {w->shared_up, L.su, Fs, (int)H},
+                        {w->shared_down, L.sd, H, (int)Fs}};
+    for (const SJob& j : sj) {
+      QS_HIP(hipMemcpyAsync(h->staging, j.src, q8_raw, hipMemcpyDefault, st));
+      const size_t total = j.rows * (size_t)(j.K / kQ8W);
+      hipLaunchKernelGGL(k_repack_q8, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                         (const uint8_t*)h->staging, j.dst, j.rows, j.K, srow_bytes(j.K, true));
+      QS_HIP(hipGetLastError());
+    }
   }
   QS_HIP(hipStreamSynchronize(st));
   L.uploaded = true;
@@ -992,7 +1016,9 @@ QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, uint
 QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* out, void* hip_stream) {
   if (!h || !out) return QS_E_INVAL;
   const qs_moe_config& c = h->cfg;
-  if (expert < 0 || expert >= c.n_experts || which < 0 || which > 2) return QS_E_INVAL;
+  if (which < 0 || which > 5) return QS_E_INVAL;
+  if (which < 3 && (expert < 0 || expert >= c.n_experts)) return QS_E_INVAL;
+  if (which >= 3 && c.shared_ffn == 0) return QS_E_INVAL;
   int rc = check_layer_range(h, layer, 1);
   if (rc) return rc;
   DeviceGuard dg(h->device);
@@ -1000,6 +1026,17 @@ QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* ou
   hipStream_t st = (hipStream_t)hip_stream;
   const LayerDev& L = h->layers[layer];
   const size_t H = c.hidden, F = c.expert_ffn;
+  if (which >= 3) {
+    const bool sq8 = c.shared_format == QS_FMT_Q8;
+    const uint8_t* mat = which == 3 ? L.sg : which == 4 ? L.su : L.sd;
+    const size_t rows = which == 5 ? H : (size_t)c.shared_ffn;
+    const int K = which == 5 ? c.shared_ffn : c.hidden;
+    const size_t total = rows * (size_t)K;
+    hipLaunchKernelGGL(k_dequant_shared, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, mat, rows, K,
+                       sq8 ? 1 : 0, srow_bytes(K, sq8), out);
+    QS_HIP(hipGetLastError());
+    return QS_OK;
+  }
   const uint8_t* mat;
   size_t nblk;
   bool cb2;

@@ -65,9 +65,9 @@ struct LayerPtrs {
   const uint8_t* gate;
   const uint8_t* up;
   const uint8_t* down;
-  const uint16_t* sg;
-  const uint16_t* su;
-  const uint16_t* sd;
+  const uint8_t* sg;          // shared expert rows (bf16, or the 8-bit rows below)
+  const uint8_t* su;
+  const uint8_t* sd;
 };
 
 struct PersistArgs {
@@ -75,6 +75,7 @@ struct PersistArgs {
   int G;                     // workgroups of the launch (a multiple of 8)
   int n_layers, T, H, E, k, F, Fs;
   int gq2k, prenorm, residual;
+  int sq8;                   // shared expert in 8-bit blocks (else bf16)
   int r_et, r_tt;            // router unit: experts x tokens
   uint32_t pfb;              // bytes of the LDS weight-staging buffer
   uint32_t pfa;              // SMALL: bytes of its first region (router, shared items, gate/up tiles);
@@ -356,6 +357,13 @@ __device__ __forceinline__ bool grid_barrier(const A& a, uint32_t epoch, PF&& pf
 // --------------------------------------------------------- LDS layout ---
 __host__ __device__ inline uint32_t al16(uint32_t v) { return (v + 15u) & ~15u; }
 
+// A shared-expert row of K weights: K bf16, or (8-bit blocks of 32 weights)
+// the K int8 codes followed by the K/32 binary16 block scales, padded to 16
+// bytes.  The same stride in HBM and LDS.
+__host__ __device__ inline uint32_t srow_bytes(int K, bool q8) {
+  return q8 ? al16((uint32_t)K + (uint32_t)K / 16) : (uint32_t)K * 2;
+}
+
 // SMALL activation buffer: [x fp32 T*H | logits fp64 T*E] during R and K;
 // [a limbs hi | lo | scales | sums | shared SwiGLU T*Fs] during D.
 __host__ __device__ inline uint32_t abuf_bytes(int T, int H, int E, int P, int F, int Fs) {
@@ -371,7 +379,7 @@ struct LdsLayout {
 
 __host__ __device__ inline int kf_stride(int E) { return (E + 7) & ~7; }
 
-__host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int F, int Fs, bool cb2,
+__host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int F, int Fs, bool sq8, bool cb2,
                                                 bool small, uint32_t pfb) {
   LdsLayout l;
   uint32_t o = 0;
@@ -417,7 +425,7 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.xl = take(xq);
   l.xs = take(xq / 4);      // T*H/16 floats
   l.xa = take(xq / 4);
-  l.sdr = take(small ? (uint32_t)kDownRows * Fs * 2 : 0);
+  l.sdr = take(small ? (uint32_t)kDownRows * srow_bytes(Fs, sq8) : 0);
   l.end = o;
   return l;
 }
@@ -467,7 +475,7 @@ struct PersistLds {
 template <bool SMALL, class A>
 __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const A& a, bool cb2) {
   const uint32_t T = a.T, H = a.H, E = a.E, F = a.F, P = T * a.k;
-  const LdsLayout l = lds_layout(E, T, P, H, F, a.Fs, cb2, SMALL, a.pfb);
+  const LdsLayout l = lds_layout(E, T, P, H, F, a.Fs, a.sq8 != 0, cb2, SMALL, a.pfb);
   QS_LDS uint8_t* b = (QS_LDS uint8_t*)raw;
   PersistLds L;
   L.tab = (QS_LDS uint32_t*)(b + l.tab);
@@ -538,7 +546,7 @@ template <bool SMALL, class A>
 __device__ __forceinline__ int n_shared_items(const A& a) { return a.Fs / sh_rows<SMALL>(a); }
 template <bool SMALL, class A>
 __device__ __forceinline__ uint32_t shared_item_bytes(const A& a) {
-  return (uint32_t)sh_rows<SMALL>(a) * 2 * a.H * 2;
+  return (uint32_t)sh_rows<SMALL>(a) * 2 * srow_bytes(a.H, a.sq8 != 0);
 }
 template <class A>
 __device__ __forceinline__ uint32_t gu_tile_bytes(const A& a) {
@@ -547,7 +555,7 @@ __device__ __forceinline__ uint32_t gu_tile_bytes(const A& a) {
   return 2u * (uint32_t)kGateTile * nbh * (64u + sper + dper);
 }
 template <class A>
-__device__ __forceinline__ uint32_t sd_bytes(const A& a) { return (uint32_t)kDownRows * a.Fs * 2; }
+__device__ __forceinline__ uint32_t sd_bytes(const A& a) { return (uint32_t)kDownRows * srow_bytes(a.Fs, a.sq8 != 0); }
 template <class A>
 __device__ __forceinline__ uint32_t dn_expert_bytes(const A& a) {
   return (uint32_t)kDownRows * (a.F / kBlockW) * kQ2KBytes;
@@ -607,12 +615,12 @@ __device__ __forceinline__ void copy_router_rows(const A& a, const LayerPtrs& Lp
 template <bool SMALL, class A>
 __device__ __forceinline__ void copy_shared_item(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
                                                  int item, int w, int nw) {
-  const uint32_t row = (uint32_t)a.H * 2;
+  const uint32_t row = srow_bytes(a.H, a.sq8 != 0);
   const int rows = sh_rows<SMALL>(a);
   for (int r = 0; r < rows; ++r) {
     const int f = item * rows + r;
-    dma_to_lds<0>(Lp.sg + (size_t)f * a.H, dst + (2 * r) * row, row, w, nw);
-    dma_to_lds<0>(Lp.su + (size_t)f * a.H, dst + (2 * r + 1) * row, row, w, nw);
+    dma_to_lds<0>(Lp.sg + (size_t)f * row, dst + (2 * r) * row, row, w, nw);
+    dma_to_lds<0>(Lp.su + (size_t)f * row, dst + (2 * r + 1) * row, row, w, nw);
   }
 }
 
@@ -667,7 +675,7 @@ __device__ __forceinline__ void copy_down_rows(const A& a, const LayerPtrs& Lp, 
 template <class A>
 __device__ __forceinline__ void copy_sd_rows(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int r0,
                                              int w, int nw) {
-  if (a.Fs) dma_to_lds<0>(Lp.sd + (size_t)r0 * a.Fs, dst, sd_bytes(a), w, nw);
+  if (a.Fs) dma_to_lds<0>(Lp.sd + (size_t)r0 * srow_bytes(a.Fs, a.sq8 != 0), dst, sd_bytes(a), w, nw);
 }
 
 // prefetches issued during barriers
@@ -868,8 +876,32 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
 }
 
 // ------------------------------------------------- shared gate/up item ---
-// Rows [2*item, 2*item+2) from LDS ([row][gate, up][H] bf16), 4 waves per
-// row, each over a quarter of H; fp32 FMA.
+// Weights [h, h+8) of a staged shared-expert row of K weights (h a multiple
+// of 8).  8-bit blocks: w = d*q, exact in fp32 (an 11-bit significand times
+// a 7-bit magnitude); bf16 widens exactly.
+template <class A>
+__device__ __forceinline__ void shared_w8(const A& a, lds_cptr row, int K, int h, float w[8]) {
+  if (a.sq8) {
+    const uint32_t q0 = ld4(row + h), q1 = ld4(row + h + 4);
+    const float d = half_to_f32(ld2(row + K + (h >> 5) * 2));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[c] = d * (float)(int8_t)(q0 >> (8 * c));
+      w[4 + c] = d * (float)(int8_t)(q1 >> (8 * c));
+    }
+  } else {
+    const uint4 v = ld16(row + h * 2);
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[2 * c] = bf16_to_f32(vw[c] & 0xFFFFu);
+      w[2 * c + 1] = bf16_to_f32(vw[c] >> 16);
+    }
+  }
+}
+
+// Rows of the item from LDS ([row][gate, up] shared rows), 8/rows waves
+// per row, each over a slice of H; fp32 FMA.
 // Word offsets of the SwiGLU outputs in the flagged buffer, in the order
 // the down phase copies them into LDS: [ah P*F/4 | al | as P*F/16 | aa | ash T*Fs].
 template <class A>
@@ -903,7 +935,7 @@ __device__ __forceinline__ void shared_gu_item(const A& a, lds_cptr wbase, const
   const int rw = wave / wpr, qtr = wave % wpr;
   const int hq = a.H / wpr;
   const int T = a.T;
-  const uint32_t row = (uint32_t)a.H * 2;
+  const uint32_t row = srow_bytes(a.H, a.sq8 != 0);
   lds_cptr gsrc = wbase + (2 * rw) * row;
   lds_cptr usrc = wbase + (2 * rw + 1) * row;
 #pragma unroll 1
@@ -911,16 +943,15 @@ __device__ __forceinline__ void shared_gu_item(const A& a, lds_cptr wbase, const
     float g = 0.f, u = 0.f;
 #pragma unroll 1
     for (int h = qtr * hq + 8 * lane; h < (qtr + 1) * hq; h += 512) {
-      const uint4 wg = ld16(gsrc + h * 2), wu = ld16(usrc + h * 2);
+      float gw[8], uw[8];
+      shared_w8(a, gsrc, a.H, h, gw);
+      shared_w8(a, usrc, a.H, h, uw);
       const float4 x0 = x_f4<SMALL>(a, L, x, t, h), x1 = x_f4<SMALL>(a, L, x, t, h + 4);
-      const uint32_t gw[4] = {wg.x, wg.y, wg.z, wg.w}, uw[4] = {wu.x, wu.y, wu.z, wu.w};
       const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        g = fmaf(bf16_to_f32(gw[c] & 0xFFFFu), xv[2 * c], g);
-        g = fmaf(bf16_to_f32(gw[c] >> 16), xv[2 * c + 1], g);
-        u = fmaf(bf16_to_f32(uw[c] & 0xFFFFu), xv[2 * c], u);
-        u = fmaf(bf16_to_f32(uw[c] >> 16), xv[2 * c + 1], u);
+      for (int c = 0; c < 8; ++c) {
+        g = fmaf(gw[c], xv[c], g);
+        u = fmaf(uw[c], xv[c], u);
       }
     }
     g = bfly_sum<6>(g);
@@ -1839,8 +1870,8 @@ __device__ __forceinline__ void shared_down_row(const A& a, lds_cptr srow, Persi
     float s = 0.f;
 #pragma unroll 1
     for (int f = 8 * lane; f < a.Fs; f += 512) {
-      const uint4 w = ld16(srow + f * 2);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      float ww[8];
+      shared_w8(a, srow, a.Fs, f, ww);
       float av[8];
       if (SMALL) {
         const float4 a0 = lds_f4(L.dash + t * a.Fs + f);
@@ -1857,10 +1888,7 @@ __device__ __forceinline__ void shared_down_row(const A& a, lds_cptr srow, Persi
         }
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s = fmaf(bf16_to_f32(ww[c] & 0xFFFFu), av[2 * c], s);
-        s = fmaf(bf16_to_f32(ww[c] >> 16), av[2 * c + 1], s);
-      }
+      for (int c = 0; c < 8; ++c) s = fmaf(ww[c], av[c], s);
     }
     s = bfly_sum<6>(s);
     if (lane == 0) L.sh[t * kDownRows + wave] = s;
@@ -1917,7 +1945,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
       }
       for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, base + (uint32_t)(u - u0) * pe, u, L);
       QS_STAMP2(23);
-      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, L.sdr + (uint32_t)wave * a.Fs * 2, L);
+      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, L.sdr + (uint32_t)wave * srow_bytes(a.Fs, a.sq8 != 0), L);
     }
     __syncthreads();
     QS_STAMP(li, 13);
@@ -2032,15 +2060,15 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a
 // One layer shape fixed at compile time.  The launch passes the same values
 // in the runtime fields (the host checks); the static members shadow them,
 // so every loop bound, offset and division by a shape folds to a constant.
-template <int FMT, int H_, int E_, int K_, int F_, int FS_, int T_, int G_>
+template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int T_, int G_>
 struct FixedArgs : PersistArgs {
-  static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, T = T_, G = G_;
+  static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, sq8 = SQ8_, T = T_, G = G_;
   static constexpr int gq2k = FMT == 1, r_et = 1, r_tt = T_;
 };
 
-template <int FMT, int H, int E, int K, int F, int FS, int T, int G>
+template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int T, int G>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_small_fixed(PersistArgs a) {
-  persist_small_body<FMT>(static_cast<const FixedArgs<FMT, H, E, K, F, FS, T, G>&>(a));
+  persist_small_body<FMT>(static_cast<const FixedArgs<FMT, H, E, K, F, FS, SQ8, T, G>&>(a));
 }
 
 }  // namespace qs

@@ -11,9 +11,11 @@ class MoE:
     """qs_moe handle for one model configuration on the current HIP device."""
 
     def __init__(self, hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format,
-                 down_format, n_layers, max_tokens, codebook=None, mfma_min_tokens=0, device=-1):
+                 down_format, n_layers, max_tokens, codebook=None, mfma_min_tokens=0, device=-1,
+                 shared_format="bf16"):
         self.cfg = L.make_config(hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format,
-                                 down_format, n_layers, max_tokens, mfma_min_tokens, device)
+                                 down_format, n_layers, max_tokens, mfma_min_tokens, device,
+                                 shared_format)
         cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
         self._cb = cb
         self.h = L.qs_moe_create(self.cfg, cb)
@@ -22,7 +24,7 @@ class MoE:
     def for_workload(cls, wl, codebook, n_layers=None, max_tokens=64, **kw):
         return cls(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ffn, wl.shared_ffn,
                    wl.gate_up_format, wl.down_format, n_layers or wl.n_layers, max_tokens,
-                   codebook=codebook, **kw)
+                   codebook=codebook, shared_format=getattr(wl, "shared_format", "bf16"), **kw)
 
     # -- lifetime ---------------------------------------------------------
     def close(self):
@@ -102,9 +104,10 @@ class MoE:
         }
 
     def dequant(self, layer, expert, which, stream=None):
+        """which: 0..2 routed gate/up/down of `expert`, 3..5 shared gate/up/down."""
         import torch
-        H, F = self.cfg.hidden, self.cfg.expert_ffn
-        shape = (F, H) if which < 2 else (H, F)
+        H, F, Fs = self.cfg.hidden, self.cfg.expert_ffn, self.cfg.shared_ffn
+        shape = {0: (F, H), 1: (F, H), 2: (H, F), 3: (Fs, H), 4: (Fs, H), 5: (H, Fs)}[which]
         out = torch.empty(shape, dtype=torch.float32, device="cuda")
         L.qs_moe_dequant(self.h, layer, expert, which, out, stream)
         return out

@@ -15,8 +15,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def workload(name, **over):
-    wl = synth.WORKLOADS[name]
+def workload(key, **over):
+    wl = synth.WORKLOADS[key]
     if over:
         d = dict(wl.__dict__)
         d.update(over)

@@ -44,6 +44,18 @@ def test_header_constants_match_binding():
         assert int(defs[name]) == getattr(qm, name), name
 
 
+def test_header_formats_match_binding():
+    text = open(HEADER).read()
+    enum = re.search(r"typedef enum \{([^}]*)\} qs_format;", text).group(1)
+    vals = {n: int(v) for n, v in re.findall(r"(QS_FMT_\w+)\s*=\s*(\d+)", enum)}
+    assert vals == {"QS_FMT_BF16": qm.QS_FMT_BF16, "QS_FMT_Q2K": qm.QS_FMT_Q2K,
+                    "QS_FMT_CB2": qm.QS_FMT_CB2, "QS_FMT_Q8": qm.QS_FMT_Q8}
+    # the config struct's fields, in the header's order
+    body = re.search(r"typedef struct \{([^}]*)\} qs_moe_config;", text).group(1)
+    names = re.findall(r"int32_t\s+(\w+);", body)
+    assert names == [f for f, _ in qm.QsMoeConfig._fields_]
+
+
 def test_status_strings():
     assert qm.status_string(qm.QS_OK) == "ok"
     for s in (qm.QS_E_INVAL, qm.QS_E_NOMEM, qm.QS_E_HIP, qm.QS_E_STATE, qm.QS_E_UNSUPPORTED):
@@ -61,6 +73,7 @@ def _good():
     ("n_experts", 0), ("n_experts", 2048), ("top_k", 0), ("top_k", 17), ("top_k", 32),
     ("shared_ffn", -64), ("shared_ffn", 100), ("gate_up_format", 7), ("down_format", 0),
     ("n_layers", 0), ("max_tokens", 0), ("max_tokens", 257), ("mfma_min_tokens", -1),
+    ("shared_format", 1), ("shared_format", 2), ("shared_format", 4), ("shared_format", -1),
 ])
 def test_create_rejects_invalid_config_without_gpu(field, value):
     kw = _good()
