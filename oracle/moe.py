@@ -13,6 +13,9 @@ What it computes and where that comes from
   DwarfStar page, "Model Weights").
 * Dequantisation fused into the matrix-vector products of single-stream
   decode (Quasar README, "Design decisions" and "Performance model").
+* Optional directional steering of each layer's FFN output,
+  m - scale * d * (d . m), before the residual add (QuarkStar README,
+  "Steering").
 * The pages name the block types but print no layout, no router equations
   and no layer shapes.  The block layouts below, softmax-then-top-k with
   renormalisation, ties to the lower expert index, an ungated shared expert
@@ -286,13 +289,27 @@ def route(lw, x: np.ndarray, k: int, prenorm: bool = False):
     return u, logits, ids, wts, gap
 
 
-def moe_layer(layer: Layer, x: np.ndarray, residual: bool = False, prenorm: bool = False):
+def steer(m: np.ndarray, direction: np.ndarray, scale: float) -> np.ndarray:
+    """Directional steering of an FFN output (QuarkStar README, "Steering"):
+    each row m becomes m - scale * d * (d . m), d the layer's direction taken
+    as given (the pages store unit directions; nothing is normalised here).
+    A positive scale removes the component along a unit d (scale 1 removes
+    it entirely), a negative one amplifies it.  fp64."""
+    m = np.asarray(m, dtype=np.float64)
+    d = np.asarray(direction, dtype=np.float64)
+    proj = m @ d                                   # d . m per row
+    return m - scale * proj[..., None] * d
+
+
+def moe_layer(layer: Layer, x: np.ndarray, residual: bool = False, prenorm: bool = False,
+              steering=None):
     """One decode step of one MoE layer for T tokens.
 
     With u = x (or u = x * rms_inv(x) if prenorm):
-    y[t] = sum_{j<k} w[t][j] * FFN_{ids[t][j]}(u[t]) + S(u[t])  (+ x[t] if
-    residual), with S the ungated shared expert (weight 1) when present and
-    the router evaluated on u.
+    m[t] = sum_{j<k} w[t][j] * FFN_{ids[t][j]}(u[t]) + S(u[t]), with S the
+    ungated shared expert (weight 1) when present and the router evaluated on
+    u; with steering = (direction, scale) m is replaced by steer(m, ...);
+    y[t] = m[t] (+ x[t] if residual).
     Returns a dict with y (fp32 [T][H]), ids, w (fp64), logits, gap.
     """
     wl, lw = layer.wl, layer.lw
@@ -309,20 +326,25 @@ def moe_layer(layer: Layer, x: np.ndarray, residual: bool = False, prenorm: bool
             sg, su, sd = layer.shared()
             _, s = swiglu_ffn(u[t], sg, su, sd)
             y[t] += s
-        if residual:
-            y[t] += x[t].astype(np.float64)
+    if steering is not None:
+        y = steer(y, steering[0], steering[1])
+    if residual:
+        y += x.astype(np.float64)
     return {"y": y.astype(np.float32), "ids": ids, "w": wts, "logits": logits, "gap": gap}
 
 
-def moe_stack(layers, x: np.ndarray, prenorm: bool = True):
+def moe_stack(layers, x: np.ndarray, prenorm: bool = True, steering=None):
     """Stacked layers chained by the residual stream:
     x_{l+1} = x_l + MoE_l(RMSNorm(x_l)) (pre-norm; without the norm an
     un-normalised SwiGLU chain grows without bound), each layer's output
-    rounded to fp32.  Returns the final x and the per-layer results."""
+    rounded to fp32.  steering = (directions [L][H], scale) steers every
+    layer's MoE output with its own direction.  Returns the final x and the
+    per-layer results."""
     outs = []
     cur = np.asarray(x, dtype=np.float32)
-    for layer in layers:
-        r = moe_layer(layer, cur, residual=True, prenorm=prenorm)
+    for l, layer in enumerate(layers):
+        st = None if steering is None else (steering[0][l], steering[1])
+        r = moe_layer(layer, cur, residual=True, prenorm=prenorm, steering=st)
         outs.append(r)
         cur = r["y"]
     return cur, outs
