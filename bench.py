@@ -57,9 +57,13 @@ def parse():
 
 
 # The other workloads the bench line reports beside the headline one: the
-# routed-only 40-layer stack and the 8-layer large-layer stack, at their
-# batch sizes, with fewer timed steps.
-EXTRA = (("a3b_routed40", (1, 4)), ("a3b_stack40_zipf_q8", (1, 4)), ("flash_stack8_zipf", (1, 8, 32)))
+# routed-only 40-layer stack, the stack with an 8-bit shared expert, the
+# headline stack with every layer's output steered, and the 8-layer
+# large-layer stack, at their batch sizes, with fewer timed steps.
+STEERED = "+steer"
+EXTRA = (("a3b_routed40", (1, 4)), ("a3b_stack40_zipf_q8", (1, 4)), ("a3b_stack40_zipf" + STEERED, (1, 4, 16)),
+         ("flash_stack8_zipf", (1, 8, 32)))
+STEER_SCALE = 0.8
 EXTRA_STEPS = 100
 
 
@@ -119,13 +123,14 @@ def kernel_name(wl, T):
     return ("k_persist_small" if small else "k_persist_big") + f"<{fmt}> (one launch = the whole decode call)"
 
 
-def run_workload(qm, wl, L, tok_list, steps, warmup):
-    """Time `steps` decode calls through all L layers at each batch size;
+def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False):
+    """Time `steps` decode calls through all L layers at each batch size
+    (with steer: every layer's output steered along a seeded unit direction);
     returns {T: figures}."""
     import torch
     import synth
     cb = synth.codebook()
-    log(f"[bench] workload {wl.name}: {L} layers, H={wl.hidden} E={wl.n_experts} k={wl.top_k} "
+    log(f"[bench] workload {wl.name}{STEERED if steer else ''}: {L} layers, H={wl.hidden} E={wl.n_experts} k={wl.top_k} "
         f"F={wl.expert_ffn} Fs={wl.shared_ffn}, tokens {list(tok_list)}")
     t0 = time.time()
     moe = qm.MoE.for_workload(wl, cb, n_layers=L, max_tokens=max(tok_list))
@@ -133,15 +138,18 @@ def run_workload(qm, wl, L, tok_list, steps, warmup):
         moe.upload(l, synth.layer_weights(wl, l))
         if l % 10 == 9 or l == L - 1:
             log(f"[bench] uploaded {l + 1}/{L} layers ({time.time() - t0:.1f}s)")
+    if steer:
+        dirs = np.random.default_rng(12).standard_normal((L, wl.hidden))
+        moe.set_steering((dirs / np.linalg.norm(dirs, axis=1, keepdims=True)).astype(np.float32), STEER_SCALE)
     g, u, d = wl.expert_bytes()
     per_expert = g + u + d
-    fixed_layer = wl.router_bytes() + wl.shared_bytes()
+    fixed_layer = wl.router_bytes() + wl.shared_bytes() + (wl.hidden * 4 if steer else 0)
     # decode() launches on torch's current stream; every event below is
     # recorded on that same stream
     stream = torch.cuda.current_stream()
 
     def step(x, y, ids=None):
-        moe.decode(x, y, n_layers=L, residual=True, prenorm=True, ids_out=ids, stream=stream)
+        moe.decode(x, y, n_layers=L, residual=True, prenorm=True, ids_out=ids, stream=stream, steer=steer)
 
     results = {}
     for T in tok_list:
@@ -190,7 +198,7 @@ def run_workload(qm, wl, L, tok_list, steps, warmup):
             "roofline": {"bound": "hbm", "kernel": kernel_name(wl, T), "achieved": achieved,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS},
         }
-        log(f"[bench] {wl.name} T={T}: {ms:.3f} ms/step, {T / (ms * 1e-3):.1f} tok/s, {gbs:.1f} GB/s "
+        log(f"[bench] {wl.name}{STEERED if steer else ''} T={T}: {ms:.3f} ms/step, {T / (ms * 1e-3):.1f} tok/s, {gbs:.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), U={uniq.mean():.1f}, "
             f"launch {launch_ms.mean():.3f} ms (p10 {np.percentile(launch_ms, 10):.3f}, "
             f"p90 {np.percentile(launch_ms, 90):.3f})")
@@ -223,8 +231,9 @@ def main():
         for name, toks in EXTRA:
             if name == wl.name:
                 continue
-            w2 = synth.WORKLOADS[name]
-            r = run_workload(qm, w2, w2.n_layers, toks, min(args.steps, EXTRA_STEPS), args.warmup)
+            steer = name.endswith(STEERED)
+            w2 = synth.WORKLOADS[name[:-len(STEERED)] if steer else name]
+            r = run_workload(qm, w2, w2.n_layers, toks, min(args.steps, EXTRA_STEPS), args.warmup, steer=steer)
             others[name] = {"layers": w2.n_layers, "per_batch": {str(T): v for T, v in r.items()}}
 
     T0 = tok_list[0]

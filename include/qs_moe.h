@@ -93,6 +93,8 @@ typedef enum { QS_FMT_BF16 = 0, QS_FMT_Q2K = 1, QS_FMT_CB2 = 2, QS_FMT_Q8 = 3 } 
                                    without learned weight, as a pre-norm residual
                                    stream applies before each MoE block); without
                                    this flag u_l = x_l */
+#define QS_DECODE_STEER    4u   /* steer each layer's MoE output with the
+                                   handle's directions (qs_moe_set_steering) */
 
 typedef struct qs_moe qs_moe;   /* opaque, owned by the library */
 
@@ -166,8 +168,10 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
  * QuarkStar README, "Server").
  * x: device fp32 [n_tokens][H]; y: device fp32 [n_tokens][H].
  * u_l is x_l, or RMSNorm(x_l) with QS_DECODE_RMSNORM (router and experts both
- * see u_l).  Without QS_DECODE_RESIDUAL: n_layers must be 1 and y = MoE(u);
- * x and y must not overlap.  With it: x_{l+1} = x_l + MoE_l(u_l) layer by
+ * see u_l).  QS_DECODE_STEER steers each layer's MoE output (see
+ * qs_moe_set_steering; QS_E_STATE if no directions are set).
+ * Without QS_DECODE_RESIDUAL: n_layers must be 1 and y = MoE(u); x and y
+ * must not overlap.  With it: x_{l+1} = x_l + MoE_l(u_l) layer by
  * layer and y receives the final x; y == x (in place) is allowed.
  * x and y must be 16-byte aligned.
  * ids_out: device int32 [n_layers][n_tokens][k] or NULL -- selected experts
@@ -193,7 +197,7 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
  * that forbid hipMalloc).  Same arguments, kernels and results as
  * qs_moe_decode, but every per-call scratch buffer (synchronisation words,
  * flagged words, logits, activation limbs, partial outputs) lives in one
- * static device array of 8 MiB per device, which the library holds until
+ * static device array of 12 MiB per device, which the library holds until
  * the process ends; the call allocates nothing and runs no allocating
  * library routine.  QS_E_UNSUPPORTED (nothing enqueued, a message on stderr)
  * when this call's scratch -- sized for n_tokens tokens of the handle's
@@ -220,6 +224,27 @@ QS_API int qs_moe_sync_status(qs_moe* h, void* hip_stream);
  * path and qs_moe_sync_status reports the give-up (tests of the error path).
  * Takes effect from the next decode call.  QS_E_INVAL for polls < 0. */
 QS_API int qs_moe_set_wait_limit(qs_moe* h, int32_t polls);
+
+/* Directional steering of the MoE outputs (QuarkStar README, "Steering": the
+ * FFN output of a layer is edited with the projection of the DwarfStar
+ * engine).  A decode call with QS_DECODE_STEER replaces the MoE output m_l
+ * of every layer l it runs (routed combine plus shared expert, before the
+ * residual add) by
+ *     m_l - scale * d_l * (d_l . m_l)
+ * in fp32, d_l the layer's direction.  With unit directions a positive scale
+ * removes the component along d_l (scale 1 removes it entirely), a negative
+ * one amplifies it.  Routing is unaffected (it reads u_l, not m_l).
+ * dirs: host or device fp32 [n_layers][H], one direction per resident layer,
+ *   used as given (not normalised); copied into device memory the handle
+ *   owns (n_layers * H * 4 bytes, counted by qs_moe_memory_bytes).  NULL
+ *   frees the directions; a later QS_DECODE_STEER call then fails with
+ *   QS_E_STATE (as it does before the first qs_moe_set_steering).
+ * scale: finite, else QS_E_INVAL.
+ * Returns after the copy.  Must not overlap a decode call on the handle.
+ * The steered combine of the small-batch kernel exchanges one more set of
+ * flagged words per layer (the per-workgroup partial dot products); the
+ * batched kernel takes one more grid barrier per layer. */
+QS_API int qs_moe_set_steering(qs_moe* h, const float* dirs, float scale, void* hip_stream);
 
 /* Routing only (diagnostics and tests): the router, top-k and grouping steps
  * of one layer for n_tokens tokens, with every intermediate written out

@@ -15,12 +15,14 @@ QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED = 0, -1, -
 QS_FMT_BF16, QS_FMT_Q2K, QS_FMT_CB2, QS_FMT_Q8 = 0, 1, 2, 3
 QS_DECODE_RESIDUAL = 1
 QS_DECODE_RMSNORM = 2
+QS_DECODE_STEER = 4
 
 FORMATS = {"bf16": QS_FMT_BF16, "q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2, "q8": QS_FMT_Q8}
 
 # Every function include/qs_moe.h declares.
 EXPORTS = (
     "qs_moe_create", "qs_moe_upload", "qs_moe_decode", "qs_moe_decode_static", "qs_moe_sync_status", "qs_moe_set_wait_limit",
+    "qs_moe_set_steering",
     "qs_moe_route", "qs_moe_dequant", "qs_moe_memory_bytes", "qs_moe_destroy", "qs_moe_status_string",
 )
 
@@ -64,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "qs_moe_decode_static": [vp, i32, i32, vp, vp, i32, u32, vp, vp, vp],
         "qs_moe_sync_status": [vp, vp],
         "qs_moe_set_wait_limit": [vp, ctypes.c_int32],
+        "qs_moe_set_steering": [vp, vp, ctypes.c_float, vp],
         "qs_moe_route": [vp, i32, vp, i32, u32, vp, vp, vp, vp, vp],
         "qs_moe_dequant": [vp, i32, i32, i32, vp, vp],
         "qs_moe_memory_bytes": [vp, ctypes.POINTER(ctypes.c_uint64)],
@@ -153,6 +156,10 @@ def qs_moe_sync_status(h: int, stream=None) -> None:
 
 def qs_moe_set_wait_limit(h: int, polls: int) -> None:
     check("qs_moe_set_wait_limit", LIB.qs_moe_set_wait_limit(h, polls))
+
+
+def qs_moe_set_steering(h: int, dirs, scale: float, stream=None) -> None:
+    check("qs_moe_set_steering", LIB.qs_moe_set_steering(h, _ptr(dirs), scale, _stream(stream)))
 
 
 def qs_moe_route(h: int, layer: int, x, n_tokens: int, flags: int = 0, logits_out=None,

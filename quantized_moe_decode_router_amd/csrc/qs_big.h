@@ -1352,7 +1352,65 @@ __device__ __forceinline__ void big_combine(const A& a, const PersistLds& L, con
 }
 
 // ------------------------------------------------------------- kernel ---
-template <int FMT, class A>
+// Steered combine, in two halves around one more grid barrier.  Workgroup b
+// owns rows [b*rpw, (b+1)*rpw) of every token; a group of gl lanes (the
+// rows, gl a power of two) takes one token at a time.  First half: the MoE
+// output m of those rows into mb and the workgroup's partial d . m per token
+// into part[t][b] (lane order, then a fixed tree).  Second half: d . m summed
+// over the G partials in a fixed order, then m - sscale * d * (d . m) (+ x).
+template <class A>
+__device__ __forceinline__ int steer_rows(const A& a) { return (a.H + a.G - 1) / a.G; }
+__device__ __forceinline__ int steer_lanes(int rpw) {
+  int gl = 1;
+  while (gl < rpw && gl < 64) gl <<= 1;
+  return gl;
+}
+
+template <class A>
+__device__ __forceinline__ void big_steer_partials(const A& a, const PersistLds& L, const float* dir) {
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
+  const int rpw = steer_rows(a), gl = steer_lanes(rpw), per = 64 / gl;
+  const int r0 = blockIdx.x * rpw, r1 = r0 + rpw < a.H ? r0 + rpw : a.H;
+  const int g = lane % gl;
+  for (int t0 = wave * per; t0 < a.T; t0 += nw * per) {   // wave-uniform
+    const int t = t0 + lane / gl;
+    float p = 0.f;
+    for (int h = r0 + g; h < r1; h += gl) {
+      if (t >= a.T) break;
+      float acc = 0.f;
+      for (int jj = 0; jj < a.k; ++jj) {
+        const int pos = L.tok_order[t * a.k + jj];
+        acc = fmaf(L.wl[L.pairs[pos]], cldf(&a.ob[(size_t)pos * a.H + h]), acc);
+      }
+      if (a.Fs) acc += cldf(&a.sb[(size_t)t * a.H + h]);
+      cstf(&a.mb[(size_t)t * a.H + h], acc);
+      p = fmaf(dir[h], acc, p);
+    }
+    p = bfly_sum_dyn(p, gl);
+    if (g == 0 && t < a.T) cstf(&a.part[(size_t)t * a.G + blockIdx.x], p);
+  }
+}
+
+template <class A>
+__device__ __forceinline__ void big_steer_apply(const A& a, const float* dir, const float* x, float* y) {
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
+  const int rpw = steer_rows(a);
+  const int r0 = blockIdx.x * rpw, r1 = r0 + rpw < a.H ? r0 + rpw : a.H;
+  if (r0 >= r1) return;
+  for (int t = wave; t < a.T; t += nw) {
+    float dm = 0.f;
+    for (int b = lane; b < a.G; b += 64) dm += cldf(&a.part[(size_t)t * a.G + b]);
+    dm = bfly_sum<6>(dm);   // every lane holds the sum
+    for (int h = r0 + lane; h < r1; h += 64) {
+      const size_t i = (size_t)t * a.H + h;
+      float acc = cldf(&a.mb[i]) - a.sscale * dir[h] * dm;
+      if (a.residual) acc += cldf(&x[i]);
+      cstf(&y[i], acc);
+    }
+  }
+}
+
+template <int FMT, bool STEER, class A>
 __device__ __forceinline__ void persist_big_body(const A& a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   BigL L = carve_big(lds_raw, a, FMT == 2);
@@ -1401,7 +1459,14 @@ __device__ __forceinline__ void persist_big_body(const A& a) {
     if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
     QS_STAMP(li, 8);
     // ---- C
-    big_combine(a, L.P, x, y);
+    if constexpr (STEER) {
+      const float* dir = a.sdir + (size_t)li * a.H;
+      big_steer_partials(a, L.P, dir);
+      if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
+      big_steer_apply(a, dir, x, y);
+    } else {
+      big_combine(a, L.P, x, y);
+    }
     QS_STAMP(li, 9);
     if (more && !grid_barrier(a, ++epoch, [&](int w, int n) {
           if ((int)blockIdx.x < router_groups(a)) copy_router_rows(a, a.layers[li + 1], L.P, blockIdx.x, w, n);
@@ -1410,9 +1475,9 @@ __device__ __forceinline__ void persist_big_body(const A& a) {
   }
 }
 
-template <int FMT>
+template <int FMT, bool STEER>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_big(PersistArgs a) {
-  persist_big_body<FMT>(a);
+  persist_big_body<FMT, STEER>(a);
 }
 
 // The layer shape fixed at compile time, the batch size at run time (as
@@ -1423,9 +1488,9 @@ struct FixedBigArgs : PersistArgs {
   static constexpr int gq2k = FMT == 1, r_et = 1;
 };
 
-template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int G>
+template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int G, bool STEER = false>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_big_fixed(PersistArgs a) {
-  persist_big_body<FMT>(static_cast<const FixedBigArgs<FMT, H, E, K, F, FS, SQ8, G>&>(a));
+  persist_big_body<FMT, STEER>(static_cast<const FixedBigArgs<FMT, H, E, K, F, FS, SQ8, G>&>(a));
 }
 
 }  // namespace qs

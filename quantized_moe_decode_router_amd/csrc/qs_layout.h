@@ -48,6 +48,7 @@ constexpr int kFixedBits = 14;        // |v| <= 2^14 after scaling
 constexpr int kDownRows = 8;          // output rows per down-GEMV workgroup
 constexpr int kGateTile = 16;         // gate/up rows per workgroup task
 constexpr int kMaxTokens = 256;
+constexpr int kMaxGrid = 1024;        // workgroups of a persistent launch (steering partials)
 constexpr int kMaxPairs = 1024;
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

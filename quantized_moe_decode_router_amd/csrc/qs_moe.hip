@@ -7,6 +7,7 @@
 // handle keeps until destroy and re-lays them out with a repack kernel.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -65,7 +66,13 @@ struct Scratch {
   uint64_t* ll_lg;   // small-batch persistent flow: flagged logits, SwiGLU outputs, residual stream
   uint64_t* ll_a;
   uint64_t* llx[2];
+  uint64_t* ll_dot;  // steering partials [T][kMaxGrid]
   size_t ll_bytes;   // bytes of the flagged buffers (contiguous, zeroed at create)
+  float* mb;     // steering: MoE outputs before the projection [T][H] (= sb: the
+                 // batched kernel's steered combine reads each sb entry once,
+                 // in the thread that then writes mb there; the small-batch
+                 // kernel does not use sb)
+  float* part;   // steering: per-workgroup partial dot products [T][kMaxGrid]
   float* af;     // batched persistent flow: SwiGLU outputs of MFMA buckets [P][F]
   float* ob;     // routed down outputs by bucket position [P][H]
   float* sb;     // shared-expert down outputs [T][H]
@@ -109,11 +116,17 @@ struct qs_moe {
   size_t lds_limit = 0;           // LDS bytes per workgroup available on the device
   bool persist_small_ok = false; // T <= kSmallT instantiation usable
   bool persist_big_ok = false;   // batched instantiation usable
+  bool steer_small_ok = false;   // the instantiations with the steered combine usable
+  bool steer_big_ok = false;
   int mfma_min = 1;               // bucket size from which the MFMA path runs
   bool mfma_explicit = false;     // the config set mfma_min_tokens
   bool fixed_ok = false;          // the fixed-shape small-batch kernels are usable
   bool big_fixed_ok = false;      // the fixed-shape batched kernel is usable
+  bool fixed_steer_ok = false;    // the same with the steered combine
+  bool big_fixed_steer_ok = false;
   uint32_t ll_epoch = 0;          // flags used by the small-batch kernel so far
+  float* steer_dirs = nullptr;    // steering directions, device fp32 [n_layers][H] (null: none set)
+  float steer_scale = 0.f;
 };
 
 namespace {
@@ -195,12 +208,12 @@ T* carve(uint8_t*& p, size_t count) {
 
 // Words of the small-batch kernel's flagged buffers (batches of up to kSmallT).
 struct LLWords {
-  size_t lg, a, x;
+  size_t lg, a, x, dot;
 };
 LLWords ll_words(const qs_moe_config& c) {
   const size_t T = std::min(c.max_tokens, kSmallT), P = T * c.top_k, F = c.expert_ffn;
   return LLWords{T * c.n_experts * 2, 2 * P * (F / 4) + 2 * P * (F / 16) + T * (size_t)c.shared_ffn,
-                 T * (size_t)c.hidden};
+                 T * (size_t)c.hidden, T * (size_t)kMaxGrid};
 }
 
 size_t scratch_bytes(const qs_moe_config& c) {
@@ -209,7 +222,7 @@ size_t scratch_bytes(const qs_moe_config& c) {
   size_t b = 0;
   auto add = [&](size_t n) { b += align_up(n, 256); };
   const LLWords lw = ll_words(c);
-  add(lw.lg * 8); add(lw.a * 8); add(lw.x * 8); add(lw.x * 8);
+  add(lw.lg * 8); add(lw.a * 8); add(lw.x * 8); add(lw.x * 8); add(lw.dot * 8);
   add(T * E * 8);                 // logits
   add(P * 4); add(P * 4);         // ids, wts
   add(E * 4); add((E + 1) * 4);   // cnt, off
@@ -223,7 +236,8 @@ size_t scratch_bytes(const qs_moe_config& c) {
   add(T * 8);                     // rinv
   add(P * F * 4);                 // af
   add(P * H * 4);                 // ob
-  add(T * H * 4);                 // sb
+  add(T * H * 4);                 // sb (and mb)
+  add(T * (size_t)kMaxGrid * 4);  // part
   return b;
 }
 
@@ -236,6 +250,7 @@ void carve_scratch(const qs_moe_config& c, Scratch& s) {
   s.ll_a = carve<uint64_t>(p, lw.a);
   s.llx[0] = carve<uint64_t>(p, lw.x);
   s.llx[1] = carve<uint64_t>(p, lw.x);
+  s.ll_dot = carve<uint64_t>(p, lw.dot);
   s.ll_bytes = (size_t)(p - s.base);
   s.logits = carve<double>(p, T * E);
   s.ids = carve<int32_t>(p, P);
@@ -261,12 +276,15 @@ void carve_scratch(const qs_moe_config& c, Scratch& s) {
   s.af = carve<float>(p, P * F);
   s.ob = carve<float>(p, P * H);
   s.sb = carve<float>(p, T * H);
+  s.mb = s.sb;
+  s.part = carve<float>(p, T * (size_t)kMaxGrid);
 }
 
 void free_all(qs_moe* h) {
   for (auto& L : h->layers)
     if (L.base) (void)hipFree(L.base);
   if (h->s.base) (void)hipFree(h->s.base);
+  if (h->steer_dirs) (void)hipFree(h->steer_dirs);
   if (h->cbtab) (void)hipFree(h->cbtab);
   if (h->staging) (void)hipFree(h->staging);
   if (h->d_layers) (void)hipFree(h->d_layers);
@@ -377,22 +395,26 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   return p;
 }
 
-const void* persist_fn(bool cb2, bool small) {
-  if (cb2) return small ? (const void*)k_persist_small<2> : (const void*)k_persist_big<2>;
-  return small ? (const void*)k_persist_small<1> : (const void*)k_persist_big<1>;
+const void* persist_fn(bool cb2, bool small, bool steer = false) {
+  if (steer) {
+    if (cb2) return small ? (const void*)k_persist_small<2, true> : (const void*)k_persist_big<2, true>;
+    return small ? (const void*)k_persist_small<1, true> : (const void*)k_persist_big<1, true>;
+  }
+  if (cb2) return small ? (const void*)k_persist_small<2, false> : (const void*)k_persist_big<2, false>;
+  return small ? (const void*)k_persist_small<1, false> : (const void*)k_persist_big<1, false>;
 }
 
 // Small-batch instantiations with the layer shape fixed at compile time:
 // hidden 2048, 256 experts, top-8, expert width 512, shared width 512
 // (bf16 or 8-bit) or 0, codebook gate/up, one workgroup per CU of a 256-CU
-// device.
-template <int FS, int SQ8>
+// device; with the steered combine (STEER) for the bf16 shared expert.
+template <int FS, int SQ8, bool STEER = false>
 const void* fixed_a3b(int T) {
   switch (T) {
-    case 1: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 1, 256>;
-    case 2: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 2, 256>;
-    case 3: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 3, 256>;
-    case 4: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 4, 256>;
+    case 1: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 1, 256, STEER>;
+    case 2: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 2, 256, STEER>;
+    case 3: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 3, 256, STEER>;
+    case 4: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 4, 256, STEER>;
     default: return nullptr;
   }
 }
@@ -400,10 +422,15 @@ const void* fixed_a3b(int T) {
 // Batched instantiations with the layer shape fixed (the batch size stays a
 // run-time value): the shapes above, and hidden 4096, 256 experts, top-6,
 // expert and shared width 2048.
-const void* persist_big_fixed_fn(const qs_moe* h) {
+const void* persist_big_fixed_fn(const qs_moe* h, bool steer = false) {
   const qs_moe_config& c = h->cfg;
   if (h->grid != 256 || c.gate_up_format != QS_FMT_CB2 || c.n_experts != 256) return nullptr;
   const bool sq8 = c.shared_format == QS_FMT_Q8;
+  if (steer) {
+    if (c.hidden == 2048 && c.top_k == 8 && c.expert_ffn == 512 && c.shared_ffn == 512 && !sq8)
+      return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 0, 256, true>;
+    return nullptr;
+  }
   if (c.hidden == 2048 && c.top_k == 8 && c.expert_ffn == 512) {
     if (c.shared_ffn == 512 && sq8) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 1, 256>;
     if (c.shared_ffn == 512) return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 0, 256>;
@@ -415,11 +442,12 @@ const void* persist_big_fixed_fn(const qs_moe* h) {
 }
 
 // The fixed-shape kernel for a T-token call of this handle, or nullptr.
-const void* persist_fixed_fn(const qs_moe* h, int T) {
+const void* persist_fixed_fn(const qs_moe* h, int T, bool steer = false) {
   const qs_moe_config& c = h->cfg;
   if (h->grid_small != 256 || c.gate_up_format != QS_FMT_CB2 || c.hidden != 2048 || c.n_experts != 256 ||
       c.top_k != 8 || c.expert_ffn != 512)
     return nullptr;
+  if (steer) return c.shared_ffn == 512 && c.shared_format != QS_FMT_Q8 ? fixed_a3b<512, 0, true>(T) : nullptr;
   if (c.shared_ffn == 512 && c.shared_format == QS_FMT_Q8) return fixed_a3b<512, 1>(T);
   if (c.shared_ffn == 512) return fixed_a3b<512, 0>(T);
   if (c.shared_ffn == 0) return fixed_a3b<0, 0>(T);
@@ -428,8 +456,8 @@ const void* persist_fixed_fn(const qs_moe* h, int T) {
 
 // Every workgroup must be resident at once for the grid barrier (a
 // cooperative launch also enforces this).
-bool persist_resident(const qs_moe* h, bool small, size_t lds) {
-  const void* fn = persist_fn(h->cfg.gate_up_format == QS_FMT_CB2, small);
+bool persist_resident(const qs_moe* h, bool small, size_t lds, bool steer = false) {
+  const void* fn = persist_fn(h->cfg.gate_up_format == QS_FMT_CB2, small, steer);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
     (void)hipGetLastError();
     return false;
@@ -468,7 +496,7 @@ int setup_persistent(qs_moe* h) {
   if (!hip_ok(hipGetDeviceProperties(&prop, h->device), "hipGetDeviceProperties")) return QS_E_HIP;
   int coop = 0;
   (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device);
-  h->grid = prop.multiProcessorCount & ~7;
+  h->grid = std::min(prop.multiProcessorCount & ~7, kMaxGrid);
   // The small-batch kernel exchanges data through flagged words that are
   // reused from layer to layer.  A workgroup rewrites layer l's words only
   // after it has seen layer l+1's input complete, which every workgroup
@@ -481,14 +509,15 @@ int setup_persistent(qs_moe* h) {
   // barrier keeps a few bytes there)
   size_t static_lds = 0;
   for (int cb = 0; cb < 2; ++cb)
-    for (int sm = 0; sm < 2; ++sm) {
-      hipFuncAttributes fa;
-      if (hipFuncGetAttributes(&fa, persist_fn(cb != 0, sm != 0)) != hipSuccess) {
-        (void)hipGetLastError();
-        return QS_OK;
+    for (int sm = 0; sm < 2; ++sm)
+      for (int st = 0; st < 2; ++st) {
+        hipFuncAttributes fa;
+        if (hipFuncGetAttributes(&fa, persist_fn(cb != 0, sm != 0, st != 0)) != hipSuccess) {
+          (void)hipGetLastError();
+          return QS_OK;
+        }
+        static_lds = std::max(static_lds, (size_t)fa.sharedSizeBytes);
       }
-      static_lds = std::max(static_lds, (size_t)fa.sharedSizeBytes);
-    }
   const size_t dev_lds = prop.maxSharedMemoryPerMultiProcessor;
   h->lds_limit = dev_lds > static_lds ? (dev_lds - static_lds) & ~(size_t)255 : 0;
   if (!coop || h->grid < 8) return QS_OK;
@@ -504,27 +533,30 @@ int setup_persistent(qs_moe* h) {
   }
   h->persist_small_ok = lds_small && persist_resident(h, true, lds_small);
   h->persist_big_ok = lds_big && persist_resident(h, false, lds_big);
+  h->steer_small_ok = h->persist_small_ok && persist_resident(h, true, lds_small, true);
+  h->steer_big_ok = h->persist_big_ok && persist_resident(h, false, lds_big, true);
+  // fixed-shape instantiations: the same LDS limits, checked one by one
+  auto resident = [](const void* fn, size_t lds) {
+    int occ = 0;
+    const bool ok = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess &&
+                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds) == hipSuccess &&
+                    occ >= 1;
+    (void)hipGetLastError();
+    return ok;
+  };
   if (h->persist_big_ok) {
     const void* fn = persist_big_fixed_fn(h);
-    int occ = 0;
-    h->big_fixed_ok = fn && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_big) ==
-                                hipSuccess &&
-                      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds_big) == hipSuccess &&
-                      occ >= 1;
-    (void)hipGetLastError();
+    h->big_fixed_ok = fn && resident(fn, lds_big);
+    const void* fs = persist_big_fixed_fn(h, true);
+    h->big_fixed_steer_ok = fs && resident(fs, lds_big);
   }
-  // fixed-shape instantiations: the same LDS limit, checked one by one
   h->fixed_ok = h->persist_small_ok;
-  for (int T = 1; T <= kSmallT && h->fixed_ok; ++T) {
+  h->fixed_steer_ok = h->persist_small_ok;
+  for (int T = 1; T <= kSmallT; ++T) {
     const void* fn = persist_fixed_fn(h, T);
-    if (!fn) continue;
-    int occ = 0;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_small) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds_small) != hipSuccess ||
-        occ < 1) {
-      (void)hipGetLastError();
-      h->fixed_ok = false;
-    }
+    if (fn && h->fixed_ok) h->fixed_ok = resident(fn, lds_small);
+    const void* fs = persist_fixed_fn(h, T, true);
+    if (fs && h->fixed_steer_ok) h->fixed_steer_ok = resident(fs, lds_small);
   }
   return QS_OK;
 }
@@ -549,13 +581,16 @@ bool choose_kernel(const qs_moe* h, int T, bool& small, PersistShape& p) {
 
 // The whole decode call as one cooperative launch.
 int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const float* x, float* y, int T,
-                      bool residual, bool prenorm, int32_t* ids_out, float* w_out, hipStream_t st) {
+                      bool residual, bool prenorm, bool steer, int32_t* ids_out, float* w_out, hipStream_t st) {
   const qs_moe_config& c = h->cfg;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
   bool small = false;
   PersistShape p;
   if (!choose_kernel(h, T, small, p)) return QS_E_UNSUPPORTED;   // (create checked every T)
-  const uint32_t barriers = small ? 0u : 5u * nL - 1u;
+  if (steer && !(small ? h->steer_small_ok : h->steer_big_ok)) return QS_E_UNSUPPORTED;
+  // the batched kernel's grid barriers: five per layer (six with steering)
+  // but none after the last
+  const uint32_t barriers = small ? 0u : (steer ? 6u : 5u) * nL - 1u;
   if (small && *cs.ll_epoch > 0xF0000000u - 3u * (uint32_t)nL) {
     // flags are about to wrap: clear the flagged buffers and start again
     launch_zero(cs.zero_base, cs.zero_bytes, st);
@@ -595,15 +630,19 @@ int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const 
   a.ll_lg = s.ll_lg; a.ll_a = s.ll_a; a.llx0 = s.llx[0]; a.llx1 = s.llx[1];
   a.ll_epoch = *cs.ll_epoch;
   a.af = s.af; a.ob = s.ob; a.sb = s.sb;
+  a.ll_dot = s.ll_dot; a.mb = s.mb; a.part = s.part;
+  a.sscale = h->steer_scale;
+  a.sdir = steer ? h->steer_dirs + (size_t)layer0 * c.hidden : nullptr;
   a.sync = cs.sync;
   a.epoch0 = *cs.epoch;
   void* args[] = {&a};
   // the fixed-shape kernel needs the router unit it assumes (one expert per
   // workgroup, all tokens at once)
   const void* fn = nullptr;
-  if (small && h->fixed_ok && p.r_et == 1 && p.r_tt == T) fn = persist_fixed_fn(h, T);
-  if (!small && h->big_fixed_ok && p.r_et == 1) fn = persist_big_fixed_fn(h);
-  if (!fn) fn = persist_fn(cb2, small);
+  if (small && (steer ? h->fixed_steer_ok : h->fixed_ok) && p.r_et == 1 && p.r_tt == T)
+    fn = persist_fixed_fn(h, T, steer);
+  if (!small && (steer ? h->big_fixed_steer_ok : h->big_fixed_ok) && p.r_et == 1) fn = persist_big_fixed_fn(h, steer);
+  if (!fn) fn = persist_fn(cb2, small, steer);
   hipError_t e = hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kPersistThreads), args,
                                             (unsigned)p.lds, st);
   if (e != hipSuccess) {
@@ -647,7 +686,7 @@ int check_decode_args(const qs_moe* h, int layer0, int n_layers, const float* x,
                       int n_tokens, uint32_t flags) {
   if (!h || !x || !y) return QS_E_INVAL;
   const qs_moe_config& c = h->cfg;
-  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM)) return QS_E_INVAL;
+  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM | QS_DECODE_STEER)) return QS_E_INVAL;
   if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
   if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
   const bool residual = flags & QS_DECODE_RESIDUAL;
@@ -655,7 +694,10 @@ int check_decode_args(const qs_moe* h, int layer0, int n_layers, const float* x,
   const size_t act_bytes = (size_t)n_tokens * c.hidden * sizeof(float);
   if (!residual && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
   if (residual && x != y && ranges_overlap(x, act_bytes, y, act_bytes)) return QS_E_INVAL;
-  return check_layer_range(h, layer0, n_layers);
+  const int rc = check_layer_range(h, layer0, n_layers);
+  if (rc) return rc;
+  if ((flags & QS_DECODE_STEER) && !h->steer_dirs) return QS_E_STATE;   // no qs_moe_set_steering
+  return QS_OK;
 }
 
 // ---------------------------------------------- static decode scratch ---
@@ -666,7 +708,7 @@ int check_decode_args(const qs_moe* h, int layer0, int n_layers, const float* x,
 // names a host-side stand-in: its device address, per device, comes from
 // hipGetSymbolAddress once (at the first qs_moe_create on that device) and
 // only that address is passed to kernels.
-constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr size_t kStaticScratchBytes = size_t(12) << 20;
 constexpr size_t kStaticSyncBytes = 4096;       // the sync words, then the carve
 constexpr int kMaxDevices = 64;
 
@@ -911,7 +953,8 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
   if (!dg.ok) return QS_E_HIP;
   const CallState cs{&h->s, h->sync, &h->epoch, &h->ll_epoch, h->s.base, h->s.ll_bytes};
   return launch_persistent(h, cs, layer0, n_layers, x, y, n_tokens, (flags & QS_DECODE_RESIDUAL) != 0,
-                           (flags & QS_DECODE_RMSNORM) != 0, ids_out, w_out, (hipStream_t)hip_stream);
+                           (flags & QS_DECODE_RMSNORM) != 0, (flags & QS_DECODE_STEER) != 0, ids_out, w_out,
+                           (hipStream_t)hip_stream);
 }
 
 QS_API int qs_moe_decode_static(qs_moe* h, int layer0, int n_layers, const float* x, float* y,
@@ -941,7 +984,8 @@ QS_API int qs_moe_decode_static(qs_moe* h, int layer0, int n_layers, const float
   const CallState cs{&s, (uint32_t*)sd.base, &sd.epoch, &sd.ll_epoch, s.base,
                      kStaticScratchBytes - kStaticSyncBytes};
   return launch_persistent(h, cs, layer0, n_layers, x, y, n_tokens, (flags & QS_DECODE_RESIDUAL) != 0,
-                           (flags & QS_DECODE_RMSNORM) != 0, ids_out, w_out, (hipStream_t)hip_stream);
+                           (flags & QS_DECODE_RMSNORM) != 0, (flags & QS_DECODE_STEER) != 0, ids_out, w_out,
+                           (hipStream_t)hip_stream);
 }
 
 QS_API int qs_moe_sync_status(qs_moe* h, void* hip_stream) {
@@ -975,6 +1019,36 @@ QS_API int qs_moe_sync_status(qs_moe* h, void* hip_stream) {
   QS_HIP(hipStreamSynchronize(st));
   fprintf(stderr, "qs_moe: a decode call gave up a bounded wait; its outputs are undefined\n");
   return QS_E_HIP;
+}
+
+QS_API int qs_moe_set_steering(qs_moe* h, const float* dirs, float scale, void* hip_stream) {
+  if (!h || !std::isfinite(scale)) return QS_E_INVAL;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const qs_moe_config& c = h->cfg;
+  const size_t bytes = (size_t)c.n_layers * c.hidden * sizeof(float);
+  if (!dirs) {
+    if (h->steer_dirs) {
+      QS_HIP(hipDeviceSynchronize());   // no decode call still reads them
+      QS_HIP(hipFree(h->steer_dirs));
+      h->total_bytes -= bytes;
+    }
+    h->steer_dirs = nullptr;
+    h->steer_scale = 0.f;
+    return QS_OK;
+  }
+  if (!h->steer_dirs) {
+    if (hipMalloc(&h->steer_dirs, bytes) != hipSuccess) {
+      h->steer_dirs = nullptr;
+      return QS_E_NOMEM;
+    }
+    h->total_bytes += bytes;
+  }
+  QS_HIP(hipMemcpyAsync(h->steer_dirs, dirs, bytes, hipMemcpyDefault, st));
+  QS_HIP(hipStreamSynchronize(st));
+  h->steer_scale = scale;
+  return QS_OK;
 }
 
 QS_API int qs_moe_set_wait_limit(qs_moe* h, int32_t polls) {

@@ -111,6 +111,12 @@ struct PersistArgs {
   uint64_t* llx0;            // [T][H]     residual stream between layers
   uint64_t* llx1;
   uint32_t ll_epoch;         // flags of this call: ll_epoch + 3*layer + {0: x in, 1: logits, 2: SwiGLU}
+  uint64_t* ll_dot;          // [T][G] steering: per-workgroup partial dot products (flag of the SwiGLU words)
+  // steering (the STEER instantiations): m_l -> m_l - sscale * d_l * (d_l . m_l) before the residual add
+  float sscale;
+  const float* sdir;         // [n_layers][H] directions of this call's layers
+  float* mb;                 // [T][H] MoE outputs before steering
+  float* part;               // [T][G] batched flow: per-workgroup partial dot products
   // batched flow only
   int mfma_min;              // bucket size from which the MFMA path runs
   float* af;                 // [T*k][F] SwiGLU outputs of MFMA buckets (by pair id)
@@ -1895,14 +1901,66 @@ __device__ __forceinline__ void shared_down_row(const A& a, lds_cptr srow, Persi
   }
 }
 
+// Steering of the small-batch kernel's layer output (the instantiations
+// with steering compiled in; the others carry none of it).  The combine left each output m of
+// the workgroup's first tile in the register macc of thread idx (dres: its
+// direction entry), those of later tiles in mb.  Every workgroup publishes
+// its partial d . m per token (lanes 8t..8t+7 of wave 0, tile by tile, then
+// a fixed tree) as flagged words, reads all G of them (the same words in
+// every workgroup), sums them per token in a fixed order and writes
+// m - sscale * d * (d . m) (+ x) for its rows.  The partial words are reused
+// from layer to layer, which is safe for the reason the other flagged words
+// are: every workgroup owns output rows.
+template <class A>
+__device__ __forceinline__ bool steer_small(const A& a, const float* dir, float macc, float dres, float xres,
+                                         const float* x, const uint64_t* xll, float* y, uint64_t* yll,
+                                         uint32_t flag, uint32_t flag_y, QS_LDS uint32_t* pw, QS_LDS float* dm,
+                                         QS_LDS int* err) {
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, T = a.T;
+  const int n_tiles = a.H / kDownRows;
+  if (wave == 0) {   // T * kDownRows <= 32 lanes of wave 0 hold a tile's outputs
+    float part = 0.f;
+    const int t = lane / kDownRows;
+    for (int tile = blockIdx.x; tile < n_tiles; tile += a.G) {
+      const int h = tile * kDownRows + lane % kDownRows;
+      const bool first = tile == (int)blockIdx.x;
+      const float m = lane >= T * kDownRows ? 0.f : first ? macc : a.mb[(size_t)t * a.H + h];
+      part += bfly_sum<3>(lane < T * kDownRows ? (first ? dres : dir[h]) * m : 0.f);
+    }
+    if ((lane & 7) == 0 && t < T)
+      ll_store(a.ll_dot + (size_t)t * a.G + blockIdx.x, __float_as_uint(part), flag);
+  }
+  if (!ll_read(a, a.ll_dot, pw, T * a.G, flag, err, ll_waves(a, T * a.G))) return false;
+  if (wave < T) {   // token `wave`: lanes take the partials g = lane + 64 i in order, then a fixed tree
+    float s = 0.f;
+    for (int g = lane; g < a.G; g += 64) s += __uint_as_float(pw[wave * a.G + g]);
+    s = bfly_sum<6>(s);
+    if (lane == 0) dm[wave] = s;
+  }
+  __syncthreads();
+  for (int tile = blockIdx.x; tile < n_tiles; tile += a.G)
+    for (int idx = qs_tid(); idx < T * kDownRows; idx += kPersistThreads) {
+      const int t = idx / kDownRows, h = tile * kDownRows + idx % kDownRows;
+      const size_t xi = (size_t)t * a.H + h;
+      const bool first = tile == (int)blockIdx.x;   // (its output and residual input are in registers)
+      float acc = (first ? macc : a.mb[xi]) - a.sscale * (first ? dres : dir[h]) * dm[t];
+      if (a.residual)
+        acc += first ? xres : (xll ? __uint_as_float((uint32_t)cld64(xll + xi)) : cldf(&x[xi]));
+      if (yll) ll_store(yll + xi, __float_as_uint(acc), flag_y);
+      else cstf(&y[xi], acc);
+    }
+  __syncthreads();   // dm (L.sh) is rewritten by the next layer
+  return true;
+}
+
 // Down phase of the small-batch kernel.  The SwiGLU outputs arrive as
 // flagged words (flag_a); the layer input x is plain (layer 0) or flagged
 // words xll, already checked complete by this workgroup in phase R; the
 // output goes to y (plain, last layer) or as flagged words (flag_y) to yll.
 // The down rows of the first chunk were copied ahead into region B.
 // `spare(w, nw)` runs once, on the waves that have no combine work of the
-// last tile.
-template <class A, class HK>
+// last tile.  STEER: the layer output is steered (steer_small).
+template <bool STEER, class A, class HK>
 __device__ __forceinline__ bool phase_down_small(const A& a, int li, const LayerPtrs& Lp, const float* x,
                                                  const uint64_t* xll, float* y, uint64_t* yll, uint32_t flag_a,
                                                  uint32_t flag_y, PersistLds& L, HK&& spare) {
@@ -1920,10 +1978,15 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
     const size_t xi = (size_t)(qs_tid() / kDownRows) * a.H + blockIdx.x * kDownRows + qs_tid() % kDownRows;
     xres = xll ? __uint_as_float((uint32_t)cld64(xll + xi)) : cldf(&x[xi]);
   }
+  // steering: the direction entries of the first tile, also before the waits
+  const float* dir = STEER ? a.sdir + (size_t)li * a.H : nullptr;
+  const float dres = dir && qs_tid() < T * kDownRows && (int)blockIdx.x < n_tiles
+                         ? dir[blockIdx.x * kDownRows + qs_tid() % kDownRows] : 0.f;
   // every pair's SwiGLU limbs and the shared SwiGLU vector -> LDS (on the
   // waves without down-row copies in flight, when the words fit them)
   if (!ll_read(a, a.ll_a, (QS_LDS uint32_t*)L.dah, ll_a_words(a), flag_a, L.llerr, ll_a_waves(a))) return false;
   QS_STAMP(li, 11);
+  float macc = 0.f;   // steering: this thread's output of the first tile (idx = thread)
   wait_all_and_sync();   // the down rows copied ahead
   QS_STAMP(li, 12);
   for (int tile = blockIdx.x; tile < n_tiles; tile += a.G) {
@@ -1959,6 +2022,11 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
         acc = fmaf(L.cw[t * a.k + jj], L.o[pos * kDownRows + rr], acc);
       }
       if (a.Fs) acc += L.sh[idx];
+      if (dir) {        // kept until the layer's d . m is known
+        if (first) macc = acc;
+        else a.mb[(size_t)t * a.H + h] = acc;
+        continue;
+      }
       if (a.residual) {
         const size_t xi = (size_t)t * a.H + h;
         acc += first && own_res && idx == qs_tid() ? xres
@@ -1971,6 +2039,10 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
     __syncthreads();     // L.o and L.sh are rewritten by the next tile
   }
   if ((int)blockIdx.x >= n_tiles && wave >= copy_w0(a)) spare(wave - copy_w0(a), kPersistThreads / 64 - copy_w0(a));
+  // (the SwiGLU limbs are consumed: their LDS takes the partial words)
+  if (dir)
+    return steer_small(a, dir, macc, dres, own_res ? xres : 0.f, x, xll, y, yll, flag_a, flag_y,
+                       (QS_LDS uint32_t*)L.dah, L.sh, L.llerr);
   return true;
 }
 
@@ -1978,7 +2050,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
 // The small-batch kernel (T <= kSmallT); qs_big.h holds the batched one.
 // Every step takes its arguments as `const A&`: PersistArgs, or FixedArgs,
 // whose compile-time shape constants shadow the runtime fields.
-template <int FMT, class A>
+template <int FMT, bool STEER, class A>
 __device__ __forceinline__ void persist_small_body(const A& a) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   PersistLds L = carve_lds<true>(lds_raw, a, FMT == 2);
@@ -2038,7 +2110,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     // ---- D; region A is free: the next layer's router rows and shared
     // items are issued beside the combine
     QS_STAMP(li, 10);
-    if (!phase_down_small(a, li, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L, [&](int w, int n) {
+    if (!phase_down_small<STEER>(a, li, Lp, a.x_in, xll, a.y_out, yll, fl + 2, fl + 3, L, [&](int w, int n) {
           if (!more) return;
           pf_router_and_shared<true>(a, Ln, L, w, n);
           // the shared down rows are no longer read by this layer
@@ -2051,10 +2123,11 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
   }
 }
 
-// Any shape: the layer shapes come from the arguments.
-template <int FMT>
+// Any shape: the layer shapes come from the arguments.  STEER: with the
+// steered combine (every layer's output steered).
+template <int FMT, bool STEER>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a) {
-  persist_small_body<FMT>(a);
+  persist_small_body<FMT, STEER>(a);
 }
 
 // One layer shape fixed at compile time.  The launch passes the same values
@@ -2066,9 +2139,9 @@ struct FixedArgs : PersistArgs {
   static constexpr int gq2k = FMT == 1, r_et = 1, r_tt = T_;
 };
 
-template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int T, int G>
+template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int T, int G, bool STEER = false>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_small_fixed(PersistArgs a) {
-  persist_small_body<FMT>(static_cast<const FixedArgs<FMT, H, E, K, F, FS, SQ8, T, G>&>(a));
+  persist_small_body<FMT, STEER>(static_cast<const FixedArgs<FMT, H, E, K, F, FS, SQ8, T, G>&>(a));
 }
 
 }  // namespace qs

@@ -55,25 +55,27 @@ class MoE:
                         None if lw.shared_down is None else c(lw.shared_down), stream)
 
     def decode(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
-               w_out=None, stream=None):
+               w_out=None, stream=None, steer=False):
         """One qs_moe_decode call (one persistent kernel launch) on `stream`
         (torch's current stream by default); asynchronous."""
         import torch
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
-        flags = (L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
+        flags = ((L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
+                 | (L.QS_DECODE_STEER if steer else 0))
         L.qs_moe_decode(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
 
     def decode_static(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
-                      w_out=None, stream=None):
+                      w_out=None, stream=None, steer=False):
         """qs_moe_decode_static: decode with the library's static device scratch."""
         import torch
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
-        flags = (L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
+        flags = ((L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
+                 | (L.QS_DECODE_STEER if steer else 0))
         L.qs_moe_decode_static(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
 
@@ -84,6 +86,14 @@ class MoE:
 
     def set_wait_limit(self, polls):
         L.qs_moe_set_wait_limit(self.h, polls)
+
+    def set_steering(self, dirs, scale=1.0, stream=None):
+        """qs_moe_set_steering: directions fp32 [n_layers][H] (numpy or torch,
+        host or device), or None to clear them."""
+        if dirs is not None and not hasattr(dirs, "data_ptr"):
+            dirs = np.ascontiguousarray(dirs, dtype=np.float32)
+        self._steer = dirs      # keeps a host array alive across the call
+        L.qs_moe_set_steering(self.h, dirs, float(scale), stream)
 
     def route(self, x, layer=0, prenorm=False, stream=None):
         import torch

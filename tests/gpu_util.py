@@ -42,14 +42,14 @@ def oracle_layer(wl, lw):
 
 
 def check_layer(wl, lw, x_np, y_gpu, ids_gpu=None, w_gpu=None, residual=False, prenorm=False,
-                label="", tokens=None):
+                label="", tokens=None, steering=None):
     """Compare one layer's GPU outputs with the oracle (optionally only the
     token rows in ``tokens``); returns max rel-L2."""
     if tokens is not None:
         x_np, y_gpu = x_np[tokens], y_gpu[tokens]
         ids_gpu = None if ids_gpu is None else ids_gpu[tokens]
         w_gpu = None if w_gpu is None else w_gpu[tokens]
-    ref = om.moe_layer(oracle_layer(wl, lw), x_np, residual=residual, prenorm=prenorm)
+    ref = om.moe_layer(oracle_layer(wl, lw), x_np, residual=residual, prenorm=prenorm, steering=steering)
     assert np.all(ref["gap"] > 1e-9), f"{label}: near-tie in the routing set"
     if ids_gpu is not None:
         assert np.array_equal(ids_gpu, ref["ids"]), f"{label}: expert ids differ"

@@ -396,7 +396,9 @@ def test_error_statuses_with_gpu(lib):
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), x.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr() + 4, y.data_ptr(), 2, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 16, None, None, st) == lib.QS_E_INVAL
-        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 4, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 8, None, None, st) == lib.QS_E_INVAL
+        # steering asked for before any directions were set
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 4, None, None, st) == lib.QS_E_STATE
         assert L.qs_moe_decode(moe.h, 2, 1, x.data_ptr(), y.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_dequant(moe.h, 0, wl.n_experts, 0, y.data_ptr(), st) == lib.QS_E_INVAL
         assert L.qs_moe_dequant(moe.h, 0, 0, 3, y.data_ptr(), st) == lib.QS_E_INVAL

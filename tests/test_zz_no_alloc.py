@@ -46,15 +46,15 @@ def test_static_scratch_matches_decode(lib, name, L, Ts):
 
 
 def test_static_scratch_refuses_oversize(lib):
-    """The large-layer shape at 32 tokens needs more scratch than the static
+    """The large-layer shape at 64 tokens needs more scratch than the static
     array holds: QS_E_UNSUPPORTED, nothing enqueued; 8 tokens fit."""
     wl = workload("flash_stack8_zipf")
-    moe, _ = make_handle(lib, wl, n_layers=1, max_tokens=32)
+    moe, _ = make_handle(lib, wl, n_layers=1, max_tokens=64)
     with moe:
-        say("static scratch flash T=32 (refused) and T=8")
-        x = torch.from_numpy(synth.tokens(wl, 32, 1)).cuda()
+        say("static scratch flash T=64 (refused) and T=8")
+        x = torch.from_numpy(synth.tokens(wl, 64, 1)).cuda()
         y = torch.empty_like(x)
-        rc = lib.LIB.qs_moe_decode_static(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 32, 0, None, None,
+        rc = lib.LIB.qs_moe_decode_static(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 64, 0, None, None,
                                           torch.cuda.current_stream().cuda_stream)
         assert rc == lib.QS_E_UNSUPPORTED
         _pair(lib, moe, wl, 8, 1, 3)
