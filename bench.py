@@ -119,7 +119,10 @@ def copy_calibration(mib: int):
 
 def kernel_name(wl, T):
     fmt = "cb2" if wl.gate_up_format == "cb2" else "q2k"
-    small = T <= 4 and wl.hidden <= 2048
+    # the small-batch kernel: batches up to 4 at hidden sizes up to 2048, and
+    # the large-layer shape's fixed instantiation at one token
+    small = T <= 4 and (wl.hidden <= 2048 or (T == 1 and wl.hidden == 4096 and wl.top_k == 6
+                                                and wl.expert_ffn == 2048 and wl.shared_ffn == 2048))
     return ("k_persist_small" if small else "k_persist_big") + f"<{fmt}> (one launch = the whole decode call)"
 
 

@@ -345,6 +345,8 @@ int gu_units(int H) {
   return (slots >= kGateTile ? 1 : kGateTile / slots) * (nch / lpr);
 }
 
+const void* persist_fixed_fn(const qs_moe* h, int T, bool steer = false);
+
 PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   const qs_moe_config& c = h->cfg;
   if (!small) return big_shape(h, T);
@@ -376,10 +378,12 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
     p.pfa = (uint32_t)A;
     // the routed gate/up tiles stream through registers (at most kGuUnits
     // (row, chunk) units per thread and tile), not through the staging buffer
-    // Hidden sizes above 2048 take the batched kernel: on the 4096-wide
-    // large-layer shape the small-batch kernel, which streams its shared
-    // items and down rows one staging at a time, measured 5 % slower.
-    fits = A <= p.pfb && (p.pfb - A) + xl >= pe && gu_units(c.hidden) <= kGuUnits && c.hidden <= 2048;
+    // Hidden sizes above 2048 take the small-batch kernel only in a
+    // fixed-shape instantiation: on the 4096-wide large-layer shape at T = 1
+    // the generic one measured 83 us per layer against the batched kernel's
+    // 73, the fixed one 57.
+    fits = A <= p.pfb && (p.pfb - A) + xl >= pe && gu_units(c.hidden) <= kGuUnits &&
+           (c.hidden <= 2048 || persist_fixed_fn(h, T) != nullptr);
     (void)sd;
     // each flagged read is at most 32 words per thread
     const uint64_t P = (uint64_t)T * c.top_k;
@@ -441,9 +445,16 @@ const void* persist_big_fixed_fn(const qs_moe* h, bool steer = false) {
   return nullptr;
 }
 
-// The fixed-shape kernel for a T-token call of this handle, or nullptr.
-const void* persist_fixed_fn(const qs_moe* h, int T, bool steer = false) {
+// The fixed-shape kernel for a T-token call of this handle, or nullptr:
+// the A3B shapes above at T = 1..4, and the large-layer shape (hidden 4096,
+// 256 experts, top-6, expert and shared width 2048, bf16 shared expert) at
+// T = 1.
+const void* persist_fixed_fn(const qs_moe* h, int T, bool steer) {
   const qs_moe_config& c = h->cfg;
+  if (!steer && T == 1 && h->grid_small == 256 && c.gate_up_format == QS_FMT_CB2 && c.hidden == 4096 &&
+      c.n_experts == 256 && c.top_k == 6 && c.expert_ffn == 2048 && c.shared_ffn == 2048 &&
+      c.shared_format == QS_FMT_BF16)
+    return (const void*)k_persist_small_fixed<2, 4096, 256, 6, 2048, 2048, 0, 1, 256>;
   if (h->grid_small != 256 || c.gate_up_format != QS_FMT_CB2 || c.hidden != 2048 || c.n_experts != 256 ||
       c.top_k != 8 || c.expert_ffn != 512)
     return nullptr;
