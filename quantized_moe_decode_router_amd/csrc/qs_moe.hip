@@ -353,8 +353,11 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   PersistShape p;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
   const bool sq8 = c.shared_format == QS_FMT_Q8;
+  // the shared expert through registers: the fixed-shape kernels above
+  // hidden 2048 (sh_regs), the only small-batch kernels there
+  const bool shregs = c.hidden > 2048;
   const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, sq8, cb2,
-                                 small, 0).end;
+                                 small, 0, shregs).end;
   if (base >= h->lds_limit || h->grid_small < 8) return p;
   p.pfb = (uint32_t)std::min((size_t)kPfbMax, (h->lds_limit - base) & ~(size_t)15);
   p.lds = base + p.pfb;
@@ -367,12 +370,12 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   auto a16 = [](uint64_t v) { return (v + 15) & ~15ull; };
   bool fits;
   if (small) {
-    // region A: router rows + one shared item (phase R); regions A and B:
-    // gate/up tiles (K, GU); region B and the x limbs after it: experts'
-    // down rows (D).  The shared down rows have their own slot.
-    // one shared gate/up row per item above hidden 2048, two otherwise (sh_rows)
-    const uint64_t sitem = (H > 2048 ? 2 : 4) * (uint64_t)srow_bytes(c.hidden, sq8);
-    const uint64_t r_sh = a16(rb) + (Fs ? sitem : 0);
+    // region A: router rows + one shared item (phase R; no item when the
+    // shared expert streams through registers); region B and the x limbs
+    // after it: experts' down rows (D).  The shared down rows have their own
+    // slot (none with registers).
+    const uint64_t sitem = 4 * (uint64_t)srow_bytes(c.hidden, sq8);
+    const uint64_t r_sh = a16(rb) + (Fs && !shregs ? sitem : 0);
     const uint64_t xl = 2 * a16((uint64_t)T * H) + 2 * a16((uint64_t)T * H / 4);
     const uint64_t A = a16(r_sh);
     p.pfa = (uint32_t)A;
@@ -384,6 +387,9 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
     // 73, the fixed one 57.
     fits = A <= p.pfb && (p.pfb - A) + xl >= pe && gu_units(c.hidden) <= kGuUnits &&
            (c.hidden <= 2048 || persist_fixed_fn(h, T) != nullptr);
+    // with registers: a row's chunks per lane fit one register round
+    if (shregs)
+      fits = fits && (H / 4 + 511) / 512 <= (uint64_t)kShPairsLds && (Fs + 511) / 512 <= (uint64_t)kShDnRegs;
     (void)sd;
     // each flagged read is at most 32 words per thread
     const uint64_t P = (uint64_t)T * c.top_k;

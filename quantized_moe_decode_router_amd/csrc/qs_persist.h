@@ -49,6 +49,8 @@ namespace qs {
 
 constexpr int kPersistThreads = 512;
 constexpr int kSmallT = 4;
+constexpr int kShPairsLds = 8;        // shared gate/up items per register round (their LDS partials)
+constexpr int kShDnRegs = 8;          // shared down chunks per thread per register round
 constexpr int kSpinMax = 1 << 22;
 constexpr int kLLSpinMax = 1 << 16;    // polls of a flagged read (about 0.1 s) before it gives up
 // sync words (uint32 index): [16*x] per-XCD counters, [128] global counter,
@@ -71,6 +73,7 @@ struct LayerPtrs {
 };
 
 struct PersistArgs {
+  static constexpr bool kFixedShape = false;
   const LayerPtrs* layers;   // device array, first entry = layer0
   int G;                     // workgroups of the launch (a multiple of 8)
   int n_layers, T, H, E, k, F, Fs;
@@ -386,7 +389,7 @@ struct LdsLayout {
 __host__ __device__ inline int kf_stride(int E) { return (E + 7) & ~7; }
 
 __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int F, int Fs, bool sq8, bool cb2,
-                                                bool small, uint32_t pfb) {
+                                                bool small, uint32_t pfb, bool shregs = false) {
   LdsLayout l;
   uint32_t o = 0;
   auto take = [&](uint32_t n) {
@@ -412,7 +415,7 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.red = take(8 * 64 * 8);
   l.sh = take((uint32_t)T * kDownRows * 4);
   l.ga = take((uint32_t)T * kGateTile * 4);
-  l.sred = take((uint32_t)8 * T * 2 * 4);
+  l.sred = take((uint32_t)(shregs ? kShPairsLds : 1) * 8 * T * 2 * 4);
   l.qtmp = take((uint32_t)T * kGateTile * 4);
   l.rinv = take((uint32_t)T * 8);
   // SMALL top-k: keys [T][S], group maxima [T][S/8], thresholds [T]
@@ -431,7 +434,7 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.xl = take(xq);
   l.xs = take(xq / 4);      // T*H/16 floats
   l.xa = take(xq / 4);
-  l.sdr = take(small ? (uint32_t)kDownRows * srow_bytes(Fs, sq8) : 0);
+  l.sdr = take(small && !shregs ? (uint32_t)kDownRows * srow_bytes(Fs, sq8) : 0);
   l.end = o;
   return l;
 }
@@ -481,7 +484,7 @@ struct PersistLds {
 template <bool SMALL, class A>
 __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const A& a, bool cb2) {
   const uint32_t T = a.T, H = a.H, E = a.E, F = a.F, P = T * a.k;
-  const LdsLayout l = lds_layout(E, T, P, H, F, a.Fs, a.sq8 != 0, cb2, SMALL, a.pfb);
+  const LdsLayout l = lds_layout(E, T, P, H, F, a.Fs, a.sq8 != 0, cb2, SMALL, a.pfb, SMALL && sh_regs(a));
   QS_LDS uint8_t* b = (QS_LDS uint8_t*)raw;
   PersistLds L;
   L.tab = (QS_LDS uint32_t*)(b + l.tab);
@@ -543,11 +546,16 @@ __device__ __forceinline__ int router_groups(const A& a) { return (a.E + a.r_et 
 template <class A>
 __device__ __forceinline__ uint32_t router_bytes(const A& a) { return (uint32_t)a.r_et * a.H * 4; }
 
-// Shared gate/up rows per item: the small-batch kernel takes one row at a
-// time for hidden sizes above 2048 (its staging region then still holds a
-// router row and an item), two otherwise; the batched kernel always two.
+// Shared gate/up rows per item (both kernels).
 template <bool SMALL, class A>
-__device__ __forceinline__ int sh_rows(const A& a) { return SMALL && a.H > 2048 ? 1 : kSharedItemRows; }
+__device__ __forceinline__ int sh_rows(const A& a) { return kSharedItemRows; }
+// The small-batch kernel's shared expert streams through registers instead
+// of LDS staging in its fixed-shape instantiations of hidden sizes above
+// 2048 (the only ones above 2048): there the rows are too many to prefetch a
+// layer ahead, and staging them would crowd the routed down rows out of LDS.
+// Below, LDS staging a layer ahead by the copy waves measured faster.
+template <class A>
+__device__ __forceinline__ bool sh_regs(const A& a) { return A::kFixedShape && a.H > 2048; }
 template <bool SMALL, class A>
 __device__ __forceinline__ int n_shared_items(const A& a) { return a.Fs / sh_rows<SMALL>(a); }
 template <bool SMALL, class A>
@@ -689,7 +697,7 @@ template <bool SMALL, class A>
 __device__ __forceinline__ void pf_router_and_shared(const A& a, const LayerPtrs& Lp, PersistLds& L,
                                                      int w, int nw) {
   if ((int)blockIdx.x < router_groups(a)) copy_router_rows(a, Lp, L, blockIdx.x, w, nw);
-  if (SMALL) {
+  if (SMALL && !sh_regs(a)) {
     const int n = shared_pf_count<true>(a);
     for (int j = 0; j < n; ++j)
       copy_shared_item<true>(a, Lp, L.pfb + shared_off<true>(a) + (uint32_t)j * shared_item_bytes<true>(a),
@@ -998,6 +1006,200 @@ __device__ __forceinline__ void shared_items(const A& a, const LayerPtrs& Lp, co
       stage_now([&](int w, int n) { copy_shared_item<SMALL>(a, Lp, L.pfb + off, it, w, n); });
     }
     shared_gu_item<SMALL>(a, L.pfb + slot, x, it, L, flag);
+  }
+}
+
+// ------------------------------ shared expert through registers (SMALL) ---
+// With sh_regs the small-batch kernel streams the shared expert's rows from
+// HBM straight into registers (no LDS staging).  A 16-byte chunk holds 8
+// weights: bf16, or (8-bit rows) 8 code bytes with the block's scale bits
+// in .z.
+// Chunks per thread in flight: (gate, up) pairs and down chunks.
+template <class A>
+constexpr int sh_pairs() { return kShPairsLds; }
+template <class A>
+constexpr int sh_dn_regs() { return kShDnRegs; }
+
+template <class A>
+__device__ __forceinline__ uint4 sh_chunk_load(const A& a, const uint8_t* row, int K, int h) {
+  if (a.sq8) {
+    const uint2 q = *(const uint2*)(row + h);
+    return make_uint4(q.x, q.y, *(const uint16_t*)(row + K + (h >> 5) * 2), 0u);
+  }
+  return *(const uint4*)(row + (size_t)h * 2);
+}
+// the 8 weights of a chunk (the values shared_w8 gives)
+template <class A>
+__device__ __forceinline__ void sh_chunk_decode(const A& a, uint4 v, float w[8]) {
+  if (a.sq8) {
+    const float d = half_to_f32(v.z);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[c] = d * (float)(int8_t)(v.x >> (8 * c));
+      w[4 + c] = d * (float)(int8_t)(v.y >> (8 * c));
+    }
+  } else {
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[2 * c] = bf16_to_f32(vw[c] & 0xFFFFu);
+      w[2 * c + 1] = bf16_to_f32(vw[c] >> 16);
+    }
+  }
+}
+
+// Gate/up: item `it` is rows [2 it, 2 it + 2); waves 4r..4r+3 take row r,
+// wave quarter q covers h in [q H/4, (q+1) H/4) with lane chunks
+// h = q H/4 + 8 lane + 512 i -- the batched kernel's mapping, so both
+// kernels produce bitwise the same SwiGLU values.  A round holds
+// sh_pairs / ni items (ni chunks per lane); the workgroup's items are
+// it = b + j G.  (A round never exceeds the items a workgroup has, so the
+// fixed-shape kernels keep only the registers they use.)
+template <class A>
+__device__ __forceinline__ int sh_gu_chunks(const A& a) { return (a.H / 4 + 511) / 512; }
+template <class A>
+__device__ __forceinline__ int sh_gu_round(const A& a) {   // (at most the items any workgroup has)
+  const int cap = sh_pairs<A>() / sh_gu_chunks(a), most = (n_shared_items<true>(a) + a.G - 1) / a.G;
+  return cap < most ? cap : most;
+}
+
+template <class A, int NP>
+__device__ __forceinline__ void sh_gu_issue(const A& a, const LayerPtrs& Lp, int j0, uint4 (&g)[NP],
+                                            uint4 (&u)[NP]) {
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
+  const int rw = wave >> 2, qtr = wave & 3, hq = a.H / 4, ni = sh_gu_chunks(a), nr = sh_gu_round(a);
+  const uint32_t rb = srow_bytes(a.H, a.sq8 != 0);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int k = p / ni, i = p % ni;
+    const int it = (int)blockIdx.x + (j0 + k) * a.G;
+    const int h = qtr * hq + 8 * lane + 512 * i;
+    if (k < nr && it < n_shared_items<true>(a) && h < (qtr + 1) * hq) {
+      const size_t f = (size_t)it * kSharedItemRows + rw;
+      g[p] = sh_chunk_load(a, Lp.sg + f * rb, a.H, h);
+      u[p] = sh_chunk_load(a, Lp.su + f * rb, a.H, h);
+    }
+  }
+}
+
+// The SwiGLU outputs of the round's items (x, the RMS scales in LDS) as
+// flagged words.
+template <class A, int NP>
+__device__ __forceinline__ void sh_gu_compute(const A& a, const uint4 (&g)[NP], const uint4 (&u)[NP], int j0,
+                                              PersistLds& L, uint32_t flag) {
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, T = a.T;
+  const int qtr = wave & 3, hq = a.H / 4, ni = sh_gu_chunks(a), nr = sh_gu_round(a);
+  float ga[kSmallT], ua[kSmallT];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int k = p / ni, i = p % ni;
+    const int it = (int)blockIdx.x + (j0 + k) * a.G;
+    if (k >= nr || it >= n_shared_items<true>(a)) break;   // (wave-uniform)
+    if (i == 0) {
+#pragma unroll
+      for (int t = 0; t < kSmallT; ++t) ga[t] = ua[t] = 0.f;
+    }
+    const int h = qtr * hq + 8 * lane + 512 * i;
+    if (h < (qtr + 1) * hq) {
+      float wg[8], wu[8];
+      sh_chunk_decode(a, g[p], wg);
+      sh_chunk_decode(a, u[p], wu);
+#pragma unroll
+      for (int t = 0; t < kSmallT; ++t) {
+        if (t >= T) break;
+        const float4 x0 = lds_f4(L.ax + t * a.H + h), x1 = lds_f4(L.ax + t * a.H + h + 4);
+        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          ga[t] = fmaf(wg[c], xv[c], ga[t]);
+          ua[t] = fmaf(wu[c], xv[c], ua[t]);
+        }
+      }
+    }
+    if (i == ni - 1) {
+#pragma unroll
+      for (int t = 0; t < kSmallT; ++t) {
+        if (t >= T) break;
+        const float gs = bfly_sum<6>(ga[t]), us = bfly_sum<6>(ua[t]);
+        if (lane == 0) {
+          L.sred[((k * 8 + wave) * T + t) * 2] = gs;
+          L.sred[((k * 8 + wave) * T + t) * 2 + 1] = us;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // the 4 wave partials of each row in a fixed order
+  int nk = 0;
+  for (int k = 0; k < nr; ++k)
+    if ((int)blockIdx.x + (j0 + k) * a.G < n_shared_items<true>(a)) nk = k + 1;
+  for (int q = qs_tid(); q < nk * kSharedItemRows * T; q += kPersistThreads) {
+    const int k = q / (kSharedItemRows * T), r = (q / T) % kSharedItemRows, t = q % T;
+    float gg = 0.f, uu = 0.f;
+    for (int w4 = 0; w4 < 4; ++w4) {
+      gg += L.sred[((k * 8 + r * 4 + w4) * T + t) * 2];
+      uu += L.sred[((k * 8 + r * 4 + w4) * T + t) * 2 + 1];
+    }
+    const float rs = (float)L.rinv[t];
+    const int ff = ((int)blockIdx.x + (j0 + k) * a.G) * kSharedItemRows + r;
+    ll_store(a.ll_a + ll_ash(a) + (size_t)t * a.Fs + ff, __float_as_uint(silu_mul(gg * rs, uu * rs)), flag);
+  }
+  __syncthreads();
+}
+
+// Down: wave w takes row 8 tile + w of each of the workgroup's tiles
+// (tile = b + j G), lane chunks f = 8 lane + 512 i -- the batched kernel's
+// mapping.  A round holds sh_dn_regs / nd tiles (nd chunks per lane).
+template <class A>
+__device__ __forceinline__ int sh_dn_chunks(const A& a) { return (a.Fs + 511) / 512; }
+template <class A>
+__device__ __forceinline__ int sh_dn_round(const A& a) {   // (at most the tiles any workgroup has)
+  const int cap = sh_dn_regs<A>() / sh_dn_chunks(a), most = (a.H / kDownRows + a.G - 1) / a.G;
+  return cap < most ? cap : most;
+}
+
+template <class A, int ND>
+__device__ __forceinline__ void sh_dn_issue(const A& a, const LayerPtrs& Lp, int j0, uint4 (&v)[ND]) {
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63;
+  const int nd = sh_dn_chunks(a), nr = sh_dn_round(a), n_tiles = a.H / kDownRows;
+  const uint32_t rb = srow_bytes(a.Fs, a.sq8 != 0);
+#pragma unroll
+  for (int p = 0; p < ND; ++p) {
+    const int j = p / nd, i = p % nd;
+    const int tile = (int)blockIdx.x + (j0 + j) * a.G, f = 8 * lane + 512 * i;
+    if (j < nr && tile < n_tiles && f < a.Fs)
+      v[p] = sh_chunk_load(a, Lp.sd + (size_t)(tile * kDownRows + wave) * rb, a.Fs, f);
+  }
+}
+
+// The shared down outputs of round-local tile j (its rows' chunks in v) for
+// every token, from the shared SwiGLU vector in LDS, into L.sh[t][row].
+template <class A, int ND>
+__device__ __forceinline__ void sh_dn_compute(const A& a, const uint4 (&v)[ND], int j, PersistLds& L) {
+  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, T = a.T, nd = sh_dn_chunks(a);
+  float s[kSmallT];
+#pragma unroll
+  for (int t = 0; t < kSmallT; ++t) s[t] = 0.f;
+#pragma unroll
+  for (int p = 0; p < ND; ++p) {
+    const int i = p - j * nd, f = 8 * lane + 512 * i;
+    if (i < 0 || i >= nd || f >= a.Fs) continue;
+    float w[8];
+    sh_chunk_decode(a, v[p], w);
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) {
+      if (t >= T) break;
+      const float4 a0 = lds_f4(L.dash + t * a.Fs + f), a1 = lds_f4(L.dash + t * a.Fs + f + 4);
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s[t] = fmaf(w[c], av[c], s[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kSmallT; ++t) {
+    if (t >= T) break;
+    const float r = bfly_sum<6>(s[t]);
+    if (lane == 0) L.sh[t * kDownRows + wave] = r;
   }
 }
 
@@ -1986,6 +2188,12 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
   // waves without down-row copies in flight, when the words fit them)
   if (!ll_read(a, a.ll_a, (QS_LDS uint32_t*)L.dah, ll_a_words(a), flag_a, L.llerr, ll_a_waves(a))) return false;
   QS_STAMP(li, 11);
+  // sh_regs: the shared down rows of this workgroup's first tiles, into
+  // registers (after the wait, which their loads would delay); they land
+  // during the routed down GEMVs
+  static_assert(kDownRows == kPersistThreads / 64, "one shared down row per wave");
+  uint4 sdv[sh_dn_regs<A>()];
+  if (sh_regs(a) && a.Fs) sh_dn_issue(a, Lp, 0, sdv);
   float macc = 0.f;   // steering: this thread's output of the first tile (idx = thread)
   wait_all_and_sync();   // the down rows copied ahead
   QS_STAMP(li, 12);
@@ -1997,7 +2205,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
       const int u1 = na - u0 < chunk ? na : u0 + chunk;
       if (!first || u0 > 0) {
         stage_now([&](int w, int n) {
-          if (u0 == 0) copy_sd_rows(a, Lp, L.sdr, r0, w, n);
+          if (u0 == 0 && !sh_regs(a)) copy_sd_rows(a, Lp, L.sdr, r0, w, n);
           for (int c0 = u0; c0 < u1; c0 += 64) {
             const int el = act_lanes(L, c0, u1);
             const int m = u1 - c0 < 64 ? u1 - c0 : 64;
@@ -2008,7 +2216,15 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
       }
       for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, base + (uint32_t)(u - u0) * pe, u, L);
       QS_STAMP2(23);
-      if (u0 == 0 && a.Fs && wave < kDownRows) shared_down_row<true>(a, L.sdr + (uint32_t)wave * srow_bytes(a.Fs, a.sq8 != 0), L);
+      if (u0 == 0 && a.Fs) {
+        if (!sh_regs(a)) {
+          shared_down_row<true>(a, L.sdr + (uint32_t)wave * srow_bytes(a.Fs, a.sq8 != 0), L);
+        } else {
+          const int jr = (tile - (int)blockIdx.x) / a.G, nr = sh_dn_round(a);
+          if (jr > 0 && jr % nr == 0) sh_dn_issue(a, Lp, jr, sdv);   // the next round of rows
+          sh_dn_compute(a, sdv, jr % nr, L);
+        }
+      }
     }
     __syncthreads();
     QS_STAMP(li, 13);
@@ -2059,7 +2275,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
   if (FMT == 2) dma_to_lds<0>(a.cbtab, L.tab, (uint32_t)kCbTabWords * 4, wave, nw);
   LayerPtrs Lp = a.layers[0];
   pf_router_and_shared<true>(a, Lp, L, wave, nw);
-  if ((int)blockIdx.x * kDownRows < a.H)
+  if (!sh_regs(a) && (int)blockIdx.x * kDownRows < a.H)
     copy_sd_rows(a, Lp, L.sdr, blockIdx.x * kDownRows, wave, nw);
   wait_all_and_sync();
   for (int li = 0; li < a.n_layers; ++li) {
@@ -2074,12 +2290,25 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     if (li == 0) dma_to_lds<kCoherent>(a.x_in, L.ax, (uint32_t)a.T * a.H * 4, wave, nw);
     else if (!ll_read(a, xll, (QS_LDS uint32_t*)L.ax, a.T * a.H, fl, L.llerr, ll_waves(a, a.T * a.H))) return;
     QS_STAMP(li, 1);
-    wait_all_and_sync();   // (and this layer's router rows and shared items)
+    // sh_regs: the first round of this workgroup's shared gate/up rows is
+    // requested into registers now (after the wait, which its loads would
+    // delay) and lands during the router
+    uint4 shg[sh_pairs<A>()], shu[sh_pairs<A>()];
+    if (sh_regs(a) && a.Fs) sh_gu_issue(a, Lp, 0, shg, shu);
+    wait_all_and_sync();   // (and this layer's router rows and staged shared items)
     QS_STAMP(li, 2);
     if ((int)blockIdx.x >= router_groups(a)) token_rinv<true>(a, L, a.x_in, 0, a.T);
     phase_router<true>(a, Lp, a.x_in, L, fl + 1);   // ends with a block barrier
     QS_STAMP(li, 3);
-    shared_items<true>(a, Lp, a.x_in, L, fl + 2);
+    if (!sh_regs(a)) {
+      shared_items<true>(a, Lp, a.x_in, L, fl + 2);
+    } else if (a.Fs) {
+      const int nr = sh_gu_round(a), mine = my_count(a, n_shared_items<true>(a));
+      for (int j0 = 0; j0 < mine; j0 += nr) {
+        if (j0 > 0) sh_gu_issue(a, Lp, j0, shg, shu);
+        sh_gu_compute(a, shg, shu, j0, L, fl + 2);
+      }
+    }
     QS_STAMP(li, 4);
     // ---- K: logits -> LDS, top-k, grouping, routed tiles -> LDS, x limbs
     if (!ll_read(a, a.ll_lg, (QS_LDS uint32_t*)L.lg, 2 * a.T * a.E, fl + 1, L.llerr)) return;
@@ -2114,7 +2343,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
           if (!more) return;
           pf_router_and_shared<true>(a, Ln, L, w, n);
           // the shared down rows are no longer read by this layer
-          if ((int)blockIdx.x * kDownRows < a.H)
+          if (!sh_regs(a) && (int)blockIdx.x * kDownRows < a.H)
             copy_sd_rows(a, Ln, L.sdr, blockIdx.x * kDownRows, w, n);
         }))
       return;
@@ -2137,6 +2366,7 @@ template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int T_, in
 struct FixedArgs : PersistArgs {
   static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, sq8 = SQ8_, T = T_, G = G_;
   static constexpr int gq2k = FMT == 1, r_et = 1, r_tt = T_;
+  static constexpr bool kFixedShape = true;
 };
 
 template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int T, int G, bool STEER = false>
