@@ -118,6 +118,56 @@ def dequant_cb2(blocks: np.ndarray, codebook: np.ndarray) -> np.ndarray:
     return w.astype(np.float32).reshape(*lead, 256)
 
 
+# Q4_K-style block, 144 bytes per 256 weights (the 4-bit type the pages keep
+# the routed experts of the last layers at -- QuarkStar README, "Model
+# Weights": the Layers34-39Q4KExperts model; DwarfStar page, "Model
+# Weights": q2 with the last 6 layers at q4):
+#   bytes 0..1    d (fp16)          bytes 2..3   dmin (fp16)
+#   bytes 4..15   scales[12]: eight 6-bit (sc, m) pairs, one per 32-weight
+#                 sub-block j:  j < 4:  sc = scales[j] & 63,
+#                                       m  = scales[j + 4] & 63
+#                               j >= 4: sc = (scales[j + 4] & 15) | (scales[j - 4] >> 6) << 4,
+#                                       m  = (scales[j + 4] >> 4) | (scales[j] >> 6) << 4
+#   bytes 16..143 qs[128]: weights 64c + r of chunk c = 0..3 take the low
+#                 nibble of qs[32c + r] for r < 32, the high nibble of
+#                 qs[32c + r - 32] for r >= 32
+#   w_j = d * sc * q_j - dmin * m   (sc, m of sub-block j // 32)
+
+
+def q4k_scales(scales: np.ndarray):
+    """12 packed scale bytes [..., 12] -> (sc [..., 8], m [..., 8]) as int64."""
+    b = np.asarray(scales, dtype=np.int64)
+    sc = np.empty(b.shape[:-1] + (8,), dtype=np.int64)
+    m = np.empty_like(sc)
+    for j in range(8):
+        if j < 4:
+            sc[..., j] = b[..., j] & 63
+            m[..., j] = b[..., j + 4] & 63
+        else:
+            sc[..., j] = (b[..., j + 4] & 15) | ((b[..., j - 4] >> 6) << 4)
+            m[..., j] = (b[..., j + 4] >> 4) | ((b[..., j] >> 6) << 4)
+    return sc, m
+
+
+def dequant_q4k(blocks: np.ndarray) -> np.ndarray:
+    """Raw Q4_K-style blocks [..., 144] uint8 -> fp32 weights [..., 256]."""
+    blk = np.asarray(blocks, dtype=np.uint8)
+    lead = blk.shape[:-1]
+    blk = blk.reshape(-1, 144)
+    d = fp16_bits_to_f64(blk[:, 0].astype(np.uint16) | (blk[:, 1].astype(np.uint16) << 8))[:, None]
+    dmin = fp16_bits_to_f64(blk[:, 2].astype(np.uint16) | (blk[:, 3].astype(np.uint16) << 8))[:, None]
+    sc, m = q4k_scales(blk[:, 4:16])
+    j = np.arange(256)
+    c, r = j // 64, j % 64
+    byte = blk[:, 16:144][:, 32 * c + (r % 32)].astype(np.int64)
+    q = np.where(r < 32, byte & 15, byte >> 4)
+    sub = j // 32
+    # exact in fp64 (products of at most 21 significant bits), then one
+    # rounding to fp32
+    w = d * sc[:, sub] * q - dmin * m[:, sub]
+    return w.astype(np.float32).reshape(*lead, 256)
+
+
 # 8-bit block, 34 bytes per 32 weights (the Q8_0 type the pages use for the
 # tensors they keep at 8 bits -- QuarkStar README, "Model Weights" (Q8 rest);
 # DwarfStar page, "Distributed Inference" (Q8 shared experts)):
@@ -139,11 +189,13 @@ def dequant_q8(blocks: np.ndarray) -> np.ndarray:
 
 def dequant_matrix(raw: np.ndarray, fmt: str, codebook=None) -> np.ndarray:
     """Raw matrix [rows][cols/block][block bytes] -> fp32 [rows][cols]
-    (blocks of 256 weights for q2k/cb2, of 32 for q8)."""
+    (blocks of 256 weights for q2k/q4k/cb2, of 32 for q8)."""
     raw = np.asarray(raw, dtype=np.uint8)
     rows, nb = raw.shape[0], raw.shape[1]
     if fmt == "q2k":
         w = dequant_q2k(raw)
+    elif fmt == "q4k":
+        w = dequant_q4k(raw)
     elif fmt == "cb2":
         w = dequant_cb2(raw, codebook)
     elif fmt == "q8":
@@ -245,10 +297,12 @@ class Layer:
         if e not in self._cache:
             i = self._slot[e]
             wl, lw = self.wl, self.lw
+            gfmt = getattr(lw, "gate_up_format", None) or wl.gate_up_format
+            dfmt = getattr(lw, "down_format", None) or wl.down_format
             self._cache[e] = (
-                dequant_matrix(lw.gate[i], wl.gate_up_format, self.codebook),
-                dequant_matrix(lw.up[i], wl.gate_up_format, self.codebook),
-                dequant_matrix(lw.down[i], wl.down_format, self.codebook),
+                dequant_matrix(lw.gate[i], gfmt, self.codebook),
+                dequant_matrix(lw.up[i], gfmt, self.codebook),
+                dequant_matrix(lw.down[i], dfmt, self.codebook),
             )
         return self._cache[e]
 

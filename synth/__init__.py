@@ -6,6 +6,6 @@ dequantisation, no routing, no products); both the HIP library and the CPU
 oracle consume what it produces.
 """
 from .gen import (  # noqa: F401
-    WORKLOADS, Workload, codebook, q2k_blocks, cb2_blocks, block_bytes,
+    WORKLOADS, Workload, codebook, q2k_blocks, cb2_blocks, q4k_blocks, block_bytes,
     expert_tensor, layer_weights, tokens, fp32_to_bf16_bits,
 )

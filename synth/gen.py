@@ -16,6 +16,9 @@ workload; the pages themselves print no weights):
 * the codebook: 256 rows x 8 entries, each uniform over {1, 3, 5, 7};
 * router weights fp32 ~ N(0, 0.02^2); an optional Zipf(s) expert-popularity
   bias b[e] = -s * ln(1 + rank(e)) with rank a seeded permutation;
+* the routed experts of a stack's tail layers (the pages' models with the
+  last layers' experts at 4 bits) as Q4_K-style blocks, fields uniform and
+  d, dmin = fp16(U[0,1) * 2^-14);
 * the shared expert in bf16 ~ N(0, 0.02^2), rounded to nearest even;
 * token activations fp32 ~ N(0, 1).
 
@@ -31,6 +34,7 @@ import numpy as np
 # Block geometry of the two routed-expert formats (bytes per 256 weights).
 Q2K_BLOCK_BYTES = 84
 CB2_BLOCK_BYTES = 70
+Q4K_BLOCK_BYTES = 144
 BLOCK_WEIGHTS = 256
 # 8-bit shared-expert blocks: 32 weights, fp16 scale + 32 int8 codes
 Q8_BLOCK_BYTES = 34
@@ -58,15 +62,24 @@ class Workload:
     zipf_s: Optional[float] = None
     note: str = ""
     shared_format: str = "bf16"   # "bf16" or "q8" (8-bit blocks of 32)
+    tail_layers: int = 0          # the last tail_layers layers hold their experts as "q4k"
 
     def block_bytes(self, fmt: str) -> int:
         return block_bytes(fmt)
 
-    def expert_bytes(self) -> Tuple[int, int, int]:
-        """Bytes of one expert's gate, up and down matrices in the raw format."""
+    def layer_formats(self, layer: int) -> Tuple[str, str]:
+        """(gate/up format, down format) of a layer's routed experts."""
+        if layer >= self.n_layers - self.tail_layers:
+            return "q4k", "q4k"
+        return self.gate_up_format, self.down_format
+
+    def expert_bytes(self, layer: int = 0) -> Tuple[int, int, int]:
+        """Bytes of one expert's gate, up and down matrices in the raw format
+        (of layer `layer`)."""
         H, F = self.hidden, self.expert_ffn
-        g = F * (H // BLOCK_WEIGHTS) * block_bytes(self.gate_up_format)
-        d = H * (F // BLOCK_WEIGHTS) * block_bytes(self.down_format)
+        gf, df = self.layer_formats(layer)
+        g = F * (H // BLOCK_WEIGHTS) * block_bytes(gf)
+        d = H * (F // BLOCK_WEIGHTS) * block_bytes(df)
         return g, g, d
 
     def router_bytes(self) -> int:
@@ -79,17 +92,19 @@ class Workload:
         return n * 2
 
     def stored_bytes(self) -> int:
-        g, u, d = self.expert_bytes()
-        per_layer = self.n_experts * (g + u + d) + self.router_bytes() + self.shared_bytes()
-        return self.n_layers * per_layer
+        total = 0
+        for l in range(self.n_layers):
+            g, u, d = self.expert_bytes(l)
+            total += self.n_experts * (g + u + d) + self.router_bytes() + self.shared_bytes()
+        return total
 
     def step_bytes(self, distinct_experts_per_layer, n_tokens: int) -> int:
         """Algorithmic bytes one decode step must read and write: per layer the
         router, the shared expert and each distinct selected expert once, plus
         the activations in and out."""
-        g, u, d = self.expert_bytes()
         total = 0
-        for u_l in distinct_experts_per_layer:
+        for l, u_l in enumerate(distinct_experts_per_layer):
+            g, u, d = self.expert_bytes(l)
             total += self.router_bytes() + self.shared_bytes() + int(u_l) * (g + u + d)
         return total + 2 * n_tokens * self.hidden * 4
 
@@ -116,6 +131,11 @@ WORKLOADS = {
     "a3b_stack40_zipf_q8": Workload("a3b_stack40_zipf_q8", 6, 2048, 256, 8, 512, 512, "cb2", "q2k", 40,
                                     (1, 4), zipf_s=1.1, shared_format="q8",
                                     note="40-layer A3B stack, 8-bit shared expert, Zipf(1.1) popularity"),
+    # the A3B stack with the last 6 layers' experts at a Q4_K type (the
+    # pages' Layers34-39Q4KExperts model)
+    "a3b_stack40_q4tail": Workload("a3b_stack40_q4tail", 7, 2048, 256, 8, 512, 512, "cb2", "q2k", 40,
+                                   (1, 4, 16), zipf_s=1.1, tail_layers=6,
+                                   note="40-layer A3B stack, layers 34-39 with Q4_K-style experts"),
     # DeepSeek-V4-Flash-class large layer, 8 stacked
     "flash_stack8_zipf": Workload("flash_stack8_zipf", 4, 4096, 256, 6, 2048, 2048, "cb2", "q2k", 8,
                                   (1, 8, 32), zipf_s=1.1,
@@ -128,6 +148,8 @@ def block_bytes(fmt: str) -> int:
         return Q2K_BLOCK_BYTES
     if fmt == "cb2":
         return CB2_BLOCK_BYTES
+    if fmt == "q4k":
+        return Q4K_BLOCK_BYTES
     raise ValueError(f"unknown block format {fmt!r}")
 
 
@@ -182,6 +204,17 @@ def cb2_blocks(rng: np.random.Generator, nblocks: int, out=None) -> np.ndarray:
     return raw
 
 
+def q4k_blocks(rng: np.random.Generator, nblocks: int, out=None) -> np.ndarray:
+    """nblocks raw Q4_K-style blocks [nblocks][144]: d (bytes 0..1) and dmin
+    (2..3) fp16(U[0,1)*2^-14), every other byte uniform."""
+    raw = out if out is not None else np.empty((nblocks, Q4K_BLOCK_BYTES), dtype=np.uint8)
+    raw = raw.reshape(nblocks, Q4K_BLOCK_BYTES)
+    raw[:] = np.frombuffer(rng.bytes(nblocks * Q4K_BLOCK_BYTES), dtype=np.uint8).reshape(nblocks, Q4K_BLOCK_BYTES)
+    u = rng.random((nblocks, 2), dtype=np.float32) * np.float32(2.0 ** -14)
+    raw[:, 0:4] = u.astype(np.float16).view(np.uint16).view(np.uint8).reshape(nblocks, 4)
+    return raw
+
+
 def q8_blocks(rng: np.random.Generator, nblocks: int) -> np.ndarray:
     """nblocks 8-bit blocks [nblocks][34]: d (bytes 0..1) fp16(U[0,1)*2^-11),
     then 32 int8 codes uniform over [-128, 127]."""
@@ -195,14 +228,15 @@ def expert_tensor(wl: Workload, layer: int, tensor: int, expert: int, out=None) 
     """Raw bytes of one expert matrix, shape [rows][cols/256][block bytes]:
     gate/up are [F][H/256] blocks, down is [H][F/256] blocks."""
     H, F = wl.hidden, wl.expert_ffn
+    gf, df = wl.layer_formats(layer)
     if tensor in (T_GATE, T_UP):
-        rows, kb, fmt = F, H // BLOCK_WEIGHTS, wl.gate_up_format
+        rows, kb, fmt = F, H // BLOCK_WEIGHTS, gf
     elif tensor == T_DOWN:
-        rows, kb, fmt = H, F // BLOCK_WEIGHTS, wl.down_format
+        rows, kb, fmt = H, F // BLOCK_WEIGHTS, df
     else:
         raise ValueError("not an expert tensor")
     rng = _rng(wl.seed_id, layer, tensor, expert)
-    gen = q2k_blocks if fmt == "q2k" else cb2_blocks
+    gen = {"q2k": q2k_blocks, "cb2": cb2_blocks, "q4k": q4k_blocks}[fmt]
     return gen(rng, rows * kb, out).reshape(rows, kb, block_bytes(fmt))
 
 
@@ -219,6 +253,8 @@ class LayerWeights:
     shared_up: Optional[np.ndarray] = None     # the same layout as shared_gate
     shared_down: Optional[np.ndarray] = None   # bf16 bits [H][Fs], or 8-bit blocks [H][Fs/32][34]
     experts: Tuple[int, ...] = field(default_factory=tuple)
+    gate_up_format: Optional[str] = None       # this layer's routed formats
+    down_format: Optional[str] = None
 
 
 def layer_weights(wl: Workload, layer: int, experts=None) -> LayerWeights:
@@ -233,7 +269,8 @@ def layer_weights(wl: Workload, layer: int, experts=None) -> LayerWeights:
         rank = _rng(wl.seed_id, layer, T_BIAS, 0).permutation(E)
         bias = (-wl.zipf_s * np.log1p(rank.astype(np.float64))).astype(np.float32)
     H, F = wl.hidden, wl.expert_ffn
-    bg, bd = block_bytes(wl.gate_up_format), block_bytes(wl.down_format)
+    gf, df = wl.layer_formats(layer)
+    bg, bd = block_bytes(gf), block_bytes(df)
     gate = np.empty((len(ex), F, H // BLOCK_WEIGHTS, bg), dtype=np.uint8)
     up = np.empty_like(gate)
     down = np.empty((len(ex), H, F // BLOCK_WEIGHTS, bd), dtype=np.uint8)
@@ -241,7 +278,7 @@ def layer_weights(wl: Workload, layer: int, experts=None) -> LayerWeights:
         expert_tensor(wl, layer, T_GATE, e, gate[i])
         expert_tensor(wl, layer, T_UP, e, up[i])
         expert_tensor(wl, layer, T_DOWN, e, down[i])
-    lw = LayerWeights(router, bias, gate, up, down, experts=ex)
+    lw = LayerWeights(router, bias, gate, up, down, experts=ex, gate_up_format=gf, down_format=df)
     if Fs and wl.shared_format == "q8":
         def q8(tid, rows, cols):
             return q8_blocks(_rng(wl.seed_id, layer, tid, 0), rows * cols // Q8_BLOCK_WEIGHTS).reshape(

@@ -122,6 +122,15 @@ def test_handworked_block(case):
     elif fmt == "q8":
         blk = pack_q8(d=int(kv.get("d", "0"), 16), q=_indexed(kv, "q", 32))
         w = om.dequant_q8(blk)
+    elif fmt == "q4k":
+        # raw bytes, no encoder: the byte offsets themselves are what is pinned
+        blk = np.zeros(144, dtype=np.uint8)
+        for name, off in (("d", 0), ("dmin", 2)):
+            v = int(kv.get(name, "0"), 16)
+            blk[off], blk[off + 1] = v & 0xFF, v >> 8
+        raw = _indexed(kv, "b", 144, 16)
+        blk[4:] = raw[4:]
+        w = om.dequant_q4k(blk)
     else:
         blk = pack_cb2(d=int(kv.get("d", "0"), 16), s=_indexed(kv, "s", 8),
                        idx=_indexed(kv, "idx", 32), sign=_indexed(kv, "sign", 32, 16))
@@ -136,6 +145,7 @@ def test_golden_file_has_cases():
     cases = _parse_golden()
     assert sum(c[0] == "q2k" for c in cases) >= 8 and sum(c[0] == "cb2" for c in cases) >= 8
     assert sum(c[0] == "q8" for c in cases) >= 6
+    assert sum(c[0] == "q4k" for c in cases) >= 8
 
 
 # ---------------------------------------------------- layout invariants ---
@@ -312,7 +322,7 @@ def _fp16_bits(v):
     return int(np.array([v], dtype=np.float16).view(np.uint16)[0])
 
 
-@pytest.mark.parametrize("fmt", ["q2k", "cb2", "q8"])
+@pytest.mark.parametrize("fmt", ["q2k", "cb2", "q8", "q4k"])
 def test_dequant_matrix_block_order(fmt):
     """A matrix is [rows][cols/256] blocks, row-major: block (r, b) holds
     columns 256*b .. 256*b+255 of row r.  Every block here decodes to the
@@ -328,6 +338,13 @@ def test_dequant_matrix_block_order(fmt):
                 row.append(pack_q2k(d=d, sc=np.ones(16, int), q=np.ones(256, int)))
             elif fmt == "cb2":  # w = d*1*C[0][j%8] with an all-ones codebook row 0
                 row.append(pack_cb2(d=d, s=np.ones(8, int)))
+            elif fmt == "q4k":  # every sc = 1 (bytes 4..7 and the low nibbles of 12..15), m = 0, codes 1
+                blk = np.zeros(144, dtype=np.uint8)
+                blk[0], blk[1] = d & 0xFF, d >> 8
+                blk[4:8] = 1
+                blk[12:16] = 1
+                blk[16:144] = 0x11
+                row.append(blk)
             else:              # w = d*1
                 row.append(pack_q8(d=d, q=np.ones(32, int)))
         raw.append(row)
@@ -338,6 +355,66 @@ def test_dequant_matrix_block_order(fmt):
     for r in range(rows):
         for b in range(nb):
             assert np.all(w[r, bw * b:bw * (b + 1)] == np.float32(r * nb + b + 1)), (r, b)
+
+
+def _rand_q4k(rng):
+    blk = rng.integers(0, 256, 144).astype(np.uint8)
+    for off in (0, 2):   # normal fp16 d and dmin
+        v = _fp16_bits(float(rng.uniform(0.25, 2.0)))
+        blk[off], blk[off + 1] = v & 0xFF, v >> 8
+    return blk
+
+
+def test_q4k_each_code_nibble_moves_only_its_weight():
+    rng = np.random.default_rng(41)
+    for _ in range(4):
+        blk = _rand_q4k(rng)
+        w0 = om.dequant_q4k(blk)
+        for byte in range(128):
+            c, r = byte // 32, byte % 32
+            for hi in (0, 1):
+                b2 = blk.copy()
+                b2[16 + byte] ^= 0xF0 if hi else 0x0F
+                moved = np.nonzero(om.dequant_q4k(b2) != w0)[0]
+                want = 64 * c + r + 32 * hi
+                assert set(moved) <= {want}, (byte, hi, moved)
+
+
+def test_q4k_each_scale_byte_moves_only_its_sub_blocks():
+    """Byte 4+j (j < 4) holds sc of sub-block j (low 6 bits) and the top bits
+    of sc of sub-block j+4; byte 8+j holds m of j and the top bits of m of
+    j+4; byte 12+j holds the low nibbles of sc and m of sub-block j+4."""
+    rng = np.random.default_rng(42)
+    owners = {}
+    for j in range(4):
+        owners[4 + j] = {j, j + 4}
+        owners[8 + j] = {j, j + 4}
+        owners[12 + j] = {j + 4}
+    for _ in range(4):
+        blk = _rand_q4k(rng)
+        blk[16:144] = 0x77   # every code 7: every sub-block shows its sc
+        w0 = om.dequant_q4k(blk)
+        for byte, subs in owners.items():
+            for bit in range(8):
+                b2 = blk.copy()
+                b2[byte] ^= 1 << bit
+                moved = set(np.nonzero(om.dequant_q4k(b2) != w0)[0] // 32)
+                assert moved and moved <= subs, (byte, bit, moved)
+                low6 = byte < 12 and bit < 6
+                if low6:      # the low 6 bits belong to sub-block byte%4 only
+                    assert moved == {(byte - 4) % 4}, (byte, bit, moved)
+
+
+def test_q4k_exact_linearity_in_d_and_dmin():
+    rng = np.random.default_rng(43)
+    for _ in range(8):
+        blk = _rand_q4k(rng)
+        w = om.dequant_q4k(blk).astype(np.float64)
+        b2 = blk.copy()
+        for off in (0, 2):   # exponent + 1: exactly twice the value (normal fp16)
+            v = (int(b2[off]) | int(b2[off + 1]) << 8) + 0x0400
+            b2[off], b2[off + 1] = v & 0xFF, v >> 8
+        assert np.array_equal(om.dequant_q4k(b2).astype(np.float64), 2 * w)
 
 
 def test_q8_code_bytes_are_signed_and_linear():

@@ -9,9 +9,9 @@ import synth
 from oracle import moe as om
 
 
-def _tiny(gate_up="q2k", shared=0, E=8, k=2, zipf=None, L=1, shared_format="bf16"):
+def _tiny(gate_up="q2k", shared=0, E=8, k=2, zipf=None, L=1, shared_format="bf16", tail=0):
     return synth.Workload("pin", 99, 256, E, k, 256, shared, gate_up, "q2k", L, (1,), zipf_s=zipf,
-                          shared_format=shared_format)
+                          shared_format=shared_format, tail_layers=tail)
 
 
 def _dense_reference(wl, lw, cb, x):
@@ -26,10 +26,11 @@ def _dense_reference(wl, lw, cb, x):
     mask = torch.zeros(lg.shape, dtype=torch.float64)
     mask.scatter_(1, idx, wts)
     y = torch.zeros((x.shape[0], wl.hidden), dtype=torch.float64)
+    gf, df = lw.gate_up_format, lw.down_format
     for e in range(wl.n_experts):
-        wg = torch.from_numpy(om.dequant_matrix(lw.gate[e], wl.gate_up_format, cb).astype(np.float64))
-        wu = torch.from_numpy(om.dequant_matrix(lw.up[e], wl.gate_up_format, cb).astype(np.float64))
-        wd = torch.from_numpy(om.dequant_matrix(lw.down[e], wl.down_format, cb).astype(np.float64))
+        wg = torch.from_numpy(om.dequant_matrix(lw.gate[e], gf, cb).astype(np.float64))
+        wu = torch.from_numpy(om.dequant_matrix(lw.up[e], gf, cb).astype(np.float64))
+        wd = torch.from_numpy(om.dequant_matrix(lw.down[e], df, cb).astype(np.float64))
         o = (torch.nn.functional.silu(xt @ wg.T) * (xt @ wu.T)) @ wd.T
         y += mask[:, e:e + 1] * o
     if wl.shared_ffn and wl.shared_format == "q8":
@@ -43,11 +44,12 @@ def _dense_reference(wl, lw, cb, x):
     return y.numpy(), idx.numpy()
 
 
-@pytest.mark.parametrize("gate_up,shared,zipf,sfmt", [("q2k", 0, None, "bf16"), ("cb2", 0, None, "bf16"),
-                                                      ("cb2", 256, 1.1, "bf16"), ("q2k", 256, None, "bf16"),
-                                                      ("cb2", 256, 1.1, "q8")])
-def test_routed_layer_equals_dense_masked_brute_force(gate_up, shared, zipf, sfmt):
-    wl = _tiny(gate_up, shared, zipf=zipf, shared_format=sfmt)
+@pytest.mark.parametrize("gate_up,shared,zipf,sfmt,tail", [("q2k", 0, None, "bf16", 0), ("cb2", 0, None, "bf16", 0),
+                                                           ("cb2", 256, 1.1, "bf16", 0), ("q2k", 256, None, "bf16", 0),
+                                                           ("cb2", 256, 1.1, "q8", 0), ("cb2", 256, 1.1, "bf16", 1)])
+def test_routed_layer_equals_dense_masked_brute_force(gate_up, shared, zipf, sfmt, tail):
+    """(tail = 1: the layer's experts in the Q4_K-style type.)"""
+    wl = _tiny(gate_up, shared, zipf=zipf, shared_format=sfmt, tail=tail)
     lw = synth.layer_weights(wl, 0)
     cb = synth.codebook()
     x = synth.tokens(wl, 6)
