@@ -62,7 +62,7 @@ def parse():
 # large-layer stack, at their batch sizes, with fewer timed steps.
 STEERED = "+steer"
 EXTRA = (("a3b_routed40", (1, 4)), ("a3b_stack40_zipf_q8", (1, 4)), ("a3b_stack40_zipf" + STEERED, (1, 4, 16)),
-         ("flash_stack8_zipf", (1, 8, 32)))
+         ("a3b_stack40_q4tail", (1, 4, 16)), ("flash_stack8_zipf", (1, 8, 32)))
 STEER_SCALE = 0.8
 EXTRA_STEPS = 100
 
@@ -118,12 +118,21 @@ def copy_calibration(mib: int):
 
 
 def kernel_name(wl, T):
+    if getattr(wl, "tail_layers", 0):
+        return ("2-bit layers: " + kernel_name(synth_plain(wl), T) +
+                f"; last {wl.tail_layers} layers: k_persist_big<q4k> (a second launch)")
     fmt = "cb2" if wl.gate_up_format == "cb2" else "q2k"
     # the small-batch kernel: batches up to 4 at hidden sizes up to 2048, and
     # the large-layer shape's fixed instantiation at one token
     small = T <= 4 and (wl.hidden <= 2048 or (T == 1 and wl.hidden == 4096 and wl.top_k == 6
                                                 and wl.expert_ffn == 2048 and wl.shared_ffn == 2048))
     return ("k_persist_small" if small else "k_persist_big") + f"<{fmt}> (one launch = the whole decode call)"
+
+
+def synth_plain(wl):
+    """The workload without its Q4_K-style tail (for naming the 2-bit kernel)."""
+    import dataclasses
+    return dataclasses.replace(wl, tail_layers=0)
 
 
 def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False):
@@ -144,8 +153,8 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False):
     if steer:
         dirs = np.random.default_rng(12).standard_normal((L, wl.hidden))
         moe.set_steering((dirs / np.linalg.norm(dirs, axis=1, keepdims=True)).astype(np.float32), STEER_SCALE)
-    g, u, d = wl.expert_bytes()
-    per_expert = g + u + d
+    # bytes of one expert in each layer (the Q4_K-style tail layers' are larger)
+    per_expert = np.array([sum(wl.expert_bytes(l)) for l in range(L)], dtype=np.float64)
     fixed_layer = wl.router_bytes() + wl.shared_bytes() + (wl.hidden * 4 if steer else 0)
     # decode() launches on torch's current stream; every event below is
     # recorded on that same stream
@@ -165,7 +174,7 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False):
         moe.sync_status(stream)
         idn = ids.cpu().numpy()
         uniq = np.array([[len(np.unique(idn[b, l])) for l in range(L)] for b in range(N_BATCHES)])
-        bytes_batch = uniq.sum(axis=1) * per_expert + L * fixed_layer + 2 * T * wl.hidden * 4
+        bytes_batch = uniq @ per_expert + L * fixed_layer + 2 * T * wl.hidden * 4
         for i in range(warmup):
             step(xs[i % N_BATCHES], y)
         torch.cuda.synchronize()

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define QS_MOE_ABI_VERSION 3
+#define QS_MOE_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define QS_API __attribute__((visibility("default")))
@@ -72,6 +72,20 @@ typedef enum {
  *   value w_j = +/- d*s*C[idx[j/8]][j%8] (exact in fp32), with C the
  *   256 x 8 int8 codebook given to qs_moe_create.
  *
+ * QS_FMT_Q4K, 144 bytes (the 4-bit Q4_K type at which the pages keep the
+ *   routed experts of the last layers: QuarkStar README, "Model Weights",
+ *   the Layers34-39Q4KExperts model; DwarfStar page, "Model Weights", q2
+ *   with the last 6 layers at q4):
+ *   [0,2)    d (binary16), [2,4) dmin (binary16)
+ *   [4,16)   scales[12]: sub-block j = weights 32j..32j+31 has 6-bit sc, m:
+ *            j < 4:  sc = scales[j] & 63, m = scales[j+4] & 63
+ *            j >= 4: sc = (scales[j+4] & 15) | (scales[j-4] >> 6) << 4,
+ *                    m  = (scales[j+4] >> 4) | (scales[j] >> 6) << 4
+ *   [16,144) qs[128]: weight 64c + r (c < 4) is the low nibble of
+ *            qs[32c + r] for r < 32, the high nibble of qs[32c + r - 32]
+ *            otherwise
+ *   value w_j = d*sc*q_j - dmin*m, rounded once to fp32.
+ *
  * Matrix layout: row-major [rows][cols/256] blocks, rows consecutive.
  * gate/up of one expert are [F][H/256] blocks, down is [H][F/256] blocks;
  * the E experts of a layer are consecutive.
@@ -85,7 +99,7 @@ typedef enum {
  *   [0,2)   d (binary16)
  *   [2,34)  q[32] int8
  *   value w_j = d*q_j (exact in fp32); row-major [rows][cols/32] blocks. */
-typedef enum { QS_FMT_BF16 = 0, QS_FMT_Q2K = 1, QS_FMT_CB2 = 2, QS_FMT_Q8 = 3 } qs_format;
+typedef enum { QS_FMT_BF16 = 0, QS_FMT_Q2K = 1, QS_FMT_CB2 = 2, QS_FMT_Q8 = 3, QS_FMT_Q4K = 4 } qs_format;
 
 /* qs_moe_decode / qs_moe_route flags */
 #define QS_DECODE_RESIDUAL 1u   /* x_{l+1} = x_l + MoE_l(u_l); y gets the last x */
@@ -121,6 +135,12 @@ typedef struct {
                               items (the measured faster choice on MI355X) */
   int32_t device;          /* HIP device ordinal; -1 = the current device */
   int32_t shared_format;   /* QS_FMT_BF16 or QS_FMT_Q8 (shared expert weights) */
+  int32_t tail_layers;     /* 0..n_layers: the last tail_layers resident layers
+                              hold their routed experts (gate, up and down) in
+                              QS_FMT_Q4K instead of gate_up_format/down_format.
+                              Those layers run the batched kernel's GEMV items
+                              (no MFMA items), at every batch size; a decode
+                              call over both kinds of layer is two launches */
 } qs_moe_config;
 
 /* One layer's weights in the raw block layout above.  Host or device
@@ -128,9 +148,9 @@ typedef struct {
 typedef struct {
   const float*    router;       /* fp32 [E][H] */
   const float*    router_bias;  /* fp32 [E], or NULL for zeros */
-  const void*     gate;         /* [E][F][H/256] blocks of gate_up_format */
-  const void*     up;           /* [E][F][H/256] blocks of gate_up_format */
-  const void*     down;         /* [E][H][F/256] blocks of down_format */
+  const void*     gate;         /* [E][F][H/256] blocks of gate_up_format (QS_FMT_Q4K in a tail layer) */
+  const void*     up;           /* [E][F][H/256] blocks of gate_up_format (QS_FMT_Q4K in a tail layer) */
+  const void*     down;         /* [E][H][F/256] blocks of down_format (QS_FMT_Q4K in a tail layer) */
   const void*     shared_gate;  /* [Fs][H] in shared_format; NULL iff Fs == 0 */
   const void*     shared_up;    /* [Fs][H] in shared_format */
   const void*     shared_down;  /* [H][Fs] in shared_format */
@@ -268,7 +288,7 @@ QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, uint
 
 /* Dequantise one matrix from the handle's device copy with the same field
  * decoding the GEMV kernels use (tests of the IQ2_XXS-class gate/up, Q2_K
- * down and Q8_0 shared types of the QuarkStar README, "Model Weights").
+ * down, Q4_K and Q8_0 shared types of the QuarkStar README, "Model Weights").
  * which: 0 gate, 1 up, 2 down of routed expert `expert`; 3 gate, 4 up,
  * 5 down of the shared expert (expert ignored; QS_E_INVAL when Fs == 0).
  * out: device fp32 [F][H] (gate/up), [H][F] (down), [Fs][H] (shared

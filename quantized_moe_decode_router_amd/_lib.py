@@ -10,14 +10,14 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsmoe.so")
 
-QS_MOE_ABI_VERSION = 3
+QS_MOE_ABI_VERSION = 4
 QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
-QS_FMT_BF16, QS_FMT_Q2K, QS_FMT_CB2, QS_FMT_Q8 = 0, 1, 2, 3
+QS_FMT_BF16, QS_FMT_Q2K, QS_FMT_CB2, QS_FMT_Q8, QS_FMT_Q4K = 0, 1, 2, 3, 4
 QS_DECODE_RESIDUAL = 1
 QS_DECODE_RMSNORM = 2
 QS_DECODE_STEER = 4
 
-FORMATS = {"bf16": QS_FMT_BF16, "q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2, "q8": QS_FMT_Q8}
+FORMATS = {"bf16": QS_FMT_BF16, "q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2, "q8": QS_FMT_Q8, "q4k": QS_FMT_Q4K}
 
 # Every function include/qs_moe.h declares.
 EXPORTS = (
@@ -31,7 +31,7 @@ class QsMoeConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "n_experts", "top_k", "expert_ffn", "shared_ffn",
         "gate_up_format", "down_format", "n_layers", "max_tokens", "mfma_min_tokens", "device",
-        "shared_format")]
+        "shared_format", "tail_layers")]
 
 
 class QsMoeLayerWeights(ctypes.Structure):
@@ -118,11 +118,12 @@ def _stream(stream) -> int:
 
 
 def make_config(hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format, down_format,
-                n_layers, max_tokens, mfma_min_tokens=0, device=-1, shared_format="bf16") -> QsMoeConfig:
+                n_layers, max_tokens, mfma_min_tokens=0, device=-1, shared_format="bf16",
+                tail_layers=0) -> QsMoeConfig:
     fmt = lambda f: FORMATS[f] if isinstance(f, str) else int(f)  # noqa: E731
     return QsMoeConfig(QS_MOE_ABI_VERSION, hidden, n_experts, top_k, expert_ffn, shared_ffn,
                        fmt(gate_up_format), fmt(down_format), n_layers, max_tokens,
-                       mfma_min_tokens, device, fmt(shared_format))
+                       mfma_min_tokens, device, fmt(shared_format), tail_layers)
 
 
 def qs_moe_create(cfg: QsMoeConfig, codebook=None) -> int:

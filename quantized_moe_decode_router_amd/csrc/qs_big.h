@@ -138,12 +138,17 @@ __device__ __forceinline__ BigL carve_big(uint8_t* raw, const A& a, bool cb2) {
 // functions of the arguments (the host checks the same sizes).
 __host__ __device__ inline uint32_t big_item_b(int H, bool sq8) { return (uint32_t)kSharedItemRows * 2 * srow_bytes(H, sq8); }
 __host__ __device__ inline uint32_t big_sdrows_b(int Fs, bool sq8) { return (uint32_t)kDownRows * srow_bytes(Fs, sq8); }
-__host__ __device__ inline uint32_t big_tile_b(int H, bool q2k) {
-  return 2u * (uint32_t)kGateTile * (H / kBlockW) * (64u + (q2k ? 16u : 4u) + (q2k ? 4u : 2u));
+__host__ __device__ inline uint32_t big_tile_b(int H, int gfmt) {
+  return 2u * (uint32_t)kGateTile * (H / kBlockW) * blk_bytes(gfmt);
 }
-// one staged token of the GEMV gate/up pass: limbs hi, lo, scales (, sums)
-__host__ __device__ inline uint32_t big_xtok_b(int H, bool q2k) { return 2u * H + (q2k ? 2u : 1u) * (H / 4); }
-__host__ __device__ inline uint32_t big_dnw_b(int F) { return (uint32_t)kDnRows * (F / kBlockW) * kQ2KBytes; }
+// one staged token of the GEMV gate/up pass: limbs hi, lo, scales (, sums
+// for the formats with a min term)
+__host__ __device__ inline uint32_t big_xtok_b(int H, int gfmt) {
+  return 2u * H + (gfmt != kFmtCB2 ? 2u : 1u) * (H / 4);
+}
+__host__ __device__ inline uint32_t big_dnw_b(int F, int dfmt) {
+  return (uint32_t)kDnRows * (F / kBlockW) * blk_bytes(dfmt);
+}
 // one staged pair of the GEMV down pass: limbs hi, lo, scales, sums, and its
 // kDnRows outputs
 __host__ __device__ inline uint32_t big_apair_b(int F) { return 2u * F + 2u * (F / 4) + kDnRows * 4u; }
@@ -170,15 +175,16 @@ struct BigPlan {
   bool ok;
 };
 
-__host__ __device__ inline BigPlan big_plan(int H, int F, int Fs, bool sq8, bool q2k, uint32_t pfb, int rtr_bytes) {
+__host__ __device__ inline BigPlan big_plan(int H, int F, int Fs, bool sq8, int gfmt, int dfmt, uint32_t pfb,
+                                            int rtr_bytes) {
   BigPlan p;
   const int nbh = H / kBlockW, nb = F / kBlockW;
   const uint32_t ga = big_gu_area(H, Fs, sq8), da = big_dn_area(Fs, sq8);
   const uint32_t gfree = pfb > ga ? pfb - ga : 0u, dfree = pfb > da ? pfb - da : 0u;
-  const uint32_t tb = al16(big_tile_b(H, q2k));
-  p.xg = gfree > tb ? (int)((gfree - tb) / big_xtok_b(H, q2k)) : 0;
+  const uint32_t tb = al16(big_tile_b(H, gfmt));
+  p.xg = gfree > tb ? (int)((gfree - tb) / big_xtok_b(H, gfmt)) : 0;
   if (p.xg > kXgMax) p.xg = kXgMax;
-  const uint32_t wb = al16(big_dnw_b(F));
+  const uint32_t wb = al16(big_dnw_b(F, dfmt));
   p.xp = dfree > wb ? (int)((dfree - wb) / big_apair_b(F)) : 0;
   if (p.xp > kXgMax) p.xp = kXgMax;
   p.kbg = 0;
@@ -202,7 +208,7 @@ __host__ __device__ inline BigPlan big_plan(int H, int F, int Fs, bool sq8, bool
 
 template <class A>
 __device__ __forceinline__ BigPlan big_plan_of(const A& a) {
-  return big_plan(a.H, a.F, a.Fs, a.sq8 != 0, a.gq2k != 0, a.pfb, (int)router_bytes(a));
+  return big_plan(a.H, a.F, a.Fs, a.sq8 != 0, a.gfmt, a.dfmt, a.pfb, (int)router_bytes(a));
 }
 
 // ------------------------------------------------------- cost model ---
@@ -212,23 +218,23 @@ constexpr int kStageCost = 240;
 
 template <class A>
 __device__ __forceinline__ int gu_gemv_cost(const A& a, int n) {
-  const int w = (int)(big_tile_b(a.H, a.gq2k != 0) >> 8);
+  const int w = (int)(big_tile_b(a.H, a.gfmt) >> 8);
   return kStageCost + w + (3 * w * n) / 5;
 }
 template <class A>
 __device__ __forceinline__ int gu_mfma_cost(const A& a, int n) {
-  const int w = (int)(big_tile_b(a.H, a.gq2k != 0) >> 8) * (kMguRows / kGateTile);
+  const int w = (int)(big_tile_b(a.H, a.gfmt) >> 8) * (kMguRows / kGateTile);
   const int ng = (n + kMfmaTok - 1) / kMfmaTok;
   return w + ng * (kStageCost + 16 * (a.H / kBlockW));
 }
 template <class A>
 __device__ __forceinline__ int dn_gemv_cost(const A& a, int n) {
-  const int w = (int)(big_dnw_b(a.F) >> 8);
+  const int w = (int)(big_dnw_b(a.F, a.dfmt) >> 8);
   return kStageCost + w + (w * n) / 8;
 }
 template <class A>
 __device__ __forceinline__ int dn_mfma_cost(const A& a, int n) {
-  const int w = (int)(big_dnw_b(a.F) >> 8) * (kMfmaRows / kDnRows);
+  const int w = (int)(big_dnw_b(a.F, a.dfmt) >> 8) * (kMfmaRows / kDnRows);
   const int ng = (n + kMfmaTok - 1) / kMfmaTok;
   return w + ng * (kStageCost + 16 * (a.F / kBlockW));
 }
@@ -296,17 +302,20 @@ __device__ __forceinline__ void assign_items(const A& a, const PersistLds& L, QS
 }
 
 // ------------------------------------------------------ copy issuers ---
-// Rows [r0, r0+n) of one Q2_K down matrix as [codes | scales | d,dmin].
+// Rows [r0, r0+n) of one down matrix (Q2_K- or Q4_K-style) as
+// [codes | scales | d,dmin].
 template <class A>
 __device__ __forceinline__ void copy_dn_rows(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst, int e,
                                              int r0, int n, int w, int nw) {
   const uint32_t nb = a.F / kBlockW;
-  const MatPlanes pl = q2k_planes((size_t)a.H * nb);
+  const MatPlanes pl = fmt_planes(a.dfmt, (size_t)a.H * nb);
+  const BlkGeom g = blk_geom(a.dfmt);
   const uint8_t* base = Lp.down + (size_t)e * a.dn_stride;
   const size_t b0 = (size_t)r0 * nb;
-  dma_to_lds<0>(base + pl.q + b0 * 64, dst, (uint32_t)n * nb * 64, w, nw);
-  dma_to_lds<0>(base + pl.s + b0 * 16, dst + (uint32_t)n * nb * 64, (uint32_t)n * nb * 16, w, nw);
-  dma_to_lds<0>(base + pl.d + b0 * 4, dst + (uint32_t)n * nb * 80, (uint32_t)n * nb * 4, w, nw);
+  const uint32_t nq = (uint32_t)n * nb * g.q, ns = (uint32_t)n * nb * g.s;
+  dma_to_lds<0>(base + pl.q + b0 * g.q, dst, nq, w, nw);
+  dma_to_lds<0>(base + pl.s + b0 * g.s, dst + nq, ns, w, nw);
+  dma_to_lds<0>(base + pl.d + b0 * g.d, dst + nq + ns, (uint32_t)n * nb * g.d, w, nw);
 }
 
 // Gather `rows` rows of `rb` bytes (a multiple of 16): row i from
@@ -506,7 +515,7 @@ __device__ __forceinline__ void copy_x_tokens(const A& a, const PersistLds& L, c
                       (QS_LDS uint8_t*)s.xl, (uint32_t)H, (uint32_t)H, n, w, nw);
   dma_rows<kCoherent>([&](int i) { return (const uint8_t*)(a.xs + (size_t)tok(i) * (H / kSubW)); },
                       (QS_LDS uint8_t*)s.xs, (uint32_t)H / 4, (uint32_t)H / 4, n, w, nw);
-  if (a.gq2k)
+  if (a.gfmt != kFmtCB2)   // the min term needs the sums
     dma_rows<kCoherent>([&](int i) { return (const uint8_t*)(a.xa + (size_t)tok(i) * (H / kSubW)); },
                         (QS_LDS uint8_t*)s.xa, (uint32_t)H / 4, (uint32_t)H / 4, n, w, nw);
 }
@@ -525,7 +534,7 @@ __device__ __forceinline__ void x_chunk_st(const A& a, const XStage& s, int slot
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     xs[i] = s.xs[si + i];
-    xa[i] = a.gq2k ? s.xa[si + i] : 0;
+    xa[i] = a.gfmt != kFmtCB2 ? s.xa[si + i] : 0;
   }
 }
 
@@ -557,9 +566,20 @@ __device__ __forceinline__ void gu_gemv_compute(const A& a, lds_cptr tile, const
         const int c = ch & 3;
         uint32_t gw[16], uw[16];
         uint32_t gsc, usc, gdd, udd;
-        const uint4 gv = ld16(gq + blk * 64 + c * 16);
-        const uint4 uv = ld16(uq_ + blk * 64 + c * 16);
-        if (q2k) {
+        if constexpr (FMT == kFmtQ4K) {   // 32 code bytes per chunk; its two scales and mins
+          const uint4 g0 = ld16(gq + blk * 128 + c * 32), g1 = ld16(gq + blk * 128 + c * 32 + 16);
+          const uint4 u0 = ld16(uq_ + blk * 128 + c * 32), u1 = ld16(uq_ + blk * 128 + c * 32 + 16);
+          gw[0] = g0.x; gw[1] = g0.y; gw[2] = g0.z; gw[3] = g0.w; gw[4] = g1.x; gw[5] = g1.y; gw[6] = g1.z; gw[7] = g1.w;
+          uw[0] = u0.x; uw[1] = u0.y; uw[2] = u0.z; uw[3] = u0.w; uw[4] = u1.x; uw[5] = u1.y; uw[6] = u1.z; uw[7] = u1.w;
+          gsc = ld2(gs + blk * 16 + 2 * c) | ld2(gs + blk * 16 + 8 + 2 * c) << 16;
+          usc = ld2(us + blk * 16 + 2 * c) | ld2(us + blk * 16 + 8 + 2 * c) << 16;
+          gdd = ld4(gd + blk * 4);
+          udd = ld4(ud + blk * 4);
+        }
+        const uint4 gv = FMT == kFmtQ4K ? make_uint4(0, 0, 0, 0) : ld16(gq + blk * 64 + c * 16);
+        const uint4 uv = FMT == kFmtQ4K ? make_uint4(0, 0, 0, 0) : ld16(uq_ + blk * 64 + c * 16);
+        if (FMT == kFmtQ4K) {
+        } else if (q2k) {
           gsc = ld4(gs + blk * 16 + c * 4);
           usc = ld4(us + blk * 16 + c * 4);
           gdd = ld4(gd + blk * 4);
@@ -588,7 +608,12 @@ __device__ __forceinline__ void gu_gemv_compute(const A& a, lds_cptr tile, const
           int xa[4];
           x_chunk_st(a, xst, tg + tt, ch, xh, xl, xs, xa);
           float gp, up;
-          if (q2k) {
+          if (FMT == kFmtQ4K) {
+            const uint32_t g8[8] = {gw[0], gw[1], gw[2], gw[3], gw[4], gw[5], gw[6], gw[7]};
+            const uint32_t u8[8] = {uw[0], uw[1], uw[2], uw[3], uw[4], uw[5], uw[6], uw[7]};
+            gp = q4k_chunk_dot(g8, gsc, half_to_f32(gdd & 0xFFFFu), half_to_f32(gdd >> 16), xh, xl, xs, xa);
+            up = q4k_chunk_dot(u8, usc, half_to_f32(udd & 0xFFFFu), half_to_f32(udd >> 16), xh, xl, xs, xa);
+          } else if (q2k) {
             const uint32_t g4[4] = {gw[0], gw[1], gw[2], gw[3]}, u4[4] = {uw[0], uw[1], uw[2], uw[3]};
             gp = q2k_chunk_dot(g4, gsc, half_to_f32(gdd & 0xFFFFu), half_to_f32(gdd >> 16), xh, xl, xs, xa);
             up = q2k_chunk_dot(u4, usc, half_to_f32(udd & 0xFFFFu), half_to_f32(udd >> 16), xh, xl, xs, xa);
@@ -627,10 +652,11 @@ __device__ __forceinline__ void gu_gemv_compute(const A& a, lds_cptr tile, const
     __builtin_amdgcn_wave_barrier();
     if (live) {
       const int pair = L.pairs[q0 + tt];
-      if (r < 4) {
+      if (r < 4) {   // dword r: elements r, 4+r, 8+r, 12+r (Q2_K down) or 4r..4r+3 (Q4_K down)
         int h[4], l[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) split_limbs(L.qtmp[tt * kGateTile + 4 * i + r], h[i], l[i]);
+        for (int i = 0; i < 4; ++i)
+          split_limbs(L.qtmp[tt * kGateTile + (FMT == kFmtQ4K ? 4 * r + i : 4 * i + r)], h[i], l[i]);
         cst(&a.ah[(size_t)pair * (a.F / 4) + f0 / 4 + r], pack4(h[0], h[1], h[2], h[3]));
         cst(&a.al[(size_t)pair * (a.F / 4) + f0 / 4 + r], pack4(l[0], l[1], l[2], l[3]));
       }
@@ -652,7 +678,7 @@ __device__ __forceinline__ void gu_gemv_item(const A& a, const LayerPtrs& Lp, Bi
   PersistLds& P = L.P;
   const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0, e = P.act[u];
   QS_LDS uint8_t* wt = P.pfb + big_gu_area(a.H, a.Fs, a.sq8 != 0);
-  const XStage xst = x_stage(a, wt + al16(big_tile_b(a.H, a.gq2k != 0)), pp.xg);
+  const XStage xst = x_stage(a, wt + al16(big_tile_b(a.H, a.gfmt)), pp.xg);
   for (int g0 = 0; g0 < n; g0 += pp.xg) {
     const int ng = n - g0 < pp.xg ? n - g0 : pp.xg;
     if (g0 == 0 && pre) {
@@ -902,8 +928,7 @@ __device__ __forceinline__ void big_gu_phase(const A& a, const LayerPtrs& Lp, co
   __syncthreads();
   const int na = *P.nact;
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
-  const bool q2k = a.gq2k != 0;
-  const uint32_t tb = al16(big_tile_b(a.H, q2k)), xtok = big_xtok_b(a.H, q2k);
+  const uint32_t tb = al16(big_tile_b(a.H, a.gfmt)), xtok = big_xtok_b(a.H, a.gfmt);
   Batcher B;
   B.area = P.pfb + big_gu_area(a.H, a.Fs, a.sq8 != 0);
   B.cap = a.pfb - big_gu_area(a.H, a.Fs, a.sq8 != 0);
@@ -952,8 +977,12 @@ __device__ __forceinline__ void big_gu_phase(const A& a, const LayerPtrs& Lp, co
         continue;
       }
       if (end) break;
-      if (mf) gu_mfma_item<FMT>(a, Lp, L, pp, u, j * kMguRows);
-      else gu_gemv_item<FMT>(a, Lp, L, pp, u, j * kGateTile, false, false);
+      if constexpr (FMT != kFmtQ4K) {   // (the Q4_K layers run GEMV items only)
+        if (mf) gu_mfma_item<FMT>(a, Lp, L, pp, u, j * kMguRows);
+        else gu_gemv_item<FMT>(a, Lp, L, pp, u, j * kGateTile, false, false);
+      } else {
+        gu_gemv_item<FMT>(a, Lp, L, pp, u, j * kGateTile, false, false);
+      }
       ++j;
       continue;
     }
@@ -1013,8 +1042,9 @@ __device__ __forceinline__ void copy_a_pairs(const A& a, const PersistLds& L, co
 }
 
 // One wave: its 8 rows (of the item's 64, in LDS) against the ng staged
-// pairs; the per-(row, pair) arithmetic is down_expert's.
-template <class A>
+// pairs; the per-(row, pair) arithmetic is down_expert's (Q4_K: the same
+// with 32-byte chunks and q4k_chunk_dot).
+template <int FMT, class A>
 __device__ __forceinline__ void dn_gemv_rows(const A& a, lds_cptr w, int wrow0, const AStage& st, int ng) {
   const int lane = qs_tid() & 63;
   const int nb = a.F / kBlockW;
@@ -1023,7 +1053,9 @@ __device__ __forceinline__ void dn_gemv_rows(const A& a, lds_cptr w, int wrow0, 
   const int cpl = nch / lpr;
   const int rpi = 64 / lpr;
   const int rsub = lane / lpr, j = lane % lpr;
-  lds_cptr wq = w, ws = w + kDnRows * nb * 64, wd = w + kDnRows * nb * 80;
+  constexpr bool q4k = FMT == kFmtQ4K;
+  const BlkGeom g = blk_geom(q4k ? kFmtQ4K : kFmtQ2K);
+  lds_cptr wq = w, ws = w + kDnRows * nb * g.q, wd = ws + kDnRows * nb * g.s;
 #pragma unroll 1
   for (int rr = rsub; rr < kDownRows; rr += rpi) {
     const int row = wrow0 + rr;       // row within the item
@@ -1032,10 +1064,18 @@ __device__ __forceinline__ void dn_gemv_rows(const A& a, lds_cptr w, int wrow0, 
       const int ch = j + cc * lpr;
       const int c = ch & 3;
       const uint32_t blk = (uint32_t)row * nb + ch / 4;
-      const uint4 qv = ld16(wq + blk * 64 + c * 16);
-      const uint32_t scm = ld4(ws + blk * 16 + c * 4);
+      uint32_t qw[8];
+      uint32_t scm;
+      if (q4k) {
+        const uint4 q0 = ld16(wq + blk * 128 + c * 32), q1 = ld16(wq + blk * 128 + c * 32 + 16);
+        qw[0] = q0.x; qw[1] = q0.y; qw[2] = q0.z; qw[3] = q0.w; qw[4] = q1.x; qw[5] = q1.y; qw[6] = q1.z; qw[7] = q1.w;
+        scm = ld2(ws + blk * 16 + 2 * c) | ld2(ws + blk * 16 + 8 + 2 * c) << 16;
+      } else {
+        const uint4 qv = ld16(wq + blk * 64 + c * 16);
+        qw[0] = qv.x; qw[1] = qv.y; qw[2] = qv.z; qw[3] = qv.w;
+        scm = ld4(ws + blk * 16 + c * 4);
+      }
       const uint32_t dd = ld4(wd + blk * 4);
-      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
       const float d = half_to_f32(dd & 0xFFFFu), dm = half_to_f32(dd >> 16);
 #pragma unroll 1
       for (int sl = 0; sl < ng; ++sl) {
@@ -1056,7 +1096,13 @@ __device__ __forceinline__ void dn_gemv_rows(const A& a, lds_cptr w, int wrow0, 
           xs[i] = st.as[si + i];
           xa[i] = st.aa[si + i];
         }
-        float part = q2k_chunk_dot(qw, scm, d, dm, xh, xl, xs, xa);
+        float part;
+        if (q4k) {
+          part = q4k_chunk_dot(qw, scm, d, dm, xh, xl, xs, xa);
+        } else {
+          const uint32_t q4[4] = {qw[0], qw[1], qw[2], qw[3]};
+          part = q2k_chunk_dot(q4, scm, d, dm, xh, xl, xs, xa);
+        }
         part = bfly_sum_dyn(part, lpr);
         if (j == 0) st.o[sl * kDnRows + row] = cc == 0 ? part : st.o[sl * kDnRows + row] + part;
       }
@@ -1064,14 +1110,14 @@ __device__ __forceinline__ void dn_gemv_rows(const A& a, lds_cptr w, int wrow0, 
   }
 }
 
-template <class A>
+template <int FMT, class A>
 __device__ __forceinline__ void dn_gemv_item(const A& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp,
                                              int u, int h0, bool pre) {
   PersistLds& P = L.P;
   const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0, e = P.act[u];
   const int wave = qs_tid() >> 6;
   QS_LDS uint8_t* wt = P.pfb + big_dn_area(a.Fs, a.sq8 != 0);
-  const AStage st = a_stage(a, wt + al16(big_dnw_b(a.F)), pp.xp);
+  const AStage st = a_stage(a, wt + al16(big_dnw_b(a.F, a.dfmt)), pp.xp);
   for (int g0 = 0; g0 < n; g0 += pp.xp) {
     const int ng = n - g0 < pp.xp ? n - g0 : pp.xp;
     if (g0 == 0 && pre) {
@@ -1082,7 +1128,7 @@ __device__ __forceinline__ void dn_gemv_item(const A& a, const LayerPtrs& Lp, Bi
         copy_a_pairs(a, P, st, q0 + g0, ng, w, nw);
       });
     }
-    dn_gemv_rows(a, wt, wave * kDownRows, st, ng);
+    dn_gemv_rows<FMT>(a, wt, wave * kDownRows, st, ng);
     __syncthreads();
     for (int i = qs_tid(); i < ng * kDnRows; i += kPersistThreads) {
       const int sl = i / kDnRows, row = i % kDnRows;
@@ -1236,7 +1282,7 @@ __device__ __forceinline__ void big_shared_dn_tile(const A& a, lds_cptr srows, c
   __syncthreads();
 }
 
-template <class A>
+template <int FMT, class A>
 __device__ __forceinline__ void big_dn_phase(const A& a, const LayerPtrs& Lp, BigL& L, const BigPlan& pp) {
   PersistLds& P = L.P;
   const int na = *P.nact;
@@ -1260,7 +1306,7 @@ __device__ __forceinline__ void big_dn_phase(const A& a, const LayerPtrs& Lp, Bi
   }
   // routed items, GEMV ones staged in batches as in the gate/up phase
   const int wave = qs_tid() >> 6, nw = kPersistThreads >> 6;
-  const uint32_t wb = al16(big_dnw_b(a.F)), pb = big_apair_b(a.F);
+  const uint32_t wb = al16(big_dnw_b(a.F, a.dfmt)), pb = big_apair_b(a.F);
   Batcher B;
   B.area = P.pfb + big_dn_area(a.Fs, a.sq8 != 0);
   B.cap = a.pfb - big_dn_area(a.Fs, a.sq8 != 0);
@@ -1276,7 +1322,7 @@ __device__ __forceinline__ void big_dn_phase(const A& a, const LayerPtrs& Lp, Bi
       const uint32_t wo = (uint32_t)L.bat[4 * i + 2], xo = (uint32_t)L.bat[4 * i + 3];
       const int q0 = P.aoff[u], n = P.aoff[u + 1] - q0;
       const AStage st = a_stage(a, B.area + xo, n);
-      dn_gemv_rows(a, B.area + wo, wave * kDownRows, st, n);
+      dn_gemv_rows<FMT>(a, B.area + wo, wave * kDownRows, st, n);
       __syncthreads();
       for (int k = qs_tid(); k < n * kDnRows; k += kPersistThreads) {
         const int sl = k / kDnRows, row = k % kDnRows;
@@ -1308,8 +1354,12 @@ __device__ __forceinline__ void big_dn_phase(const A& a, const LayerPtrs& Lp, Bi
         continue;
       }
       if (end) break;
-      if (mf) dn_mfma_item(a, Lp, L, pp, u, j * kMfmaRows);
-      else dn_gemv_item(a, Lp, L, pp, u, j * kDnRows, false);
+      if constexpr (FMT != kFmtQ4K) {   // (the Q4_K layers run GEMV items only)
+        if (mf) dn_mfma_item(a, Lp, L, pp, u, j * kMfmaRows);
+        else dn_gemv_item<FMT>(a, Lp, L, pp, u, j * kDnRows, false);
+      } else {
+        dn_gemv_item<FMT>(a, Lp, L, pp, u, j * kDnRows, false);
+      }
       ++j;
       continue;
     }
@@ -1454,7 +1504,7 @@ __device__ __forceinline__ void persist_big_body(const A& a) {
       return;
     QS_STAMP(li, 6);
     // ---- D
-    big_dn_phase(a, Lp, L, pp);
+    big_dn_phase<FMT>(a, Lp, L, pp);
     QS_STAMP(li, 7);
     if (!grid_barrier(a, ++epoch, [](int, int) {})) return;
     QS_STAMP(li, 8);
@@ -1486,6 +1536,7 @@ template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int G_>
 struct FixedBigArgs : PersistArgs {
   static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, sq8 = SQ8_, G = G_;
   static constexpr int gq2k = FMT == 1, r_et = 1;
+  static constexpr int gfmt = FMT, dfmt = FMT == kFmtQ4K ? kFmtQ4K : kFmtQ2K;
 };
 
 template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int G, bool STEER = false>

@@ -150,6 +150,34 @@ __device__ __forceinline__ float q2k_chunk_dot(const uint32_t (&qw)[4], uint32_t
   return part;
 }
 
+// One 64-weight chunk of a Q4_K-style block against activation limbs in
+// natural order.  qw: its 32 code bytes; dword k holds in its low nibbles
+// weights 4k..4k+3 of the chunk (k < 8), in its high nibbles weights
+// 32+4k..32+4k+3.  scm: the chunk's two sub-block scales in bytes 0, 1 and
+// its two mins in bytes 2, 3.  16-element group g belongs to sub-block g/2.
+__device__ __forceinline__ float q4k_chunk_dot(const uint32_t (&qw)[8], uint32_t scm, float d,
+                                               float dmin, const uint32_t (&xh)[16],
+                                               const uint32_t (&xl)[16], const float (&xs)[4],
+                                               const int (&xa)[4]) {
+  float part = 0.f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    int sh = 0, sl = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t src = qw[(g & 1) * 4 + k];
+      const uint32_t b = g < 2 ? (src & 0x0F0F0F0Fu) : ((src >> 4) & 0x0F0F0F0Fu);
+      sh = sdot4(b, xh[4 * g + k], sh);
+      sl = sdot4(b, xl[4 * g + k], sl);
+    }
+    const int S = sh * 256 + sl;
+    const float sc = (float)((scm >> (8 * (g >> 1))) & 0xFFu);
+    const float m = (float)((scm >> (16 + 8 * (g >> 1))) & 0xFFu);
+    part = fmaf(xs[g], fmaf(d * sc, (float)S, -(dmin * m) * (float)xa[g]), part);
+  }
+  return part;
+}
+
 // ----------------------------------------------------------- repack ---
 
 // Raw codebook 2-bit blocks -> QD/SC/D planes; one thread per block.
@@ -183,6 +211,31 @@ __global__ void k_repack_q2k(const uint8_t* __restrict__ src, uint8_t* __restric
   for (int i = 0; i < 64; ++i) base[pl.q + blk * 64 + i] = s[16 + i];
   for (int i = 0; i < 16; ++i) base[pl.s + blk * 16 + i] = s[i];
   for (int i = 0; i < 4; ++i) base[pl.d + blk * 4 + i] = s[80 + i];
+}
+
+// Q4_K-style blocks -> planes (one thread per block): codes unchanged, the
+// 12 packed scale bytes unpacked into 8 scales and 8 mins, d and dmin.
+__global__ void k_repack_q4k(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                             size_t nblk_per_mat, size_t mat_stride, size_t n_mat) {
+  const size_t gi = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= nblk_per_mat * n_mat) return;
+  const size_t mat = gi / nblk_per_mat, blk = gi % nblk_per_mat;
+  const uint8_t* s = src + gi * kQ4KBytes;
+  const MatPlanes pl = q4k_planes(nblk_per_mat);
+  uint8_t* base = dst + mat * mat_stride;
+  for (int i = 0; i < 128; ++i) base[pl.q + blk * 128 + i] = s[16 + i];
+  const uint8_t* sc = s + 4;
+  uint8_t* o = base + pl.s + blk * 16;
+  for (int j = 0; j < 8; ++j) {
+    if (j < 4) {
+      o[j] = sc[j] & 63;
+      o[8 + j] = sc[j + 4] & 63;
+    } else {
+      o[j] = (uint8_t)((sc[j + 4] & 15) | ((sc[j - 4] >> 6) << 4));
+      o[8 + j] = (uint8_t)((sc[j + 4] >> 4) | ((sc[j] >> 6) << 4));
+    }
+  }
+  for (int i = 0; i < 4; ++i) base[pl.d + blk * 4 + i] = s[i];
 }
 
 // 8-bit shared-expert blocks (d binary16, then 32 int8 codes; row-major
@@ -242,6 +295,24 @@ __global__ void k_dequant_q2k(const uint8_t* __restrict__ mat, size_t nblk, floa
       const uint32_t quad = (qs[i] >> (2 * p)) & 0x03030303u;
       for (int b = 0; b < 4; ++b) o[16 * i + 4 * b + p] = fmaf(dsc, (float)((quad >> (8 * b)) & 3u), -dm);
     }
+  }
+}
+
+__global__ void k_dequant_q4k(const uint8_t* __restrict__ mat, size_t nblk, float* __restrict__ out) {
+  const size_t blk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= nblk) return;
+  const MatPlanes pl = q4k_planes(nblk);
+  const uint8_t* qs = mat + pl.q + blk * 128;
+  const uint8_t* scm = mat + pl.s + blk * 16;
+  const uint32_t dd = *(const uint32_t*)(mat + pl.d + blk * 4);
+  const float d = half_to_f32(dd & 0xFFFFu), dmin = half_to_f32(dd >> 16);
+  float* o = out + blk * kBlockW;
+  for (int j = 0; j < kBlockW; ++j) {
+    const int c = j / 64, r = j % 64, sub = j / 32;
+    const uint32_t byte = qs[32 * c + (r & 31)];
+    const float q = (float)(r < 32 ? byte & 15u : byte >> 4);
+    // d*sc and dmin*m are exact in fp32; one rounding of the difference
+    o[j] = fmaf(d * (float)scm[sub], q, -(dmin * (float)scm[8 + sub]));
   }
 }
 

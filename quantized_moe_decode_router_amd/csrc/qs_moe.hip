@@ -34,6 +34,7 @@ struct LayerDev {
   uint8_t* gate = nullptr;
   uint8_t* up = nullptr;
   uint8_t* down = nullptr;
+  bool q4k = false;          // routed experts in the Q4_K-style format (a tail layer)
   uint8_t* sg = nullptr;     // shared expert rows (srow_bytes each)
   uint8_t* su = nullptr;
   uint8_t* sd = nullptr;
@@ -97,6 +98,8 @@ struct qs_moe {
   int device = 0;
   size_t gu_stride = 0;      // bytes per repacked gate/up expert matrix
   size_t dn_stride = 0;      // bytes per repacked down expert matrix
+  size_t gu_stride4 = 0;     // the same for the Q4_K-style tail layers
+  size_t dn_stride4 = 0;
   size_t layer_bytes = 0;
   std::vector<LayerDev> layers;
   Scratch s;
@@ -118,6 +121,8 @@ struct qs_moe {
   bool persist_big_ok = false;   // batched instantiation usable
   bool steer_small_ok = false;   // the instantiations with the steered combine usable
   bool steer_big_ok = false;
+  bool q4k_ok = false;           // the batched Q4_K-style instantiation (tail layers) usable
+  bool q4k_steer_ok = false;
   int mfma_min = 1;               // bucket size from which the MFMA path runs
   bool mfma_explicit = false;     // the config set mfma_min_tokens
   bool fixed_ok = false;          // the fixed-shape small-batch kernels are usable
@@ -178,6 +183,7 @@ int validate_config(const qs_moe_config* c) {
   if (c->mfma_min_tokens < 0) return QS_E_INVAL;
   if (c->device < -1) return QS_E_INVAL;
   if (c->shared_format != QS_FMT_BF16 && c->shared_format != QS_FMT_Q8) return QS_E_INVAL;
+  if (c->tail_layers < 0 || c->tail_layers > c->n_layers) return QS_E_INVAL;
   if (c->down_format != QS_FMT_Q2K) return QS_E_UNSUPPORTED;
   return QS_OK;
 }
@@ -320,18 +326,20 @@ struct PersistShape {
   int r_et = 1, r_tt = 1;
 };
 
-PersistShape big_shape(const qs_moe* h, int T) {
+// fmt: the routed gate/up format of the launch's layers (QS_FMT_Q4K for
+// the tail layers, whose down matrices are Q4_K-style too)
+PersistShape big_shape(const qs_moe* h, int T, int fmt) {
   const qs_moe_config& c = h->cfg;
   PersistShape p;
-  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
+  const bool cb2 = fmt == QS_FMT_CB2;
   const size_t base = big_layout(c.n_experts, T, T * c.top_k, cb2, 0).end;
   if (base >= h->lds_limit || h->grid < 8) return p;
   p.pfb = (uint32_t)std::min((size_t)kPfbMax, (h->lds_limit - base) & ~(size_t)15);
   p.lds = base + p.pfb;
   p.r_tt = T < 4 ? T : 4;
   while (p.r_et < 4 && (c.n_experts + p.r_et - 1) / p.r_et > h->grid) p.r_et *= 2;
-  p.ok = big_plan(c.hidden, c.expert_ffn, c.shared_ffn, c.shared_format == QS_FMT_Q8, !cb2, p.pfb,
-                  p.r_et * c.hidden * 4).ok;
+  p.ok = big_plan(c.hidden, c.expert_ffn, c.shared_ffn, c.shared_format == QS_FMT_Q8, fmt,
+                  fmt == QS_FMT_Q4K ? kFmtQ4K : kFmtQ2K, p.pfb, p.r_et * c.hidden * 4).ok;
   return p;
 }
 
@@ -349,7 +357,7 @@ const void* persist_fixed_fn(const qs_moe* h, int T, bool steer = false);
 
 PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   const qs_moe_config& c = h->cfg;
-  if (!small) return big_shape(h, T);
+  if (!small) return big_shape(h, T, c.gate_up_format);
   PersistShape p;
   const bool cb2 = c.gate_up_format == QS_FMT_CB2;
   const bool sq8 = c.shared_format == QS_FMT_Q8;
@@ -471,8 +479,26 @@ const void* persist_fixed_fn(const qs_moe* h, int T, bool steer) {
   return nullptr;
 }
 
+// The batched instantiation of the Q4_K-style tail layers (GEMV items only).
+const void* persist_q4k_fn(bool steer) {
+  return steer ? (const void*)k_persist_big<kFmtQ4K, true> : (const void*)k_persist_big<kFmtQ4K, false>;
+}
+
 // Every workgroup must be resident at once for the grid barrier (a
 // cooperative launch also enforces this).
+bool fn_resident(const void* fn, size_t lds) {
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kPersistThreads, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return occ >= 1;
+}
+
 bool persist_resident(const qs_moe* h, bool small, size_t lds, bool steer = false) {
   const void* fn = persist_fn(h->cfg.gate_up_format == QS_FMT_CB2, small, steer);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
@@ -535,6 +561,14 @@ int setup_persistent(qs_moe* h) {
         }
         static_lds = std::max(static_lds, (size_t)fa.sharedSizeBytes);
       }
+  for (int st = 0; st < 2; ++st) {
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, persist_q4k_fn(st != 0)) != hipSuccess) {
+      (void)hipGetLastError();
+      return QS_OK;
+    }
+    static_lds = std::max(static_lds, (size_t)fa.sharedSizeBytes);
+  }
   const size_t dev_lds = prop.maxSharedMemoryPerMultiProcessor;
   h->lds_limit = dev_lds > static_lds ? (dev_lds - static_lds) & ~(size_t)255 : 0;
   if (!coop || h->grid < 8) return QS_OK;
@@ -550,6 +584,17 @@ int setup_persistent(qs_moe* h) {
   }
   h->persist_small_ok = lds_small && persist_resident(h, true, lds_small);
   h->persist_big_ok = lds_big && persist_resident(h, false, lds_big);
+  if (c.tail_layers > 0) {   // the Q4_K-style tail layers: the batched kernel at every T
+    size_t lds4 = 0;
+    bool all = true;
+    for (int T = 1; T <= c.max_tokens; ++T) {
+      const PersistShape p = big_shape(h, T, QS_FMT_Q4K);
+      all = all && p.ok;
+      if (p.ok) lds4 = std::max(lds4, p.lds);
+    }
+    h->q4k_ok = all && lds4 && fn_resident(persist_q4k_fn(false), lds4);
+    h->q4k_steer_ok = h->q4k_ok && fn_resident(persist_q4k_fn(true), lds4);
+  }
   h->steer_small_ok = h->persist_small_ok && persist_resident(h, true, lds_small, true);
   h->steer_big_ok = h->persist_big_ok && persist_resident(h, false, lds_big, true);
   // fixed-shape instantiations: the same LDS limits, checked one by one
@@ -596,15 +641,23 @@ bool choose_kernel(const qs_moe* h, int T, bool& small, PersistShape& p) {
   return true;
 }
 
-// The whole decode call as one cooperative launch.
-int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const float* x, float* y, int T,
-                      bool residual, bool prenorm, bool steer, int32_t* ids_out, float* w_out, hipStream_t st) {
+// Layers [layer0, layer0 + nL), all of one routed format, as one cooperative
+// launch.  q4k: the Q4_K-style tail layers (batched kernel, GEMV items).
+int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const float* x, float* y, int T,
+                   bool residual, bool prenorm, bool steer, int32_t* ids_out, float* w_out, hipStream_t st,
+                   bool q4k) {
   const qs_moe_config& c = h->cfg;
-  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
+  const bool cb2 = !q4k && c.gate_up_format == QS_FMT_CB2;
   bool small = false;
   PersistShape p;
-  if (!choose_kernel(h, T, small, p)) return QS_E_UNSUPPORTED;   // (create checked every T)
-  if (steer && !(small ? h->steer_small_ok : h->steer_big_ok)) return QS_E_UNSUPPORTED;
+  if (q4k) {
+    if (!(steer ? h->q4k_steer_ok : h->q4k_ok)) return QS_E_UNSUPPORTED;
+    p = big_shape(h, T, QS_FMT_Q4K);
+    if (!p.ok) return QS_E_UNSUPPORTED;
+  } else {
+    if (!choose_kernel(h, T, small, p)) return QS_E_UNSUPPORTED;   // (create checked every T)
+    if (steer && !(small ? h->steer_small_ok : h->steer_big_ok)) return QS_E_UNSUPPORTED;
+  }
   // the batched kernel's grid barriers: five per layer (six with steering)
   // but none after the last
   const uint32_t barriers = small ? 0u : (steer ? 6u : 5u) * nL - 1u;
@@ -625,7 +678,9 @@ int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const 
   a.spin_bar = h->wait_limit ? h->wait_limit : kSpinMax;
   a.n_layers = nL;
   a.T = T; a.H = c.hidden; a.E = c.n_experts; a.k = c.top_k; a.F = c.expert_ffn; a.Fs = c.shared_ffn;
-  a.gq2k = c.gate_up_format == QS_FMT_Q2K;
+  a.gq2k = !q4k && c.gate_up_format == QS_FMT_Q2K;
+  a.gfmt = q4k ? kFmtQ4K : c.gate_up_format;
+  a.dfmt = q4k ? kFmtQ4K : kFmtQ2K;
   a.sq8 = c.shared_format == QS_FMT_Q8;
   a.prenorm = prenorm;
   a.residual = residual;
@@ -633,8 +688,8 @@ int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const 
   a.r_et = p.r_et;
   a.pfb = p.pfb;
   a.pfa = p.pfa;
-  a.gu_stride = h->gu_stride;
-  a.dn_stride = h->dn_stride;
+  a.gu_stride = q4k ? h->gu_stride4 : h->gu_stride;
+  a.dn_stride = q4k ? h->dn_stride4 : h->dn_stride;
   a.cbtab = h->cbtab;
   a.x_in = x; a.y_out = y; a.ids_out = ids_out; a.w_out = w_out;
   a.logits = s.logits; a.rinv = s.rinv; a.ids = s.ids; a.wts = s.wts;
@@ -644,6 +699,7 @@ int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const 
   // default threshold: one-token buckets of a one-token batch stay on the
   // GEMV items (measured faster there: Flash stack T = 1, 1680 vs 1274 tok/s)
   a.mfma_min = !h->mfma_explicit && T == 1 ? 2 : h->mfma_min;
+  if (q4k) a.mfma_min = 1 << 30;   // GEMV items only
   a.ll_lg = s.ll_lg; a.ll_a = s.ll_a; a.llx0 = s.llx[0]; a.llx1 = s.llx[1];
   a.ll_epoch = *cs.ll_epoch;
   a.af = s.af; a.ob = s.ob; a.sb = s.sb;
@@ -656,10 +712,15 @@ int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const 
   // the fixed-shape kernel needs the router unit it assumes (one expert per
   // workgroup, all tokens at once)
   const void* fn = nullptr;
-  if (small && (steer ? h->fixed_steer_ok : h->fixed_ok) && p.r_et == 1 && p.r_tt == T)
-    fn = persist_fixed_fn(h, T, steer);
-  if (!small && (steer ? h->big_fixed_steer_ok : h->big_fixed_ok) && p.r_et == 1) fn = persist_big_fixed_fn(h, steer);
-  if (!fn) fn = persist_fn(cb2, small, steer);
+  if (q4k) {
+    fn = persist_q4k_fn(steer);
+  } else {
+    if (small && (steer ? h->fixed_steer_ok : h->fixed_ok) && p.r_et == 1 && p.r_tt == T)
+      fn = persist_fixed_fn(h, T, steer);
+    if (!small && (steer ? h->big_fixed_steer_ok : h->big_fixed_ok) && p.r_et == 1)
+      fn = persist_big_fixed_fn(h, steer);
+    if (!fn) fn = persist_fn(cb2, small, steer);
+  }
   hipError_t e = hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kPersistThreads), args,
                                             (unsigned)p.lds, st);
   if (e != hipSuccess) {
@@ -669,6 +730,24 @@ int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const 
   *cs.epoch += barriers;
   if (small) *cs.ll_epoch += 3u * (uint32_t)nL;
   return QS_OK;
+}
+
+// The whole decode call: one launch per run of layers of one routed format
+// (the 2-bit layers, then the Q4_K-style tail layers), chained through y.
+int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const float* x, float* y, int T,
+                      bool residual, bool prenorm, bool steer, int32_t* ids_out, float* w_out, hipStream_t st) {
+  const qs_moe_config& c = h->cfg;
+  const int split = c.n_layers - c.tail_layers;   // the first tail layer
+  if (layer0 + nL <= split || layer0 >= split)
+    return launch_segment(h, cs, layer0, nL, x, y, T, residual, prenorm, steer, ids_out, w_out, st,
+                          layer0 >= split);
+  // (several layers: the residual chain, so the second run continues in y)
+  const int n1 = split - layer0;
+  int rc = launch_segment(h, cs, layer0, n1, x, y, T, residual, prenorm, steer, ids_out, w_out, st, false);
+  if (rc) return rc;
+  const size_t skip = (size_t)n1 * T * c.top_k;
+  return launch_segment(h, cs, split, nL - n1, y, y, T, residual, prenorm, steer, ids_out ? ids_out + skip : nullptr,
+                        w_out ? w_out + skip : nullptr, st, true);
 }
 
 int check_layer_range(const qs_moe* h, int layer0, int n) {
@@ -806,17 +885,18 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   const size_t gu_blk = F * (H / kBlockW), dn_blk = H * (F / kBlockW);
   h->gu_stride = align_up(gu_blk * gate_up_block_bytes(c), 256);
   h->dn_stride = align_up(dn_blk * kQ2KBytes, 256);
-  size_t lb = 0;
-  lb += align_up(E * H * 4, 256) + align_up(E * 4, 256);
-  lb += 2 * E * h->gu_stride + E * h->dn_stride;
+  h->gu_stride4 = align_up(gu_blk * blk_bytes(kFmtQ4K), 256);
+  h->dn_stride4 = align_up(dn_blk * blk_bytes(kFmtQ4K), 256);
   const bool sq8 = c.shared_format == QS_FMT_Q8;
   const size_t sgu = Fs * (size_t)srow_bytes((int)H, sq8), sdn = H * (size_t)srow_bytes((int)Fs, sq8);
-  if (Fs) lb += 2 * align_up(sgu, 256) + align_up(sdn, 256);
-  h->layer_bytes = lb;
   h->layers.resize(c.n_layers);
   rc = QS_OK;
   for (int l = 0; l < c.n_layers && rc == QS_OK; ++l) {
     LayerDev& L = h->layers[l];
+    L.q4k = l >= c.n_layers - c.tail_layers;
+    const size_t gs = L.q4k ? h->gu_stride4 : h->gu_stride, ds = L.q4k ? h->dn_stride4 : h->dn_stride;
+    size_t lb = align_up(E * H * 4, 256) + align_up(E * 4, 256) + 2 * E * gs + E * ds;
+    if (Fs) lb += 2 * align_up(sgu, 256) + align_up(sdn, 256);
     if (!hip_ok(hipMalloc(&L.base, lb), "hipMalloc(layer)")) {
       L.base = nullptr;
       rc = QS_E_NOMEM;
@@ -825,15 +905,16 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
     uint8_t* p = L.base;
     L.router = carve<float>(p, E * H);
     L.bias = carve<float>(p, E);
-    L.gate = p; p += E * h->gu_stride;
-    L.up = p; p += E * h->gu_stride;
-    L.down = p; p += E * h->dn_stride;
+    L.gate = p; p += E * gs;
+    L.up = p; p += E * gs;
+    L.down = p; p += E * ds;
     if (Fs) {
       L.sg = carve<uint8_t>(p, sgu);
       L.su = carve<uint8_t>(p, sgu);
       L.sd = carve<uint8_t>(p, sdn);
     }
     h->total_bytes += lb;
+    h->layer_bytes = std::max(h->layer_bytes, lb);
   }
   if (rc == QS_OK) {
     h->s.bytes = scratch_bytes(c);
@@ -870,14 +951,19 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   }
   if (rc == QS_OK) {
     // every batch size up to max_tokens must have a persistent kernel that
-    // fits the device (there is no other decode path)
+    // fits the device (there is no other decode path), for the 2-bit layers
+    // and for the Q4_K-style tail layers
     for (int T = 1; T <= c.max_tokens && rc == QS_OK; ++T) {
       bool small = false;
       PersistShape p;
-      if (!choose_kernel(h, T, small, p)) {
+      if (c.tail_layers < c.n_layers && !choose_kernel(h, T, small, p)) {
         fprintf(stderr, "qs_moe: no persistent decode kernel fits a %d-token call of this shape\n", T);
         rc = QS_E_UNSUPPORTED;
       }
+    }
+    if (rc == QS_OK && c.tail_layers > 0 && !h->q4k_ok) {
+      fprintf(stderr, "qs_moe: the batched decode kernel of the Q4_K-style layers does not fit this shape\n");
+      rc = QS_E_UNSUPPORTED;
     }
   }
   if (rc != QS_OK) {
@@ -913,9 +999,11 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
     QS_HIP(hipMemcpyAsync(L.sd, w->shared_down, Fs * H * 2, hipMemcpyDefault, st));
   }
   const size_t gu_blk = F * (H / kBlockW), dn_blk = H * (F / kBlockW);
-  const size_t gbb = gate_up_block_bytes(c);
+  const bool q4 = L.q4k;   // a tail layer: every routed matrix in the Q4_K-style format
+  const size_t gbb = q4 ? (size_t)kQ4KBytes : gate_up_block_bytes(c);
+  const size_t dbb = q4 ? (size_t)kQ4KBytes : (size_t)kQ2KBytes;
   const size_t q8_raw = Fs * (H / kQ8W) * (size_t)kQ8Bytes;   // one shared matrix in 8-bit blocks
-  const size_t need = std::max({E * gu_blk * gbb, E * dn_blk * (size_t)kQ2KBytes, sq8 ? q8_raw : (size_t)0});
+  const size_t need = std::max({E * gu_blk * gbb, E * dn_blk * dbb, sq8 ? q8_raw : (size_t)0});
   if (h->staging_bytes < need) {
     if (h->staging) QS_HIP(hipFree(h->staging));
     h->staging = nullptr;
@@ -926,19 +1014,24 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
     }
     h->staging_bytes = need;
   }
-  struct Job { const void* src; uint8_t* dst; size_t nblk; size_t stride; bool cb2; };
+  struct Job { const void* src; uint8_t* dst; size_t nblk; size_t stride; int fmt; };
+  const int gfmt = q4 ? kFmtQ4K : c.gate_up_format, dfmt = q4 ? kFmtQ4K : kFmtQ2K;
+  const size_t gst = q4 ? h->gu_stride4 : h->gu_stride, dst_ = q4 ? h->dn_stride4 : h->dn_stride;
   const Job jobs[3] = {
-      {w->gate, L.gate, gu_blk, h->gu_stride, c.gate_up_format == QS_FMT_CB2},
-      {w->up, L.up, gu_blk, h->gu_stride, c.gate_up_format == QS_FMT_CB2},
-      {w->down, L.down, dn_blk, h->dn_stride, false},
+      {w->gate, L.gate, gu_blk, gst, gfmt},
+      {w->up, L.up, gu_blk, gst, gfmt},
+      {w->down, L.down, dn_blk, dst_, dfmt},
   };
   for (const Job& j : jobs) {
-    const size_t bytes = E * j.nblk * (j.cb2 ? kCB2Bytes : kQ2KBytes);
-    QS_HIP(hipMemcpyAsync(h->staging, j.src, bytes, hipMemcpyDefault, st));
+    const size_t raw = j.fmt == kFmtCB2 ? kCB2Bytes : j.fmt == kFmtQ4K ? kQ4KBytes : kQ2KBytes;
+    QS_HIP(hipMemcpyAsync(h->staging, j.src, E * j.nblk * raw, hipMemcpyDefault, st));
     const size_t total = E * j.nblk;
     const dim3 grid((unsigned)((total + 255) / 256));
-    if (j.cb2)
+    if (j.fmt == kFmtCB2)
       hipLaunchKernelGGL(k_repack_cb2, grid, dim3(256), 0, st, (const uint8_t*)h->staging, j.dst,
+                         j.nblk, j.stride, E);
+    else if (j.fmt == kFmtQ4K)
+      hipLaunchKernelGGL(k_repack_q4k, grid, dim3(256), 0, st, (const uint8_t*)h->staging, j.dst,
                          j.nblk, j.stride, E);
     else
       hipLaunchKernelGGL(k_repack_q2k, grid, dim3(256), 0, st, (const uint8_t*)h->staging, j.dst,
@@ -1130,19 +1223,21 @@ QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* ou
   }
   const uint8_t* mat;
   size_t nblk;
-  bool cb2;
+  int fmt;
   if (which < 2) {
-    mat = (which == 0 ? L.gate : L.up) + (size_t)expert * h->gu_stride;
+    mat = (which == 0 ? L.gate : L.up) + (size_t)expert * (L.q4k ? h->gu_stride4 : h->gu_stride);
     nblk = F * (H / kBlockW);
-    cb2 = c.gate_up_format == QS_FMT_CB2;
+    fmt = L.q4k ? kFmtQ4K : c.gate_up_format;
   } else {
-    mat = L.down + (size_t)expert * h->dn_stride;
+    mat = L.down + (size_t)expert * (L.q4k ? h->dn_stride4 : h->dn_stride);
     nblk = H * (F / kBlockW);
-    cb2 = false;
+    fmt = L.q4k ? kFmtQ4K : kFmtQ2K;
   }
   const dim3 grid((unsigned)((nblk + 255) / 256));
-  if (cb2)
+  if (fmt == kFmtCB2)
     hipLaunchKernelGGL(k_dequant_cb2, grid, dim3(256), 0, st, mat, (const uint32_t*)h->cbtab, nblk, out);
+  else if (fmt == kFmtQ4K)
+    hipLaunchKernelGGL(k_dequant_q4k, grid, dim3(256), 0, st, mat, nblk, out);
   else
     hipLaunchKernelGGL(k_dequant_q2k, grid, dim3(256), 0, st, mat, nblk, out);
   QS_HIP(hipGetLastError());

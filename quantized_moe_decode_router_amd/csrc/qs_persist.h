@@ -78,6 +78,7 @@ struct PersistArgs {
   int G;                     // workgroups of the launch (a multiple of 8)
   int n_layers, T, H, E, k, F, Fs;
   int gq2k, prenorm, residual;
+  int gfmt, dfmt;            // routed gate/up and down formats (kFmt*): Q4_K layers have both at kFmtQ4K
   int sq8;                   // shared expert in 8-bit blocks (else bf16)
   int r_et, r_tt;            // router unit: experts x tokens
   uint32_t pfb;              // bytes of the LDS weight-staging buffer
@@ -564,9 +565,7 @@ __device__ __forceinline__ uint32_t shared_item_bytes(const A& a) {
 }
 template <class A>
 __device__ __forceinline__ uint32_t gu_tile_bytes(const A& a) {
-  const uint32_t nbh = a.H / kBlockW;
-  const uint32_t sper = a.gq2k ? 16u : 4u, dper = a.gq2k ? 4u : 2u;
-  return 2u * (uint32_t)kGateTile * nbh * (64u + sper + dper);
+  return 2u * (uint32_t)kGateTile * (a.H / kBlockW) * blk_bytes(a.gfmt);
 }
 template <class A>
 __device__ __forceinline__ uint32_t sd_bytes(const A& a) { return (uint32_t)kDownRows * srow_bytes(a.Fs, a.sq8 != 0); }
@@ -647,9 +646,10 @@ template <class A>
 __device__ __forceinline__ TileLds tile_lds(const A& a) {
   TileLds t;
   const uint32_t nbh = a.H / kBlockW;
-  t.qb = (uint32_t)kGateTile * nbh * 64;
-  t.sb = (uint32_t)kGateTile * nbh * (a.gq2k ? 16u : 4u);
-  t.db = (uint32_t)kGateTile * nbh * (a.gq2k ? 4u : 2u);
+  const BlkGeom g = blk_geom(a.gfmt);
+  t.qb = (uint32_t)kGateTile * nbh * g.q;
+  t.sb = (uint32_t)kGateTile * nbh * g.s;
+  t.db = (uint32_t)kGateTile * nbh * g.d;
   t.s = 2 * t.qb;
   t.d = 2 * t.qb + 2 * t.sb;
   return t;
@@ -660,15 +660,15 @@ __device__ __forceinline__ void copy_tile(const A& a, const LayerPtrs& Lp, QS_LD
                                           int f0, int w, int nw) {
   const uint32_t nbh = a.H / kBlockW;
   const size_t nblk = (size_t)a.F * nbh;
-  const MatPlanes pl = a.gq2k ? q2k_planes(nblk) : cb2_planes(nblk);
-  const uint32_t sper = a.gq2k ? 16u : 4u, dper = a.gq2k ? 4u : 2u;
+  const MatPlanes pl = fmt_planes(a.gfmt, nblk);
+  const BlkGeom g = blk_geom(a.gfmt);
   const TileLds tl = tile_lds(a);
   const size_t b0 = (size_t)f0 * nbh;
   for (int m = 0; m < 2; ++m) {
     const uint8_t* src = (m ? Lp.up : Lp.gate) + (size_t)e * a.gu_stride;
-    dma_to_lds<0>(src + pl.q + b0 * 64, dst + m * tl.qb, tl.qb, w, nw);
-    dma_to_lds<0>(src + pl.s + b0 * sper, dst + tl.s + m * tl.sb, tl.sb, w, nw);
-    dma_to_lds<0>(src + pl.d + b0 * dper, dst + tl.d + m * tl.db, tl.db, w, nw);
+    dma_to_lds<0>(src + pl.q + b0 * g.q, dst + m * tl.qb, tl.qb, w, nw);
+    dma_to_lds<0>(src + pl.s + b0 * g.s, dst + tl.s + m * tl.sb, tl.sb, w, nw);
+    dma_to_lds<0>(src + pl.d + b0 * g.d, dst + tl.d + m * tl.db, tl.db, w, nw);
   }
 }
 
@@ -2366,6 +2366,7 @@ template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int T_, in
 struct FixedArgs : PersistArgs {
   static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, sq8 = SQ8_, T = T_, G = G_;
   static constexpr int gq2k = FMT == 1, r_et = 1, r_tt = T_;
+  static constexpr int gfmt = FMT, dfmt = FMT == kFmtQ4K ? kFmtQ4K : kFmtQ2K;
   static constexpr bool kFixedShape = true;
 };
 

@@ -12,19 +12,24 @@ class MoE:
 
     def __init__(self, hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format,
                  down_format, n_layers, max_tokens, codebook=None, mfma_min_tokens=0, device=-1,
-                 shared_format="bf16"):
+                 shared_format="bf16", tail_layers=0):
         self.cfg = L.make_config(hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format,
                                  down_format, n_layers, max_tokens, mfma_min_tokens, device,
-                                 shared_format)
+                                 shared_format, tail_layers)
         cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
         self._cb = cb
         self.h = L.qs_moe_create(self.cfg, cb)
 
     @classmethod
     def for_workload(cls, wl, codebook, n_layers=None, max_tokens=64, **kw):
+        """A handle for the first n_layers layers of a synthetic workload (its
+        Q4_K-style tail layers among them, if any)."""
+        n = n_layers or wl.n_layers
+        tail = max(0, n - (wl.n_layers - getattr(wl, "tail_layers", 0)))
         return cls(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ffn, wl.shared_ffn,
-                   wl.gate_up_format, wl.down_format, n_layers or wl.n_layers, max_tokens,
-                   codebook=codebook, shared_format=getattr(wl, "shared_format", "bf16"), **kw)
+                   wl.gate_up_format, wl.down_format, n, max_tokens,
+                   codebook=codebook, shared_format=getattr(wl, "shared_format", "bf16"),
+                   tail_layers=tail, **kw)
 
     # -- lifetime ---------------------------------------------------------
     def close(self):

@@ -49,7 +49,7 @@ def test_header_formats_match_binding():
     enum = re.search(r"typedef enum \{([^}]*)\} qs_format;", text).group(1)
     vals = {n: int(v) for n, v in re.findall(r"(QS_FMT_\w+)\s*=\s*(\d+)", enum)}
     assert vals == {"QS_FMT_BF16": qm.QS_FMT_BF16, "QS_FMT_Q2K": qm.QS_FMT_Q2K,
-                    "QS_FMT_CB2": qm.QS_FMT_CB2, "QS_FMT_Q8": qm.QS_FMT_Q8}
+                    "QS_FMT_CB2": qm.QS_FMT_CB2, "QS_FMT_Q8": qm.QS_FMT_Q8, "QS_FMT_Q4K": qm.QS_FMT_Q4K}
     # the config struct's fields, in the header's order
     body = re.search(r"typedef struct \{([^}]*)\} qs_moe_config;", text).group(1)
     names = re.findall(r"int32_t\s+(\w+);", body)
@@ -74,6 +74,7 @@ def _good():
     ("shared_ffn", -64), ("shared_ffn", 100), ("gate_up_format", 7), ("down_format", 0),
     ("n_layers", 0), ("max_tokens", 0), ("max_tokens", 257), ("mfma_min_tokens", -1),
     ("shared_format", 1), ("shared_format", 2), ("shared_format", 4), ("shared_format", -1),
+    ("tail_layers", -1), ("tail_layers", 2),
 ])
 def test_create_rejects_invalid_config_without_gpu(field, value):
     kw = _good()

@@ -25,6 +25,7 @@ CASES = {
     "a3b_routed40": ((1, 4), (0, 39), 2),
     "a3b_routed40_q2k": ((1,), (0, 39), 1),
     "a3b_stack40_zipf_q8": ((1, 4, 16), (0, 39), 2),
+    "a3b_stack40_q4tail": ((1, 4, 16), (0, 33, 34, 39), 2),
     "flash_stack8_zipf": ((1, 8, 32), (0, 7), 2),
 }
 PARAMS = [(n, T) for n, c in CASES.items() for T in c[0]]
