@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define QS_MOE_ABI_VERSION 4
+#define QS_MOE_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define QS_API __attribute__((visibility("default")))
@@ -141,6 +141,26 @@ typedef struct {
                               Those layers run the batched kernel's GEMV items
                               (no MFMA items), at every batch size; a decode
                               call over both kinds of layer is two launches */
+  /* Routed-expert paging, the MI355X form of running a model whose routed
+   * experts exceed device memory (QuarkStar README, "Running Models Larger
+   * Than Available Memory": non-routed weights stay resident, a prefix of
+   * layers can stay fully resident, the selected routed experts go through
+   * a bounded cache filled from a slower tier).  The slower tier here is
+   * pinned host memory: a decode call reads an expert that is not in the
+   * cache straight from host memory over PCIe, so no call waits for a copy
+   * or a host round trip; after the call the cache admits the experts it
+   * missed (least-recently-used eviction, copies by the DMA engines), in
+   * the background of later calls.  Outputs are bitwise the same as with
+   * every layer resident: only where the bytes are read from changes. */
+  int32_t expert_paging;   /* 0: every layer resident (the next two fields must
+                              be 0); 1: paging on */
+  int32_t resident_layers; /* paging: layers [0, resident_layers) keep their
+                              routed experts in HBM; the routed experts of the
+                              later layers ("paged layers") live in pinned host
+                              memory.  0..n_layers */
+  int32_t cache_slots;     /* paging: HBM slots of the expert cache, each holding
+                              one paged expert's gate, up and down matrices;
+                              0..(paged layers * E) */
 } qs_moe_config;
 
 /* One layer's weights in the raw block layout above.  Host or device
@@ -175,6 +195,9 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
  * The weights stay resident in HBM, as the pages keep the whole quantised
  * model resident when it fits (QuarkStar README, "Model Weights" and
  * "Running Models Larger Than Available Memory").
+ * A paged layer (expert_paging) keeps its router and shared expert in HBM
+ * and its re-laid routed experts in the handle's pinned host memory;
+ * re-uploading it drops its experts from the cache.
  * hip_stream: a hipStream_t or NULL for the null stream.  Returns after the
  * copies are complete, so the sources may be freed at once.  Re-uploading a
  * layer replaces it. */
@@ -198,7 +221,10 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
  * in rank order (logit descending, ties to the lower index).
  * w_out: device fp32 [n_layers][n_tokens][k] or NULL -- their renormalised
  * softmax weights.  One persistent kernel launch on hip_stream, asynchronous;
- * performs no allocation and no host synchronisation.
+ * performs no allocation and no host synchronisation.  With expert_paging a
+ * call over paged layers also first enqueues the cache admissions of earlier
+ * completed calls (see qs_moe_cache_sync), and afterwards copies its ids to
+ * host memory and records an event; it does not wait for either.
  * 1 <= n_tokens <= max_tokens.  Non-finite inputs give non-finite outputs but
  * never an out-of-range expert id.
  * Every wait inside the kernel is bounded: a call whose wait gives up (a
@@ -266,6 +292,39 @@ QS_API int qs_moe_set_wait_limit(qs_moe* h, int32_t polls);
  * batched kernel takes one more grid barrier per layer. */
 QS_API int qs_moe_set_steering(qs_moe* h, const float* dirs, float scale, void* hip_stream);
 
+/* Expert cache of a handle with expert_paging (QS_E_STATE without it).
+ *
+ * Policy: least-recently-used over all slots of all paged layers.  The uses
+ * of a decode call are the distinct (layer, expert) pairs of its paged
+ * layers in (layer, token, rank) order; a use of a cached expert refreshes
+ * it, a use of an uncached one admits it into a free slot (lowest index
+ * first) or else evicts the least recently used expert.  A call's uses are
+ * applied after the call, in call order; qs_moe_decode applies those of
+ * earlier calls that have completed by the time it is called, without
+ * waiting, so the cache state a call sees may lag by a few calls (outputs
+ * never depend on it).  qs_moe_decode_static neither reads back ids nor
+ * updates the cache (it reads through the map as it stands).
+ *
+ * qs_moe_cache_sync: waits for hip_stream and every pending call, applies
+ *   their uses and enqueues the admissions on hip_stream, then waits for
+ *   them; afterwards the cache state is exactly that of the policy applied
+ *   to every completed call in order.
+ * qs_moe_cache_preload: the popularity hotlist warm start (QuarkStar README,
+ *   "Running Models Larger Than Available Memory": warm streaming preloads a
+ *   bounded popularity hotlist).  keys: host int32 [n][2] of (layer,
+ *   expert), hottest first; each paged pair not cached takes a free slot
+ *   until none is left (nothing is evicted).  Synchronises like
+ *   qs_moe_cache_sync.  QS_E_INVAL for a key outside the paged layers.
+ * qs_moe_cache_stats: host uint64 out[8] = {hits, misses, admissions,
+ *   evictions, preloaded, slots in use, slots, host bytes of the paged
+ *   experts}, counted over the uses applied so far.
+ * qs_moe_cache_slots: host int32 out[cache_slots][2]: (layer, expert) held by
+ *   each slot, (-1, -1) for a free slot, as of the uses applied so far. */
+QS_API int qs_moe_cache_sync(qs_moe* h, void* hip_stream);
+QS_API int qs_moe_cache_preload(qs_moe* h, const int32_t* keys, int n, void* hip_stream);
+QS_API int qs_moe_cache_stats(qs_moe* h, uint64_t* out);
+QS_API int qs_moe_cache_slots(qs_moe* h, int32_t* out);
+
 /* Routing only (diagnostics and tests): the router, top-k and grouping steps
  * of one layer for n_tokens tokens, with every intermediate written out
  * (the selection of the QuarkStar README, "Model Weights": the router stays
@@ -295,7 +354,8 @@ QS_API int qs_moe_route(qs_moe* h, int layer, const float* x, int n_tokens, uint
  * gate/up) or [H][Fs] (shared down).  Asynchronous. */
 QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* out, void* hip_stream);
 
-/* Bytes of device memory the handle holds (weights + scratch); the pages
+/* Bytes of device memory the handle holds (weights + scratch; the paged
+ * experts' host copies are not counted, see qs_moe_cache_stats); the pages
  * budget the resident weight footprint against the device memory
  * (QuarkStar README, "Model Weights"). */
 QS_API int qs_moe_memory_bytes(const qs_moe* h, uint64_t* bytes);

@@ -10,7 +10,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsmoe.so")
 
-QS_MOE_ABI_VERSION = 4
+QS_MOE_ABI_VERSION = 5
 QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 QS_FMT_BF16, QS_FMT_Q2K, QS_FMT_CB2, QS_FMT_Q8, QS_FMT_Q4K = 0, 1, 2, 3, 4
 QS_DECODE_RESIDUAL = 1
@@ -22,7 +22,7 @@ FORMATS = {"bf16": QS_FMT_BF16, "q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2, "q8": QS_F
 # Every function include/qs_moe.h declares.
 EXPORTS = (
     "qs_moe_create", "qs_moe_upload", "qs_moe_decode", "qs_moe_decode_static", "qs_moe_sync_status", "qs_moe_set_wait_limit",
-    "qs_moe_set_steering",
+    "qs_moe_set_steering", "qs_moe_cache_sync", "qs_moe_cache_preload", "qs_moe_cache_stats", "qs_moe_cache_slots",
     "qs_moe_route", "qs_moe_dequant", "qs_moe_memory_bytes", "qs_moe_destroy", "qs_moe_status_string",
 )
 
@@ -31,7 +31,7 @@ class QsMoeConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "hidden", "n_experts", "top_k", "expert_ffn", "shared_ffn",
         "gate_up_format", "down_format", "n_layers", "max_tokens", "mfma_min_tokens", "device",
-        "shared_format", "tail_layers")]
+        "shared_format", "tail_layers", "expert_paging", "resident_layers", "cache_slots")]
 
 
 class QsMoeLayerWeights(ctypes.Structure):
@@ -67,6 +67,10 @@ def _load() -> ctypes.CDLL:
         "qs_moe_sync_status": [vp, vp],
         "qs_moe_set_wait_limit": [vp, ctypes.c_int32],
         "qs_moe_set_steering": [vp, vp, ctypes.c_float, vp],
+        "qs_moe_cache_sync": [vp, vp],
+        "qs_moe_cache_preload": [vp, vp, i32, vp],
+        "qs_moe_cache_stats": [vp, vp],
+        "qs_moe_cache_slots": [vp, vp],
         "qs_moe_route": [vp, i32, vp, i32, u32, vp, vp, vp, vp, vp],
         "qs_moe_dequant": [vp, i32, i32, i32, vp, vp],
         "qs_moe_memory_bytes": [vp, ctypes.POINTER(ctypes.c_uint64)],
@@ -119,11 +123,12 @@ def _stream(stream) -> int:
 
 def make_config(hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format, down_format,
                 n_layers, max_tokens, mfma_min_tokens=0, device=-1, shared_format="bf16",
-                tail_layers=0) -> QsMoeConfig:
+                tail_layers=0, expert_paging=0, resident_layers=0, cache_slots=0) -> QsMoeConfig:
     fmt = lambda f: FORMATS[f] if isinstance(f, str) else int(f)  # noqa: E731
     return QsMoeConfig(QS_MOE_ABI_VERSION, hidden, n_experts, top_k, expert_ffn, shared_ffn,
                        fmt(gate_up_format), fmt(down_format), n_layers, max_tokens,
-                       mfma_min_tokens, device, fmt(shared_format), tail_layers)
+                       mfma_min_tokens, device, fmt(shared_format), tail_layers,
+                       expert_paging, resident_layers, cache_slots)
 
 
 def qs_moe_create(cfg: QsMoeConfig, codebook=None) -> int:
@@ -161,6 +166,25 @@ def qs_moe_set_wait_limit(h: int, polls: int) -> None:
 
 def qs_moe_set_steering(h: int, dirs, scale: float, stream=None) -> None:
     check("qs_moe_set_steering", LIB.qs_moe_set_steering(h, _ptr(dirs), scale, _stream(stream)))
+
+
+def qs_moe_cache_sync(h: int, stream=None) -> None:
+    check("qs_moe_cache_sync", LIB.qs_moe_cache_sync(h, _stream(stream)))
+
+
+def qs_moe_cache_preload(h: int, keys, stream=None) -> None:
+    """keys: numpy int32 [n][2] of (layer, expert), hottest first."""
+    check("qs_moe_cache_preload", LIB.qs_moe_cache_preload(h, _ptr(keys), len(keys), _stream(stream)))
+
+
+def qs_moe_cache_stats(h: int, out) -> None:
+    """out: numpy uint64 [8]."""
+    check("qs_moe_cache_stats", LIB.qs_moe_cache_stats(h, _ptr(out)))
+
+
+def qs_moe_cache_slots(h: int, out) -> None:
+    """out: numpy int32 [cache_slots][2]."""
+    check("qs_moe_cache_slots", LIB.qs_moe_cache_slots(h, _ptr(out)))
 
 
 def qs_moe_route(h: int, layer: int, x, n_tokens: int, flags: int = 0, logits_out=None,

@@ -310,7 +310,7 @@ __device__ __forceinline__ void copy_dn_rows(const A& a, const LayerPtrs& Lp, QS
   const uint32_t nb = a.F / kBlockW;
   const MatPlanes pl = fmt_planes(a.dfmt, (size_t)a.H * nb);
   const BlkGeom g = blk_geom(a.dfmt);
-  const uint8_t* base = Lp.down + (size_t)e * a.dn_stride;
+  const uint8_t* base = ex_mat(a, Lp, 2, e);
   const size_t b0 = (size_t)r0 * nb;
   const uint32_t nq = (uint32_t)n * nb * g.q, ns = (uint32_t)n * nb * g.s;
   dma_to_lds<0>(base + pl.q + b0 * g.q, dst, nq, w, nw);
@@ -804,8 +804,8 @@ __device__ __forceinline__ void gu_mfma_item(const A& a, const LayerPtrs& Lp, Bi
   const int rg = wave & 3, kh = wave >> 2;
   const int H = a.H, nbh = H / kBlockW;
   const MatPlanes pl = q2k ? q2k_planes((size_t)a.F * nbh) : cb2_planes((size_t)a.F * nbh);
-  const uint8_t* gm = Lp.gate + (size_t)e * a.gu_stride;
-  const uint8_t* um = Lp.up + (size_t)e * a.gu_stride;
+  const uint8_t* gm = ex_mat(a, Lp, 0, e);
+  const uint8_t* um = ex_mat(a, Lp, 1, e);
   const int arow = f0 + 16 * rg + r, drow0 = f0 + 16 * rg + 4 * g;
   const MguStage st = mgu_stage(P.pfb + big_gu_area(H, a.Fs, a.sq8 != 0), pp.kbg);
 #pragma unroll 1
@@ -1182,7 +1182,7 @@ __device__ __forceinline__ void dn_mfma_item(const A& a, const LayerPtrs& Lp, Bi
   const int wave = qs_tid() >> 6, lane = qs_tid() & 63, r = lane & 15, g = lane >> 4, nw = kPersistThreads >> 6;
   const int F = a.F, nb = F / kBlockW;
   const MatPlanes pl = q2k_planes((size_t)a.H * nb);
-  const uint8_t* dm = Lp.down + (size_t)e * a.dn_stride;
+  const uint8_t* dm = ex_mat(a, Lp, 2, e);
   const int arow = h0 + 16 * wave + r, drow0 = h0 + 16 * wave + 4 * g;
   const MdnStage st = mdn_stage(P.pfb + big_dn_area(a.Fs, a.sq8 != 0), pp.kbd);
 #pragma unroll 1
@@ -1528,6 +1528,11 @@ __device__ __forceinline__ void persist_big_body(const A& a) {
 template <int FMT, bool STEER>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_big(PersistArgs a) {
   persist_big_body<FMT, STEER>(a);
+}
+
+template <int FMT, bool STEER>
+__global__ void __launch_bounds__(kPersistThreads) k_persist_big_paged(PersistArgs a) {
+  persist_big_body<FMT, STEER>(static_cast<const PagedArgs&>(a));
 }
 
 // The layer shape fixed at compile time, the batch size at run time (as

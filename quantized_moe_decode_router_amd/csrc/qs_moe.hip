@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <mutex>
 #include <new>
+#include <set>
 #include <vector>
 
 #include "qs_moe.h"
@@ -39,6 +40,19 @@ struct LayerDev {
   uint8_t* su = nullptr;
   uint8_t* sd = nullptr;
   bool uploaded = false;
+  // a paged layer: its routed experts as records [gate | up | down] in
+  // pinned host memory, E * rec_bytes, and the address the GPU reads them at
+  uint8_t* host = nullptr;
+  uint64_t host_dev = 0;
+  size_t rec_bytes = 0;
+};
+
+// One decode call over paged layers whose ids have not been applied to the
+// expert cache yet: its ids travel to pinned host memory behind the call.
+struct PendingCall {
+  hipEvent_t ev = nullptr;
+  int32_t* ids = nullptr;    // pinned [nL][T][k] of the call's paged layers
+  int layer0 = 0, nL = 0, T = 0;
 };
 
 struct Scratch {
@@ -129,9 +143,33 @@ struct qs_moe {
   bool big_fixed_ok = false;      // the fixed-shape batched kernel is usable
   bool fixed_steer_ok = false;    // the same with the steered combine
   bool big_fixed_steer_ok = false;
+  bool pg_small_ok[2] = {false, false};   // the instantiations for paged layers, [steer]
+  bool pg_big_ok[2] = {false, false};
+  bool pg_q4k_ok[2] = {false, false};
   uint32_t ll_epoch = 0;          // flags used by the small-batch kernel so far
   float* steer_dirs = nullptr;    // steering directions, device fp32 [n_layers][H] (null: none set)
   float steer_scale = 0.f;
+  // ---- expert paging (layers [resident_layers, n_layers) are paged)
+  int n_paged = 0;
+  size_t slot_bytes = 0;          // one cache slot: the largest paged record
+  uint8_t* slots = nullptr;       // HBM [cache_slots][slot_bytes]
+  uint64_t* d_emap = nullptr;     // device [n_paged][E]: the address each expert is read at
+  uint8_t* pstage = nullptr;      // HBM: one paged layer's records, re-laid before the copy to host
+  int32_t* ids_buf = nullptr;     // device [n_layers][max_tokens][k]: ids of a call whose caller passes none
+  std::vector<uint64_t> emap;     // host mirror of d_emap
+  std::vector<int32_t> slot_of;   // [n_paged * E] slot holding the expert, or -1
+  std::vector<int32_t> owner;     // [cache_slots] key (paged layer * E + expert) or -1
+  std::vector<int32_t> lru_prev, lru_next;   // the occupied slots, least recent first
+  int lru_head = -1, lru_tail = -1;
+  std::set<int32_t> free_slots;
+  std::vector<int32_t> copy_key;  // [cache_slots] key to copy into the slot at the next flush, or -1
+  std::vector<int32_t> dirty;     // keys whose map entry changed since the last flush
+  std::vector<uint8_t> seen;      // [E] marks of one layer's uses
+  uint64_t c_hits = 0, c_misses = 0, c_admits = 0, c_evicts = 0, c_preloaded = 0;
+  uint64_t host_bytes = 0;
+  std::vector<PendingCall> ring;  // pending calls, oldest at ring_head
+  int ring_head = 0, ring_count = 0;
+  int32_t* ring_ids = nullptr;    // pinned, the ring's id buffers
 };
 
 namespace {
@@ -184,6 +222,11 @@ int validate_config(const qs_moe_config* c) {
   if (c->device < -1) return QS_E_INVAL;
   if (c->shared_format != QS_FMT_BF16 && c->shared_format != QS_FMT_Q8) return QS_E_INVAL;
   if (c->tail_layers < 0 || c->tail_layers > c->n_layers) return QS_E_INVAL;
+  if (c->expert_paging != 0 && c->expert_paging != 1) return QS_E_INVAL;
+  if (!c->expert_paging && (c->resident_layers || c->cache_slots)) return QS_E_INVAL;
+  if (c->resident_layers < 0 || c->resident_layers > c->n_layers) return QS_E_INVAL;
+  if (c->cache_slots < 0 || (long)c->cache_slots > (long)(c->n_layers - c->resident_layers) * c->n_experts)
+    return QS_E_INVAL;
   if (c->down_format != QS_FMT_Q2K) return QS_E_UNSUPPORTED;
   return QS_OK;
 }
@@ -287,8 +330,17 @@ void carve_scratch(const qs_moe_config& c, Scratch& s) {
 }
 
 void free_all(qs_moe* h) {
-  for (auto& L : h->layers)
+  for (auto& L : h->layers) {
     if (L.base) (void)hipFree(L.base);
+    if (L.host) (void)hipHostFree(L.host);
+  }
+  if (h->slots) (void)hipFree(h->slots);
+  if (h->d_emap) (void)hipFree(h->d_emap);
+  if (h->pstage) (void)hipFree(h->pstage);
+  if (h->ids_buf) (void)hipFree(h->ids_buf);
+  for (auto& pc : h->ring)
+    if (pc.ev) (void)hipEventDestroy(pc.ev);
+  if (h->ring_ids) (void)hipHostFree(h->ring_ids);
   if (h->s.base) (void)hipFree(h->s.base);
   if (h->steer_dirs) (void)hipFree(h->steer_dirs);
   if (h->cbtab) (void)hipFree(h->cbtab);
@@ -313,6 +365,249 @@ void launch_zero(void* p, size_t bytes, hipStream_t st) {
   const size_t n = bytes / 16;
   const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
   if (n) hipLaunchKernelGGL(k_zero16, dim3(blocks), dim3(256), 0, st, (uint4*)p, n);
+}
+
+// ------------------------------------------------------ expert paging ---
+// The expert cache's policy runs on the host: least-recently-used over all
+// slots, a use per distinct (layer, expert) of a call's paged layers in
+// (layer, token, rank) order.  The device sees only its result, the map of
+// each paged expert to the address it is read at (a slot, or its host
+// record).  A flush enqueues the admitted experts' copies (DMA engines) and
+// then the changed map entries on the stream, ahead of the next decode
+// launch; a launch never runs between the two.
+constexpr int kRing = 8;          // decode calls whose ids may be in flight to the host
+constexpr int kEmapBatch = 48;    // map entries per update launch (kernel arguments)
+
+struct EmapUpd {
+  int32_t n;
+  int32_t idx[kEmapBatch];
+  uint64_t val[kEmapBatch];
+};
+
+__global__ void k_emap_set(uint64_t* emap, EmapUpd u) {
+  const int i = threadIdx.x;
+  if (i < u.n) emap[u.idx[i]] = u.val[i];
+}
+
+uint64_t host_addr(const qs_moe* h, int key) {
+  const int E = h->cfg.n_experts;
+  const LayerDev& L = h->layers[h->cfg.resident_layers + key / E];
+  return L.host_dev + (uint64_t)(key % E) * L.rec_bytes;
+}
+
+uint64_t slot_addr(const qs_moe* h, int v) { return (uint64_t)(uintptr_t)(h->slots + (size_t)v * h->slot_bytes); }
+
+void lru_unlink(qs_moe* h, int v) {
+  const int p = h->lru_prev[v], n = h->lru_next[v];
+  (p >= 0 ? h->lru_next[p] : h->lru_head) = n;
+  (n >= 0 ? h->lru_prev[n] : h->lru_tail) = p;
+  h->lru_prev[v] = h->lru_next[v] = -1;
+}
+
+void lru_push_back(qs_moe* h, int v) {   // most recent end
+  h->lru_prev[v] = h->lru_tail;
+  h->lru_next[v] = -1;
+  (h->lru_tail >= 0 ? h->lru_next[h->lru_tail] : h->lru_head) = v;
+  h->lru_tail = v;
+}
+
+void lru_push_front(qs_moe* h, int v) {  // least recent end
+  h->lru_next[v] = h->lru_head;
+  h->lru_prev[v] = -1;
+  (h->lru_head >= 0 ? h->lru_prev[h->lru_head] : h->lru_tail) = v;
+  h->lru_head = v;
+}
+
+// Slot v now holds `key`; its bytes are copied at the next flush.
+void slot_take(qs_moe* h, int v, int key) {
+  h->owner[v] = key;
+  h->slot_of[key] = v;
+  h->copy_key[v] = key;
+  h->dirty.push_back(key);
+}
+
+// One use of expert `key` by a decode call.
+void cache_use(qs_moe* h, int key) {
+  const int s = h->slot_of[key];
+  if (s >= 0) {
+    ++h->c_hits;
+    lru_unlink(h, s);
+    lru_push_back(h, s);
+    return;
+  }
+  ++h->c_misses;
+  int v;
+  if (!h->free_slots.empty()) {
+    v = *h->free_slots.begin();
+    h->free_slots.erase(h->free_slots.begin());
+  } else if (h->lru_head >= 0) {
+    v = h->lru_head;
+    lru_unlink(h, v);
+    const int old = h->owner[v];
+    h->slot_of[old] = -1;
+    h->dirty.push_back(old);
+    ++h->c_evicts;
+  } else {
+    return;   // no slots at all
+  }
+  slot_take(h, v, key);
+  lru_push_back(h, v);
+  ++h->c_admits;
+}
+
+// The uses of one completed call.
+void cache_apply(qs_moe* h, const PendingCall& pc) {
+  const qs_moe_config& c = h->cfg;
+  const int E = c.n_experts, k = c.top_k, R = c.resident_layers;
+  const int lp0 = std::max(pc.layer0, R);
+  for (int l = lp0; l < pc.layer0 + pc.nL; ++l) {
+    const int32_t* id = pc.ids + (size_t)(l - lp0) * pc.T * k;
+    for (int i = 0; i < pc.T * k; ++i) {
+      const int e = id[i];
+      if (e < 0 || e >= E || h->seen[e]) continue;
+      h->seen[e] = 1;
+      cache_use(h, (l - R) * E + e);
+    }
+    for (int i = 0; i < pc.T * k; ++i)
+      if (id[i] >= 0 && id[i] < E) h->seen[id[i]] = 0;
+  }
+}
+
+// Enqueue the pending slot copies, then the changed map entries.
+int cache_flush(qs_moe* h, hipStream_t st) {
+  const int E = h->cfg.n_experts;
+  for (int v = 0; v < (int)h->copy_key.size(); ++v) {
+    const int key = h->copy_key[v];
+    if (key < 0) continue;
+    h->copy_key[v] = -1;
+    if (h->owner[v] != key) continue;   // replaced again before this flush
+    const LayerDev& L = h->layers[h->cfg.resident_layers + key / E];
+    QS_HIP(hipMemcpyAsync(h->slots + (size_t)v * h->slot_bytes, L.host + (size_t)(key % E) * L.rec_bytes,
+                          L.rec_bytes, hipMemcpyHostToDevice, st));
+  }
+  std::sort(h->dirty.begin(), h->dirty.end());
+  h->dirty.erase(std::unique(h->dirty.begin(), h->dirty.end()), h->dirty.end());
+  for (size_t i0 = 0; i0 < h->dirty.size(); i0 += kEmapBatch) {
+    EmapUpd u{};
+    u.n = (int)std::min<size_t>(kEmapBatch, h->dirty.size() - i0);
+    for (int j = 0; j < u.n; ++j) {
+      const int key = h->dirty[i0 + j];
+      const int v = h->slot_of[key];
+      const uint64_t a = v >= 0 ? slot_addr(h, v) : host_addr(h, key);
+      h->emap[key] = a;
+      u.idx[j] = key;
+      u.val[j] = a;
+    }
+    hipLaunchKernelGGL(k_emap_set, dim3(1), dim3(64), 0, st, h->d_emap, u);
+    QS_HIP(hipGetLastError());
+  }
+  h->dirty.clear();
+  return QS_OK;
+}
+
+// Apply the pending calls that have completed (all of them, waiting, with
+// `wait`), then flush.
+int cache_poll(qs_moe* h, hipStream_t st, bool wait) {
+  while (h->ring_count > 0) {
+    PendingCall& pc = h->ring[h->ring_head];
+    if (wait) {
+      QS_HIP(hipEventSynchronize(pc.ev));
+    } else {
+      const hipError_t q = hipEventQuery(pc.ev);
+      if (q == hipErrorNotReady) {
+        (void)hipGetLastError();
+        break;
+      }
+      QS_HIP(q);
+    }
+    cache_apply(h, pc);
+    h->ring_head = (h->ring_head + 1) % kRing;
+    --h->ring_count;
+  }
+  return cache_flush(h, st);
+}
+
+// After a decode call over layers [layer0, layer0 + nL): its paged layers'
+// ids (device [nL][T][k] at ids) go to host memory behind it.
+int cache_record(qs_moe* h, const int32_t* ids, int layer0, int nL, int T, hipStream_t st) {
+  const int k = h->cfg.top_k, lp0 = std::max(layer0, h->cfg.resident_layers);
+  if (lp0 >= layer0 + nL) return QS_OK;
+  if (h->ring_count == kRing) {   // the oldest pending call must be applied first
+    PendingCall& old = h->ring[h->ring_head];
+    QS_HIP(hipEventSynchronize(old.ev));
+    cache_apply(h, old);
+    h->ring_head = (h->ring_head + 1) % kRing;
+    --h->ring_count;
+  }
+  PendingCall& pc = h->ring[(h->ring_head + h->ring_count) % kRing];
+  const size_t n = (size_t)(layer0 + nL - lp0) * T * k;
+  QS_HIP(hipMemcpyAsync(pc.ids, ids + (size_t)(lp0 - layer0) * T * k, n * 4, hipMemcpyDeviceToHost, st));
+  QS_HIP(hipEventRecord(pc.ev, st));
+  pc.layer0 = layer0;
+  pc.nL = nL;
+  pc.T = T;
+  ++h->ring_count;
+  return QS_OK;
+}
+
+// Paging state at create: every paged expert is read from host memory.
+int setup_paging(qs_moe* h) {
+  const qs_moe_config& c = h->cfg;
+  const size_t E = c.n_experts, keys = (size_t)h->n_paged * E, S = c.cache_slots;
+  if (S) {
+    if (!hip_ok(hipMalloc(&h->slots, S * h->slot_bytes), "hipMalloc(cache slots)")) {
+      h->slots = nullptr;
+      return QS_E_NOMEM;
+    }
+    h->total_bytes += S * h->slot_bytes;
+  }
+  if (!hip_ok(hipMalloc(&h->d_emap, keys * 8), "hipMalloc(expert map)")) {
+    h->d_emap = nullptr;
+    return QS_E_NOMEM;
+  }
+  const size_t idsn = (size_t)c.n_layers * c.max_tokens * c.top_k;
+  if (!hip_ok(hipMalloc(&h->ids_buf, idsn * 4), "hipMalloc(ids)")) {
+    h->ids_buf = nullptr;
+    return QS_E_NOMEM;
+  }
+  h->total_bytes += keys * 8 + idsn * 4;
+  const size_t per = (size_t)h->n_paged * c.max_tokens * c.top_k;
+  void* hp = nullptr;
+  if (!hip_ok(hipHostMalloc(&hp, kRing * per * 4, hipHostMallocDefault), "hipHostMalloc(ids ring)"))
+    return QS_E_NOMEM;
+  h->ring_ids = (int32_t*)hp;
+  h->ring.resize(kRing);
+  for (int i = 0; i < kRing; ++i) {
+    QS_HIP(hipEventCreateWithFlags(&h->ring[i].ev, hipEventDisableTiming));
+    h->ring[i].ids = h->ring_ids + i * per;
+  }
+  h->emap.resize(keys);
+  for (size_t key = 0; key < keys; ++key) h->emap[key] = host_addr(h, (int)key);
+  QS_HIP(hipMemcpy(h->d_emap, h->emap.data(), keys * 8, hipMemcpyHostToDevice));
+  h->slot_of.assign(keys, -1);
+  h->owner.assign(S, -1);
+  h->lru_prev.assign(S, -1);
+  h->lru_next.assign(S, -1);
+  h->copy_key.assign(S, -1);
+  h->seen.assign(E, 0);
+  for (size_t v = 0; v < S; ++v) h->free_slots.insert((int32_t)v);
+  return QS_OK;
+}
+
+// A re-uploaded paged layer: its cached experts are dropped (their slots
+// become free) and read from the new host records.
+void cache_drop_layer(qs_moe* h, int pl) {
+  const int E = h->cfg.n_experts;
+  for (int e = 0; e < E; ++e) {
+    const int key = pl * E + e, v = h->slot_of[key];
+    if (v < 0) continue;
+    lru_unlink(h, v);
+    h->owner[v] = -1;
+    h->copy_key[v] = -1;
+    h->free_slots.insert(v);
+    h->slot_of[key] = -1;
+    h->dirty.push_back(key);
+  }
 }
 
 // Shape of one persistent launch: LDS carve plus as much weight-staging
@@ -355,7 +650,8 @@ int gu_units(int H) {
 
 const void* persist_fixed_fn(const qs_moe* h, int T, bool steer = false);
 
-PersistShape persist_shape(const qs_moe* h, int T, bool small) {
+// paged: for the instantiations of paged layers, which have no fixed shape
+PersistShape persist_shape(const qs_moe* h, int T, bool small, bool paged = false) {
   const qs_moe_config& c = h->cfg;
   if (!small) return big_shape(h, T, c.gate_up_format);
   PersistShape p;
@@ -363,7 +659,7 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
   const bool sq8 = c.shared_format == QS_FMT_Q8;
   // the shared expert through registers: the fixed-shape kernels above
   // hidden 2048 (sh_regs), the only small-batch kernels there
-  const bool shregs = c.hidden > 2048;
+  const bool shregs = c.hidden > 2048 && !paged;
   const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, sq8, cb2,
                                  small, 0, shregs).end;
   if (base >= h->lds_limit || h->grid_small < 8) return p;
@@ -394,7 +690,7 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small) {
     // the generic one measured 83 us per layer against the batched kernel's
     // 73, the fixed one 57.
     fits = A <= p.pfb && (p.pfb - A) + xl >= pe && gu_units(c.hidden) <= kGuUnits &&
-           (c.hidden <= 2048 || persist_fixed_fn(h, T) != nullptr);
+           (c.hidden <= 2048 || (!paged && persist_fixed_fn(h, T) != nullptr));
     // with registers: a row's chunks per lane fit one register round
     if (shregs)
       fits = fits && (H / 4 + 511) / 512 <= (uint64_t)kShPairsLds && (Fs + 511) / 512 <= (uint64_t)kShDnRegs;
@@ -420,6 +716,18 @@ const void* persist_fn(bool cb2, bool small, bool steer = false) {
   }
   if (cb2) return small ? (const void*)k_persist_small<2, false> : (const void*)k_persist_big<2, false>;
   return small ? (const void*)k_persist_small<1, false> : (const void*)k_persist_big<1, false>;
+}
+
+// The instantiations for launches over paged layers (generic shapes only).
+const void* persist_paged_fn(int fmt, bool small, bool steer) {
+  if (fmt == kFmtQ4K)
+    return steer ? (const void*)k_persist_big_paged<4, true> : (const void*)k_persist_big_paged<4, false>;
+  if (fmt == kFmtCB2) {
+    if (small) return steer ? (const void*)k_persist_small_paged<2, true> : (const void*)k_persist_small_paged<2, false>;
+    return steer ? (const void*)k_persist_big_paged<2, true> : (const void*)k_persist_big_paged<2, false>;
+  }
+  if (small) return steer ? (const void*)k_persist_small_paged<1, true> : (const void*)k_persist_small_paged<1, false>;
+  return steer ? (const void*)k_persist_big_paged<1, true> : (const void*)k_persist_big_paged<1, false>;
 }
 
 // Small-batch instantiations with the layer shape fixed at compile time:
@@ -520,7 +828,9 @@ int setup_persistent(qs_moe* h) {
   std::vector<LayerPtrs> tab(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerDev& L = h->layers[l];
-    tab[l] = LayerPtrs{L.router, L.bias, L.gate, L.up, L.down, L.sg, L.su, L.sd};
+    const int pl = l - c.resident_layers;   // paged layers read their experts through the map
+    const uint64_t* em = L.host ? h->d_emap + (size_t)pl * c.n_experts : nullptr;
+    tab[l] = LayerPtrs{L.router, L.bias, L.gate, L.up, L.down, L.sg, L.su, L.sd, em};
   }
   if (!hip_ok(hipMalloc(&h->d_layers, tab.size() * sizeof(LayerPtrs)), "hipMalloc(layers)")) {
     h->d_layers = nullptr;
@@ -562,12 +872,17 @@ int setup_persistent(qs_moe* h) {
         static_lds = std::max(static_lds, (size_t)fa.sharedSizeBytes);
       }
   for (int st = 0; st < 2; ++st) {
-    hipFuncAttributes fa;
-    if (hipFuncGetAttributes(&fa, persist_q4k_fn(st != 0)) != hipSuccess) {
-      (void)hipGetLastError();
-      return QS_OK;
+    const void* fns[] = {persist_q4k_fn(st != 0), persist_paged_fn(kFmtQ4K, false, st != 0),
+                         persist_paged_fn(kFmtCB2, true, st != 0), persist_paged_fn(kFmtCB2, false, st != 0),
+                         persist_paged_fn(kFmtQ2K, true, st != 0), persist_paged_fn(kFmtQ2K, false, st != 0)};
+    for (const void* fn : fns) {
+      hipFuncAttributes fa;
+      if (hipFuncGetAttributes(&fa, fn) != hipSuccess) {
+        (void)hipGetLastError();
+        return QS_OK;
+      }
+      static_lds = std::max(static_lds, (size_t)fa.sharedSizeBytes);
     }
-    static_lds = std::max(static_lds, (size_t)fa.sharedSizeBytes);
   }
   const size_t dev_lds = prop.maxSharedMemoryPerMultiProcessor;
   h->lds_limit = dev_lds > static_lds ? (dev_lds - static_lds) & ~(size_t)255 : 0;
@@ -584,16 +899,25 @@ int setup_persistent(qs_moe* h) {
   }
   h->persist_small_ok = lds_small && persist_resident(h, true, lds_small);
   h->persist_big_ok = lds_big && persist_resident(h, false, lds_big);
+  size_t lds4 = 0;
   if (c.tail_layers > 0) {   // the Q4_K-style tail layers: the batched kernel at every T
-    size_t lds4 = 0;
     bool all = true;
     for (int T = 1; T <= c.max_tokens; ++T) {
       const PersistShape p = big_shape(h, T, QS_FMT_Q4K);
       all = all && p.ok;
       if (p.ok) lds4 = std::max(lds4, p.lds);
     }
-    h->q4k_ok = all && lds4 && fn_resident(persist_q4k_fn(false), lds4);
+    if (!all) lds4 = 0;
+    h->q4k_ok = lds4 && fn_resident(persist_q4k_fn(false), lds4);
     h->q4k_steer_ok = h->q4k_ok && fn_resident(persist_q4k_fn(true), lds4);
+  }
+  if (h->n_paged) {
+    const int gf = c.gate_up_format == QS_FMT_CB2 ? kFmtCB2 : kFmtQ2K;
+    for (int st = 0; st < 2; ++st) {
+      h->pg_small_ok[st] = lds_small && fn_resident(persist_paged_fn(gf, true, st != 0), lds_small);
+      h->pg_big_ok[st] = lds_big && fn_resident(persist_paged_fn(gf, false, st != 0), lds_big);
+      h->pg_q4k_ok[st] = lds4 && fn_resident(persist_paged_fn(kFmtQ4K, false, st != 0), lds4);
+    }
   }
   h->steer_small_ok = h->persist_small_ok && persist_resident(h, true, lds_small, true);
   h->steer_big_ok = h->persist_big_ok && persist_resident(h, false, lds_big, true);
@@ -627,14 +951,15 @@ int setup_persistent(qs_moe* h) {
 // instantiation when its working set fits and (with an explicit threshold)
 // no bucket can reach the MFMA size, otherwise the batched one.  False when
 // neither fits.
-bool choose_kernel(const qs_moe* h, int T, bool& small, PersistShape& p) {
-  small = T <= kSmallT && (!h->mfma_explicit || T < h->mfma_min) && h->persist_small_ok;
+bool choose_kernel(const qs_moe* h, int T, bool& small, PersistShape& p, bool paged = false) {
+  small = T <= kSmallT && (!h->mfma_explicit || T < h->mfma_min) &&
+          (paged ? h->pg_small_ok[0] : h->persist_small_ok);
   if (small) {
-    p = persist_shape(h, T, true);
+    p = persist_shape(h, T, true, paged);
     small = p.ok;
   }
   if (!small) {
-    if (!h->persist_big_ok) return false;
+    if (!(paged ? h->pg_big_ok[0] : h->persist_big_ok)) return false;
     p = persist_shape(h, T, false);
     if (!p.ok) return false;
   }
@@ -648,15 +973,19 @@ int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const flo
                    bool q4k) {
   const qs_moe_config& c = h->cfg;
   const bool cb2 = !q4k && c.gate_up_format == QS_FMT_CB2;
+  // a launch over any paged layer takes the instantiations that read the map
+  const bool paged = h->n_paged && layer0 + nL > c.resident_layers;
   bool small = false;
   PersistShape p;
   if (q4k) {
-    if (!(steer ? h->q4k_steer_ok : h->q4k_ok)) return QS_E_UNSUPPORTED;
+    if (!(paged ? h->pg_q4k_ok[steer] : steer ? h->q4k_steer_ok : h->q4k_ok)) return QS_E_UNSUPPORTED;
     p = big_shape(h, T, QS_FMT_Q4K);
     if (!p.ok) return QS_E_UNSUPPORTED;
   } else {
-    if (!choose_kernel(h, T, small, p)) return QS_E_UNSUPPORTED;   // (create checked every T)
-    if (steer && !(small ? h->steer_small_ok : h->steer_big_ok)) return QS_E_UNSUPPORTED;
+    if (!choose_kernel(h, T, small, p, paged)) return QS_E_UNSUPPORTED;   // (create checked every T)
+    if (steer && !(paged ? (small ? h->pg_small_ok[1] : h->pg_big_ok[1])
+                         : (small ? h->steer_small_ok : h->steer_big_ok)))
+      return QS_E_UNSUPPORTED;
   }
   // the batched kernel's grid barriers: five per layer (six with steering)
   // but none after the last
@@ -712,7 +1041,9 @@ int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const flo
   // the fixed-shape kernel needs the router unit it assumes (one expert per
   // workgroup, all tokens at once)
   const void* fn = nullptr;
-  if (q4k) {
+  if (paged) {
+    fn = persist_paged_fn(q4k ? kFmtQ4K : cb2 ? kFmtCB2 : kFmtQ2K, small, steer);
+  } else if (q4k) {
     fn = persist_q4k_fn(steer);
   } else {
     if (small && (steer ? h->fixed_steer_ok : h->fixed_ok) && p.r_et == 1 && p.r_tt == T)
@@ -891,11 +1222,13 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
   const size_t sgu = Fs * (size_t)srow_bytes((int)H, sq8), sdn = H * (size_t)srow_bytes((int)Fs, sq8);
   h->layers.resize(c.n_layers);
   rc = QS_OK;
+  h->n_paged = c.expert_paging ? c.n_layers - c.resident_layers : 0;
   for (int l = 0; l < c.n_layers && rc == QS_OK; ++l) {
     LayerDev& L = h->layers[l];
     L.q4k = l >= c.n_layers - c.tail_layers;
     const size_t gs = L.q4k ? h->gu_stride4 : h->gu_stride, ds = L.q4k ? h->dn_stride4 : h->dn_stride;
-    size_t lb = align_up(E * H * 4, 256) + align_up(E * 4, 256) + 2 * E * gs + E * ds;
+    const bool paged = h->n_paged && l >= c.resident_layers;
+    size_t lb = align_up(E * H * 4, 256) + align_up(E * 4, 256) + (paged ? 0 : 2 * E * gs + E * ds);
     if (Fs) lb += 2 * align_up(sgu, 256) + align_up(sdn, 256);
     if (!hip_ok(hipMalloc(&L.base, lb), "hipMalloc(layer)")) {
       L.base = nullptr;
@@ -905,9 +1238,27 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
     uint8_t* p = L.base;
     L.router = carve<float>(p, E * H);
     L.bias = carve<float>(p, E);
-    L.gate = p; p += E * gs;
-    L.up = p; p += E * gs;
-    L.down = p; p += E * ds;
+    if (paged) {   // the routed experts: one record per expert in pinned host memory
+      L.rec_bytes = 2 * gs + ds;
+      void* hp = nullptr;
+      if (!hip_ok(hipHostMalloc(&hp, E * L.rec_bytes, hipHostMallocDefault), "hipHostMalloc(experts)")) {
+        rc = QS_E_NOMEM;
+        break;
+      }
+      L.host = (uint8_t*)hp;
+      void* dp = nullptr;
+      if (!hip_ok(hipHostGetDevicePointer(&dp, hp, 0), "hipHostGetDevicePointer")) {
+        rc = QS_E_HIP;
+        break;
+      }
+      L.host_dev = (uint64_t)(uintptr_t)dp;
+      h->host_bytes += E * L.rec_bytes;
+      h->slot_bytes = std::max(h->slot_bytes, L.rec_bytes);
+    } else {
+      L.gate = p; p += E * gs;
+      L.up = p; p += E * gs;
+      L.down = p; p += E * ds;
+    }
     if (Fs) {
       L.sg = carve<uint8_t>(p, sgu);
       L.su = carve<uint8_t>(p, sgu);
@@ -941,6 +1292,7 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
       h->total_bytes += tab.size() * 4;
     }
   }
+  if (rc == QS_OK && h->n_paged) rc = setup_paging(h);
   if (rc == QS_OK) rc = setup_persistent(h);
   if (rc == QS_OK) rc = static_setup(h->device);
   if (rc == QS_OK) {
@@ -953,15 +1305,19 @@ QS_API int qs_moe_create(const qs_moe_config* cfg, const int8_t* codebook, qs_mo
     // every batch size up to max_tokens must have a persistent kernel that
     // fits the device (there is no other decode path), for the 2-bit layers
     // and for the Q4_K-style tail layers
+    // (with paging, layers [resident_layers, n_layers) run the paged
+    // instantiations, and a call that reaches them runs them throughout)
+    const int split = c.n_layers - c.tail_layers, R = h->n_paged ? c.resident_layers : c.n_layers;
+    const bool res2 = split > 0 && (R > 0 || !h->n_paged), pg2 = h->n_paged && R < split;
     for (int T = 1; T <= c.max_tokens && rc == QS_OK; ++T) {
       bool small = false;
       PersistShape p;
-      if (c.tail_layers < c.n_layers && !choose_kernel(h, T, small, p)) {
+      if ((res2 && !choose_kernel(h, T, small, p)) || (pg2 && !choose_kernel(h, T, small, p, true))) {
         fprintf(stderr, "qs_moe: no persistent decode kernel fits a %d-token call of this shape\n", T);
         rc = QS_E_UNSUPPORTED;
       }
     }
-    if (rc == QS_OK && c.tail_layers > 0 && !h->q4k_ok) {
+    if (rc == QS_OK && c.tail_layers > 0 && (!h->q4k_ok || (h->n_paged && !h->pg_q4k_ok[0]))) {
       fprintf(stderr, "qs_moe: the batched decode kernel of the Q4_K-style layers does not fit this shape\n");
       rc = QS_E_UNSUPPORTED;
     }
@@ -1017,10 +1373,19 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
   struct Job { const void* src; uint8_t* dst; size_t nblk; size_t stride; int fmt; };
   const int gfmt = q4 ? kFmtQ4K : c.gate_up_format, dfmt = q4 ? kFmtQ4K : kFmtQ2K;
   const size_t gst = q4 ? h->gu_stride4 : h->gu_stride, dst_ = q4 ? h->dn_stride4 : h->dn_stride;
+  const bool paged = L.host != nullptr;
+  if (paged && !h->pstage) {   // a paged layer's records are re-laid in HBM, then copied to host
+    if (hipMalloc(&h->pstage, E * h->slot_bytes) != hipSuccess) {
+      h->pstage = nullptr;
+      return QS_E_NOMEM;
+    }
+  }
+  // a paged layer: expert e's record [gate | up | down] at e * rec_bytes
+  const size_t rs = L.rec_bytes;
   const Job jobs[3] = {
-      {w->gate, L.gate, gu_blk, gst, gfmt},
-      {w->up, L.up, gu_blk, gst, gfmt},
-      {w->down, L.down, dn_blk, dst_, dfmt},
+      {w->gate, paged ? h->pstage : L.gate, gu_blk, paged ? rs : gst, gfmt},
+      {w->up, paged ? h->pstage + gst : L.up, gu_blk, paged ? rs : gst, gfmt},
+      {w->down, paged ? h->pstage + 2 * gst : L.down, dn_blk, paged ? rs : dst_, dfmt},
   };
   for (const Job& j : jobs) {
     const size_t raw = j.fmt == kFmtCB2 ? kCB2Bytes : j.fmt == kFmtQ4K ? kQ4KBytes : kQ2KBytes;
@@ -1050,6 +1415,12 @@ QS_API int qs_moe_upload(qs_moe* h, int layer, const qs_moe_layer_weights* w, vo
       QS_HIP(hipGetLastError());
     }
   }
+  if (paged) {
+    QS_HIP(hipMemcpyAsync(L.host, h->pstage, E * rs, hipMemcpyDeviceToHost, st));
+    cache_drop_layer(h, layer - c.resident_layers);
+    const int rc = cache_flush(h, st);
+    if (rc) return rc;
+  }
   QS_HIP(hipStreamSynchronize(st));
   L.uploaded = true;
   return QS_OK;
@@ -1062,9 +1433,17 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
   DeviceGuard dg(h->device);
   if (!dg.ok) return QS_E_HIP;
   const CallState cs{&h->s, h->sync, &h->epoch, &h->ll_epoch, h->s.base, h->s.ll_bytes};
-  return launch_persistent(h, cs, layer0, n_layers, x, y, n_tokens, (flags & QS_DECODE_RESIDUAL) != 0,
-                           (flags & QS_DECODE_RMSNORM) != 0, (flags & QS_DECODE_STEER) != 0, ids_out, w_out,
-                           (hipStream_t)hip_stream);
+  hipStream_t st = (hipStream_t)hip_stream;
+  const bool paged = h->n_paged && layer0 + n_layers > h->cfg.resident_layers;
+  if (paged) {   // admissions of earlier calls that have completed
+    rc = cache_poll(h, st, false);
+    if (rc) return rc;
+  }
+  int32_t* ids = paged && !ids_out ? h->ids_buf : ids_out;
+  rc = launch_persistent(h, cs, layer0, n_layers, x, y, n_tokens, (flags & QS_DECODE_RESIDUAL) != 0,
+                         (flags & QS_DECODE_RMSNORM) != 0, (flags & QS_DECODE_STEER) != 0, ids, w_out, st);
+  if (rc || !paged) return rc;
+  return cache_record(h, ids, layer0, n_layers, n_tokens, st);
 }
 
 QS_API int qs_moe_decode_static(qs_moe* h, int layer0, int n_layers, const float* x, float* y,
@@ -1224,12 +1603,18 @@ QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* ou
   const uint8_t* mat;
   size_t nblk;
   int fmt;
+  const size_t gs = L.q4k ? h->gu_stride4 : h->gu_stride;
+  if (L.host) {   // a paged layer: the expert's host record, read over PCIe
+    mat = (const uint8_t*)(uintptr_t)(L.host_dev + (uint64_t)expert * L.rec_bytes) + (size_t)which * gs;
+  } else {
+    mat = which == 0 ? L.gate + (size_t)expert * gs
+                     : which == 1 ? L.up + (size_t)expert * gs
+                                  : L.down + (size_t)expert * (L.q4k ? h->dn_stride4 : h->dn_stride);
+  }
   if (which < 2) {
-    mat = (which == 0 ? L.gate : L.up) + (size_t)expert * (L.q4k ? h->gu_stride4 : h->gu_stride);
     nblk = F * (H / kBlockW);
     fmt = L.q4k ? kFmtQ4K : c.gate_up_format;
   } else {
-    mat = L.down + (size_t)expert * (L.q4k ? h->dn_stride4 : h->dn_stride);
     nblk = H * (F / kBlockW);
     fmt = L.q4k ? kFmtQ4K : kFmtQ2K;
   }
@@ -1241,6 +1626,71 @@ QS_API int qs_moe_dequant(qs_moe* h, int layer, int expert, int which, float* ou
   else
     hipLaunchKernelGGL(k_dequant_q2k, grid, dim3(256), 0, st, mat, nblk, out);
   QS_HIP(hipGetLastError());
+  return QS_OK;
+}
+
+QS_API int qs_moe_cache_sync(qs_moe* h, void* hip_stream) {
+  if (!h) return QS_E_INVAL;
+  if (!h->n_paged) return QS_E_STATE;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
+  hipStream_t st = (hipStream_t)hip_stream;
+  QS_HIP(hipStreamSynchronize(st));
+  const int rc = cache_poll(h, st, true);
+  if (rc) return rc;
+  QS_HIP(hipStreamSynchronize(st));
+  return QS_OK;
+}
+
+QS_API int qs_moe_cache_preload(qs_moe* h, const int32_t* keys, int n, void* hip_stream) {
+  if (!h || n < 0 || (n && !keys)) return QS_E_INVAL;
+  if (!h->n_paged) return QS_E_STATE;
+  const qs_moe_config& c = h->cfg;
+  for (int i = 0; i < n; ++i)
+    if (keys[2 * i] < c.resident_layers || keys[2 * i] >= c.n_layers || keys[2 * i + 1] < 0 ||
+        keys[2 * i + 1] >= c.n_experts)
+      return QS_E_INVAL;
+  int rc = qs_moe_cache_sync(h, hip_stream);
+  if (rc) return rc;
+  DeviceGuard dg(h->device);
+  if (!dg.ok) return QS_E_HIP;
+  // hottest first into the free slots; each later (colder) one goes to the
+  // least-recent end, so the coldest preloaded expert is evicted first
+  for (int i = 0; i < n && !h->free_slots.empty(); ++i) {
+    const int key = (keys[2 * i] - c.resident_layers) * c.n_experts + keys[2 * i + 1];
+    if (h->slot_of[key] >= 0) continue;
+    const int v = *h->free_slots.begin();
+    h->free_slots.erase(h->free_slots.begin());
+    slot_take(h, v, key);
+    lru_push_front(h, v);
+    ++h->c_preloaded;
+  }
+  hipStream_t st = (hipStream_t)hip_stream;
+  rc = cache_flush(h, st);
+  if (rc) return rc;
+  QS_HIP(hipStreamSynchronize(st));
+  return QS_OK;
+}
+
+QS_API int qs_moe_cache_stats(qs_moe* h, uint64_t* out) {
+  if (!h || !out) return QS_E_INVAL;
+  if (!h->n_paged) return QS_E_STATE;
+  const uint64_t S = (uint64_t)h->cfg.cache_slots;
+  const uint64_t v[8] = {h->c_hits, h->c_misses, h->c_admits, h->c_evicts, h->c_preloaded,
+                         S - (uint64_t)h->free_slots.size(), S, h->host_bytes};
+  memcpy(out, v, sizeof(v));
+  return QS_OK;
+}
+
+QS_API int qs_moe_cache_slots(qs_moe* h, int32_t* out) {
+  if (!h || !out) return QS_E_INVAL;
+  if (!h->n_paged) return QS_E_STATE;
+  const int E = h->cfg.n_experts;
+  for (int v = 0; v < h->cfg.cache_slots; ++v) {
+    const int key = h->owner[v];
+    out[2 * v] = key < 0 ? -1 : h->cfg.resident_layers + key / E;
+    out[2 * v + 1] = key < 0 ? -1 : key % E;
+  }
   return QS_OK;
 }
 

@@ -70,10 +70,32 @@ struct LayerPtrs {
   const uint8_t* sg;          // shared expert rows (bf16, or the 8-bit rows below)
   const uint8_t* su;
   const uint8_t* sd;
+  const uint64_t* emap;       // paged layer: [E] address of each expert's record, else null
 };
+
+// Expert e's gate (which 0), up (1) or down (2) matrix.  A resident layer
+// holds each kind as one array of E matrices.  A paged layer holds one
+// record per expert, [gate | up | down] at offsets 0, gu_stride and
+// 2 gu_stride, at the address its expert map gives: an HBM cache slot, or
+// the expert's copy in pinned host memory, which the loads then read over
+// PCIe.  The map does not change during a launch.
+// Only the kernels built for paged layers (kPaged) read the map; the
+// others keep the resident addressing alone.
+template <class A>
+__device__ __forceinline__ const uint8_t* ex_mat(const A& a, const LayerPtrs& Lp, int which, int e) {
+  if constexpr (A::kPaged) {
+    if (Lp.emap) {
+      const uint8_t* rec = (const uint8_t*)(uintptr_t)Lp.emap[e];
+      return rec + (size_t)which * a.gu_stride;
+    }
+  }
+  return which == 0 ? Lp.gate + (size_t)e * a.gu_stride
+                    : which == 1 ? Lp.up + (size_t)e * a.gu_stride : Lp.down + (size_t)e * a.dn_stride;
+}
 
 struct PersistArgs {
   static constexpr bool kFixedShape = false;
+  static constexpr bool kPaged = false;
   const LayerPtrs* layers;   // device array, first entry = layer0
   int G;                     // workgroups of the launch (a multiple of 8)
   int n_layers, T, H, E, k, F, Fs;
@@ -665,7 +687,7 @@ __device__ __forceinline__ void copy_tile(const A& a, const LayerPtrs& Lp, QS_LD
   const TileLds tl = tile_lds(a);
   const size_t b0 = (size_t)f0 * nbh;
   for (int m = 0; m < 2; ++m) {
-    const uint8_t* src = (m ? Lp.up : Lp.gate) + (size_t)e * a.gu_stride;
+    const uint8_t* src = ex_mat(a, Lp, m, e);
     dma_to_lds<0>(src + pl.q + b0 * g.q, dst + m * tl.qb, tl.qb, w, nw);
     dma_to_lds<0>(src + pl.s + b0 * g.s, dst + tl.s + m * tl.sb, tl.sb, w, nw);
     dma_to_lds<0>(src + pl.d + b0 * g.d, dst + tl.d + m * tl.db, tl.db, w, nw);
@@ -679,7 +701,7 @@ __device__ __forceinline__ void copy_down_rows(const A& a, const LayerPtrs& Lp, 
                                                int e, int r0, int w, int nw) {
   const uint32_t nb = a.F / kBlockW;
   const MatPlanes pl = q2k_planes((size_t)a.H * nb);
-  const uint8_t* base = Lp.down + (size_t)e * a.dn_stride;
+  const uint8_t* base = ex_mat(a, Lp, 2, e);
   const size_t b0 = (size_t)r0 * nb;
   dma_to_lds<0>(base + pl.q + b0 * 64, dst, kDownRows * nb * 64, w, nw);
   dma_to_lds<0>(base + pl.s + b0 * 16, dst + kDownRows * nb * 64, kDownRows * nb * 16, w, nw);
@@ -1830,8 +1852,8 @@ __device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, co
   const uint32_t nbh = a.H / kBlockW;
   const size_t nblk = (size_t)a.F * nbh;
   const MatPlanes pl = FMT == 1 ? q2k_planes(nblk) : cb2_planes(nblk);
-  const uint8_t* g = Lp.gate + (size_t)e * a.gu_stride;
-  const uint8_t* up = Lp.up + (size_t)e * a.gu_stride;
+  const uint8_t* g = ex_mat(a, Lp, 0, e);
+  const uint8_t* up = ex_mat(a, Lp, 1, e);
 #pragma unroll
   for (int i = 0; i < kGuUnits; ++i) {
     const int r = slot + (i / cpl) * slots, ch = j + (i % cpl) * lpr;
@@ -2357,6 +2379,16 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
 template <int FMT, bool STEER>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_small(PersistArgs a) {
   persist_small_body<FMT, STEER>(a);
+}
+
+// Launches over paged layers (experts read through the layer's expert map).
+struct PagedArgs : PersistArgs {
+  static constexpr bool kPaged = true;
+};
+
+template <int FMT, bool STEER>
+__global__ void __launch_bounds__(kPersistThreads) k_persist_small_paged(PersistArgs a) {
+  persist_small_body<FMT, STEER>(static_cast<const PagedArgs&>(a));
 }
 
 // One layer shape fixed at compile time.  The launch passes the same values

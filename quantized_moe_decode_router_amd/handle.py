@@ -12,10 +12,14 @@ class MoE:
 
     def __init__(self, hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format,
                  down_format, n_layers, max_tokens, codebook=None, mfma_min_tokens=0, device=-1,
-                 shared_format="bf16", tail_layers=0):
+                 shared_format="bf16", tail_layers=0, resident_layers=None, cache_slots=0):
+        """resident_layers: None = every layer resident; else expert paging
+        with that many leading resident layers and `cache_slots` HBM slots."""
+        paging = resident_layers is not None
         self.cfg = L.make_config(hidden, n_experts, top_k, expert_ffn, shared_ffn, gate_up_format,
                                  down_format, n_layers, max_tokens, mfma_min_tokens, device,
-                                 shared_format, tail_layers)
+                                 shared_format, tail_layers, int(paging),
+                                 resident_layers if paging else 0, cache_slots if paging else 0)
         cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
         self._cb = cb
         self.h = L.qs_moe_create(self.cfg, cb)
@@ -126,6 +130,29 @@ class MoE:
         out = torch.empty(shape, dtype=torch.float32, device="cuda")
         L.qs_moe_dequant(self.h, layer, expert, which, out, stream)
         return out
+
+    # -- expert cache (expert paging) ---------------------------------------
+    def cache_sync(self, stream=None):
+        L.qs_moe_cache_sync(self.h, stream)
+
+    def cache_preload(self, keys, stream=None):
+        """keys: (layer, expert) pairs, hottest first."""
+        k = np.ascontiguousarray(np.asarray(keys, dtype=np.int32).reshape(-1, 2))
+        L.qs_moe_cache_preload(self.h, k, stream)
+
+    CACHE_STATS = ("hits", "misses", "admissions", "evictions", "preloaded", "slots_used", "slots",
+                   "host_bytes")
+
+    def cache_stats(self):
+        out = np.zeros(8, dtype=np.uint64)
+        L.qs_moe_cache_stats(self.h, out)
+        return {n: int(v) for n, v in zip(self.CACHE_STATS, out)}
+
+    def cache_slots(self):
+        """(layer, expert) per slot, (-1, -1) when free: numpy int32 [slots][2]."""
+        out = np.zeros((max(self.cfg.cache_slots, 1), 2), dtype=np.int32)
+        L.qs_moe_cache_slots(self.h, out)
+        return out[:self.cfg.cache_slots]
 
     def memory_bytes(self):
         return L.qs_moe_memory_bytes(self.h)

@@ -7,5 +7,5 @@ oracle consume what it produces.
 """
 from .gen import (  # noqa: F401
     WORKLOADS, Workload, codebook, q2k_blocks, cb2_blocks, q4k_blocks, block_bytes,
-    expert_tensor, layer_weights, tokens, fp32_to_bf16_bits,
+    expert_tensor, layer_weights, tokens, fp32_to_bf16_bits, hotlist,
 )

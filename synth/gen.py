@@ -296,6 +296,22 @@ def layer_weights(wl: Workload, layer: int, experts=None) -> LayerWeights:
     return lw
 
 
+def hotlist(wl: Workload, layers) -> np.ndarray:
+    """(layer, expert) pairs of the given layers, most popular first: the
+    rank of the Zipf popularity bias (every layer's rank 0, then every
+    layer's rank 1, ...); expert order without one.  int32 [n][2]."""
+    layers = list(layers)
+    order = []
+    for l in layers:
+        if wl.zipf_s is not None:
+            rank = _rng(wl.seed_id, l, T_BIAS, 0).permutation(wl.n_experts)
+            order.append(np.argsort(rank, kind="stable"))
+        else:
+            order.append(np.arange(wl.n_experts))
+    out = [(l, int(order[i][r])) for r in range(wl.n_experts) for i, l in enumerate(layers)]
+    return np.array(out, dtype=np.int32).reshape(-1, 2)
+
+
 def tokens(wl: Workload, n_tokens: int, batch: int = 0) -> np.ndarray:
     """Token activations fp32 [T][H] ~ N(0, 1) for input batch ``batch``."""
     return _rng(wl.seed_id, 0xFFFF, T_X, n_tokens, batch).standard_normal(

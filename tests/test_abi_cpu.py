@@ -75,6 +75,7 @@ def _good():
     ("n_layers", 0), ("max_tokens", 0), ("max_tokens", 257), ("mfma_min_tokens", -1),
     ("shared_format", 1), ("shared_format", 2), ("shared_format", 4), ("shared_format", -1),
     ("tail_layers", -1), ("tail_layers", 2),
+    ("expert_paging", 2), ("expert_paging", -1), ("resident_layers", 1), ("cache_slots", 3),
 ])
 def test_create_rejects_invalid_config_without_gpu(field, value):
     kw = _good()
@@ -83,6 +84,18 @@ def test_create_rejects_invalid_config_without_gpu(field, value):
     h = ctypes.c_void_p(123)
     rc = qm.LIB.qs_moe_create(ctypes.byref(cfg), None, ctypes.byref(h))
     assert rc == qm.QS_E_INVAL
+    assert h.value is None
+
+
+@pytest.mark.parametrize("resident,slots", [(-1, 0), (3, 0), (0, -1), (0, 33), (1, 17), (2, 1)])
+def test_create_rejects_invalid_paging_without_gpu(resident, slots):
+    """With paging on: 0 <= resident_layers <= n_layers, and at most one
+    slot per paged expert (2 layers of 16 experts here)."""
+    kw = _good()
+    kw.update(n_layers=2, expert_paging=1, resident_layers=resident, cache_slots=slots)
+    cfg = qm.make_config(**kw)
+    h = ctypes.c_void_p(123)
+    assert qm.LIB.qs_moe_create(ctypes.byref(cfg), None, ctypes.byref(h)) == qm.QS_E_INVAL
     assert h.value is None
 
 
@@ -126,3 +139,7 @@ def test_null_arguments():
     assert qm.LIB.qs_moe_memory_bytes(None, None) == qm.QS_E_INVAL
     assert qm.LIB.qs_moe_sync_status(None, None) == qm.QS_E_INVAL
     assert qm.LIB.qs_moe_set_wait_limit(None, 0) == qm.QS_E_INVAL
+    assert qm.LIB.qs_moe_cache_sync(None, None) == qm.QS_E_INVAL
+    assert qm.LIB.qs_moe_cache_preload(None, None, 0, None) == qm.QS_E_INVAL
+    assert qm.LIB.qs_moe_cache_stats(None, None) == qm.QS_E_INVAL
+    assert qm.LIB.qs_moe_cache_slots(None, None) == qm.QS_E_INVAL
