@@ -59,10 +59,15 @@ def parse():
 # The other workloads the bench line reports beside the headline one: the
 # routed-only 40-layer stack, the stack with an 8-bit shared expert, the
 # headline stack with every layer's output steered, and the 8-layer
-# large-layer stack, at their batch sizes, with fewer timed steps.
+# large-layer stack, at their batch sizes, with fewer timed steps; and the
+# headline stack with expert paging: 4 resident layers, the routed experts of
+# the other 36 in host memory behind a cache of a quarter of them, warmed
+# with the popularity hotlist.
 STEERED = "+steer"
+PAGED = "+paged"
+PAGING = {"resident_layers": 4, "cache_fraction": 0.25}
 EXTRA = (("a3b_routed40", (1, 4)), ("a3b_stack40_zipf_q8", (1, 4)), ("a3b_stack40_zipf" + STEERED, (1, 4, 16)),
-         ("a3b_stack40_q4tail", (1, 4, 16)), ("flash_stack8_zipf", (1, 8, 32)))
+         ("a3b_stack40_q4tail", (1, 4, 16)), ("flash_stack8_zipf", (1, 8, 32)), ("a3b_stack40_zipf" + PAGED, (1, 4)))
 STEER_SCALE = 0.8
 EXTRA_STEPS = 100
 
@@ -135,21 +140,29 @@ def synth_plain(wl):
     return dataclasses.replace(wl, tail_layers=0)
 
 
-def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False):
+def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False, paging=None):
     """Time `steps` decode calls through all L layers at each batch size
-    (with steer: every layer's output steered along a seeded unit direction);
-    returns {T: figures}."""
+    (with steer: every layer's output steered along a seeded unit direction;
+    with paging: expert paging as PAGING describes); returns {T: figures}."""
     import torch
     import synth
     cb = synth.codebook()
-    log(f"[bench] workload {wl.name}{STEERED if steer else ''}: {L} layers, H={wl.hidden} E={wl.n_experts} k={wl.top_k} "
+    tag = (STEERED if steer else "") + (PAGED if paging else "")
+    log(f"[bench] workload {wl.name}{tag}: {L} layers, H={wl.hidden} E={wl.n_experts} k={wl.top_k} "
         f"F={wl.expert_ffn} Fs={wl.shared_ffn}, tokens {list(tok_list)}")
     t0 = time.time()
-    moe = qm.MoE.for_workload(wl, cb, n_layers=L, max_tokens=max(tok_list))
+    kw = {}
+    if paging:
+        R = paging["resident_layers"]
+        kw = dict(resident_layers=R, cache_slots=int(paging["cache_fraction"] * (L - R) * wl.n_experts))
+    moe = qm.MoE.for_workload(wl, cb, n_layers=L, max_tokens=max(tok_list), **kw)
     for l in range(L):
         moe.upload(l, synth.layer_weights(wl, l))
         if l % 10 == 9 or l == L - 1:
             log(f"[bench] uploaded {l + 1}/{L} layers ({time.time() - t0:.1f}s)")
+    if paging:
+        moe.cache_preload(synth.hotlist(wl, range(kw["resident_layers"], L)))
+        log(f"[bench] paging: {kw}, preloaded {moe.cache_stats()['preloaded']} experts")
     if steer:
         dirs = np.random.default_rng(12).standard_normal((L, wl.hidden))
         moe.set_steering((dirs / np.linalg.norm(dirs, axis=1, keepdims=True)).astype(np.float32), STEER_SCALE)
@@ -178,6 +191,9 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False):
         for i in range(warmup):
             step(xs[i % N_BATCHES], y)
         torch.cuda.synchronize()
+        if paging:
+            moe.cache_sync(stream)
+            c0 = moe.cache_stats()
         # whole timed region: K steps back to back
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
@@ -187,6 +203,19 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False):
         end.record(stream)
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / steps
+        cache = None
+        if paging:   # the cache over the timed steps (their uses applied after the region)
+            moe.cache_sync(stream)
+            c1 = moe.cache_stats()
+            d = {n: c1[n] - c0[n] for n in ("hits", "misses", "admissions", "evictions")}
+            exp_b = float(np.mean(per_expert[kw["resident_layers"]:]))
+            cache = dict(kw, **d, hit_rate=d["hits"] / max(1, d["hits"] + d["misses"]),
+                         expert_bytes=exp_b, host_bytes=c1["host_bytes"],
+                         pcie_bytes_per_step=(d["misses"] + d["admissions"]) * exp_b / steps,
+                         pcie_GBps=(d["misses"] + d["admissions"]) * exp_b / (ms * 1e-3 * steps) / 1e9)
+            log(f"[bench] cache over the timed steps: hit rate {cache['hit_rate']:.3f}, "
+                f"{d['misses'] / steps:.1f} misses and {d['admissions'] / steps:.1f} admissions per step, "
+                f"PCIe {cache['pcie_GBps']:.1f} GB/s")
         # per launch: an event pair around each decode call (one kernel
         # launch), same stream, same inputs
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -207,10 +236,14 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False):
             "mean_distinct_experts_per_layer": float(uniq.mean()),
             "launch_ms_mean": float(launch_ms.mean()), "launch_ms_p10": float(np.percentile(launch_ms, 10)),
             "launch_ms_p90": float(np.percentile(launch_ms, 90)),
-            "roofline": {"bound": "hbm", "kernel": kernel_name(wl, T), "achieved": achieved,
+            "roofline": {"bound": "hbm", "achieved": achieved,
+                         "kernel": kernel_name(wl, T).replace("k_persist_small", "k_persist_small_paged").replace(
+                             "k_persist_big", "k_persist_big_paged") if paging else kernel_name(wl, T),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS},
         }
-        log(f"[bench] {wl.name}{STEERED if steer else ''} T={T}: {ms:.3f} ms/step, {T / (ms * 1e-3):.1f} tok/s, {gbs:.1f} GB/s "
+        if cache:
+            results[T]["cache"] = cache
+        log(f"[bench] {wl.name}{tag} T={T}: {ms:.3f} ms/step, {T / (ms * 1e-3):.1f} tok/s, {gbs:.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), U={uniq.mean():.1f}, "
             f"launch {launch_ms.mean():.3f} ms (p10 {np.percentile(launch_ms, 10):.3f}, "
             f"p90 {np.percentile(launch_ms, 90):.3f})")
@@ -243,9 +276,10 @@ def main():
         for name, toks in EXTRA:
             if name == wl.name:
                 continue
-            steer = name.endswith(STEERED)
-            w2 = synth.WORKLOADS[name[:-len(STEERED)] if steer else name]
-            r = run_workload(qm, w2, w2.n_layers, toks, min(args.steps, EXTRA_STEPS), args.warmup, steer=steer)
+            steer, paged = name.endswith(STEERED), name.endswith(PAGED)
+            w2 = synth.WORKLOADS[name.split("+")[0]]
+            r = run_workload(qm, w2, w2.n_layers, toks, min(args.steps, EXTRA_STEPS), args.warmup, steer=steer,
+                             paging=PAGING if paged else None)
             others[name] = {"layers": w2.n_layers, "per_batch": {str(T): v for T, v in r.items()}}
 
     T0 = tok_list[0]

@@ -1537,16 +1537,18 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist_big_paged(PersistAr
 
 // The layer shape fixed at compile time, the batch size at run time (as
 // FixedArgs for the small-batch kernel).
-template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int G_>
+template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int G_, bool PG = false>
 struct FixedBigArgs : PersistArgs {
   static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, sq8 = SQ8_, G = G_;
   static constexpr int gq2k = FMT == 1, r_et = 1;
   static constexpr int gfmt = FMT, dfmt = FMT == kFmtQ4K ? kFmtQ4K : kFmtQ2K;
+  static constexpr bool kPaged = PG;
 };
 
-template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int G, bool STEER = false>
+// PG: for launches over paged layers
+template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int G, bool STEER = false, bool PG = false>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_big_fixed(PersistArgs a) {
-  persist_big_body<FMT, STEER>(static_cast<const FixedBigArgs<FMT, H, E, K, F, FS, SQ8, G>&>(a));
+  persist_big_body<FMT, STEER>(static_cast<const FixedBigArgs<FMT, H, E, K, F, FS, SQ8, G, PG>&>(a));
 }
 
 }  // namespace qs

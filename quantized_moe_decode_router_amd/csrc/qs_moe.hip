@@ -146,6 +146,8 @@ struct qs_moe {
   bool pg_small_ok[2] = {false, false};   // the instantiations for paged layers, [steer]
   bool pg_big_ok[2] = {false, false};
   bool pg_q4k_ok[2] = {false, false};
+  bool pg_fixed_ok = false;       // the fixed-shape instantiations for paged layers
+  bool pg_big_fixed_ok = false;
   uint32_t ll_epoch = 0;          // flags used by the small-batch kernel so far
   float* steer_dirs = nullptr;    // steering directions, device fp32 [n_layers][H] (null: none set)
   float steer_scale = 0.f;
@@ -648,7 +650,7 @@ int gu_units(int H) {
   return (slots >= kGateTile ? 1 : kGateTile / slots) * (nch / lpr);
 }
 
-const void* persist_fixed_fn(const qs_moe* h, int T, bool steer = false);
+const void* persist_fixed_fn(const qs_moe* h, int T, bool steer = false, bool paged = false);
 
 // paged: for the instantiations of paged layers, which have no fixed shape
 PersistShape persist_shape(const qs_moe* h, int T, bool small, bool paged = false) {
@@ -734,13 +736,13 @@ const void* persist_paged_fn(int fmt, bool small, bool steer) {
 // hidden 2048, 256 experts, top-8, expert width 512, shared width 512
 // (bf16 or 8-bit) or 0, codebook gate/up, one workgroup per CU of a 256-CU
 // device; with the steered combine (STEER) for the bf16 shared expert.
-template <int FS, int SQ8, bool STEER = false>
+template <int FS, int SQ8, bool STEER = false, bool PG = false>
 const void* fixed_a3b(int T) {
   switch (T) {
-    case 1: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 1, 256, STEER>;
-    case 2: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 2, 256, STEER>;
-    case 3: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 3, 256, STEER>;
-    case 4: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 4, 256, STEER>;
+    case 1: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 1, 256, STEER, PG>;
+    case 2: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 2, 256, STEER, PG>;
+    case 3: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 3, 256, STEER, PG>;
+    case 4: return (const void*)k_persist_small_fixed<2, 2048, 256, 8, 512, FS, SQ8, 4, 256, STEER, PG>;
     default: return nullptr;
   }
 }
@@ -748,10 +750,14 @@ const void* fixed_a3b(int T) {
 // Batched instantiations with the layer shape fixed (the batch size stays a
 // run-time value): the shapes above, and hidden 4096, 256 experts, top-6,
 // expert and shared width 2048.
-const void* persist_big_fixed_fn(const qs_moe* h, bool steer = false) {
+const void* persist_big_fixed_fn(const qs_moe* h, bool steer = false, bool paged = false) {
   const qs_moe_config& c = h->cfg;
   if (h->grid != 256 || c.gate_up_format != QS_FMT_CB2 || c.n_experts != 256) return nullptr;
   const bool sq8 = c.shared_format == QS_FMT_Q8;
+  if (paged)   // paged layers: the A3B shape with the bf16 shared expert, unsteered
+    return !steer && c.hidden == 2048 && c.top_k == 8 && c.expert_ffn == 512 && c.shared_ffn == 512 && !sq8
+               ? (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 0, 256, false, true>
+               : nullptr;
   if (steer) {
     if (c.hidden == 2048 && c.top_k == 8 && c.expert_ffn == 512 && c.shared_ffn == 512 && !sq8)
       return (const void*)k_persist_big_fixed<2, 2048, 256, 8, 512, 512, 0, 256, true>;
@@ -771,8 +777,14 @@ const void* persist_big_fixed_fn(const qs_moe* h, bool steer = false) {
 // the A3B shapes above at T = 1..4, and the large-layer shape (hidden 4096,
 // 256 experts, top-6, expert and shared width 2048, bf16 shared expert) at
 // T = 1.
-const void* persist_fixed_fn(const qs_moe* h, int T, bool steer) {
+const void* persist_fixed_fn(const qs_moe* h, int T, bool steer, bool paged) {
   const qs_moe_config& c = h->cfg;
+  if (paged)   // paged layers: the A3B shape with the bf16 shared expert, unsteered
+    return !steer && h->grid_small == 256 && c.gate_up_format == QS_FMT_CB2 && c.hidden == 2048 &&
+                   c.n_experts == 256 && c.top_k == 8 && c.expert_ffn == 512 && c.shared_ffn == 512 &&
+                   c.shared_format == QS_FMT_BF16
+               ? fixed_a3b<512, 0, false, true>(T)
+               : nullptr;
   if (!steer && T == 1 && h->grid_small == 256 && c.gate_up_format == QS_FMT_CB2 && c.hidden == 4096 &&
       c.n_experts == 256 && c.top_k == 6 && c.expert_ffn == 2048 && c.shared_ffn == 2048 &&
       c.shared_format == QS_FMT_BF16)
@@ -936,6 +948,15 @@ int setup_persistent(qs_moe* h) {
     const void* fs = persist_big_fixed_fn(h, true);
     h->big_fixed_steer_ok = fs && resident(fs, lds_big);
   }
+  if (h->n_paged) {
+    const void* fb = persist_big_fixed_fn(h, false, true);
+    h->pg_big_fixed_ok = h->pg_big_ok[0] && fb && resident(fb, lds_big);
+    h->pg_fixed_ok = h->pg_small_ok[0];
+    for (int T = 1; T <= kSmallT && h->pg_fixed_ok; ++T) {
+      const void* fn = persist_fixed_fn(h, T, false, true);
+      h->pg_fixed_ok = fn && resident(fn, lds_small);
+    }
+  }
   h->fixed_ok = h->persist_small_ok;
   h->fixed_steer_ok = h->persist_small_ok;
   for (int T = 1; T <= kSmallT; ++T) {
@@ -1042,7 +1063,10 @@ int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const flo
   // workgroup, all tokens at once)
   const void* fn = nullptr;
   if (paged) {
-    fn = persist_paged_fn(q4k ? kFmtQ4K : cb2 ? kFmtCB2 : kFmtQ2K, small, steer);
+    if (!q4k && !steer && small && h->pg_fixed_ok && p.r_et == 1 && p.r_tt == T)
+      fn = persist_fixed_fn(h, T, false, true);
+    if (!q4k && !steer && !small && h->pg_big_fixed_ok && p.r_et == 1) fn = persist_big_fixed_fn(h, false, true);
+    if (!fn) fn = persist_paged_fn(q4k ? kFmtQ4K : cb2 ? kFmtCB2 : kFmtQ2K, small, steer);
   } else if (q4k) {
     fn = persist_q4k_fn(steer);
   } else {

@@ -2394,17 +2394,19 @@ __global__ void __launch_bounds__(kPersistThreads) k_persist_small_paged(Persist
 // One layer shape fixed at compile time.  The launch passes the same values
 // in the runtime fields (the host checks); the static members shadow them,
 // so every loop bound, offset and division by a shape folds to a constant.
-template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int T_, int G_>
+template <int FMT, int H_, int E_, int K_, int F_, int FS_, int SQ8_, int T_, int G_, bool PG = false>
 struct FixedArgs : PersistArgs {
   static constexpr int H = H_, E = E_, k = K_, F = F_, Fs = FS_, sq8 = SQ8_, T = T_, G = G_;
   static constexpr int gq2k = FMT == 1, r_et = 1, r_tt = T_;
   static constexpr int gfmt = FMT, dfmt = FMT == kFmtQ4K ? kFmtQ4K : kFmtQ2K;
   static constexpr bool kFixedShape = true;
+  static constexpr bool kPaged = PG;
 };
 
-template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int T, int G, bool STEER = false>
+// PG: for launches over paged layers
+template <int FMT, int H, int E, int K, int F, int FS, int SQ8, int T, int G, bool STEER = false, bool PG = false>
 __global__ void __launch_bounds__(kPersistThreads) k_persist_small_fixed(PersistArgs a) {
-  persist_small_body<FMT, STEER>(static_cast<const FixedArgs<FMT, H, E, K, F, FS, SQ8, T, G>&>(a));
+  persist_small_body<FMT, STEER>(static_cast<const FixedArgs<FMT, H, E, K, F, FS, SQ8, T, G, PG>&>(a));
 }
 
 }  // namespace qs
