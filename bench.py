@@ -173,8 +173,12 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False, paging=None):
     # recorded on that same stream
     stream = torch.cuda.current_stream()
 
-    def step(x, y, ids=None):
-        moe.decode(x, y, n_layers=L, residual=True, prenorm=True, ids_out=ids, stream=stream, steer=steer)
+    # the bench runs nothing else on the device: exclusive launches (the same
+    # kernel dispatched without the cooperative launch's serialisation); the
+    # cooperative launch is timed as well
+    def step(x, y, ids=None, exclusive=True):
+        moe.decode(x, y, n_layers=L, residual=True, prenorm=True, ids_out=ids, stream=stream, steer=steer,
+                   exclusive=exclusive)
 
     results = {}
     for T in tok_list:
@@ -216,6 +220,13 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False, paging=None):
             log(f"[bench] cache over the timed steps: hit rate {cache['hit_rate']:.3f}, "
                 f"{d['misses'] / steps:.1f} misses and {d['admissions'] / steps:.1f} admissions per step, "
                 f"PCIe {cache['pcie_GBps']:.1f} GB/s")
+        # the same steps with cooperative launches
+        start.record(stream)
+        for i in range(steps):
+            step(xs[i % N_BATCHES], y, exclusive=False)
+        end.record(stream)
+        torch.cuda.synchronize()
+        coop_ms = start.elapsed_time(end) / steps
         # per launch: an event pair around each decode call (one kernel
         # launch), same stream, same inputs
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -232,6 +243,7 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False, paging=None):
         achieved = step_bytes / (launch_ms.mean() * 1e-3) / 1e9
         results[T] = {
             "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms, "bytes_per_step": step_bytes,
+            "cooperative_ms_per_step": coop_ms, "cooperative_tokens_per_s": T / (coop_ms * 1e-3),
             "weight_read_GBps": gbs, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
             "mean_distinct_experts_per_layer": float(uniq.mean()),
             "launch_ms_mean": float(launch_ms.mean()), "launch_ms_p10": float(np.percentile(launch_ms, 10)),
@@ -246,7 +258,7 @@ def run_workload(qm, wl, L, tok_list, steps, warmup, steer=False, paging=None):
         log(f"[bench] {wl.name}{tag} T={T}: {ms:.3f} ms/step, {T / (ms * 1e-3):.1f} tok/s, {gbs:.1f} GB/s "
             f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), U={uniq.mean():.1f}, "
             f"launch {launch_ms.mean():.3f} ms (p10 {np.percentile(launch_ms, 10):.3f}, "
-            f"p90 {np.percentile(launch_ms, 90):.3f})")
+            f"p90 {np.percentile(launch_ms, 90):.3f}); cooperative launches {coop_ms:.3f} ms/step")
         del xs, ids
     moe.close()
     return results
@@ -306,6 +318,8 @@ def main():
         "arith": "2-bit weights decoded to int8, activations as 16-bit fixed point in two int8 "
                  "limbs, int32-exact dot products, fp32 scales and combine, fp64 router",
         "data": "synthetic (seeded weights and activations, 64 rotating input batches)",
+        "launch": "QS_DECODE_EXCLUSIVE (the persistent kernel as an ordinary dispatch; the bench runs nothing "
+                  "else on the device); per_batch.*.cooperative_ms_per_step times the cooperative launch",
         "config": {"workload": wl.name, "layers": L, "hidden": wl.hidden, "experts": wl.n_experts,
                    "top_k": wl.top_k, "expert_ffn": wl.expert_ffn, "shared_ffn": wl.shared_ffn,
                    "gate_up_format": wl.gate_up_format, "down_format": wl.down_format,

@@ -109,6 +109,16 @@ typedef enum { QS_FMT_BF16 = 0, QS_FMT_Q2K = 1, QS_FMT_CB2 = 2, QS_FMT_Q8 = 3, Q
                                    this flag u_l = x_l */
 #define QS_DECODE_STEER    4u   /* steer each layer's MoE output with the
                                    handle's directions (qs_moe_set_steering) */
+#define QS_DECODE_EXCLUSIVE 8u  /* the caller runs no other kernel on the device
+                                   during the call: the persistent kernel is
+                                   dispatched as an ordinary launch instead of a
+                                   cooperative one, which saves the cooperative
+                                   launch's serialisation (about 20 us per call
+                                   on MI355X).  Same kernel, same results.  If
+                                   another kernel does hold compute units, some
+                                   workgroups start late, the kernel's bounded
+                                   waits give up and qs_moe_sync_status reports
+                                   QS_E_HIP */
 
 typedef struct qs_moe qs_moe;   /* opaque, owned by the library */
 

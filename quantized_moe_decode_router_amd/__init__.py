@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     qs_moe_set_steering, qs_moe_route, qs_moe_dequant,
     qs_moe_memory_bytes, qs_moe_destroy,
     QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED,
-    QS_FMT_BF16, QS_FMT_Q2K, QS_FMT_CB2, QS_FMT_Q8, QS_FMT_Q4K, QS_DECODE_RESIDUAL, QS_DECODE_RMSNORM, QS_DECODE_STEER,
+    QS_FMT_BF16, QS_FMT_Q2K, QS_FMT_CB2, QS_FMT_Q8, QS_FMT_Q4K, QS_DECODE_RESIDUAL, QS_DECODE_RMSNORM, QS_DECODE_STEER, QS_DECODE_EXCLUSIVE,
     QS_MOE_ABI_VERSION,
 )
 from .handle import MoE  # noqa: F401

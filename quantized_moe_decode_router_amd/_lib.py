@@ -16,6 +16,7 @@ QS_FMT_BF16, QS_FMT_Q2K, QS_FMT_CB2, QS_FMT_Q8, QS_FMT_Q4K = 0, 1, 2, 3, 4
 QS_DECODE_RESIDUAL = 1
 QS_DECODE_RMSNORM = 2
 QS_DECODE_STEER = 4
+QS_DECODE_EXCLUSIVE = 8
 
 FORMATS = {"bf16": QS_FMT_BF16, "q2k": QS_FMT_Q2K, "cb2": QS_FMT_CB2, "q8": QS_FMT_Q8, "q4k": QS_FMT_Q4K}
 

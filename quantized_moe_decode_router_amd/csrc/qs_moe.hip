@@ -991,7 +991,7 @@ bool choose_kernel(const qs_moe* h, int T, bool& small, PersistShape& p, bool pa
 // launch.  q4k: the Q4_K-style tail layers (batched kernel, GEMV items).
 int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const float* x, float* y, int T,
                    bool residual, bool prenorm, bool steer, int32_t* ids_out, float* w_out, hipStream_t st,
-                   bool q4k) {
+                   bool q4k, bool exclusive) {
   const qs_moe_config& c = h->cfg;
   const bool cb2 = !q4k && c.gate_up_format == QS_FMT_CB2;
   // a launch over any paged layer takes the instantiations that read the map
@@ -1076,8 +1076,13 @@ int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const flo
       fn = persist_big_fixed_fn(h, steer);
     if (!fn) fn = persist_fn(cb2, small, steer);
   }
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kPersistThreads), args,
-                                            (unsigned)p.lds, st);
+  // (every workgroup must be resident at once: a cooperative launch
+  // guarantees it; an exclusive caller guarantees that nothing else holds
+  // the compute units, and the create-time occupancy check that one
+  // workgroup fits each of the grid's CUs)
+  hipError_t e = exclusive ? hipLaunchKernel(fn, dim3(a.G), dim3(kPersistThreads), args, (size_t)p.lds, st)
+                           : hipLaunchCooperativeKernel(fn, dim3(a.G), dim3(kPersistThreads), args,
+                                                        (unsigned)p.lds, st);
   if (e != hipSuccess) {
     fprintf(stderr, "qs_moe: persistent launch failed: %s\n", hipGetErrorString(e));
     return QS_E_HIP;
@@ -1090,19 +1095,21 @@ int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const flo
 // The whole decode call: one launch per run of layers of one routed format
 // (the 2-bit layers, then the Q4_K-style tail layers), chained through y.
 int launch_persistent(qs_moe* h, const CallState& cs, int layer0, int nL, const float* x, float* y, int T,
-                      bool residual, bool prenorm, bool steer, int32_t* ids_out, float* w_out, hipStream_t st) {
+                      bool residual, bool prenorm, bool steer, int32_t* ids_out, float* w_out, hipStream_t st,
+                      bool exclusive) {
   const qs_moe_config& c = h->cfg;
   const int split = c.n_layers - c.tail_layers;   // the first tail layer
   if (layer0 + nL <= split || layer0 >= split)
     return launch_segment(h, cs, layer0, nL, x, y, T, residual, prenorm, steer, ids_out, w_out, st,
-                          layer0 >= split);
+                          layer0 >= split, exclusive);
   // (several layers: the residual chain, so the second run continues in y)
   const int n1 = split - layer0;
-  int rc = launch_segment(h, cs, layer0, n1, x, y, T, residual, prenorm, steer, ids_out, w_out, st, false);
+  int rc = launch_segment(h, cs, layer0, n1, x, y, T, residual, prenorm, steer, ids_out, w_out, st, false,
+                          exclusive);
   if (rc) return rc;
   const size_t skip = (size_t)n1 * T * c.top_k;
   return launch_segment(h, cs, split, nL - n1, y, y, T, residual, prenorm, steer, ids_out ? ids_out + skip : nullptr,
-                        w_out ? w_out + skip : nullptr, st, true);
+                        w_out ? w_out + skip : nullptr, st, true, exclusive);
 }
 
 int check_layer_range(const qs_moe* h, int layer0, int n) {
@@ -1137,7 +1144,7 @@ int check_decode_args(const qs_moe* h, int layer0, int n_layers, const float* x,
                       int n_tokens, uint32_t flags) {
   if (!h || !x || !y) return QS_E_INVAL;
   const qs_moe_config& c = h->cfg;
-  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM | QS_DECODE_STEER)) return QS_E_INVAL;
+  if (flags & ~(QS_DECODE_RESIDUAL | QS_DECODE_RMSNORM | QS_DECODE_STEER | QS_DECODE_EXCLUSIVE)) return QS_E_INVAL;
   if (n_tokens < 1 || n_tokens > c.max_tokens) return QS_E_INVAL;
   if (((uintptr_t)x | (uintptr_t)y) & 15) return QS_E_INVAL;
   const bool residual = flags & QS_DECODE_RESIDUAL;
@@ -1465,7 +1472,8 @@ QS_API int qs_moe_decode(qs_moe* h, int layer0, int n_layers, const float* x, fl
   }
   int32_t* ids = paged && !ids_out ? h->ids_buf : ids_out;
   rc = launch_persistent(h, cs, layer0, n_layers, x, y, n_tokens, (flags & QS_DECODE_RESIDUAL) != 0,
-                         (flags & QS_DECODE_RMSNORM) != 0, (flags & QS_DECODE_STEER) != 0, ids, w_out, st);
+                         (flags & QS_DECODE_RMSNORM) != 0, (flags & QS_DECODE_STEER) != 0, ids, w_out, st,
+                         (flags & QS_DECODE_EXCLUSIVE) != 0);
   if (rc || !paged) return rc;
   return cache_record(h, ids, layer0, n_layers, n_tokens, st);
 }
@@ -1498,7 +1506,7 @@ QS_API int qs_moe_decode_static(qs_moe* h, int layer0, int n_layers, const float
                      kStaticScratchBytes - kStaticSyncBytes};
   return launch_persistent(h, cs, layer0, n_layers, x, y, n_tokens, (flags & QS_DECODE_RESIDUAL) != 0,
                            (flags & QS_DECODE_RMSNORM) != 0, (flags & QS_DECODE_STEER) != 0, ids_out, w_out,
-                           (hipStream_t)hip_stream);
+                           (hipStream_t)hip_stream, (flags & QS_DECODE_EXCLUSIVE) != 0);
 }
 
 QS_API int qs_moe_sync_status(qs_moe* h, void* hip_stream) {

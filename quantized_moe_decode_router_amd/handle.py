@@ -64,27 +64,28 @@ class MoE:
                         None if lw.shared_down is None else c(lw.shared_down), stream)
 
     def decode(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
-               w_out=None, stream=None, steer=False):
+               w_out=None, stream=None, steer=False, exclusive=False):
         """One qs_moe_decode call (one persistent kernel launch) on `stream`
-        (torch's current stream by default); asynchronous."""
+        (torch's current stream by default); asynchronous.  exclusive: the
+        caller runs nothing else on the device meanwhile (QS_DECODE_EXCLUSIVE)."""
         import torch
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
         flags = ((L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
-                 | (L.QS_DECODE_STEER if steer else 0))
+                 | (L.QS_DECODE_STEER if steer else 0) | (L.QS_DECODE_EXCLUSIVE if exclusive else 0))
         L.qs_moe_decode(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
 
     def decode_static(self, x, y=None, layer0=0, n_layers=1, residual=False, prenorm=False, ids_out=None,
-                      w_out=None, stream=None, steer=False):
+                      w_out=None, stream=None, steer=False, exclusive=False):
         """qs_moe_decode_static: decode with the library's static device scratch."""
         import torch
         T = x.shape[0]
         if y is None:
             y = torch.empty_like(x)
         flags = ((L.QS_DECODE_RESIDUAL if residual else 0) | (L.QS_DECODE_RMSNORM if prenorm else 0)
-                 | (L.QS_DECODE_STEER if steer else 0))
+                 | (L.QS_DECODE_STEER if steer else 0) | (L.QS_DECODE_EXCLUSIVE if exclusive else 0))
         L.qs_moe_decode_static(self.h, layer0, n_layers, x, y, T, flags, ids_out, w_out, stream)
         return y
 

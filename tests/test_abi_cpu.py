@@ -39,7 +39,8 @@ def test_no_other_exported_qs_symbols():
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define\s+(QS_\w+)\s+(\d+)u?\b", text))
-    for name in ("QS_MOE_ABI_VERSION", "QS_DECODE_RESIDUAL", "QS_DECODE_RMSNORM"):
+    for name in ("QS_MOE_ABI_VERSION", "QS_DECODE_RESIDUAL", "QS_DECODE_RMSNORM", "QS_DECODE_STEER",
+                 "QS_DECODE_EXCLUSIVE"):
         assert hasattr(qm, name), name
         assert int(defs[name]) == getattr(qm, name), name
 

@@ -326,6 +326,28 @@ def test_multilayer_small_hidden(lib, T):
     _chain_check(lib, workload("tiny_q2k", n_layers=5, zipf_s=1.1), 5, T, True)
 
 
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_exclusive_launch_same_bits(lib, T):
+    """QS_DECODE_EXCLUSIVE dispatches the same persistent kernel as an
+    ordinary launch: outputs, ids and weights equal the cooperative launch's
+    bitwise (fixed-shape small-batch kernel at T = 1, 4, batched at 16, and
+    the generic small-batch kernel of the tiny shape)."""
+    for wl, L in ((workload("a3b_stack40_zipf"), 3), (workload("tiny_q2k", n_layers=3, zipf_s=1.1), 3)):
+        say(f"exclusive launch {wl.name} T={T}")
+        moe, _ = make_handle(lib, wl, n_layers=L, max_tokens=16)
+        with moe:
+            x = torch.from_numpy(synth.tokens(wl, T, 5)).cuda()
+            out = []
+            for excl in (False, True, False, True):
+                ids = torch.full((L, T, wl.top_k), -1, dtype=torch.int32, device="cuda")
+                w = torch.empty((L, T, wl.top_k), dtype=torch.float32, device="cuda")
+                y = moe.decode(x, n_layers=L, residual=True, prenorm=True, ids_out=ids, w_out=w, exclusive=excl)
+                moe.sync_status()
+                out.append((y, ids, w))
+            for y, ids, w in out[1:]:
+                assert torch.equal(y, out[0][0]) and torch.equal(ids, out[0][1]) and torch.equal(w, out[0][2])
+
+
 def test_wait_limit_reports_give_up(lib):
     """A wait limit of one poll makes the kernels' bounded waits give up while
     data is still on its way; every workgroup leaves through its normal path,
@@ -396,7 +418,7 @@ def test_error_statuses_with_gpu(lib):
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), x.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr() + 4, y.data_ptr(), 2, 0, None, None, st) == lib.QS_E_INVAL
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 16, None, None, st) == lib.QS_E_INVAL
-        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 8, None, None, st) == lib.QS_E_INVAL
+        assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 32, None, None, st) == lib.QS_E_INVAL
         # steering asked for before any directions were set
         assert L.qs_moe_decode(moe.h, 0, 1, x.data_ptr(), y.data_ptr(), 4, 4, None, None, st) == lib.QS_E_STATE
         assert L.qs_moe_decode(moe.h, 2, 1, x.data_ptr(), y.data_ptr(), 4, 0, None, None, st) == lib.QS_E_INVAL
