@@ -563,7 +563,8 @@ int setup_paging(qs_moe* h) {
     }
     h->total_bytes += S * h->slot_bytes;
   }
-  if (!hip_ok(hipMalloc(&h->d_emap, keys * 8), "hipMalloc(expert map)")) {
+  // (+16: the small-batch kernel copies a layer's map in 16-byte units)
+  if (!hip_ok(hipMalloc(&h->d_emap, keys * 8 + 16), "hipMalloc(expert map)")) {
     h->d_emap = nullptr;
     return QS_E_NOMEM;
   }
@@ -663,7 +664,7 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small, bool paged = fals
   // hidden 2048 (sh_regs), the only small-batch kernels there
   const bool shregs = c.hidden > 2048 && !paged;
   const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, sq8, cb2,
-                                 small, 0, shregs).end;
+                                 small, 0, shregs, paged).end;
   if (base >= h->lds_limit || h->grid_small < 8) return p;
   p.pfb = (uint32_t)std::min((size_t)kPfbMax, (h->lds_limit - base) & ~(size_t)15);
   p.lds = base + p.pfb;
@@ -911,7 +912,7 @@ int setup_persistent(qs_moe* h) {
   }
   h->persist_small_ok = lds_small && persist_resident(h, true, lds_small);
   h->persist_big_ok = lds_big && persist_resident(h, false, lds_big);
-  size_t lds4 = 0;
+  size_t lds4 = 0, lds_pg = 0;
   if (c.tail_layers > 0) {   // the Q4_K-style tail layers: the batched kernel at every T
     bool all = true;
     for (int T = 1; T <= c.max_tokens; ++T) {
@@ -925,8 +926,13 @@ int setup_persistent(qs_moe* h) {
   }
   if (h->n_paged) {
     const int gf = c.gate_up_format == QS_FMT_CB2 ? kFmtCB2 : kFmtQ2K;
+    // (the paged small-batch carve also holds the layer's expert map)
+    for (int T = 1; T <= std::min(c.max_tokens, kSmallT); ++T) {
+      const PersistShape p = persist_shape(h, T, true, true);
+      if (p.ok) lds_pg = std::max(lds_pg, p.lds);
+    }
     for (int st = 0; st < 2; ++st) {
-      h->pg_small_ok[st] = lds_small && fn_resident(persist_paged_fn(gf, true, st != 0), lds_small);
+      h->pg_small_ok[st] = lds_pg && fn_resident(persist_paged_fn(gf, true, st != 0), lds_pg);
       h->pg_big_ok[st] = lds_big && fn_resident(persist_paged_fn(gf, false, st != 0), lds_big);
       h->pg_q4k_ok[st] = lds4 && fn_resident(persist_paged_fn(kFmtQ4K, false, st != 0), lds4);
     }
@@ -954,7 +960,7 @@ int setup_persistent(qs_moe* h) {
     h->pg_fixed_ok = h->pg_small_ok[0];
     for (int T = 1; T <= kSmallT && h->pg_fixed_ok; ++T) {
       const void* fn = persist_fixed_fn(h, T, false, true);
-      h->pg_fixed_ok = fn && resident(fn, lds_small);
+      h->pg_fixed_ok = fn && resident(fn, lds_pg);
     }
   }
   h->fixed_ok = h->persist_small_ok;

@@ -406,13 +406,13 @@ __host__ __device__ inline uint32_t abuf_bytes(int T, int H, int E, int P, int F
 
 struct LdsLayout {
   uint32_t tab, cnt, off, act, aoff, nact, llerr, mask, ids, pairs, tok_order, cw, pos_of, wl, o, red, sh, ga, sred,
-      qtmp, rinv, kf, cand, ncand, sv, xh, xl, xs, xa, abuf, pfb, sdr, end;
+      qtmp, rinv, kf, cand, ncand, sv, xh, xl, xs, xa, abuf, emap, pfb, sdr, end;
 };
 
 __host__ __device__ inline int kf_stride(int E) { return (E + 7) & ~7; }
 
 __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int F, int Fs, bool sq8, bool cb2,
-                                                bool small, uint32_t pfb, bool shregs = false) {
+                                                bool small, uint32_t pfb, bool shregs = false, bool paged = false) {
   LdsLayout l;
   uint32_t o = 0;
   auto take = [&](uint32_t n) {
@@ -448,6 +448,7 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.ncand = take(small ? (uint32_t)T * 4 : 0);
   l.sv = take(small ? (uint32_t)P * 8 : 0);
   l.abuf = take(small ? abuf_bytes(T, H, E, P, F, Fs) : 0);
+  l.emap = take(small && paged ? (uint32_t)E * 8 : 0);   // a paged layer's expert map, a layer ahead
   l.pfb = take(pfb);
   // SMALL: the x limbs follow the staging buffer, so that once the gate/up
   // tiles are done the down rows can spill over them; the shared down rows
@@ -491,6 +492,7 @@ struct PersistLds {
   QS_LDS uint32_t* xh;    // [T*H/4] SMALL: x limbs
   QS_LDS uint32_t* xl;
   QS_LDS float* xs;       // [T*H/16]
+  QS_LDS uint64_t* emap;  // [E] paged layers (small-batch kernel): the layer's expert map
   QS_LDS int* xa;
   QS_LDS uint8_t* pfb;    // weight staging buffer
   QS_LDS uint8_t* sdr;    // SMALL: shared-expert down rows of this workgroup's output rows
@@ -507,7 +509,7 @@ struct PersistLds {
 template <bool SMALL, class A>
 __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const A& a, bool cb2) {
   const uint32_t T = a.T, H = a.H, E = a.E, F = a.F, P = T * a.k;
-  const LdsLayout l = lds_layout(E, T, P, H, F, a.Fs, a.sq8 != 0, cb2, SMALL, a.pfb, SMALL && sh_regs(a));
+  const LdsLayout l = lds_layout(E, T, P, H, F, a.Fs, a.sq8 != 0, cb2, SMALL, a.pfb, SMALL && sh_regs(a), A::kPaged);
   QS_LDS uint8_t* b = (QS_LDS uint8_t*)raw;
   PersistLds L;
   L.tab = (QS_LDS uint32_t*)(b + l.tab);
@@ -538,6 +540,7 @@ __device__ __forceinline__ PersistLds carve_lds(uint8_t* raw, const A& a, bool c
   L.xh = (QS_LDS uint32_t*)(b + l.xh);
   L.xl = (QS_LDS uint32_t*)(b + l.xl);
   L.xs = (QS_LDS float*)(b + l.xs);
+  L.emap = (QS_LDS uint64_t*)(b + l.emap);
   L.xa = (QS_LDS int*)(b + l.xa);
   L.pfb = b + l.pfb;
   L.sdr = b + l.sdr;
@@ -696,12 +699,13 @@ __device__ __forceinline__ void copy_tile(const A& a, const LayerPtrs& Lp, QS_LD
 
 
 // Routed down rows r0..r0+7 of expert e as [codes 8*nb*64 | scales 8*nb*16 | d,dmin 8*nb*4].
+// rec: a paged expert's record (its down matrix at 2 gu_stride), or null.
 template <class A>
 __device__ __forceinline__ void copy_down_rows(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
-                                               int e, int r0, int w, int nw) {
+                                               int e, int r0, int w, int nw, const uint8_t* rec = nullptr) {
   const uint32_t nb = a.F / kBlockW;
   const MatPlanes pl = q2k_planes((size_t)a.H * nb);
-  const uint8_t* base = ex_mat(a, Lp, 2, e);
+  const uint8_t* base = rec ? rec + 2 * a.gu_stride : ex_mat(a, Lp, 2, e);
   const size_t b0 = (size_t)r0 * nb;
   dma_to_lds<0>(base + pl.q + b0 * 64, dst, kDownRows * nb * 64, w, nw);
   dma_to_lds<0>(base + pl.s + b0 * 16, dst + kDownRows * nb * 64, kDownRows * nb * 16, w, nw);
@@ -719,6 +723,9 @@ template <bool SMALL, class A>
 __device__ __forceinline__ void pf_router_and_shared(const A& a, const LayerPtrs& Lp, PersistLds& L,
                                                      int w, int nw) {
   if ((int)blockIdx.x < router_groups(a)) copy_router_rows(a, Lp, L, blockIdx.x, w, nw);
+  if constexpr (SMALL && A::kPaged) {
+    if (Lp.emap) dma_to_lds<0>(Lp.emap, L.emap, (uint32_t)a.E * 8, w, nw);
+  }
   if (SMALL && !sh_regs(a)) {
     const int n = shared_pf_count<true>(a);
     for (int j = 0; j < n; ++j)
@@ -754,9 +761,23 @@ __device__ __forceinline__ void pf_down(const A& a, const LayerPtrs& Lp, Persist
   for (int u0 = 0; u0 < n; u0 += 64) {
     const int el = act_lanes(L, u0, n);
     const int m = n - u0 < 64 ? n - u0 : 64;
-    for (int i = 0; i < m; ++i)
+    // paged layer: the experts' records, gathered into lanes from the LDS
+    // map before any copy is issued (a wave with copies in flight waits for
+    // them at its next LDS access)
+    uint64_t rl = 0;
+    if constexpr (SMALL && A::kPaged) {
+      if (Lp.emap && (int)(qs_tid() & 63) < m) rl = L.emap[el];
+    }
+    for (int i = 0; i < m; ++i) {
+      const uint8_t* rec = nullptr;
+      if constexpr (SMALL && A::kPaged) {
+        if (Lp.emap)
+          rec = (const uint8_t*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(rl >> 32), i) << 32) |
+                                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rl, i));
+      }
       copy_down_rows(a, Lp, base + (SMALL ? 0u : al16(sd_bytes(a))) + (uint32_t)(u0 + i) * dn_expert_bytes(a),
-                     __builtin_amdgcn_readlane(el, i), r0, w, nw);
+                     __builtin_amdgcn_readlane(el, i), r0, w, nw, rec);
+    }
   }
 }
 
@@ -1852,8 +1873,16 @@ __device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, co
   const uint32_t nbh = a.H / kBlockW;
   const size_t nblk = (size_t)a.F * nbh;
   const MatPlanes pl = FMT == 1 ? q2k_planes(nblk) : cb2_planes(nblk);
-  const uint8_t* g = ex_mat(a, Lp, 0, e);
-  const uint8_t* up = ex_mat(a, Lp, 1, e);
+  const uint8_t* g;
+  const uint8_t* up;
+  if constexpr (A::kPaged) {   // the record's address from the layer's map in LDS
+    const uint8_t* rec = Lp.emap ? (const uint8_t*)(uintptr_t)L.emap[e] : nullptr;
+    g = rec ? rec : ex_mat(a, Lp, 0, e);
+    up = rec ? rec + a.gu_stride : ex_mat(a, Lp, 1, e);
+  } else {
+    g = ex_mat(a, Lp, 0, e);
+    up = ex_mat(a, Lp, 1, e);
+  }
 #pragma unroll
   for (int i = 0; i < kGuUnits; ++i) {
     const int r = slot + (i / cpl) * slots, ch = j + (i % cpl) * lpr;
