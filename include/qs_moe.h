@@ -148,9 +148,11 @@ typedef struct {
   int32_t tail_layers;     /* 0..n_layers: the last tail_layers resident layers
                               hold their routed experts (gate, up and down) in
                               QS_FMT_Q4K instead of gate_up_format/down_format.
-                              Those layers run the batched kernel's GEMV items
-                              (no MFMA items), at every batch size; a decode
-                              call over both kinds of layer is two launches */
+                              Those layers run the small-batch kernel for
+                              batches it takes (as the 2-bit layers do) and
+                              otherwise the batched kernel's GEMV items (no
+                              MFMA items); a decode call over both kinds of
+                              layer is two launches */
   /* Routed-expert paging, the MI355X form of running a model whose routed
    * experts exceed device memory (QuarkStar README, "Running Models Larger
    * Than Available Memory": non-routed weights stay resident, a prefix of

@@ -137,6 +137,8 @@ struct qs_moe {
   bool steer_big_ok = false;
   bool q4k_ok = false;           // the batched Q4_K-style instantiation (tail layers) usable
   bool q4k_steer_ok = false;
+  bool q4k_small_ok[2] = {false, false};   // the small-batch Q4_K-style instantiations, [steer]
+  bool q4k_fixed_ok = false;                // and their fixed-shape ones
   int mfma_min = 1;               // bucket size from which the MFMA path runs
   bool mfma_explicit = false;     // the config set mfma_min_tokens
   bool fixed_ok = false;          // the fixed-shape small-batch kernels are usable
@@ -653,16 +655,19 @@ int gu_units(int H) {
 
 const void* persist_fixed_fn(const qs_moe* h, int T, bool steer = false, bool paged = false);
 
-// paged: for the instantiations of paged layers, which have no fixed shape
-PersistShape persist_shape(const qs_moe* h, int T, bool small, bool paged = false) {
+// paged: for the instantiations of paged layers, which have no fixed shape.
+// fmt: the routed format of the launch's layers (-1: the 2-bit layers;
+// QS_FMT_Q4K: the tail layers, gate/up and down both Q4_K-style)
+PersistShape persist_shape(const qs_moe* h, int T, bool small, bool paged = false, int fmt = -1) {
   const qs_moe_config& c = h->cfg;
-  if (!small) return big_shape(h, T, c.gate_up_format);
+  const bool q4k = fmt == QS_FMT_Q4K;
+  if (!small) return big_shape(h, T, q4k ? QS_FMT_Q4K : c.gate_up_format);
   PersistShape p;
-  const bool cb2 = c.gate_up_format == QS_FMT_CB2;
+  const bool cb2 = !q4k && c.gate_up_format == QS_FMT_CB2;
   const bool sq8 = c.shared_format == QS_FMT_Q8;
   // the shared expert through registers: the fixed-shape kernels above
   // hidden 2048 (sh_regs), the only small-batch kernels there
-  const bool shregs = c.hidden > 2048 && !paged;
+  const bool shregs = c.hidden > 2048 && !paged && !q4k;
   const size_t base = lds_layout(c.n_experts, T, T * c.top_k, c.hidden, c.expert_ffn, c.shared_ffn, sq8, cb2,
                                  small, 0, shregs, paged).end;
   if (base >= h->lds_limit || h->grid_small < 8) return p;
@@ -673,7 +678,7 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small, bool paged = fals
   const uint64_t H = c.hidden, F = c.expert_ffn, Fs = c.shared_ffn, nbh = H / 256, nb = F / 256;
   const uint64_t rb = (uint64_t)p.r_et * H * 4, item = big_item_b(c.hidden, sq8);
   const uint64_t tile = 2ull * 16 * nbh * (64 + (cb2 ? 4 : 16) + (cb2 ? 2 : 4));
-  const uint64_t sd = big_sdrows_b(c.shared_ffn, sq8), pe = 8 * nb * 84;
+  const uint64_t sd = big_sdrows_b(c.shared_ffn, sq8), pe = 8 * nb * blk_bytes(q4k ? kFmtQ4K : kFmtQ2K);
   auto a16 = [](uint64_t v) { return (v + 15) & ~15ull; };
   bool fits;
   if (small) {
@@ -693,7 +698,7 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small, bool paged = fals
     // the generic one measured 83 us per layer against the batched kernel's
     // 73, the fixed one 57.
     fits = A <= p.pfb && (p.pfb - A) + xl >= pe && gu_units(c.hidden) <= kGuUnits &&
-           (c.hidden <= 2048 || (!paged && persist_fixed_fn(h, T) != nullptr));
+           (c.hidden <= 2048 || (!paged && !q4k && persist_fixed_fn(h, T) != nullptr));
     // with registers: a row's chunks per lane fit one register round
     if (shregs)
       fits = fits && (H / 4 + 511) / 512 <= (uint64_t)kShPairsLds && (Fs + 511) / 512 <= (uint64_t)kShDnRegs;
@@ -800,6 +805,22 @@ const void* persist_fixed_fn(const qs_moe* h, int T, bool steer, bool paged) {
   return nullptr;
 }
 
+// The fixed-shape small-batch instantiations of the Q4_K-style tail layers:
+// the A3B shape with the bf16 shared expert, T = 1..4, unsteered.
+const void* q4k_fixed_fn(const qs_moe* h, int T) {
+  const qs_moe_config& c = h->cfg;
+  if (h->grid_small != 256 || c.hidden != 2048 || c.n_experts != 256 || c.top_k != 8 || c.expert_ffn != 512 ||
+      c.shared_ffn != 512 || c.shared_format != QS_FMT_BF16)
+    return nullptr;
+  switch (T) {
+    case 1: return (const void*)k_persist_small_fixed<kFmtQ4K, 2048, 256, 8, 512, 512, 0, 1, 256>;
+    case 2: return (const void*)k_persist_small_fixed<kFmtQ4K, 2048, 256, 8, 512, 512, 0, 2, 256>;
+    case 3: return (const void*)k_persist_small_fixed<kFmtQ4K, 2048, 256, 8, 512, 512, 0, 3, 256>;
+    case 4: return (const void*)k_persist_small_fixed<kFmtQ4K, 2048, 256, 8, 512, 512, 0, 4, 256>;
+    default: return nullptr;
+  }
+}
+
 // The batched instantiation of the Q4_K-style tail layers (GEMV items only).
 const void* persist_q4k_fn(bool steer) {
   return steer ? (const void*)k_persist_big<kFmtQ4K, true> : (const void*)k_persist_big<kFmtQ4K, false>;
@@ -886,6 +907,7 @@ int setup_persistent(qs_moe* h) {
       }
   for (int st = 0; st < 2; ++st) {
     const void* fns[] = {persist_q4k_fn(st != 0), persist_paged_fn(kFmtQ4K, false, st != 0),
+                         st ? (const void*)k_persist_small<kFmtQ4K, true> : (const void*)k_persist_small<kFmtQ4K, false>,
                          persist_paged_fn(kFmtCB2, true, st != 0), persist_paged_fn(kFmtCB2, false, st != 0),
                          persist_paged_fn(kFmtQ2K, true, st != 0), persist_paged_fn(kFmtQ2K, false, st != 0)};
     for (const void* fn : fns) {
@@ -923,6 +945,20 @@ int setup_persistent(qs_moe* h) {
     if (!all) lds4 = 0;
     h->q4k_ok = lds4 && fn_resident(persist_q4k_fn(false), lds4);
     h->q4k_steer_ok = h->q4k_ok && fn_resident(persist_q4k_fn(true), lds4);
+    size_t lds4s = 0;   // the small-batch kernel for the tail layers' small batches
+    for (int T = 1; T <= std::min(c.max_tokens, kSmallT); ++T) {
+      const PersistShape p = persist_shape(h, T, true, false, QS_FMT_Q4K);
+      if (p.ok) lds4s = std::max(lds4s, p.lds);
+    }
+    for (int st = 0; st < 2; ++st)
+      h->q4k_small_ok[st] = lds4s && h->grid_small >= 8 &&
+                            fn_resident(st ? (const void*)k_persist_small<kFmtQ4K, true>
+                                           : (const void*)k_persist_small<kFmtQ4K, false>, lds4s);
+    h->q4k_fixed_ok = h->q4k_small_ok[0];
+    for (int T = 1; T <= kSmallT && h->q4k_fixed_ok; ++T) {
+      const void* fn = q4k_fixed_fn(h, T);
+      h->q4k_fixed_ok = fn && fn_resident(fn, lds4s);
+    }
   }
   if (h->n_paged) {
     const int gf = c.gate_up_format == QS_FMT_CB2 ? kFmtCB2 : kFmtQ2K;
@@ -1005,9 +1041,17 @@ int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const flo
   bool small = false;
   PersistShape p;
   if (q4k) {
-    if (!(paged ? h->pg_q4k_ok[steer] : steer ? h->q4k_steer_ok : h->q4k_ok)) return QS_E_UNSUPPORTED;
-    p = big_shape(h, T, QS_FMT_Q4K);
-    if (!p.ok) return QS_E_UNSUPPORTED;
+    // small batches of resident tail layers: the small-batch kernel when it fits
+    small = !paged && T <= kSmallT && (!h->mfma_explicit || T < h->mfma_min) && h->q4k_small_ok[steer];
+    if (small) {
+      p = persist_shape(h, T, true, false, QS_FMT_Q4K);
+      small = p.ok;
+    }
+    if (!small) {
+      if (!(paged ? h->pg_q4k_ok[steer] : steer ? h->q4k_steer_ok : h->q4k_ok)) return QS_E_UNSUPPORTED;
+      p = big_shape(h, T, QS_FMT_Q4K);
+      if (!p.ok) return QS_E_UNSUPPORTED;
+    }
   } else {
     if (!choose_kernel(h, T, small, p, paged)) return QS_E_UNSUPPORTED;   // (create checked every T)
     if (steer && !(paged ? (small ? h->pg_small_ok[1] : h->pg_big_ok[1])
@@ -1055,7 +1099,7 @@ int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const flo
   // default threshold: one-token buckets of a one-token batch stay on the
   // GEMV items (measured faster there: Flash stack T = 1, 1680 vs 1274 tok/s)
   a.mfma_min = !h->mfma_explicit && T == 1 ? 2 : h->mfma_min;
-  if (q4k) a.mfma_min = 1 << 30;   // GEMV items only
+  if (q4k) a.mfma_min = 1 << 30;   // GEMV items only (batched kernel)
   a.ll_lg = s.ll_lg; a.ll_a = s.ll_a; a.llx0 = s.llx[0]; a.llx1 = s.llx[1];
   a.ll_epoch = *cs.ll_epoch;
   a.af = s.af; a.ob = s.ob; a.sb = s.sb;
@@ -1074,7 +1118,10 @@ int launch_segment(qs_moe* h, const CallState& cs, int layer0, int nL, const flo
     if (!q4k && !steer && !small && h->pg_big_fixed_ok && p.r_et == 1) fn = persist_big_fixed_fn(h, false, true);
     if (!fn) fn = persist_paged_fn(q4k ? kFmtQ4K : cb2 ? kFmtCB2 : kFmtQ2K, small, steer);
   } else if (q4k) {
-    fn = persist_q4k_fn(steer);
+    if (small && !steer && h->q4k_fixed_ok && p.r_et == 1 && p.r_tt == T) fn = q4k_fixed_fn(h, T);
+    if (!fn)
+      fn = small ? (steer ? (const void*)k_persist_small<kFmtQ4K, true> : (const void*)k_persist_small<kFmtQ4K, false>)
+                 : persist_q4k_fn(steer);
   } else {
     if (small && (steer ? h->fixed_steer_ok : h->fixed_ok) && p.r_et == 1 && p.r_tt == T)
       fn = persist_fixed_fn(h, T, steer);

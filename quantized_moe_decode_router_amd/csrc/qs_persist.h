@@ -596,7 +596,7 @@ template <class A>
 __device__ __forceinline__ uint32_t sd_bytes(const A& a) { return (uint32_t)kDownRows * srow_bytes(a.Fs, a.sq8 != 0); }
 template <class A>
 __device__ __forceinline__ uint32_t dn_expert_bytes(const A& a) {
-  return (uint32_t)kDownRows * (a.F / kBlockW) * kQ2KBytes;
+  return (uint32_t)kDownRows * (a.F / kBlockW) * blk_bytes(a.dfmt);
 }
 
 // SMALL: region A = [0, pfa) holds the router rows and shared items (phase
@@ -698,18 +698,20 @@ __device__ __forceinline__ void copy_tile(const A& a, const LayerPtrs& Lp, QS_LD
 }
 
 
-// Routed down rows r0..r0+7 of expert e as [codes 8*nb*64 | scales 8*nb*16 | d,dmin 8*nb*4].
+// Routed down rows r0..r0+7 of expert e as [codes | scales | d,dmin] (per
+// block 64 | 16 | 4 bytes for Q2_K, 128 | 16 | 4 for the Q4_K-style planes).
 // rec: a paged expert's record (its down matrix at 2 gu_stride), or null.
 template <class A>
 __device__ __forceinline__ void copy_down_rows(const A& a, const LayerPtrs& Lp, QS_LDS uint8_t* dst,
                                                int e, int r0, int w, int nw, const uint8_t* rec = nullptr) {
   const uint32_t nb = a.F / kBlockW;
-  const MatPlanes pl = q2k_planes((size_t)a.H * nb);
+  const MatPlanes pl = fmt_planes(a.dfmt, (size_t)a.H * nb);
+  const BlkGeom g = blk_geom(a.dfmt);
   const uint8_t* base = rec ? rec + 2 * a.gu_stride : ex_mat(a, Lp, 2, e);
   const size_t b0 = (size_t)r0 * nb;
-  dma_to_lds<0>(base + pl.q + b0 * 64, dst, kDownRows * nb * 64, w, nw);
-  dma_to_lds<0>(base + pl.s + b0 * 16, dst + kDownRows * nb * 64, kDownRows * nb * 16, w, nw);
-  dma_to_lds<0>(base + pl.d + b0 * 4, dst + kDownRows * nb * 80, kDownRows * nb * 4, w, nw);
+  dma_to_lds<0>(base + pl.q + b0 * g.q, dst, kDownRows * nb * g.q, w, nw);
+  dma_to_lds<0>(base + pl.s + b0 * g.s, dst + kDownRows * nb * g.q, kDownRows * nb * g.s, w, nw);
+  dma_to_lds<0>(base + pl.d + b0 * g.d, dst + kDownRows * nb * (g.q + g.s), kDownRows * nb * g.d, w, nw);
 }
 
 template <class A>
@@ -1856,6 +1858,16 @@ struct GuChunk {
 struct GuTile {
   GuChunk c[kGuUnits];
 };
+// Q4_K-style chunks: 32 code bytes per matrix (gq, gq2 / uq, uq2); gs, us
+// the chunk's two scales (bytes 0, 1) and mins (bytes 2, 3); gd, ud d | dmin << 16.
+struct GuChunk4 : GuChunk {
+  uint4 gq2, uq2;
+};
+struct GuTile4 {
+  GuChunk4 c[kGuUnits];
+};
+template <int FMT> struct GuTileOf { typedef GuTile T; };
+template <> struct GuTileOf<kFmtQ4K> { typedef GuTile4 T; };
 
 template <class A>
 __device__ __forceinline__ int gu_tiles_mine(const A& a, const PersistLds& L) {
@@ -1864,7 +1876,7 @@ __device__ __forceinline__ int gu_tiles_mine(const A& a, const PersistLds& L) {
 
 template <int FMT, class A>
 __device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, const PersistLds& L, int m,
-                                             GuTile& t) {
+                                             typename GuTileOf<FMT>::T& t) {
   const int tiles = a.F / kGateTile, nch = a.H / kChunkW, lpr = lanes_per_row(nch), cpl = nch / lpr;
   const int slots = kPersistThreads / lpr, slot = qs_tid() / lpr, j = qs_tid() % lpr;
   const int item = (int)blockIdx.x + m * a.G;
@@ -1872,7 +1884,7 @@ __device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, co
   const int e = L.act[u];
   const uint32_t nbh = a.H / kBlockW;
   const size_t nblk = (size_t)a.F * nbh;
-  const MatPlanes pl = FMT == 1 ? q2k_planes(nblk) : cb2_planes(nblk);
+  const MatPlanes pl = fmt_planes(FMT, nblk);
   const uint8_t* g;
   const uint8_t* up;
   if constexpr (A::kPaged) {   // the record's address from the layer's map in LDS
@@ -1889,7 +1901,20 @@ __device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, co
     if (r >= kGateTile || i >= ((kGateTile - 1 - slot) / slots + 1) * cpl) continue;
     const size_t blk = (size_t)(f0 + r) * nbh + ch / 4;
     const int c = ch & 3;
-    GuChunk& w = t.c[i];
+    auto& w = t.c[i];
+    if constexpr (FMT == kFmtQ4K) {
+      w.gq = *(const uint4*)(g + pl.q + blk * 128 + c * 32);
+      w.gq2 = *(const uint4*)(g + pl.q + blk * 128 + c * 32 + 16);
+      w.uq = *(const uint4*)(up + pl.q + blk * 128 + c * 32);
+      w.uq2 = *(const uint4*)(up + pl.q + blk * 128 + c * 32 + 16);
+      w.gs = (uint32_t)*(const uint16_t*)(g + pl.s + blk * 16 + 2 * c) |
+             (uint32_t)*(const uint16_t*)(g + pl.s + blk * 16 + 8 + 2 * c) << 16;
+      w.us = (uint32_t)*(const uint16_t*)(up + pl.s + blk * 16 + 2 * c) |
+             (uint32_t)*(const uint16_t*)(up + pl.s + blk * 16 + 8 + 2 * c) << 16;
+      w.gd = *(const uint32_t*)(g + pl.d + blk * 4);
+      w.ud = *(const uint32_t*)(up + pl.d + blk * 4);
+      continue;
+    }
     w.gq = *(const uint4*)(g + pl.q + blk * 64 + c * 16);
     w.uq = *(const uint4*)(up + pl.q + blk * 64 + c * 16);
     if (FMT == 1) {
@@ -1926,7 +1951,10 @@ __device__ __forceinline__ void gu_tile_store(const A& a, int p0, int n, int f0,
       if (r < 4) {
         int h[4], l[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) split_limbs(L.qtmp[tt * kGateTile + 4 * i + r], h[i], l[i]);
+        // (word r: values r, 4+r, 8+r, 12+r for the Q2_K down dot; 4r..4r+3
+        // for the Q4_K-style one)
+        for (int i = 0; i < 4; ++i)
+          split_limbs(L.qtmp[tt * kGateTile + (a.dfmt == kFmtQ4K ? 4 * r + i : 4 * i + r)], h[i], l[i]);
         const size_t wi = (size_t)pair * (a.F / 4) + f0 / 4 + r;
         ll_store(a.ll_a + wi, pack4(h[0], h[1], h[2], h[3]), flag);
         ll_store(a.ll_a + ll_al(a) + wi, pack4(l[0], l[1], l[2], l[3]), flag);
@@ -1946,7 +1974,8 @@ __device__ __forceinline__ void gu_tile_store(const A& a, int p0, int n, int f0,
 // every token of the bucket (at most kSmallT), quantised per 16 rows and
 // stored as flagged words.
 template <int FMT, class A>
-__device__ __forceinline__ void gu_tile_compute(const A& a, const GuTile& t, int m, PersistLds& L, uint32_t flag) {
+__device__ __forceinline__ void gu_tile_compute(const A& a, const typename GuTileOf<FMT>::T& t, int m, PersistLds& L,
+                                                uint32_t flag) {
   const int tiles = a.F / kGateTile, nch = a.H / kChunkW, lpr = lanes_per_row(nch), cpl = nch / lpr;
   const int slots = kPersistThreads / lpr, slot = qs_tid() / lpr, j = qs_tid() % lpr;
   const int item = (int)blockIdx.x + m * a.G;
@@ -1962,11 +1991,18 @@ __device__ __forceinline__ void gu_tile_compute(const A& a, const GuTile& t, int
 #pragma unroll
       for (int q = 0; q < 4; ++q) gacc[q] = uacc[q] = 0.f;
     }
-    const GuChunk& w = t.c[i];
+    const auto& w = t.c[i];
     const int c = ch & 3;
     uint32_t gw[16], uw[16];
     uint32_t gsc, usc;
-    if (q2k) {
+    if constexpr (FMT == kFmtQ4K) {
+      gsc = w.gs;
+      usc = w.us;
+      gw[0] = w.gq.x; gw[1] = w.gq.y; gw[2] = w.gq.z; gw[3] = w.gq.w;
+      gw[4] = w.gq2.x; gw[5] = w.gq2.y; gw[6] = w.gq2.z; gw[7] = w.gq2.w;
+      uw[0] = w.uq.x; uw[1] = w.uq.y; uw[2] = w.uq.z; uw[3] = w.uq.w;
+      uw[4] = w.uq2.x; uw[5] = w.uq2.y; uw[6] = w.uq2.z; uw[7] = w.uq2.w;
+    } else if (q2k) {
       gsc = w.gs;
       usc = w.us;
       gw[0] = w.gq.x; gw[1] = w.gq.y; gw[2] = w.gq.z; gw[3] = w.gq.w;
@@ -1994,7 +2030,12 @@ __device__ __forceinline__ void gu_tile_compute(const A& a, const GuTile& t, int
       int xa[4];
       x_chunk<true>(a, L, tok, ch, xh, xl, xs, xa);
       float gp, up;
-      if (q2k) {
+      if constexpr (FMT == kFmtQ4K) {
+        const uint32_t g8[8] = {gw[0], gw[1], gw[2], gw[3], gw[4], gw[5], gw[6], gw[7]};
+        const uint32_t u8[8] = {uw[0], uw[1], uw[2], uw[3], uw[4], uw[5], uw[6], uw[7]};
+        gp = q4k_chunk_dot(g8, gsc, half_to_f32(w.gd & 0xFFFFu), half_to_f32(w.gd >> 16), xh, xl, xs, xa);
+        up = q4k_chunk_dot(u8, usc, half_to_f32(w.ud & 0xFFFFu), half_to_f32(w.ud >> 16), xh, xl, xs, xa);
+      } else if (q2k) {
         const uint32_t g4[4] = {gw[0], gw[1], gw[2], gw[3]}, u4[4] = {uw[0], uw[1], uw[2], uw[3]};
         gp = q2k_chunk_dot(g4, gsc, half_to_f32(w.gd & 0xFFFFu), half_to_f32(w.gd >> 16), xh, xl, xs, xa);
         up = q2k_chunk_dot(u4, usc, half_to_f32(w.ud & 0xFFFFu), half_to_f32(w.ud >> 16), xh, xl, xs, xa);
@@ -2027,7 +2068,7 @@ __device__ __forceinline__ void gu_tile_compute(const A& a, const GuTile& t, int
 // computes every tile and refills each buffer with the tile kGuWin ahead.
 template <int FMT, class A>
 __device__ __forceinline__ void gu_tiles_issue(const A& a, const LayerPtrs& Lp, const PersistLds& L,
-                                               GuTile (&b)[kGuWin]) {
+                                               typename GuTileOf<FMT>::T (&b)[kGuWin]) {
   const int n = gu_tiles_mine(a, L);
 #pragma unroll
   for (int i = 0; i < kGuWin; ++i)
@@ -2035,7 +2076,8 @@ __device__ __forceinline__ void gu_tiles_issue(const A& a, const LayerPtrs& Lp, 
 }
 
 template <int FMT, class A>
-__device__ __forceinline__ void gu_tiles_run(const A& a, const LayerPtrs& Lp, PersistLds& L, GuTile (&b)[kGuWin],
+__device__ __forceinline__ void gu_tiles_run(const A& a, const LayerPtrs& Lp, PersistLds& L,
+                                             typename GuTileOf<FMT>::T (&b)[kGuWin],
                                              uint32_t flag) {
   const int n = gu_tiles_mine(a, L);
 #pragma unroll 1
@@ -2061,7 +2103,9 @@ __device__ __forceinline__ void down_expert(const A& a, lds_cptr w, int u, Persi
   const int rpi = 64 / lpr;
   const int rsub = lane / lpr, j = lane % lpr;
   const int q0 = L.aoff[u], q1 = L.aoff[u + 1];
-  lds_cptr wq = w, ws = w + kDownRows * nb * 64, wd = w + kDownRows * nb * 80;
+  const bool q4k = a.dfmt == kFmtQ4K;   // else Q2_K
+  const BlkGeom g = blk_geom(a.dfmt);
+  lds_cptr wq = w, ws = w + kDownRows * nb * g.q, wd = ws + kDownRows * nb * g.s;
 #pragma unroll 1
   for (int rr = rsub; rr < kDownRows; rr += rpi) {
     // one 64-weight chunk of this row at a time, read once for all pairs
@@ -2070,10 +2114,19 @@ __device__ __forceinline__ void down_expert(const A& a, lds_cptr w, int u, Persi
       const int ch = j + cc * lpr;
       const int c = ch & 3;
       const uint32_t blk = (uint32_t)rr * nb + ch / 4;
-      const uint4 qv = ld16(wq + blk * 64 + c * 16);
-      const uint32_t scm = ld4(ws + blk * 16 + c * 4);
+      uint32_t qw[8];
+      uint32_t scm;
+      if (q4k) {   // 32 code bytes per chunk; its two scales and mins
+        const uint4 qa = ld16(wq + blk * 128 + c * 32), qb = ld16(wq + blk * 128 + c * 32 + 16);
+        qw[0] = qa.x; qw[1] = qa.y; qw[2] = qa.z; qw[3] = qa.w; qw[4] = qb.x; qw[5] = qb.y; qw[6] = qb.z; qw[7] = qb.w;
+        scm = ld2(ws + blk * 16 + 2 * c) | ld2(ws + blk * 16 + 8 + 2 * c) << 16;
+      } else {
+        const uint4 qv = ld16(wq + blk * 64 + c * 16);
+        qw[0] = qv.x; qw[1] = qv.y; qw[2] = qv.z; qw[3] = qv.w;
+        qw[4] = qw[5] = qw[6] = qw[7] = 0u;
+        scm = ld4(ws + blk * 16 + c * 4);
+      }
       const uint32_t dd = ld4(wd + blk * 4);
-      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
       const float d = half_to_f32(dd & 0xFFFFu), dm = half_to_f32(dd >> 16);
 #pragma unroll 1
       for (int pos = q0; pos < q1; ++pos) {
@@ -2111,7 +2164,13 @@ __device__ __forceinline__ void down_expert(const A& a, lds_cptr w, int u, Persi
             xa[i] = cldi(&a.aa[si + i]);
           }
         }
-        float part = q2k_chunk_dot(qw, scm, d, dm, xh, xl, xs, xa);
+        float part;
+        if (q4k) {
+          part = q4k_chunk_dot(qw, scm, d, dm, xh, xl, xs, xa);
+        } else {
+          const uint32_t q2[4] = {qw[0], qw[1], qw[2], qw[3]};
+          part = q2k_chunk_dot(q2, scm, d, dm, xh, xl, xs, xa);
+        }
         part = bfly_sum_dyn(part, lpr);
         // lane j == 0 of this row group owns the entry for every chunk
         if (j == 0) L.o[pos * kDownRows + rr] = cc == 0 ? part : L.o[pos * kDownRows + rr] + part;
@@ -2369,7 +2428,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     QS_STAMP(li, 6);
     // the routed gate/up tiles' chunks are requested at once (registers);
     // meanwhile x becomes fixed-point limbs
-    GuTile gut[kGuWin];
+    typename GuTileOf<FMT>::T gut[kGuWin];
     gu_tiles_issue<FMT>(a, Lp, L, gut);
     {
       const int nb = a.H / kBlockW;
