@@ -167,6 +167,7 @@ struct qs_moe {
   int lru_head = -1, lru_tail = -1;
   std::set<int32_t> free_slots;
   std::vector<int32_t> copy_key;  // [cache_slots] key to copy into the slot at the next flush, or -1
+  std::vector<int32_t> copy_list; // the slots whose copy_key is set
   std::vector<int32_t> dirty;     // keys whose map entry changed since the last flush
   std::vector<uint8_t> seen;      // [E] marks of one layer's uses
   uint64_t c_hits = 0, c_misses = 0, c_admits = 0, c_evicts = 0, c_preloaded = 0;
@@ -426,6 +427,7 @@ void lru_push_front(qs_moe* h, int v) {  // least recent end
 void slot_take(qs_moe* h, int v, int key) {
   h->owner[v] = key;
   h->slot_of[key] = v;
+  if (h->copy_key[v] < 0) h->copy_list.push_back(v);
   h->copy_key[v] = key;
   h->dirty.push_back(key);
 }
@@ -480,15 +482,16 @@ void cache_apply(qs_moe* h, const PendingCall& pc) {
 // Enqueue the pending slot copies, then the changed map entries.
 int cache_flush(qs_moe* h, hipStream_t st) {
   const int E = h->cfg.n_experts;
-  for (int v = 0; v < (int)h->copy_key.size(); ++v) {
+  for (const int v : h->copy_list) {
     const int key = h->copy_key[v];
-    if (key < 0) continue;
+    if (key < 0) continue;              // freed again before this flush
     h->copy_key[v] = -1;
     if (h->owner[v] != key) continue;   // replaced again before this flush
     const LayerDev& L = h->layers[h->cfg.resident_layers + key / E];
     QS_HIP(hipMemcpyAsync(h->slots + (size_t)v * h->slot_bytes, L.host + (size_t)(key % E) * L.rec_bytes,
                           L.rec_bytes, hipMemcpyHostToDevice, st));
   }
+  h->copy_list.clear();
   std::sort(h->dirty.begin(), h->dirty.end());
   h->dirty.erase(std::unique(h->dirty.begin(), h->dirty.end()), h->dirty.end());
   for (size_t i0 = 0; i0 < h->dirty.size(); i0 += kEmapBatch) {
