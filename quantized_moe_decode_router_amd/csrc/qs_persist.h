@@ -2401,8 +2401,10 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     else if (!ll_read(a, xll, (QS_LDS uint32_t*)L.ax, a.T * a.H, fl, L.llerr, ll_waves(a, a.T * a.H))) return;
     QS_STAMP(li, 1);
     // sh_regs: the first round of this workgroup's shared gate/up rows is
-    // requested into registers now (after the wait, which its loads would
-    // delay) and lands during the router
+    // requested into registers now (after the x wait, which its loads would
+    // delay); the wait below takes it with the router rows.  Requested after
+    // the router instead, it delays every wave's logits polls by as long
+    // (a wave's memory operations complete in order): measured the same.
     uint4 shg[sh_pairs<A>()], shu[sh_pairs<A>()];
     if (sh_regs(a) && a.Fs) sh_gu_issue(a, Lp, 0, shg, shu);
     wait_all_and_sync();   // (and this layer's router rows and staged shared items)
