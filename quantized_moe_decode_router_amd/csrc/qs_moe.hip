@@ -711,6 +711,9 @@ PersistShape persist_shape(const qs_moe* h, int T, bool small, bool paged = fals
     const uint64_t wa = 2 * P * (F / 4) + 2 * P * (F / 16) + (uint64_t)T * Fs;
     fits = fits && wa <= 32u * kPersistThreads && (uint64_t)T * H <= 32u * kPersistThreads &&
            2ull * T * c.n_experts <= 32u * kPersistThreads;
+    // the gate/up items' cost split (gu_range) in 32-bit arithmetic: total
+    // cost at most (F / 16) * 2 P
+    fits = fits && 2ull * (h->grid_small + 1) * (F / kGateTile) * 2 * P < (1ull << 31);
   } else {
     fits = rb <= p.pfb && tile <= p.pfb && a16(sd) + pe <= p.pfb;
     // at least one shared item ahead of the routed tiles' slot

@@ -49,6 +49,7 @@ namespace qs {
 
 constexpr int kPersistThreads = 512;
 constexpr int kSmallT = 4;
+constexpr int kGuWinMax = 4;           // SMALL: routed gate/up tiles in flight per workgroup, at most
 constexpr int kShPairsLds = 8;        // shared gate/up items per register round (their LDS partials)
 constexpr int kShDnRegs = 8;          // shared down chunks per thread per register round
 constexpr int kSpinMax = 1 << 22;
@@ -165,11 +166,22 @@ __device__ int g_qs_stamp_li[kStampWgs];   // layer of the workgroup's current s
     }                                                                                     \
   } while (0)
 #define QS_STAMP2(k) QS_STAMP(g_qs_stamp_li[blockIdx.x], k)
+// point k of whichever layer ran last, in the spare row kStampLayers - 1
+// (no load of the current layer)
+#define QS_STAMP3(k)                                                                      \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < kStampWgs)                                       \
+      g_qs_stamps[((kStampLayers - 1) * kStampWgs + blockIdx.x) * kStampPts + (k)] =      \
+          __builtin_amdgcn_s_memrealtime();                                               \
+  } while (0)
 #else
 #define QS_STAMP(li, k) \
   do {                  \
   } while (0)
 #define QS_STAMP2(k) \
+  do {               \
+  } while (0)
+#define QS_STAMP3(k) \
   do {               \
   } while (0)
 #endif
@@ -437,9 +449,9 @@ __host__ __device__ inline LdsLayout lds_layout(int E, int T, int P, int H, int 
   l.o = take((uint32_t)P * kDownRows * 4);
   l.red = take(8 * 64 * 8);
   l.sh = take((uint32_t)T * kDownRows * 4);
-  l.ga = take((uint32_t)T * kGateTile * 4);
+  l.ga = take((uint32_t)(small && T > 1 ? kGuWinMax : 1) * T * kGateTile * 4);
   l.sred = take((uint32_t)(shregs ? kShPairsLds : 1) * 8 * T * 2 * 4);
-  l.qtmp = take((uint32_t)T * kGateTile * 4);
+  l.qtmp = take((uint32_t)(small && T > 1 ? kGuWinMax : 1) * T * kGateTile * 4);
   l.rinv = take((uint32_t)T * 8);
   // SMALL top-k: keys [T][S], group maxima [T][S/8], thresholds [T]
   l.kf = take(small && E > 256 ? (uint32_t)T * kf_stride(E) * 4 + (uint32_t)T * (((kf_stride(E) / 8) + 3) & ~3) * 4 +
@@ -481,9 +493,9 @@ struct PersistLds {
   QS_LDS float* o;        // [P*kDownRows] down outputs
   QS_LDS double* red;     // [8*64] cross-wave partials
   QS_LDS float* sh;       // [T*kDownRows] shared-expert down outputs
-  QS_LDS float* ga;       // [T*kGateTile] SwiGLU tile, per bucket token
+  QS_LDS float* ga;       // SMALL: [kGuWinMax][T*kGateTile] SwiGLU tiles, per bucket token
   QS_LDS float* sred;     // [8*T*2] shared gate/up cross-wave partials
-  QS_LDS int* qtmp;       // [T*kGateTile] fixed-point tile values
+  QS_LDS int* qtmp;       // SMALL: [kGuWinMax][T*kGateTile] fixed-point tile values
   QS_LDS double* rinv;    // [T] per-token RMS scale
   QS_LDS float* kf;       // SMALL [T][kf_stride(E)] fp32 selection keys
   QS_LDS int* cand;       // SMALL [T][E] top-k candidates
@@ -753,12 +765,24 @@ __device__ __forceinline__ int act_lanes(const PersistLds& L, int u0, int n) {
   return i < n ? L.act[i] : 0;
 }
 
+// SMALL: the experts' rows of the workgroup's second down tile are copied
+// ahead as well, after the first tile's, when both tiles' rows fit the region
+// at once and the shared down rows need no staging beside them (they stream
+// through registers, or there are none).
+template <class A>
+__device__ __forceinline__ bool down_pf_second(const A& a, int na) {
+  return a.H / kDownRows > a.G && (int)blockIdx.x + a.G < a.H / kDownRows && 2 * na <= down_chunk<true>(a) &&
+         (sh_regs(a) || !a.Fs);
+}
+
 template <bool SMALL, class A>
 __device__ __forceinline__ void pf_down(const A& a, const LayerPtrs& Lp, PersistLds& L, int w, int nw) {
   const int r0 = blockIdx.x * kDownRows;
   if (r0 >= a.H) return;
   QS_LDS uint8_t* base = L.pfb + down_base<SMALL>(a);
-  const int n = down_pf_count<SMALL>(a, *L.nact);
+  const int na = *L.nact;
+  const int n = down_pf_count<SMALL>(a, na);
+  const bool two = SMALL && down_pf_second(a, na);
   if (!SMALL) copy_sd_rows(a, Lp, base, r0, w, nw);   // SMALL: in L.sdr, copied a layer ahead
   for (int u0 = 0; u0 < n; u0 += 64) {
     const int el = act_lanes(L, u0, n);
@@ -777,8 +801,10 @@ __device__ __forceinline__ void pf_down(const A& a, const LayerPtrs& Lp, Persist
           rec = (const uint8_t*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(rl >> 32), i) << 32) |
                                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rl, i));
       }
-      copy_down_rows(a, Lp, base + (SMALL ? 0u : al16(sd_bytes(a))) + (uint32_t)(u0 + i) * dn_expert_bytes(a),
-                     __builtin_amdgcn_readlane(el, i), r0, w, nw, rec);
+      const int e = __builtin_amdgcn_readlane(el, i);
+      QS_LDS uint8_t* dst = base + (SMALL ? 0u : al16(sd_bytes(a))) + (uint32_t)(u0 + i) * dn_expert_bytes(a);
+      copy_down_rows(a, Lp, dst, e, r0, w, nw, rec);
+      if (two) copy_down_rows(a, Lp, dst + (uint32_t)na * dn_expert_bytes(a), e, r0 + a.G * kDownRows, w, nw, rec);
     }
   }
 }
@@ -903,9 +929,9 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
             if (lane == 0) L.red[32 + wave * V + ET * TT + j] = s;
           }
       }
-      QS_STAMP2(21);
+      QS_STAMP3(20);
       __syncthreads();
-      QS_STAMP2(22);
+      QS_STAMP3(21);
       if (qs_tid() < ET * TT) {
         const int ii = qs_tid() / TT, j = qs_tid() % TT;
         const int e = e0 + ii, t = t0 + j;
@@ -1436,6 +1462,7 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
     tau = min(tau, partner_u32<4>(tau));
     tau = min(tau, partner_u32<5>(tau));
     if (ng < k) tau = 0;
+    QS_STAMP3(22);
     bool p[4];
     int cnt = 0;
 #pragma unroll
@@ -1472,6 +1499,7 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
         }
       }
       const bool sel = live && r < k;
+      QS_STAMP3(23);
       // move each pick to the lane of its rank: expert, logit image, and its
       // position among the picks in ascending expert order
       const int u = wave_incl_scan(sel ? 1 : 0) - 1;
@@ -1844,10 +1872,9 @@ __device__ __forceinline__ void x_chunk(const A& a, const PersistLds& L, int t, 
 // slot + slots, ... and chunks j + cc*lpr of each row (the lane-per-chunk
 // layout of every gate/up GEMV here), so each 64-weight chunk is decoded
 // once and applied to every token of the bucket; a row's lanes then sum by
-// butterfly.  The chunks of the first kGuWin tiles are requested as soon as
+// butterfly.  The chunks of the first tiles (GuWin) are requested as soon as
 // the grouping is known, and each computed tile's registers are refilled
-// with the tile kGuWin ahead, so no tile waits for its own round trip.
-constexpr int kGuWin = 3;      // tiles in flight per workgroup
+// with the tile GuWin ahead, so no tile waits for its own round trip.
 constexpr int kGuUnits = 2;    // (row, chunk) units per thread and tile: H <= 4096
 
 struct GuChunk {
@@ -1869,17 +1896,63 @@ struct GuTile4 {
 template <int FMT> struct GuTileOf { typedef GuTile T; };
 template <> struct GuTileOf<kFmtQ4K> { typedef GuTile4 T; };
 
+// Tiles in flight: four for the fixed shapes of several tokens up to hidden
+// 2048 (one (row, chunk) unit per thread and tile; a workgroup's run there
+// is up to four items), three otherwise (register budget, code size).
+template <class A, bool FIXED = A::kFixedShape>
+struct GuWin {
+  static constexpr int v = 3;
+};
 template <class A>
-__device__ __forceinline__ int gu_tiles_mine(const A& a, const PersistLds& L) {
-  return my_count(a, *L.nact * (a.F / kGateTile));
+struct GuWin<A, true> {
+  static constexpr int v = A::H <= 2048 && A::T > 1 ? kGuWinMax : 3;
+};
+
+// The routed gate/up items (active expert u, 16-row tile), u-major, of
+// workgroup b: items i0 + m * stride, m < n.  One token: every bucket holds
+// one pair, so an even split (runs of N / G items when G divides the N
+// items, else items b, b + G, ...).  More tokens: split by cost -- an item of a
+// bucket of n tokens costs n + 1 (its chunks are decoded once, then dotted
+// with each token's), and workgroup b takes the items whose cost midpoint
+// falls in the b-th 1/G of the total, a contiguous run.  Every wave computes
+// the same run (the host bounds 2 (G + 1) times the total cost below 2^31).
+struct GuRange {
+  int i0, stride, n;
+};
+template <class A>
+__device__ __forceinline__ GuRange gu_range(const A& a, const PersistLds& L) {
+  const int lane = qs_tid() & 63, na = *L.nact, tiles = a.F / kGateTile;
+  if (a.T == 1) {   // (a run of N / G items when G divides them: adjacent tiles of one expert)
+    const int N = na * tiles;
+    if (N % a.G == 0) return {(int)blockIdx.x * (N / a.G), 1, N / a.G};
+    return {(int)blockIdx.x, a.G, my_count(a, N)};
+  }
+  const uint32_t G = (uint32_t)a.G, C = (uint32_t)tiles * (uint32_t)(L.aoff[na] + na), b = blockIdx.x;
+  // items of this lane's experts whose owner is below x: owner(u, t) < x
+  // <=> G (2 S_u + (2 t + 1) c_u) < 2 x C, S_u the cost of the items before u
+  int c0 = 0, c1 = 0;
+  for (int u = lane; u < na; u += 64) {
+    const uint32_t cu = (uint32_t)(L.aoff[u + 1] - L.aoff[u] + 1), S = (uint32_t)tiles * (uint32_t)(L.aoff[u] + u);
+    const uint32_t base = G * (2 * S + cu), den = 2 * G * cu;
+    auto below = [&](uint32_t x) {
+      const uint32_t lim = 2 * x * C;
+      if (lim <= base) return 0;
+      const uint32_t t = (lim - base + den - 1) / den;
+      return (int)(t < (uint32_t)tiles ? t : (uint32_t)tiles);
+    };
+    c0 += below(b);
+    c1 += below(b + 1);
+  }
+  c0 = bfly_sum_i32<6>(c0);
+  c1 = bfly_sum_i32<6>(c1);
+  return {__builtin_amdgcn_readfirstlane(c0), 1, __builtin_amdgcn_readfirstlane(c1 - c0)};
 }
 
 template <int FMT, class A>
-__device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, const PersistLds& L, int m,
+__device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, const PersistLds& L, int item,
                                              typename GuTileOf<FMT>::T& t) {
   const int tiles = a.F / kGateTile, nch = a.H / kChunkW, lpr = lanes_per_row(nch), cpl = nch / lpr;
   const int slots = kPersistThreads / lpr, slot = qs_tid() / lpr, j = qs_tid() % lpr;
-  const int item = (int)blockIdx.x + m * a.G;
   const int u = item / tiles, f0 = (item % tiles) * kGateTile;
   const int e = L.act[u];
   const uint32_t nbh = a.H / kBlockW;
@@ -1931,55 +2004,61 @@ __device__ __forceinline__ void gu_tile_load(const A& a, const LayerPtrs& Lp, co
   }
 }
 
-// Quantise the 16 SwiGLU outputs of each bucket token (16 lanes per token)
-// and store them as flagged words.
+// One wave: quantise the 16 SwiGLU outputs of each bucket token (16 lanes
+// per token; a bucket holds at most kSmallT = 4 tokens) from the tile's slot
+// ga, and store them as flagged words (qt: this wave's scratch slot).
 template <class A>
-__device__ __forceinline__ void gu_tile_store(const A& a, int p0, int n, int f0, PersistLds& L, uint32_t flag) {
-  const int wave = qs_tid() >> 6, lane = qs_tid() & 63, nw = kPersistThreads >> 6;
-  for (int tb = wave * 4; tb < n; tb += nw * 4) {
-    const int tt = tb + (lane >> 4), r = lane & 15;
-    const bool live = tt < n;
-    const float v = live ? L.ga[tt * kGateTile + r] : 0.f;
-    const float m = bfly_max<4>(fabsf(v));
-    const int ex = fixed_exp(m);
-    const int q = to_fixed(v, ex);
-    const int s = bfly_sum_i32<4>(q);
-    if (live) L.qtmp[tt * kGateTile + r] = q;
-    __builtin_amdgcn_wave_barrier();
-    if (live) {
-      const int pair = L.pairs[p0 + tt];
-      if (r < 4) {
-        int h[4], l[4];
+__device__ __forceinline__ void gu_tile_store_wave(const A& a, int p0, int n, int f0, const QS_LDS float* ga,
+                                                   QS_LDS int* qt, const PersistLds& L, uint32_t flag) {
+  const int lane = qs_tid() & 63;
+  const int tt = lane >> 4, r = lane & 15;
+  const bool live = tt < n;
+  const float v = live ? ga[tt * kGateTile + r] : 0.f;
+  const float m = bfly_max<4>(fabsf(v));
+  const int ex = fixed_exp(m);
+  const int q = to_fixed(v, ex);
+  const int s = bfly_sum_i32<4>(q);
+  if (live) qt[tt * kGateTile + r] = q;
+  __builtin_amdgcn_wave_barrier();
+  if (live) {
+    const int pair = L.pairs[p0 + tt];
+    if (r < 4) {
+      int h[4], l[4];
 #pragma unroll
-        // (word r: values r, 4+r, 8+r, 12+r for the Q2_K down dot; 4r..4r+3
-        // for the Q4_K-style one)
-        for (int i = 0; i < 4; ++i)
-          split_limbs(L.qtmp[tt * kGateTile + (a.dfmt == kFmtQ4K ? 4 * r + i : 4 * i + r)], h[i], l[i]);
-        const size_t wi = (size_t)pair * (a.F / 4) + f0 / 4 + r;
-        ll_store(a.ll_a + wi, pack4(h[0], h[1], h[2], h[3]), flag);
-        ll_store(a.ll_a + ll_al(a) + wi, pack4(l[0], l[1], l[2], l[3]), flag);
-      }
-      if (r == 0) {
-        const size_t si = (size_t)pair * (a.F / kSubW) + f0 / kSubW;
-        ll_store(a.ll_a + ll_as(a) + si, __float_as_uint(ldexpf(1.0f, ex - kFixedBits)), flag);
-        ll_store(a.ll_a + ll_aa(a) + si, (uint32_t)s, flag);
-      }
+      // (word r: values r, 4+r, 8+r, 12+r for the Q2_K down dot; 4r..4r+3
+      // for the Q4_K-style one)
+      for (int i = 0; i < 4; ++i)
+        split_limbs(qt[tt * kGateTile + (a.dfmt == kFmtQ4K ? 4 * r + i : 4 * i + r)], h[i], l[i]);
+      const size_t wi = (size_t)pair * (a.F / 4) + f0 / 4 + r;
+      ll_store(a.ll_a + wi, pack4(h[0], h[1], h[2], h[3]), flag);
+      ll_store(a.ll_a + ll_al(a) + wi, pack4(l[0], l[1], l[2], l[3]), flag);
+    }
+    if (r == 0) {
+      const size_t si = (size_t)pair * (a.F / kSubW) + f0 / kSubW;
+      ll_store(a.ll_a + ll_as(a) + si, __float_as_uint(ldexpf(1.0f, ex - kFixedBits)), flag);
+      ll_store(a.ll_a + ll_aa(a) + si, (uint32_t)s, flag);
     }
   }
-  // (also keeps the other waves' later reads of L.ga behind these stores)
-  __syncthreads();
 }
 
-// Tile m of this workgroup from its registers: SwiGLU of its 16 rows for
-// every token of the bucket (at most kSmallT), quantised per 16 rows and
-// stored as flagged words.
+// An item's active-expert slot u and first row f0.
+template <class A>
+__device__ __forceinline__ void gu_tile_item(const A& a, int item, int& u, int& f0) {
+  const int tiles = a.F / kGateTile;
+  u = item / tiles;
+  f0 = (item % tiles) * kGateTile;
+}
+
+// Item `item` from its registers: SwiGLU of its 16 rows for every token of
+// the bucket (at most kSmallT), into the slot ga.
 template <int FMT, class A>
-__device__ __forceinline__ void gu_tile_compute(const A& a, const typename GuTileOf<FMT>::T& t, int m, PersistLds& L,
-                                                uint32_t flag) {
-  const int tiles = a.F / kGateTile, nch = a.H / kChunkW, lpr = lanes_per_row(nch), cpl = nch / lpr;
+__device__ __forceinline__ void gu_tile_dots(const A& a, const typename GuTileOf<FMT>::T& t, int item,
+                                             const PersistLds& L, QS_LDS float* ga) {
+  const int nch = a.H / kChunkW, lpr = lanes_per_row(nch), cpl = nch / lpr;
   const int slots = kPersistThreads / lpr, slot = qs_tid() / lpr, j = qs_tid() % lpr;
-  const int item = (int)blockIdx.x + m * a.G;
-  const int u = item / tiles, f0 = (item % tiles) * kGateTile;
+  int u, f0;
+  gu_tile_item(a, item, u, f0);
+  (void)f0;
   const int p0 = L.aoff[u], n = L.aoff[u + 1] - p0;
   constexpr bool q2k = FMT == 1;
   float gacc[4] = {0.f, 0.f, 0.f, 0.f}, uacc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -2055,39 +2134,58 @@ __device__ __forceinline__ void gu_tile_compute(const A& a, const typename GuTil
         if (tt >= n) continue;
         const float g = bfly_sum_dyn(gacc[tt], lpr);
         const float uu = bfly_sum_dyn(uacc[tt], lpr);
-        if (j == 0) L.ga[tt * kGateTile + r] = silu_mul(g, uu);
+        if (j == 0) ga[tt * kGateTile + r] = silu_mul(g, uu);
       }
     }
   }
-  __syncthreads();
-  QS_STAMP2(16);
-  gu_tile_store(a, p0, n, f0, L, flag);
 }
 
-// Tiles [0, kGuWin) of this workgroup are requested by gu_tiles_issue; this
-// computes every tile and refills each buffer with the tile kGuWin ahead.
-template <int FMT, class A>
+// The first W items of this workgroup are requested by gu_tiles_issue.
+template <int FMT, class A, int W>
 __device__ __forceinline__ void gu_tiles_issue(const A& a, const LayerPtrs& Lp, const PersistLds& L,
-                                               typename GuTileOf<FMT>::T (&b)[kGuWin]) {
-  const int n = gu_tiles_mine(a, L);
+                                               const GuRange& R, typename GuTileOf<FMT>::T (&b)[W]) {
 #pragma unroll
-  for (int i = 0; i < kGuWin; ++i)
-    if (i < n) gu_tile_load<FMT>(a, Lp, L, i, b[i]);
+  for (int i = 0; i < W; ++i)
+    if (i < R.n) gu_tile_load<FMT>(a, Lp, L, R.i0 + i * R.stride, b[i]);
 }
 
-template <int FMT, class A>
-__device__ __forceinline__ void gu_tiles_run(const A& a, const LayerPtrs& Lp, PersistLds& L,
-                                             typename GuTileOf<FMT>::T (&b)[kGuWin],
-                                             uint32_t flag) {
-  const int n = gu_tiles_mine(a, L);
+// Every tile in registers at once (n <= W): the dots of all of them, one
+// block barrier, then tile m's stores by wave m, side by side.  More tiles:
+// each tile's dots, a barrier, its stores by wave 0 and a barrier before its
+// slot is reused, and its registers are refilled with the tile W ahead.
+template <int FMT, class A, int W>
+__device__ __forceinline__ void gu_tiles_run(const A& a, const LayerPtrs& Lp, PersistLds& L, const GuRange& R,
+                                             typename GuTileOf<FMT>::T (&b)[W], uint32_t flag) {
+  static_assert(W <= kGuWinMax && W <= kPersistThreads / 64, "an LDS slot and a storing wave per tile");
+  const int n = R.n;
+  const int wave = qs_tid() >> 6, slot = a.T * kGateTile;   // (the LDS holds kGuWinMax slots of T * kGateTile)
+  const bool side = n <= W && a.T > 1;   // (one token: one slot in LDS)
+  auto store = [&](int m, int s) {
+    int u, f0;
+    gu_tile_item(a, R.i0 + m * R.stride, u, f0);
+    const int p0 = L.aoff[u];
+    gu_tile_store_wave(a, p0, L.aoff[u + 1] - p0, f0, L.ga + s * slot, L.qtmp + s * slot, L, flag);
+  };
 #pragma unroll 1
-  for (int m0 = 0; m0 < n; m0 += kGuWin) {
+  for (int m0 = 0; m0 < n; m0 += W) {
 #pragma unroll
-    for (int i = 0; i < kGuWin; ++i) {
+    for (int i = 0; i < W; ++i) {
       if (m0 + i >= n) break;
-      gu_tile_compute<FMT>(a, b[i], m0 + i, L, flag);
-      if (m0 + i + kGuWin < n) gu_tile_load<FMT>(a, Lp, L, m0 + i + kGuWin, b[i]);
+      gu_tile_dots<FMT>(a, b[i], R.i0 + (m0 + i) * R.stride, L, L.ga + (side ? i : 0) * slot);
+      if (side) continue;
+      __syncthreads();
+      if (wave == 0) store(m0 + i, 0);
+      __syncthreads();   // (the slot is rewritten by the next tile)
+      if (m0 + i + W < n) gu_tile_load<FMT>(a, Lp, L, R.i0 + (m0 + i + W) * R.stride, b[i]);
     }
+  }
+  if (side) {
+    QS_STAMP3(1);
+    __syncthreads();
+    if (wave < n) store(wave, wave);
+    // (also keeps the other waves' polls and copies of the next phase behind
+    // these stores)
+    __syncthreads();
   }
 }
 
@@ -2298,22 +2396,28 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
   // waves without down-row copies in flight, when the words fit them)
   if (!ll_read(a, a.ll_a, (QS_LDS uint32_t*)L.dah, ll_a_words(a), flag_a, L.llerr, ll_a_waves(a))) return false;
   QS_STAMP(li, 11);
-  // sh_regs: the shared down rows of this workgroup's first tiles, into
-  // registers (after the wait, which their loads would delay); they land
-  // during the routed down GEMVs
-  static_assert(kDownRows == kPersistThreads / 64, "one shared down row per wave");
-  uint4 sdv[sh_dn_regs<A>()];
-  if (sh_regs(a) && a.Fs) sh_dn_issue(a, Lp, 0, sdv);
   float macc = 0.f;   // steering: this thread's output of the first tile (idx = thread)
   wait_all_and_sync();   // the down rows copied ahead
   QS_STAMP(li, 12);
+  // sh_regs: the shared down rows of this workgroup's first tiles, into
+  // registers; requested after both waits (the flagged read's polls and the
+  // copies' landing would each wait for them: a wave's memory operations
+  // complete in order), they land during the routed down GEMVs
+  static_assert(kDownRows == kPersistThreads / 64, "one shared down row per wave");
+  uint4 sdv[sh_dn_regs<A>()];
+  if (sh_regs(a) && a.Fs) sh_dn_issue(a, Lp, 0, sdv);
+  const bool two = down_pf_second(a, na);   // the second tile's rows were copied ahead too
   for (int tile = blockIdx.x; tile < n_tiles; tile += a.G) {
     const int r0 = tile * kDownRows;
     const bool first = tile == (int)blockIdx.x;
     // experts in chunks that fit beside the shared rows
     for (int u0 = 0; u0 < na; u0 += chunk) {       // na >= 1, chunk >= 1
       const int u1 = na - u0 < chunk ? na : u0 + chunk;
-      if (!first || u0 > 0) {
+      const int jq = (tile - (int)blockIdx.x) / a.G;
+      if (u0 == 0 && jq < 2) QS_STAMP3(12 + 4 * jq);
+      const bool ahead = first ? u0 == 0 : two && jq == 1;   // (then u0 == 0: one chunk holds every expert)
+      QS_LDS uint8_t* rows = base + (first || !ahead ? 0u : (uint32_t)na * pe);
+      if (!ahead) {
         stage_now([&](int w, int n) {
           if (u0 == 0 && !sh_regs(a)) copy_sd_rows(a, Lp, L.sdr, r0, w, n);
           for (int c0 = u0; c0 < u1; c0 += 64) {
@@ -2324,8 +2428,9 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
           }
         });
       }
-      for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, base + (uint32_t)(u - u0) * pe, u, L);
-      QS_STAMP2(23);
+      if (u0 == 0 && jq < 2) QS_STAMP3(13 + 4 * jq);
+      for (int u = u0 + wave; u < u1; u += kPersistThreads / 64) down_expert<true>(a, rows + (uint32_t)(u - u0) * pe, u, L);
+      if (u0 == 0 && jq < 2) QS_STAMP3(14 + 4 * jq);
       if (u0 == 0 && a.Fs) {
         if (!sh_regs(a)) {
           shared_down_row<true>(a, L.sdr + (uint32_t)wave * srow_bytes(a.Fs, a.sq8 != 0), L);
@@ -2334,6 +2439,7 @@ __device__ __forceinline__ bool phase_down_small(const A& a, int li, const Layer
           if (jr > 0 && jr % nr == 0) sh_dn_issue(a, Lp, jr, sdv);   // the next round of rows
           sh_dn_compute(a, sdv, jr % nr, L);
         }
+        if (jq < 2) QS_STAMP3(15 + 4 * jq);
       }
     }
     __syncthreads();
@@ -2407,6 +2513,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     // (a wave's memory operations complete in order): measured the same.
     uint4 shg[sh_pairs<A>()], shu[sh_pairs<A>()];
     if (sh_regs(a) && a.Fs) sh_gu_issue(a, Lp, 0, shg, shu);
+    QS_STAMP3(8);
     wait_all_and_sync();   // (and this layer's router rows and staged shared items)
     QS_STAMP(li, 2);
     if ((int)blockIdx.x >= router_groups(a)) token_rinv<true>(a, L, a.x_in, 0, a.T);
@@ -2419,6 +2526,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
       for (int j0 = 0; j0 < mine; j0 += nr) {
         if (j0 > 0) sh_gu_issue(a, Lp, j0, shg, shu);
         sh_gu_compute(a, shg, shu, j0, L, fl + 2);
+        if (j0 / nr < 3) QS_STAMP3(9 + j0 / nr);
       }
     }
     QS_STAMP(li, 4);
@@ -2430,8 +2538,10 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     QS_STAMP(li, 6);
     // the routed gate/up tiles' chunks are requested at once (registers);
     // meanwhile x becomes fixed-point limbs
-    typename GuTileOf<FMT>::T gut[kGuWin];
-    gu_tiles_issue<FMT>(a, Lp, L, gut);
+    typename GuTileOf<FMT>::T gut[GuWin<A>::v];
+    const GuRange gr = gu_range(a, L);
+    gu_tiles_issue<FMT>(a, Lp, L, gr, gut);
+    QS_STAMP3(0);
     {
       const int nb = a.H / kBlockW;
       for (int u = wave; u < a.T * nb; u += nw) quant_x_wave<true>(a, a.x_in, u / nb, u % nb, L);
@@ -2440,7 +2550,7 @@ __device__ __forceinline__ void persist_small_body(const A& a) {
     __syncthreads();
     QS_STAMP(li, 8);
     // ---- GU
-    gu_tiles_run<FMT>(a, Lp, L, gut, fl + 2);
+    gu_tiles_run<FMT>(a, Lp, L, gr, gut, fl + 2);
     QS_STAMP(li, 9);
     // region B (unused during GU) receives the down rows of the active
     // experts, from the waves that do not poll the SwiGLU words
