@@ -1412,8 +1412,10 @@ __device__ __forceinline__ void group_one_token(const A& a, PersistLds& L) {
 // bounds every top-k key from below (k groups hold a key >= tau, and a
 // larger key means a larger logit).  The experts with key >= tau -- about
 // k + 3 at these shapes -- are compacted in index order and each ranks
-// itself against all of them on the order-preserving images of their fp64
-// logits, ties to the lower position, i.e. the lower expert id.  The picks
+// itself against all of them: on their fp32 keys when no two candidates
+// share one (a larger key means a larger logit), else on the
+// order-preserving images of their fp64 logits, ties to the lower position,
+// i.e. the lower expert id.  The picks
 // are then moved to the lane of their rank (one crossbar permute) so that
 // the weights are summed in rank order, as the batched kernel does.
 template <class A>
@@ -1473,29 +1475,58 @@ __device__ __forceinline__ void topk_small(const A& a, int layer_i, PersistLds& 
     const int incl = wave_incl_scan(cnt);
     const int m = __builtin_amdgcn_readlane(incl, 63);
     // candidates in index order: ids in cd, fp64 keys over this token's
-    // logit row (read into registers above)
+    // logit row (read into registers above), fp32 keys in the router's
+    // partials area (free until the next layer's router)
     QS_LDS uint64_t* ck = (QS_LDS uint64_t*)lg;
+    static_assert(kSmallT * 80 * 4 <= 8 * 64 * 8, "fp32 candidate keys fit the router partials area");
+    QS_LDS uint32_t* c32 = (QS_LDS uint32_t*)L.red + t * 80;
     int pos = incl - cnt;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (p[j]) {
         cd[pos] = e0 + j;
         ck[pos] = f64_ord(v[j]);
+        c32[pos] = ku[j];
         ++pos;
       }
     if (m <= 64) {
       const bool live = lane < m;
+      if (lane < 16) c32[m + lane] = 0u;   // padding: below every real key
       const uint64_t K = live ? ck[lane] : 0;
+      const uint32_t K32 = live ? c32[lane] : 0u;
       const int e = live ? cd[lane] : 0;
-      int r = 0;
+      // rank on the fp32 keys: a larger key means a larger logit, so when no
+      // two candidates share an fp32 key the rank is the count of larger keys
+      int r = 0, eq = 0;
       for (int j0 = 0; j0 < m; j0 += 16) {
-        uint64_t w[16];
+        uint32_t w[16];
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) w[jj] = j0 + jj < m ? ck[j0 + jj] : 0;
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v4 = lds_u4(c32 + j0 + 4 * q);
+          w[4 * q] = v4.x;
+          w[4 * q + 1] = v4.y;
+          w[4 * q + 2] = v4.z;
+          w[4 * q + 3] = v4.w;
+        }
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          const int j = j0 + jj;
-          r += (j < m && (w[jj] > K || (w[jj] == K && j < lane))) ? 1 : 0;
+          r += w[jj] > K32 ? 1 : 0;
+          eq += w[jj] == K32 ? 1 : 0;
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(live && eq > 1)) {
+        // equal fp32 keys: rank on the order-preserving images of the fp64
+        // logits, ties to the lower position (the lower expert id)
+        r = 0;
+        for (int j0 = 0; j0 < m; j0 += 16) {
+          uint64_t w[16];
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) w[jj] = j0 + jj < m ? ck[j0 + jj] : 0;
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int j = j0 + jj;
+            r += (j < m && (w[jj] > K || (w[jj] == K && j < lane))) ? 1 : 0;
+          }
         }
       }
       const bool sel = live && r < k;
