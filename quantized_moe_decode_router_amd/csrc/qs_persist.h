@@ -936,10 +936,19 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
         const int ii = qs_tid() / TT, j = qs_tid() % TT;
         const int e = e0 + ii, t = t0 + j;
         if (e < a.E && j < nt) {
+          // every wave's partials requested at once, then summed in wave
+          // order (the q slots hold no sums without the pre-norm; unused)
+          double sp[kPersistThreads / 64], qp[kPersistThreads / 64];
+#pragma unroll
+          for (int w = 0; w < kPersistThreads / 64; ++w) {
+            sp[w] = L.red[32 + w * V + ii * TT + j];
+            qp[w] = L.red[32 + w * V + ET * TT + j];
+          }
           double s = 0.0, q = 0.0;
-          for (int w = 0; w < nw; ++w) {
-            s += L.red[32 + w * V + ii * TT + j];
-            if (want_ss) q += L.red[32 + w * V + ET * TT + j];
+#pragma unroll
+          for (int w = 0; w < kPersistThreads / 64; ++w) {
+            s += sp[w];
+            q += qp[w];
           }
           const double r = a.prenorm ? rms_inv_of(q, a.H) : 1.0;
           const double lv = a.prenorm ? fma(s, r, bias) : s + bias;
