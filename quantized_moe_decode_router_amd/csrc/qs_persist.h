@@ -594,6 +594,12 @@ __device__ __forceinline__ int sh_rows(const A& a) { return kSharedItemRows; }
 // Below, LDS staging a layer ahead by the copy waves measured faster.
 template <class A>
 __device__ __forceinline__ bool sh_regs(const A& a) { return A::kFixedShape && a.H > 2048; }
+// the same at compile time
+template <class A>
+constexpr bool wide_fixed() {
+  if constexpr (A::kFixedShape) return A::H > 2048;
+  else return false;
+}
 template <bool SMALL, class A>
 __device__ __forceinline__ int n_shared_items(const A& a) { return a.Fs / sh_rows<SMALL>(a); }
 template <bool SMALL, class A>
@@ -944,6 +950,7 @@ __device__ __forceinline__ void phase_router(const A& a, const LayerPtrs& Lp, co
             sp[w] = L.red[32 + w * V + ii * TT + j];
             qp[w] = L.red[32 + w * V + ET * TT + j];
           }
+          __builtin_amdgcn_sched_barrier(0);
           double s = 0.0, q = 0.0;
 #pragma unroll
           for (int w = 0; w < kPersistThreads / 64; ++w) {
@@ -2287,6 +2294,9 @@ __device__ __forceinline__ void down_expert(const A& a, lds_cptr w, int u, Persi
             xs[i] = L.das[si + i];
             xa[i] = L.daa[si + i];
           }
+          // (every read above in flight before the first use: one wait;
+          // not where the registers are spent on the shared expert)
+          if constexpr (!wide_fixed<A>()) __builtin_amdgcn_sched_barrier(0);
         } else {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
