@@ -8,7 +8,10 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqsmoe.so")
+# QSMOE_LIB_VARIANT=stamps selects the profiling build (phase stamps
+# compiled in, see build.py); otherwise the library itself
+LIB_PATH = os.path.join(_HERE, "libqsmoe_stamps.so" if os.environ.get("QSMOE_LIB_VARIANT") == "stamps"
+                        else "libqsmoe.so")
 
 QS_MOE_ABI_VERSION = 5
 QS_OK, QS_E_INVAL, QS_E_NOMEM, QS_E_HIP, QS_E_STATE, QS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5

@@ -35,11 +35,19 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every source into libqsmoe.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+# The profiling variant: the same sources with phase stamps compiled in
+# (thread 0 of each workgroup records the wall clock at phase boundaries;
+# read back by phase_stamps.py).  Never loaded unless asked for.
+LIB_STAMPS = os.path.join(PKG, "libqsmoe_stamps.so")
+
+
+def build_library(verbose: bool = False, stamps: bool = False) -> str:
+    """Compile every source into libqsmoe.so (stamps: libqsmoe_stamps.so);
+    returns its path."""
+    out = LIB_STAMPS if stamps else LIB
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *(["-DQS_STAMPS"] if stamps else []), "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,9 +58,9 @@ def build_library(verbose: bool = False) -> str:
                      if "packed-fp32-ops" not in l and l.strip())
     if warn and verbose:
         sys.stderr.write(warn + "\n")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build_library(verbose=True))
+    print(build_library(verbose=True, stamps="--stamps" in sys.argv[1:]))
