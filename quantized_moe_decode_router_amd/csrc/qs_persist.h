@@ -493,9 +493,9 @@ struct PersistLds {
   QS_LDS float* o;        // [P*kDownRows] down outputs
   QS_LDS double* red;     // [8*64] cross-wave partials
   QS_LDS float* sh;       // [T*kDownRows] shared-expert down outputs
-  QS_LDS float* ga;       // SMALL: [kGuWinMax][T*kGateTile] SwiGLU tiles, per bucket token
+  QS_LDS float* ga;       // SMALL: [kGuWinMax][T*kGateTile] SwiGLU tiles, per bucket token (one slot at T = 1)
   QS_LDS float* sred;     // [8*T*2] shared gate/up cross-wave partials
-  QS_LDS int* qtmp;       // SMALL: [kGuWinMax][T*kGateTile] fixed-point tile values
+  QS_LDS int* qtmp;       // SMALL: [kGuWinMax][T*kGateTile] fixed-point tile values (one slot at T = 1)
   QS_LDS double* rinv;    // [T] per-token RMS scale
   QS_LDS float* kf;       // SMALL [T][kf_stride(E)] fp32 selection keys
   QS_LDS int* cand;       // SMALL [T][E] top-k candidates
@@ -2205,7 +2205,7 @@ __device__ __forceinline__ void gu_tiles_run(const A& a, const LayerPtrs& Lp, Pe
                                              typename GuTileOf<FMT>::T (&b)[W], uint32_t flag) {
   static_assert(W <= kGuWinMax && W <= kPersistThreads / 64, "an LDS slot and a storing wave per tile");
   const int n = R.n;
-  const int wave = qs_tid() >> 6, slot = a.T * kGateTile;   // (the LDS holds kGuWinMax slots of T * kGateTile)
+  const int wave = qs_tid() >> 6, slot = a.T * kGateTile;   // (LDS: kGuWinMax slots of T * kGateTile above one token)
   const bool side = n <= W && a.T > 1;   // (one token: one slot in LDS)
   auto store = [&](int m, int s) {
     int u, f0;
